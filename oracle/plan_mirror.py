@@ -1,0 +1,166 @@
+"""Independent mirror of the plan rule -- TEST INFRASTRUCTURE ONLY.
+
+The pages fix no plan: the tLoRA page (tLoRA: Efficient Multi-LoRA Training
+with Elastic Shared Super-Models, abstract) says only that the fused kernel
+re-forms low-rank tiles and schedules rank-aware nano-batches, and the PLoRA
+page (§9.2) that adapters are concatenated and work is tiled along the token
+and hidden axes, never along the rank.  The rule below is this library's own;
+it is written down once (the library header states the same rule) and
+re-implemented here in plain Python so the C++ builder can be checked bit for
+bit.
+
+Rule (all integers; counts and indexes int32, offsets into tensors int64):
+ 1. r_pad(i) = max(32, smallest power of two >= r_i); 1 <= r_i <= 256.
+ 2. zoff(i) = sum_{j<i} n_j r_pad(j);  roff(i) = sum_{j<i} r_pad(j).
+ 3. Stream groups: S' = min(S, n); g_0 = 0, g_S' = n; for 1 <= s < S',
+    g_s = max(g_{s-1}, first adapter a with o_a >= ceil(s T / S'), else n).
+ 4. Within each group, adapters are visited by r_pad descending, then index
+    ascending ("bucket order").
+ 5. Nano-batches: in bucket order, each adapter's rows cut into consecutive
+    pieces of NB rows (last one partial; none when n_i = 0).  Entry
+    (adapter, first row, rows).
+ 6. Reduction chunks: the same walk with KC_i = min(chunk_max, max(chunk_min,
+    chunk_per_rank * r_pad(i))) rows per piece.  Entry (adapter, first row,
+    rows); cpref(c) = sum of r_pad over earlier chunks.  Each adapter's chunks
+    are consecutive: first(i), count(i) (first = total chunks before it in the
+    walk order when count is 0 is still defined as the walk position).
+ 7. GEMM row tiles: per group, rows [o_{g_s}, o_{g_{s+1}}) cut into tiles of
+    BM rows.  For each tile, its extension steps: for every adapter j
+    (ascending) whose rows meet the tile, for k0 = 0, 64, ... < r_pad(j): entry
+    (j, lo, hi, k0) with [lo, hi) the rows of j inside the tile.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+KSTEP = 64
+
+
+@dataclass
+class PlanOpts:
+    nano_rows: int = 32
+    gemm_rows: int = 256
+    n_streams: int = 1
+    chunk_min: int = 256
+    chunk_max: int = 2048
+    chunk_per_rank: int = 8
+
+
+def _pow2_at_least(r: int) -> int:
+    p = 1
+    while p < r:
+        p *= 2
+    return p
+
+
+def build_plan(offsets, ranks, opts: PlanOpts | None = None) -> dict:
+    opts = opts or PlanOpts()
+    o = [int(v) for v in offsets]
+    rk = [int(v) for v in ranks]
+    n = len(rk)
+    assert len(o) == n + 1 and o[0] == 0
+    assert all(o[i] <= o[i + 1] for i in range(n))
+    assert all(1 <= r <= 256 for r in rk)
+    T = o[n]
+    cnt = [o[i + 1] - o[i] for i in range(n)]
+    rpad = [max(32, _pow2_at_least(r)) for r in rk]
+
+    zoff, roff = [], []
+    z = rr = 0
+    for i in range(n):
+        zoff.append(z)
+        roff.append(rr)
+        z += cnt[i] * rpad[i]
+        rr += rpad[i]
+
+    S = min(opts.n_streams, n)
+    g = [0] * (S + 1)
+    g[S] = n
+    for s in range(1, S):
+        target = -(-(s * T) // S)  # ceil
+        a = n
+        for j in range(n):
+            if o[j] >= target:
+                a = j
+                break
+        g[s] = max(g[s - 1], a)
+
+    def bucket_order(s):
+        idx = list(range(g[s], g[s + 1]))
+        return sorted(idx, key=lambda i: (-rpad[i], i))
+
+    nb, nb_start = [], []
+    ch, ch_start, cpref = [], [], []
+    ch_first = [0] * n
+    ch_count = [0] * n
+    cp = 0
+    for s in range(S):
+        nb_start.append(len(nb))
+        ch_start.append(len(ch))
+        for i in bucket_order(s):
+            r0 = o[i]
+            while r0 < o[i + 1]:
+                nb.append((i, r0, min(opts.nano_rows, o[i + 1] - r0)))
+                r0 += opts.nano_rows
+            kc = min(opts.chunk_max, max(opts.chunk_min, opts.chunk_per_rank * rpad[i]))
+            ch_first[i] = len(ch)
+            r0 = o[i]
+            while r0 < o[i + 1]:
+                ch.append((i, r0, min(kc, o[i + 1] - r0)))
+                cpref.append(cp)
+                cp += rpad[i]
+                ch_count[i] += 1
+                r0 += kc
+    nb_start.append(len(nb))
+    ch_start.append(len(ch))
+
+    tiles, tile_start, ext, ext_start = [], [], [], []
+    BM = opts.gemm_rows
+    for s in range(S):
+        tile_start.append(len(tiles))
+        R0, R1 = o[g[s]], o[g[s + 1]]
+        t0 = R0
+        while t0 < R1:
+            rows = min(BM, R1 - t0)
+            ext_start.append(len(ext))
+            for j in range(g[s], g[s + 1]):
+                lo, hi = max(o[j], t0), min(o[j + 1], t0 + rows)
+                if lo < hi:
+                    for k0 in range(0, rpad[j], KSTEP):
+                        ext.append((j, lo, hi, k0))
+            tiles.append((t0, rows))
+            t0 += BM
+    tile_start.append(len(tiles))
+    ext_start.append(len(ext))
+
+    def a32(x, cols=None):
+        a = np.asarray(x, dtype=np.int32)
+        if cols is not None:
+            a = a.reshape(-1, cols)
+        return a
+
+    return {
+        "T": T,
+        "n": n,
+        "n_groups": S,
+        "z_elems": z,
+        "rpad_total": rr,
+        "partial_rows": cp,
+        "rpad": a32(rpad),
+        "zoff": np.asarray(zoff, dtype=np.int64),
+        "roff": a32(roff),
+        "group_first_adapter": a32(g),
+        "nb": a32(nb, 3),
+        "nb_start": a32(nb_start),
+        "chunks": a32(ch, 3),
+        "chunk_start": a32(ch_start),
+        "chunk_rpref": a32(cpref),
+        "adapter_chunk_first": a32(ch_first),
+        "adapter_chunk_count": a32(ch_count),
+        "tiles": a32(tiles, 2),
+        "tile_start": a32(tile_start),
+        "ext": a32(ext, 4),
+        "tile_ext_start": a32(ext_start),
+    }
