@@ -1,0 +1,10 @@
+"""Packed multi-LoRA linear layer (forward and backward) for AMD MI355X.
+
+The compute lives in ``libmlora.so`` (HIP, gfx950, built in-tree by
+``adapter_lora_segments_amd.build``); this package only marshals arguments.
+Importing the binding does not load the library; the first call does, and
+fails loudly if it has not been built.
+"""
+from .binding import (Plan, PackedLoRALinear, mlora_plan, mlora_forward, mlora_backward,  # noqa: F401
+                      pointer_table, device_check)
+from ._lib import MloraError, lib  # noqa: F401

@@ -1,0 +1,231 @@
+"""Python binding of the C interface: argument marshalling only.
+
+Names mirror include/mlora.h: ``mlora_plan`` builds a host plan,
+``mlora_forward`` / ``mlora_backward`` launch the HIP kernels on torch
+device tensors.  torch is used for device memory and the current stream;
+every step of the layer runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Sequence
+
+import numpy as np
+
+from . import _lib
+from ._lib import check, lib
+
+
+def _torch():
+    import torch  # imported first so libmlora binds to torch's HIP runtime
+    return torch
+
+
+class Plan:
+    """Host plan for one packed layer (seg_offsets, ranks, d_in, d_out)."""
+
+    def __init__(self, seg_offsets, ranks, d_in: int, d_out: int, dtype: str = "bf16",
+                 nano_rows: int = 0, n_streams: int = 0, chunk_min: int = 0, chunk_max: int = 0,
+                 chunk_per_rank: int = 0, w0_layout: str = "kn", gemm_rows: int = 0):
+        off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
+        rk = np.ascontiguousarray(np.asarray(ranks, dtype=np.int32))
+        n = int(rk.shape[0])
+        if off.shape != (n + 1,):
+            raise ValueError("seg_offsets must have len(ranks) + 1 entries")
+        opts = _lib.PlanOpts(nano_rows, gemm_rows, n_streams, chunk_min, chunk_max, chunk_per_rank,
+                             _lib.W0_LAYOUTS[w0_layout])
+        h = ctypes.c_void_p()
+        check(lib().mlora_plan(n, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                               rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in),
+                               int(d_out), _lib.DTYPES[dtype], ctypes.byref(opts), ctypes.byref(h)))
+        self._h = h
+        inf = _lib.PlanInfo()
+        check(lib().mlora_plan_get_info(h, ctypes.byref(inf)))
+        self.info = {k: getattr(inf, k) for k, _ in _lib.PlanInfo._fields_}
+        self.dtype = dtype
+        self.w0_layout = w0_layout
+        self.offsets = off
+        self.ranks = rk
+        self._ws_uploaded = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def export(self, name: str) -> np.ndarray:
+        tid = _lib.TABLES.index(name)
+        nbytes = ctypes.c_size_t(0)
+        check(lib().mlora_plan_export(self._h, tid, None, ctypes.byref(nbytes)))
+        dt = np.int64 if name in _lib.TABLE_I64 else np.int32
+        buf = np.zeros(nbytes.value // np.dtype(dt).itemsize, dtype=dt)
+        check(lib().mlora_plan_export(self._h, tid, buf.ctypes.data_as(ctypes.c_void_p),
+                                      ctypes.byref(nbytes)))
+        if name in _lib.TABLE_COLS:
+            buf = buf.reshape(-1, _lib.TABLE_COLS[name])
+        return buf
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib().mlora_plan_destroy(h)
+            self._h = ctypes.c_void_p()
+
+    # ---- device-side helpers (torch) ----
+    def alloc_workspace(self, device="cuda"):
+        torch = _torch()
+        return torch.empty(max(1, self.info["workspace_bytes"]), dtype=torch.uint8, device=device)
+
+    def alloc_z(self, device="cuda"):
+        torch = _torch()
+        dt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        return torch.empty(max(1, self.info["z_elems"]), dtype=dt, device=device)
+
+    def upload(self, ws, stream=None):
+        torch = _torch()
+        s = stream if stream is not None else torch.cuda.current_stream()
+        check(lib().mlora_plan_upload(self._h, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                      ctypes.c_void_p(s.cuda_stream)))
+        self._ws_uploaded = ws
+
+    def profile_enable(self, on: bool = True):
+        check(lib().mlora_profile_enable(self._h, 1 if on else 0))
+
+    def profile_read(self) -> dict:
+        n = len(_lib.KERNELS)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        check(lib().mlora_profile_read(self._h, ms, cnt))
+        return {k: (ms[i], cnt[i]) for i, k in enumerate(_lib.KERNELS)}
+
+
+def mlora_plan(seg_offsets, ranks, d_in, d_out, dtype="bf16", **opts) -> Plan:
+    return Plan(seg_offsets, ranks, d_in, d_out, dtype, **opts)
+
+
+def pointer_table(tensors: Sequence, device="cuda"):
+    """Device int64 array of the data pointers of ``tensors``."""
+    torch = _torch()
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def _check_t(t, name, shape, dtype, numel_min=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel_min is not None and t.numel() < numel_min:
+        raise ValueError(f"{name} needs at least {numel_min} elements")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(plan):
+    torch = _torch()
+    return torch.bfloat16 if plan.dtype == "bf16" else torch.float32
+
+
+def _w0_shape(plan):
+    i = plan.info
+    return (i["d_in"], i["d_out"]) if plan.w0_layout == "kn" else (i["d_out"], i["d_in"])
+
+
+def mlora_forward(plan: Plan, X, W0, A_ptrs, B_ptrs, scales, Y, Z, ws, stream=None):
+    """Y = X W0 + s_i (X A_i) B_i per segment; Z <- s_i X A_i (plan layout)."""
+    torch = _torch()
+    i = plan.info
+    dt = _dt(plan)
+    _check_t(X, "X", (i["T"], i["d_in"]), dt)
+    _check_t(W0, "W0", _w0_shape(plan), dt)
+    _check_t(Y, "Y", (i["T"], i["d_out"]), dt)
+    _check_t(Z, "Z", None, dt, i["z_elems"])
+    for nm, t in (("A_ptrs", A_ptrs), ("B_ptrs", B_ptrs)):
+        _check_t(t, nm, (i["n"],), torch.int64)
+    _check_t(scales, "scales", (i["n"],), torch.float32)
+    check(lib().mlora_forward(plan.handle, _p(X), _p(W0), _p(A_ptrs), _p(B_ptrs), _p(scales),
+                              _p(Y), _p(Z), _p(ws), ws.numel(), _stream(stream)))
+    return Y, Z
+
+
+def mlora_backward(plan: Plan, dY, X, W0, A_ptrs, B_ptrs, scales, Z, dX, dA_ptrs, dB_ptrs, ws,
+                   stream=None):
+    """dX (optional) and fp32 dA_i, dB_i through the pointer tables."""
+    torch = _torch()
+    i = plan.info
+    dt = _dt(plan)
+    _check_t(dY, "dY", (i["T"], i["d_out"]), dt)
+    _check_t(X, "X", (i["T"], i["d_in"]), dt)
+    _check_t(W0, "W0", _w0_shape(plan), dt)
+    _check_t(Z, "Z", None, dt, i["z_elems"])
+    if dX is not None:
+        _check_t(dX, "dX", (i["T"], i["d_in"]), dt)
+    for nm, t in (("A_ptrs", A_ptrs), ("B_ptrs", B_ptrs), ("dA_ptrs", dA_ptrs), ("dB_ptrs", dB_ptrs)):
+        _check_t(t, nm, (i["n"],), torch.int64)
+    _check_t(scales, "scales", (i["n"],), torch.float32)
+    check(lib().mlora_backward(plan.handle, _p(dY), _p(X), _p(W0), _p(A_ptrs), _p(B_ptrs),
+                               _p(scales), _p(Z), _p(dX), _p(dA_ptrs), _p(dB_ptrs), _p(ws),
+                               ws.numel(), _stream(stream)))
+    return dX
+
+
+def device_check() -> None:
+    check(lib().mlora_device_check())
+
+
+class PackedLoRALinear:
+    """One packed layer with its adapters, buffers and pointer tables.
+
+    Holds device tensors A_i, B_i (parameters), dA_i, dB_i (fp32 gradients),
+    the saved activation Z and the workspace; ``forward``/``backward`` call the
+    library.  Pointer tables are uploaded once at construction.
+    """
+
+    def __init__(self, plan: Plan, W0, A: Sequence, B: Sequence, scales, device="cuda"):
+        torch = _torch()
+        self.plan = plan
+        self.W0 = W0
+        self.A = list(A)
+        self.B = list(B)
+        n = plan.info["n"]
+        self.scales = torch.as_tensor(np.asarray(scales, dtype=np.float32), device=device)
+        self.dA = [torch.empty((plan.info["d_in"], int(r)), dtype=torch.float32, device=device)
+                   for r in plan.ranks]
+        self.dB = [torch.empty((int(r), plan.info["d_out"]), dtype=torch.float32, device=device)
+                   for r in plan.ranks]
+        assert len(self.A) == n and len(self.B) == n
+        self.A_ptrs = pointer_table(self.A, device)
+        self.B_ptrs = pointer_table(self.B, device)
+        self.dA_ptrs = pointer_table(self.dA, device)
+        self.dB_ptrs = pointer_table(self.dB, device)
+        self.ws = plan.alloc_workspace(device)
+        self.Z = plan.alloc_z(device)
+        plan.upload(self.ws)
+
+    def forward(self, X, Y=None, stream=None):
+        torch = _torch()
+        if Y is None:
+            Y = torch.empty((self.plan.info["T"], self.plan.info["d_out"]), dtype=X.dtype, device=X.device)
+        mlora_forward(self.plan, X, self.W0, self.A_ptrs, self.B_ptrs, self.scales, Y, self.Z,
+                      self.ws, stream)
+        return Y
+
+    def backward(self, dY, X, dX=None, want_dx=True, stream=None):
+        torch = _torch()
+        if want_dx and dX is None:
+            dX = torch.empty((self.plan.info["T"], self.plan.info["d_in"]), dtype=X.dtype, device=X.device)
+        mlora_backward(self.plan, dY, X, self.W0, self.A_ptrs, self.B_ptrs, self.scales, self.Z,
+                       dX if want_dx else None, self.dA_ptrs, self.dB_ptrs, self.ws, stream)
+        return dX

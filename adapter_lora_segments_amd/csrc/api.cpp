@@ -1,0 +1,522 @@
+// C interface (include/mlora.h): argument checks, the plan object, launch
+// orchestration over adapter groups and streams, and per-kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/mlora.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+mlora_status fail(mlora_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+struct Range {
+  int32_t begin, count, rp;
+};
+
+}  // namespace
+
+struct mlora_plan_s {
+  mlora::PlanTables P;
+  mlora::DeviceLayout L;
+  std::vector<uint8_t> blob;
+  void* uploaded_ws = nullptr;
+  std::vector<std::vector<Range>> nano_b, chunk_b;  // per group: one range per padded rank
+  std::vector<int32_t> group_max_rank;
+  int32_t max_rank = 1;
+  // internal streams (n_groups > 1) and fork/join events
+  std::vector<hipStream_t> streams;
+  std::vector<hipEvent_t> join_ev;
+  hipEvent_t fork_ev = nullptr;
+  // profiling
+  bool prof = false;
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+};
+
+namespace {
+
+std::vector<Range> bucket_ranges(const std::vector<int32_t>& items, int stride, int32_t begin,
+                                 int32_t end, const std::vector<int32_t>& rpad) {
+  std::vector<Range> out;
+  for (int32_t i = begin; i < end; ++i) {
+    const int32_t rp = rpad[items[(size_t)stride * i]];
+    if (out.empty() || out.back().rp != rp) out.push_back({i, 0, rp});
+    out.back().count++;
+  }
+  return out;
+}
+
+mlora::DevTables dev_tables(const mlora_plan_s* p, void* ws) {
+  const uint8_t* b = static_cast<const uint8_t*>(ws);
+  const auto& L = p->L;
+  mlora::DevTables t;
+  t.offsets = reinterpret_cast<const int64_t*>(b + L.offsets);
+  t.zoff = reinterpret_cast<const int64_t*>(b + L.zoff);
+  t.ranks = reinterpret_cast<const int32_t*>(b + L.ranks);
+  t.rpad = reinterpret_cast<const int32_t*>(b + L.rpad);
+  t.roff = reinterpret_cast<const int32_t*>(b + L.roff);
+  t.ch_first = reinterpret_cast<const int32_t*>(b + L.ch_first);
+  t.ch_count = reinterpret_cast<const int32_t*>(b + L.ch_count);
+  t.nano = reinterpret_cast<const int32_t*>(b + L.nano);
+  t.chunks = reinterpret_cast<const int32_t*>(b + L.chunks);
+  t.cpref = reinterpret_cast<const int32_t*>(b + L.cpref);
+  t.tiles = reinterpret_cast<const int32_t*>(b + L.tiles);
+  t.ext_start = reinterpret_cast<const int32_t*>(b + L.ext_start);
+  t.ext = reinterpret_cast<const int32_t*>(b + L.ext);
+  return t;
+}
+
+mlora_status hip_fail(hipError_t e, const char* what) {
+  return fail(MLORA_ERR_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                                 hipGetErrorString(e) + ")");
+}
+
+// Brackets one launch with events when profiling is on.
+template <class F>
+mlora_status timed(mlora_plan_s* p, int kind, hipStream_t s, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (p->prof) {
+    for (hipEvent_t* e : {&a, &b}) {
+      if (!p->pool.empty()) {
+        *e = p->pool.back();
+        p->pool.pop_back();
+      } else {
+        hipError_t err = hipEventCreate(e);
+        if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+      }
+    }
+    hipError_t err = hipEventRecord(a, s);
+    if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+  }
+  launch();
+  hipError_t err = hipGetLastError();
+  if (p->prof) {
+    hipError_t e2 = hipEventRecord(b, s);
+    p->recs.push_back({kind, a, b});
+    if (err == hipSuccess && e2 != hipSuccess) return hip_fail(e2, "hipEventRecord");
+  }
+  if (err != hipSuccess) return hip_fail(err, "kernel launch");
+  return MLORA_OK;
+}
+
+mlora_status ensure_streams(mlora_plan_s* p) {
+  const int S = p->P.n_groups;
+  if (S <= 1 || (int)p->streams.size() == S) return MLORA_OK;
+  for (int g = (int)p->streams.size(); g < S; ++g) {
+    hipStream_t s;
+    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+    p->streams.push_back(s);
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    p->join_ev.push_back(ev);
+  }
+  if (!p->fork_ev) {
+    hipError_t e = hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  }
+  return MLORA_OK;
+}
+
+mlora_status fork_groups(mlora_plan_s* p, hipStream_t cs) {
+  if (p->P.n_groups <= 1) return MLORA_OK;
+  mlora_status st = ensure_streams(p);
+  if (st != MLORA_OK) return st;
+  hipError_t e = hipEventRecord(p->fork_ev, cs);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  for (hipStream_t s : p->streams) {
+    e = hipStreamWaitEvent(s, p->fork_ev, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  return MLORA_OK;
+}
+
+mlora_status join_groups(mlora_plan_s* p, hipStream_t cs) {
+  if (p->P.n_groups <= 1) return MLORA_OK;
+  for (size_t g = 0; g < p->streams.size(); ++g) {
+    hipError_t e = hipEventRecord(p->join_ev[g], p->streams[g]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    e = hipStreamWaitEvent(cs, p->join_ev[g], 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  return MLORA_OK;
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+mlora_status check_ws(const mlora_plan_s* p, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(MLORA_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < p->L.workspace_bytes)
+    return fail(MLORA_ERR_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, plan needs " +
+                                         std::to_string(p->L.workspace_bytes));
+  if (ws != p->uploaded_ws)
+    return fail(MLORA_ERR_WORKSPACE, "plan tables were not uploaded to this workspace (mlora_plan_upload)");
+  return MLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mlora_version(void) { return "mlora 0.1 gfx950"; }
+
+const char* mlora_status_string(mlora_status s) {
+  switch (s) {
+    case MLORA_OK: return "MLORA_OK";
+    case MLORA_ERR_INVALID_ARG: return "MLORA_ERR_INVALID_ARG";
+    case MLORA_ERR_UNSUPPORTED: return "MLORA_ERR_UNSUPPORTED";
+    case MLORA_ERR_HIP: return "MLORA_ERR_HIP";
+    case MLORA_ERR_WORKSPACE: return "MLORA_ERR_WORKSPACE";
+    case MLORA_ERR_NOMEM: return "MLORA_ERR_NOMEM";
+  }
+  return "MLORA_ERR_UNKNOWN";
+}
+
+const char* mlora_last_error(void) { return g_err.c_str(); }
+
+mlora_status mlora_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ranks, int64_t d_in,
+                        int64_t d_out, mlora_dtype dtype, const mlora_plan_opts* opts,
+                        mlora_plan_t* out) {
+  if (!out) return fail(MLORA_ERR_INVALID_ARG, "out is NULL");
+  try {
+    mlora::PlanTables P;
+    std::string err;
+    mlora_status st = mlora::build_plan(n, seg_offsets, ranks, d_in, d_out, (int32_t)dtype, opts, P, err);
+    if (st != MLORA_OK) return fail(st, err);
+    auto* p = new mlora_plan_s();
+    p->P = std::move(P);
+    p->L = mlora::device_layout(p->P);
+    p->blob = mlora::table_blob(p->P, p->L);
+    const int S = p->P.n_groups;
+    p->nano_b.resize(S);
+    p->chunk_b.resize(S);
+    p->group_max_rank.assign(S, 1);
+    for (int g = 0; g < S; ++g) {
+      p->nano_b[g] = bucket_ranges(p->P.nano, 3, p->P.nano_start[g], p->P.nano_start[g + 1], p->P.rpad);
+      p->chunk_b[g] = bucket_ranges(p->P.chunks, 3, p->P.chunk_start[g], p->P.chunk_start[g + 1], p->P.rpad);
+      for (int32_t j = p->P.groups[g]; j < p->P.groups[g + 1]; ++j)
+        p->group_max_rank[g] = std::max(p->group_max_rank[g], p->P.ranks[j]);
+      p->max_rank = std::max(p->max_rank, p->group_max_rank[g]);
+    }
+    *out = p;
+    return MLORA_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(MLORA_ERR_NOMEM, "host allocation failed while building the plan");
+  }
+}
+
+void mlora_plan_destroy(mlora_plan_t p) {
+  if (!p) return;
+  // Teardown is best effort: errors here have no caller to report to.
+  for (hipStream_t s : p->streams) (void)hipStreamDestroy(s);
+  for (hipEvent_t e : p->join_ev) (void)hipEventDestroy(e);
+  if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
+  for (auto& r : p->recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (hipEvent_t e : p->pool) (void)hipEventDestroy(e);
+  delete p;
+}
+
+mlora_status mlora_plan_get_info(mlora_plan_t p, mlora_plan_info* info) {
+  if (!p || !info) return fail(MLORA_ERR_INVALID_ARG, "plan and info must be non-NULL");
+  const auto& P = p->P;
+  mlora_plan_info i{};
+  i.T = P.T;
+  i.n = P.n;
+  i.d_in = P.d_in;
+  i.d_out = P.d_out;
+  i.dtype = P.dtype;
+  i.n_groups = P.n_groups;
+  i.z_elems = P.z_elems;
+  i.z_bytes = P.z_elems * (P.dtype == MLORA_BF16 ? 2 : 4);
+  i.workspace_bytes = (int64_t)p->L.workspace_bytes;
+  i.table_bytes = (int64_t)p->L.table_bytes;
+  i.rpad_total = P.rpad_total;
+  i.partial_rows = P.partial_rows;
+  i.n_nano = P.n_nano();
+  i.n_chunks = P.n_chunks();
+  i.n_tiles = P.n_tiles();
+  i.n_ext = P.n_ext();
+  *info = i;
+  return MLORA_OK;
+}
+
+mlora_status mlora_plan_export(mlora_plan_t p, int32_t table, void* dst, size_t* bytes_inout) {
+  if (!p || !bytes_inout) return fail(MLORA_ERR_INVALID_ARG, "plan and bytes_inout must be non-NULL");
+  const auto& P = p->P;
+  const void* src = nullptr;
+  size_t bytes = 0;
+  auto v32 = [&](const std::vector<int32_t>& v) { src = v.data(); bytes = 4 * v.size(); };
+  auto v64 = [&](const std::vector<int64_t>& v) { src = v.data(); bytes = 8 * v.size(); };
+  switch (table) {
+    case MLORA_TAB_RPAD: v32(P.rpad); break;
+    case MLORA_TAB_ZOFF: v64(P.zoff); break;
+    case MLORA_TAB_ROFF: v32(P.roff); break;
+    case MLORA_TAB_GROUPS: v32(P.groups); break;
+    case MLORA_TAB_NANO: v32(P.nano); break;
+    case MLORA_TAB_NANO_START: v32(P.nano_start); break;
+    case MLORA_TAB_CHUNKS: v32(P.chunks); break;
+    case MLORA_TAB_CHUNK_START: v32(P.chunk_start); break;
+    case MLORA_TAB_CHUNK_RPREF: v32(P.cpref); break;
+    case MLORA_TAB_ADAPTER_CHUNK_FIRST: v32(P.ch_first); break;
+    case MLORA_TAB_ADAPTER_CHUNK_COUNT: v32(P.ch_count); break;
+    case MLORA_TAB_TILES: v32(P.tiles); break;
+    case MLORA_TAB_TILE_START: v32(P.tile_start); break;
+    case MLORA_TAB_EXT: v32(P.ext); break;
+    case MLORA_TAB_TILE_EXT_START: v32(P.ext_start); break;
+    case MLORA_TAB_OFFSETS: v64(P.offsets); break;
+    case MLORA_TAB_RANKS: v32(P.ranks); break;
+    default: return fail(MLORA_ERR_INVALID_ARG, "unknown table id " + std::to_string(table));
+  }
+  if (!dst) {
+    *bytes_inout = bytes;
+    return MLORA_OK;
+  }
+  if (*bytes_inout < bytes) {
+    *bytes_inout = bytes;
+    return fail(MLORA_ERR_INVALID_ARG, "destination too small for table");
+  }
+  if (bytes) std::memcpy(dst, src, bytes);
+  *bytes_inout = bytes;
+  return MLORA_OK;
+}
+
+mlora_status mlora_plan_upload(mlora_plan_t p, void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
+  if (!ws) return fail(MLORA_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(ws)) return fail(MLORA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (ws_bytes < p->L.workspace_bytes)
+    return fail(MLORA_ERR_WORKSPACE, "workspace has " + std::to_string(ws_bytes) + " bytes, plan needs " +
+                                         std::to_string(p->L.workspace_bytes));
+  hipError_t e = hipMemcpyAsync(ws, p->blob.data(), p->blob.size(), hipMemcpyHostToDevice,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan tables)");
+  p->uploaded_ws = ws;
+  return MLORA_OK;
+}
+
+mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const void* const* A,
+                           const void* const* B, const float* scales, void* Y, void* Z, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
+  // With no rows at all, the row-indexed buffers may be NULL.
+  const bool rows = p->P.T > 0;
+  if ((rows && (!X || !Y || !Z)) || !W0 || !A || !B || !scales)
+    return fail(MLORA_ERR_INVALID_ARG, "forward: X, W0, A, B, scales, Y and Z must be non-NULL");
+  for (const void* q : {X, W0, (const void*)A, (const void*)B, (const void*)scales, (const void*)Y, (const void*)Z})
+    if (!aligned16(q)) return fail(MLORA_ERR_INVALID_ARG, "forward: device pointers must be 16-byte aligned");
+  mlora_status st = check_ws(p, ws, ws_bytes);
+  if (st != MLORA_OK) return st;
+  const auto& P = p->P;
+  const auto& L = p->L;
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  mlora::DevTables t = dev_tables(p, ws);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const bool nk = P.opts.w0_layout == MLORA_W0_NK;
+
+  if (P.dtype == MLORA_FP32) {
+    st = timed(p, MLORA_K_SHRINK, cs, [&] {
+      mlora::launch_f32_shrink(t, P.n, P.T, P.d_in, (const float*)X, A, scales, (float*)Z, cs);
+    });
+    if (st != MLORA_OK) return st;
+    return timed(p, MLORA_K_GEMM_FWD, cs, [&] {
+      mlora::launch_f32_gemm(true, nk, t, P.n, P.T, (const float*)X, P.d_in, (const float*)W0,
+                             nk ? P.d_in : P.d_out, (float*)Y, P.d_out, (int32_t)P.d_in,
+                             (int32_t)P.d_out, (const float*)Z, B, cs);
+    });
+  }
+
+  uint16_t* acat_t = reinterpret_cast<uint16_t*>(wsb + L.acat_t);
+  st = timed(p, MLORA_K_PREP, cs, [&] { mlora::launch_prep_acat_t(t, P.n, P.d_in, A, acat_t, cs); });
+  if (st != MLORA_OK) return st;
+  st = fork_groups(p, cs);
+  if (st != MLORA_OK) return st;
+  for (int g = 0; g < P.n_groups; ++g) {
+    hipStream_t s = P.n_groups > 1 ? p->streams[g] : cs;
+    for (const Range& r : p->nano_b[g]) {
+      st = timed(p, MLORA_K_SHRINK, s, [&] {
+        mlora::launch_skinny(0 | (r.rp << 8), t, r.begin, r.count, (const uint16_t*)X, P.d_in,
+                             acat_t, nullptr, scales, (uint16_t*)Z, s);
+      });
+      if (st != MLORA_OK) return st;
+    }
+    mlora::GemmArgs ga;
+    ga.A = (const uint16_t*)X;
+    ga.lda = P.d_in;
+    ga.B = (const uint16_t*)W0;
+    ga.ldb = nk ? P.d_in : P.d_out;
+    ga.C = (uint16_t*)Y;
+    ga.ldc = P.d_out;
+    ga.K = (int32_t)P.d_in;
+    ga.N = (int32_t)P.d_out;
+    ga.tile_begin = P.tile_start[g];
+    ga.n_mtiles = P.tile_start[g + 1] - P.tile_start[g];
+    ga.n_ntiles = (int32_t)((P.d_out + 255) / 256);
+    ga.ebuf = (const uint16_t*)Z;
+    ga.eb = B;
+    ga.t = t;
+    st = timed(p, MLORA_K_GEMM_FWD, s, [&] { mlora::launch_gemm(true, nk, ga, s); });
+    if (st != MLORA_OK) return st;
+  }
+  return join_groups(p, cs);
+}
+
+mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const void* W0,
+                            const void* const* A, const void* const* B, const float* scales,
+                            const void* Z, void* dX, void* const* dA, void* const* dB, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
+  const bool rows = p->P.T > 0;
+  if ((rows && (!dY || !X || !Z)) || !W0 || !A || !B || !scales || !dA || !dB)
+    return fail(MLORA_ERR_INVALID_ARG,
+                "backward: dY, X, W0, A, B, scales, Z, dA and dB must be non-NULL (dX may be NULL)");
+  for (const void* q : {dY, X, W0, (const void*)A, (const void*)B, (const void*)scales, Z,
+                        (const void*)dA, (const void*)dB})
+    if (!aligned16(q)) return fail(MLORA_ERR_INVALID_ARG, "backward: device pointers must be 16-byte aligned");
+  if (dX && !aligned16(dX)) return fail(MLORA_ERR_INVALID_ARG, "backward: dX must be 16-byte aligned");
+  mlora_status st = check_ws(p, ws, ws_bytes);
+  if (st != MLORA_OK) return st;
+  const auto& P = p->P;
+  const auto& L = p->L;
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  mlora::DevTables t = dev_tables(p, ws);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const bool nk = P.opts.w0_layout == MLORA_W0_NK;
+
+  if (P.dtype == MLORA_FP32) {
+    float* dZ = reinterpret_cast<float*>(wsb + L.dz);
+    st = timed(p, MLORA_K_DZ, cs, [&] {
+      mlora::launch_f32_dz(t, P.n, P.T, P.d_out, (const float*)dY, B, scales, dZ, cs);
+    });
+    if (st != MLORA_OK) return st;
+    st = timed(p, MLORA_K_DB, cs, [&] {
+      mlora::launch_f32_db(t, P.n, P.d_out, (const float*)Z, (const float*)dY, dB, p->max_rank, cs);
+    });
+    if (st != MLORA_OK) return st;
+    st = timed(p, MLORA_K_DA, cs, [&] {
+      mlora::launch_f32_da(t, P.n, P.d_in, (const float*)X, dZ, dA, p->max_rank, cs);
+    });
+    if (st != MLORA_OK) return st;
+    if (!dX) return MLORA_OK;
+    return timed(p, MLORA_K_GEMM_DX, cs, [&] {
+      mlora::launch_f32_gemm(false, !nk, t, P.n, P.T, (const float*)dY, P.d_out, (const float*)W0,
+                             nk ? P.d_in : P.d_out, (float*)dX, P.d_in, (int32_t)P.d_out,
+                             (int32_t)P.d_in, dZ, A, cs);
+    });
+  }
+
+  uint16_t* dZ = reinterpret_cast<uint16_t*>(wsb + L.dz);
+  float* partA = reinterpret_cast<float*>(wsb + L.part_a);
+  float* partB = reinterpret_cast<float*>(wsb + L.part_b);
+  st = fork_groups(p, cs);
+  if (st != MLORA_OK) return st;
+  for (int g = 0; g < P.n_groups; ++g) {
+    hipStream_t s = P.n_groups > 1 ? p->streams[g] : cs;
+    for (const Range& r : p->nano_b[g]) {
+      st = timed(p, MLORA_K_DZ, s, [&] {
+        mlora::launch_skinny(1 | (r.rp << 8), t, r.begin, r.count, (const uint16_t*)dY, P.d_out,
+                             nullptr, B, scales, dZ, s);
+      });
+      if (st != MLORA_OK) return st;
+    }
+    for (const Range& r : p->chunk_b[g]) {
+      st = timed(p, MLORA_K_DB, s, [&] {
+        mlora::launch_token_reduce(0 | (r.rp << 8), t, r.begin, r.count, (const uint16_t*)dY,
+                                   P.d_out, (const uint16_t*)Z, partB, s);
+      });
+      if (st != MLORA_OK) return st;
+    }
+    for (const Range& r : p->chunk_b[g]) {
+      st = timed(p, MLORA_K_DA, s, [&] {
+        mlora::launch_token_reduce(1 | (r.rp << 8), t, r.begin, r.count, (const uint16_t*)X,
+                                   P.d_in, dZ, partA, s);
+      });
+      if (st != MLORA_OK) return st;
+    }
+    st = timed(p, MLORA_K_REDUCE, s, [&] {
+      mlora::launch_reduce_partials(t, P.groups[g], P.groups[g + 1], P.d_in, P.d_out, partA,
+                                    partB, dA, dB, p->group_max_rank[g], s);
+    });
+    if (st != MLORA_OK) return st;
+    if (dX) {
+      mlora::GemmArgs ga;
+      ga.A = (const uint16_t*)dY;
+      ga.lda = P.d_out;
+      ga.B = (const uint16_t*)W0;
+      ga.ldb = nk ? P.d_in : P.d_out;
+      ga.C = (uint16_t*)dX;
+      ga.ldc = P.d_in;
+      ga.K = (int32_t)P.d_out;
+      ga.N = (int32_t)P.d_in;
+      ga.tile_begin = P.tile_start[g];
+      ga.n_mtiles = P.tile_start[g + 1] - P.tile_start[g];
+      ga.n_ntiles = (int32_t)((P.d_in + 255) / 256);
+      ga.ebuf = dZ;
+      ga.eb = A;
+      ga.t = t;
+      st = timed(p, MLORA_K_GEMM_DX, s, [&] { mlora::launch_gemm(false, !nk, ga, s); });
+      if (st != MLORA_OK) return st;
+    }
+  }
+  return join_groups(p, cs);
+}
+
+mlora_status mlora_profile_enable(mlora_plan_t p, int32_t on) {
+  if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
+  p->prof = on != 0;
+  return MLORA_OK;
+}
+
+mlora_status mlora_profile_read(mlora_plan_t p, double* total_ms, int64_t* launches) {
+  if (!p || !total_ms || !launches) return fail(MLORA_ERR_INVALID_ARG, "NULL argument");
+  for (int k = 0; k < MLORA_K_COUNT; ++k) {
+    total_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  mlora_status st = MLORA_OK;
+  for (auto& r : p->recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess && st == MLORA_OK) st = hip_fail(e, "profile event");
+    total_ms[r.kind] += ms;
+    launches[r.kind] += 1;
+    p->pool.push_back(r.a);
+    p->pool.push_back(r.b);
+  }
+  p->recs.clear();
+  return st;
+}
+
+mlora_status mlora_device_check(void) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MLORA_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", library is built for gfx950");
+  return MLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Device helpers shared by the gfx950 kernels: bf16 bit handling, the
+// MFMA wrappers, and the swizzled LDS tile layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlora {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// D[i][j] += sum_k a[i][k] b[k][j] on a 32x32x16 bf16 tile.  Lane l supplies
+// row/column l%32 and eight consecutive k values starting at 8*(l/32); the
+// accumulator holds D[8g + 4(l/32) + e][l%32] in element 4g+e.
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// LDS tile: rows of 64 bf16 (eight 16-byte chunks).  Chunk c of row r lives
+// at chunk position c ^ ((r ^ (r >> 3)) & 7): eight consecutive rows read at
+// one chunk, and eight rows 8 apart written at one chunk, both land in eight
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 8 + (chunk ^ ((row ^ (row >> 3)) & 7));
+}
+
+// Transpose an 8x8 block of 16-bit values.  in[i] holds row i (8 values,
+// value j in half j&1 of word j>>1); out[j] receives column j.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {     // word p of the input rows: columns 2p, 2p+1
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {   // word q of the output: rows 2q, 2q+1
+      const uint32_t lo = in[2 * q][p], hi = in[2 * q + 1][p];
+      out[2 * p][q] = (lo & 0xffffu) | (hi << 16);
+      out[2 * p + 1][q] = (lo >> 16) | (hi & 0xffff0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+}  // namespace mlora

@@ -1,0 +1,88 @@
+// Launch interface of the device kernels (host side).  Every launcher checks
+// nothing itself: the C interface validates shapes and sizes before calling.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlora {
+
+// Device copies of the plan tables (pointers into the workspace).
+struct DevTables {
+  const int64_t* offsets;   // [n+1]
+  const int64_t* zoff;      // [n]
+  const int32_t* ranks;     // [n]
+  const int32_t* rpad;      // [n]
+  const int32_t* roff;      // [n]
+  const int32_t* ch_first;  // [n]
+  const int32_t* ch_count;  // [n]
+  const int32_t* nano;      // [n_nano][3]
+  const int32_t* chunks;    // [n_chunks][3]
+  const int32_t* cpref;     // [n_chunks]
+  const int32_t* tiles;     // [n_tiles][2]
+  const int32_t* ext_start; // [n_tiles+1]
+  const int32_t* ext;       // [n_ext][4]
+};
+
+// ---------------- bf16 path (MFMA) ----------------
+
+// A_cat^T [rpad_total][d_in]: row roff(j)+c holds column c of A_j (zero for c >= r_j).
+void launch_prep_acat_t(const DevTables& t, int32_t n, int64_t d_in, const void* const* A,
+                        uint16_t* acat_t, hipStream_t s);
+
+// Skinny products over nano-batches: out rows of adapter j (r_pad(j) columns)
+//   mode 0 (shrink): Z'[t][c] = s_j sum_k X[t][k] A_cat^T[roff_j + c][k]
+//   mode 1 (dZ)    : dZ[t][c] = s_j sum_k dY[t][k] B_j[c][k]
+void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nano_count,
+                   const uint16_t* P, int64_t K, const uint16_t* acat_t, const void* const* Bptr,
+                   const float* scales, uint16_t* out, hipStream_t s);
+
+// Token reductions over chunks, partial sums in fp32:
+//   mode 0 (dB): partB[cpref][c][n] = sum_t Z'[t][c] dY[t][n]       (n < d_out)
+//   mode 1 (dA): partA[cpref][d][c] = sum_t X[t][d] dZ[t][c]        (d < d_in)
+void launch_token_reduce(int mode, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
+                         const uint16_t* big, int64_t big_ld, const uint16_t* rk, float* part,
+                         hipStream_t s);
+
+// Fixed-order sum of the chunk partials into the caller's dA_j / dB_j
+// (adapters [a_begin, a_end)); adapters without rows get zeros.
+void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, int64_t d_in,
+                            int64_t d_out, const float* partA, const float* partB,
+                            void* const* dA, void* const* dB, int32_t max_rank, hipStream_t s);
+
+// C[row][n] = sum_k Aop[row][k] Bop[k][n] over K, then the extension steps of
+// each row tile: rows of adapter j times E_j (Z' or dZ) against EB_j.
+//   fwd: Aop = X, Bop = W0, E = Z', EB_j = B_j ([r_j][N], n contiguous)
+//   dx : Aop = dY, Bop = W0^T, E = dZ, EB_j = A_j^T (A_j is [N][r_j])
+struct GemmArgs {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  uint16_t* C;
+  int64_t ldc;
+  int32_t K, N;
+  int32_t tile_begin, n_mtiles, n_ntiles;
+  const uint16_t* ebuf;
+  const void* const* eb;
+  DevTables t;
+};
+// main_b_kcontig: Bop element (k, n) at B[n*ldb + k] (else at B[k*ldb + n]).
+void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s);
+
+// ---------------- fp32 path (vector ALU) ----------------
+void launch_f32_shrink(const DevTables& t, int32_t n, int64_t T, int64_t d_in, const float* X,
+                       const void* const* A, const float* scales, float* Z, hipStream_t s);
+void launch_f32_dz(const DevTables& t, int32_t n, int64_t T, int64_t d_out, const float* dY,
+                   const void* const* B, const float* scales, float* dZ, hipStream_t s);
+// fwd: Y = X W0 + Z' B; dx: dX = dY W0^T + dZ A^T.
+void launch_f32_gemm(bool fwd, bool main_b_kcontig, const DevTables& t, int32_t n, int64_t T,
+                     const float* A, int64_t lda, const float* B, int64_t ldb, float* C,
+                     int64_t ldc, int32_t K, int32_t N, const float* E, const void* const* eb,
+                     hipStream_t s);
+void launch_f32_db(const DevTables& t, int32_t n, int64_t d_out, const float* Z, const float* dY,
+                   void* const* dB, int32_t max_rank, hipStream_t s);
+void launch_f32_da(const DevTables& t, int32_t n, int64_t d_in, const float* X, const float* dZ,
+                   void* const* dA, int32_t max_rank, hipStream_t s);
+
+}  // namespace mlora

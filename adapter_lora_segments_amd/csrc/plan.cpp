@@ -1,0 +1,285 @@
+// Host plan builder.  The rule is stated in include/mlora.h (mlora_plan); it
+// is this library's own: the tLoRA page (tLoRA: Efficient Multi-LoRA Training
+// with Elastic Shared Super-Models, abstract) asks for rank-aware nano-batches
+// and per-rank low-rank tiles without fixing them, and the PLoRA page (§9.2)
+// asks that work be tiled along tokens and hidden dimensions, never the rank.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstring>
+
+namespace mlora {
+
+namespace {
+
+int32_t pad_rank(int32_t r) {
+  int32_t p = 1;
+  while (p < r) p <<= 1;
+  return std::max(p, kMinRankPad);
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ranks, int64_t d_in,
+                        int64_t d_out, int32_t dtype, const mlora_plan_opts* opts, PlanTables& P,
+                        std::string& err) {
+  if (!seg_offsets || !ranks) {
+    err = "seg_offsets and ranks must be non-NULL";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (n < 1 || n > MLORA_MAX_ADAPTERS) {
+    err = "n must be in [1, " + std::to_string(MLORA_MAX_ADAPTERS) + "], got " + std::to_string(n);
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (dtype != MLORA_FP32 && dtype != MLORA_BF16) {
+    err = "unknown dtype " + std::to_string(dtype);
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (d_in <= 0 || d_out <= 0) {
+    err = "d_in and d_out must be positive";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (d_in % 64 != 0 || d_out % 64 != 0 || d_in > (1 << 20) || d_out > (1 << 20)) {
+    err = "d_in and d_out must be multiples of 64 and at most 2^20 (got " + std::to_string(d_in) +
+          ", " + std::to_string(d_out) + ")";
+    return MLORA_ERR_UNSUPPORTED;
+  }
+  if (seg_offsets[0] != 0) {
+    err = "seg_offsets[0] must be 0";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (seg_offsets[i + 1] < seg_offsets[i]) {
+      err = "seg_offsets must be non-decreasing (index " + std::to_string(i + 1) + ")";
+      return MLORA_ERR_INVALID_ARG;
+    }
+  }
+  const int64_t T = seg_offsets[n];
+  if (T >= (int64_t(1) << 31) - 1) {
+    err = "total rows must be below 2^31 - 1";
+    return MLORA_ERR_UNSUPPORTED;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (ranks[i] < 1) {
+      err = "rank of adapter " + std::to_string(i) + " must be >= 1";
+      return MLORA_ERR_INVALID_ARG;
+    }
+    if (ranks[i] > MLORA_MAX_RANK) {
+      err = "rank of adapter " + std::to_string(i) + " exceeds " + std::to_string(MLORA_MAX_RANK);
+      return MLORA_ERR_UNSUPPORTED;
+    }
+  }
+  Opts o;
+  if (opts) {
+    if (opts->nano_rows) o.nano_rows = opts->nano_rows;
+    if (opts->gemm_rows) o.gemm_rows = opts->gemm_rows;
+    if (opts->n_streams) o.n_streams = opts->n_streams;
+    if (opts->chunk_min) o.chunk_min = opts->chunk_min;
+    if (opts->chunk_max) o.chunk_max = opts->chunk_max;
+    if (opts->chunk_per_rank) o.chunk_per_rank = opts->chunk_per_rank;
+    o.w0_layout = opts->w0_layout;
+  }
+  if (o.nano_rows < 16 || o.nano_rows > 256 || o.nano_rows % 16 != 0) {
+    err = "nano_rows must be a multiple of 16 in [16, 256]";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (o.gemm_rows < 32 || o.gemm_rows > 1024 || o.gemm_rows % 32 != 0) {
+    err = "gemm_rows must be a multiple of 32 in [32, 1024]";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (dtype == MLORA_BF16 && o.gemm_rows != 256) {
+    err = "bf16 plans use 256-row GEMM tiles (gemm_rows must be 0 or 256)";
+    return MLORA_ERR_UNSUPPORTED;
+  }
+  if (dtype == MLORA_BF16 && o.nano_rows % 32 != 0) {
+    err = "bf16 plans need nano_rows to be a multiple of 32";
+    return MLORA_ERR_UNSUPPORTED;
+  }
+  if (o.n_streams < 1 || o.n_streams > MLORA_MAX_STREAMS) {
+    err = "n_streams must be in [1, " + std::to_string(MLORA_MAX_STREAMS) + "]";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (o.chunk_min < 16 || o.chunk_max < o.chunk_min || o.chunk_max > (1 << 20) ||
+      o.chunk_per_rank < 0 || o.chunk_per_rank > 4096) {
+    err = "chunk_min/chunk_max/chunk_per_rank out of range";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (o.w0_layout != MLORA_W0_KN && o.w0_layout != MLORA_W0_NK) {
+    err = "w0_layout must be MLORA_W0_KN or MLORA_W0_NK";
+    return MLORA_ERR_INVALID_ARG;
+  }
+
+  PlanTables p;
+  p.n = n;
+  p.T = T;
+  p.d_in = d_in;
+  p.d_out = d_out;
+  p.dtype = dtype;
+  p.opts = o;
+  p.offsets.assign(seg_offsets, seg_offsets + n + 1);
+  p.ranks.assign(ranks, ranks + n);
+
+  // 1-2: padded ranks, Z' offsets, rank offsets
+  p.rpad.resize(n);
+  p.zoff.resize(n);
+  p.roff.resize(n);
+  int64_t z = 0, rr = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    p.rpad[i] = pad_rank(ranks[i]);
+    p.zoff[i] = z;
+    p.roff[i] = (int32_t)rr;
+    z += (seg_offsets[i + 1] - seg_offsets[i]) * p.rpad[i];
+    rr += p.rpad[i];
+  }
+  p.z_elems = z;
+  p.rpad_total = rr;
+
+  // 3: stream groups of consecutive adapters split near equal row counts
+  const int32_t S = std::min<int32_t>(o.n_streams, n);
+  p.n_groups = S;
+  p.groups.assign(S + 1, 0);
+  p.groups[S] = n;
+  for (int32_t s = 1; s < S; ++s) {
+    const int64_t target = (s * T + S - 1) / S;
+    int32_t a = n;
+    for (int32_t j = 0; j < n; ++j) {
+      if (seg_offsets[j] >= target) {
+        a = j;
+        break;
+      }
+    }
+    p.groups[s] = std::max(p.groups[s - 1], a);
+  }
+
+  // 4-6: bucket-ordered walk producing nano-batches and reduction chunks
+  p.ch_first.assign(n, 0);
+  p.ch_count.assign(n, 0);
+  int64_t cp = 0;
+  std::vector<int32_t> order;
+  for (int32_t s = 0; s < S; ++s) {
+    p.nano_start.push_back((int32_t)p.n_nano());
+    p.chunk_start.push_back((int32_t)p.n_chunks());
+    order.clear();
+    for (int32_t i = p.groups[s]; i < p.groups[s + 1]; ++i) order.push_back(i);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return p.rpad[a] > p.rpad[b]; });
+    for (int32_t i : order) {
+      const int64_t lo = seg_offsets[i], hi = seg_offsets[i + 1];
+      for (int64_t r0 = lo; r0 < hi; r0 += o.nano_rows) {
+        p.nano.push_back(i);
+        p.nano.push_back((int32_t)r0);
+        p.nano.push_back((int32_t)std::min<int64_t>(o.nano_rows, hi - r0));
+      }
+      const int64_t kc = std::min<int64_t>(
+          o.chunk_max, std::max<int64_t>(o.chunk_min, (int64_t)o.chunk_per_rank * p.rpad[i]));
+      p.ch_first[i] = (int32_t)p.n_chunks();
+      for (int64_t r0 = lo; r0 < hi; r0 += kc) {
+        p.chunks.push_back(i);
+        p.chunks.push_back((int32_t)r0);
+        p.chunks.push_back((int32_t)std::min<int64_t>(kc, hi - r0));
+        p.cpref.push_back((int32_t)cp);
+        cp += p.rpad[i];
+        p.ch_count[i] += 1;
+      }
+    }
+  }
+  p.nano_start.push_back((int32_t)p.n_nano());
+  p.chunk_start.push_back((int32_t)p.n_chunks());
+  p.partial_rows = cp;
+
+  // 7: GEMM row tiles per group with their extension steps
+  const int64_t BM = o.gemm_rows;
+  for (int32_t s = 0; s < S; ++s) {
+    p.tile_start.push_back((int32_t)p.n_tiles());
+    const int64_t R0 = seg_offsets[p.groups[s]], R1 = seg_offsets[p.groups[s + 1]];
+    int32_t first = p.groups[s];  // first adapter that can still meet a tile
+    for (int64_t t0 = R0; t0 < R1; t0 += BM) {
+      const int64_t rows = std::min<int64_t>(BM, R1 - t0);
+      p.ext_start.push_back((int32_t)p.n_ext());
+      while (first < p.groups[s + 1] && seg_offsets[first + 1] <= t0) ++first;
+      for (int32_t j = first; j < p.groups[s + 1] && seg_offsets[j] < t0 + rows; ++j) {
+        const int64_t lo = std::max<int64_t>(seg_offsets[j], t0);
+        const int64_t hi = std::min<int64_t>(seg_offsets[j + 1], t0 + rows);
+        if (lo >= hi) continue;
+        for (int32_t k0 = 0; k0 < p.rpad[j]; k0 += kKStep) {
+          p.ext.push_back(j);
+          p.ext.push_back((int32_t)lo);
+          p.ext.push_back((int32_t)hi);
+          p.ext.push_back(k0);
+        }
+      }
+      p.tiles.push_back((int32_t)t0);
+      p.tiles.push_back((int32_t)rows);
+    }
+  }
+  p.tile_start.push_back((int32_t)p.n_tiles());
+  p.ext_start.push_back((int32_t)p.n_ext());
+
+  P = std::move(p);
+  return MLORA_OK;
+}
+
+DeviceLayout device_layout(const PlanTables& p) {
+  DeviceLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + std::max<size_t>(bytes, 1), 256);
+    return at;
+  };
+  const size_t n = (size_t)p.n;
+  L.offsets = take(8 * (n + 1));
+  L.zoff = take(8 * n);
+  L.ranks = take(4 * n);
+  L.rpad = take(4 * n);
+  L.roff = take(4 * n);
+  L.ch_first = take(4 * n);
+  L.ch_count = take(4 * n);
+  L.nano = take(4 * p.nano.size());
+  L.chunks = take(4 * p.chunks.size());
+  L.cpref = take(4 * p.cpref.size());
+  L.tiles = take(4 * p.tiles.size());
+  L.ext_start = take(4 * p.ext_start.size());
+  L.ext = take(4 * p.ext.size());
+  L.table_bytes = off;
+  const size_t esz = p.dtype == MLORA_BF16 ? 2 : 4;
+  if (p.dtype == MLORA_BF16) {
+    L.acat_t = take((size_t)p.rpad_total * (size_t)p.d_in * esz);
+  } else {
+    L.acat_t = off;
+  }
+  L.dz = take((size_t)p.z_elems * esz);
+  if (p.dtype == MLORA_BF16) {
+    L.part_a = take((size_t)p.partial_rows * (size_t)p.d_in * 4);
+    L.part_b = take((size_t)p.partial_rows * (size_t)p.d_out * 4);
+  } else {
+    L.part_a = L.part_b = off;
+  }
+  L.workspace_bytes = off;
+  return L;
+}
+
+std::vector<uint8_t> table_blob(const PlanTables& p, const DeviceLayout& L) {
+  std::vector<uint8_t> b(L.table_bytes, 0);
+  auto put = [&](size_t at, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(b.data() + at, src, bytes);
+  };
+  put(L.offsets, p.offsets.data(), 8 * p.offsets.size());
+  put(L.zoff, p.zoff.data(), 8 * p.zoff.size());
+  put(L.ranks, p.ranks.data(), 4 * p.ranks.size());
+  put(L.rpad, p.rpad.data(), 4 * p.rpad.size());
+  put(L.roff, p.roff.data(), 4 * p.roff.size());
+  put(L.ch_first, p.ch_first.data(), 4 * p.ch_first.size());
+  put(L.ch_count, p.ch_count.data(), 4 * p.ch_count.size());
+  put(L.nano, p.nano.data(), 4 * p.nano.size());
+  put(L.chunks, p.chunks.data(), 4 * p.chunks.size());
+  put(L.cpref, p.cpref.data(), 4 * p.cpref.size());
+  put(L.tiles, p.tiles.data(), 4 * p.tiles.size());
+  put(L.ext_start, p.ext_start.data(), 4 * p.ext_start.size());
+  put(L.ext, p.ext.data(), 4 * p.ext.size());
+  return b;
+}
+
+}  // namespace mlora

@@ -1,0 +1,68 @@
+// Host plan: the integer tables that drive every kernel of the packed
+// multi-LoRA layer.  Pure C++17, no HIP call, so it is testable without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/mlora.h"
+
+namespace mlora {
+
+constexpr int kKStep = 64;       // K extent of one extension step
+constexpr int kMinRankPad = 32;  // smallest padded rank (one MFMA tile edge)
+
+struct Opts {
+  int32_t nano_rows = 32;
+  int32_t gemm_rows = 256;
+  int32_t n_streams = 1;
+  int32_t chunk_min = 256;
+  int32_t chunk_max = 2048;
+  int32_t chunk_per_rank = 8;
+  int32_t w0_layout = MLORA_W0_KN;
+};
+
+struct PlanTables {
+  int32_t n = 0;
+  int64_t T = 0, d_in = 0, d_out = 0;
+  int32_t dtype = MLORA_BF16;
+  Opts opts;
+  int32_t n_groups = 0;
+  int64_t z_elems = 0, rpad_total = 0, partial_rows = 0;
+
+  std::vector<int64_t> offsets, zoff;
+  std::vector<int32_t> ranks, rpad, roff, groups;
+  std::vector<int32_t> nano, nano_start;           // nano: [n_nano][3]
+  std::vector<int32_t> chunks, chunk_start, cpref; // chunks: [n_chunks][3]
+  std::vector<int32_t> ch_first, ch_count;
+  std::vector<int32_t> tiles, tile_start;          // tiles: [n_tiles][2]
+  std::vector<int32_t> ext, ext_start;             // ext: [n_ext][4]
+
+  int64_t n_nano() const { return (int64_t)nano.size() / 3; }
+  int64_t n_chunks() const { return (int64_t)chunks.size() / 3; }
+  int64_t n_tiles() const { return (int64_t)tiles.size() / 2; }
+  int64_t n_ext() const { return (int64_t)ext.size() / 4; }
+};
+
+// Validates and fills `out`.  On error returns the status and a message.
+mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ranks, int64_t d_in,
+                        int64_t d_out, int32_t dtype, const mlora_plan_opts* opts, PlanTables& out,
+                        std::string& err);
+
+// Byte layout of the device copy of the tables and of the workspace.
+struct DeviceLayout {
+  // offsets (bytes) of each table inside the table blob
+  size_t offsets, zoff, ranks, rpad, roff, ch_first, ch_count, nano, chunks, cpref, tiles,
+      ext_start, ext;
+  size_t table_bytes;
+  // offsets (bytes) of the work buffers inside the workspace
+  size_t acat_t, dz, part_a, part_b;
+  size_t workspace_bytes;
+};
+
+DeviceLayout device_layout(const PlanTables& p);
+std::vector<uint8_t> table_blob(const PlanTables& p, const DeviceLayout& L);
+
+}  // namespace mlora

@@ -1,0 +1,157 @@
+"""Benchmark: packed multi-LoRA linear forward+backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward (shrink, base GEMM with fused expand) and one backward
+(dZ, dB, dA, reduction, dX GEMM with fused dZ.A^T) of the whole layer over
+one batch, on inputs already resident in device memory.  Four independent
+(X, dY) sets rotate across steps so activations do not stay in the 256 MB
+last-level cache.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def alg_flops(w, proj):
+    """Algorithmic FLOPs of forward+backward: sum_i n_i (4 d_in d_out + 6 r_i (d_in + d_out))."""
+    p = w.projections[proj]
+    return sum(n * (4 * p.d_in * p.d_out + 6 * r * (p.d_in + p.d_out))
+               for n, r in zip(w.tokens, w.ranks))
+
+
+def gemm_fwd_flops(w, proj):
+    """One forward GEMM launch: base X.W0 plus the fused expand Z'.B."""
+    p = w.projections[proj]
+    return 2 * w.T * p.d_in * p.d_out + sum(2 * n * r * p.d_out for n, r in zip(w.tokens, w.ranks))
+
+
+def cpu_baseline(w, proj, budget_s=20.0):
+    """The oracle (numpy fp64) on the host, whole workload once, or a prefix of
+    the adapters if one pass would exceed the budget."""
+    from oracle import lora as ol
+    from workloads.tensors import host_tensors
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    h = host_tensors(w, proj)
+    t0 = time.perf_counter()
+    ol.forward(h["X"], h["W0"], h["A"], h["B"], h["scales"], h["offsets"], w.dtype)
+    ol.backward(h["dY"], h["X"], h["W0"], h["A"], h["B"], h["scales"], h["offsets"], w.dtype)
+    dt = time.perf_counter() - t0
+    return {"value": w.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full forward+backward of the workload ({w.T} tokens) in float64 numpy, "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_proj")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--streams", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="do not bracket launches with events (for external profilers)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: the packed layer is measured on one device's "
+              f"share (--gpus {a.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from adapter_lora_segments_amd import Plan, PackedLoRALinear, device_check
+    from workloads import load_workload
+    from workloads.tensors import device_tensors
+
+    torch.cuda.set_device(0)
+    device_check()
+    w = load_workload(a.workload, a.seed)
+    proj = 0
+    p = w.projections[proj]
+    SETS = 4
+    d = device_tensors(w, proj, sets=SETS)
+    plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16",
+                n_streams=a.streams or w.n_streams)
+    layer = PackedLoRALinear(plan, d["W0"], d["A"], d["B"], d["scales"])
+    Ys = [torch.empty((w.T, p.d_out), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
+    dXs = [torch.empty((w.T, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
+
+    def step(i):
+        k = i % SETS
+        layer.forward(d["X"][k], Ys[k])
+        layer.backward(d["dY"][k], d["X"][k], dXs[k])
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    prof = not a.no_profile
+    plan.profile_enable(prof)
+    if prof:
+        plan.profile_read()  # clear
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    kern = plan.profile_read() if prof else {}
+    plan.profile_enable(False)
+
+    ms = el / a.steps * 1e3
+    tok_s = w.T * a.steps / el
+    F = alg_flops(w, proj)
+    tflops = F / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "multi-LoRA fwd+bwd tokens/sec per layer",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {p.d_in}x{p.d_out} bf16, {w.n} adapters, ranks "
+                               f"{sorted(set(w.ranks))}, {w.T} tokens (seed {w.seed})",
+                   "T": w.T, "d_in": p.d_in, "d_out": p.d_out, "adapters": w.n,
+                   "streams": plan.info["n_groups"]},
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+    }
+    if kern:
+        out["kernels_ms_per_step"] = {k: v[0] / a.steps for k, v in kern.items() if v[1]}
+        g_ms, g_n = kern["gemm_fwd"]
+        if g_n:
+            avg = g_ms / g_n
+            ach = gemm_fwd_flops(w, proj) / (avg * 1e-3) / 1e12
+            out["roofline"] = {"kernel": "k_gemm<fwd> (base GEMM + fused expand)", "bound": "mfma",
+                               "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                               "avg_launch_ms": avg}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, proj)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

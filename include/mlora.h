@@ -1,0 +1,234 @@
+/*
+ * mlora.h -- C interface of the packed multi-LoRA linear layer for AMD MI355X
+ * (gfx950).
+ *
+ * What it computes.  Many LoRA adapters share one frozen base weight W0.  The
+ * packed token axis (sequence length x batch, PLoRA: Efficient Concurrent LoRA
+ * Training for Large Language Models, §9.2) is split into contiguous
+ * segments: rows [o_i, o_{i+1}) belong to adapter i.  Each adapter computes
+ * exactly standard LoRA on its rows (same page, §2.4), with the shapes of
+ * §2.1 (W0: d_in x d_out, A_i: d_in x r_i, B_i: r_i x d_out; the page's
+ * product "B x A" is read as A.B, the only order the shapes allow):
+ *
+ *   forward :  Z'_i = s_i X_i A_i                      (saved activation)
+ *              Y_i  = X_i W0 + Z'_i B_i
+ *   backward:  dZ_i = s_i dY_i B_i^T                   (PLoRA §9.2 Case 2)
+ *              dB_i = Z'_i^T dY_i  (= s_i Z_i^T dY_i)  (Case 1)
+ *              dA_i = X_i^T dZ_i                       (Case 3)
+ *              dX_i = dY_i W0^T + dZ_i A_i^T           (Case 4 plus the base)
+ *
+ * W0 is frozen and gets no gradient.  An adapter with no rows gets dA_i = 0
+ * and dB_i = 0.  Gradients are written, never accumulated.
+ *
+ * Precision.  MLORA_BF16: X, W0, A_i, B_i, dY, Y, dX, Z' and the internal
+ * dZ are bf16 (round to nearest even); every product accumulates in fp32;
+ * dA_i and dB_i are fp32.  MLORA_FP32: every tensor fp32, fp32 arithmetic,
+ * no reduced-precision step anywhere.
+ *
+ * Layouts.  Row-major, densely packed: X [T][d_in], Y [T][d_out],
+ * dY [T][d_out], dX [T][d_in], A_i [d_in][r_i], B_i [r_i][d_out],
+ * dA_i [d_in][r_i] fp32, dB_i [r_i][d_out] fp32.  W0 is [d_in][d_out]
+ * (MLORA_W0_KN, the math layout) or [d_out][d_in] (MLORA_W0_NK, the layout of
+ * an nn.Linear weight).  The saved activation Z' is plan-defined: adapter i
+ * occupies plan.zoff[i] .. + n_i*r_pad(i) elements as [n_i][r_pad(i)], the
+ * padding columns zero.
+ *
+ * Memory and ownership.  Every device buffer belongs to the caller: tensors,
+ * the saved activation (mlora_plan_info.z_bytes) and the workspace
+ * (mlora_plan_info.workspace_bytes).  Per-adapter pointers and scales are
+ * passed as DEVICE arrays (as batched BLAS interfaces take them): the caller
+ * uploads the n pointers / floats once and reuses them while the adapter set
+ * is unchanged.  Device pointers must be 16-byte aligned.  The plan owns only
+ * host tables and, when it uses more than one stream, its internal streams
+ * and events.
+ *
+ * Streams.  Work is enqueued on the caller's stream (a hipStream_t passed as
+ * void*, NULL = the null stream) and the calls return without waiting.  With
+ * n_streams > 1 the plan forks its adapter groups onto internal streams with
+ * events and joins them back onto the caller's stream before returning, so
+ * the caller sees ordinary single-stream ordering.
+ *
+ * Errors.  Every call validates its arguments on the host before launching
+ * anything; on failure it returns a negative status, launches nothing and
+ * writes no output.  mlora_last_error() gives a thread-local message.  No call
+ * aborts or throws.  Calls on one plan are not thread-safe.
+ */
+#ifndef MLORA_H
+#define MLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLORA_OK = 0,
+  MLORA_ERR_INVALID_ARG = -1, /* malformed offsets/ranks/pointers/sizes   */
+  MLORA_ERR_UNSUPPORTED = -2, /* rank > 256, dims not multiples of 64, device not gfx950 */
+  MLORA_ERR_HIP = -3,         /* a HIP runtime call failed (message has the hipError_t) */
+  MLORA_ERR_WORKSPACE = -4,   /* workspace too small or plan tables not uploaded to it */
+  MLORA_ERR_NOMEM = -5        /* host allocation failed                    */
+} mlora_status;
+
+typedef enum { MLORA_FP32 = 0, MLORA_BF16 = 1 } mlora_dtype;
+typedef enum { MLORA_W0_KN = 0, MLORA_W0_NK = 1 } mlora_w0_layout;
+
+#define MLORA_MAX_RANK 256
+#define MLORA_MAX_ADAPTERS 65536
+#define MLORA_MAX_STREAMS 4
+
+/* Plan options.  A zero field takes its default. */
+typedef struct {
+  int32_t nano_rows;      /* NB, rows per nano-batch (16..256, multiple of 16); default 32 */
+  int32_t gemm_rows;      /* BM, rows per GEMM tile; default 256 (bf16 requires 256)        */
+  int32_t n_streams;      /* adapter groups on separate streams, 1..4; default 1            */
+  int32_t chunk_min;      /* reduction chunk rows, KC_i = min(chunk_max,                    */
+  int32_t chunk_max;      /*   max(chunk_min, chunk_per_rank * r_pad(i)));                  */
+  int32_t chunk_per_rank; /*   defaults 256, 2048, 8                                        */
+  int32_t w0_layout;      /* mlora_w0_layout; default MLORA_W0_KN                          */
+} mlora_plan_opts;
+
+typedef struct mlora_plan_s *mlora_plan_t;
+
+/*
+ * mlora_plan -- build the host plan for one packed layer (no HIP call).
+ *
+ * seg_offsets: host, n+1 entries, seg_offsets[0] = 0, non-decreasing,
+ *   T = seg_offsets[n] < 2^31.  ranks: host, n entries in [1, 256].
+ *   1 <= n <= MLORA_MAX_ADAPTERS; d_in, d_out positive multiples of 64.
+ * The rule (tLoRA: Efficient Multi-LoRA Training with Elastic Shared
+ * Super-Models, abstract: low-rank tiles re-formed per rank, rank-aware
+ * nano-batches; PLoRA §9.2: tile tokens and hidden dims, never the rank):
+ *  1. r_pad(i) = max(32, next power of two >= r_i).
+ *  2. zoff(i) = sum_{j<i} n_j r_pad(j); roff(i) = sum_{j<i} r_pad(j).
+ *  3. S' = min(n_streams, n) groups of consecutive adapters: g_0 = 0,
+ *     g_S' = n, g_s = max(g_{s-1}, first a with o_a >= ceil(s T / S')).
+ *  4. Inside a group adapters are visited by r_pad descending, index
+ *     ascending.
+ *  5. Nano-batches: each adapter's rows cut into pieces of NB rows.
+ *  6. Reduction chunks: pieces of KC_i rows; chunk c's partial sums sit at
+ *     rank-row prefix cpref(c) = sum of r_pad over earlier chunks.
+ *  7. GEMM row tiles of BM rows per group; each tile lists extension steps
+ *     (adapter j, rows [lo,hi) of j in the tile, k0 = 0,64,..<r_pad(j)).
+ * The copies of seg_offsets/ranks are the plan's; the caller's arrays may be
+ * freed on return.  On error *out is left untouched.
+ */
+mlora_status mlora_plan(int32_t n, const int64_t *seg_offsets, const int32_t *ranks, int64_t d_in,
+                        int64_t d_out, mlora_dtype dtype, const mlora_plan_opts *opts,
+                        mlora_plan_t *out);
+
+void mlora_plan_destroy(mlora_plan_t plan);
+
+typedef struct {
+  int64_t T, n, d_in, d_out;
+  int32_t dtype, n_groups;
+  int64_t z_elems, z_bytes;  /* saved activation Z' size                        */
+  int64_t workspace_bytes;   /* device workspace for forward and backward       */
+  int64_t table_bytes;       /* leading part of the workspace holding the tables */
+  int64_t rpad_total, partial_rows;
+  int64_t n_nano, n_chunks, n_tiles, n_ext;
+} mlora_plan_info;
+
+mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);
+
+/* Plan tables, for inspection and bit-exact testing.  All int32 except
+ * MLORA_TAB_ZOFF and MLORA_TAB_OFFSETS (int64).  Shapes:
+ *   RPAD[n], ZOFF[n], ROFF[n], GROUPS[S'+1] (first adapter of each group),
+ *   NANO[n_nano][3] (adapter, row0, rows), NANO_START[S'+1],
+ *   CHUNKS[n_chunks][3], CHUNK_START[S'+1], CHUNK_RPREF[n_chunks],
+ *   ADAPTER_CHUNK_FIRST[n], ADAPTER_CHUNK_COUNT[n],
+ *   TILES[n_tiles][2] (row0, rows), TILE_START[S'+1],
+ *   EXT[n_ext][4] (adapter, lo, hi, k0), TILE_EXT_START[n_tiles+1],
+ *   OFFSETS[n+1], RANKS[n]. */
+typedef enum {
+  MLORA_TAB_RPAD = 0,
+  MLORA_TAB_ZOFF,
+  MLORA_TAB_ROFF,
+  MLORA_TAB_GROUPS,
+  MLORA_TAB_NANO,
+  MLORA_TAB_NANO_START,
+  MLORA_TAB_CHUNKS,
+  MLORA_TAB_CHUNK_START,
+  MLORA_TAB_CHUNK_RPREF,
+  MLORA_TAB_ADAPTER_CHUNK_FIRST,
+  MLORA_TAB_ADAPTER_CHUNK_COUNT,
+  MLORA_TAB_TILES,
+  MLORA_TAB_TILE_START,
+  MLORA_TAB_EXT,
+  MLORA_TAB_TILE_EXT_START,
+  MLORA_TAB_OFFSETS,
+  MLORA_TAB_RANKS,
+  MLORA_TAB_COUNT
+} mlora_table;
+
+/* Copies table `table` into host buffer dst.  *bytes_inout: capacity in,
+ * bytes written out.  Capacity too small -> MLORA_ERR_INVALID_ARG with
+ * *bytes_inout set to the size needed.  dst may be NULL to query the size. */
+mlora_status mlora_plan_export(mlora_plan_t plan, int32_t table, void *dst, size_t *bytes_inout);
+
+/* Copies the plan tables into the leading table_bytes of `workspace` on
+ * `stream` and remembers the workspace address.  Needed once per (plan,
+ * workspace) pair before forward/backward; they refuse any other workspace
+ * with MLORA_ERR_WORKSPACE.  The copy is asynchronous from plan-owned host
+ * memory that stays valid until the plan is destroyed. */
+mlora_status mlora_plan_upload(mlora_plan_t plan, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * mlora_forward -- Y = X W0 + Z' B per adapter, and Z' = s X A saved.
+ * X [T][d_in]; W0 per w0_layout; A, B: device arrays of n device pointers;
+ * scales: device array of n floats (any value, 0 and negatives allowed).
+ * Y [T][d_out] and Z (z_elems) are overwritten.  Kernels: grouped rank-padded
+ * shrink (PLoRA §9.2: split the input dimension for A), then the base GEMM
+ * with the LoRA expand as extra K-steps on the same accumulators (split the
+ * output dimension for B).
+ */
+mlora_status mlora_forward(mlora_plan_t plan, const void *X, const void *W0, const void *const *A,
+                           const void *const *B, const float *scales, void *Y, void *Z,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * mlora_backward -- dX (optional, NULL skips it), dA_i, dB_i (fp32).
+ * Inputs as in forward plus dY [T][d_out] and the Z' saved by forward.
+ * dA, dB: device arrays of n device pointers to fp32 buffers.  Case 2 (dZ)
+ * reduces over d_out inside one workgroup; Cases 1 and 3 reduce over tokens in
+ * fixed-size chunks whose partial sums are added in a fixed order (no float
+ * atomics: results are bitwise repeatable for a given plan); Case 4 runs as
+ * extra K-steps of the dX GEMM.
+ */
+mlora_status mlora_backward(mlora_plan_t plan, const void *dY, const void *X, const void *W0,
+                            const void *const *A, const void *const *B, const float *scales,
+                            const void *Z, void *dX, void *const *dA, void *const *dB,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+/* Per-kernel timing.  When enabled, every launch is bracketed by HIP events
+ * on the stream it runs on; mlora_profile_read waits for them, adds their
+ * durations to the totals of kernel `kind` and returns them, then clears. */
+typedef enum {
+  MLORA_K_SHRINK = 0,
+  MLORA_K_GEMM_FWD,
+  MLORA_K_DZ,
+  MLORA_K_DB,
+  MLORA_K_DA,
+  MLORA_K_REDUCE,
+  MLORA_K_GEMM_DX,
+  MLORA_K_PREP,
+  MLORA_K_COUNT
+} mlora_kernel_kind;
+
+mlora_status mlora_profile_enable(mlora_plan_t plan, int32_t on);
+mlora_status mlora_profile_read(mlora_plan_t plan, double *total_ms /*[MLORA_K_COUNT]*/,
+                                int64_t *launches /*[MLORA_K_COUNT]*/);
+
+/* MLORA_OK when the current device is gfx950, else MLORA_ERR_UNSUPPORTED. */
+mlora_status mlora_device_check(void);
+
+const char *mlora_status_string(mlora_status s);
+const char *mlora_last_error(void);
+const char *mlora_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLORA_H */

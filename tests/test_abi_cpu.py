@@ -1,0 +1,148 @@
+"""Host-side checks of libmlora.so without a GPU: it loads, exports every
+symbol include/mlora.h declares, builds plans bit-identical to the
+independent Python mirror, and rejects malformed arguments with the
+documented status codes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from adapter_lora_segments_amd import _lib
+from adapter_lora_segments_amd.binding import Plan
+from adapter_lora_segments_amd._lib import MloraError
+from oracle.plan_mirror import build_plan, PlanOpts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "mlora.h")) as f:
+        hdr = f.read()
+    declared = set(re.findall(r"\b(mlora_[a-z_]+)\s*\(", hdr))
+    assert declared == set(_lib.EXPORTS), declared ^ set(_lib.EXPORTS)
+    L = _lib.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.mlora_version().decode().startswith("mlora")
+    assert L.mlora_status_string(-4).decode() == "MLORA_ERR_WORKSPACE"
+
+
+def _mirror_vs_library(off, ranks, d_in, d_out, dtype, opts):
+    p = Plan(off, ranks, d_in, d_out, dtype, nano_rows=opts.nano_rows, gemm_rows=opts.gemm_rows,
+             n_streams=opts.n_streams, chunk_min=opts.chunk_min, chunk_max=opts.chunk_max,
+             chunk_per_rank=opts.chunk_per_rank)
+    m = build_plan(off, ranks, opts)
+    for name in ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks",
+                 "chunk_start", "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count",
+                 "tiles", "tile_start", "ext", "tile_ext_start"]:
+        got = p.export(name)
+        want = m[name]
+        if want.size == 0:
+            assert got.size == 0, name
+        else:
+            assert np.array_equal(got, want.reshape(got.shape)) and got.dtype == want.dtype, name
+    assert p.info["z_elems"] == m["z_elems"]
+    assert p.info["partial_rows"] == m["partial_rows"]
+    assert p.info["rpad_total"] == m["rpad_total"]
+    assert p.info["n_groups"] == m["n_groups"]
+    assert np.array_equal(p.export("offsets"), np.asarray(off, dtype=np.int64))
+
+
+@st.composite
+def plan_cases(draw):
+    n = draw(st.integers(1, 40))
+    toks = draw(st.lists(st.one_of(st.just(0), st.just(1), st.integers(0, 900)), min_size=n, max_size=n))
+    ranks = draw(st.lists(st.one_of(st.sampled_from([1, 4, 8, 16, 31, 32, 33, 64, 65, 128, 129, 255, 256]),
+                                    st.integers(1, 256)), min_size=n, max_size=n))
+    nb = draw(st.sampled_from([32, 64, 96, 256]))
+    S = draw(st.integers(1, 4))
+    cmin = draw(st.sampled_from([16, 64, 256]))
+    cmax = cmin * draw(st.sampled_from([1, 4, 8]))
+    cpr = draw(st.sampled_from([1, 8, 16]))
+    off = [0]
+    for t in toks:
+        off.append(off[-1] + t)
+    return off, ranks, PlanOpts(nano_rows=nb, gemm_rows=256, n_streams=S, chunk_min=cmin,
+                                chunk_max=cmax, chunk_per_rank=cpr)
+
+
+@settings(max_examples=200, deadline=None)
+@given(plan_cases())
+def test_plan_bit_exact_against_mirror(case):
+    off, ranks, opts = case
+    _mirror_vs_library(off, ranks, 128, 192, "bf16", opts)
+
+
+@pytest.mark.parametrize("name,seed", [(w, s) for w in ["tiny_fp32", "llama7b_proj", "llama3_8b_layer",
+                                                          "nano_stress", "mlp70b_pair"] for s in (0, 1, 2)])
+def test_plan_bit_exact_on_workloads(name, seed):
+    from workloads import load_workload
+    w = load_workload(name, seed)
+    for p in w.projections:
+        _mirror_vs_library(w.seg_offsets(), w.ranks, p.d_in, p.d_out, w.dtype,
+                           PlanOpts(n_streams=w.n_streams))
+
+
+def _status(fn):
+    with pytest.raises(MloraError) as e:
+        fn()
+    return e.value.status
+
+
+def test_plan_argument_errors():
+    ok = dict(seg_offsets=[0, 5, 9], ranks=[4, 8], d_in=128, d_out=64)
+    Plan(**ok)  # valid
+    assert _status(lambda: Plan([1, 5, 9], [4, 8], 128, 64)) == -1          # offsets[0] != 0
+    assert _status(lambda: Plan([0, 5, 3], [4, 8], 128, 64)) == -1          # decreasing
+    assert _status(lambda: Plan([0, 5, 9], [0, 8], 128, 64)) == -1          # rank 0
+    assert _status(lambda: Plan([0, 5, 9], [4, 257], 128, 64)) == -2        # rank > 256
+    assert _status(lambda: Plan([0, 5, 9], [4, 8], 100, 64)) == -2          # d_in % 64
+    assert _status(lambda: Plan([0, 5, 9], [4, 8], 128, 0)) == -1           # d_out <= 0
+    assert _status(lambda: Plan([0, 5, 9], [4, 8], 128, 64, nano_rows=8)) == -1
+    assert _status(lambda: Plan([0, 5, 9], [4, 8], 128, 64, n_streams=5)) == -1
+    assert _status(lambda: Plan([0, 5, 9], [4, 8], 128, 64, gemm_rows=128)) == -2  # bf16 needs 256
+    Plan([0, 5, 9], [4, 8], 128, 64, "fp32", gemm_rows=128)
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    off = (ctypes.c_int64 * 1)(0)
+    rk = (ctypes.c_int32 * 1)(4)
+    assert L.mlora_plan(0, off, rk, 64, 64, 1, None, ctypes.byref(h)) == -1  # n = 0
+    assert L.mlora_plan(1, None, rk, 64, 64, 1, None, ctypes.byref(h)) == -1
+    assert L.mlora_plan(1, off, rk, 64, 64, 1, None, None) == -1
+    assert "out" in L.mlora_last_error().decode()
+    assert not h.value  # untouched on error
+
+
+def test_forward_rejects_bad_arguments_without_launching():
+    """Errors found on the host return before any HIP call (no GPU here)."""
+    L = _lib.lib()
+    p = Plan([0, 5, 9], [4, 8], 128, 64)
+    vp = ctypes.c_void_p
+    dummy = vp(4096)
+    # NULL X
+    assert L.mlora_forward(p.handle, None, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 30, None) == -1
+    # misaligned pointer
+    assert L.mlora_forward(p.handle, vp(4097), dummy, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 30, None) == -1
+    # workspace too small
+    assert L.mlora_forward(p.handle, dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 16, None) == -4
+    # workspace never uploaded
+    assert L.mlora_forward(p.handle, dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 30, None) == -4
+    assert L.mlora_backward(p.handle, dummy, dummy, dummy, dummy, dummy, dummy, None, None, None,
+                            dummy, dummy, 1 << 30, None) == -1
+    # unknown table id / small buffer
+    n = ctypes.c_size_t(0)
+    assert L.mlora_plan_export(p.handle, 99, None, ctypes.byref(n)) == -1
+    assert L.mlora_plan_export(p.handle, 0, None, ctypes.byref(n)) == 0 and n.value == 8
+    small = ctypes.c_size_t(4)
+    buf = (ctypes.c_int32 * 1)()
+    assert L.mlora_plan_export(p.handle, 0, buf, ctypes.byref(small)) == -1 and small.value == 8
+
+
+def test_plan_info_sizes():
+    p = Plan([0, 40, 40, 200, 300], [8, 64, 100, 16], 256, 512)
+    i = p.info
+    assert i["T"] == 300 and i["n"] == 4 and i["z_elems"] == 24960 and i["z_bytes"] == 2 * 24960
+    assert i["workspace_bytes"] >= i["table_bytes"] + 2 * i["z_elems"] + 4 * i["partial_rows"] * (256 + 512)
