@@ -38,6 +38,27 @@ def gemm_fwd_flops(w, proj):
     return 2 * w.T * p.d_in * p.d_out + sum(2 * n * r * p.d_out for n, r in zip(w.tokens, w.ranks))
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per forward-GEMM launch from the committed counter summary
+    (profiles/hbm_bytes_<workload>.txt), or None when that file is missing or
+    was taken from a different version of the kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_bytes_{workload}.txt")
+    src = os.path.join(ROOT, "adapter_lora_segments_amd", "csrc", "kernels_bf16.hip")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernels_bf16_sha256_16") != sha:
+        return None
+    v = vals.get("traffic_bytes k_gemm_fwd")
+    return int(v) if v else None
+
+
 def cpu_baseline(w, proj, budget_s=20.0):
     """The oracle (numpy fp64) on the host, whole workload once, or a prefix of
     the adapters if one pass would exceed the budget."""
@@ -67,6 +88,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--streams", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="first run one elementwise copy kernel (torch.neg on float32) reading and "
+                         "writing this many MiB, to scale hardware byte counters")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not bracket launches with events (for external profilers)")
     a = ap.parse_args()
@@ -98,6 +122,14 @@ def main():
         layer.forward(d["X"][k], Ys[k])
         layer.backward(d["dY"][k], d["X"][k], dXs[k])
 
+    if a.calib_copy_mb:
+        nel = a.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -146,7 +178,8 @@ def main():
             ach = gemm_fwd_flops(w, proj) / (avg * 1e-3) / 1e12
             out["roofline"] = {"kernel": "k_gemm<fwd> (base GEMM + fused expand)", "bound": "mfma",
                                "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                               "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                               "frac": ach / PEAK_BF16_TFLOPS,
+                               "traffic": measured_traffic(w.name),
                                "avg_launch_ms": avg}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, proj)
