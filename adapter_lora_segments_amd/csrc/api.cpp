@@ -79,6 +79,7 @@ mlora::DevTables dev_tables(const mlora_plan_s* p, void* ws) {
   t.tiles = reinterpret_cast<const int32_t*>(b + L.tiles);
   t.ext_start = reinterpret_cast<const int32_t*>(b + L.ext_start);
   t.ext = reinterpret_cast<const int32_t*>(b + L.ext);
+  t.zero = reinterpret_cast<const uint16_t*>(b + L.zero);
   return t;
 }
 
@@ -373,6 +374,7 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     ga.n_ntiles = (int32_t)((P.d_out + 255) / 256);
     ga.ebuf = (const uint16_t*)Z;
     ga.eb = B;
+    ga.acat_t = acat_t;
     ga.t = t;
     st = timed(p, MLORA_K_GEMM_FWD, s, [&] { mlora::launch_gemm(true, nk, ga, s); });
     if (st != MLORA_OK) return st;
@@ -427,6 +429,13 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
   uint16_t* dZ = reinterpret_cast<uint16_t*>(wsb + L.dz);
   float* partA = reinterpret_cast<float*>(wsb + L.part_a);
   float* partB = reinterpret_cast<float*>(wsb + L.part_b);
+  uint16_t* acat_t = reinterpret_cast<uint16_t*>(wsb + L.acat_t);
+  // A_cat^T feeds the dZ.A^T extension steps of the dX GEMM; rebuilt here so
+  // the backward does not depend on what the workspace held before.
+  if (dX) {
+    st = timed(p, MLORA_K_PREP, cs, [&] { mlora::launch_prep_acat_t(t, P.n, P.d_in, A, acat_t, cs); });
+    if (st != MLORA_OK) return st;
+  }
   st = fork_groups(p, cs);
   if (st != MLORA_OK) return st;
   for (int g = 0; g < P.n_groups; ++g) {
@@ -472,6 +481,7 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
       ga.n_ntiles = (int32_t)((P.d_in + 255) / 256);
       ga.ebuf = dZ;
       ga.eb = A;
+      ga.acat_t = acat_t;
       ga.t = t;
       st = timed(p, MLORA_K_GEMM_DX, s, [&] { mlora::launch_gemm(false, !nk, ga, s); });
       if (st != MLORA_OK) return st;

@@ -65,4 +65,13 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// Load of a value that no kernel writes while it runs (plan tables, pointer
+// arrays) through the constant address space, so a wave-uniform address
+// becomes a scalar load: it then waits on lgkmcnt, not on the vector-memory
+// counter that tracks the direct-to-LDS pipeline.
+template <class T>
+__device__ __forceinline__ T ldc(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 }  // namespace mlora

@@ -22,6 +22,7 @@ struct DevTables {
   const int32_t* tiles;     // [n_tiles][2]
   const int32_t* ext_start; // [n_tiles+1]
   const int32_t* ext;       // [n_ext][4]
+  const uint16_t* zero;     // 256 zero bytes
 };
 
 // ---------------- bf16 path (MFMA) ----------------
@@ -53,7 +54,7 @@ void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, 
 // C[row][n] = sum_k Aop[row][k] Bop[k][n] over K, then the extension steps of
 // each row tile: rows of adapter j times E_j (Z' or dZ) against EB_j.
 //   fwd: Aop = X, Bop = W0, E = Z', EB_j = B_j ([r_j][N], n contiguous)
-//   dx : Aop = dY, Bop = W0^T, E = dZ, EB_j = A_j^T (A_j is [N][r_j])
+//   dx : Aop = dY, Bop = W0^T, E = dZ, EB_j = A_j^T = rows roff_j.. of A_cat^T
 struct GemmArgs {
   const uint16_t* A;
   int64_t lda;
@@ -63,8 +64,9 @@ struct GemmArgs {
   int64_t ldc;
   int32_t K, N;
   int32_t tile_begin, n_mtiles, n_ntiles;
-  const uint16_t* ebuf;
-  const void* const* eb;
+  const uint16_t* ebuf;     // Z' (fwd) or dZ (dx), plan layout
+  const void* const* eb;    // fwd: B_j pointers
+  const uint16_t* acat_t;   // dx: A_cat^T [rpad_total][N]
   DevTables t;
 };
 // main_b_kcontig: Bop element (k, n) at B[n*ldb + k] (else at B[k*ldb + n]).

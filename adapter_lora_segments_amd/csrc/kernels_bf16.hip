@@ -376,9 +376,71 @@ void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, 
 // rows [lo,hi) of E_j (other rows zero) and k-rows [k0, k0+64) of EB_j
 // (rows >= r_j zero).  Output written as bf16.
 // ---------------------------------------------------------------------------
+#define MLORA_LDS __attribute__((address_space(3)))
+
+// 16 bytes per lane from global memory straight into LDS: the wave's 64 lanes
+// fill the 1 KiB block at `blk` in lane order (lane i at byte 16 i).  Issued
+// as inline assembly (M0 = block address) so the compiler does not treat the
+// copy as an LDS store it must drain before every LDS read: the kernel's own
+// vmcnt waits and barriers order the ring (the asm still receives the ring's
+// address and clobbers memory, so LDS reads are never cached across it).
+__device__ __forceinline__ void dma16(const uint16_t* src, u32x4* blk) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(MLORA_LDS void*)blk);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// Wait until at most N direct-to-LDS loads of this wave are in flight, then
+// meet the other waves.  A bare s_barrier (no fence): the loads still in
+// flight target other ring stages and must not be drained here.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 0, "unsupported wait count");
+}
+
+// LDS tile layouts of one 32-deep K-step (16 KiB each):
+//  k-contiguous: 256 rows x 32 bf16 (four 16-byte chunks); chunk c of row r
+//    sits at position c ^ ((r >> 1) & 3), so the eight rows one MFMA fragment
+//    read touches per 128-byte phase fall in distinct banks;
+//  n-contiguous: 32 k-rows x 256 bf16 (thirty-two chunks); chunk c of k-row
+//    kr sits at c ^ (2 (kr & 3)), so the four k-rows of one transposing
+//    read fall in distinct banks.
+__device__ __forceinline__ int kpos(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
+__device__ __forceinline__ int npos(int kr, int c) { return kr * 32 + (c ^ (2 * (kr & 3))); }
+
+// B fragment of a 32x32x16 MFMA from an n-contiguous tile: lane l needs
+// B[k = kb + 8 (l/32) + 0..7][n = nb + l%32].  ds_read_b64_tr_b16 hands lane i
+// of a 16-lane group element (i % 4) of the 8 bytes addressed by group lane
+// 4e + i/4, so group lane s addresses k-row kb' + s/4, columns n' + 4 (s%4).
+__device__ __forceinline__ u32x4 read_b_tr(const u32x4* tile, int nb, int kb, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int g = lane >> 4, s = lane & 15;
+  const int n = nb + 16 * (g & 1) + 4 * (s & 3);
+  const int k = kb + 8 * (g >> 1) + (s >> 2);
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kr = k + 4 * h;
+    const int byte = npos(kr, n >> 3) * 16 + 2 * (n & 7);
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MLORA_LDS s16x4*)((MLORA_LDS char*)(MLORA_LDS void*)tile + byte));
+    const u32x2 u = __builtin_bit_cast(u32x2, v);
+    out[2 * h] = u[0];
+    out[2 * h + 1] = u[1];
+  }
+  return out;
+}
+
 template <bool FWD, bool MAIN_B_KC>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
-  __shared__ u32x4 lds[2][2][256 * 8];
+  constexpr int NS = 5;                    // ring stages (loads run NS-1 steps ahead)
+  constexpr int LPS = 8;                   // direct loads per wave per stage
+  __shared__ u32x4 ring[NS][2][1024];      // [stage][A/B][16 KiB]
 
   // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
   // contiguous range of logical tiles, grouped 8 row tiles at a time.
@@ -394,99 +456,84 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   const int tm = fm + within % gm, tn = within / gm;
 
   const int tix = g.tile_begin + tm;
-  const int row0 = g.t.tiles[2 * tix], mrows = g.t.tiles[2 * tix + 1];
-  const int e0 = g.t.ext_start[tix], e1 = g.t.ext_start[tix + 1];
+  const int row0 = ldc(g.t.tiles + 2 * tix), mrows = ldc(g.t.tiles + 2 * tix + 1);
+  const int e0 = ldc(g.t.ext_start + tix), e1 = ldc(g.t.ext_start + tix + 1);
   const int n0 = tn * 256;
-  const int nk = g.K / 64;
+  const int nk = g.K / 32;
   const int nsteps = nk + (e1 - e0);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int wm = w >> 1, wn = w & 1;
-  const int lrow = tid >> 3, lch = tid & 7;      // k-contiguous loader: row, chunk
-  const int tmb = tid & 31, tkb = tid >> 5;      // transposing loader: 8x8 block
 
-  u32x4 ra[8], rb[8];
-  bool b_transposed = false;  // how rb must be written for the staged step
+  // This lane's rows/chunks in the four k-contiguous and the four
+  // n-contiguous 1 KiB blocks it loads per stage (block index q = 4w + i).
+  int kr_row[4], kr_chunk[4], nc_krow[4], nc_chunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qb = 4 * w + i;
+    kr_row[i] = 16 * qb + (lane >> 2);
+    kr_chunk[i] = (lane & 3) ^ ((kr_row[i] >> 1) & 3);
+    nc_krow[i] = 2 * qb + (lane >> 5);
+    nc_chunk[i] = (lane & 31) ^ (2 * (nc_krow[i] & 3));
+  }
+  const uint16_t* aptr[4];
+  const uint16_t* bptr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    aptr[i] = g.A + (int64_t)(row0 + min(kr_row[i], mrows - 1)) * g.lda + 8 * kr_chunk[i];
+    if (MAIN_B_KC)
+      bptr[i] = g.B + (int64_t)min(n0 + kr_row[i], g.N - 1) * g.ldb + 8 * kr_chunk[i];
+    else
+      bptr[i] = g.B + (int64_t)nc_krow[i] * g.ldb + min(n0 + 8 * nc_chunk[i], g.N - 8);
+  }
 
-  auto load = [&](int step) {
+  // Global sources of this lane's eight 1 KiB blocks of step `step` (four of
+  // the A tile, four of the B tile); rows that must read as zero point at the
+  // zero page.
+  auto sources = [&](int step, const uint16_t* (&src)[8]) {
     if (step < nk) {
-      const int k0 = step * 64;
+      const int k0 = step * 32;
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int r = lrow + 32 * p;
-        const int grow = row0 + min(r, mrows - 1);
-        ra[p] = ld16(g.A + (int64_t)grow * g.lda + k0 + 8 * lch);
-      }
-      if (MAIN_B_KC) {
+      for (int i = 0; i < 4; ++i) src[i] = aptr[i] + k0;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const int gn = min(n0 + lrow + 32 * p, g.N - 1);
-          rb[p] = ld16(g.B + (int64_t)gn * g.ldb + k0 + 8 * lch);
-        }
-        b_transposed = false;
-      } else {
-        const int col = min(n0 + 8 * tmb, g.N - 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rb[i] = ld16(g.B + (int64_t)(k0 + 8 * tkb + i) * g.ldb + col);
-        b_transposed = true;
-      }
+      for (int i = 0; i < 4; ++i) src[4 + i] = MAIN_B_KC ? bptr[i] + k0 : bptr[i] + (int64_t)k0 * g.ldb;
     } else {
       const int e = e0 + step - nk;
-      const int j = g.t.ext[4 * e], lo = g.t.ext[4 * e + 1], hi = g.t.ext[4 * e + 2];
-      const int k0 = g.t.ext[4 * e + 3];
-      const int rp = g.t.rpad[j], rj = g.t.ranks[j];
-      const int64_t oj = g.t.offsets[j];
-      const uint16_t* zb = g.ebuf + g.t.zoff[j];
-      const int kk = k0 + 8 * lch;
+      const int j = ldc(g.t.ext + 4 * e), lo = ldc(g.t.ext + 4 * e + 1), hi = ldc(g.t.ext + 4 * e + 2);
+      const int k0 = ldc(g.t.ext + 4 * e + 3);
+      const int rp = ldc(g.t.rpad + j);
+      const int64_t oj = ldc(g.t.offsets + j);
+      const uint16_t* zb = g.ebuf + ldc(g.t.zoff + j);
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int grow = row0 + lrow + 32 * p;
-        ra[p] = (grow >= lo && grow < hi && kk < rp) ? ld16(zb + (grow - oj) * rp + kk) : zero4();
+      for (int i = 0; i < 4; ++i) {
+        const int grow = row0 + kr_row[i];
+        src[i] = (grow >= lo && grow < hi) ? zb + (int64_t)(grow - oj) * rp + k0 + 8 * kr_chunk[i]
+                                           : g.t.zero;
       }
-      const uint16_t* eb = static_cast<const uint16_t*>(g.eb[j]);
-      if (FWD) {
-        // EB_j = B_j [r_j][N], n contiguous: transposing loader
-        const int col = min(n0 + 8 * tmb, g.N - 8);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int k = k0 + 8 * tkb + i;
-          rb[i] = k < rj ? ld16(eb + (int64_t)k * g.N + col) : zero4();
+      for (int i = 0; i < 4; ++i) {
+        const int k = k0 + nc_krow[i];
+        const int col = min(n0 + 8 * nc_chunk[i], g.N - 8);
+        if (FWD) {
+          const int rj = ldc(g.t.ranks + j);
+          src[4 + i] = k < rj ? static_cast<const uint16_t*>(ldc(g.eb + j)) + (int64_t)k * g.N + col
+                              : g.t.zero;
+        } else {
+          src[4 + i] = g.acat_t + (int64_t)(ldc(g.t.roff + j) + k) * g.N + col;
         }
-        b_transposed = true;
-      } else {
-        // EB_j(k, n) = A_j[n][k], k contiguous with row stride r_j
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const int gn = min(n0 + lrow + 32 * p, g.N - 1);
-          const uint16_t* src = eb + (int64_t)gn * rj;
-          if ((rj & 7) == 0) {
-            rb[p] = kk < rj ? ld16(src + kk) : zero4();
-          } else {
-            uint32_t v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (kk + i < rj) ? (uint32_t)src[kk + i] : 0u;
-            rb[p] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
-                          v[6] | (v[7] << 16)};
-          }
-        }
-        b_transposed = false;
       }
     }
   };
-
-  auto store = [&](int buf) {
+  // Block i (0..7) of a stage: this wave's four A blocks, then its four B blocks.
+  auto block = [&](int step, int i) -> u32x4* {
+    return ring[step % NS][i >> 2] + 64 * (4 * w + (i & 3));
+  };
+  auto issue = [&](int step) {
+    const uint16_t* src[8];
+    sources(step, src);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) lds[buf][0][swz(lrow + 32 * p, lch)] = ra[p];
-    if (b_transposed) {
-      u32x4 tr[8];
-      transpose8x8(rb, tr);
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) lds[buf][1][swz(8 * tmb + jj, tkb)] = tr[jj];
-    } else {
-#pragma unroll
-      for (int p = 0; p < 8; ++p) lds[buf][1][swz(lrow + 32 * p, lch)] = rb[p];
-    }
+    for (int i = 0; i < 8; ++i) dma16(src[i], block(step, i));
   };
 
   f32x16 acc[4][4];
@@ -497,26 +544,86 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nsteps) load(st + 1);
+  // Fragments of one 16-deep slice.  The pipeline runs at slice
+  // granularity: the LDS reads of the next slice are in flight while the
+  // current slice's 16 MFMAs run from registers.
+  struct Frags {
+    u32x4 a[4], b[4];
+  };
+  auto read_slice = [&](int step, int ks, Frags& F) {
+    const u32x4* sa = ring[step % NS][0];
+    const u32x4* sb = ring[step % NS][1];
+    const bool b_kc = step < nk ? MAIN_B_KC : false;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 af[4], bfr[4];
+    for (int fi = 0; fi < 4; ++fi) F.a[fi] = sa[kpos(128 * wm + 32 * fi + l32, 2 * ks + half)];
+    if (b_kc) {
 #pragma unroll
-      for (int fi = 0; fi < 4; ++fi) af[fi] = lds[buf][0][swz(128 * wm + 32 * fi + l32, 2 * ks + half)];
+      for (int fj = 0; fj < 4; ++fj) F.b[fj] = sb[kpos(128 * wn + 32 * fj + l32, 2 * ks + half)];
+    } else {
 #pragma unroll
-      for (int fj = 0; fj < 4; ++fj) bfr[fj] = lds[buf][1][swz(128 * wn + 32 * fj + l32, 2 * ks + half)];
-#pragma unroll
-      for (int fi = 0; fi < 4; ++fi)
-#pragma unroll
-        for (int fj = 0; fj < 4; ++fj) acc[fi][fj] = mfma32(bfr[fj], af[fi], acc[fi][fj]);
+      for (int fj = 0; fj < 4; ++fj) F.b[fj] = read_b_tr(sb, 128 * wn + 32 * fj, 16 * ks, lane);
     }
-    if (st + 1 < nsteps) store(buf ^ 1);
-    __syncthreads();
+  };
+  auto mma = [&](const Frags& F) {
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < 4; ++fj) acc[fi][fj] = mfma32(F.b[fj], F.a[fi], acc[fi][fj]);
+  };
+  // Wait until this wave's loads of step `need` have landed (loads of later
+  // steps, up to `last_issued`, may stay in flight), then meet the others.
+  auto sync_step = [&](int need, int last_issued) {
+    const int ahead = min(last_issued, nsteps - 1) - need;
+    if (ahead >= 3) wait_vm_barrier<3 * LPS>();
+    else if (ahead == 2) wait_vm_barrier<2 * LPS>();
+    else if (ahead == 1) wait_vm_barrier<LPS>();
+    else wait_vm_barrier<0>();
+  };
+
+  // Slice-1 MFMAs with the next refill's eight copies spread between them
+  // (one after every second MFMA): a copy whose issue has to wait for the
+  // address path then stalls behind matrix work already in flight.
+  auto mma_with_copies = [&](const Frags& F, int step) {
+    const uint16_t* src[8];
+    sources(min(step, nsteps - 1), src);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int fi = q >> 1;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int fj = 2 * (q & 1) + h;
+        acc[fi][fj] = mfma32(F.b[fj], F.a[fi], acc[fi][fj]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (step < nsteps) dma16(src[q], block(step, q));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Loads run NS-1 steps ahead.  At step st: read slice 1 of st, MFMAs of
+  // slice 0; wait for step st+1's tile; read slice 0 of st+1; MFMAs of slice
+  // 1 interleaved with the copies of step st+NS-1 into the stage of step
+  // st-1 (every wave finished reading it before this barrier).
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nsteps) issue(p);
+  Frags S0, S1;
+  if (nsteps > 0) {
+    sync_step(0, NS - 2);
+    read_slice(0, 0, S0);
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    read_slice(st, 1, S1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(S0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < nsteps) {
+      sync_step(st + 1, st + NS - 2);
+      read_slice(st + 1, 0, S0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma_with_copies(S1, st + NS - 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // acc[fi][fj][4gg+e] = C[m = 128wm + 32fi + l32][n = 128wn + 32fj + 8gg + 4half + e]

@@ -243,6 +243,7 @@ DeviceLayout device_layout(const PlanTables& p) {
   L.tiles = take(4 * p.tiles.size());
   L.ext_start = take(4 * p.ext_start.size());
   L.ext = take(4 * p.ext.size());
+  L.zero = take(256);  // a zero page: loads of rows that must read as zero point here
   L.table_bytes = off;
   const size_t esz = p.dtype == MLORA_BF16 ? 2 : 4;
   if (p.dtype == MLORA_BF16) {

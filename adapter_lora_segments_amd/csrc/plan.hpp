@@ -11,7 +11,7 @@
 
 namespace mlora {
 
-constexpr int kKStep = 64;       // K extent of one extension step
+constexpr int kKStep = 32;       // K extent of one extension step
 constexpr int kMinRankPad = 32;  // smallest padded rank (one MFMA tile edge)
 
 struct Opts {
@@ -55,7 +55,7 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
 struct DeviceLayout {
   // offsets (bytes) of each table inside the table blob
   size_t offsets, zoff, ranks, rpad, roff, ch_first, ch_count, nano, chunks, cpref, tiles,
-      ext_start, ext;
+      ext_start, ext, zero;
   size_t table_bytes;
   // offsets (bytes) of the work buffers inside the workspace
   size_t acat_t, dz, part_a, part_b;

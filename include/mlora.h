@@ -111,7 +111,7 @@ typedef struct mlora_plan_s *mlora_plan_t;
  *  6. Reduction chunks: pieces of KC_i rows; chunk c's partial sums sit at
  *     rank-row prefix cpref(c) = sum of r_pad over earlier chunks.
  *  7. GEMM row tiles of BM rows per group; each tile lists extension steps
- *     (adapter j, rows [lo,hi) of j in the tile, k0 = 0,64,..<r_pad(j)).
+ *     (adapter j, rows [lo,hi) of j in the tile, k0 = 0,32,..<r_pad(j)).
  * The copies of seg_offsets/ranks are the plan's; the caller's arrays may be
  * freed on return.  On error *out is left untouched.
  */

@@ -26,7 +26,7 @@ Rule (all integers; counts and indexes int32, offsets into tensors int64):
     walk order when count is 0 is still defined as the walk position).
  7. GEMM row tiles: per group, rows [o_{g_s}, o_{g_{s+1}}) cut into tiles of
     BM rows.  For each tile, its extension steps: for every adapter j
-    (ascending) whose rows meet the tile, for k0 = 0, 64, ... < r_pad(j): entry
+    (ascending) whose rows meet the tile, for k0 = 0, 32, ... < r_pad(j): entry
     (j, lo, hi, k0) with [lo, hi) the rows of j inside the tile.
 """
 from __future__ import annotations
@@ -35,7 +35,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-KSTEP = 64
+KSTEP = 32
 
 
 @dataclass

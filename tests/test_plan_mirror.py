@@ -66,7 +66,7 @@ def check_invariants(offsets, ranks, opts, p):
         for j in range(n):
             lo, hi = max(o[j], r0), min(o[j + 1], r0 + m)
             if lo < hi:
-                want += [(j, lo, hi, k0) for k0 in range(0, int(rpad[j]), 64)]
+                want += [(j, lo, hi, k0) for k0 in range(0, int(rpad[j]), 32)]
         got = [tuple(e) for e in p["ext"][p["tile_ext_start"][t]:p["tile_ext_start"][t + 1]]]
         assert got == want
     assert np.all(cover == 1)
