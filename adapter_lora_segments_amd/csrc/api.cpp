@@ -346,9 +346,20 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     });
   }
 
+  // A_cat^T feeds the shrink; with W0 as [d_out][d_in] the expand steps read
+  // B in k-contiguous form, B_cat^T.
   uint16_t* acat_t = reinterpret_cast<uint16_t*>(wsb + L.acat_t);
-  st = timed(p, MLORA_K_PREP, cs, [&] { mlora::launch_prep_acat_t(t, P.n, P.d_in, A, acat_t, cs); });
+  uint16_t* bcat_t = reinterpret_cast<uint16_t*>(wsb + L.bcat_t);
+  st = timed(p, MLORA_K_PREP, cs, [&] {
+    mlora::launch_prep_a(t, P.n, P.d_in, P.rpad_total, A, acat_t, nullptr, cs);
+  });
   if (st != MLORA_OK) return st;
+  if (nk) {
+    st = timed(p, MLORA_K_PREP, cs, [&] {
+      mlora::launch_prep_b(t, P.n, P.d_out, P.rpad_total, B, bcat_t, cs);
+    });
+    if (st != MLORA_OK) return st;
+  }
   st = fork_groups(p, cs);
   if (st != MLORA_OK) return st;
   for (int g = 0; g < P.n_groups; ++g) {
@@ -374,7 +385,9 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     ga.n_ntiles = (int32_t)((P.d_out + 255) / 256);
     ga.ebuf = (const uint16_t*)Z;
     ga.eb = B;
-    ga.acat_t = acat_t;
+    ga.ext_n = nullptr;
+    ga.ext_k = bcat_t;
+    ga.rtot = P.rpad_total;
     ga.t = t;
     st = timed(p, MLORA_K_GEMM_FWD, s, [&] { mlora::launch_gemm(true, nk, ga, s); });
     if (st != MLORA_OK) return st;
@@ -430,10 +443,16 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
   float* partA = reinterpret_cast<float*>(wsb + L.part_a);
   float* partB = reinterpret_cast<float*>(wsb + L.part_b);
   uint16_t* acat_t = reinterpret_cast<uint16_t*>(wsb + L.acat_t);
-  // A_cat^T feeds the dZ.A^T extension steps of the dX GEMM; rebuilt here so
-  // the backward does not depend on what the workspace held before.
+  uint16_t* acat = reinterpret_cast<uint16_t*>(wsb + L.acat);
+  // The dZ.A^T extension steps of the dX GEMM read A in the layout of the
+  // main B operand: k-contiguous A_cat with W0 as [d_in][d_out], n-contiguous
+  // A_cat^T otherwise.  Rebuilt here so the backward does not depend on what
+  // the workspace held before.
   if (dX) {
-    st = timed(p, MLORA_K_PREP, cs, [&] { mlora::launch_prep_acat_t(t, P.n, P.d_in, A, acat_t, cs); });
+    st = timed(p, MLORA_K_PREP, cs, [&] {
+      mlora::launch_prep_a(t, P.n, P.d_in, P.rpad_total, A, nk ? acat_t : nullptr,
+                           nk ? nullptr : acat, cs);
+    });
     if (st != MLORA_OK) return st;
   }
   st = fork_groups(p, cs);
@@ -481,7 +500,9 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
       ga.n_ntiles = (int32_t)((P.d_in + 255) / 256);
       ga.ebuf = dZ;
       ga.eb = A;
-      ga.acat_t = acat_t;
+      ga.ext_n = acat_t;
+      ga.ext_k = acat;
+      ga.rtot = P.rpad_total;
       ga.t = t;
       st = timed(p, MLORA_K_GEMM_DX, s, [&] { mlora::launch_gemm(false, !nk, ga, s); });
       if (st != MLORA_OK) return st;

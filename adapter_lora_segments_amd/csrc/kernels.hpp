@@ -27,9 +27,13 @@ struct DevTables {
 
 // ---------------- bf16 path (MFMA) ----------------
 
-// A_cat^T [rpad_total][d_in]: row roff(j)+c holds column c of A_j (zero for c >= r_j).
-void launch_prep_acat_t(const DevTables& t, int32_t n, int64_t d_in, const void* const* A,
-                        uint16_t* acat_t, hipStream_t s);
+// Rank-padded concatenations (zero for r_j <= c < r_pad(j)):
+//   A_cat^T [rtot][d_in] (row roff(j)+c = column c of A_j), A_cat [d_in][rtot],
+//   B_cat^T [d_out][rtot] (column roff(j)+c = row c of B_j).  NULL skips an output.
+void launch_prep_a(const DevTables& t, int32_t n, int64_t d_in, int64_t rtot, const void* const* A,
+                   uint16_t* acat_t, uint16_t* acat, hipStream_t s);
+void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
+                   const void* const* B, uint16_t* bcat_t, hipStream_t s);
 
 // Skinny products over nano-batches: out rows of adapter j (r_pad(j) columns)
 //   mode 0 (shrink): Z'[t][c] = s_j sum_k X[t][k] A_cat^T[roff_j + c][k]
@@ -52,9 +56,12 @@ void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, 
                             void* const* dA, void* const* dB, int32_t max_rank, hipStream_t s);
 
 // C[row][n] = sum_k Aop[row][k] Bop[k][n] over K, then the extension steps of
-// each row tile: rows of adapter j times E_j (Z' or dZ) against EB_j.
-//   fwd: Aop = X, Bop = W0, E = Z', EB_j = B_j ([r_j][N], n contiguous)
-//   dx : Aop = dY, Bop = W0^T, E = dZ, EB_j = A_j^T = rows roff_j.. of A_cat^T
+// each row tile: rows of adapter j times E_j (Z' or dZ) against EB_j, read in
+// the same layout as the main B operand:
+//   fwd: Aop = X, Bop = W0, E = Z', EB_j = B_j: n-contiguous from B_j itself,
+//        k-contiguous from B_cat^T
+//   dx : Aop = dY, Bop = W0^T, E = dZ, EB_j = A_j^T: n-contiguous from rows
+//        roff_j.. of A_cat^T, k-contiguous from A_cat
 struct GemmArgs {
   const uint16_t* A;
   int64_t lda;
@@ -65,8 +72,10 @@ struct GemmArgs {
   int32_t K, N;
   int32_t tile_begin, n_mtiles, n_ntiles;
   const uint16_t* ebuf;     // Z' (fwd) or dZ (dx), plan layout
-  const void* const* eb;    // fwd: B_j pointers
-  const uint16_t* acat_t;   // dx: A_cat^T [rpad_total][N]
+  const void* const* eb;    // fwd, n-contiguous: B_j pointers
+  const uint16_t* ext_n;    // dx, n-contiguous: A_cat^T [rtot][N]
+  const uint16_t* ext_k;    // k-contiguous: [N][rtot] (B_cat^T fwd, A_cat dx)
+  int64_t rtot;             // sum of padded ranks
   DevTables t;
 };
 // main_b_kcontig: Bop element (k, n) at B[n*ldb + k] (else at B[k*ldb + n]).

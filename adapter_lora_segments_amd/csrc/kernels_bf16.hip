@@ -15,34 +15,75 @@
 namespace mlora {
 
 // ---------------------------------------------------------------------------
-// A_cat^T: row roff(j)+c, c < r_pad(j), holds column c of A_j (zero past r_j).
-// One workgroup per (64-row slab of A_j, adapter j).
+// Rank-padded concatenations of the adapters, rebuilt per call (A_i and B_i
+// change every training step):
+//   A_cat^T [rpad_total][d_in]: row roff(j)+c holds column c of A_j
+//   A_cat   [d_in][rpad_total]: column roff(j)+c holds column c of A_j
+//   B_cat^T [d_out][rpad_total]: column roff(j)+c holds row c of B_j
+// with zeros for r_j <= c < r_pad(j).  Either A output may be NULL.  One
+// workgroup per (64-row slab, adapter j), staged through LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_prep_acat_t(DevTables t, int32_t n, int64_t d_in,
-                                                     const void* const* A, uint16_t* acat_t) {
+__global__ __launch_bounds__(256) void k_prep_a(DevTables t, int32_t n, int64_t d_in,
+                                                int64_t rtot, const void* const* A,
+                                                uint16_t* acat_t, uint16_t* acat) {
   __shared__ uint16_t tile[64][258];
   const int64_t k0 = (int64_t)blockIdx.x * 64;
   for (int32_t j = blockIdx.y; j < n; j += gridDim.y) {
-    const int r = t.ranks[j], rp = t.rpad[j];
+    const int r = t.ranks[j], rp = t.rpad[j], ro = t.roff[j];
     const uint16_t* Aj = static_cast<const uint16_t*>(A[j]);
     for (int i = threadIdx.x; i < 64 * r; i += 256) {
       const int k = i / r, c = i - k * r;
       tile[k][c] = Aj[k0 * r + i];
     }
     __syncthreads();
-    uint16_t* dst = acat_t + (int64_t)t.roff[j] * d_in + k0;
-    for (int i = threadIdx.x; i < 64 * rp; i += 256) {
-      const int c = i >> 6, k = i & 63;
-      dst[(int64_t)c * d_in + k] = c < r ? tile[k][c] : (uint16_t)0;
+    if (acat_t) {
+      uint16_t* dst = acat_t + (int64_t)ro * d_in + k0;
+      for (int i = threadIdx.x; i < 64 * rp; i += 256) {
+        const int c = i >> 6, k = i & 63;
+        dst[(int64_t)c * d_in + k] = c < r ? tile[k][c] : (uint16_t)0;
+      }
+    }
+    if (acat) {
+      for (int i = threadIdx.x; i < 64 * rp; i += 256) {
+        const int k = i / rp, c = i - k * rp;
+        acat[(k0 + k) * rtot + ro + c] = c < r ? tile[k][c] : (uint16_t)0;
+      }
     }
     __syncthreads();
   }
 }
 
-void launch_prep_acat_t(const DevTables& t, int32_t n, int64_t d_in, const void* const* A,
-                        uint16_t* acat_t, hipStream_t s) {
+__global__ __launch_bounds__(256) void k_prep_b(DevTables t, int32_t n, int64_t d_out,
+                                                int64_t rtot, const void* const* B,
+                                                uint16_t* bcat_t) {
+  __shared__ uint16_t tile[256][66];
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  for (int32_t j = blockIdx.y; j < n; j += gridDim.y) {
+    const int r = t.ranks[j], rp = t.rpad[j], ro = t.roff[j];
+    const uint16_t* Bj = static_cast<const uint16_t*>(B[j]);
+    for (int i = threadIdx.x; i < 64 * r; i += 256) {
+      const int c = i >> 6, nn = i & 63;
+      tile[c][nn] = Bj[(int64_t)c * d_out + n0 + nn];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * rp; i += 256) {
+      const int nn = i / rp, c = i - nn * rp;
+      bcat_t[(n0 + nn) * rtot + ro + c] = c < r ? tile[c][nn] : (uint16_t)0;
+    }
+    __syncthreads();
+  }
+}
+
+void launch_prep_a(const DevTables& t, int32_t n, int64_t d_in, int64_t rtot, const void* const* A,
+                   uint16_t* acat_t, uint16_t* acat, hipStream_t s) {
   dim3 grid((unsigned)(d_in / 64), (unsigned)(n < 65535 ? n : 65535));
-  hipLaunchKernelGGL(k_prep_acat_t, grid, dim3(256), 0, s, t, n, d_in, A, acat_t);
+  hipLaunchKernelGGL(k_prep_a, grid, dim3(256), 0, s, t, n, d_in, rtot, A, acat_t, acat);
+}
+
+void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
+                   const void* const* B, uint16_t* bcat_t, hipStream_t s) {
+  dim3 grid((unsigned)(d_out / 64), (unsigned)(n < 65535 ? n : 65535));
+  hipLaunchKernelGGL(k_prep_b, grid, dim3(256), 0, s, t, n, d_out, rtot, B, bcat_t);
 }
 
 // ---------------------------------------------------------------------------
@@ -400,6 +441,8 @@ __device__ __forceinline__ void wait_vm_barrier() {
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
   else static_assert(N == 0, "unsupported wait count");
 }
 
@@ -436,10 +479,18 @@ __device__ __forceinline__ u32x4 read_b_tr(const u32x4* tile, int nb, int kb, in
   return out;
 }
 
-template <bool FWD, bool MAIN_B_KC>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
+// NW waves (4 or 8) share one 256x256 output tile, two along M and NW/2
+// along N; each wave owns 128 rows x (512/NW) columns of accumulators.  With
+// eight waves two share each SIMD, so one wave's MFMAs run while the other
+// waits on an LDS read or a copy issue.
+template <bool FWD, bool MAIN_B_KC, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
   constexpr int NS = 5;                    // ring stages (loads run NS-1 steps ahead)
-  constexpr int LPS = 8;                   // direct loads per wave per stage
+  constexpr int WN = NW / 2;               // waves along N
+  constexpr int FI = 4;                    // 32-row fragments per wave
+  constexpr int FJ = 8 / WN;               // 32-column fragments per wave
+  constexpr int BPW = 16 / NW;             // 1 KiB blocks per operand per wave per stage
+  constexpr int LPS = 2 * BPW;             // direct loads per wave per stage
   __shared__ u32x4 ring[NS][2][1024];      // [stage][A/B][16 KiB]
 
   // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
@@ -462,25 +513,27 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   const int nk = g.K / 32;
   const int nsteps = nk + (e1 - e0);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
+  const int wrow = 128 * wm, wcol = (256 / WN) * wn;
 
-  // This lane's rows/chunks in the four k-contiguous and the four
-  // n-contiguous 1 KiB blocks it loads per stage (block index q = 4w + i).
-  int kr_row[4], kr_chunk[4], nc_krow[4], nc_chunk[4];
+  // This lane's rows/chunks in its k-contiguous and n-contiguous 1 KiB
+  // blocks of a stage (block index qb = BPW w + i).
+  int kr_row[BPW], kr_chunk[BPW], nc_krow[BPW], nc_chunk[BPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qb = 4 * w + i;
+  for (int i = 0; i < BPW; ++i) {
+    const int qb = BPW * w + i;
     kr_row[i] = 16 * qb + (lane >> 2);
     kr_chunk[i] = (lane & 3) ^ ((kr_row[i] >> 1) & 3);
     nc_krow[i] = 2 * qb + (lane >> 5);
     nc_chunk[i] = (lane & 31) ^ (2 * (nc_krow[i] & 3));
   }
-  const uint16_t* aptr[4];
-  const uint16_t* bptr[4];
+  const uint16_t* aptr[BPW];
+  const uint16_t* bptr[BPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < BPW; ++i) {
     aptr[i] = g.A + (int64_t)(row0 + min(kr_row[i], mrows - 1)) * g.lda + 8 * kr_chunk[i];
     if (MAIN_B_KC)
       bptr[i] = g.B + (int64_t)min(n0 + kr_row[i], g.N - 1) * g.ldb + 8 * kr_chunk[i];
@@ -488,16 +541,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
       bptr[i] = g.B + (int64_t)nc_krow[i] * g.ldb + min(n0 + 8 * nc_chunk[i], g.N - 8);
   }
 
-  // Global sources of this lane's eight 1 KiB blocks of step `step` (four of
-  // the A tile, four of the B tile); rows that must read as zero point at the
-  // zero page.
-  auto sources = [&](int step, const uint16_t* (&src)[8]) {
+  // Global sources of this lane's blocks of step `step` (BPW of the A tile,
+  // then BPW of the B tile); rows that must read as zero point at the zero
+  // page.
+  auto sources = [&](int step, const uint16_t* (&src)[LPS]) {
     if (step < nk) {
       const int k0 = step * 32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) src[i] = aptr[i] + k0;
+      for (int i = 0; i < BPW; ++i) src[i] = aptr[i] + k0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) src[4 + i] = MAIN_B_KC ? bptr[i] + k0 : bptr[i] + (int64_t)k0 * g.ldb;
+      for (int i = 0; i < BPW; ++i)
+        src[BPW + i] = MAIN_B_KC ? bptr[i] + k0 : bptr[i] + (int64_t)k0 * g.ldb;
     } else {
       const int e = e0 + step - nk;
       const int j = ldc(g.t.ext + 4 * e), lo = ldc(g.t.ext + 4 * e + 1), hi = ldc(g.t.ext + 4 * e + 2);
@@ -506,69 +560,76 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
       const int64_t oj = ldc(g.t.offsets + j);
       const uint16_t* zb = g.ebuf + ldc(g.t.zoff + j);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < BPW; ++i) {
         const int grow = row0 + kr_row[i];
         src[i] = (grow >= lo && grow < hi) ? zb + (int64_t)(grow - oj) * rp + k0 + 8 * kr_chunk[i]
                                            : g.t.zero;
       }
+      if (MAIN_B_KC) {
+        // k-contiguous [N][rtot] concatenation, padded columns already zero
+        const int64_t ro = ldc(g.t.roff + j);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = k0 + nc_krow[i];
-        const int col = min(n0 + 8 * nc_chunk[i], g.N - 8);
-        if (FWD) {
-          const int rj = ldc(g.t.ranks + j);
-          src[4 + i] = k < rj ? static_cast<const uint16_t*>(ldc(g.eb + j)) + (int64_t)k * g.N + col
-                              : g.t.zero;
-        } else {
-          src[4 + i] = g.acat_t + (int64_t)(ldc(g.t.roff + j) + k) * g.N + col;
+        for (int i = 0; i < BPW; ++i)
+          src[BPW + i] = g.ext_k + (int64_t)min(n0 + kr_row[i], g.N - 1) * g.rtot + ro + k0 + 8 * kr_chunk[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+          const int k = k0 + nc_krow[i];
+          const int col = min(n0 + 8 * nc_chunk[i], g.N - 8);
+          if (FWD) {
+            const int rj = ldc(g.t.ranks + j);
+            src[BPW + i] = k < rj ? static_cast<const uint16_t*>(ldc(g.eb + j)) + (int64_t)k * g.N + col
+                                  : g.t.zero;
+          } else {
+            src[BPW + i] = g.ext_n + (int64_t)(ldc(g.t.roff + j) + k) * g.N + col;
+          }
         }
       }
     }
   };
-  // Block i (0..7) of a stage: this wave's four A blocks, then its four B blocks.
+  // Block i of a stage for this wave: A blocks first, then B blocks.
   auto block = [&](int step, int i) -> u32x4* {
-    return ring[step % NS][i >> 2] + 64 * (4 * w + (i & 3));
+    return ring[step % NS][i / BPW] + 64 * (BPW * w + (i % BPW));
   };
   auto issue = [&](int step) {
-    const uint16_t* src[8];
+    const uint16_t* src[LPS];
     sources(step, src);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(src[i], block(step, i));
+    for (int i = 0; i < LPS; ++i) dma16(src[i], block(step, i));
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[FI][FJ];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < FI; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < FJ; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
   // Fragments of one 16-deep slice.  The pipeline runs at slice
   // granularity: the LDS reads of the next slice are in flight while the
-  // current slice's 16 MFMAs run from registers.
+  // current slice's MFMAs run from registers.
   struct Frags {
-    u32x4 a[4], b[4];
+    u32x4 a[FI], b[FJ];
   };
   auto read_slice = [&](int step, int ks, Frags& F) {
     const u32x4* sa = ring[step % NS][0];
     const u32x4* sb = ring[step % NS][1];
-    const bool b_kc = step < nk ? MAIN_B_KC : false;
 #pragma unroll
-    for (int fi = 0; fi < 4; ++fi) F.a[fi] = sa[kpos(128 * wm + 32 * fi + l32, 2 * ks + half)];
-    if (b_kc) {
+    for (int fi = 0; fi < FI; ++fi) F.a[fi] = sa[kpos(wrow + 32 * fi + l32, 2 * ks + half)];
+    if (MAIN_B_KC) {
 #pragma unroll
-      for (int fj = 0; fj < 4; ++fj) F.b[fj] = sb[kpos(128 * wn + 32 * fj + l32, 2 * ks + half)];
+      for (int fj = 0; fj < FJ; ++fj) F.b[fj] = sb[kpos(wcol + 32 * fj + l32, 2 * ks + half)];
     } else {
 #pragma unroll
-      for (int fj = 0; fj < 4; ++fj) F.b[fj] = read_b_tr(sb, 128 * wn + 32 * fj, 16 * ks, lane);
+      for (int fj = 0; fj < FJ; ++fj) F.b[fj] = read_b_tr(sb, wcol + 32 * fj, 16 * ks, lane);
     }
   };
   auto mma = [&](const Frags& F) {
 #pragma unroll
-    for (int fi = 0; fi < 4; ++fi)
+    for (int fi = 0; fi < FI; ++fi)
 #pragma unroll
-      for (int fj = 0; fj < 4; ++fj) acc[fi][fj] = mfma32(F.b[fj], F.a[fi], acc[fi][fj]);
+      for (int fj = 0; fj < FJ; ++fj) acc[fi][fj] = mfma32(F.b[fj], F.a[fi], acc[fi][fj]);
   };
   // Wait until this wave's loads of step `need` have landed (loads of later
   // steps, up to `last_issued`, may stay in flight), then meet the others.
@@ -580,18 +641,44 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     else wait_vm_barrier<0>();
   };
 
-  // Slice-1 MFMAs with the next refill's eight copies spread between them
-  // (one after every second MFMA): a copy whose issue has to wait for the
-  // address path then stalls behind matrix work already in flight.
+  // Slice-1 MFMAs with the next refill's copies spread evenly between them:
+  // a copy whose issue has to wait for the address path then stalls behind
+  // matrix work already in flight.
+  constexpr int MPC = FI * FJ / LPS;       // MFMAs per copy
+  // Sources of a main (not extension) step: address arithmetic only.
+  auto main_sources = [&](int step, const uint16_t* (&src)[LPS]) {
+    const int k0 = step * 32;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) src[i] = aptr[i] + k0;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)
+      src[BPW + i] = MAIN_B_KC ? bptr[i] + k0 : bptr[i] + (int64_t)k0 * g.ldb;
+  };
+  auto mma_with_main_copies = [&](const Frags& F, int step) {
+    const uint16_t* src[LPS];
+    main_sources(step, src);
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) {
+#pragma unroll
+      for (int h = 0; h < MPC; ++h) {
+        const int m = q * MPC + h;
+        const int fi = m / FJ, fj = m % FJ;
+        acc[fi][fj] = mfma32(F.b[fj], F.a[fi], acc[fi][fj]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dma16(src[q], block(step, q));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto mma_with_copies = [&](const Frags& F, int step) {
-    const uint16_t* src[8];
+    const uint16_t* src[LPS];
     sources(min(step, nsteps - 1), src);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int fi = q >> 1;
+    for (int q = 0; q < LPS; ++q) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int fj = 2 * (q & 1) + h;
+      for (int h = 0; h < MPC; ++h) {
+        const int m = q * MPC + h;
+        const int fi = m / FJ, fj = m % FJ;
         acc[fi][fj] = mfma32(F.b[fj], F.a[fi], acc[fi][fj]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -612,7 +699,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     sync_step(0, NS - 2);
     read_slice(0, 0, S0);
   }
-  for (int st = 0; st < nsteps; ++st) {
+  // Steady state: the step refilled is a main step, two later steps are in
+  // flight, no table lookups.  Kept free of extension-step code so the
+  // compiler can track each LDS read's wait precisely.
+  auto main_step = [&](int st) {
+    read_slice(st, 1, S1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(S0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_barrier<(NS - 3) * LPS>();
+    read_slice(st + 1, 0, S0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_with_main_copies(S1, st + NS - 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Unrolled: across a loop back-edge the compiler waits for every LDS read
+  // in flight, so only one step in UNR pays that wait.  (The transposing B
+  // path needs more address registers; four copies of it would spill.)
+  constexpr int UNR = MAIN_B_KC ? 4 : 2;
+  const int n_main = max(0, nk - (NS - 1));
+  int st = 0;
+  for (; st + UNR <= n_main; st += UNR) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) main_step(st + u);
+  }
+  for (; st < n_main; ++st) main_step(st);
+  // Tail: refills of extension steps, then the last steps' drain.
+  for (; st < nsteps; ++st) {
     read_slice(st, 1, S1);
     __builtin_amdgcn_sched_barrier(0);
     mma(S0);
@@ -626,17 +739,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // acc[fi][fj][4gg+e] = C[m = 128wm + 32fi + l32][n = 128wn + 32fj + 8gg + 4half + e]
+  // acc[fi][fj][4gg+e] = C[m = wrow + 32fi + l32][n = wcol + 32fj + 8gg + 4half + e]
 #pragma unroll
-  for (int fi = 0; fi < 4; ++fi) {
-    const int m = 128 * wm + 32 * fi + l32;
+  for (int fi = 0; fi < FI; ++fi) {
+    const int m = wrow + 32 * fi + l32;
     if (m < mrows) {
       uint16_t* crow = g.C + (int64_t)(row0 + m) * g.ldc;
 #pragma unroll
-      for (int fj = 0; fj < 4; ++fj) {
+      for (int fj = 0; fj < FJ; ++fj) {
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-          const int n = n0 + 128 * wn + 32 * fj + 8 * gg + 4 * half;
+          const int n = n0 + wcol + 32 * fj + 8 * gg + 4 * half;
           if (n < g.N) {
             u32x2 pk;
             pk[0] = pack_bf16x2(acc[fi][fj][4 * gg + 0], acc[fi][fj][4 * gg + 1]);
@@ -649,16 +762,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   }
 }
 
+#ifndef MLORA_GEMM_WAVES
+#define MLORA_GEMM_WAVES 8
+#endif
+
 void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s) {
+  constexpr int NW = MLORA_GEMM_WAVES;
   const int total = g.n_mtiles * g.n_ntiles;
   if (total <= 0) return;
-  dim3 grid((unsigned)total), block(256);
+  dim3 grid((unsigned)total), block(64 * NW);
   if (fwd) {
-    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<true, true>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((k_gemm<true, false>), grid, block, 0, s, g);
+    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<true, true, NW>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((k_gemm<true, false, NW>), grid, block, 0, s, g);
   } else {
-    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<false, true>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((k_gemm<false, false>), grid, block, 0, s, g);
+    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<false, true, NW>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((k_gemm<false, false, NW>), grid, block, 0, s, g);
   }
 }
 

@@ -248,8 +248,10 @@ DeviceLayout device_layout(const PlanTables& p) {
   const size_t esz = p.dtype == MLORA_BF16 ? 2 : 4;
   if (p.dtype == MLORA_BF16) {
     L.acat_t = take((size_t)p.rpad_total * (size_t)p.d_in * esz);
+    L.acat = take((size_t)p.rpad_total * (size_t)p.d_in * esz);
+    L.bcat_t = take((size_t)p.rpad_total * (size_t)p.d_out * esz);
   } else {
-    L.acat_t = off;
+    L.acat_t = L.acat = L.bcat_t = off;
   }
   L.dz = take((size_t)p.z_elems * esz);
   if (p.dtype == MLORA_BF16) {

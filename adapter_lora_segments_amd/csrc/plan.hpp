@@ -58,7 +58,7 @@ struct DeviceLayout {
       ext_start, ext, zero;
   size_t table_bytes;
   // offsets (bytes) of the work buffers inside the workspace
-  size_t acat_t, dz, part_a, part_b;
+  size_t acat_t, acat, bcat_t, dz, part_a, part_b;
   size_t workspace_bytes;
 };
 
