@@ -32,7 +32,7 @@ struct mlora_plan_s {
   mlora::DeviceLayout L;
   std::vector<uint8_t> blob;
   void* uploaded_ws = nullptr;
-  std::vector<std::vector<Range>> nano_b, chunk_b;  // per group: one range per padded rank
+  std::vector<std::vector<Range>> chunk_b;  // per group: one chunk range per padded rank
   std::vector<int32_t> group_max_rank;
   int32_t max_rank = 1;
   // internal streams (n_groups > 1) and fork/join events
@@ -206,11 +206,9 @@ mlora_status mlora_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
     p->L = mlora::device_layout(p->P);
     p->blob = mlora::table_blob(p->P, p->L);
     const int S = p->P.n_groups;
-    p->nano_b.resize(S);
     p->chunk_b.resize(S);
     p->group_max_rank.assign(S, 1);
     for (int g = 0; g < S; ++g) {
-      p->nano_b[g] = bucket_ranges(p->P.nano, 3, p->P.nano_start[g], p->P.nano_start[g + 1], p->P.rpad);
       p->chunk_b[g] = bucket_ranges(p->P.chunks, 3, p->P.chunk_start[g], p->P.chunk_start[g + 1], p->P.rpad);
       for (int32_t j = p->P.groups[g]; j < p->P.groups[g + 1]; ++j)
         p->group_max_rank[g] = std::max(p->group_max_rank[g], p->P.ranks[j]);
@@ -364,13 +362,11 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
   if (st != MLORA_OK) return st;
   for (int g = 0; g < P.n_groups; ++g) {
     hipStream_t s = P.n_groups > 1 ? p->streams[g] : cs;
-    for (const Range& r : p->nano_b[g]) {
-      st = timed(p, MLORA_K_SHRINK, s, [&] {
-        mlora::launch_skinny(0 | (r.rp << 8), t, r.begin, r.count, (const uint16_t*)X, P.d_in,
-                             acat_t, nullptr, scales, (uint16_t*)Z, s);
-      });
-      if (st != MLORA_OK) return st;
-    }
+    st = timed(p, MLORA_K_SHRINK, s, [&] {
+      mlora::launch_skinny(0, t, P.nano_start[g], P.nano_start[g + 1] - P.nano_start[g],
+                           (const uint16_t*)X, P.d_in, acat_t, nullptr, scales, (uint16_t*)Z, s);
+    });
+    if (st != MLORA_OK) return st;
     mlora::GemmArgs ga;
     ga.A = (const uint16_t*)X;
     ga.lda = P.d_in;
@@ -459,13 +455,11 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
   if (st != MLORA_OK) return st;
   for (int g = 0; g < P.n_groups; ++g) {
     hipStream_t s = P.n_groups > 1 ? p->streams[g] : cs;
-    for (const Range& r : p->nano_b[g]) {
-      st = timed(p, MLORA_K_DZ, s, [&] {
-        mlora::launch_skinny(1 | (r.rp << 8), t, r.begin, r.count, (const uint16_t*)dY, P.d_out,
-                             nullptr, B, scales, dZ, s);
-      });
-      if (st != MLORA_OK) return st;
-    }
+    st = timed(p, MLORA_K_DZ, s, [&] {
+      mlora::launch_skinny(1, t, P.nano_start[g], P.nano_start[g + 1] - P.nano_start[g],
+                           (const uint16_t*)dY, P.d_out, nullptr, B, scales, dZ, s);
+    });
+    if (st != MLORA_OK) return st;
     for (const Range& r : p->chunk_b[g]) {
       st = timed(p, MLORA_K_DB, s, [&] {
         mlora::launch_token_reduce(0 | (r.rp << 8), t, r.begin, r.count, (const uint16_t*)dY,

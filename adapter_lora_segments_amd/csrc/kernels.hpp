@@ -35,7 +35,8 @@ void launch_prep_a(const DevTables& t, int32_t n, int64_t d_in, int64_t rtot, co
 void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
                    const void* const* B, uint16_t* bcat_t, hipStream_t s);
 
-// Skinny products over nano-batches: out rows of adapter j (r_pad(j) columns)
+// Skinny products over nano-batches [nano_begin, nano_begin + nano_count) of
+// any padded ranks: out rows of adapter j (r_pad(j) columns)
 //   mode 0 (shrink): Z'[t][c] = s_j sum_k X[t][k] A_cat^T[roff_j + c][k]
 //   mode 1 (dZ)    : dZ[t][c] = s_j sum_k dY[t][k] B_j[c][k]
 void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nano_count,

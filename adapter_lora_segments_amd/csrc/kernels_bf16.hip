@@ -14,6 +14,30 @@
 
 namespace mlora {
 
+#define MLORA_LDS __attribute__((address_space(3)))
+
+// 16 bytes per lane from global memory straight into LDS: the wave's 64 lanes
+// fill the 1 KiB block at `blk` in lane order (lane i at byte 16 i).  Issued
+// as inline assembly (M0 = block address) so the compiler does not treat the
+// copy as an LDS store it must drain before every LDS read: the kernel's own
+// vmcnt waits and barriers order the ring (the asm still receives the ring's
+// address and clobbers memory, so LDS reads are never cached across it).
+__device__ __forceinline__ void dma16(const uint16_t* src, u32x4* blk) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(MLORA_LDS void*)blk);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// Wait until at most N direct-to-LDS loads of this wave are in flight, then
+// meet the other waves.  A bare s_barrier (no fence): the loads still in
+// flight target other ring stages and must not be drained here.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N <= 63, "vmcnt takes 0..63");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Rank-padded concatenations of the adapters, rebuilt per call (A_i and B_i
 // change every training step):
@@ -89,78 +113,138 @@ void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
 // ---------------------------------------------------------------------------
 // Skinny products over one nano-batch (<= nano_rows rows of one adapter):
 //   out[row][c] = s_j * sum_k P[row][k] * Q_j[c][k],  c < RP = r_pad(j)
-// Both operands are k-contiguous, so MFMA fragments load straight from
-// global memory (16 bytes per lane).  The four waves split K into quarters
-// and their accumulators are summed through LDS.  MODE 0: shrink (Q = rows
-// of A_cat^T, all RP rows present); MODE 1: dZ (Q = B_j, rows >= r_j are 0).
+// MODE 0: shrink (P = X, Q = rows of A_cat^T, all RP rows present);
+// MODE 1: dZ (P = dY, Q = B_j, rows >= r_j read as zeros).
+//
+// One workgroup of four waves per nano-batch, 32 rows at a time.  Both
+// operands are k-contiguous rows; a wave-wide load in MFMA fragment order
+// would give every lane a different row (64 separate cache accesses per
+// instruction), so each K-stage of 128 is copied straight into LDS instead,
+// 256 contiguous bytes per row (16 lanes per row), and the fragments are read
+// from LDS.  Stage layout: the 32 P rows then the RP Q rows, 16 chunks of 16
+// bytes per row, chunk c of row r at position c ^ (r & 15), so the 16 rows
+// one fragment read touches per 256-byte phase hit distinct banks.  A ring of
+// NS stages keeps NS-1 stages of copies in flight; each wave takes two of the
+// eight 16-deep k-steps of every stage, and the four partial accumulators are
+// summed through LDS in wave order.  One launch covers every padded-rank
+// bucket of a stream group: each workgroup switches on its adapter's r_pad.
 // ---------------------------------------------------------------------------
-template <int RP, int MODE>
-__global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin, const uint16_t* P,
-                                                int64_t K, const uint16_t* acat_t,
-                                                const void* const* Bptr, const float* scales,
-                                                uint16_t* out) {
-  constexpr int F = RP / 32;
-  constexpr int U = F <= 2 ? 8 : (F == 4 ? 4 : 2);
-  __shared__ float red[4][16 * 64];
+constexpr int kSkinnyKB = 128;                  // K per stage
+constexpr int kSkinnyNC = kSkinnyKB / 8;        // 16-byte chunks per row per stage
+constexpr int kSkinnyLdsEntries = 9216;         // 144 KiB of u32x4
 
-  const int nb = nano_begin + blockIdx.x;
-  const int j = t.nano[3 * nb], row0 = t.nano[3 * nb + 1], nrows = t.nano[3 * nb + 2];
-  const float s = scales[j];
-  const int64_t oj = t.offsets[j];
-  const int64_t zo = t.zoff[j];
-  const int rj = t.ranks[j];
-  const uint16_t* Q = MODE == 0 ? acat_t + (int64_t)t.roff[j] * K : static_cast<const uint16_t*>(Bptr[j]);
+template <int RP>
+struct SkinnyCfg {
+  static constexpr int ROWS = 32 + RP;                       // rows per stage
+  static constexpr int STAGE = ROWS * kSkinnyNC;             // u32x4 per stage
+  static constexpr int NS = RP == 32 ? 9 : (RP == 64 ? 6 : (RP == 128 ? 3 : 2));
+  static constexpr int LPS = ROWS / 16;                      // copies per wave per stage
+  static_assert(NS * STAGE <= kSkinnyLdsEntries, "ring exceeds LDS");
+  static_assert(4 * 16 * 64 / 4 <= NS * STAGE, "reduction area exceeds ring");
+  static_assert((NS - 2) * LPS <= 63, "vmcnt takes 0..63");
+};
+
+template <int RP, int MODE>
+__device__ __forceinline__ void skinny_body(const DevTables& t, int j, int row0, int nrows,
+                                            const uint16_t* P, int64_t K, const uint16_t* acat_t,
+                                            const void* const* Bptr, float s, uint16_t* out,
+                                            u32x4* ring) {
+  using C = SkinnyCfg<RP>;
+  constexpr int F = RP / 32, NS = C::NS, LPS = C::LPS;
+  const int64_t oj = ldc(t.offsets + j);
+  const int64_t zo = ldc(t.zoff + j);
+  const int rj = ldc(t.ranks + j);
+  const uint16_t* Q = MODE == 0 ? acat_t + (int64_t)ldc(t.roff + j) * K
+                                : static_cast<const uint16_t*>(ldc(Bptr + j));
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t kq = K / 4, kbeg = w * kq;
   const int half = lane >> 5, l32 = lane & 31;
-
-  const uint16_t* qp[F];
-  bool qv[F];
-#pragma unroll
-  for (int f = 0; f < F; ++f) {
-    const int c = 32 * f + l32;
-    qv[f] = MODE == 0 || c < rj;
-    qp[f] = Q + (int64_t)(qv[f] ? c : 0) * K + kbeg + 8 * half;
-  }
+  const int nks = (int)(K >> 4);                    // 16-deep k-steps
+  const int nst = (int)((K + kSkinnyKB - 1) / kSkinnyKB);
+  float* red = reinterpret_cast<float*>(ring);
 
   for (int rf = 0; rf * 32 < nrows; ++rf) {
-    const int prow = row0 + 32 * rf + min(l32, nrows - 32 * rf - 1);
-    const uint16_t* pp = P + (int64_t)prow * K + kbeg + 8 * half;
+    // vmcnt also counts the previous fragment's output stores: drain them so
+    // the ring waits below count copies only
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int frag_rows = min(32, nrows - 32 * rf);
+    // Copy q of this wave fills stage entries [64 m, 64 m + 64), m = w + 4 q:
+    // lane i -> row 4 m + i / 16, position i % 16, global chunk
+    // (i % 16) ^ (row & 15).  Rows past the operand read zeros (no advance).
+    const uint16_t* src[LPS];
+    bool adv[LPS];
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) {
+      const int m = w + 4 * q;
+      const int row = 4 * m + (lane >> 4);
+      const int gc = (lane & 15) ^ (row & 15);
+      if (row < 32) {
+        const int pr = row0 + 32 * rf + min(row, frag_rows - 1);
+        src[q] = P + (int64_t)pr * K + 8 * gc;
+        adv[q] = true;
+      } else {
+        const int c = row - 32;
+        adv[q] = MODE == 0 || c < rj;
+        src[q] = adv[q] ? Q + (int64_t)c * K + 8 * gc : t.zero + 8 * (lane & 15);
+      }
+    }
+    // Stages past the end repeat the last one (the ring slot is never read),
+    // so every wave issues the same number of copies per step.  A partial
+    // last stage reads its upper chunks from a clamped column, never used.
+    auto issue = [&](int stage) {
+      const int sc = min(stage, nst - 1);
+      u32x4* slot = ring + (stage % NS) * C::STAGE;
+#pragma unroll
+      for (int q = 0; q < LPS; ++q) {
+        const int m = w + 4 * q;
+        int64_t ko = (int64_t)sc * kSkinnyKB;
+        const uint16_t* p = src[q];
+        if (adv[q]) {
+          // clamp so a 64-wide tail stage never reads past column K
+          const int gc = (lane & 15) ^ ((4 * m + (lane >> 4)) & 15);
+          ko = min(ko, K - 8 - 8 * (int64_t)gc);
+          p += ko;
+        }
+        dma16(p, slot + 64 * m);
+      }
+    };
+
     f32x16 acc[F];
 #pragma unroll
     for (int f = 0; f < F; ++f)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[f][e] = 0.f;
 
-    int64_t k = 0;
-    for (; k + 16 * U <= kq; k += 16 * U) {
-      u32x4 pa[U], qa[U][F];
 #pragma unroll
-      for (int u = 0; u < U; ++u) pa[u] = ld16(pp + k + 16 * u);
+    for (int i = 0; i < NS - 1; ++i) issue(i);
+    for (int st = 0; st < nst; ++st) {
+      wait_vm_barrier<(NS - 2) * LPS>();
+      issue(st + NS - 1);
+      const u32x4* slot = ring + (st % NS) * C::STAGE;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ks = 2 * w + kk;
+        if (st * (kSkinnyKB / 16) + ks < nks) {
+          const int c = 2 * ks + half;
+          const int pos = c ^ (l32 & 15);
+          const u32x4 pa = slot[l32 * kSkinnyNC + pos];
 #pragma unroll
-        for (int f = 0; f < F; ++f) qa[u][f] = qv[f] ? ld16(qp[f] + k + 16 * u) : zero4();
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int f = 0; f < F; ++f) acc[f] = mfma32(qa[u][f], pa[u], acc[f]);
-    }
-    for (; k < kq; k += 16) {
-      const u32x4 pa = ld16(pp + k);
-#pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const u32x4 qa = qv[f] ? ld16(qp[f] + k) : zero4();
-        acc[f] = mfma32(qa, pa, acc[f]);
+          for (int f = 0; f < F; ++f) {
+            const u32x4 qa = slot[(32 + 32 * f + l32) * kSkinnyNC + pos];
+            acc[f] = mfma32(qa, pa, acc[f]);
+          }
+        }
       }
     }
+    // drain the trailing copies before the ring is reused for the reduction
+    wait_vm_barrier<0>();
 
-    // acc[f][4g+e] = D[c = 32f + 8g + 4*half + e][row = l32]
+    // acc[f][4g+e] = D[c = 32f + 8g + 4*half + e][row = l32]; thread (l, g)
+    // sums elements 4g..4g+3 of lane l over the four waves.
 #pragma unroll
     for (int f = 0; f < F; ++f) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) red[w][e * 64 + lane] = acc[f][e];
+      for (int e = 0; e < 16; ++e) red[(w * 16 + e) * 64 + lane] = acc[f][e];
       __syncthreads();
       {
         const int l = tid & 63, g = tid >> 6;
@@ -168,15 +252,16 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * g + i;
-          v[i] = red[0][e * 64 + l] + red[1][e * 64 + l] + red[2][e * 64 + l] + red[3][e * 64 + l];
+          v[i] = red[(0 * 16 + e) * 64 + l] + red[(1 * 16 + e) * 64 + l] +
+                 red[(2 * 16 + e) * 64 + l] + red[(3 * 16 + e) * 64 + l];
         }
-        const int row = 32 * rf + (l & 31);
-        if (row < nrows) {
+        const int row = l & 31;
+        if (row < frag_rows) {
           const int c = 32 * f + 8 * g + 4 * (l >> 5);
           u32x2 pk;
           pk[0] = pack_bf16x2(s * v[0], s * v[1]);
           pk[1] = pack_bf16x2(s * v[2], s * v[3]);
-          *reinterpret_cast<u32x2*>(out + zo + (int64_t)(row0 + row - oj) * RP + c) = pk;
+          *reinterpret_cast<u32x2*>(out + zo + (int64_t)(row0 + 32 * rf + row - oj) * RP + c) = pk;
         }
       }
       __syncthreads();
@@ -185,30 +270,31 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
 }
 
 template <int MODE>
-static void skinny_dispatch(int rp, const DevTables& t, int32_t nb0, int32_t cnt, const uint16_t* P,
-                            int64_t K, const uint16_t* acat_t, const void* const* Bptr,
-                            const float* scales, uint16_t* out, hipStream_t s) {
-  dim3 grid((unsigned)cnt), block(256);
-  switch (rp) {
-    case 32: hipLaunchKernelGGL((k_skinny<32, MODE>), grid, block, 0, s, t, nb0, P, K, acat_t, Bptr, scales, out); break;
-    case 64: hipLaunchKernelGGL((k_skinny<64, MODE>), grid, block, 0, s, t, nb0, P, K, acat_t, Bptr, scales, out); break;
-    case 128: hipLaunchKernelGGL((k_skinny<128, MODE>), grid, block, 0, s, t, nb0, P, K, acat_t, Bptr, scales, out); break;
-    default: hipLaunchKernelGGL((k_skinny<256, MODE>), grid, block, 0, s, t, nb0, P, K, acat_t, Bptr, scales, out); break;
+__global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin, const uint16_t* P,
+                                                int64_t K, const uint16_t* acat_t,
+                                                const void* const* Bptr, const float* scales,
+                                                uint16_t* out) {
+  __shared__ u32x4 ring[kSkinnyLdsEntries];
+  const int nb = nano_begin + blockIdx.x;
+  const int j = ldc(t.nano + 3 * nb), row0 = ldc(t.nano + 3 * nb + 1), nrows = ldc(t.nano + 3 * nb + 2);
+  const float s = ldc(scales + j);
+  switch (ldc(t.rpad + j)) {
+    case 32: skinny_body<32, MODE>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
+    case 64: skinny_body<64, MODE>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
+    case 128: skinny_body<128, MODE>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
+    default: skinny_body<256, MODE>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
   }
 }
 
-// One launch per padded-rank bucket: the caller passes a nano range whose
-// adapters share r_pad (the plan orders nano-batches by r_pad inside a group).
 void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nano_count,
                    const uint16_t* P, int64_t K, const uint16_t* acat_t, const void* const* Bptr,
                    const float* scales, uint16_t* out, hipStream_t s) {
-  // The bucket's padded rank is passed in the high bits of `mode`.
-  const int rp = mode >> 8;
   if (nano_count <= 0) return;
-  if ((mode & 0xff) == 0)
-    skinny_dispatch<0>(rp, t, nano_begin, nano_count, P, K, acat_t, Bptr, scales, out, s);
+  dim3 grid((unsigned)nano_count), block(256);
+  if (mode == 0)
+    hipLaunchKernelGGL(k_skinny<0>, grid, block, 0, s, t, nano_begin, P, K, acat_t, Bptr, scales, out);
   else
-    skinny_dispatch<1>(rp, t, nano_begin, nano_count, P, K, acat_t, Bptr, scales, out, s);
+    hipLaunchKernelGGL(k_skinny<1>, grid, block, 0, s, t, nano_begin, P, K, acat_t, Bptr, scales, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -417,35 +503,6 @@ void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, 
 // rows [lo,hi) of E_j (other rows zero) and k-rows [k0, k0+64) of EB_j
 // (rows >= r_j zero).  Output written as bf16.
 // ---------------------------------------------------------------------------
-#define MLORA_LDS __attribute__((address_space(3)))
-
-// 16 bytes per lane from global memory straight into LDS: the wave's 64 lanes
-// fill the 1 KiB block at `blk` in lane order (lane i at byte 16 i).  Issued
-// as inline assembly (M0 = block address) so the compiler does not treat the
-// copy as an LDS store it must drain before every LDS read: the kernel's own
-// vmcnt waits and barriers order the ring (the asm still receives the ring's
-// address and clobbers memory, so LDS reads are never cached across it).
-__device__ __forceinline__ void dma16(const uint16_t* src, u32x4* blk) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(MLORA_LDS void*)blk);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(src) : "memory", "m0");
-}
-
-// Wait until at most N direct-to-LDS loads of this wave are in flight, then
-// meet the other waves.  A bare s_barrier (no fence): the loads still in
-// flight target other ring stages and must not be drained here.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-  else static_assert(N == 0, "unsupported wait count");
-}
-
 // LDS tile layouts of one 32-deep K-step (16 KiB each):
 //  k-contiguous: 256 rows x 32 bf16 (four 16-byte chunks); chunk c of row r
 //    sits at position c ^ ((r >> 1) & 3), so the eight rows one MFMA fragment

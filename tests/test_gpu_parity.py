@@ -88,6 +88,16 @@ def test_bf16_scales_zero_and_negative():
     assert np.all(out["dB"][0] == 0.0) and np.all(out["dA"][0] == 0.0)
 
 
+@pytest.mark.parametrize("nano_rows", [64, 96])
+def test_bf16_long_nano_batches(nano_rows):
+    # nano-batches of several 32-row fragments, the last one partial; K with a
+    # 64-wide tail stage in both skinny products
+    w = custom_workload("bf16_nano", "bf16", 320, 192, [8, 128, 256, 32], [150, 70, 97, 33], seed=13)
+    say(f"case bf16 nano_rows {nano_rows}")
+    h, out = run_gpu(w, nano_rows=nano_rows)
+    compare(w, h, out, what=f"bf16_nano{nano_rows}")
+
+
 def test_bf16_small_chunks_many_partials():
     # tiny reduction chunks: many partial sums per adapter
     w = custom_workload("bf16_chunks", "bf16", 256, 256, [32, 64], [700, 333], seed=11)
