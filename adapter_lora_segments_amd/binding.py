@@ -38,6 +38,7 @@ class Plan:
         check(lib().mlora_plan(n, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in),
                                int(d_out), _lib.DTYPES[dtype], ctypes.byref(opts), ctypes.byref(h)))
+        self._L = lib()
         self._h = h
         inf = _lib.PlanInfo()
         check(lib().mlora_plan_get_info(h, ctypes.byref(inf)))
@@ -65,9 +66,12 @@ class Plan:
         return buf
 
     def __del__(self):
+        # The library handle is held by the plan itself: at interpreter exit
+        # the module globals lib() needs may already be gone.
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            lib().mlora_plan_destroy(h)
+        L = getattr(self, "_L", None)
+        if h is not None and h.value and L is not None:
+            L.mlora_plan_destroy(h)
             self._h = ctypes.c_void_p()
 
     # ---- device-side helpers (torch) ----

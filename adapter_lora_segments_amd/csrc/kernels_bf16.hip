@@ -497,21 +497,32 @@ void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, 
 
 // ---------------------------------------------------------------------------
 // Base GEMM with the LoRA term as extra K-steps (the expand of the forward,
-// PLoRA §9.2 Case 4's dZ.A^T in the backward).  256x256 tile per workgroup,
-// four waves of 128x128, 64-deep K-steps through double-buffered swizzled
-// LDS (128 KiB), one barrier per step.  Extension step e of a row tile loads
-// rows [lo,hi) of E_j (other rows zero) and k-rows [k0, k0+64) of EB_j
-// (rows >= r_j zero).  Output written as bf16.
+// PLoRA §9.2 Case 4's dZ.A^T in the backward).  256x256 tile per workgroup of
+// eight waves, 32-deep K-steps copied straight from global memory into a
+// five-stage LDS ring (160 KiB).  Extension step e of a row tile loads rows
+// [lo,hi) of E_j (other rows zero) and k-rows [k0, k0+32) of EB_j (rows >=
+// r_j zero).  Output written as bf16.
 // ---------------------------------------------------------------------------
-// LDS tile layouts of one 32-deep K-step (16 KiB each):
-//  k-contiguous: 256 rows x 32 bf16 (four 16-byte chunks); chunk c of row r
-//    sits at position c ^ ((r >> 1) & 3), so the eight rows one MFMA fragment
-//    read touches per 128-byte phase fall in distinct banks;
+// LDS tile layouts of one 32-deep K-step (16 KiB each).  LDS has 64 banks
+// of 4 bytes.  Measured on gfx950 (read timings of many layouts): a 16-byte
+// read is served in 16-lane groups that never mix the two half-waves and
+// split each half-wave by the parity of lane-index bits 2 and 4; an 8-byte
+// transposing read in 32-lane groups.  The layouts give every group distinct
+// banks:
+//  k-contiguous: 256 rows x 32 bf16 (four 16-byte chunks, one 64-byte row
+//    each, so a direct copy reads whole rows with four adjacent lanes); chunk
+//    c of row r sits at position c ^ ((r >> 2) & 3).  Within a read group the
+//    rows r and r ^ 16 never meet, so the sixteen rows of a group fill all
+//    sixteen 16-byte positions of a 256-byte bank line;
 //  n-contiguous: 32 k-rows x 256 bf16 (thirty-two chunks); chunk c of k-row
-//    kr sits at c ^ (2 (kr & 3)), so the four k-rows of one transposing
-//    read fall in distinct banks.
-__device__ __forceinline__ int kpos(int r, int c) { return r * 4 + (c ^ ((r >> 1) & 3)); }
-__device__ __forceinline__ int npos(int kr, int c) { return kr * 32 + (c ^ (2 * (kr & 3))); }
+//    kr sits at c ^ nx(kr), nx the XOR of 4, 8 and 9 over bits 0, 1 and 3 of
+//    kr, so the k-rows and chunks of one transposing read group are distinct.
+__device__ __forceinline__ int kx(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int kpos(int r, int c) { return r * 4 + (c ^ kx(r)); }
+__device__ __forceinline__ int nx(int kr) {
+  return ((kr & 1) ? 4 : 0) ^ ((kr & 2) ? 8 : 0) ^ ((kr & 8) ? 9 : 0);
+}
+__device__ __forceinline__ int npos(int kr, int c) { return kr * 32 + (c ^ nx(kr)); }
 
 // B fragment of a 32x32x16 MFMA from an n-contiguous tile: lane l needs
 // B[k = kb + 8 (l/32) + 0..7][n = nb + l%32].  ds_read_b64_tr_b16 hands lane i
@@ -536,13 +547,27 @@ __device__ __forceinline__ u32x4 read_b_tr(const u32x4* tile, int nb, int kb, in
   return out;
 }
 
-// NW waves (4 or 8) share one 256x256 output tile, two along M and NW/2
-// along N; each wave owns 128 rows x (512/NW) columns of accumulators.  With
-// eight waves two share each SIMD, so one wave's MFMAs run while the other
-// waits on an LDS read or a copy issue.
-template <bool FWD, bool MAIN_B_KC, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
-  constexpr int NS = 5;                    // ring stages (loads run NS-1 steps ahead)
+// Eight waves share one 256x256 output tile, two along M and four along N;
+// each wave owns 128 rows x 64 columns of accumulators.  Ping-pong schedule:
+// waves 0-3 (one per SIMD) and waves 4-7 alternate phases.  In every phase one wave per SIMD issues the
+// sixteen MFMAs of one 32-deep step from registers while its partner reads
+// the twelve fragments of its next step from LDS and issues its share of the
+// direct copies; a barrier ends each phase and the roles swap.  The matrix
+// cores are fed by one wave at a time, and the read latency, the copy issue
+// and most of the barrier cost hide behind the other wave's MFMAs.
+//
+// Phase 2k:   waves 0-3 read step k, waves 4-7 multiply step k-1;
+// phase 2k+1: waves 0-3 multiply step k, waves 4-7 read step k.
+// A barrier before phase 0 makes every wave's copies of step 0 visible.
+// Ring slot k is read in phases 2k and 2k+1, so it is refilled (with step
+// k + NS) from phase 2k+2 on: each wave issues its copies of step t+NS-1
+// while reading step t.  Copies past the last step repeat it into the slot
+// just freed (never read again), so every wave keeps the same count in flight
+// and every barrier waits for the same vmcnt.
+template <bool FWD, bool MAIN_B_KC>
+__global__ __launch_bounds__(512, 1) void k_gemm(GemmArgs g) {
+  constexpr int NW = 8;
+  constexpr int NS = 5;                    // ring stages
   constexpr int WN = NW / 2;               // waves along N
   constexpr int FI = 4;                    // 32-row fragments per wave
   constexpr int FJ = 8 / WN;               // 32-column fragments per wave
@@ -550,17 +575,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
   constexpr int LPS = 2 * BPW;             // direct loads per wave per stage
   __shared__ u32x4 ring[NS][2][1024];      // [stage][A/B][16 KiB]
 
-  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of logical tiles, grouped 8 row tiles at a time.
   const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7, q = bid >> 3, per = G >> 3, rem = G & 7;
   const int L = xcd * per + min(xcd, rem) + q;
   const int nM = g.n_mtiles, nN = g.n_ntiles;
   constexpr int GM = 8;
-  const int grp = L / (GM * nN);
-  const int fm = grp * GM;
+  const int grpm = L / (GM * nN);
+  const int fm = grpm * GM;
   const int gm = min(GM, nM - fm);
-  const int within = L - grp * GM * nN;
+  const int within = L - grpm * GM * nN;
   const int tm = fm + within % gm, tn = within / gm;
 
   const int tix = g.tile_begin + tm;
@@ -576,16 +599,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
   const int wm = w / WN, wn = w % WN;
   const int wrow = 128 * wm, wcol = (256 / WN) * wn;
 
-  // This lane's rows/chunks in its k-contiguous and n-contiguous 1 KiB
-  // blocks of a stage (block index qb = BPW w + i).
   int kr_row[BPW], kr_chunk[BPW], nc_krow[BPW], nc_chunk[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int qb = BPW * w + i;
     kr_row[i] = 16 * qb + (lane >> 2);
-    kr_chunk[i] = (lane & 3) ^ ((kr_row[i] >> 1) & 3);
+    kr_chunk[i] = (lane & 3) ^ kx(kr_row[i]);
     nc_krow[i] = 2 * qb + (lane >> 5);
-    nc_chunk[i] = (lane & 31) ^ (2 * (nc_krow[i] & 3));
+    nc_chunk[i] = (lane & 31) ^ nx(nc_krow[i]);
   }
   const uint16_t* aptr[BPW];
   const uint16_t* bptr[BPW];
@@ -623,7 +644,6 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
                                            : g.t.zero;
       }
       if (MAIN_B_KC) {
-        // k-contiguous [N][rtot] concatenation, padded columns already zero
         const int64_t ro = ldc(g.t.roff + j);
 #pragma unroll
         for (int i = 0; i < BPW; ++i)
@@ -644,15 +664,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
       }
     }
   };
-  // Block i of a stage for this wave: A blocks first, then B blocks.
-  auto block = [&](int step, int i) -> u32x4* {
-    return ring[step % NS][i / BPW] + 64 * (BPW * w + (i % BPW));
-  };
+  // Copies of step `step` into its ring slot; past the last step the source
+  // repeats the last step (the slot it fills is never read again).
   auto issue = [&](int step) {
     const uint16_t* src[LPS];
-    sources(step, src);
+    sources(min(step, nsteps - 1), src);
+    u32x4* slot = &ring[step % NS][0][0];
 #pragma unroll
-    for (int i = 0; i < LPS; ++i) dma16(src[i], block(step, i));
+    for (int i = 0; i < LPS; ++i)
+      dma16(src[i], slot + (i / BPW) * 1024 + 64 * (BPW * w + (i % BPW)));
   };
 
   f32x16 acc[FI][FJ];
@@ -663,138 +683,72 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  // Fragments of one 16-deep slice.  The pipeline runs at slice
-  // granularity: the LDS reads of the next slice are in flight while the
-  // current slice's MFMAs run from registers.
-  struct Frags {
-    u32x4 a[FI], b[FJ];
-  };
-  auto read_slice = [&](int step, int ks, Frags& F) {
+  // All fragments of one 32-deep step: two 16-deep slices.
+  u32x4 fa[2][FI], fb[2][FJ];
+  auto read_step = [&](int step) {
     const u32x4* sa = ring[step % NS][0];
     const u32x4* sb = ring[step % NS][1];
 #pragma unroll
-    for (int fi = 0; fi < FI; ++fi) F.a[fi] = sa[kpos(wrow + 32 * fi + l32, 2 * ks + half)];
-    if (MAIN_B_KC) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int fj = 0; fj < FJ; ++fj) F.b[fj] = sb[kpos(wcol + 32 * fj + l32, 2 * ks + half)];
-    } else {
+      for (int fi = 0; fi < FI; ++fi) fa[ks][fi] = sa[kpos(wrow + 32 * fi + l32, 2 * ks + half)];
+      if (MAIN_B_KC) {
 #pragma unroll
-      for (int fj = 0; fj < FJ; ++fj) F.b[fj] = read_b_tr(sb, wcol + 32 * fj, 16 * ks, lane);
-    }
-  };
-  auto mma = [&](const Frags& F) {
+        for (int fj = 0; fj < FJ; ++fj) fb[ks][fj] = sb[kpos(wcol + 32 * fj + l32, 2 * ks + half)];
+      } else {
 #pragma unroll
-    for (int fi = 0; fi < FI; ++fi)
-#pragma unroll
-      for (int fj = 0; fj < FJ; ++fj) acc[fi][fj] = mfma32(F.b[fj], F.a[fi], acc[fi][fj]);
-  };
-  // Wait until this wave's loads of step `need` have landed (loads of later
-  // steps, up to `last_issued`, may stay in flight), then meet the others.
-  auto sync_step = [&](int need, int last_issued) {
-    const int ahead = min(last_issued, nsteps - 1) - need;
-    if (ahead >= 3) wait_vm_barrier<3 * LPS>();
-    else if (ahead == 2) wait_vm_barrier<2 * LPS>();
-    else if (ahead == 1) wait_vm_barrier<LPS>();
-    else wait_vm_barrier<0>();
-  };
-
-  // Slice-1 MFMAs with the next refill's copies spread evenly between them:
-  // a copy whose issue has to wait for the address path then stalls behind
-  // matrix work already in flight.
-  constexpr int MPC = FI * FJ / LPS;       // MFMAs per copy
-  // Sources of a main (not extension) step: address arithmetic only.
-  auto main_sources = [&](int step, const uint16_t* (&src)[LPS]) {
-    const int k0 = step * 32;
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) src[i] = aptr[i] + k0;
-#pragma unroll
-    for (int i = 0; i < BPW; ++i)
-      src[BPW + i] = MAIN_B_KC ? bptr[i] + k0 : bptr[i] + (int64_t)k0 * g.ldb;
-  };
-  auto mma_with_main_copies = [&](const Frags& F, int step) {
-    const uint16_t* src[LPS];
-    main_sources(step, src);
-#pragma unroll
-    for (int q = 0; q < LPS; ++q) {
-#pragma unroll
-      for (int h = 0; h < MPC; ++h) {
-        const int m = q * MPC + h;
-        const int fi = m / FJ, fj = m % FJ;
-        acc[fi][fj] = mfma32(F.b[fj], F.a[fi], acc[fi][fj]);
+        for (int fj = 0; fj < FJ; ++fj) fb[ks][fj] = read_b_tr(sb, wcol + 32 * fj, 16 * ks, lane);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      dma16(src[q], block(step, q));
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto mma_with_copies = [&](const Frags& F, int step) {
-    const uint16_t* src[LPS];
-    sources(min(step, nsteps - 1), src);
+  auto mma_step = [&]() {
 #pragma unroll
-    for (int q = 0; q < LPS; ++q) {
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int h = 0; h < MPC; ++h) {
-        const int m = q * MPC + h;
-        const int fi = m / FJ, fj = m % FJ;
-        acc[fi][fj] = mfma32(F.b[fj], F.a[fi], acc[fi][fj]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (step < nsteps) dma16(src[q], block(step, q));
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int fi = 0; fi < FI; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < FJ; ++fj) acc[fi][fj] = mfma32(fb[ks][fj], fa[ks][fi], acc[fi][fj]);
   };
+  // End of a memory phase: the fragment reads have landed (so no copy can
+  // overwrite a slot still being read) and this wave's copies up to two
+  // steps ahead have landed; then meet the other waves.
+  auto end_mem_phase = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wait_vm_barrier<(NS - 2) * LPS>();
+  };
+  auto end_mma_phase = [&]() { wait_vm_barrier<(NS - 2) * LPS>(); };
 
-  // Loads run NS-1 steps ahead.  At step st: read slice 1 of st, MFMAs of
-  // slice 0; wait for step st+1's tile; read slice 0 of st+1; MFMAs of slice
-  // 1 interleaved with the copies of step st+NS-1 into the stage of step
-  // st-1 (every wave finished reading it before this barrier).
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nsteps) issue(p);
-  Frags S0, S1;
-  if (nsteps > 0) {
-    sync_step(0, NS - 2);
-    read_slice(0, 0, S0);
-  }
-  // Steady state: the step refilled is a main step, two later steps are in
-  // flight, no table lookups.  Kept free of extension-step code so the
-  // compiler can track each LDS read's wait precisely.
-  auto main_step = [&](int st) {
-    read_slice(st, 1, S1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(S0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm_barrier<(NS - 3) * LPS>();
-    read_slice(st + 1, 0, S0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_with_main_copies(S1, st + NS - 1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // Unrolled: across a loop back-edge the compiler waits for every LDS read
-  // in flight, so only one step in UNR pays that wait.  (The transposing B
-  // path needs more address registers; four copies of it would spill.)
-  constexpr int UNR = MAIN_B_KC ? 4 : 2;
-  const int n_main = max(0, nk - (NS - 1));
-  int st = 0;
-  for (; st + UNR <= n_main; st += UNR) {
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) main_step(st + u);
-  }
-  for (; st < n_main; ++st) main_step(st);
-  // Tail: refills of extension steps, then the last steps' drain.
-  for (; st < nsteps; ++st) {
-    read_slice(st, 1, S1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(S0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (st + 1 < nsteps) {
-      sync_step(st + 1, st + NS - 2);
-      read_slice(st + 1, 0, S0);
+  for (int p = 0; p < NS - 1; ++p) issue(p);
+  // every wave's copies of step 0 land before waves 0-3 read it in phase 0
+  wait_vm_barrier<(NS - 2) * LPS>();
+  if (w < 4) {
+    for (int k = 0; k < nsteps; ++k) {
+      read_step(k);
+      issue(k + NS - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      end_mem_phase();
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step();
+      __builtin_amdgcn_sched_barrier(0);
+      end_mma_phase();
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mma_with_copies(S1, st + NS - 1);
-    __builtin_amdgcn_sched_barrier(0);
+    end_mma_phase();
+  } else {
+    end_mma_phase();
+    for (int k = 0; k < nsteps; ++k) {
+      read_step(k);
+      issue(k + NS - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      end_mem_phase();
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step();
+      __builtin_amdgcn_sched_barrier(0);
+      end_mma_phase();
+    }
   }
+  // the repeated copies past the last step are still in flight
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // acc[fi][fj][4gg+e] = C[m = wrow + 32fi + l32][n = wcol + 32fj + 8gg + 4half + e]
 #pragma unroll
@@ -819,21 +773,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_gemm(GemmArgs g) {
   }
 }
 
-#ifndef MLORA_GEMM_WAVES
-#define MLORA_GEMM_WAVES 8
-#endif
-
 void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s) {
-  constexpr int NW = MLORA_GEMM_WAVES;
   const int total = g.n_mtiles * g.n_ntiles;
   if (total <= 0) return;
-  dim3 grid((unsigned)total), block(64 * NW);
+  dim3 grid((unsigned)total), block(512);
   if (fwd) {
-    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<true, true, NW>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((k_gemm<true, false, NW>), grid, block, 0, s, g);
+    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<true, true>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((k_gemm<true, false>), grid, block, 0, s, g);
   } else {
-    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<false, true, NW>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((k_gemm<false, false, NW>), grid, block, 0, s, g);
+    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<false, true>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((k_gemm<false, false>), grid, block, 0, s, g);
   }
 }
 
