@@ -19,7 +19,7 @@ TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chun
 TABLE_COLS = {"nb": 3, "chunks": 3, "tiles": 2, "ext": 4}
 TABLE_I64 = {"zoff", "offsets"}
 
-KERNELS = ["shrink", "gemm_fwd", "dz", "db", "da", "reduce", "gemm_dx", "prep"]
+KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep"]
 
 # every symbol include/mlora.h declares
 EXPORTS = ["mlora_plan", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",

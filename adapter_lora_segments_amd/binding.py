@@ -91,8 +91,18 @@ class Plan:
                                       ctypes.c_void_p(s.cuda_stream)))
         self._ws_uploaded = ws
 
-    def profile_enable(self, on: bool = True):
-        check(lib().mlora_profile_enable(self._h, 1 if on else 0))
+    def profile_enable(self, on=True):
+        """True: time every kernel kind; False: none; or an iterable of kind
+        names (``_lib.KERNELS``) to time only those."""
+        if on is True:
+            mask = -1
+        elif not on:
+            mask = 0
+        else:
+            mask = 0
+            for k in on:
+                mask |= 1 << _lib.KERNELS.index(k)
+        check(lib().mlora_profile_enable(self._h, mask))
 
     def profile_read(self) -> dict:
         n = len(_lib.KERNELS)

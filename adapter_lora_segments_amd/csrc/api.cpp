@@ -40,7 +40,7 @@ struct mlora_plan_s {
   std::vector<hipEvent_t> join_ev;
   hipEvent_t fork_ev = nullptr;
   // profiling
-  bool prof = false;
+  uint32_t prof = 0;  // bit k: bracket launches of kernel kind k
   struct Rec {
     int kind;
     hipEvent_t a, b;
@@ -92,7 +92,8 @@ mlora_status hip_fail(hipError_t e, const char* what) {
 template <class F>
 mlora_status timed(mlora_plan_s* p, int kind, hipStream_t s, F&& launch) {
   hipEvent_t a = nullptr, b = nullptr;
-  if (p->prof) {
+  const bool on = (p->prof >> kind) & 1u;
+  if (on) {
     for (hipEvent_t* e : {&a, &b}) {
       if (!p->pool.empty()) {
         *e = p->pool.back();
@@ -107,7 +108,7 @@ mlora_status timed(mlora_plan_s* p, int kind, hipStream_t s, F&& launch) {
   }
   launch();
   hipError_t err = hipGetLastError();
-  if (p->prof) {
+  if (on) {
     hipError_t e2 = hipEventRecord(b, s);
     p->recs.push_back({kind, a, b});
     if (err == hipSuccess && e2 != hipSuccess) return hip_fail(e2, "hipEventRecord");
@@ -419,11 +420,11 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
       mlora::launch_f32_dz(t, P.n, P.T, P.d_out, (const float*)dY, B, scales, dZ, cs);
     });
     if (st != MLORA_OK) return st;
-    st = timed(p, MLORA_K_DB, cs, [&] {
+    st = timed(p, MLORA_K_TOKEN_REDUCE, cs, [&] {
       mlora::launch_f32_db(t, P.n, P.d_out, (const float*)Z, (const float*)dY, dB, p->max_rank, cs);
     });
     if (st != MLORA_OK) return st;
-    st = timed(p, MLORA_K_DA, cs, [&] {
+    st = timed(p, MLORA_K_TOKEN_REDUCE, cs, [&] {
       mlora::launch_f32_da(t, P.n, P.d_in, (const float*)X, dZ, dA, p->max_rank, cs);
     });
     if (st != MLORA_OK) return st;
@@ -461,16 +462,10 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     });
     if (st != MLORA_OK) return st;
     for (const Range& r : p->chunk_b[g]) {
-      st = timed(p, MLORA_K_DB, s, [&] {
-        mlora::launch_token_reduce(0 | (r.rp << 8), t, r.begin, r.count, (const uint16_t*)dY,
-                                   P.d_out, (const uint16_t*)Z, partB, s);
-      });
-      if (st != MLORA_OK) return st;
-    }
-    for (const Range& r : p->chunk_b[g]) {
-      st = timed(p, MLORA_K_DA, s, [&] {
-        mlora::launch_token_reduce(1 | (r.rp << 8), t, r.begin, r.count, (const uint16_t*)X,
-                                   P.d_in, dZ, partA, s);
+      st = timed(p, MLORA_K_TOKEN_REDUCE, s, [&] {
+        mlora::launch_token_reduce(r.rp, t, r.begin, r.count, (const uint16_t*)dY,
+                                   (const uint16_t*)Z, partB, P.d_out, (const uint16_t*)X, dZ,
+                                   partA, P.d_in, s);
       });
       if (st != MLORA_OK) return st;
     }
@@ -505,9 +500,9 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
   return join_groups(p, cs);
 }
 
-mlora_status mlora_profile_enable(mlora_plan_t p, int32_t on) {
+mlora_status mlora_profile_enable(mlora_plan_t p, int32_t mask) {
   if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
-  p->prof = on != 0;
+  p->prof = (uint32_t)mask & ((1u << MLORA_K_COUNT) - 1u);
   return MLORA_OK;
 }
 

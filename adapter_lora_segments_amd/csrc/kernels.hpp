@@ -43,11 +43,14 @@ void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nan
                    const uint16_t* P, int64_t K, const uint16_t* acat_t, const void* const* Bptr,
                    const float* scales, uint16_t* out, hipStream_t s);
 
-// Token reductions over chunks, partial sums in fp32:
-//   mode 0 (dB): partB[cpref][c][n] = sum_t Z'[t][c] dY[t][n]       (n < d_out)
-//   mode 1 (dA): partA[cpref][d][c] = sum_t X[t][d] dZ[t][c]        (d < d_in)
-void launch_token_reduce(int mode, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
-                         const uint16_t* big, int64_t big_ld, const uint16_t* rk, float* part,
+// Token reductions over the chunks [chunk_begin, chunk_begin + chunk_count)
+// of one padded-rank bucket (r_pad = rp), both in one launch; partial sums in
+// fp32:
+//   dB: partB[cpref][c][n] = sum_t Z'[t][c] dY[t][n]       (n < d_out)
+//   dA: partA[cpref][d][c] = sum_t X[t][d] dZ[t][c]        (d < d_in)
+void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
+                         const uint16_t* dY, const uint16_t* Z, float* partB, int64_t d_out,
+                         const uint16_t* X, const uint16_t* dZ, float* partA, int64_t d_in,
                          hipStream_t s);
 
 // Fixed-order sum of the chunk partials into the caller's dA_j / dB_j

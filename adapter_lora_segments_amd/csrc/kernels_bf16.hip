@@ -300,67 +300,89 @@ void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nan
 // ---------------------------------------------------------------------------
 // Token reductions over one chunk (<= KC rows of one adapter) and one block of
 // 128 columns of the wide operand:
-//   MODE 0 (dB): part[c][n] = sum_t R[t][c] Wd[t][n]  (R = Z', Wd = dY)
-//   MODE 1 (dA): part[d][c] = sum_t Wd[t][d] R[t][c]  (R = dZ, Wd = X)
-// Both operands are token-major, so each 8x8 block is transposed in
-// registers on its way into k-contiguous, swizzled LDS tiles (double
-// buffered, one barrier per 64-token step).  Rows past the chunk are zero.
+//   dB item: part[c][n] = sum_t R[t][c] Wd[t][n]  (R = Z', Wd = dY)
+//   dA item: part[d][c] = sum_t Wd[t][d] R[t][c]  (R = dZ, Wd = X)
+// One launch per padded-rank bucket holds the dB items of the bucket's chunks
+// followed by their dA items.  Both operands are token-major, so each 8x8
+// block is transposed in registers on its way into k-contiguous, swizzled LDS
+// tiles (double buffered, one barrier per 64-token step).  The global loads
+// run two steps ahead in two register stages up to r_pad 64 (one above, to
+// keep the registers of two waves per SIMD); every load is issued, at a clamped
+// address, and rows past the chunk or columns past the operand are zeroed
+// after it, so the compiler's wait counts stay exact.
 // ---------------------------------------------------------------------------
+struct TokenReduceArgs {
+  DevTables t;
+  int32_t chunk_begin, n_chunks;
+  const uint16_t* dY;
+  const uint16_t* Z;
+  float* partB;
+  int64_t d_out;
+  const uint16_t* X;
+  const uint16_t* dZ;
+  float* partA;
+  int64_t d_in;
+};
+
 template <int RP, int MODE>
-__global__ __launch_bounds__(256) void k_token_reduce(DevTables t, int32_t chunk_begin, int32_t nbb,
-                                                      const uint16_t* big, int64_t big_ld,
-                                                      const uint16_t* rk, float* part) {
+__device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int ch, int col0,
+                                                  u32x4 (*sbig)[128 * 8], u32x4 (*srk)[RP * 8]) {
   constexpr int F = RP / 32;
   constexpr int NBLK = 128 + RP;                 // 8x8 blocks per 64-token step
   constexpr int PER = (NBLK + 255) / 256;        // blocks per thread
-  __shared__ u32x4 sbig[2][128 * 8];
-  __shared__ u32x4 srk[2][RP * 8];
-
-  const int ch = chunk_begin + blockIdx.x / nbb;
-  const int col0 = (blockIdx.x % nbb) * 128;
-  const int j = t.chunks[3 * ch], r0 = t.chunks[3 * ch + 1], nr = t.chunks[3 * ch + 2];
-  const int64_t cp = t.cpref[ch];
-  const uint16_t* rbase = rk + t.zoff[j] + (int64_t)(r0 - t.offsets[j]) * RP;
+  const uint16_t* big = MODE == 0 ? a.dY : a.X;
+  const int64_t big_ld = MODE == 0 ? a.d_out : a.d_in;
+  const uint16_t* rk = MODE == 0 ? a.Z : a.dZ;
+  float* part = MODE == 0 ? a.partB : a.partA;
+  const int j = ldc(a.t.chunks + 3 * ch), r0 = ldc(a.t.chunks + 3 * ch + 1), nr = ldc(a.t.chunks + 3 * ch + 2);
+  const int64_t cp = ldc(a.t.cpref + ch);
+  const uint16_t* rbase = rk + ldc(a.t.zoff + j) + (int64_t)(r0 - ldc(a.t.offsets + j)) * RP;
   const uint16_t* bbase = big + (int64_t)r0 * big_ld;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
 
-  u32x4 stage[PER][8];
-
-  auto load = [&](int step) {
+  // Block b of a step: b < 128 -> 8 tokens x 8 columns of the wide operand
+  // (column block mb = b % 16, token block kb = b / 16), else of the rank
+  // operand (mb = (b-128) % (RP/8), kb = (b-128) / (RP/8)).
+  // Threads past the last block (256*PER > NBLK) duplicate block b - NBLK:
+  // same loads, same values to the same LDS slots, and no branch around the
+  // loads (which would make the compiler drain every load in flight).
+  auto load = [&](int step, u32x4 (&stage)[PER][8]) {
     const int t0 = step * 64;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int b = tid + 256 * p;
-      if (b < NBLK) {
+      const int b = tid + 256 * p < NBLK ? tid + 256 * p : tid + 256 * p - NBLK;
+      {
+        const bool isbig = b < 128;
+        const int bb = isbig ? b : b - 128;
+        const int MB = isbig ? 16 : RP / 8;
+        const int mb = bb % MB, kb = bb / MB;
+        const int64_t col = isbig ? min((int64_t)(col0 + 8 * mb), big_ld - 8) : 8 * mb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tc = min(t0 + 8 * kb + i, nr - 1);
+          stage[p][i] = isbig ? ld16(bbase + (int64_t)tc * big_ld + col) : ld16(rbase + (int64_t)tc * RP + col);
+        }
+      }
+    }
+  };
+  // Rows past the chunk and columns past the operand are zeroed here, when
+  // the stage is consumed, not when it is loaded.
+  auto store = [&](int buf, int step, u32x4 (&stage)[PER][8]) {
+    const int t0 = step * 64;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int b = tid + 256 * p < NBLK ? tid + 256 * p : tid + 256 * p - NBLK;
+      {
         const bool isbig = b < 128;
         const int bb = isbig ? b : b - 128;
         const int MB = isbig ? 16 : RP / 8;
         const int mb = bb % MB, kb = bb / MB;
         const bool colok = !isbig || (col0 + 8 * mb < big_ld);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tk = t0 + 8 * kb + i;
-          if (tk < nr && colok) {
-            stage[p][i] = isbig ? ld16(bbase + (int64_t)tk * big_ld + col0 + 8 * mb)
-                                : ld16(rbase + (int64_t)tk * RP + 8 * mb);
-          } else {
-            stage[p][i] = zero4();
-          }
-        }
-      }
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int b = tid + 256 * p;
-      if (b < NBLK) {
-        const bool isbig = b < 128;
-        const int bb = isbig ? b : b - 128;
-        const int MB = isbig ? 16 : RP / 8;
-        const int mb = bb % MB, kb = bb / MB;
+        for (int i = 0; i < 8; ++i)
+          stage[p][i] = (t0 + 8 * kb + i < nr && colok) ? stage[p][i] : zero4();
         u32x4 tr[8];
         transpose8x8(stage[p], tr);
         u32x4* dst = isbig ? sbig[buf] : srk[buf];
@@ -375,14 +397,7 @@ __global__ __launch_bounds__(256) void k_token_reduce(DevTables t, int32_t chunk
   for (int f = 0; f < F; ++f)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[f][e] = 0.f;
-
-  const int steps = (nr + 63) / 64;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int st = 0; st < steps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < steps) load(st + 1);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const u32x4 bf = sbig[buf][swz(32 * w + l32, 2 * ks + half)];
@@ -395,8 +410,49 @@ __global__ __launch_bounds__(256) void k_token_reduce(DevTables t, int32_t chunk
           acc[f] = mfma32(rf, bf, acc[f]);  // D[c][d]
       }
     }
-    if (st + 1 < steps) store(buf ^ 1);
+  };
+
+  const int steps = (nr + 63) / 64;
+  if constexpr (RP <= 64) {
+    // Two register stages S0/S1.  Invariant at the loop top: LDS buffer 0
+    // holds step st, S1 holds (or is receiving) step st+1.
+    u32x4 S0[PER][8], S1[PER][8];
+    load(0, S0);
+    if (steps > 1) load(1, S1);
+    store(0, 0, S0);
     __syncthreads();
+    int st = 0;
+    for (; st + 3 < steps; st += 2) {
+      load(st + 2, S0);
+      compute(0);
+      store(1, st + 1, S1);
+      __syncthreads();
+      load(st + 3, S1);
+      compute(1);
+      store(0, st + 2, S0);
+      __syncthreads();
+    }
+    // at most three steps remain: st, st+1, st+2
+    if (st + 2 < steps) load(st + 2, S0);
+    compute(0);
+    if (st + 1 < steps) store(1, st + 1, S1);
+    __syncthreads();
+    if (st + 1 < steps) compute(1);
+    if (st + 2 < steps) store(0, st + 2, S0);
+    __syncthreads();
+    if (st + 2 < steps) compute(0);
+  } else {
+    u32x4 S0[PER][8];
+    load(0, S0);
+    store(0, 0, S0);
+    __syncthreads();
+    for (int st = 0; st < steps; ++st) {
+      const int buf = st & 1;
+      if (st + 1 < steps) load(st + 1, S0);
+      compute(buf);
+      if (st + 1 < steps) store(buf ^ 1, st + 1, S0);
+      __syncthreads();
+    }
   }
 
 #pragma unroll
@@ -425,29 +481,33 @@ __global__ __launch_bounds__(256) void k_token_reduce(DevTables t, int32_t chunk
   }
 }
 
-template <int MODE>
-static void token_reduce_dispatch(int rp, const DevTables& t, int32_t c0, int32_t cnt,
-                                  const uint16_t* big, int64_t big_ld, const uint16_t* rk,
-                                  float* part, hipStream_t s) {
-  const int nbb = (int)((big_ld + 127) / 128);
-  dim3 grid((unsigned)(cnt * nbb)), block(256);
-  switch (rp) {
-    case 32: hipLaunchKernelGGL((k_token_reduce<32, MODE>), grid, block, 0, s, t, c0, nbb, big, big_ld, rk, part); break;
-    case 64: hipLaunchKernelGGL((k_token_reduce<64, MODE>), grid, block, 0, s, t, c0, nbb, big, big_ld, rk, part); break;
-    case 128: hipLaunchKernelGGL((k_token_reduce<128, MODE>), grid, block, 0, s, t, c0, nbb, big, big_ld, rk, part); break;
-    default: hipLaunchKernelGGL((k_token_reduce<256, MODE>), grid, block, 0, s, t, c0, nbb, big, big_ld, rk, part); break;
-  }
+template <int RP>
+__global__ __launch_bounds__(256) void k_token_reduce(TokenReduceArgs a) {
+  __shared__ u32x4 sbig[2][128 * 8];
+  __shared__ u32x4 srk[2][RP * 8];
+  const int nbb_b = (int)((a.d_out + 127) / 128);
+  const int nbb_a = (int)((a.d_in + 127) / 128);
+  const int b = blockIdx.x, nb_b = a.n_chunks * nbb_b;
+  if (b < nb_b)
+    token_reduce_body<RP, 0>(a, a.chunk_begin + b / nbb_b, (b % nbb_b) * 128, sbig, srk);
+  else
+    token_reduce_body<RP, 1>(a, a.chunk_begin + (b - nb_b) / nbb_a, ((b - nb_b) % nbb_a) * 128, sbig, srk);
 }
 
-void launch_token_reduce(int mode, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
-                         const uint16_t* big, int64_t big_ld, const uint16_t* rk, float* part,
+void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
+                         const uint16_t* dY, const uint16_t* Z, float* partB, int64_t d_out,
+                         const uint16_t* X, const uint16_t* dZ, float* partA, int64_t d_in,
                          hipStream_t s) {
-  const int rp = mode >> 8;
   if (chunk_count <= 0) return;
-  if ((mode & 0xff) == 0)
-    token_reduce_dispatch<0>(rp, t, chunk_begin, chunk_count, big, big_ld, rk, part, s);
-  else
-    token_reduce_dispatch<1>(rp, t, chunk_begin, chunk_count, big, big_ld, rk, part, s);
+  TokenReduceArgs a{t, chunk_begin, chunk_count, dY, Z, partB, d_out, X, dZ, partA, d_in};
+  const int nbb_b = (int)((d_out + 127) / 128), nbb_a = (int)((d_in + 127) / 128);
+  dim3 grid((unsigned)(chunk_count * (nbb_b + nbb_a))), block(256);
+  switch (rp) {
+    case 32: hipLaunchKernelGGL((k_token_reduce<32>), grid, block, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_token_reduce<64>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((k_token_reduce<128>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_token_reduce<256>), grid, block, 0, s, a); break;
+  }
 }
 
 // ---------------------------------------------------------------------------

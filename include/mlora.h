@@ -202,22 +202,26 @@ mlora_status mlora_backward(mlora_plan_t plan, const void *dY, const void *X, co
                             const void *Z, void *dX, void *const *dA, void *const *dB,
                             void *workspace, size_t ws_bytes, void *stream);
 
-/* Per-kernel timing.  When enabled, every launch is bracketed by HIP events
- * on the stream it runs on; mlora_profile_read waits for them, adds their
- * durations to the totals of kernel `kind` and returns them, then clears. */
+/* Per-kernel timing.  Launches of the selected kinds are bracketed by HIP
+ * events on the stream they run on; mlora_profile_read waits for them, adds
+ * their durations to the totals of kernel `kind` and returns them, then
+ * clears.  Each pair of events costs a few microseconds of stream time, so a
+ * caller timing whole steps selects only the kernels it needs. */
 typedef enum {
-  MLORA_K_SHRINK = 0,
-  MLORA_K_GEMM_FWD,
-  MLORA_K_DZ,
-  MLORA_K_DB,
-  MLORA_K_DA,
-  MLORA_K_REDUCE,
-  MLORA_K_GEMM_DX,
-  MLORA_K_PREP,
+  MLORA_K_SHRINK = 0,    /* Z' = s X A (F1)                                  */
+  MLORA_K_GEMM_FWD,      /* Y = X W0 + Z' B (F2)                             */
+  MLORA_K_DZ,            /* dZ = s dY B^T (B1)                               */
+  MLORA_K_TOKEN_REDUCE,  /* chunk partials of dB (B2) and dA (B3), one launch */
+  MLORA_K_REDUCE,        /* fixed-order sum of the chunk partials            */
+  MLORA_K_GEMM_DX,       /* dX = dY W0^T + dZ A^T (B4)                       */
+  MLORA_K_PREP,          /* rank-padded concatenations of A and B            */
   MLORA_K_COUNT
 } mlora_kernel_kind;
 
-mlora_status mlora_profile_enable(mlora_plan_t plan, int32_t on);
+/* mask: bit k selects kind k (1 << MLORA_K_GEMM_FWD, ...); 0 disables
+ * timing; MLORA_PROFILE_ALL selects every kind. */
+#define MLORA_PROFILE_ALL (-1)
+mlora_status mlora_profile_enable(mlora_plan_t plan, int32_t mask);
 mlora_status mlora_profile_read(mlora_plan_t plan, double *total_ms /*[MLORA_K_COUNT]*/,
                                 int64_t *launches /*[MLORA_K_COUNT]*/);
 

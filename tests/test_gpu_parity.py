@@ -148,3 +148,27 @@ def test_llama7b_proj_full_size():
     say("case llama7b_proj full")
     h, out = run_gpu(w)
     compare(w, h, out, what="llama7b_proj")
+
+
+def test_profile_mask_selects_kernels():
+    import torch
+    w = custom_workload("prof", "bf16", 256, 256, [16, 64], [100, 140], seed=3)
+    say("case profile mask")
+    h, out = run_gpu(w)
+    layer, d = out["layer"], out["dev"]
+    plan = layer.plan
+    plan.profile_enable(["gemm_fwd"])
+    plan.profile_read()
+    layer.forward(d["X"])
+    layer.backward(d["dY"], d["X"])
+    torch.cuda.synchronize()
+    r = plan.profile_read()
+    assert r["gemm_fwd"][1] == plan.info["n_groups"] and r["gemm_fwd"][0] > 0.0
+    assert all(cnt == 0 for k, (ms, cnt) in r.items() if k != "gemm_fwd")
+    plan.profile_enable(True)
+    layer.forward(d["X"])
+    layer.backward(d["dY"], d["X"])
+    torch.cuda.synchronize()
+    r = plan.profile_read()
+    plan.profile_enable(False)
+    assert all(cnt > 0 for k, (ms, cnt) in r.items()), r
