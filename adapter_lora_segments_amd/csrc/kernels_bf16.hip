@@ -45,32 +45,42 @@ __device__ __forceinline__ void wait_vm_barrier() {
 //   A_cat   [d_in][rpad_total]: column roff(j)+c holds column c of A_j
 //   B_cat^T [d_out][rpad_total]: column roff(j)+c holds row c of B_j
 // with zeros for r_j <= c < r_pad(j).  Either A output may be NULL.  One
-// workgroup per (64-row slab, adapter j), staged through LDS.
+// workgroup per (64-row slab, adapter j): a slab of A_j ([64][r_j]) is one
+// contiguous, 128-byte-aligned block, and a slab of B_j ([r_j][64]) is r_j
+// 128-byte rows, so both arrive with 16-byte loads into LDS and leave
+// transposed or padded from there.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_prep_a(DevTables t, int32_t n, int64_t d_in,
                                                 int64_t rtot, const void* const* A,
                                                 uint16_t* acat_t, uint16_t* acat) {
-  __shared__ uint16_t tile[64][258];
+  __shared__ u32x4 tile4[64 * 256 / 8];          // [64][r] bf16, r <= 256
+  const uint16_t* tile = reinterpret_cast<const uint16_t*>(tile4);
   const int64_t k0 = (int64_t)blockIdx.x * 64;
   for (int32_t j = blockIdx.y; j < n; j += gridDim.y) {
-    const int r = t.ranks[j], rp = t.rpad[j], ro = t.roff[j];
-    const uint16_t* Aj = static_cast<const uint16_t*>(A[j]);
-    for (int i = threadIdx.x; i < 64 * r; i += 256) {
-      const int k = i / r, c = i - k * r;
-      tile[k][c] = Aj[k0 * r + i];
-    }
+    const int r = ldc(t.ranks + j), rp = ldc(t.rpad + j), ro = ldc(t.roff + j);
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(ldc(A + j)) + k0 * r);
+    const int nv = 8 * r;                          // 16-byte vectors in the slab
+    for (int i = threadIdx.x; i < nv; i += 256) tile4[i] = src[i];
     __syncthreads();
     if (acat_t) {
+      // eight consecutive k of one column c per thread: one 16-byte store
       uint16_t* dst = acat_t + (int64_t)ro * d_in + k0;
-      for (int i = threadIdx.x; i < 64 * rp; i += 256) {
-        const int c = i >> 6, k = i & 63;
-        dst[(int64_t)c * d_in + k] = c < r ? tile[k][c] : (uint16_t)0;
+      for (int i = threadIdx.x; i < rp * 8; i += 256) {
+        const int c = i >> 3, kb = (i & 7) * 8;
+        uint32_t wv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = c < r ? tile[(kb + 2 * q) * r + c] : 0u;
+          const uint32_t hi = c < r ? tile[(kb + 2 * q + 1) * r + c] : 0u;
+          wv[q] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(dst + (int64_t)c * d_in + kb) = u32x4{wv[0], wv[1], wv[2], wv[3]};
       }
     }
     if (acat) {
       for (int i = threadIdx.x; i < 64 * rp; i += 256) {
         const int k = i / rp, c = i - k * rp;
-        acat[(k0 + k) * rtot + ro + c] = c < r ? tile[k][c] : (uint16_t)0;
+        acat[(k0 + k) * rtot + ro + c] = c < r ? tile[k * r + c] : (uint16_t)0;
       }
     }
     __syncthreads();
@@ -80,19 +90,20 @@ __global__ __launch_bounds__(256) void k_prep_a(DevTables t, int32_t n, int64_t 
 __global__ __launch_bounds__(256) void k_prep_b(DevTables t, int32_t n, int64_t d_out,
                                                 int64_t rtot, const void* const* B,
                                                 uint16_t* bcat_t) {
-  __shared__ uint16_t tile[256][66];
+  __shared__ u32x4 tile4[256 * 8];               // [r][64] bf16, r <= 256
+  const uint16_t* tile = reinterpret_cast<const uint16_t*>(tile4);
   const int64_t n0 = (int64_t)blockIdx.x * 64;
   for (int32_t j = blockIdx.y; j < n; j += gridDim.y) {
-    const int r = t.ranks[j], rp = t.rpad[j], ro = t.roff[j];
-    const uint16_t* Bj = static_cast<const uint16_t*>(B[j]);
-    for (int i = threadIdx.x; i < 64 * r; i += 256) {
-      const int c = i >> 6, nn = i & 63;
-      tile[c][nn] = Bj[(int64_t)c * d_out + n0 + nn];
+    const int r = ldc(t.ranks + j), rp = ldc(t.rpad + j), ro = ldc(t.roff + j);
+    const uint16_t* Bj = static_cast<const uint16_t*>(ldc(B + j));
+    for (int i = threadIdx.x; i < 8 * r; i += 256) {
+      const int c = i >> 3, q = i & 7;
+      tile4[i] = *reinterpret_cast<const u32x4*>(Bj + (int64_t)c * d_out + n0 + 8 * q);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < 64 * rp; i += 256) {
       const int nn = i / rp, c = i - nn * rp;
-      bcat_t[(n0 + nn) * rtot + ro + c] = c < r ? tile[c][nn] : (uint16_t)0;
+      bcat_t[(n0 + nn) * rtot + ro + c] = c < r ? tile[c * 64 + nn] : (uint16_t)0;
     }
     __syncthreads();
   }
@@ -512,31 +523,37 @@ void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_
 
 // ---------------------------------------------------------------------------
 // Fixed-order sum of chunk partials: dA_j[d][c] and dB_j[c][n] for c < r_j.
-// grid.y walks adapters; each thread owns one output element.
+// grid.y walks adapters; each thread owns four consecutive partial columns
+// (c of one d for dA, n of one c for dB) and adds the adapter's chunks in
+// chunk order, so results do not depend on the launch shape.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_reduce_partials(DevTables t, int32_t a_begin, int32_t a_end,
                                                          int64_t d_in, int64_t d_out,
                                                          const float* partA, const float* partB,
                                                          void* const* dA, void* const* dB) {
   for (int32_t j = a_begin + blockIdx.y; j < a_end; j += gridDim.y) {
-    const int r = t.ranks[j], rp = t.rpad[j];
-    const int first = t.ch_first[j], cnt = t.ch_count[j];
-    const int64_t na = d_in * r, nbv = (int64_t)r * d_out;
-    float* gA = static_cast<float*>(dA[j]);
-    float* gB = static_cast<float*>(dB[j]);
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < na + nbv;
+    const int r = ldc(t.ranks + j), rp = ldc(t.rpad + j);
+    const int first = ldc(t.ch_first + j), cnt = ldc(t.ch_count + j);
+    const int64_t na4 = d_in * (rp / 4), nb4 = (int64_t)r * (d_out / 4);
+    float* gA = static_cast<float*>(ldc(dA + j));
+    float* gB = static_cast<float*>(ldc(dB + j));
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < na4 + nb4;
          i += (int64_t)gridDim.x * 256) {
-      float sum = 0.f;
-      if (i < na) {
-        const int64_t d = i / r;
-        const int c = (int)(i - d * r);
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+      if (i < na4) {
+        const int64_t d = i / (rp / 4);
+        const int c0 = 4 * (int)(i - d * (rp / 4));
+        if (c0 >= r) continue;
         for (int k = 0; k < cnt; ++k)
-          sum += partA[(int64_t)t.cpref[first + k] * d_in + d * rp + c];
-        gA[i] = sum;
+          sum += *reinterpret_cast<const f32x4*>(partA + (int64_t)ldc(t.cpref + first + k) * d_in + d * rp + c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c0 + e < r) gA[d * r + c0 + e] = sum[e];
       } else {
-        const int64_t q = i - na;
-        for (int k = 0; k < cnt; ++k) sum += partB[(int64_t)t.cpref[first + k] * d_out + q];
-        gB[q] = sum;
+        const int64_t q = 4 * (i - na4);
+        for (int k = 0; k < cnt; ++k)
+          sum += *reinterpret_cast<const f32x4*>(partB + (int64_t)ldc(t.cpref + first + k) * d_out + q);
+        *reinterpret_cast<f32x4*>(gB + q) = sum;
       }
     }
   }
@@ -547,7 +564,8 @@ void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, 
                             void* const* dA, void* const* dB, int32_t max_rank, hipStream_t s) {
   const int32_t na = a_end - a_begin;
   if (na <= 0) return;
-  int64_t per = (d_in + d_out) * (int64_t)max_rank;
+  const int64_t max_rp = max_rank <= 32 ? 32 : (max_rank <= 64 ? 64 : (max_rank <= 128 ? 128 : 256));
+  const int64_t per = (d_in * max_rp + (int64_t)max_rank * d_out) / 4;
   int64_t bx = (per + 255) / 256;
   if (bx > 1024) bx = 1024;
   dim3 grid((unsigned)bx, (unsigned)(na < 65535 ? na : 65535));
