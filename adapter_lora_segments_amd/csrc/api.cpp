@@ -39,6 +39,11 @@ struct mlora_plan_s {
   std::vector<hipStream_t> streams;
   std::vector<hipEvent_t> join_ev;
   hipEvent_t fork_ev = nullptr;
+  // per group: the stream of the weight-gradient branch of the backward
+  // (token reductions and partial sums, concurrent with the dX GEMM), and the
+  // events that fork it after dZ and join it back
+  std::vector<hipStream_t> wg_streams;
+  std::vector<hipEvent_t> dz_ev, wg_ev;
   // profiling
   uint32_t prof = 0;  // bit k: bracket launches of kernel kind k
   struct Rec {
@@ -137,6 +142,23 @@ mlora_status ensure_streams(mlora_plan_s* p) {
   return MLORA_OK;
 }
 
+mlora_status ensure_wg_streams(mlora_plan_s* p) {
+  const int S = p->P.n_groups;
+  for (int g = (int)p->wg_streams.size(); g < S; ++g) {
+    hipStream_t s;
+    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+    p->wg_streams.push_back(s);
+    for (auto* v : {&p->dz_ev, &p->wg_ev}) {
+      hipEvent_t ev;
+      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+      v->push_back(ev);
+    }
+  }
+  return MLORA_OK;
+}
+
 mlora_status fork_groups(mlora_plan_s* p, hipStream_t cs) {
   if (p->P.n_groups <= 1) return MLORA_OK;
   mlora_status st = ensure_streams(p);
@@ -228,6 +250,9 @@ void mlora_plan_destroy(mlora_plan_t p) {
   for (hipStream_t s : p->streams) (void)hipStreamDestroy(s);
   for (hipEvent_t e : p->join_ev) (void)hipEventDestroy(e);
   if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
+  for (hipStream_t s : p->wg_streams) (void)hipStreamDestroy(s);
+  for (hipEvent_t e : p->dz_ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->wg_ev) (void)hipEventDestroy(e);
   for (auto& r : p->recs) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
@@ -452,6 +477,10 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     });
     if (st != MLORA_OK) return st;
   }
+  if (dX) {
+    st = ensure_wg_streams(p);
+    if (st != MLORA_OK) return st;
+  }
   st = fork_groups(p, cs);
   if (st != MLORA_OK) return st;
   for (int g = 0; g < P.n_groups; ++g) {
@@ -461,17 +490,28 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
                            (const uint16_t*)dY, P.d_out, nullptr, B, scales, dZ, s);
     });
     if (st != MLORA_OK) return st;
+    // Weight gradients (token reductions, then the fixed-order partial sums)
+    // need dZ but not dX; with dX requested they run on a second stream so
+    // their workgroups fill the CUs the dX GEMM's last round of tiles leaves
+    // idle.
+    hipStream_t sw = s;
+    if (dX) {
+      sw = p->wg_streams[g];
+      hipError_t e = hipEventRecord(p->dz_ev[g], s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(sw, p->dz_ev[g], 0);
+      if (e != hipSuccess) return hip_fail(e, "fork of the weight-gradient stream");
+    }
     for (const Range& r : p->chunk_b[g]) {
-      st = timed(p, MLORA_K_TOKEN_REDUCE, s, [&] {
+      st = timed(p, MLORA_K_TOKEN_REDUCE, sw, [&] {
         mlora::launch_token_reduce(r.rp, t, r.begin, r.count, (const uint16_t*)dY,
                                    (const uint16_t*)Z, partB, P.d_out, (const uint16_t*)X, dZ,
-                                   partA, P.d_in, s);
+                                   partA, P.d_in, sw);
       });
       if (st != MLORA_OK) return st;
     }
-    st = timed(p, MLORA_K_REDUCE, s, [&] {
+    st = timed(p, MLORA_K_REDUCE, sw, [&] {
       mlora::launch_reduce_partials(t, P.groups[g], P.groups[g + 1], P.d_in, P.d_out, partA,
-                                    partB, dA, dB, p->group_max_rank[g], s);
+                                    partB, dA, dB, p->group_max_rank[g], sw);
     });
     if (st != MLORA_OK) return st;
     if (dX) {
@@ -495,6 +535,9 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
       ga.t = t;
       st = timed(p, MLORA_K_GEMM_DX, s, [&] { mlora::launch_gemm(false, !nk, ga, s); });
       if (st != MLORA_OK) return st;
+      hipError_t e = hipEventRecord(p->wg_ev[g], sw);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, p->wg_ev[g], 0);
+      if (e != hipSuccess) return hip_fail(e, "join of the weight-gradient stream");
     }
   }
   return join_groups(p, cs);

@@ -82,8 +82,8 @@ def cpu_baseline(w, proj, budget_s=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="llama7b_proj")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--streams", type=int, default=0)

@@ -45,8 +45,11 @@
  * Streams.  Work is enqueued on the caller's stream (a hipStream_t passed as
  * void*, NULL = the null stream) and the calls return without waiting.  With
  * n_streams > 1 the plan forks its adapter groups onto internal streams with
- * events and joins them back onto the caller's stream before returning, so
- * the caller sees ordinary single-stream ordering.
+ * events; a backward that computes dX also runs each group's weight
+ * gradients (dA, dB) on an internal stream of their own, concurrently with
+ * that group's dX GEMM.  Every internal stream is joined back onto the
+ * caller's stream before the call returns, so the caller sees ordinary
+ * single-stream ordering.
  *
  * Errors.  Every call validates its arguments on the host before launching
  * anything; on failure it returns a negative status, launches nothing and
