@@ -490,55 +490,60 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
                            (const uint16_t*)dY, P.d_out, nullptr, B, scales, dZ, s);
     });
     if (st != MLORA_OK) return st;
-    // Weight gradients (token reductions, then the fixed-order partial sums)
-    // need dZ but not dX; with dX requested they run on a second stream so
-    // their workgroups fill the CUs the dX GEMM's last round of tiles leaves
-    // idle.
-    hipStream_t sw = s;
-    if (dX) {
-      sw = p->wg_streams[g];
-      hipError_t e = hipEventRecord(p->dz_ev[g], s);
-      if (e == hipSuccess) e = hipStreamWaitEvent(sw, p->dz_ev[g], 0);
-      if (e != hipSuccess) return hip_fail(e, "fork of the weight-gradient stream");
-    }
-    for (const Range& r : p->chunk_b[g]) {
-      st = timed(p, MLORA_K_TOKEN_REDUCE, sw, [&] {
-        mlora::launch_token_reduce(r.rp, t, r.begin, r.count, (const uint16_t*)dY,
-                                   (const uint16_t*)Z, partB, P.d_out, (const uint16_t*)X, dZ,
-                                   partA, P.d_in, sw);
+    // Weight gradients: token reductions, then the fixed-order partial sums.
+    auto weight_grads = [&](hipStream_t sw) -> mlora_status {
+      for (const Range& r : p->chunk_b[g]) {
+        mlora_status s2 = timed(p, MLORA_K_TOKEN_REDUCE, sw, [&] {
+          mlora::launch_token_reduce(r.rp, t, r.begin, r.count, (const uint16_t*)dY,
+                                     (const uint16_t*)Z, partB, P.d_out, (const uint16_t*)X, dZ,
+                                     partA, P.d_in, sw);
+        });
+        if (s2 != MLORA_OK) return s2;
+      }
+      return timed(p, MLORA_K_REDUCE, sw, [&] {
+        mlora::launch_reduce_partials(t, P.groups[g], P.groups[g + 1], P.d_in, P.d_out, partA,
+                                      partB, dA, dB, p->group_max_rank[g], sw);
       });
+    };
+    if (!dX) {
+      st = weight_grads(s);
       if (st != MLORA_OK) return st;
+      continue;
     }
-    st = timed(p, MLORA_K_REDUCE, sw, [&] {
-      mlora::launch_reduce_partials(t, P.groups[g], P.groups[g + 1], P.d_in, P.d_out, partA,
-                                    partB, dA, dB, p->group_max_rank[g], sw);
-    });
+    // With dX requested, the weight gradients need dZ but not dX: they run on
+    // a second stream, enqueued after the dX GEMM so the GEMM's tiles take
+    // the chip first and the reductions fill the CUs its last round of tiles
+    // leaves idle.
+    hipStream_t sw = p->wg_streams[g];
+    hipError_t e = hipEventRecord(p->dz_ev[g], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    mlora::GemmArgs ga;
+    ga.A = (const uint16_t*)dY;
+    ga.lda = P.d_out;
+    ga.B = (const uint16_t*)W0;
+    ga.ldb = nk ? P.d_in : P.d_out;
+    ga.C = (uint16_t*)dX;
+    ga.ldc = P.d_in;
+    ga.K = (int32_t)P.d_out;
+    ga.N = (int32_t)P.d_in;
+    ga.tile_begin = P.tile_start[g];
+    ga.n_mtiles = P.tile_start[g + 1] - P.tile_start[g];
+    ga.n_ntiles = (int32_t)((P.d_in + 255) / 256);
+    ga.ebuf = dZ;
+    ga.eb = A;
+    ga.ext_n = acat_t;
+    ga.ext_k = acat;
+    ga.rtot = P.rpad_total;
+    ga.t = t;
+    st = timed(p, MLORA_K_GEMM_DX, s, [&] { mlora::launch_gemm(false, !nk, ga, s); });
     if (st != MLORA_OK) return st;
-    if (dX) {
-      mlora::GemmArgs ga;
-      ga.A = (const uint16_t*)dY;
-      ga.lda = P.d_out;
-      ga.B = (const uint16_t*)W0;
-      ga.ldb = nk ? P.d_in : P.d_out;
-      ga.C = (uint16_t*)dX;
-      ga.ldc = P.d_in;
-      ga.K = (int32_t)P.d_out;
-      ga.N = (int32_t)P.d_in;
-      ga.tile_begin = P.tile_start[g];
-      ga.n_mtiles = P.tile_start[g + 1] - P.tile_start[g];
-      ga.n_ntiles = (int32_t)((P.d_in + 255) / 256);
-      ga.ebuf = dZ;
-      ga.eb = A;
-      ga.ext_n = acat_t;
-      ga.ext_k = acat;
-      ga.rtot = P.rpad_total;
-      ga.t = t;
-      st = timed(p, MLORA_K_GEMM_DX, s, [&] { mlora::launch_gemm(false, !nk, ga, s); });
-      if (st != MLORA_OK) return st;
-      hipError_t e = hipEventRecord(p->wg_ev[g], sw);
-      if (e == hipSuccess) e = hipStreamWaitEvent(s, p->wg_ev[g], 0);
-      if (e != hipSuccess) return hip_fail(e, "join of the weight-gradient stream");
-    }
+    e = hipStreamWaitEvent(sw, p->dz_ev[g], 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    st = weight_grads(sw);
+    if (st != MLORA_OK) return st;
+    e = hipEventRecord(p->wg_ev[g], sw);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, p->wg_ev[g], 0);
+    if (e != hipSuccess) return hip_fail(e, "join of the weight-gradient stream");
   }
   return join_groups(p, cs);
 }
