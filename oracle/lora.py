@@ -107,26 +107,67 @@ def adapter_of_rows(offsets, rows):
     return np.searchsorted(o, np.asarray(rows, dtype=np.int64), side="right") - 1
 
 
-def sampled_rows(rows, X, W0, A, B, scales, offsets, dY=None, dtype="fp32"):
+def sampled_rows(rows, X, W0, A, B, scales, offsets, dY=None, dtype="fp32", with_z=False):
     """Y (and dX if dY is given) on the listed packed rows only, float64.
 
     Each row is computed from its own adapter exactly as in ``forward`` /
-    ``backward``; used to check full-size outputs one row at a time."""
+    ``backward``; used to check full-size outputs one row at a time.  With
+    ``with_z`` the scaled shrink s_i * x A_i of each row is returned as a
+    third value (a list of rank-length vectors)."""
     W = as_f64(W0, dtype)
     rows = np.asarray(rows, dtype=np.int64)
     own = adapter_of_rows(offsets, rows)
     Y = np.zeros((len(rows), W.shape[1]))
     dX = np.zeros((len(rows), W.shape[0])) if dY is not None else None
-    for k, (t, i) in enumerate(zip(rows, own)):
+    Zs = [None] * len(rows)
+    # rows of one adapter are stacked so each product is one matrix product
+    for i in np.unique(own):
+        ks = np.nonzero(own == i)[0]
         Ai = as_f64(A[i], dtype)
         Bi = as_f64(B[i], dtype)
         s = float(scales[i])
-        x = as_f64(X[t:t + 1], dtype)
-        Y[k] = (x @ W + s * ((x @ Ai) @ Bi))[0]
+        x = as_f64(np.asarray(X)[rows[ks]], dtype)
+        Y[ks] = x @ W + s * ((x @ Ai) @ Bi)
+        if with_z:
+            zi = s * (x @ Ai)
+            for q, k in enumerate(ks):
+                Zs[k] = zi[q]
         if dY is not None:
-            g = as_f64(dY[t:t + 1], dtype)
-            dX[k] = (g @ W.T + (s * (g @ Bi.T)) @ Ai.T)[0]
+            g = as_f64(np.asarray(dY)[rows[ks]], dtype)
+            dX[ks] = g @ W.T + (s * (g @ Bi.T)) @ Ai.T
+    if with_z:
+        return Y, dX, Zs
     return Y, dX
+
+
+def projected_grads(X, dY, A, B, scales, offsets, U, V, dtype="fp32", chunk=CHUNK):
+    """dA_i u_i and dB_i v_i for given vectors u_i (length r_i) and v_i
+    (length d_out), float64, without forming dA_i or dB_i.
+
+    From the definitions above, dA_i = s_i X_i^T dY_i B_i^T and
+    dB_i = s_i A_i^T X_i^T dY_i, so
+        dA_i u = s_i X_i^T (dY_i (B_i^T u)),   dB_i v = s_i A_i^T (X_i^T (dY_i v)),
+    each a chain of matrix-vector products over the adapter's rows.  A
+    random u, v turns a full-size gradient check into these products
+    (Freivalds' check).  Streams over row chunks."""
+    out_a, out_b = [], []
+    for i, (lo, hi) in enumerate(_segments(offsets)):
+        Ai = as_f64(A[i], dtype)
+        Bi = as_f64(B[i], dtype)
+        s = float(scales[i])
+        bu = Bi.T @ np.asarray(U[i], dtype=np.float64)          # d_out
+        v = np.asarray(V[i], dtype=np.float64)                  # d_out
+        ga = np.zeros(Ai.shape[0])                              # X_i^T (dY_i B_i^T u)
+        gb = np.zeros(Ai.shape[0])                              # X_i^T (dY_i v)
+        for r0 in range(lo, hi, chunk):
+            r1 = min(hi, r0 + chunk)
+            Xc = as_f64(X[r0:r1], dtype)
+            Gc = as_f64(dY[r0:r1], dtype)
+            ga += Xc.T @ (Gc @ bu)
+            gb += Xc.T @ (Gc @ v)
+        out_a.append(s * ga)
+        out_b.append(s * (Ai.T @ gb))
+    return out_a, out_b
 
 
 def max_rel_err(got, ref) -> float:

@@ -27,6 +27,11 @@ MUTATIONS = {
                         "        s = float(scales[i])\n        Zi"),
     "wrong_scale_index": ("s = float(scales[i])\n        Zi", "s = float(scales[0])\n        Zi"),
     "bf16_decode_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "proj_da_drop_scale": ("out_a.append(s * ga)", "out_a.append(ga)"),
+    "proj_db_wrong_vector": ("gb += Xc.T @ (Gc @ v)", "gb += Xc.T @ (Gc @ bu)"),
+    "proj_chunk_tail_lost": ("            r1 = min(hi, r0 + chunk)\n            Xc = as_f64(X[r0:r1], dtype)\n            Gc",
+                             "            r1 = min(hi - 1, r0 + chunk)\n            Xc = as_f64(X[r0:r1], dtype)\n            Gc"),
+    "sampled_z_no_scale": ("zi = s * (x @ Ai)", "zi = (x @ Ai)"),
 }
 
 
