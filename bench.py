@@ -59,9 +59,11 @@ def measured_traffic(workload: str):
     return int(v) if v else None
 
 
-def cpu_baseline(w, proj, budget_s=20.0):
-    """The oracle (numpy fp64) on the host, whole workload once, or a prefix of
-    the adapters if one pass would exceed the budget."""
+def cpu_baseline(w, projs, flop_budget=2.0e12):
+    """The oracle (numpy float64) on the host over a bounded sample of the
+    workload: the first M tokens of every timed projection, M chosen so the
+    sample is about ``flop_budget`` floating-point operations (10-30 s on a
+    host), or the whole workload when it is smaller."""
     from oracle import lora as ol
     from workloads.tensors import host_tensors
     try:
@@ -69,14 +71,19 @@ def cpu_baseline(w, proj, budget_s=20.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
     except Exception:
         threads = os.cpu_count()
-    h = host_tensors(w, proj)
-    t0 = time.perf_counter()
-    ol.forward(h["X"], h["W0"], h["A"], h["B"], h["scales"], h["offsets"], w.dtype)
-    ol.backward(h["dY"], h["X"], h["W0"], h["A"], h["B"], h["scales"], h["offsets"], w.dtype)
-    dt = time.perf_counter() - t0
-    return {"value": w.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full forward+backward of the workload ({w.T} tokens) in float64 numpy, "
-                      f"{dt:.2f} s"}
+    per_token = sum(4.0 * w.projections[q].d_in * w.projections[q].d_out for q in projs)
+    M = int(min(w.T, max(256, flop_budget // per_token)))
+    dt = 0.0
+    for q in projs:
+        h = host_tensors(w, q, rows=M)
+        t0 = time.perf_counter()
+        ol.forward(h["X"], h["W0"], h["A"], h["B"], h["scales"], h["offsets"], w.dtype)
+        ol.backward(h["dY"], h["X"], h["W0"], h["A"], h["B"], h["scales"], h["offsets"], w.dtype)
+        dt += time.perf_counter() - t0
+    what = "the whole workload" if M == w.T else f"the first {M} of {w.T} tokens"
+    return {"value": M / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one forward+backward of {what} over {len(projs)} projection(s) "
+                      f"in float64 numpy, {dt:.2f} s"}
 
 
 def main():
@@ -87,6 +94,9 @@ def main():
     ap.add_argument("--workload", default="llama7b_proj")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--streams", type=int, default=0)
+    ap.add_argument("--all-projections", action="store_true",
+                    help="time every projection of the workload in each step (tokens/s per layer "
+                         "= T / the summed forward+backward time); default: the first projection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one elementwise copy kernel (torch.neg on float32) reading and "
@@ -107,20 +117,37 @@ def main():
     torch.cuda.set_device(0)
     device_check()
     w = load_workload(a.workload, a.seed)
-    proj = 0
-    p = w.projections[proj]
+    projs = list(range(len(w.projections))) if a.all_projections else [0]
     SETS = 4
-    d = device_tensors(w, proj, sets=SETS)
-    plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16",
-                n_streams=a.streams or w.n_streams)
-    layer = PackedLoRALinear(plan, d["W0"], d["A"], d["B"], d["scales"])
-    Ys = [torch.empty((w.T, p.d_out), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
-    dXs = [torch.empty((w.T, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
+    layers = []
+    for q in projs:
+        p = w.projections[q]
+        d = device_tensors(w, q, sets=SETS)
+        plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16",
+                    n_streams=a.streams or w.n_streams)
+        layer = PackedLoRALinear(plan, d["W0"], d["A"], d["B"], d["scales"])
+        Ys = [torch.empty((w.T, p.d_out), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
+        dXs = [torch.empty((w.T, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
+        layers.append((plan, layer, d, Ys, dXs))
 
     def step(i):
         k = i % SETS
-        layer.forward(d["X"][k], Ys[k])
-        layer.backward(d["dY"][k], d["X"][k], dXs[k])
+        for plan, layer, d, Ys, dXs in layers:
+            layer.forward(d["X"][k], Ys[k])
+            layer.backward(d["dY"][k], d["X"][k], dXs[k])
+
+    def profile(kinds):
+        for plan, *_ in layers:
+            plan.profile_enable(kinds)
+            plan.profile_read()  # clear
+
+    def collect():
+        tot = {}
+        for plan, *_ in layers:
+            for k, (ms, n) in plan.profile_read().items():
+                m0, n0 = tot.get(k, (0.0, 0))
+                tot[k] = (m0 + ms, n0 + n)
+        return tot
 
     if a.calib_copy_mb:
         nel = a.calib_copy_mb * (1 << 20) // 4
@@ -133,37 +160,40 @@ def main():
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
-    # Timed region: whole steps, with only the forward GEMM bracketed by
-    # events (its duration feeds the roofline); every other launch runs
-    # back to back, as in training.
+    # Timed region: whole steps, with only the forward GEMM of the first
+    # projection bracketed by events (its duration feeds the roofline); every
+    # other launch runs back to back, as in training.
     prof = not a.no_profile
-    plan.profile_enable(["gemm_fwd"] if prof else False)
-    if prof:
-        plan.profile_read()  # clear
+    for j, (plan, *_) in enumerate(layers):
+        plan.profile_enable(["gemm_fwd"] if prof and j == 0 else False)
+        plan.profile_read()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
         step(i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    gemm_rec = plan.profile_read()["gemm_fwd"] if prof else (0.0, 0)
+    gemm_rec = layers[0][0].profile_read()["gemm_fwd"] if prof else (0.0, 0)
     # Per-kernel breakdown from a separate pass with every launch bracketed
-    # (the events themselves lengthen that pass's steps).
+    # (the events themselves lengthen that pass's steps; kernels that run
+    # concurrently on two streams include each other's time).
     kern = {}
     if prof:
         nb = max(3, min(a.steps, 10))
-        plan.profile_enable(True)
-        plan.profile_read()
+        profile(True)
         for i in range(nb):
             step(i)
         torch.cuda.synchronize()
-        kern = {k: (v[0] / nb * a.steps, v[1]) for k, v in plan.profile_read().items()}
-        plan.profile_enable(False)
+        kern = {k: (v[0] / nb * a.steps, v[1]) for k, v in collect().items()}
+        profile(False)
 
     ms = el / a.steps * 1e3
     tok_s = w.T * a.steps / el
-    F = alg_flops(w, proj)
+    F = sum(alg_flops(w, q) for q in projs)
     tflops = F / (ms * 1e-3) / 1e12
+    p0 = w.projections[0]
+    shapes = ", ".join(f"{w.projections[q].name} {w.projections[q].d_in}x{w.projections[q].d_out}"
+                       for q in projs)
     out = {
         "metric": "multi-LoRA fwd+bwd tokens/sec per layer",
         "value": tok_s,
@@ -177,10 +207,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {p.d_in}x{p.d_out} bf16, {w.n} adapters, ranks "
-                               f"{sorted(set(w.ranks))}, {w.T} tokens (seed {w.seed})",
-                   "T": w.T, "d_in": p.d_in, "d_out": p.d_out, "adapters": w.n,
-                   "streams": plan.info["n_groups"]},
+        "config": {"workload": (f"{w.name}: {p0.d_in}x{p0.d_out} bf16, " if len(projs) == 1 else
+                                f"{w.name}: projections {shapes}, bf16, ") +
+                               f"{w.n} adapters, ranks {sorted(set(w.ranks))}, {w.T} tokens (seed {w.seed})",
+                   "T": w.T, "d_in": p0.d_in, "d_out": p0.d_out, "adapters": w.n,
+                   "projections": [w.projections[q].name for q in projs],
+                   "streams": layers[0][0].info["n_groups"]},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
     }
@@ -190,14 +222,15 @@ def main():
         g_ms, g_n = gemm_rec
         if g_n:
             avg = g_ms / g_n
-            ach = gemm_fwd_flops(w, proj) / (avg * 1e-3) / 1e12
-            out["roofline"] = {"kernel": "k_gemm<fwd> (base GEMM + fused expand)", "bound": "mfma",
-                               "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                               "frac": ach / PEAK_BF16_TFLOPS,
+            ach = gemm_fwd_flops(w, 0) / (avg * 1e-3) / 1e12
+            out["roofline"] = {"kernel": f"k_gemm<fwd> (base GEMM + fused expand) of {p0.name} "
+                                         f"{p0.d_in}x{p0.d_out}",
+                               "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
                                "traffic": measured_traffic(w.name),
                                "avg_launch_ms": avg}
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, proj)
+        out["cpu_baseline"] = cpu_baseline(w, projs)
     print(json.dumps(out), flush=True)
 
 

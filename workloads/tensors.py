@@ -45,17 +45,20 @@ def _draw(rng, shape, std, dtype):
 
 
 def host_tensors(w: Workload, proj: int = 0, seed: int | None = None,
-                 b_zero: bool = False) -> dict:
+                 b_zero: bool = False, rows: int | None = None) -> dict:
     """All inputs of projection ``proj`` as host arrays.
 
     Returns dict with X [T,d_in], W0 [d_in,d_out], A list of [d_in,r_i],
     B list of [r_i,d_out], dY [T,d_out], scales (float32 [n]), offsets
     (int64 [n+1]), ranks (int32 [n]).  bf16 tensors are uint16 bit arrays.
+    With ``rows`` only the first ``rows`` tokens are drawn (the same values
+    as the full tensors' leading rows; the generator fills row by row) and
+    the offsets are cut there.
     """
     s = w.seed if seed is None else seed
     p = w.projections[proj]
     dt = w.dtype
-    T = w.T
+    T = w.T if rows is None else min(int(rows), w.T)
     out = {
         "X": _draw(_rng(s, proj, "X"), (T, p.d_in), STD_X, dt),
         "W0": _draw(_rng(s, proj, "W0"), (p.d_in, p.d_out), STD_W0, dt),
@@ -65,7 +68,7 @@ def host_tensors(w: Workload, proj: int = 0, seed: int | None = None,
                np.zeros((r, p.d_out), dtype=np.uint16 if dt == "bf16" else np.float32))
               for i, r in enumerate(w.ranks)],
         "scales": np.asarray(w.scales, dtype=np.float32),
-        "offsets": w.seg_offsets(),
+        "offsets": np.minimum(w.seg_offsets(), T),
         "ranks": np.asarray(w.ranks, dtype=np.int32),
         "dtype": dt,
         "d_in": p.d_in,
