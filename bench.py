@@ -59,6 +59,42 @@ def measured_traffic(workload: str):
     return int(v) if v else None
 
 
+def kernel_rooflines(w, projs, kern, iso, steps):
+    """Achieved rate of every step of the path against its roofline, from the
+    per-kernel pass (the weight-gradient kernels from the isolated pass,
+    where they do not share the chip with the dX GEMM).  Algorithmic bytes
+    and FLOPs count each operand once (ranks unpadded)."""
+    T = w.T
+    snr = sum(n * r for n, r in zip(w.tokens, w.ranks))
+    sr = sum(w.ranks)
+    work = {"shrink": 0.0, "dz": 0.0, "token_reduce": 0.0, "gemm_fwd": 0.0, "gemm_dx": 0.0}
+    for q in projs:
+        di, do = w.projections[q].d_in, w.projections[q].d_out
+        work["shrink"] += 2.0 * (T * di + di * sr + snr)
+        work["dz"] += 2.0 * (T * do + sr * do + snr)
+        work["token_reduce"] += 2.0 * (T * do + snr) + 4.0 * sr * do + 2.0 * (T * di + snr) + 4.0 * di * sr
+        work["gemm_fwd"] += 2.0 * T * di * do + 2.0 * snr * do
+        work["gemm_dx"] += 2.0 * T * di * do + 2.0 * snr * di
+    out = {}
+    for k, src, bound in (("shrink", kern, "hbm"), ("dz", kern, "hbm"), ("token_reduce", iso, "hbm"),
+                          ("gemm_fwd", kern, "mfma"), ("gemm_dx", kern, "mfma")):
+        ms = src[k][0] / steps
+        if ms <= 0:
+            continue
+        if bound == "hbm":
+            ach = work[k] / (ms * 1e-3) / 1e9
+            out[k] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": ach / PEAK_HBM_GBS, "ms_per_step": ms}
+        else:
+            ach = work[k] / (ms * 1e-3) / 1e12
+            out[k] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": ach / PEAK_BF16_TFLOPS, "ms_per_step": ms}
+    out["gemm_dx"]["note"] = "timed beside the concurrent weight-gradient kernels"
+    for k in ("reduce", "prep"):
+        out[k] = {"bound": "overhead", "ms_per_step": iso[k][0] / steps}
+    return out
+
+
 def cpu_baseline(w, projs, flop_budget=2.0e12):
     """The oracle (numpy float64) on the host over a bounded sample of the
     workload: the first M tokens of every timed projection, M chosen so the
@@ -185,6 +221,16 @@ def main():
             step(i)
         torch.cuda.synchronize()
         kern = {k: (v[0] / nb * a.steps, v[1]) for k, v in collect().items()}
+        # Isolated pass: a backward without dX runs the weight-gradient
+        # kernels on the group's own stream, alone, for clean times.
+        profile(True)
+        for i in range(nb):
+            k = i % SETS
+            for plan, layer, d, Ys, dXs in layers:
+                layer.forward(d["X"][k], Ys[k])
+                layer.backward(d["dY"][k], d["X"][k], want_dx=False)
+        torch.cuda.synchronize()
+        iso = {k: (v[0] / nb * a.steps, v[1]) for k, v in collect().items()}
         profile(False)
 
     ms = el / a.steps * 1e3
@@ -218,6 +264,7 @@ def main():
     }
     if kern:
         out["kernels_ms_per_step"] = {k: v[0] / a.steps for k, v in kern.items() if v[1]}
+        out["kernel_rooflines"] = kernel_rooflines(w, projs, kern, iso, a.steps)
     if prof:
         g_ms, g_n = gemm_rec
         if g_n:
