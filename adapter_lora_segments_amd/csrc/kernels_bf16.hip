@@ -12,6 +12,8 @@
 #include "device_common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace mlora {
 
 #define MLORA_LDS __attribute__((address_space(3)))
@@ -576,10 +578,11 @@ void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, 
 // ---------------------------------------------------------------------------
 // Base GEMM with the LoRA term as extra K-steps (the expand of the forward,
 // PLoRA §9.2 Case 4's dZ.A^T in the backward).  256x256 tile per workgroup of
-// eight waves, 32-deep K-steps copied straight from global memory into a
+// four waves, 32-deep K-steps copied straight from global memory into a
 // five-stage LDS ring (160 KiB).  Extension step e of a row tile loads rows
 // [lo,hi) of E_j (other rows zero) and k-rows [k0, k0+32) of EB_j (rows >=
-// r_j zero).  Output written as bf16.
+// r_j zero).  Output written as bf16, staged through LDS so every store
+// writes whole 512-byte rows.
 // ---------------------------------------------------------------------------
 // LDS tile layouts of one 32-deep K-step (16 KiB each).  LDS has 64 banks
 // of 4 bytes.  Measured on gfx950 (read timings of many layouts): a 16-byte
@@ -625,31 +628,31 @@ __device__ __forceinline__ u32x4 read_b_tr(const u32x4* tile, int nb, int kb, in
   return out;
 }
 
-// Eight waves share one 256x256 output tile, two along M and four along N;
-// each wave owns 128 rows x 64 columns of accumulators.  Ping-pong schedule:
-// waves 0-3 (one per SIMD) and waves 4-7 alternate phases.  In every phase one wave per SIMD issues the
-// sixteen MFMAs of one 32-deep step from registers while its partner reads
-// the twelve fragments of its next step from LDS and issues its share of the
-// direct copies; a barrier ends each phase and the roles swap.  The matrix
-// cores are fed by one wave at a time, and the read latency, the copy issue
-// and most of the barrier cost hide behind the other wave's MFMAs.
+// Four waves, one per SIMD, share one 256x256 output tile, two along M and
+// two along N; each wave owns 128x128 accumulators (256 registers), so every
+// 16-byte fragment read from LDS feeds four MFMAs instead of two or three.
+// Software pipeline at the granularity of a 16-deep slice, fragments double
+// buffered in registers: while the 16 MFMAs of one slice run, the wave reads
+// the next slice's eight fragments into the other register set and issues
+// four of its eight copies of a later step; one memory instruction follows
+// each MFMA, so reads, copies and their address arithmetic hide behind
+// matrix work of the same wave.
 //
-// Phase 2k:   waves 0-3 read step k, waves 4-7 multiply step k-1;
-// phase 2k+1: waves 0-3 multiply step k, waves 4-7 read step k.
-// A barrier before phase 0 makes every wave's copies of step 0 visible.
-// Ring slot k is read in phases 2k and 2k+1, so it is refilled (with step
-// k + NS) from phase 2k+2 on: each wave issues its copies of step t+NS-1
-// while reading step t.  Copies past the last step repeat it into the slot
-// just freed (never read again), so every wave keeps the same count in flight
-// and every barrier waits for the same vmcnt.
+// One barrier per step, between its two slices, after the wave's reads of
+// step k have landed and its copies up to step k+1 have landed: past it
+// every wave's copies of step k+1 are visible and nobody reads slot k % NS
+// any more, so step k+NS refills it: its first four copies during the
+// second slice of step k, the other four during the first slice of step
+// k+1.  Copies past the last step repeat the last step into a slot that is
+// never read again, so every barrier waits for the same vmcnt.  Steps whose
+// refill is a plain K-step of the main operands run a branch-free loop; the
+// few whose refill is a LoRA extension step (or past the end) run a second
+// loop that looks the extension up in the plan's tables.
 template <bool FWD, bool MAIN_B_KC>
-__global__ __launch_bounds__(512, 1) void k_gemm(GemmArgs g) {
-  constexpr int NW = 8;
+__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   constexpr int NS = 5;                    // ring stages
-  constexpr int WN = NW / 2;               // waves along N
-  constexpr int FI = 4;                    // 32-row fragments per wave
-  constexpr int FJ = 8 / WN;               // 32-column fragments per wave
-  constexpr int BPW = 16 / NW;             // 1 KiB blocks per operand per wave per stage
+  constexpr int FI = 4, FJ = 4;            // 32x32 fragments per wave along M, N
+  constexpr int BPW = 4;                   // 1 KiB blocks per operand per wave per stage
   constexpr int LPS = 2 * BPW;             // direct loads per wave per stage
   __shared__ u32x4 ring[NS][2][1024];      // [stage][A/B][16 KiB]
 
@@ -674,8 +677,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-  const int wm = w / WN, wn = w % WN;
-  const int wrow = 128 * wm, wcol = (256 / WN) * wn;
+  const int wm = w >> 1, wn = w & 1;
+  const int wrow = 128 * wm, wcol = 128 * wn;
 
   int kr_row[BPW], kr_chunk[BPW], nc_krow[BPW], nc_chunk[BPW];
 #pragma unroll
@@ -742,15 +745,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmArgs g) {
       }
     }
   };
-  // Copies of step `step` into its ring slot; past the last step the source
-  // repeats the last step (the slot it fills is never read again).
-  auto issue = [&](int step) {
-    const uint16_t* src[LPS];
-    sources(min(step, nsteps - 1), src);
-    u32x4* slot = &ring[step % NS][0][0];
-#pragma unroll
-    for (int i = 0; i < LPS; ++i)
-      dma16(src[i], slot + (i / BPW) * 1024 + 64 * (BPW * w + (i % BPW)));
+  auto copy = [&](const uint16_t* src, u32x4* slot, int i) {
+    dma16(src, slot + (i / BPW) * 1024 + 64 * (BPW * w + (i % BPW)));
+  };
+  // Source of copy i of main step `step` (step < nk).
+  auto src_main = [&](int step, int i) -> const uint16_t* {
+    const int k0 = step * 32;
+    if (i < BPW) return aptr[i] + k0;
+    return MAIN_B_KC ? bptr[i - BPW] + k0 : bptr[i - BPW] + (int64_t)k0 * g.ldb;
   };
 
   f32x16 acc[FI][FJ];
@@ -761,100 +763,120 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  // All fragments of one 32-deep step: two 16-deep slices.
+  // Fragments of one 16-deep slice, two register sets.
   u32x4 fa[2][FI], fb[2][FJ];
-  auto read_step = [&](int step) {
-    const u32x4* sa = ring[step % NS][0];
-    const u32x4* sb = ring[step % NS][1];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int fi = 0; fi < FI; ++fi) fa[ks][fi] = sa[kpos(wrow + 32 * fi + l32, 2 * ks + half)];
-      if (MAIN_B_KC) {
-#pragma unroll
-        for (int fj = 0; fj < FJ; ++fj) fb[ks][fj] = sb[kpos(wcol + 32 * fj + l32, 2 * ks + half)];
-      } else {
-#pragma unroll
-        for (int fj = 0; fj < FJ; ++fj) fb[ks][fj] = read_b_tr(sb, wcol + 32 * fj, 16 * ks, lane);
-      }
+  // Fragment read r (0..7) of slice ks: A fragments first.
+  auto read_frag = [&](const u32x4* slot, int ks, u32x4 (&ra)[FI], u32x4 (&rb)[FJ], int r) {
+    const u32x4* sa = slot;
+    const u32x4* sb = slot + 1024;
+    if (r < FI) {
+      ra[r] = sa[kpos(wrow + 32 * r + l32, 2 * ks + half)];
+    } else {
+      const int fj = r - FI;
+      if (MAIN_B_KC) rb[fj] = sb[kpos(wcol + 32 * fj + l32, 2 * ks + half)];
+      else rb[fj] = read_b_tr(sb, wcol + 32 * fj, 16 * ks, lane);
     }
   };
-  auto mma_step = [&]() {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int fi = 0; fi < FI; ++fi)
-#pragma unroll
-        for (int fj = 0; fj < FJ; ++fj) acc[fi][fj] = mfma32(fb[ks][fj], fa[ks][fi], acc[fi][fj]);
+  auto mma = [&](const u32x4 (&ra)[FI], const u32x4 (&rb)[FJ], int qq) {
+    const int fi = qq >> 2, fj = qq & 3;
+    acc[fi][fj] = mfma32(rb[fj], ra[fi], acc[fi][fj]);
   };
-  // End of a memory phase: the fragment reads have landed (so no copy can
-  // overwrite a slot still being read) and this wave's copies up to two
-  // steps ahead have landed; then meet the other waves.
-  auto end_mem_phase = [&]() {
+
+  // Step k.  First slice from set 0: the reads of the second slice into set
+  // 1 after its first eight MFMAs, then the last four copies of step
+  // k-1+NS (into slot (k-1) % NS, free since the previous barrier).  Barrier.
+  // Second slice from set 1: the reads of step k+1's first slice into set 0,
+  // then the first four copies of step k+NS into slot k % NS.  MAIN: both
+  // refills are main K-steps, whose sources are the main operands' pointers
+  // plus the step's offset.
+  auto step_block = [&](int k, auto main_tag) {
+    constexpr bool MAIN = decltype(main_tag)::value;
+    const u32x4* cslot = &ring[k % NS][0][0];
+    u32x4* pslot = &ring[(k + NS - 1) % NS][0][0];
+    const uint16_t* s1[LPS];
+    if (!MAIN) sources(min(k - 1 + NS, nsteps - 1), s1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) {
+      mma(fa[0], fb[0], qq);
+      if (qq < 8) read_frag(cslot, 1, fa[1], fb[1], qq);
+      else if (qq < 12) copy(MAIN ? src_main(k - 1 + NS, qq - 4) : s1[qq - 4], pslot, qq - 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     wait_vm_barrier<(NS - 2) * LPS>();
-  };
-  auto end_mma_phase = [&]() { wait_vm_barrier<(NS - 2) * LPS>(); };
-
+    const uint16_t* s2[LPS];
+    if (!MAIN) sources(min(k + NS, nsteps - 1), s2);
+    u32x4* dslot = &ring[k % NS][0][0];
+    const u32x4* nslot = &ring[(k + 1) % NS][0][0];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p) issue(p);
-  // every wave's copies of step 0 land before waves 0-3 read it in phase 0
-  wait_vm_barrier<(NS - 2) * LPS>();
-  if (w < 4) {
-    for (int k = 0; k < nsteps; ++k) {
-      read_step(k);
-      issue(k + NS - 1);
+    for (int qq = 0; qq < 16; ++qq) {
+      mma(fa[1], fb[1], qq);
+      if (qq < 8) read_frag(nslot, 0, fa[0], fb[0], qq);
+      else if (qq < 12) copy(MAIN ? src_main(k + NS, qq - 8) : s2[qq - 8], dslot, qq - 8);
       __builtin_amdgcn_sched_barrier(0);
-      end_mem_phase();
-      __builtin_amdgcn_sched_barrier(0);
-      mma_step();
-      __builtin_amdgcn_sched_barrier(0);
-      end_mma_phase();
     }
-    end_mma_phase();
-  } else {
-    end_mma_phase();
-    for (int k = 0; k < nsteps; ++k) {
-      read_step(k);
-      issue(k + NS - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      end_mem_phase();
-      __builtin_amdgcn_sched_barrier(0);
-      mma_step();
-      __builtin_amdgcn_sched_barrier(0);
-      end_mma_phase();
-    }
-  }
-  // the repeated copies past the last step are still in flight
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
 
-  // acc[fi][fj][4gg+e] = C[m = wrow + 32fi + l32][n = wcol + 32fj + 8gg + 4half + e]
+  // Prologue: steps 0..NS-2 and the first four copies of step NS-1; step
+  // 0's first slice is read once every wave's copies of it have landed.
+#pragma unroll
+  for (int p = 0; p < NS; ++p) {
+    const uint16_t* src[LPS];
+    sources(min(p, nsteps - 1), src);
+#pragma unroll
+    for (int i = 0; i < (p < NS - 1 ? LPS : LPS / 2); ++i) copy(src[i], &ring[p][0][0], i);
+  }
+  wait_vm_barrier<(NS - 2) * LPS + LPS / 2>();
+#pragma unroll
+  for (int r = 0; r < FI + FJ; ++r) read_frag(&ring[0][0][0], 0, fa[0], fb[0], r);
+
+  int k = 0;
+  for (; k + NS < nk; ++k) step_block(k, std::true_type());
+  for (; k < nsteps; ++k) step_block(k, std::false_type());
+  // The repeated copies past the last step are still in flight, and every
+  // wave must be done with the ring before it holds the output tile.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // Output tile staged in LDS as bf16 [256][256]: 512-byte rows of 32
+  // 16-byte granules, granule c of row m at c ^ (m & 31), so the 32 rows a
+  // fragment writes and the 32 granules a row read takes both spread evenly
+  // over the banks.  acc[fi][fj][4gg+e] holds C[m = wrow + 32fi + l32]
+  // [n = wcol + 32fj + 8gg + 4half + e].
+  char* ct = reinterpret_cast<char*>(&ring[0][0][0]);
 #pragma unroll
   for (int fi = 0; fi < FI; ++fi) {
     const int m = wrow + 32 * fi + l32;
-    if (m < mrows) {
-      uint16_t* crow = g.C + (int64_t)(row0 + m) * g.ldc;
 #pragma unroll
-      for (int fj = 0; fj < FJ; ++fj) {
+    for (int fj = 0; fj < FJ; ++fj) {
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int n = n0 + wcol + 32 * fj + 8 * gg + 4 * half;
-          if (n < g.N) {
-            u32x2 pk;
-            pk[0] = pack_bf16x2(acc[fi][fj][4 * gg + 0], acc[fi][fj][4 * gg + 1]);
-            pk[1] = pack_bf16x2(acc[fi][fj][4 * gg + 2], acc[fi][fj][4 * gg + 3]);
-            *reinterpret_cast<u32x2*>(crow + n) = pk;
-          }
-        }
+      for (int gg = 0; gg < 4; ++gg) {
+        const int c = (wcol >> 3) + 4 * fj + gg;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(acc[fi][fj][4 * gg + 0], acc[fi][fj][4 * gg + 1]);
+        pk[1] = pack_bf16x2(acc[fi][fj][4 * gg + 2], acc[fi][fj][4 * gg + 3]);
+        *reinterpret_cast<u32x2*>(ct + m * 512 + 16 * (c ^ (m & 31)) + 8 * half) = pk;
       }
     }
+  }
+  __syncthreads();
+  // Each wave stores 64 rows, two 512-byte rows per instruction.
+  const int gc = lane & 31;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int m = 64 * w + 2 * it + half;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ct + m * 512 + 16 * (gc ^ (m & 31)));
+    const int n = n0 + 8 * gc;
+    if (m < mrows && n < g.N) *reinterpret_cast<u32x4*>(g.C + (int64_t)(row0 + m) * g.ldc + n) = v;
   }
 }
 
 void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s) {
   const int total = g.n_mtiles * g.n_ntiles;
   if (total <= 0) return;
-  dim3 grid((unsigned)total), block(512);
+  dim3 grid((unsigned)total), block(256);
   if (fwd) {
     if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<true, true>), grid, block, 0, s, g);
     else hipLaunchKernelGGL((k_gemm<true, false>), grid, block, 0, s, g);
