@@ -122,6 +122,11 @@ mlora_status timed(mlora_plan_s* p, int kind, hipStream_t s, F&& launch) {
   return MLORA_OK;
 }
 
+// Events that only order the internal streams on this device: no timing and
+// no system-scope fence (the host never inspects them; the producing
+// kernel's completion makes its results visible to the device).
+constexpr unsigned kOrderEvent = hipEventDisableTiming | hipEventDisableSystemFence;
+
 mlora_status ensure_streams(mlora_plan_s* p) {
   const int S = p->P.n_groups;
   if (S <= 1 || (int)p->streams.size() == S) return MLORA_OK;
@@ -131,12 +136,12 @@ mlora_status ensure_streams(mlora_plan_s* p) {
     if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
     p->streams.push_back(s);
     hipEvent_t ev;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    e = hipEventCreateWithFlags(&ev, kOrderEvent);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
     p->join_ev.push_back(ev);
   }
   if (!p->fork_ev) {
-    hipError_t e = hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming);
+    hipError_t e = hipEventCreateWithFlags(&p->fork_ev, kOrderEvent);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
   }
   return MLORA_OK;
@@ -151,7 +156,7 @@ mlora_status ensure_wg_streams(mlora_plan_s* p) {
     p->wg_streams.push_back(s);
     for (auto* v : {&p->dz_ev, &p->wg_ev}) {
       hipEvent_t ev;
-      e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      e = hipEventCreateWithFlags(&ev, kOrderEvent);
       if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
       v->push_back(ev);
     }

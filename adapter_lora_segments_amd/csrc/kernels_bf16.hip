@@ -31,6 +31,14 @@ __device__ __forceinline__ void dma16(const uint16_t* src, u32x4* blk) {
                :: "s"(lds), "v"(src) : "memory", "m0");
 }
 
+// The same copy into the 1 KiB block at LDS byte address `lds` (wave-uniform),
+// for kernels that keep their ring's LDS address as an integer: no per-copy
+// address-space conversion.
+__device__ __forceinline__ void dma16_at(const uint16_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(src) : "memory", "m0");
+}
+
 // Wait until at most N direct-to-LDS loads of this wave are in flight, then
 // meet the other waves.  A bare s_barrier (no fence): the loads still in
 // flight target other ring stages and must not be drained here.
@@ -745,8 +753,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
       }
     }
   };
-  auto copy = [&](const uint16_t* src, u32x4* slot, int i) {
-    dma16(src, slot + (i / BPW) * 1024 + 64 * (BPW * w + (i % BPW)));
+  // LDS byte address of the ring, computed once; copy i of a stage goes to
+  // block (i / BPW) * 1024 + 64 (BPW w + i % BPW) (in 16-byte units)
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(MLORA_LDS void*)&ring[0][0][0]);
+  const uint32_t wave_lds = ring_lds + 16u * 64u * (uint32_t)(BPW * w);
+  auto copy = [&](const uint16_t* src, int slot, int i) {
+    dma16_at(src, wave_lds + 16u * (uint32_t)(slot * 2048 + (i / BPW) * 1024 + 64 * (i % BPW)));
   };
   // Source of copy i of main step `step` (step < nk).
   auto src_main = [&](int step, int i) -> const uint16_t* {
@@ -792,7 +805,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   auto step_block = [&](int k, auto main_tag) {
     constexpr bool MAIN = decltype(main_tag)::value;
     const u32x4* cslot = &ring[k % NS][0][0];
-    u32x4* pslot = &ring[(k + NS - 1) % NS][0][0];
+    const int pslot = (k + NS - 1) % NS;
     const uint16_t* s1[LPS];
     if (!MAIN) sources(min(k - 1 + NS, nsteps - 1), s1);
     __builtin_amdgcn_sched_barrier(0);
@@ -807,7 +820,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     wait_vm_barrier<(NS - 2) * LPS>();
     const uint16_t* s2[LPS];
     if (!MAIN) sources(min(k + NS, nsteps - 1), s2);
-    u32x4* dslot = &ring[k % NS][0][0];
+    const int dslot = k % NS;
     const u32x4* nslot = &ring[(k + 1) % NS][0][0];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -826,7 +839,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     const uint16_t* src[LPS];
     sources(min(p, nsteps - 1), src);
 #pragma unroll
-    for (int i = 0; i < (p < NS - 1 ? LPS : LPS / 2); ++i) copy(src[i], &ring[p][0][0], i);
+    for (int i = 0; i < (p < NS - 1 ? LPS : LPS / 2); ++i) copy(src[i], p, i);
   }
   wait_vm_barrier<(NS - 2) * LPS + LPS / 2>();
 #pragma unroll
