@@ -122,6 +122,88 @@ def cpu_baseline(w, projs, flop_budget=2.0e12):
                       f"in float64 numpy, {dt:.2f} s"}
 
 
+def time_steps(step, steps, warmup):
+    """Wall time per step (ms) of ``step(i)``, synchronized on both sides."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def sequential_layers(w, q, d, sets):
+    """The same work as one library call per adapter: a one-adapter plan per
+    non-empty segment over its own rows (row slices of the packed tensors)."""
+    import torch
+    from adapter_lora_segments_amd import Plan, PackedLoRALinear
+    p = w.projections[q]
+    off = [int(v) for v in d["offsets"]]
+    out = []
+    for i in range(w.n):
+        lo, hi = off[i], off[i + 1]
+        if hi == lo:
+            continue
+        plan = Plan([0, hi - lo], [int(d["ranks"][i])], p.d_in, p.d_out, "bf16")
+        layer = PackedLoRALinear(plan, d["W0"], [d["A"][i]], [d["B"][i]], [float(d["scales"][i])])
+        Y = [torch.empty((hi - lo, p.d_out), dtype=torch.bfloat16, device="cuda") for _ in range(sets)]
+        dX = [torch.empty((hi - lo, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(sets)]
+        out.append((lo, hi, plan, layer, Y, dX))
+    return out
+
+
+def packing_sweep(steps, warmup):
+    """Packed against sequential over the shapes of the PLoRA page's Table 7
+    (rank 64, hidden sizes 2048-18944 of two Qwen-2.5 models, 2 to 32
+    adapters, batch 1): one plan over n adapters of 512 tokens each against
+    n one-adapter calls, forward+backward of the whole layer (base GEMM
+    included), synthetic bf16 data."""
+    import torch
+    from adapter_lora_segments_amd import Plan, PackedLoRALinear
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rows = []
+    for d_in, d_out in ((2048, 2048), (3584, 3584), (2048, 11008), (3584, 18944)):
+        W0 = (torch.randn((d_in, d_out), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        for n in (1, 2, 4, 8, 16, 32):
+            r, tok = 64, 512
+            T = n * tok
+            X = torch.randn((T, d_in), generator=g, device="cuda").to(torch.bfloat16)
+            dY = torch.randn((T, d_out), generator=g, device="cuda").to(torch.bfloat16)
+            A = [(torch.randn((d_in, r), generator=g, device="cuda") * d_in ** -0.5).to(torch.bfloat16)
+                 for _ in range(n)]
+            B = [(torch.randn((r, d_out), generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+                 for _ in range(n)]
+            sc = [16.0 / r] * n
+            plan = Plan(list(range(0, T + 1, tok)), [r] * n, d_in, d_out, "bf16")
+            layer = PackedLoRALinear(plan, W0, A, B, sc)
+            Y = torch.empty((T, d_out), dtype=torch.bfloat16, device="cuda")
+            dX = torch.empty((T, d_in), dtype=torch.bfloat16, device="cuda")
+
+            def packed(i):
+                layer.forward(X, Y)
+                layer.backward(dY, X, dX)
+            t_p = time_steps(packed, steps, warmup)
+            seq = []
+            for i in range(n):
+                pl = Plan([0, tok], [r], d_in, d_out, "bf16")
+                seq.append((i * tok, PackedLoRALinear(pl, W0, [A[i]], [B[i]], [sc[i]])))
+
+            def sequential(i):
+                for lo, lay in seq:
+                    lay.forward(X[lo:lo + tok], Y[lo:lo + tok])
+                    lay.backward(dY[lo:lo + tok], X[lo:lo + tok], dX[lo:lo + tok])
+            t_s = time_steps(sequential, steps, warmup)
+            rows.append({"d_in": d_in, "d_out": d_out, "adapters": n, "rank": r, "tokens_per_adapter": tok,
+                         "packed_ms": t_p, "sequential_ms": t_s, "speedup": t_s / t_p})
+            print(f"# {d_in}x{d_out} n={n}: packed {t_p:.3f} ms, sequential {t_s:.3f} ms, "
+                  f"{t_s / t_p:.2f}x", file=sys.stderr, flush=True)
+            del layer, plan, seq, X, dY, A, B, Y, dX
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +221,12 @@ def main():
                          "writing this many MiB, to scale hardware byte counters")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not bracket launches with events (for external profilers)")
+    ap.add_argument("--no-sequential", action="store_true",
+                    help="skip timing the same work as one library call per adapter (packed "
+                         "against sequential, on the first timed projection)")
+    ap.add_argument("--packing-sweep", action="store_true",
+                    help="only run the packed-against-sequential sweep over Table 7's shapes and "
+                         "print its results as one JSON line")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: the packed layer is measured on one device's "
@@ -152,6 +240,12 @@ def main():
 
     torch.cuda.set_device(0)
     device_check()
+    if a.packing_sweep:
+        steps = min(a.steps, 20)
+        rows = packing_sweep(steps, min(a.warmup, 5))
+        print(json.dumps({"metric": "packed vs sequential fwd+bwd time per layer", "unit": "ms",
+                          "steps": steps, "data": "synthetic", "results": rows}), flush=True)
+        return
     w = load_workload(a.workload, a.seed)
     projs = list(range(len(w.projections))) if a.all_projections else [0]
     SETS = 4
@@ -233,6 +327,23 @@ def main():
         iso = {k: (v[0] / nb * a.steps, v[1]) for k, v in collect().items()}
         profile(False)
 
+    seq_ms = None
+    if not a.no_sequential:
+        q0 = projs[0]
+        d0 = layers[0][2]
+        seq = sequential_layers(w, q0, d0, SETS)
+
+        def seq_step(i):
+            k = i % SETS
+            for lo, hi, plan, layer, Y, dX in seq:
+                layer.forward(d0["X"][k][lo:hi], Y[k])
+                layer.backward(d0["dY"][k][lo:hi], d0["X"][k][lo:hi], dX[k])
+        seq_ms = time_steps(seq_step, min(a.steps, 50), min(a.warmup, 10))
+        packed_ms = time_steps(lambda i: (layers[0][1].forward(d0["X"][i % SETS], layers[0][3][i % SETS]),
+                                          layers[0][1].backward(d0["dY"][i % SETS], d0["X"][i % SETS],
+                                                                layers[0][4][i % SETS])),
+                               min(a.steps, 50), min(a.warmup, 10))
+
     ms = el / a.steps * 1e3
     tok_s = w.T * a.steps / el
     F = sum(alg_flops(w, q) for q in projs)
@@ -276,6 +387,11 @@ def main():
                                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
                                "traffic": measured_traffic(w.name),
                                "avg_launch_ms": avg}
+    if seq_ms is not None:
+        out["packed_vs_sequential"] = {
+            "projection": w.projections[projs[0]].name, "packed_ms_per_step": packed_ms,
+            "sequential_ms_per_step": seq_ms, "speedup": seq_ms / packed_ms,
+            "sequential": f"{len(seq)} one-adapter library calls, each over its own rows"}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, projs)
     print(json.dumps(out), flush=True)
