@@ -22,22 +22,32 @@ def _torch():
 
 
 class Plan:
-    """Host plan for one packed layer (seg_offsets, ranks, d_in, d_out)."""
+    """Host plan for one packed layer (seg_offsets, ranks, d_in, d_out), or,
+    through ``Plan.from_ids``, for rows in the caller's order with one adapter
+    id per token."""
 
     def __init__(self, seg_offsets, ranks, d_in: int, d_out: int, dtype: str = "bf16",
                  nano_rows: int = 0, n_streams: int = 0, chunk_min: int = 0, chunk_max: int = 0,
-                 chunk_per_rank: int = 0, w0_layout: str = "kn", gemm_rows: int = 0):
-        off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
+                 chunk_per_rank: int = 0, w0_layout: str = "kn", gemm_rows: int = 0, _ids=None):
         rk = np.ascontiguousarray(np.asarray(ranks, dtype=np.int32))
         n = int(rk.shape[0])
-        if off.shape != (n + 1,):
-            raise ValueError("seg_offsets must have len(ranks) + 1 entries")
         opts = _lib.PlanOpts(nano_rows, gemm_rows, n_streams, chunk_min, chunk_max, chunk_per_rank,
                              _lib.W0_LAYOUTS[w0_layout])
         h = ctypes.c_void_p()
-        check(lib().mlora_plan(n, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                               rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in),
-                               int(d_out), _lib.DTYPES[dtype], ctypes.byref(opts), ctypes.byref(h)))
+        if _ids is None:
+            off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
+            if off.shape != (n + 1,):
+                raise ValueError("seg_offsets must have len(ranks) + 1 entries")
+            check(lib().mlora_plan(n, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                   rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in),
+                                   int(d_out), _lib.DTYPES[dtype], ctypes.byref(opts), ctypes.byref(h)))
+        else:
+            ids = np.ascontiguousarray(np.asarray(_ids, dtype=np.int32).reshape(-1))
+            check(lib().mlora_plan_from_ids(n, int(ids.shape[0]),
+                                            ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                            rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in),
+                                            int(d_out), _lib.DTYPES[dtype], ctypes.byref(opts),
+                                            ctypes.byref(h)))
         self._L = lib()
         self._h = h
         inf = _lib.PlanInfo()
@@ -45,9 +55,14 @@ class Plan:
         self.info = {k: getattr(inf, k) for k, _ in _lib.PlanInfo._fields_}
         self.dtype = dtype
         self.w0_layout = w0_layout
-        self.offsets = off
+        self.offsets = self.export("offsets") if _ids is not None else off
         self.ranks = rk
         self._ws_uploaded = None
+
+    @classmethod
+    def from_ids(cls, token_adapter, ranks, d_in: int, d_out: int, dtype: str = "bf16", **opts):
+        """mlora_plan_from_ids: token t belongs to adapter token_adapter[t]."""
+        return cls(None, ranks, d_in, d_out, dtype, _ids=token_adapter, **opts)
 
     @property
     def handle(self):

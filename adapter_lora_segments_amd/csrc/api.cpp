@@ -85,6 +85,7 @@ mlora::DevTables dev_tables(const mlora_plan_s* p, void* ws) {
   t.ext_start = reinterpret_cast<const int32_t*>(b + L.ext_start);
   t.ext = reinterpret_cast<const int32_t*>(b + L.ext);
   t.zero = reinterpret_cast<const uint16_t*>(b + L.zero);
+  t.perm = p->P.perm.empty() ? nullptr : reinterpret_cast<const int32_t*>(b + L.perm);
   return t;
 }
 
@@ -220,6 +221,28 @@ const char* mlora_status_string(mlora_status s) {
 
 const char* mlora_last_error(void) { return g_err.c_str(); }
 
+namespace {
+
+mlora_status finish_plan(mlora::PlanTables&& P, mlora_plan_t* out) {
+  auto* p = new mlora_plan_s();
+  p->P = std::move(P);
+  p->L = mlora::device_layout(p->P);
+  p->blob = mlora::table_blob(p->P, p->L);
+  const int S = p->P.n_groups;
+  p->chunk_b.resize(S);
+  p->group_max_rank.assign(S, 1);
+  for (int g = 0; g < S; ++g) {
+    p->chunk_b[g] = bucket_ranges(p->P.chunks, 3, p->P.chunk_start[g], p->P.chunk_start[g + 1], p->P.rpad);
+    for (int32_t j = p->P.groups[g]; j < p->P.groups[g + 1]; ++j)
+      p->group_max_rank[g] = std::max(p->group_max_rank[g], p->P.ranks[j]);
+    p->max_rank = std::max(p->max_rank, p->group_max_rank[g]);
+  }
+  *out = p;
+  return MLORA_OK;
+}
+
+}  // namespace
+
 mlora_status mlora_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ranks, int64_t d_in,
                         int64_t d_out, mlora_dtype dtype, const mlora_plan_opts* opts,
                         mlora_plan_t* out) {
@@ -229,21 +252,23 @@ mlora_status mlora_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
     std::string err;
     mlora_status st = mlora::build_plan(n, seg_offsets, ranks, d_in, d_out, (int32_t)dtype, opts, P, err);
     if (st != MLORA_OK) return fail(st, err);
-    auto* p = new mlora_plan_s();
-    p->P = std::move(P);
-    p->L = mlora::device_layout(p->P);
-    p->blob = mlora::table_blob(p->P, p->L);
-    const int S = p->P.n_groups;
-    p->chunk_b.resize(S);
-    p->group_max_rank.assign(S, 1);
-    for (int g = 0; g < S; ++g) {
-      p->chunk_b[g] = bucket_ranges(p->P.chunks, 3, p->P.chunk_start[g], p->P.chunk_start[g + 1], p->P.rpad);
-      for (int32_t j = p->P.groups[g]; j < p->P.groups[g + 1]; ++j)
-        p->group_max_rank[g] = std::max(p->group_max_rank[g], p->P.ranks[j]);
-      p->max_rank = std::max(p->max_rank, p->group_max_rank[g]);
-    }
-    *out = p;
-    return MLORA_OK;
+    return finish_plan(std::move(P), out);
+  } catch (const std::bad_alloc&) {
+    return fail(MLORA_ERR_NOMEM, "host allocation failed while building the plan");
+  }
+}
+
+mlora_status mlora_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adapter,
+                                 const int32_t* ranks, int64_t d_in, int64_t d_out, mlora_dtype dtype,
+                                 const mlora_plan_opts* opts, mlora_plan_t* out) {
+  if (!out) return fail(MLORA_ERR_INVALID_ARG, "out is NULL");
+  try {
+    mlora::PlanTables P;
+    std::string err;
+    mlora_status st = mlora::build_plan_from_ids(n, T, token_adapter, ranks, d_in, d_out,
+                                                 (int32_t)dtype, opts, P, err);
+    if (st != MLORA_OK) return fail(st, err);
+    return finish_plan(std::move(P), out);
   } catch (const std::bad_alloc&) {
     return fail(MLORA_ERR_NOMEM, "host allocation failed while building the plan");
   }
@@ -315,6 +340,7 @@ mlora_status mlora_plan_export(mlora_plan_t p, int32_t table, void* dst, size_t*
     case MLORA_TAB_TILE_EXT_START: v32(P.ext_start); break;
     case MLORA_TAB_OFFSETS: v64(P.offsets); break;
     case MLORA_TAB_RANKS: v32(P.ranks); break;
+    case MLORA_TAB_PERM: v32(P.perm); break;
     default: return fail(MLORA_ERR_INVALID_ARG, "unknown table id " + std::to_string(table));
   }
   if (!dst) {

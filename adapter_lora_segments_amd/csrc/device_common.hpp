@@ -62,6 +62,9 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// Per-lane load of a plan table entry (e.g. the row permutation).
+__device__ __forceinline__ int ldg_i32(const int32_t* p) { return *p; }
+
 // Load of a value that no kernel writes while it runs (plan tables, pointer
 // arrays) through the constant address space, so a wave-uniform address
 // becomes a scalar load: it then waits on lgkmcnt, not on the vector-memory

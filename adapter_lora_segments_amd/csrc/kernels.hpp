@@ -23,6 +23,7 @@ struct DevTables {
   const int32_t* ext_start; // [n_tiles+1]
   const int32_t* ext;       // [n_ext][4]
   const uint16_t* zero;     // 256 zero bytes
+  const int32_t* perm;      // [T] grouped row -> caller row, or NULL (rows already grouped)
 };
 
 // ---------------- bf16 path (MFMA) ----------------

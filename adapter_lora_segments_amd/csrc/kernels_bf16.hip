@@ -165,7 +165,7 @@ struct SkinnyCfg {
   static_assert((NS - 2) * LPS <= 63, "vmcnt takes 0..63");
 };
 
-template <int RP, int MODE>
+template <int RP, int MODE, bool PERM>
 __device__ __forceinline__ void skinny_body(const DevTables& t, int j, int row0, int nrows,
                                             const uint16_t* P, int64_t K, const uint16_t* acat_t,
                                             const void* const* Bptr, float s, uint16_t* out,
@@ -201,7 +201,7 @@ __device__ __forceinline__ void skinny_body(const DevTables& t, int j, int row0,
       const int gc = (lane & 15) ^ (row & 15);
       if (row < 32) {
         const int pr = row0 + 32 * rf + min(row, frag_rows - 1);
-        src[q] = P + (int64_t)pr * K + 8 * gc;
+        src[q] = P + (int64_t)(PERM ? ldg_i32(t.perm + pr) : pr) * K + 8 * gc;
         adv[q] = true;
       } else {
         const int c = row - 32;
@@ -290,7 +290,7 @@ __device__ __forceinline__ void skinny_body(const DevTables& t, int j, int row0,
   }
 }
 
-template <int MODE>
+template <int MODE, bool PERM>
 __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin, const uint16_t* P,
                                                 int64_t K, const uint16_t* acat_t,
                                                 const void* const* Bptr, const float* scales,
@@ -300,10 +300,10 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
   const int j = ldc(t.nano + 3 * nb), row0 = ldc(t.nano + 3 * nb + 1), nrows = ldc(t.nano + 3 * nb + 2);
   const float s = ldc(scales + j);
   switch (ldc(t.rpad + j)) {
-    case 32: skinny_body<32, MODE>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
-    case 64: skinny_body<64, MODE>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
-    case 128: skinny_body<128, MODE>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
-    default: skinny_body<256, MODE>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
+    case 32: skinny_body<32, MODE, PERM>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
+    case 64: skinny_body<64, MODE, PERM>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
+    case 128: skinny_body<128, MODE, PERM>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
+    default: skinny_body<256, MODE, PERM>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
   }
 }
 
@@ -312,10 +312,14 @@ void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nan
                    const float* scales, uint16_t* out, hipStream_t s) {
   if (nano_count <= 0) return;
   dim3 grid((unsigned)nano_count), block(256);
-  if (mode == 0)
-    hipLaunchKernelGGL(k_skinny<0>, grid, block, 0, s, t, nano_begin, P, K, acat_t, Bptr, scales, out);
-  else
-    hipLaunchKernelGGL(k_skinny<1>, grid, block, 0, s, t, nano_begin, P, K, acat_t, Bptr, scales, out);
+#define MLORA_SKINNY(M, PM) \
+  hipLaunchKernelGGL((k_skinny<M, PM>), grid, block, 0, s, t, nano_begin, P, K, acat_t, Bptr, scales, out)
+  if (mode == 0) {
+    if (t.perm) MLORA_SKINNY(0, true); else MLORA_SKINNY(0, false);
+  } else {
+    if (t.perm) MLORA_SKINNY(1, true); else MLORA_SKINNY(1, false);
+  }
+#undef MLORA_SKINNY
 }
 
 // ---------------------------------------------------------------------------
@@ -345,7 +349,7 @@ struct TokenReduceArgs {
   int64_t d_in;
 };
 
-template <int RP, int MODE>
+template <int RP, int MODE, bool PERM>
 __device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int ch, int col0,
                                                   u32x4 (*sbig)[128 * 8], u32x4 (*srk)[RP * 8]) {
   constexpr int F = RP / 32;
@@ -383,7 +387,9 @@ __device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int 
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int tc = min(t0 + 8 * kb + i, nr - 1);
-          stage[p][i] = isbig ? ld16(bbase + (int64_t)tc * big_ld + col) : ld16(rbase + (int64_t)tc * RP + col);
+          // PERM: the wide operand's row is the caller's row of grouped row r0 + tc
+          const int64_t br = PERM ? (int64_t)ldg_i32(a.t.perm + r0 + tc) - r0 : tc;
+          stage[p][i] = isbig ? ld16(bbase + br * big_ld + col) : ld16(rbase + (int64_t)tc * RP + col);
         }
       }
     }
@@ -502,7 +508,7 @@ __device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int 
   }
 }
 
-template <int RP>
+template <int RP, bool PERM>
 __global__ __launch_bounds__(256) void k_token_reduce(TokenReduceArgs a) {
   __shared__ u32x4 sbig[2][128 * 8];
   __shared__ u32x4 srk[2][RP * 8];
@@ -510,9 +516,9 @@ __global__ __launch_bounds__(256) void k_token_reduce(TokenReduceArgs a) {
   const int nbb_a = (int)((a.d_in + 127) / 128);
   const int b = blockIdx.x, nb_b = a.n_chunks * nbb_b;
   if (b < nb_b)
-    token_reduce_body<RP, 0>(a, a.chunk_begin + b / nbb_b, (b % nbb_b) * 128, sbig, srk);
+    token_reduce_body<RP, 0, PERM>(a, a.chunk_begin + b / nbb_b, (b % nbb_b) * 128, sbig, srk);
   else
-    token_reduce_body<RP, 1>(a, a.chunk_begin + (b - nb_b) / nbb_a, ((b - nb_b) % nbb_a) * 128, sbig, srk);
+    token_reduce_body<RP, 1, PERM>(a, a.chunk_begin + (b - nb_b) / nbb_a, ((b - nb_b) % nbb_a) * 128, sbig, srk);
 }
 
 void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
@@ -523,12 +529,16 @@ void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_
   TokenReduceArgs a{t, chunk_begin, chunk_count, dY, Z, partB, d_out, X, dZ, partA, d_in};
   const int nbb_b = (int)((d_out + 127) / 128), nbb_a = (int)((d_in + 127) / 128);
   dim3 grid((unsigned)(chunk_count * (nbb_b + nbb_a))), block(256);
+#define MLORA_TR(R)                                                                 \
+  if (t.perm) hipLaunchKernelGGL((k_token_reduce<R, true>), grid, block, 0, s, a);  \
+  else hipLaunchKernelGGL((k_token_reduce<R, false>), grid, block, 0, s, a);
   switch (rp) {
-    case 32: hipLaunchKernelGGL((k_token_reduce<32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_token_reduce<64>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_token_reduce<128>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_token_reduce<256>), grid, block, 0, s, a); break;
+    case 32: MLORA_TR(32) break;
+    case 64: MLORA_TR(64) break;
+    case 128: MLORA_TR(128) break;
+    default: MLORA_TR(256) break;
   }
+#undef MLORA_TR
 }
 
 // ---------------------------------------------------------------------------
@@ -656,7 +666,7 @@ __device__ __forceinline__ u32x4 read_b_tr(const u32x4* tile, int nb, int kb, in
 // refill is a plain K-step of the main operands run a branch-free loop; the
 // few whose refill is a LoRA extension step (or past the end) run a second
 // loop that looks the extension up in the plan's tables.
-template <bool FWD, bool MAIN_B_KC>
+template <bool FWD, bool MAIN_B_KC, bool PERM>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   constexpr int NS = 5;                    // ring stages
   constexpr int FI = 4, FJ = 4;            // 32x32 fragments per wave along M, N
@@ -701,7 +711,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   const uint16_t* bptr[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
-    aptr[i] = g.A + (int64_t)(row0 + min(kr_row[i], mrows - 1)) * g.lda + 8 * kr_chunk[i];
+    const int ar = row0 + min(kr_row[i], mrows - 1);  // grouped row; PERM: caller row via the plan
+    aptr[i] = g.A + (int64_t)(PERM ? ldg_i32(g.t.perm + ar) : ar) * g.lda + 8 * kr_chunk[i];
     if (MAIN_B_KC)
       bptr[i] = g.B + (int64_t)min(n0 + kr_row[i], g.N - 1) * g.ldb + 8 * kr_chunk[i];
     else
@@ -882,7 +893,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     const int m = 64 * w + 2 * it + half;
     const u32x4 v = *reinterpret_cast<const u32x4*>(ct + m * 512 + 16 * (gc ^ (m & 31)));
     const int n = n0 + 8 * gc;
-    if (m < mrows && n < g.N) *reinterpret_cast<u32x4*>(g.C + (int64_t)(row0 + m) * g.ldc + n) = v;
+    if (m < mrows && n < g.N) {
+      const int cr = PERM ? ldg_i32(g.t.perm + row0 + m) : row0 + m;
+      *reinterpret_cast<u32x4*>(g.C + (int64_t)cr * g.ldc + n) = v;
+    }
   }
 }
 
@@ -890,13 +904,15 @@ void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s
   const int total = g.n_mtiles * g.n_ntiles;
   if (total <= 0) return;
   dim3 grid((unsigned)total), block(256);
+#define MLORA_GEMM(F, KC)                                                                  \
+  if (g.t.perm) hipLaunchKernelGGL((k_gemm<F, KC, true>), grid, block, 0, s, g);           \
+  else hipLaunchKernelGGL((k_gemm<F, KC, false>), grid, block, 0, s, g);
   if (fwd) {
-    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<true, true>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((k_gemm<true, false>), grid, block, 0, s, g);
+    if (main_b_kcontig) { MLORA_GEMM(true, true) } else { MLORA_GEMM(true, false) }
   } else {
-    if (main_b_kcontig) hipLaunchKernelGGL((k_gemm<false, true>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((k_gemm<false, false>), grid, block, 0, s, g);
+    if (main_b_kcontig) { MLORA_GEMM(false, true) } else { MLORA_GEMM(false, false) }
   }
+#undef MLORA_GEMM
 }
 
 }  // namespace mlora

@@ -1,5 +1,7 @@
 // fp32 kernels of the packed multi-LoRA layer (vector ALU, fp32 throughout,
-// no reduced-precision step).  Same steps as the bf16 path (PLoRA: Efficient
+// no reduced-precision step).  Rows are grouped by adapter; with a plan from
+// per-token ids, X, dY, Y and dX rows are read and written at the caller's
+// row through the plan's permutation.  Same steps as the bf16 path (PLoRA: Efficient
 // Concurrent LoRA Training for Large Language Models, §2.1 and §9.2); each
 // row finds its adapter by binary search over the segment offsets, and each
 // weight gradient is one thread's sum over its adapter's rows in row order.
@@ -7,6 +9,11 @@
 #include "kernels.hpp"
 
 namespace mlora {
+
+// Caller's row of grouped row `row` (plans from per-token ids), else `row`.
+__device__ __forceinline__ int64_t caller_row(const DevTables& t, int64_t row) {
+  return t.perm ? (int64_t)t.perm[row] : row;
+}
 
 // Adapter owning `row`: the largest i with offsets[i] <= row (empty
 // segments before it are skipped because their end equals their start).
@@ -32,7 +39,7 @@ __global__ __launch_bounds__(256) void k_f32_shrink(DevTables t, int32_t n, int6
   float acc = 0.f;
   if (c < r) {
     const float* Aj = static_cast<const float*>(A[j]);
-    const float* x = X + row * d_in;
+    const float* x = X + caller_row(t, row) * d_in;
     for (int64_t k = 0; k < d_in; ++k) acc = fmaf(x[k], Aj[k * r + c], acc);
     acc *= scales[j];
   }
@@ -51,7 +58,7 @@ __global__ __launch_bounds__(256) void k_f32_dz(DevTables t, int32_t n, int64_t 
   float acc = 0.f;
   if (c < r) {
     const float* Bj = static_cast<const float*>(B[j]) + (int64_t)c * d_out;
-    const float* g = dY + row * d_out;
+    const float* g = dY + caller_row(t, row) * d_out;
     for (int64_t o = 0; o < d_out; ++o) acc = fmaf(g[o], Bj[o], acc);
     acc *= scales[j];
   }
@@ -77,7 +84,7 @@ __global__ __launch_bounds__(256) void k_f32_gemm(DevTables t, int32_t n, int64_
       const int r = i >> 4, kk = i & 15;
       int64_t row = m0 + r;
       if (row >= T) row = T - 1;
-      As[kk][r] = A[row * lda + k0 + kk];
+      As[kk][r] = A[caller_row(t, row) * lda + k0 + kk];
       const int nn = i >> 4, k2 = i & 15;
       if (B_KC) {
         Bs[k2][nn] = B[(int64_t)(n0 + nn) * ldb + k0 + k2];
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(256) void k_f32_gemm(DevTables t, int32_t n, int64_
         const float ebv = FWD ? w[(int64_t)c * N + col] : w[(int64_t)col * r + c];
         v = fmaf(e[c], ebv, v);
       }
-      C[row * ldc + col] = v;
+      C[caller_row(t, row) * ldc + col] = v;
     }
   }
 }
@@ -135,7 +142,8 @@ __global__ __launch_bounds__(256) void k_f32_db(DevTables t, int32_t n, int64_t 
     const int64_t a = t.offsets[j], b = t.offsets[j + 1];
     const float* z = Z + t.zoff[j] + c;
     float acc = 0.f;
-    for (int64_t row = a; row < b; ++row) acc = fmaf(z[(row - a) * rp], dY[row * d_out + o], acc);
+    for (int64_t row = a; row < b; ++row)
+      acc = fmaf(z[(row - a) * rp], dY[caller_row(t, row) * d_out + o], acc);
     static_cast<float*>(dB[j])[idx] = acc;
   }
 }
@@ -153,7 +161,8 @@ __global__ __launch_bounds__(256) void k_f32_da(DevTables t, int32_t n, int64_t 
     const int64_t a = t.offsets[j], b = t.offsets[j + 1];
     const float* g = dZ + t.zoff[j] + c;
     float acc = 0.f;
-    for (int64_t row = a; row < b; ++row) acc = fmaf(X[row * d_in + d], g[(row - a) * rp], acc);
+    for (int64_t row = a; row < b; ++row)
+      acc = fmaf(X[caller_row(t, row) * d_in + d], g[(row - a) * rp], acc);
     static_cast<float*>(dA[j])[idx] = acc;
   }
 }

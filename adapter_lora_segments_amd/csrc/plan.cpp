@@ -221,6 +221,45 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
   return MLORA_OK;
 }
 
+mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adapter,
+                                 const int32_t* ranks, int64_t d_in, int64_t d_out, int32_t dtype,
+                                 const mlora_plan_opts* opts, PlanTables& P, std::string& err) {
+  if (n < 1 || n > MLORA_MAX_ADAPTERS) {
+    err = "n must be in [1, " + std::to_string(MLORA_MAX_ADAPTERS) + "], got " + std::to_string(n);
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (T < 0) {
+    err = "T must be >= 0";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (T > 0 && !token_adapter) {
+    err = "token_adapter must be non-NULL";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (T >= (int64_t(1) << 31) - 1) {
+    err = "total rows must be below 2^31 - 1";
+    return MLORA_ERR_UNSUPPORTED;
+  }
+  // stable counting sort: counts, exclusive prefix sums, placement in row order
+  std::vector<int64_t> off(n + 1, 0);
+  for (int64_t t = 0; t < T; ++t) {
+    const int32_t a = token_adapter[t];
+    if (a < 0 || a >= n) {
+      err = "token_adapter[" + std::to_string(t) + "] = " + std::to_string(a) + " is not in [0, n)";
+      return MLORA_ERR_INVALID_ARG;
+    }
+    off[a + 1] += 1;
+  }
+  for (int32_t a = 0; a < n; ++a) off[a + 1] += off[a];
+  std::vector<int32_t> perm((size_t)T);
+  std::vector<int64_t> next(off.begin(), off.end() - 1);
+  for (int64_t t = 0; t < T; ++t) perm[(size_t)next[token_adapter[t]]++] = (int32_t)t;
+  mlora_status st = build_plan(n, off.data(), ranks, d_in, d_out, dtype, opts, P, err);
+  if (st != MLORA_OK) return st;
+  P.perm = std::move(perm);
+  return MLORA_OK;
+}
+
 DeviceLayout device_layout(const PlanTables& p) {
   DeviceLayout L{};
   size_t off = 0;
@@ -243,6 +282,7 @@ DeviceLayout device_layout(const PlanTables& p) {
   L.tiles = take(4 * p.tiles.size());
   L.ext_start = take(4 * p.ext_start.size());
   L.ext = take(4 * p.ext.size());
+  L.perm = take(4 * p.perm.size());
   L.zero = take(256);  // a zero page: loads of rows that must read as zero point here
   L.table_bytes = off;
   const size_t esz = p.dtype == MLORA_BF16 ? 2 : 4;
@@ -282,6 +322,7 @@ std::vector<uint8_t> table_blob(const PlanTables& p, const DeviceLayout& L) {
   put(L.tiles, p.tiles.data(), 4 * p.tiles.size());
   put(L.ext_start, p.ext_start.data(), 4 * p.ext_start.size());
   put(L.ext, p.ext.data(), 4 * p.ext.size());
+  put(L.perm, p.perm.data(), 4 * p.perm.size());
   return b;
 }
 

@@ -39,6 +39,7 @@ struct PlanTables {
   std::vector<int32_t> ch_first, ch_count;
   std::vector<int32_t> tiles, tile_start;          // tiles: [n_tiles][2]
   std::vector<int32_t> ext, ext_start;             // ext: [n_ext][4]
+  std::vector<int32_t> perm;  // [T] grouped row -> caller row (plans from ids; empty otherwise)
 
   int64_t n_nano() const { return (int64_t)nano.size() / 3; }
   int64_t n_chunks() const { return (int64_t)chunks.size() / 3; }
@@ -51,11 +52,17 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
                         int64_t d_out, int32_t dtype, const mlora_plan_opts* opts, PlanTables& out,
                         std::string& err);
 
+// The same for rows in the caller's order with per-token adapter ids: a
+// stable counting sort by id gives the segments and the permutation.
+mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adapter,
+                                 const int32_t* ranks, int64_t d_in, int64_t d_out, int32_t dtype,
+                                 const mlora_plan_opts* opts, PlanTables& out, std::string& err);
+
 // Byte layout of the device copy of the tables and of the workspace.
 struct DeviceLayout {
   // offsets (bytes) of each table inside the table blob
   size_t offsets, zoff, ranks, rpad, roff, ch_first, ch_count, nano, chunks, cpref, tiles,
-      ext_start, ext, zero;
+      ext_start, ext, zero, perm;
   size_t table_bytes;
   // offsets (bytes) of the work buffers inside the workspace
   size_t acat_t, acat, bcat_t, dz, part_a, part_b;

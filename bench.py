@@ -224,6 +224,9 @@ def main():
     ap.add_argument("--no-sequential", action="store_true",
                     help="skip timing the same work as one library call per adapter (packed "
                          "against sequential, on the first timed projection)")
+    ap.add_argument("--shuffled-ids", action="store_true",
+                    help="rows in a shuffled caller order with one adapter id per token "
+                         "(mlora_plan_from_ids) instead of contiguous segments")
     ap.add_argument("--packing-sweep", action="store_true",
                     help="only run the packed-against-sequential sweep over Table 7's shapes and "
                          "print its results as one JSON line")
@@ -253,8 +256,14 @@ def main():
     for q in projs:
         p = w.projections[q]
         d = device_tensors(w, q, sets=SETS)
-        plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16",
-                    n_streams=a.streams or w.n_streams)
+        if a.shuffled_ids:
+            ids = np.repeat(np.arange(w.n), np.diff(np.asarray(d["offsets"])))
+            ids = ids[np.random.default_rng(a.seed).permutation(w.T)]
+            plan = Plan.from_ids(ids, d["ranks"], p.d_in, p.d_out, "bf16",
+                                 n_streams=a.streams or w.n_streams)
+        else:
+            plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16",
+                        n_streams=a.streams or w.n_streams)
         layer = PackedLoRALinear(plan, d["W0"], d["A"], d["B"], d["scales"])
         Ys = [torch.empty((w.T, p.d_out), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
         dXs = [torch.empty((w.T, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
@@ -328,7 +337,7 @@ def main():
         profile(False)
 
     seq_ms = None
-    if not a.no_sequential:
+    if not a.no_sequential and not a.shuffled_ids:
         q0 = projs[0]
         d0 = layers[0][2]
         seq = sequential_layers(w, q0, d0, SETS)
@@ -369,7 +378,8 @@ def main():
                                f"{w.n} adapters, ranks {sorted(set(w.ranks))}, {w.T} tokens (seed {w.seed})",
                    "T": w.T, "d_in": p0.d_in, "d_out": p0.d_out, "adapters": w.n,
                    "projections": [w.projections[q].name for q in projs],
-                   "streams": layers[0][0].info["n_groups"]},
+                   "streams": layers[0][0].info["n_groups"],
+                   "rows": "shuffled, per-token adapter ids" if a.shuffled_ids else "adapter segments"},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
     }

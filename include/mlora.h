@@ -122,6 +122,22 @@ mlora_status mlora_plan(int32_t n, const int64_t *seg_offsets, const int32_t *ra
                         int64_t d_out, mlora_dtype dtype, const mlora_plan_opts *opts,
                         mlora_plan_t *out);
 
+/*
+ * mlora_plan_from_ids -- the same for rows in the caller's order, each
+ * token naming its adapter: token t belongs to adapter token_adapter[t]
+ * (host, T entries, each in [0, n); T may be 0).  A stable counting sort by
+ * id groups the rows (each adapter's rows keep the caller's order); the
+ * resulting segments get the plan of mlora_plan, and the permutation
+ * (MLORA_TAB_PERM: grouped row -> caller row) is applied inside forward and
+ * backward: X, dY, Y and dX stay in the caller's row order, Z' is in grouped
+ * order.  The PLoRA page (§2.4) gives every packed adapter its own inputs;
+ * ids are another way for a caller to name them.  Errors as mlora_plan, plus
+ * MLORA_ERR_INVALID_ARG for an id out of range.
+ */
+mlora_status mlora_plan_from_ids(int32_t n, int64_t T, const int32_t *token_adapter,
+                                 const int32_t *ranks, int64_t d_in, int64_t d_out, mlora_dtype dtype,
+                                 const mlora_plan_opts *opts, mlora_plan_t *out);
+
 void mlora_plan_destroy(mlora_plan_t plan);
 
 typedef struct {
@@ -144,7 +160,7 @@ mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);
  *   ADAPTER_CHUNK_FIRST[n], ADAPTER_CHUNK_COUNT[n],
  *   TILES[n_tiles][2] (row0, rows), TILE_START[S'+1],
  *   EXT[n_ext][4] (adapter, lo, hi, k0), TILE_EXT_START[n_tiles+1],
- *   OFFSETS[n+1], RANKS[n]. */
+ *   OFFSETS[n+1], RANKS[n], PERM[T] (plans from ids; empty otherwise). */
 typedef enum {
   MLORA_TAB_RPAD = 0,
   MLORA_TAB_ZOFF,
@@ -163,6 +179,7 @@ typedef enum {
   MLORA_TAB_TILE_EXT_START,
   MLORA_TAB_OFFSETS,
   MLORA_TAB_RANKS,
+  MLORA_TAB_PERM,
   MLORA_TAB_COUNT
 } mlora_table;
 

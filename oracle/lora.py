@@ -24,6 +24,10 @@ Rows [o_i, o_{i+1}) of the packed token axis belong to adapter i.  For each i:
     dB_i = s_i Z_i^T dY_i
 An adapter with no rows gets dA_i = 0 and dB_i = 0.  W0 gets no gradient.
 
+With per-token adapter ids instead of segments (forward_ids, backward_ids),
+the same is computed over the rows of each adapter, with row-indexed results
+in the caller's row order.
+
 Inputs may be float arrays or, with ``dtype="bf16"``, uint16 arrays holding
 bf16 bit patterns; everything is upcast to float64 and no intermediate
 rounding is modelled.  Work streams over row chunks so large inputs need not
@@ -98,6 +102,43 @@ def backward(dY, X, W0, A, B, scales, offsets, dtype="fp32", chunk=CHUNK, want_d
         dA.append(gA)
         dB.append(gB)
         dZ.append(dZi)
+    return dX, dA, dB, dZ
+
+
+def ids_order(token_adapter, n):
+    """Rows grouped by adapter for per-token adapter ids: token t belongs to
+    adapter token_adapter[t] (0 <= id < n); each adapter's rows keep the
+    caller's order (a stable sort by id).  Returns (perm, offsets): grouped
+    row i is the caller's row perm[i], and adapter a owns grouped rows
+    [offsets[a], offsets[a+1])."""
+    ids = np.asarray(token_adapter, dtype=np.int64)
+    assert ids.ndim == 1 and (ids.size == 0 or (ids.min() >= 0 and ids.max() < n))
+    perm = np.argsort(ids, kind="stable")
+    offsets = np.zeros(n + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(np.bincount(ids, minlength=n))
+    return perm, offsets
+
+
+def forward_ids(X, W0, A, B, scales, token_adapter, dtype="fp32", chunk=CHUNK):
+    """forward() for rows in the caller's order with per-token adapter ids:
+    Y in the caller's row order; Z_i over adapter i's rows in that order."""
+    perm, off = ids_order(token_adapter, len(A))
+    Yg, Z = forward(np.asarray(X)[perm], W0, A, B, scales, off, dtype, chunk)
+    Y = np.empty_like(Yg)
+    Y[perm] = Yg
+    return Y, Z
+
+
+def backward_ids(dY, X, W0, A, B, scales, token_adapter, dtype="fp32", chunk=CHUNK, want_dx=True):
+    """backward() for rows in the caller's order with per-token adapter ids:
+    dX in the caller's row order."""
+    perm, off = ids_order(token_adapter, len(A))
+    dXg, dA, dB, dZ = backward(np.asarray(dY)[perm], np.asarray(X)[perm], W0, A, B, scales, off, dtype,
+                               chunk, want_dx)
+    dX = None
+    if want_dx:
+        dX = np.empty_like(dXg)
+        dX[perm] = dXg
     return dX, dA, dB, dZ
 
 

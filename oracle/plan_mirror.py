@@ -164,3 +164,28 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None) -> dict:
         "ext": a32(ext, 4),
         "tile_ext_start": a32(ext_start),
     }
+
+
+def build_plan_from_ids(token_adapter, ranks, opts: PlanOpts | None = None) -> dict:
+    """The plan for rows in the caller's order with per-token adapter ids:
+    rows grouped by adapter with a stable counting sort (counts, exclusive
+    prefix sums, then every row placed at its adapter's next free position,
+    in row order); "perm" lists the caller's row of each grouped row, and the
+    grouped segments get the plan of build_plan."""
+    ids = [int(v) for v in token_adapter]
+    n = len(ranks)
+    assert all(0 <= a < n for a in ids)
+    off = [0] * (n + 1)
+    for a in ids:
+        off[a + 1] += 1
+    for a in range(n):
+        off[a + 1] += off[a]
+    nxt = off[:n]
+    perm = [0] * len(ids)
+    for t, a in enumerate(ids):
+        perm[nxt[a]] = t
+        nxt[a] += 1
+    plan = build_plan(off, ranks, opts)
+    plan["perm"] = np.asarray(perm, dtype=np.int32)
+    plan["offsets"] = np.asarray(off, dtype=np.int64)
+    return plan

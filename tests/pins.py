@@ -12,7 +12,10 @@ copy of it) and raises AssertionError when the oracle disagrees with:
   A.B) with a different association order;
 - pure-Python triple loops on tiny shapes;
 - zero padding of the rank, adapter reordering, linearity in s_i;
-- torch CPU float64 autograd of the single-adapter expression.
+- torch CPU float64 autograd of the single-adapter expression;
+- for per-token adapter ids: a hand-worked grouping (tests/golden/ids_order.json),
+  the definition applied token by token, and the segment form when the ids
+  are already in adapter order.
 """
 from __future__ import annotations
 
@@ -343,7 +346,68 @@ def pin_bf16_decode(ol):
     assert np.array_equal(ol.as_f64(bits, "bf16"), np.asarray([[1.0, -2.0], [0.25, 0.0]]))
 
 
-ALL_PINS = [pin_hand_example, pin_b_zero, pin_fused_equals_sequential, pin_finite_differences,
+def pin_ids_golden_order(ol):
+    """Grouping per-token ids, worked by hand (tests/golden/ids_order.json)."""
+    with open(os.path.join(GOLDEN, "ids_order.json")) as f:
+        g = json.load(f)
+    perm, off = ol.ids_order(g["token_adapter"], g["n"])
+    assert [int(v) for v in perm] == g["perm"], perm
+    assert [int(v) for v in off] == g["offsets"], off
+
+
+def pin_ids_brute_force(ol):
+    """Per-token ids against the definition applied token by token on tiny
+    shapes: each row uses its own adapter; each adapter's gradients sum over
+    its tokens (pure-Python loops over tokens, outer products per token)."""
+    rng = np.random.default_rng(23)
+    n, d_in, d_out, T = 3, 5, 4, 11
+    ranks = [2, 1, 3]
+    ids = rng.integers(0, n, size=T)
+    ids[3] = 2  # every adapter present ...
+    ids[7] = 0
+    ids[9] = 1
+    X = rng.standard_normal((T, d_in))
+    dY = rng.standard_normal((T, d_out))
+    W0 = rng.standard_normal((d_in, d_out))
+    A = [rng.standard_normal((d_in, r)) for r in ranks]
+    B = [rng.standard_normal((r, d_out)) for r in ranks]
+    s = np.array([0.5, -1.5, 2.0])
+    Y_ref = np.zeros((T, d_out))
+    dX_ref = np.zeros((T, d_in))
+    dA_ref = [np.zeros_like(a) for a in A]
+    dB_ref = [np.zeros_like(b) for b in B]
+    for t in range(T):
+        a = int(ids[t])
+        z = X[t] @ A[a]
+        Y_ref[t] = X[t] @ W0 + s[a] * (z @ B[a])
+        dz = s[a] * (B[a] @ dY[t])
+        dX_ref[t] = W0 @ dY[t] + A[a] @ dz
+        dA_ref[a] += np.outer(X[t], dz)
+        dB_ref[a] += s[a] * np.outer(z, dY[t])
+    Y, _ = ol.forward_ids(X, W0, A, B, s, ids, "fp32", chunk=2)
+    dX, dA, dB, _ = ol.backward_ids(dY, X, W0, A, B, s, ids, "fp32", chunk=2)
+    _close(Y, Y_ref, 1e-12, "Y ids")
+    _close(dX, dX_ref, 1e-12, "dX ids")
+    for i in range(n):
+        _close(dA[i], dA_ref[i], 1e-12, f"dA{i} ids")
+        _close(dB[i], dB_ref[i], 1e-12, f"dB{i} ids")
+
+
+def pin_ids_sorted_is_segments(ol):
+    """Ids already in adapter order give exactly the segment form."""
+    c = rand_case(29, 6, 5, [2, 4], [3, 5])
+    ids = np.repeat([0, 1], [3, 5])
+    Y, _ = ol.forward_ids(c["X"], c["W0"], c["A"], c["B"], c["s"], ids, "fp32", chunk=7)
+    Ys, _ = _fwd(ol, c)
+    assert np.array_equal(Y, Ys)
+    dX, dA, dB, _ = ol.backward_ids(c["dY"], c["X"], c["W0"], c["A"], c["B"], c["s"], ids, "fp32", chunk=7)
+    dXs, dAs, dBs, _ = _bwd(ol, c)
+    assert np.array_equal(dX, dXs)
+    for i in range(2):
+        assert np.array_equal(dA[i], dAs[i]) and np.array_equal(dB[i], dBs[i])
+
+
+ALL_PINS = [pin_ids_golden_order, pin_ids_brute_force, pin_ids_sorted_is_segments, pin_hand_example, pin_b_zero, pin_fused_equals_sequential, pin_finite_differences,
             pin_merged_weight, pin_brute_force, pin_rank_padding, pin_permutation,
             pin_scale_linearity, pin_torch_autograd, pin_sampled_rows, pin_sampled_z_rows,
             pin_projected_grads, pin_bf16_decode]

@@ -86,6 +86,43 @@ def test_plan_bit_exact_on_workloads(name, seed):
                            PlanOpts(n_streams=w.n_streams))
 
 
+@st.composite
+def ids_cases(draw):
+    n = draw(st.integers(1, 24))
+    T = draw(st.integers(0, 1500))
+    ids = draw(st.lists(st.integers(0, n - 1), min_size=T, max_size=T))
+    ranks = draw(st.lists(st.sampled_from([1, 8, 16, 33, 64, 128, 256]), min_size=n, max_size=n))
+    S = draw(st.integers(1, 4))
+    return ids, ranks, PlanOpts(nano_rows=draw(st.sampled_from([32, 64, 256])), gemm_rows=256, n_streams=S)
+
+
+@settings(max_examples=120, deadline=None)
+@given(ids_cases())
+def test_plan_from_ids_bit_exact_against_mirror(case):
+    """mlora_plan_from_ids: the grouping permutation and every table equal the
+    mirror's (an independent counting sort, then the segment rule)."""
+    from oracle.plan_mirror import build_plan_from_ids
+    ids, ranks, opts = case
+    p = Plan.from_ids(ids, ranks, 128, 192, "bf16", nano_rows=opts.nano_rows, n_streams=opts.n_streams)
+    m = build_plan_from_ids(ids, ranks, opts)
+    assert np.array_equal(p.export("perm"), m["perm"]) and p.export("perm").dtype == np.int32
+    assert np.array_equal(p.export("offsets"), m["offsets"])
+    for name in ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks",
+                 "chunk_start", "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count",
+                 "tiles", "tile_start", "ext", "tile_ext_start"]:
+        got, want = p.export(name), m[name]
+        assert (got.size == 0 and want.size == 0) or np.array_equal(got, want.reshape(got.shape)), name
+
+
+def test_plan_from_ids_errors_and_segment_plans_have_no_perm():
+    assert _status(lambda: Plan.from_ids([0, 2, 1], [4, 8], 128, 64)) == -1   # id 2 >= n
+    assert _status(lambda: Plan.from_ids([0, -1], [4, 8], 128, 64)) == -1     # negative id
+    assert _status(lambda: Plan.from_ids([0, 1], [4, 0], 128, 64)) == -1      # rank 0
+    p = Plan.from_ids([], [4, 8], 128, 64)                                      # no rows at all
+    assert p.info["T"] == 0 and p.export("perm").size == 0
+    assert Plan([0, 5, 9], [4, 8], 128, 64).export("perm").size == 0
+
+
 def _status(fn):
     with pytest.raises(MloraError) as e:
         fn()

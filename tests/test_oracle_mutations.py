@@ -32,6 +32,11 @@ MUTATIONS = {
     "proj_chunk_tail_lost": ("            r1 = min(hi, r0 + chunk)\n            Xc = as_f64(X[r0:r1], dtype)\n            Gc",
                              "            r1 = min(hi - 1, r0 + chunk)\n            Xc = as_f64(X[r0:r1], dtype)\n            Gc"),
     "sampled_z_no_scale": ("zi = s * (x @ Ai)", "zi = (x @ Ai)"),
+    "ids_unstable_sort": ('perm = np.argsort(ids, kind="stable")', 'perm = np.argsort(-ids, kind="stable")[::-1]'),
+    "ids_offsets_shift": ("offsets[1:] = np.cumsum(np.bincount(ids, minlength=n))",
+                          "offsets[1:] = np.cumsum(np.bincount(ids, minlength=n)) - 1"),
+    "ids_y_not_unpermuted": ("    Y = np.empty_like(Yg)\n    Y[perm] = Yg", "    Y = np.empty_like(Yg)\n    Y[:] = Yg"),
+    "ids_dx_wrong_inverse": ("        dX[perm] = dXg", "        dX[:] = dXg[perm]"),
 }
 
 
