@@ -28,6 +28,10 @@ Rule (all integers; counts and indexes int32, offsets into tensors int64):
     BM rows.  For each tile, its extension steps: for every adapter j
     (ascending) whose rows meet the tile, for k0 = 0, 32, ... < r_pad(j): entry
     (j, lo, hi, k0) with [lo, hi) the rows of j inside the tile.
+ 8. Optimizer blocks: for every adapter i ascending, its trained tensors A_i
+    (tensor 2i, d_in r_i elements) then B_i (tensor 2i+1, r_i d_out
+    elements), each cut into consecutive pieces of OPT_BLOCK elements (last
+    one partial).  Entry (tensor, piece).
 """
 from __future__ import annotations
 
@@ -36,6 +40,7 @@ from dataclasses import dataclass
 import numpy as np
 
 KSTEP = 32
+OPT_BLOCK = 2048
 
 
 @dataclass
@@ -189,3 +194,13 @@ def build_plan_from_ids(token_adapter, ranks, opts: PlanOpts | None = None) -> d
     plan["perm"] = np.asarray(perm, dtype=np.int32)
     plan["offsets"] = np.asarray(off, dtype=np.int64)
     return plan
+
+
+def optimizer_blocks(ranks, d_in, d_out) -> np.ndarray:
+    """Rule 8: the (tensor, piece) work items of the per-adapter optimizer step."""
+    out = []
+    for i, r in enumerate(int(v) for v in ranks):
+        for t, numel in ((2 * i, d_in * r), (2 * i + 1, r * d_out)):
+            for piece in range(-(-numel // OPT_BLOCK)):
+                out.append((t, piece))
+    return np.asarray(out, dtype=np.int32).reshape(-1, 2)

@@ -6,9 +6,11 @@ import types
 
 import pytest
 
-from tests import pins
+from tests import pins, pins_adamw
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "lora.py")
+ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE, "lora.py")
+SRC_ADAMW = os.path.join(ORACLE, "adamw.py")
 
 MUTATIONS = {
     "drop_scale_fwd": ("Y[r0:r1] = Xc @ W + s * (Zc @ Bi)", "Y[r0:r1] = Xc @ W + (Zc @ Bi)"),
@@ -39,9 +41,24 @@ MUTATIONS = {
     "ids_dx_wrong_inverse": ("        dX[perm] = dXg", "        dX[:] = dXg[perm]"),
 }
 
+ADAMW_MUTATIONS = {
+    "no_bias_correction_m": ("m_hat = m / (1.0 - beta1 ** t)", "m_hat = m"),
+    "no_bias_correction_v": ("v_hat = v / (1.0 - beta2 ** t)", "v_hat = v"),
+    "bias_exponent_off_by_one": ("beta2 ** t)", "beta2 ** (t + 1))"),
+    "coupled_decay": ("p = p * (1.0 - lr * weight_decay)", "g = g + weight_decay * p"),
+    "decay_not_scaled_by_lr": ("p = p * (1.0 - lr * weight_decay)", "p = p * (1.0 - weight_decay)"),
+    "decay_after_update": ("    p = p * (1.0 - lr * weight_decay)\n", "    p0 = p\n"),
+    "velocity_of_abs_grad": ("(1.0 - beta2) * g * g", "(1.0 - beta2) * np.abs(g)"),
+    "eps_inside_sqrt": ("(np.sqrt(v_hat) + eps)", "np.sqrt(v_hat + eps)"),
+    "momentum_betas_swapped": ("beta1 * m + (1.0 - beta1) * g", "(1.0 - beta1) * m + beta1 * g"),
+    "step_zero_updates": ("if t <= 0:", "if t < 0:"),
+    "sign_of_step": ("p = p - lr * m_hat", "p = p + lr * m_hat"),
+    "wrong_adapter_hparams": ('h["lr"], h["beta1"]', 'hparams[0]["lr"], h["beta1"]'),
+}
 
-def _mutant(old, new) -> types.ModuleType:
-    with open(SRC) as f:
+
+def _mutant(old, new, src_path=SRC) -> types.ModuleType:
+    with open(src_path) as f:
         src = f.read()
     assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
     src = src.replace(old, new, 1)
@@ -59,5 +76,18 @@ def test_pins_catch_planted_mistake(name):
         try:
             pin(mod)
         except Exception as e:  # AssertionError or a shape error both mean "caught"
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutation {name}"
+
+
+@pytest.mark.parametrize("name", sorted(ADAMW_MUTATIONS))
+def test_adamw_pins_catch_planted_mistake(name):
+    old, new = ADAMW_MUTATIONS[name]
+    mod = _mutant(old, new, SRC_ADAMW)
+    caught = []
+    for pin in pins_adamw.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:
             caught.append((pin.__name__, type(e).__name__))
     assert caught, f"no pin caught mutation {name}"

@@ -15,3 +15,10 @@ def test_max_rel_err_definition():
     assert ol.max_rel_err(np.zeros(3), np.zeros(3)) == 0.0
     assert ol.max_rel_err(np.ones(3), np.zeros(3)) == float("inf")
     assert ol.max_rel_err(np.asarray([1.0, 2.5]), np.asarray([1.0, 2.0])) == 0.25
+
+
+@pytest.mark.parametrize("pin", __import__("tests.pins_adamw", fromlist=["ALL_PINS"]).ALL_PINS,
+                         ids=lambda f: f.__name__)
+def test_adamw_pin(pin):
+    from oracle import adamw
+    pin(adamw)
