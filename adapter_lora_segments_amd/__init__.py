@@ -5,6 +5,6 @@ The compute lives in ``libmlora.so`` (HIP, gfx950, built in-tree by
 Importing the binding does not load the library; the first call does, and
 fails loudly if it has not been built.
 """
-from .binding import (Plan, PackedLoRALinear, mlora_plan, mlora_forward, mlora_backward,  # noqa: F401
-                      pointer_table, device_check)
+from .binding import (Plan, PackedLoRALinear, AdamW, mlora_plan, mlora_forward,  # noqa: F401
+                      mlora_backward, mlora_adamw_step, adamw_hparams, pointer_table, device_check)
 from ._lib import MloraError, lib  # noqa: F401

@@ -15,15 +15,15 @@ W0_LAYOUTS = {"kn": 0, "nk": 1}
 
 TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
           "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count", "tiles", "tile_start", "ext",
-          "tile_ext_start", "offsets", "ranks", "perm"]
-TABLE_COLS = {"nb": 3, "chunks": 3, "tiles": 2, "ext": 4}
+          "tile_ext_start", "offsets", "ranks", "perm", "opt_blocks"]
+TABLE_COLS = {"nb": 3, "chunks": 3, "tiles": 2, "ext": 4, "opt_blocks": 2}
 TABLE_I64 = {"zoff", "offsets"}
 
-KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep"]
+KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep", "adamw"]
 
 # every symbol include/mlora.h declares
 EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
-           "mlora_plan_upload", "mlora_forward", "mlora_backward", "mlora_profile_enable",
+           "mlora_plan_upload", "mlora_forward", "mlora_backward", "mlora_adamw_step", "mlora_profile_enable",
            "mlora_profile_read", "mlora_device_check", "mlora_status_string", "mlora_last_error",
            "mlora_version"]
 
@@ -42,7 +42,13 @@ class PlanInfo(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64), ("table_bytes", ctypes.c_int64),
                 ("rpad_total", ctypes.c_int64), ("partial_rows", ctypes.c_int64),
                 ("n_nano", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
-                ("n_tiles", ctypes.c_int64), ("n_ext", ctypes.c_int64)]
+                ("n_tiles", ctypes.c_int64), ("n_ext", ctypes.c_int64),
+                ("n_opt_blocks", ctypes.c_int64)]
+
+
+class AdamwHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32)]
 
 
 class MloraError(RuntimeError):
@@ -87,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.mlora_forward.restype = i32
     L.mlora_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.mlora_backward.restype = i32
+    L.mlora_adamw_step.argtypes = [vp] + [vp] * 11 + [vp, sz, vp]
+    L.mlora_adamw_step.restype = i32
     L.mlora_profile_enable.argtypes = [vp, i32]
     L.mlora_profile_enable.restype = i32
     L.mlora_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]

@@ -210,6 +210,37 @@ def mlora_backward(plan: Plan, dY, X, W0, A_ptrs, B_ptrs, scales, Z, dX, dA_ptrs
     return dX
 
 
+def adamw_hparams(hparams: Sequence[dict], device="cuda"):
+    """Device array of mlora_adamw_hparams from per-adapter mappings with
+    lr, beta1, beta2, eps, weight_decay and step."""
+    torch = _torch()
+    arr = (_lib.AdamwHparams * len(hparams))()
+    for k, h in enumerate(hparams):
+        arr[k] = _lib.AdamwHparams(h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"],
+                                   int(h["step"]))
+    raw = np.frombuffer(bytes(arr), dtype=np.uint8).copy()
+    return torch.from_numpy(raw).to(device)
+
+
+def mlora_adamw_step(plan: Plan, hparams, A_ptrs, B_ptrs, dA_ptrs, dB_ptrs, mA_ptrs, vA_ptrs,
+                     mB_ptrs, vB_ptrs, A_copy_ptrs, B_copy_ptrs, ws, stream=None):
+    """One AdamW step of every adapter (fp32 masters and moments through the
+    pointer tables; optional bf16 copies)."""
+    torch = _torch()
+    n = plan.info["n"]
+    _check_t(hparams, "hparams", (n * ctypes.sizeof(_lib.AdamwHparams),), torch.uint8)
+    for nm, t in (("A_ptrs", A_ptrs), ("B_ptrs", B_ptrs), ("dA_ptrs", dA_ptrs), ("dB_ptrs", dB_ptrs),
+                  ("mA_ptrs", mA_ptrs), ("vA_ptrs", vA_ptrs), ("mB_ptrs", mB_ptrs), ("vB_ptrs", vB_ptrs)):
+        _check_t(t, nm, (n,), torch.int64)
+    for nm, t in (("A_copy_ptrs", A_copy_ptrs), ("B_copy_ptrs", B_copy_ptrs)):
+        if t is not None:
+            _check_t(t, nm, (n,), torch.int64)
+    check(lib().mlora_adamw_step(plan.handle, _p(hparams), _p(A_ptrs), _p(B_ptrs), _p(dA_ptrs),
+                                 _p(dB_ptrs), _p(mA_ptrs), _p(vA_ptrs), _p(mB_ptrs), _p(vB_ptrs),
+                                 _p(A_copy_ptrs), _p(B_copy_ptrs), _p(ws), ws.numel(),
+                                 _stream(stream)))
+
+
 def device_check() -> None:
     check(lib().mlora_device_check())
 
@@ -258,3 +289,41 @@ class PackedLoRALinear:
         mlora_backward(self.plan, dY, X, self.W0, self.A_ptrs, self.B_ptrs, self.scales, self.Z,
                        dX if want_dx else None, self.dA_ptrs, self.dB_ptrs, self.ws, stream)
         return dX
+
+
+class AdamW:
+    """Per-adapter AdamW state of a PackedLoRALinear: fp32 master weights,
+    first and second moments, and their pointer tables.
+
+    For a bf16 layer the masters start as the fp32 values of the layer's bf16
+    A_i and B_i, and every ``step`` writes the updated masters back into those
+    bf16 tensors (rounded to nearest even), so the next forward uses them.
+    For an fp32 layer the layer's own A_i and B_i are the masters.  Gradients
+    are the layer's dA_i and dB_i as the last backward wrote them.
+    """
+
+    def __init__(self, layer: PackedLoRALinear, device="cuda"):
+        torch = _torch()
+        self.layer = layer
+        bf16 = layer.plan.dtype == "bf16"
+        self.A = [a.float().clone() for a in layer.A] if bf16 else layer.A
+        self.B = [b.float().clone() for b in layer.B] if bf16 else layer.B
+        self.mA = [torch.zeros_like(a) for a in self.A]
+        self.vA = [torch.zeros_like(a) for a in self.A]
+        self.mB = [torch.zeros_like(b) for b in self.B]
+        self.vB = [torch.zeros_like(b) for b in self.B]
+        tab = lambda ts: pointer_table(ts, device)
+        self.A_ptrs, self.B_ptrs = tab(self.A), tab(self.B)
+        self.mA_ptrs, self.vA_ptrs = tab(self.mA), tab(self.vA)
+        self.mB_ptrs, self.vB_ptrs = tab(self.mB), tab(self.vB)
+        self.copies = (layer.A_ptrs, layer.B_ptrs) if bf16 else (None, None)
+
+    def step(self, hparams, stream=None):
+        """hparams: per adapter a mapping (lr, beta1, beta2, eps,
+        weight_decay, step), or a device array from ``adamw_hparams``."""
+        hp = hparams if hasattr(hparams, "data_ptr") else adamw_hparams(hparams, self.layer.ws.device)
+        L = self.layer
+        mlora_adamw_step(L.plan, hp, self.A_ptrs, self.B_ptrs, L.dA_ptrs, L.dB_ptrs, self.mA_ptrs,
+                         self.vA_ptrs, self.mB_ptrs, self.vB_ptrs, self.copies[0], self.copies[1],
+                         L.ws, stream)
+        return hp

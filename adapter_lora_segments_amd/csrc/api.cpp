@@ -12,6 +12,8 @@
 #include "kernels.hpp"
 #include "plan.hpp"
 
+static_assert(mlora::kOptBlockElems == mlora::kOptBlock, "optimizer piece size differs");
+
 namespace {
 
 thread_local std::string g_err;
@@ -86,6 +88,7 @@ mlora::DevTables dev_tables(const mlora_plan_s* p, void* ws) {
   t.ext = reinterpret_cast<const int32_t*>(b + L.ext);
   t.zero = reinterpret_cast<const uint16_t*>(b + L.zero);
   t.perm = p->P.perm.empty() ? nullptr : reinterpret_cast<const int32_t*>(b + L.perm);
+  t.oblk = reinterpret_cast<const int32_t*>(b + L.oblk);
   return t;
 }
 
@@ -311,6 +314,7 @@ mlora_status mlora_plan_get_info(mlora_plan_t p, mlora_plan_info* info) {
   i.n_chunks = P.n_chunks();
   i.n_tiles = P.n_tiles();
   i.n_ext = P.n_ext();
+  i.n_opt_blocks = P.n_oblk();
   *info = i;
   return MLORA_OK;
 }
@@ -341,6 +345,7 @@ mlora_status mlora_plan_export(mlora_plan_t p, int32_t table, void* dst, size_t*
     case MLORA_TAB_OFFSETS: v64(P.offsets); break;
     case MLORA_TAB_RANKS: v32(P.ranks); break;
     case MLORA_TAB_PERM: v32(P.perm); break;
+    case MLORA_TAB_OPT_BLOCKS: v32(P.oblk); break;
     default: return fail(MLORA_ERR_INVALID_ARG, "unknown table id " + std::to_string(table));
   }
   if (!dst) {
@@ -577,6 +582,47 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     if (e != hipSuccess) return hip_fail(e, "join of the weight-gradient stream");
   }
   return join_groups(p, cs);
+}
+
+mlora_status mlora_adamw_step(mlora_plan_t p, const mlora_adamw_hparams* hparams, void* const* A,
+                              void* const* B, const void* const* dA, const void* const* dB,
+                              void* const* mA, void* const* vA, void* const* mB, void* const* vB,
+                              void* const* A_copy, void* const* B_copy, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
+  for (const void* q : {(const void*)hparams, (const void*)A, (const void*)B, (const void*)dA,
+                        (const void*)dB, (const void*)mA, (const void*)vA, (const void*)mB,
+                        (const void*)vB})
+    if (!q || !aligned16(q))
+      return fail(MLORA_ERR_INVALID_ARG,
+                  "adamw: hparams, A, B, dA, dB, mA, vA, mB and vB must be non-NULL and 16-byte aligned");
+  if ((A_copy == nullptr) != (B_copy == nullptr))
+    return fail(MLORA_ERR_INVALID_ARG, "adamw: A_copy and B_copy must be both NULL or both non-NULL");
+  if (A_copy && p->P.dtype != MLORA_BF16)
+    return fail(MLORA_ERR_INVALID_ARG, "adamw: an fp32 plan takes no weight copies (A_copy, B_copy must be NULL)");
+  if (A_copy && (!aligned16(A_copy) || !aligned16(B_copy)))
+    return fail(MLORA_ERR_INVALID_ARG, "adamw: A_copy and B_copy must be 16-byte aligned");
+  if (!p->P.oblk_ok)
+    return fail(MLORA_ERR_UNSUPPORTED, "adamw: the layer has more than 2^27 optimizer work items");
+  mlora_status st = check_ws(p, ws, ws_bytes);
+  if (st != MLORA_OK) return st;
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  mlora::AdamwArgs a;
+  a.t = dev_tables(p, ws);
+  a.hp = hparams;
+  a.d_in = p->P.d_in;
+  a.d_out = p->P.d_out;
+  a.A = reinterpret_cast<float* const*>(A);
+  a.B = reinterpret_cast<float* const*>(B);
+  a.dA = reinterpret_cast<const float* const*>(dA);
+  a.dB = reinterpret_cast<const float* const*>(dB);
+  a.mA = reinterpret_cast<float* const*>(mA);
+  a.vA = reinterpret_cast<float* const*>(vA);
+  a.mB = reinterpret_cast<float* const*>(mB);
+  a.vB = reinterpret_cast<float* const*>(vB);
+  a.A_copy = reinterpret_cast<uint16_t* const*>(A_copy);
+  a.B_copy = reinterpret_cast<uint16_t* const*>(B_copy);
+  return timed(p, MLORA_K_ADAMW, cs, [&] { mlora::launch_adamw(a, p->P.n_oblk(), cs); });
 }
 
 mlora_status mlora_profile_enable(mlora_plan_t p, int32_t mask) {

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/mlora.h"
+
 namespace mlora {
 
 // Device copies of the plan tables (pointers into the workspace).
@@ -24,6 +26,7 @@ struct DevTables {
   const int32_t* ext;       // [n_ext][4]
   const uint16_t* zero;     // 256 zero bytes
   const int32_t* perm;      // [T] grouped row -> caller row, or NULL (rows already grouped)
+  const int32_t* oblk;      // [n_oblk][2] optimizer work items (tensor, piece)
 };
 
 // ---------------- bf16 path (MFMA) ----------------
@@ -100,5 +103,30 @@ void launch_f32_db(const DevTables& t, int32_t n, int64_t d_out, const float* Z,
                    void* const* dB, int32_t max_rank, hipStream_t s);
 void launch_f32_da(const DevTables& t, int32_t n, int64_t d_in, const float* X, const float* dZ,
                    void* const* dA, int32_t max_rank, hipStream_t s);
+
+// ---------------- optimizer step ----------------
+
+constexpr int kOptBlockElems = 2048;  // elements per optimizer work item (the plan's piece size)
+
+// One AdamW update of every adapter's fp32 A_i and B_i with its own
+// hyperparameters (work items [0, n_blocks) of the plan's optimizer table);
+// A_copy/B_copy (bf16, or NULL arrays) receive the updated values rounded to
+// nearest even.
+struct AdamwArgs {
+  DevTables t;
+  const mlora_adamw_hparams* hp;  // [n]
+  int64_t d_in, d_out;
+  float* const* A;
+  float* const* B;
+  const float* const* dA;
+  const float* const* dB;
+  float* const* mA;
+  float* const* vA;
+  float* const* mB;
+  float* const* vB;
+  uint16_t* const* A_copy;
+  uint16_t* const* B_copy;
+};
+void launch_adamw(const AdamwArgs& a, int64_t n_blocks, hipStream_t s);
 
 }  // namespace mlora

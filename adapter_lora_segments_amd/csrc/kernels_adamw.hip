@@ -1,0 +1,98 @@
+// Per-adapter AdamW step for gfx950: one pass over every adapter's fp32
+// weights, gradients and moments.
+//
+// Every packed adapter owns its weights and optimizer state (PLoRA: Efficient
+// Concurrent LoRA Training for Large Language Models, §2.4) and its own
+// hyperparameters (§2.2, §11.1); AdamW keeps a momentum and a velocity beside
+// each weight (§8).  The update is elementwise and reads 16 and writes 12
+// bytes per weight (14 with the bf16 copy), so it is bound by HBM bandwidth:
+// the kernel streams 16-byte vectors, issues all of a thread's loads before
+// the arithmetic, and takes its work items from a plan table of fixed-size
+// pieces, so tensors of any rank share one launch.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace mlora {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVecPerThread = kOptBlockElems / (4 * kThreads);
+
+}  // namespace
+
+template <bool COPY>
+__global__ __launch_bounds__(kThreads) void k_adamw(AdamwArgs a) {
+  const int tsr = ldc(a.t.oblk + 2 * blockIdx.x);
+  const int piece = ldc(a.t.oblk + 2 * blockIdx.x + 1);
+  const int i = tsr >> 1;
+  const bool isB = tsr & 1;
+  const mlora_adamw_hparams* hp = a.hp + i;
+  const int32_t step = ldc(&hp->step);
+  if (step <= 0) return;  // whole workgroup: the adapter is not stepped
+  const float lr = ldc(&hp->lr), beta1 = ldc(&hp->beta1), beta2 = ldc(&hp->beta2);
+  const float eps = ldc(&hp->eps), wd = ldc(&hp->weight_decay);
+
+  const int64_t numel = (int64_t)ldc(a.t.ranks + i) * (isB ? a.d_out : a.d_in);
+  const int64_t base = (int64_t)piece * kOptBlockElems + 4 * threadIdx.x;
+  float* p = ldc((isB ? a.B : a.A) + i);
+  const float* g = ldc((isB ? a.dB : a.dA) + i);
+  float* m = ldc((isB ? a.mB : a.mA) + i);
+  float* v = ldc((isB ? a.vB : a.vA) + i);
+
+  // Bias corrections 1 - beta^t as -expm1(t log beta): no cancellation for
+  // betas near 1; a beta of 0 gives exactly 1.
+  const float t = (float)step;
+  const float bc1 = -expm1f(t * logf(beta1));
+  const float bc2 = -expm1f(t * logf(beta2));
+  const float step_size = lr / bc1;
+  const float inv_sqrt_bc2 = 1.0f / sqrtf(bc2);
+  const float decay = 1.0f - lr * wd;
+  const float omb1 = 1.0f - beta1, omb2 = 1.0f - beta2;
+
+  f32x4 P[kVecPerThread], G[kVecPerThread], M[kVecPerThread], V[kVecPerThread];
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int64_t e = base + (int64_t)u * 4 * kThreads;
+    if (e < numel) {  // numel is a multiple of 64: a vector is wholly in or out
+      P[u] = *reinterpret_cast<const f32x4*>(p + e);
+      G[u] = *reinterpret_cast<const f32x4*>(g + e);
+      M[u] = *reinterpret_cast<const f32x4*>(m + e);
+      V[u] = *reinterpret_cast<const f32x4*>(v + e);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int64_t e = base + (int64_t)u * 4 * kThreads;
+    if (e >= numel) continue;
+    f32x4 pn, mn, vn;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float gc = G[u][c];
+      const float mc = fmaf(beta1, M[u][c], omb1 * gc);
+      const float vc = fmaf(beta2, V[u][c], omb2 * (gc * gc));
+      const float den = sqrtf(vc) * inv_sqrt_bc2 + eps;
+      pn[c] = P[u][c] * decay - step_size * (mc / den);
+      mn[c] = mc;
+      vn[c] = vc;
+    }
+    *reinterpret_cast<f32x4*>(p + e) = pn;
+    *reinterpret_cast<f32x4*>(m + e) = mn;
+    *reinterpret_cast<f32x4*>(v + e) = vn;
+    if constexpr (COPY) {
+      uint16_t* w = ldc((isB ? a.B_copy : a.A_copy) + i);
+      *reinterpret_cast<u32x2*>(w + e) = u32x2{pack_bf16x2(pn[0], pn[1]), pack_bf16x2(pn[2], pn[3])};
+    }
+  }
+}
+
+void launch_adamw(const AdamwArgs& a, int64_t n_blocks, hipStream_t s) {
+  if (n_blocks <= 0) return;
+  const dim3 grid((unsigned)n_blocks), block(kThreads);
+  if (a.A_copy)
+    hipLaunchKernelGGL(k_adamw<true>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(k_adamw<false>, grid, block, 0, s, a);
+}
+
+}  // namespace mlora

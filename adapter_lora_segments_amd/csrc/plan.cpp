@@ -217,6 +217,24 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
   p.tile_start.push_back((int32_t)p.n_tiles());
   p.ext_start.push_back((int32_t)p.n_ext());
 
+  // 8: optimizer work items, A_i then B_i of every adapter in pieces of
+  // kOptBlock elements
+  int64_t nob = 0;
+  for (int32_t i = 0; i < n; ++i)
+    nob += (d_in * ranks[i] + kOptBlock - 1) / kOptBlock + (ranks[i] * d_out + kOptBlock - 1) / kOptBlock;
+  p.oblk_ok = nob <= kMaxOptBlocks;
+  if (p.oblk_ok) {
+    p.oblk.reserve((size_t)(2 * nob));
+    for (int32_t i = 0; i < n; ++i) {
+      const int64_t numel[2] = {d_in * ranks[i], ranks[i] * d_out};
+      for (int w = 0; w < 2; ++w)
+        for (int64_t q = 0; q * kOptBlock < numel[w]; ++q) {
+          p.oblk.push_back(2 * i + w);
+          p.oblk.push_back((int32_t)q);
+        }
+    }
+  }
+
   P = std::move(p);
   return MLORA_OK;
 }
@@ -283,6 +301,7 @@ DeviceLayout device_layout(const PlanTables& p) {
   L.ext_start = take(4 * p.ext_start.size());
   L.ext = take(4 * p.ext.size());
   L.perm = take(4 * p.perm.size());
+  L.oblk = take(4 * p.oblk.size());
   L.zero = take(256);  // a zero page: loads of rows that must read as zero point here
   L.table_bytes = off;
   const size_t esz = p.dtype == MLORA_BF16 ? 2 : 4;
@@ -323,6 +342,7 @@ std::vector<uint8_t> table_blob(const PlanTables& p, const DeviceLayout& L) {
   put(L.ext_start, p.ext_start.data(), 4 * p.ext_start.size());
   put(L.ext, p.ext.data(), 4 * p.ext.size());
   put(L.perm, p.perm.data(), 4 * p.perm.size());
+  put(L.oblk, p.oblk.data(), 4 * p.oblk.size());
   return b;
 }
 

@@ -13,6 +13,8 @@ namespace mlora {
 
 constexpr int kKStep = 32;       // K extent of one extension step
 constexpr int kMinRankPad = 32;  // smallest padded rank (one MFMA tile edge)
+constexpr int kOptBlock = 2048;  // elements per work item of the optimizer step
+constexpr int64_t kMaxOptBlocks = int64_t(1) << 27;  // larger layers get no optimizer table
 
 struct Opts {
   int32_t nano_rows = 32;
@@ -40,11 +42,14 @@ struct PlanTables {
   std::vector<int32_t> tiles, tile_start;          // tiles: [n_tiles][2]
   std::vector<int32_t> ext, ext_start;             // ext: [n_ext][4]
   std::vector<int32_t> perm;  // [T] grouped row -> caller row (plans from ids; empty otherwise)
+  std::vector<int32_t> oblk;  // [n_oblk][2] optimizer work items (tensor 2i: A_i, 2i+1: B_i; piece)
+  bool oblk_ok = true;        // false: the layer is too large for the optimizer table
 
   int64_t n_nano() const { return (int64_t)nano.size() / 3; }
   int64_t n_chunks() const { return (int64_t)chunks.size() / 3; }
   int64_t n_tiles() const { return (int64_t)tiles.size() / 2; }
   int64_t n_ext() const { return (int64_t)ext.size() / 4; }
+  int64_t n_oblk() const { return (int64_t)oblk.size() / 2; }
 };
 
 // Validates and fills `out`.  On error returns the status and a message.
@@ -62,7 +67,7 @@ mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adap
 struct DeviceLayout {
   // offsets (bytes) of each table inside the table blob
   size_t offsets, zoff, ranks, rpad, roff, ch_first, ch_count, nano, chunks, cpref, tiles,
-      ext_start, ext, zero, perm;
+      ext_start, ext, zero, perm, oblk;
   size_t table_bytes;
   // offsets (bytes) of the work buffers inside the workspace
   size_t acat_t, acat, bcat_t, dz, part_a, part_b;

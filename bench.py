@@ -135,6 +135,39 @@ def time_steps(step, steps, warmup):
     return (time.perf_counter() - t0) / steps * 1e3
 
 
+OPT_BYTES_PER_ELEM = 30    # read p, g, m, v (fp32); write p, m, v (fp32) and the bf16 copy
+
+
+def optimizer_step(w, plan, layer, steps, warmup, seed):
+    """The per-adapter AdamW step over the layer's adapters (fp32 masters and
+    moments, bf16 copies written back into the layer's A_i, B_i), with every
+    adapter stepping: launch time from events on its stream, against the HBM
+    roofline of its algorithmic bytes."""
+    import torch
+    from adapter_lora_segments_amd import AdamW, adamw_hparams
+    from workloads import optim
+    opt = AdamW(layer)
+    hps = [dict(h, start=0) for h in optim.hyperparameters(w.n, seed)]
+    hp = adamw_hparams(optim.step_hparams(hps, 0))
+    for _ in range(warmup):
+        opt.step(hp)
+    torch.cuda.synchronize()
+    plan.profile_enable(["adamw"])
+    plan.profile_read()
+    for _ in range(steps):
+        opt.step(hp)
+    torch.cuda.synchronize()
+    tot_ms, n = plan.profile_read()["adamw"]
+    plan.profile_enable(False)
+    avg = tot_ms / max(n, 1)
+    elems = sum(int(r) * (plan.info["d_in"] + plan.info["d_out"]) for r in plan.ranks)
+    gbs = OPT_BYTES_PER_ELEM * elems / (avg * 1e-3) / 1e9
+    return {"kernel": "k_adamw (per-adapter AdamW, bf16 copies)", "elements": elems,
+            "bytes_per_launch": OPT_BYTES_PER_ELEM * elems, "avg_launch_ms": avg, "launches": n,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS}}
+
+
 def sequential_layers(w, q, d, sets):
     """The same work as one library call per adapter: a one-adapter plan per
     non-empty segment over its own rows (row slices of the packed tensors)."""
@@ -227,6 +260,9 @@ def main():
     ap.add_argument("--shuffled-ids", action="store_true",
                     help="rows in a shuffled caller order with one adapter id per token "
                          "(mlora_plan_from_ids) instead of contiguous segments")
+    ap.add_argument("--no-optimizer", action="store_true",
+                    help="skip timing the per-adapter AdamW step (mlora_adamw_step) of the first "
+                         "timed projection")
     ap.add_argument("--packing-sweep", action="store_true",
                     help="only run the packed-against-sequential sweep over Table 7's shapes and "
                          "print its results as one JSON line")
@@ -353,6 +389,10 @@ def main():
                                                                 layers[0][4][i % SETS])),
                                min(a.steps, 50), min(a.warmup, 10))
 
+    opt_out = None
+    if prof and not a.no_optimizer:
+        opt_out = optimizer_step(w, layers[0][0], layers[0][1], a.steps, a.warmup, a.seed)
+
     ms = el / a.steps * 1e3
     tok_s = w.T * a.steps / el
     F = sum(alg_flops(w, q) for q in projs)
@@ -402,6 +442,8 @@ def main():
             "projection": w.projections[projs[0]].name, "packed_ms_per_step": packed_ms,
             "sequential_ms_per_step": seq_ms, "speedup": seq_ms / packed_ms,
             "sequential": f"{len(seq)} one-adapter library calls, each over its own rows"}
+    if opt_out is not None:
+        out["optimizer"] = opt_out
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, projs)
     print(json.dumps(out), flush=True)

@@ -148,6 +148,7 @@ typedef struct {
   int64_t table_bytes;       /* leading part of the workspace holding the tables */
   int64_t rpad_total, partial_rows;
   int64_t n_nano, n_chunks, n_tiles, n_ext;
+  int64_t n_opt_blocks;      /* optimizer work items (0: layer too large, see mlora_adamw_step) */
 } mlora_plan_info;
 
 mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);
@@ -160,7 +161,10 @@ mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);
  *   ADAPTER_CHUNK_FIRST[n], ADAPTER_CHUNK_COUNT[n],
  *   TILES[n_tiles][2] (row0, rows), TILE_START[S'+1],
  *   EXT[n_ext][4] (adapter, lo, hi, k0), TILE_EXT_START[n_tiles+1],
- *   OFFSETS[n+1], RANKS[n], PERM[T] (plans from ids; empty otherwise). */
+ *   OFFSETS[n+1], RANKS[n], PERM[T] (plans from ids; empty otherwise),
+ *   OPT_BLOCKS[n_opt_blocks][2] (tensor, piece): the work items of
+ *   mlora_adamw_step, for every adapter i ascending A_i (tensor 2i) then B_i
+ *   (tensor 2i+1), each cut into pieces of 2048 elements. */
 typedef enum {
   MLORA_TAB_RPAD = 0,
   MLORA_TAB_ZOFF,
@@ -180,6 +184,7 @@ typedef enum {
   MLORA_TAB_OFFSETS,
   MLORA_TAB_RANKS,
   MLORA_TAB_PERM,
+  MLORA_TAB_OPT_BLOCKS,
   MLORA_TAB_COUNT
 } mlora_table;
 
@@ -222,6 +227,52 @@ mlora_status mlora_backward(mlora_plan_t plan, const void *dY, const void *X, co
                             const void *Z, void *dX, void *const *dA, void *const *dB,
                             void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Per-adapter optimizer hyperparameters for mlora_adamw_step.  step is the
+ * number of this update for the adapter (1 for its first), used in the bias
+ * corrections; an adapter with step <= 0 is skipped: its weights, moments and
+ * copies are left untouched.  Useful ranges: lr >= 0, 0 <= beta1, beta2 < 1,
+ * eps > 0; the values live in device memory and are not checked (a beta of 1
+ * gives that adapter a zero bias correction and IEEE inf/NaN weights, never
+ * a fault).
+ */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int32_t step;
+} mlora_adamw_hparams;
+
+/*
+ * mlora_adamw_step -- one AdamW update of every adapter's A_i and B_i, each
+ * adapter with its own hyperparameters and state (PLoRA §2.4: every packed
+ * adapter keeps its own parameters and optimizer state; §8: AdamW keeps a
+ * momentum and a velocity per trained parameter; §2.2 and §11.1: learning
+ * rate and the other knobs differ per configuration).  The pages do not
+ * write AdamW out; the update is Adam with decoupled weight decay scaled by
+ * the learning rate (the torch.optim.AdamW form), per element:
+ *   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2
+ *   p <- p - (lr / (1 - b1^step)) m / (sqrt(v / (1 - b2^step)) + eps)
+ * in fp32.
+ *
+ * hparams: device array of n mlora_adamw_hparams.  A, B: device arrays of n
+ * device pointers to the fp32 master weights ([d_in][r_i] and [r_i][d_out]),
+ * updated in place.  dA, dB: fp32 gradients as mlora_backward writes them.
+ * mA, vA, mB, vB: fp32 first and second moments, same shapes, updated in
+ * place (zero them before an adapter's first step).  A_copy, B_copy: for a
+ * bf16 plan, NULL or device arrays of pointers to the bf16 weights the
+ * forward and backward read, overwritten with the updated masters rounded to
+ * nearest even (both or neither); for an fp32 plan both must be NULL (the
+ * masters are the weights).  No two of the buffers may overlap.  The work
+ * items are the plan's OPT_BLOCKS table, so the workspace must hold the
+ * uploaded tables; the call writes nothing else in it.  MLORA_ERR_UNSUPPORTED
+ * when the layer has more than 2^27 work items (n_opt_blocks = 0).
+ */
+mlora_status mlora_adamw_step(mlora_plan_t plan, const mlora_adamw_hparams *hparams,
+                              void *const *A, void *const *B, const void *const *dA,
+                              const void *const *dB, void *const *mA, void *const *vA,
+                              void *const *mB, void *const *vB, void *const *A_copy,
+                              void *const *B_copy, void *workspace, size_t ws_bytes,
+                              void *stream);
+
 /* Per-kernel timing.  Launches of the selected kinds are bracketed by HIP
  * events on the stream they run on; mlora_profile_read waits for them, adds
  * their durations to the totals of kernel `kind` and returns them, then
@@ -235,6 +286,7 @@ typedef enum {
   MLORA_K_REDUCE,        /* fixed-order sum of the chunk partials            */
   MLORA_K_GEMM_DX,       /* dX = dY W0^T + dZ A^T (B4)                       */
   MLORA_K_PREP,          /* rank-padded concatenations of A and B            */
+  MLORA_K_ADAMW,         /* per-adapter AdamW step (mlora_adamw_step)        */
   MLORA_K_COUNT
 } mlora_kernel_kind;
 

@@ -13,7 +13,7 @@ from hypothesis import given, settings, strategies as st
 from adapter_lora_segments_amd import _lib
 from adapter_lora_segments_amd.binding import Plan
 from adapter_lora_segments_amd._lib import MloraError
-from oracle.plan_mirror import build_plan, PlanOpts
+from oracle.plan_mirror import build_plan, optimizer_blocks, PlanOpts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -49,6 +49,8 @@ def _mirror_vs_library(off, ranks, d_in, d_out, dtype, opts):
     assert p.info["rpad_total"] == m["rpad_total"]
     assert p.info["n_groups"] == m["n_groups"]
     assert np.array_equal(p.export("offsets"), np.asarray(off, dtype=np.int64))
+    ob = optimizer_blocks(ranks, d_in, d_out)
+    assert np.array_equal(p.export("opt_blocks"), ob) and p.info["n_opt_blocks"] == ob.shape[0]
 
 
 @st.composite
@@ -183,3 +185,51 @@ def test_plan_info_sizes():
     i = p.info
     assert i["T"] == 300 and i["n"] == 4 and i["z_elems"] == 24960 and i["z_bytes"] == 2 * 24960
     assert i["workspace_bytes"] >= i["table_bytes"] + 2 * i["z_elems"] + 4 * i["partial_rows"] * (256 + 512)
+
+
+def test_optimizer_blocks_cover_every_element_once():
+    """Rule 8 read back from the library: the pieces of each tensor tile its
+    elements exactly once, adapters ascending, A before B."""
+    ranks = [1, 7, 64, 256, 3]
+    d_in, d_out = 192, 4096
+    p = Plan([0, 3, 3, 10, 11, 20], ranks, d_in, d_out)
+    ob = p.export("opt_blocks")
+    assert ob.dtype == np.int32 and ob.shape == (p.info["n_opt_blocks"], 2)
+    tensors = ob[:, 0]
+    assert np.all(np.diff(tensors) >= 0)
+    for t in range(2 * len(ranks)):
+        r = ranks[t // 2]
+        numel = r * (d_out if t % 2 else d_in)
+        pieces = ob[tensors == t, 1]
+        assert np.array_equal(pieces, np.arange(-(-numel // 2048))), t
+
+
+def test_adamw_rejects_bad_arguments_without_launching():
+    L = _lib.lib()
+    vp = ctypes.c_void_p
+    d = vp(4096)
+    ok = [d] * 9                      # hparams, A, B, dA, dB, mA, vA, mB, vB
+    bf = Plan([0, 5, 9], [4, 8], 128, 64)
+    f32 = Plan([0, 5, 9], [4, 8], 128, 64, "fp32")
+    assert L.mlora_adamw_step(None, *ok, None, None, d, 1 << 30, None) == -1
+    for k in range(9):                # each required array NULL, then misaligned
+        args = list(ok)
+        args[k] = None
+        assert L.mlora_adamw_step(bf.handle, *args, None, None, d, 1 << 30, None) == -1, k
+        args[k] = vp(4100)
+        assert L.mlora_adamw_step(bf.handle, *args, None, None, d, 1 << 30, None) == -1, k
+    assert L.mlora_adamw_step(bf.handle, *ok, d, None, d, 1 << 30, None) == -1      # one copy only
+    assert L.mlora_adamw_step(f32.handle, *ok, d, d, d, 1 << 30, None) == -1        # fp32 takes none
+    assert "fp32" in L.mlora_last_error().decode()
+    assert L.mlora_adamw_step(bf.handle, *ok, d, d, d, 16, None) == -4              # workspace small
+    assert L.mlora_adamw_step(bf.handle, *ok, None, None, d, 1 << 30, None) == -4   # not uploaded
+    assert _lib.KERNELS[-1] == "adamw" and len(_lib.KERNELS) == 8
+
+
+def test_adamw_hparams_layout():
+    """The ctypes mirror of mlora_adamw_hparams: five floats then the step."""
+    assert ctypes.sizeof(_lib.AdamwHparams) == 24
+    h = _lib.AdamwHparams(1e-4, 0.9, 0.999, 1e-8, 0.01, 3)
+    raw = np.frombuffer(bytes(h), dtype=np.uint8)
+    assert np.array_equal(raw[:20].view(np.float32), np.float32([1e-4, 0.9, 0.999, 1e-8, 0.01]))
+    assert raw[20:].view(np.int32)[0] == 3

@@ -171,4 +171,6 @@ def test_profile_mask_selects_kernels():
     torch.cuda.synchronize()
     r = plan.profile_read()
     plan.profile_enable(False)
-    assert all(cnt > 0 for k, (ms, cnt) in r.items()), r
+    # every kind the forward and backward launch (the optimizer step is a call of its own)
+    assert all(cnt > 0 for k, (ms, cnt) in r.items() if k != "adamw"), r
+    assert r["adamw"][1] == 0, r
