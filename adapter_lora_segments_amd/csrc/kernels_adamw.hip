@@ -6,9 +6,11 @@
 // hyperparameters (§2.2, §11.1); AdamW keeps a momentum and a velocity beside
 // each weight (§8).  The update is elementwise and reads 16 and writes 12
 // bytes per weight (14 with the bf16 copy), so it is bound by HBM bandwidth:
-// the kernel streams 16-byte vectors, issues all of a thread's loads before
-// the arithmetic, and takes its work items from a plan table of fixed-size
-// pieces, so tensors of any rank share one launch.
+// the kernel streams 16-byte vectors with non-temporal loads and stores
+// (every byte is touched once, so none of it is worth keeping in the caches),
+// issues all of a thread's loads before the arithmetic, and takes its work
+// items from a plan table of fixed-size pieces, so tensors of any rank share
+// one launch.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -18,6 +20,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVecPerThread = kOptBlockElems / (4 * kThreads);
+
+__device__ __forceinline__ f32x4 ld_stream(const float* q) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(q));
+}
+__device__ __forceinline__ void st_stream(float* q, const f32x4& x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(q));
+}
 
 }  // namespace
 
@@ -55,10 +64,10 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwArgs a) {
   for (int u = 0; u < kVecPerThread; ++u) {
     const int64_t e = base + (int64_t)u * 4 * kThreads;
     if (e < numel) {  // numel is a multiple of 64: a vector is wholly in or out
-      P[u] = *reinterpret_cast<const f32x4*>(p + e);
-      G[u] = *reinterpret_cast<const f32x4*>(g + e);
-      M[u] = *reinterpret_cast<const f32x4*>(m + e);
-      V[u] = *reinterpret_cast<const f32x4*>(v + e);
+      P[u] = ld_stream(p + e);
+      G[u] = ld_stream(g + e);
+      M[u] = ld_stream(m + e);
+      V[u] = ld_stream(v + e);
     }
   }
 #pragma unroll
@@ -76,12 +85,13 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwArgs a) {
       mn[c] = mc;
       vn[c] = vc;
     }
-    *reinterpret_cast<f32x4*>(p + e) = pn;
-    *reinterpret_cast<f32x4*>(m + e) = mn;
-    *reinterpret_cast<f32x4*>(v + e) = vn;
+    st_stream(p + e, pn);
+    st_stream(m + e, mn);
+    st_stream(v + e, vn);
     if constexpr (COPY) {
       uint16_t* w = ldc((isB ? a.B_copy : a.A_copy) + i);
-      *reinterpret_cast<u32x2*>(w + e) = u32x2{pack_bf16x2(pn[0], pn[1]), pack_bf16x2(pn[2], pn[3])};
+      __builtin_nontemporal_store(u32x2{pack_bf16x2(pn[0], pn[1]), pack_bf16x2(pn[2], pn[3])},
+                                  reinterpret_cast<u32x2*>(w + e));
     }
   }
 }

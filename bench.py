@@ -263,6 +263,9 @@ def main():
     ap.add_argument("--no-optimizer", action="store_true",
                     help="skip timing the per-adapter AdamW step (mlora_adamw_step) of the first "
                          "timed projection")
+    ap.add_argument("--optimizer-only", action="store_true",
+                    help="run one forward+backward for real gradients, then time only the "
+                         "per-adapter AdamW step of the first projection; one JSON line")
     ap.add_argument("--packing-sweep", action="store_true",
                     help="only run the packed-against-sequential sweep over Table 7's shapes and "
                          "print its results as one JSON line")
@@ -332,6 +335,18 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if a.optimizer_only:
+        step(0)
+        torch.cuda.synchronize()
+        o = optimizer_step(w, layers[0][0], layers[0][1], a.steps, a.warmup, a.seed)
+        p0 = w.projections[0]
+        print(json.dumps({"metric": "per-adapter AdamW step, bytes/s", "value": o["roofline"]["achieved"],
+                          "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+                          "higher_is_better": True, "data": "synthetic", "dtype": "fp32",
+                          "config": {"workload": f"{w.name}: {p0.name} {p0.d_in}x{p0.d_out}, "
+                                                 f"{w.n} adapters, ranks {sorted(set(w.ranks))}"},
+                          "optimizer": o}), flush=True)
+        return
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
