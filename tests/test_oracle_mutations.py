@@ -6,11 +6,12 @@ import types
 
 import pytest
 
-from tests import pins, pins_adamw
+from tests import pins, pins_adamw, pins_multi
 
 ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(ORACLE, "lora.py")
 SRC_ADAMW = os.path.join(ORACLE, "adamw.py")
+SRC_MULTI = os.path.join(ORACLE, "multi.py")
 
 MUTATIONS = {
     "drop_scale_fwd": ("Y[r0:r1] = Xc @ W + s * (Zc @ Bi)", "Y[r0:r1] = Xc @ W + (Zc @ Bi)"),
@@ -57,12 +58,33 @@ ADAMW_MUTATIONS = {
 }
 
 
+MULTI_MUTATIONS = {
+    "fwd_wrong_w0_columns": ("Y[r0:r1, c0:c1] = Xc @ W[:, c0:c1] + s * (Zc @ Bip)",
+                             "Y[r0:r1, c0:c1] = Xc @ W[:, :c1 - c0] + s * (Zc @ Bip)"),
+    "fwd_drop_scale": ("Y[r0:r1, c0:c1] = Xc @ W[:, c0:c1] + s * (Zc @ Bip)",
+                       "Y[r0:r1, c0:c1] = Xc @ W[:, c0:c1] + (Zc @ Bip)"),
+    "fwd_scale_of_projection_0": ("            s = float(scales[i][p])\n            Zip = np.zeros((b - a",
+                                  "            s = float(scales[i][0])\n            Zip = np.zeros((b - a"),
+    "dx_overwrites_projections": ("dX[r0:r1] += Gp @ W[:, c0:c1].T + dZc @ Aip.T",
+                                  "dX[r0:r1] = Gp @ W[:, c0:c1].T + dZc @ Aip.T"),
+    "dx_drop_lora": ("dX[r0:r1] += Gp @ W[:, c0:c1].T + dZc @ Aip.T", "dX[r0:r1] += Gp @ W[:, c0:c1].T"),
+    "dy_columns_of_first_projection": ("Gp = as_f64(dY[r0:r1], dtype)[:, c0:c1]",
+                                       "Gp = as_f64(dY[r0:r1], dtype)[:, 0:c1 - c0]"),
+    "db_drop_scale": ("gB += s * (Zc.T @ Gp)", "gB += (Zc.T @ Gp)"),
+    "columns_off_by_one": ("        c.append(c[-1] + int(d))", "        c.append(c[-1] + int(d) - (1 if len(c) == 2 else 0))"),
+    "sampled_dx_overwrites": ("dX[ks] += g[:, c0:c1] @ W[:, c0:c1].T", "dX[ks] = g[:, c0:c1] @ W[:, c0:c1].T"),
+    "projected_db_wrong_accumulator": ("rb.append(s * (as_f64(A[i][p], dtype).T @ gb[p]))",
+                                       "rb.append(s * (as_f64(A[i][p], dtype).T @ ga[p]))"),
+}
+
+
 def _mutant(old, new, src_path=SRC) -> types.ModuleType:
     with open(src_path) as f:
         src = f.read()
     assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
     src = src.replace(old, new, 1)
-    mod = types.ModuleType("oracle_mutant")
+    mod = types.ModuleType("oracle.oracle_mutant")
+    mod.__package__ = "oracle"
     exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
     return mod
 
@@ -86,6 +108,19 @@ def test_adamw_pins_catch_planted_mistake(name):
     mod = _mutant(old, new, SRC_ADAMW)
     caught = []
     for pin in pins_adamw.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutation {name}"
+
+
+@pytest.mark.parametrize("name", sorted(MULTI_MUTATIONS))
+def test_multi_pins_catch_planted_mistake(name):
+    old, new = MULTI_MUTATIONS[name]
+    mod = _mutant(old, new, SRC_MULTI)
+    caught = []
+    for pin in pins_multi.ALL_PINS:
         try:
             pin(mod)
         except Exception as e:

@@ -22,3 +22,10 @@ def test_max_rel_err_definition():
 def test_adamw_pin(pin):
     from oracle import adamw
     pin(adamw)
+
+
+@pytest.mark.parametrize("pin", __import__("tests.pins_multi", fromlist=["ALL_PINS"]).ALL_PINS,
+                         ids=lambda f: f.__name__)
+def test_multi_pin(pin):
+    from oracle import multi
+    pin(multi)
