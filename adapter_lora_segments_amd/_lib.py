@@ -15,14 +15,15 @@ W0_LAYOUTS = {"kn": 0, "nk": 1}
 
 TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
           "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count", "tiles", "tile_start", "ext",
-          "tile_ext_start", "offsets", "ranks", "perm", "opt_blocks"]
+          "tile_ext_start", "offsets", "ranks", "perm", "opt_blocks", "proj_cols", "seg_start",
+          "chunk_boff"]
 TABLE_COLS = {"nb": 3, "chunks": 3, "tiles": 2, "ext": 4, "opt_blocks": 2}
-TABLE_I64 = {"zoff", "offsets"}
+TABLE_I64 = {"zoff", "offsets", "seg_start", "chunk_boff"}
 
 KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep", "adamw"]
 
 # every symbol include/mlora.h declares
-EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
+EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_multi", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
            "mlora_plan_upload", "mlora_forward", "mlora_backward", "mlora_adamw_step", "mlora_profile_enable",
            "mlora_profile_read", "mlora_device_check", "mlora_status_string", "mlora_last_error",
            "mlora_version"]
@@ -43,7 +44,7 @@ class PlanInfo(ctypes.Structure):
                 ("rpad_total", ctypes.c_int64), ("partial_rows", ctypes.c_int64),
                 ("n_nano", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
                 ("n_tiles", ctypes.c_int64), ("n_ext", ctypes.c_int64),
-                ("n_opt_blocks", ctypes.c_int64)]
+                ("n_opt_blocks", ctypes.c_int64), ("n_proj", ctypes.c_int64)]
 
 
 class AdamwHparams(ctypes.Structure):
@@ -81,6 +82,9 @@ def lib() -> ctypes.CDLL:
     L.mlora_plan_from_ids.argtypes = [i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32), i64, i64, i32,
                                       ctypes.POINTER(PlanOpts), ctypes.POINTER(vp)]
     L.mlora_plan_from_ids.restype = i32
+    L.mlora_plan_multi.argtypes = [i32, ctypes.POINTER(i64), i32, ctypes.POINTER(i64), ctypes.POINTER(i32),
+                                   i64, i32, ctypes.POINTER(PlanOpts), ctypes.POINTER(vp)]
+    L.mlora_plan_multi.restype = i32
     L.mlora_plan_destroy.argtypes = [vp]
     L.mlora_plan_destroy.restype = None
     L.mlora_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]

@@ -22,19 +22,39 @@ def _torch():
 
 
 class Plan:
-    """Host plan for one packed layer (seg_offsets, ranks, d_in, d_out), or,
-    through ``Plan.from_ids``, for rows in the caller's order with one adapter
-    id per token."""
+    """Host plan for one packed layer (seg_offsets, ranks, d_in, d_out); through
+    ``Plan.from_ids``, for rows in the caller's order with one adapter id per
+    token; through ``Plan.multi``, for several projections sharing the input
+    (ranks [n][n_proj], output widths per projection).
+
+    ``ranks`` holds one rank per (adapter, projection) pair in the order
+    i * n_proj + q, the order of the per-adapter pointer and scale arrays."""
 
     def __init__(self, seg_offsets, ranks, d_in: int, d_out: int, dtype: str = "bf16",
                  nano_rows: int = 0, n_streams: int = 0, chunk_min: int = 0, chunk_max: int = 0,
-                 chunk_per_rank: int = 0, w0_layout: str = "kn", gemm_rows: int = 0, _ids=None):
+                 chunk_per_rank: int = 0, w0_layout: str = "kn", gemm_rows: int = 0, _ids=None,
+                 _widths=None):
         rk = np.ascontiguousarray(np.asarray(ranks, dtype=np.int32))
-        n = int(rk.shape[0])
         opts = _lib.PlanOpts(nano_rows, gemm_rows, n_streams, chunk_min, chunk_max, chunk_per_rank,
                              _lib.W0_LAYOUTS[w0_layout])
         h = ctypes.c_void_p()
-        if _ids is None:
+        widths = [int(d_out)] if _widths is None else [int(v) for v in _widths]
+        if _widths is not None:
+            P = len(widths)
+            if rk.ndim != 2 or rk.shape[1] != P:
+                raise ValueError("ranks must be [n][n_proj] for a multi-projection plan")
+            n = int(rk.shape[0])
+            rk = np.ascontiguousarray(rk.reshape(-1))
+            off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
+            if off.shape != (n + 1,):
+                raise ValueError("seg_offsets must have n + 1 entries")
+            w = np.ascontiguousarray(np.asarray(widths, dtype=np.int64))
+            check(lib().mlora_plan_multi(n, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), P,
+                                         w.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                         rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in),
+                                         _lib.DTYPES[dtype], ctypes.byref(opts), ctypes.byref(h)))
+        elif _ids is None:
+            n = int(rk.shape[0])
             off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
             if off.shape != (n + 1,):
                 raise ValueError("seg_offsets must have len(ranks) + 1 entries")
@@ -42,6 +62,7 @@ class Plan:
                                    rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in),
                                    int(d_out), _lib.DTYPES[dtype], ctypes.byref(opts), ctypes.byref(h)))
         else:
+            n = int(rk.shape[0])
             ids = np.ascontiguousarray(np.asarray(_ids, dtype=np.int32).reshape(-1))
             check(lib().mlora_plan_from_ids(n, int(ids.shape[0]),
                                             ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
@@ -57,12 +78,22 @@ class Plan:
         self.w0_layout = w0_layout
         self.offsets = self.export("offsets") if _ids is not None else off
         self.ranks = rk
+        self.widths = widths
+        self.n_proj = len(widths)
+        # output width of each pair's B (the width of its projection)
+        self.pair_widths = np.asarray([widths[v % len(widths)] for v in range(rk.shape[0])], dtype=np.int64)
         self._ws_uploaded = None
 
     @classmethod
     def from_ids(cls, token_adapter, ranks, d_in: int, d_out: int, dtype: str = "bf16", **opts):
         """mlora_plan_from_ids: token t belongs to adapter token_adapter[t]."""
         return cls(None, ranks, d_in, d_out, dtype, _ids=token_adapter, **opts)
+
+    @classmethod
+    def multi(cls, seg_offsets, ranks, d_in: int, widths, dtype: str = "bf16", **opts):
+        """mlora_plan_multi: projections of output widths ``widths`` sharing
+        the input; ranks [n][n_proj]."""
+        return cls(seg_offsets, ranks, d_in, int(sum(widths)), dtype, _widths=widths, **opts)
 
     @property
     def handle(self):
@@ -167,6 +198,10 @@ def _dt(plan):
     return torch.bfloat16 if plan.dtype == "bf16" else torch.float32
 
 
+def _npairs(plan):
+    return plan.info["n"] * plan.info["n_proj"]
+
+
 def _w0_shape(plan):
     i = plan.info
     return (i["d_in"], i["d_out"]) if plan.w0_layout == "kn" else (i["d_out"], i["d_in"])
@@ -182,8 +217,8 @@ def mlora_forward(plan: Plan, X, W0, A_ptrs, B_ptrs, scales, Y, Z, ws, stream=No
     _check_t(Y, "Y", (i["T"], i["d_out"]), dt)
     _check_t(Z, "Z", None, dt, i["z_elems"])
     for nm, t in (("A_ptrs", A_ptrs), ("B_ptrs", B_ptrs)):
-        _check_t(t, nm, (i["n"],), torch.int64)
-    _check_t(scales, "scales", (i["n"],), torch.float32)
+        _check_t(t, nm, (_npairs(plan),), torch.int64)
+    _check_t(scales, "scales", (_npairs(plan),), torch.float32)
     check(lib().mlora_forward(plan.handle, _p(X), _p(W0), _p(A_ptrs), _p(B_ptrs), _p(scales),
                               _p(Y), _p(Z), _p(ws), ws.numel(), _stream(stream)))
     return Y, Z
@@ -202,8 +237,8 @@ def mlora_backward(plan: Plan, dY, X, W0, A_ptrs, B_ptrs, scales, Z, dX, dA_ptrs
     if dX is not None:
         _check_t(dX, "dX", (i["T"], i["d_in"]), dt)
     for nm, t in (("A_ptrs", A_ptrs), ("B_ptrs", B_ptrs), ("dA_ptrs", dA_ptrs), ("dB_ptrs", dB_ptrs)):
-        _check_t(t, nm, (i["n"],), torch.int64)
-    _check_t(scales, "scales", (i["n"],), torch.float32)
+        _check_t(t, nm, (_npairs(plan),), torch.int64)
+    _check_t(scales, "scales", (_npairs(plan),), torch.float32)
     check(lib().mlora_backward(plan.handle, _p(dY), _p(X), _p(W0), _p(A_ptrs), _p(B_ptrs),
                                _p(scales), _p(Z), _p(dX), _p(dA_ptrs), _p(dB_ptrs), _p(ws),
                                ws.numel(), _stream(stream)))
@@ -227,7 +262,7 @@ def mlora_adamw_step(plan: Plan, hparams, A_ptrs, B_ptrs, dA_ptrs, dB_ptrs, mA_p
     """One AdamW step of every adapter (fp32 masters and moments through the
     pointer tables; optional bf16 copies)."""
     torch = _torch()
-    n = plan.info["n"]
+    n = _npairs(plan)
     _check_t(hparams, "hparams", (n * ctypes.sizeof(_lib.AdamwHparams),), torch.uint8)
     for nm, t in (("A_ptrs", A_ptrs), ("B_ptrs", B_ptrs), ("dA_ptrs", dA_ptrs), ("dB_ptrs", dB_ptrs),
                   ("mA_ptrs", mA_ptrs), ("vA_ptrs", vA_ptrs), ("mB_ptrs", mB_ptrs), ("vB_ptrs", vB_ptrs)):
@@ -259,12 +294,12 @@ class PackedLoRALinear:
         self.W0 = W0
         self.A = list(A)
         self.B = list(B)
-        n = plan.info["n"]
-        self.scales = torch.as_tensor(np.asarray(scales, dtype=np.float32), device=device)
+        n = _npairs(plan)
+        self.scales = torch.as_tensor(np.asarray(scales, dtype=np.float32).reshape(-1), device=device)
         self.dA = [torch.empty((plan.info["d_in"], int(r)), dtype=torch.float32, device=device)
                    for r in plan.ranks]
-        self.dB = [torch.empty((int(r), plan.info["d_out"]), dtype=torch.float32, device=device)
-                   for r in plan.ranks]
+        self.dB = [torch.empty((int(r), int(w)), dtype=torch.float32, device=device)
+                   for r, w in zip(plan.ranks, plan.pair_widths)]
         assert len(self.A) == n and len(self.B) == n
         self.A_ptrs = pointer_table(self.A, device)
         self.B_ptrs = pointer_table(self.B, device)

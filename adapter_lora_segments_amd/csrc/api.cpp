@@ -24,7 +24,7 @@ mlora_status fail(mlora_status s, const std::string& msg) {
 }
 
 struct Range {
-  int32_t begin, count, rp;
+  int32_t begin, count, rp, proj;
 };
 
 }  // namespace
@@ -58,12 +58,14 @@ struct mlora_plan_s {
 
 namespace {
 
+// Runs of consecutive items (chunks) with the same padded rank and projection.
 std::vector<Range> bucket_ranges(const std::vector<int32_t>& items, int stride, int32_t begin,
-                                 int32_t end, const std::vector<int32_t>& rpad) {
+                                 int32_t end, const std::vector<int32_t>& rpad, int32_t nproj) {
   std::vector<Range> out;
   for (int32_t i = begin; i < end; ++i) {
-    const int32_t rp = rpad[items[(size_t)stride * i]];
-    if (out.empty() || out.back().rp != rp) out.push_back({i, 0, rp});
+    const int32_t v = items[(size_t)stride * i];
+    const int32_t rp = rpad[v], q = v % nproj;
+    if (out.empty() || out.back().rp != rp || out.back().proj != q) out.push_back({i, 0, rp, q});
     out.back().count++;
   }
   return out;
@@ -89,6 +91,10 @@ mlora::DevTables dev_tables(const mlora_plan_s* p, void* ws) {
   t.zero = reinterpret_cast<const uint16_t*>(b + L.zero);
   t.perm = p->P.perm.empty() ? nullptr : reinterpret_cast<const int32_t*>(b + L.perm);
   t.oblk = reinterpret_cast<const int32_t*>(b + L.oblk);
+  t.seg0 = reinterpret_cast<const int64_t*>(b + L.seg0);
+  t.pcol = reinterpret_cast<const int32_t*>(b + L.pcol);
+  t.cboff = reinterpret_cast<const int64_t*>(b + L.cboff);
+  t.nproj = p->P.nproj;
   return t;
 }
 
@@ -235,9 +241,10 @@ mlora_status finish_plan(mlora::PlanTables&& P, mlora_plan_t* out) {
   p->chunk_b.resize(S);
   p->group_max_rank.assign(S, 1);
   for (int g = 0; g < S; ++g) {
-    p->chunk_b[g] = bucket_ranges(p->P.chunks, 3, p->P.chunk_start[g], p->P.chunk_start[g + 1], p->P.rpad);
-    for (int32_t j = p->P.groups[g]; j < p->P.groups[g + 1]; ++j)
-      p->group_max_rank[g] = std::max(p->group_max_rank[g], p->P.ranks[j]);
+    p->chunk_b[g] = bucket_ranges(p->P.chunks, 3, p->P.chunk_start[g], p->P.chunk_start[g + 1], p->P.rpad,
+                                  p->P.nproj);
+    for (int32_t v = p->P.groups[g] * p->P.nproj; v < p->P.groups[g + 1] * p->P.nproj; ++v)
+      p->group_max_rank[g] = std::max(p->group_max_rank[g], p->P.ranks[v]);
     p->max_rank = std::max(p->max_rank, p->group_max_rank[g]);
   }
   *out = p;
@@ -270,6 +277,22 @@ mlora_status mlora_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adap
     std::string err;
     mlora_status st = mlora::build_plan_from_ids(n, T, token_adapter, ranks, d_in, d_out,
                                                  (int32_t)dtype, opts, P, err);
+    if (st != MLORA_OK) return fail(st, err);
+    return finish_plan(std::move(P), out);
+  } catch (const std::bad_alloc&) {
+    return fail(MLORA_ERR_NOMEM, "host allocation failed while building the plan");
+  }
+}
+
+mlora_status mlora_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t n_proj, const int64_t* widths,
+                              const int32_t* ranks, int64_t d_in, mlora_dtype dtype,
+                              const mlora_plan_opts* opts, mlora_plan_t* out) {
+  if (!out) return fail(MLORA_ERR_INVALID_ARG, "out is NULL");
+  try {
+    mlora::PlanTables P;
+    std::string err;
+    mlora_status st = mlora::build_plan_multi(n, seg_offsets, n_proj, widths, ranks, d_in, (int32_t)dtype,
+                                               opts, P, err);
     if (st != MLORA_OK) return fail(st, err);
     return finish_plan(std::move(P), out);
   } catch (const std::bad_alloc&) {
@@ -315,6 +338,7 @@ mlora_status mlora_plan_get_info(mlora_plan_t p, mlora_plan_info* info) {
   i.n_tiles = P.n_tiles();
   i.n_ext = P.n_ext();
   i.n_opt_blocks = P.n_oblk();
+  i.n_proj = P.nproj;
   *info = i;
   return MLORA_OK;
 }
@@ -346,6 +370,9 @@ mlora_status mlora_plan_export(mlora_plan_t p, int32_t table, void* dst, size_t*
     case MLORA_TAB_RANKS: v32(P.ranks); break;
     case MLORA_TAB_PERM: v32(P.perm); break;
     case MLORA_TAB_OPT_BLOCKS: v32(P.oblk); break;
+    case MLORA_TAB_PROJ_COLS: v32(P.pcol); break;
+    case MLORA_TAB_SEG_START: v64(P.seg0); break;
+    case MLORA_TAB_CHUNK_BOFF: v64(P.cboff); break;
     default: return fail(MLORA_ERR_INVALID_ARG, "unknown table id " + std::to_string(table));
   }
   if (!dst) {
@@ -411,12 +438,12 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
   uint16_t* acat_t = reinterpret_cast<uint16_t*>(wsb + L.acat_t);
   uint16_t* bcat_t = reinterpret_cast<uint16_t*>(wsb + L.bcat_t);
   st = timed(p, MLORA_K_PREP, cs, [&] {
-    mlora::launch_prep_a(t, P.n, P.d_in, P.rpad_total, A, acat_t, nullptr, cs);
+    mlora::launch_prep_a(t, P.nv(), P.d_in, P.rpad_total, A, acat_t, nullptr, cs);
   });
   if (st != MLORA_OK) return st;
   if (nk) {
     st = timed(p, MLORA_K_PREP, cs, [&] {
-      mlora::launch_prep_b(t, P.n, P.d_out, P.rpad_total, B, bcat_t, cs);
+      mlora::launch_prep_b(t, P.nv(), P.d_out, P.rpad_total, B, bcat_t, cs);
     });
     if (st != MLORA_OK) return st;
   }
@@ -482,11 +509,11 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     });
     if (st != MLORA_OK) return st;
     st = timed(p, MLORA_K_TOKEN_REDUCE, cs, [&] {
-      mlora::launch_f32_db(t, P.n, P.d_out, (const float*)Z, (const float*)dY, dB, p->max_rank, cs);
+      mlora::launch_f32_db(t, P.nv(), P.d_out, (const float*)Z, (const float*)dY, dB, p->max_rank, cs);
     });
     if (st != MLORA_OK) return st;
     st = timed(p, MLORA_K_TOKEN_REDUCE, cs, [&] {
-      mlora::launch_f32_da(t, P.n, P.d_in, (const float*)X, dZ, dA, p->max_rank, cs);
+      mlora::launch_f32_da(t, P.nv(), P.d_in, (const float*)X, dZ, dA, p->max_rank, cs);
     });
     if (st != MLORA_OK) return st;
     if (!dX) return MLORA_OK;
@@ -508,7 +535,7 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
   // the workspace held before.
   if (dX) {
     st = timed(p, MLORA_K_PREP, cs, [&] {
-      mlora::launch_prep_a(t, P.n, P.d_in, P.rpad_total, A, nk ? acat_t : nullptr,
+      mlora::launch_prep_a(t, P.nv(), P.d_in, P.rpad_total, A, nk ? acat_t : nullptr,
                            nk ? nullptr : acat, cs);
     });
     if (st != MLORA_OK) return st;
@@ -530,15 +557,16 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     auto weight_grads = [&](hipStream_t sw) -> mlora_status {
       for (const Range& r : p->chunk_b[g]) {
         mlora_status s2 = timed(p, MLORA_K_TOKEN_REDUCE, sw, [&] {
-          mlora::launch_token_reduce(r.rp, t, r.begin, r.count, (const uint16_t*)dY,
-                                     (const uint16_t*)Z, partB, P.d_out, (const uint16_t*)X, dZ,
-                                     partA, P.d_in, sw);
+          const int64_t c0 = P.pcol[r.proj], w = P.pcol[r.proj + 1] - c0;
+          mlora::launch_token_reduce(r.rp, t, r.begin, r.count, (const uint16_t*)dY + c0, P.d_out,
+                                     (const uint16_t*)Z, partB, w, (const uint16_t*)X, dZ, partA,
+                                     P.d_in, sw);
         });
         if (s2 != MLORA_OK) return s2;
       }
       return timed(p, MLORA_K_REDUCE, sw, [&] {
-        mlora::launch_reduce_partials(t, P.groups[g], P.groups[g + 1], P.d_in, P.d_out, partA,
-                                      partB, dA, dB, p->group_max_rank[g], sw);
+        mlora::launch_reduce_partials(t, P.groups[g] * P.nproj, P.groups[g + 1] * P.nproj, P.d_in,
+                                      P.d_out, partA, partB, dA, dB, p->group_max_rank[g], sw);
       });
     };
     if (!dX) {

@@ -27,6 +27,13 @@ struct DevTables {
   const uint16_t* zero;     // 256 zero bytes
   const int32_t* perm;      // [T] grouped row -> caller row, or NULL (rows already grouped)
   const int32_t* oblk;      // [n_oblk][2] optimizer work items (tensor, piece)
+  // Several projections sharing the input: "adapter" j in the tables above
+  // is the pair (j / nproj, j % nproj); projection q owns output columns
+  // [pcol[q], pcol[q+1]).
+  const int64_t* seg0;      // [nv] first row of pair j's adapter
+  const int32_t* pcol;      // [nproj+1]
+  const int64_t* cboff;     // [n_chunks] element offset of a chunk's dB partial
+  int32_t nproj;
 };
 
 // ---------------- bf16 path (MFMA) ----------------
@@ -42,20 +49,24 @@ void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
 // Skinny products over nano-batches [nano_begin, nano_begin + nano_count) of
 // any padded ranks: out rows of adapter j (r_pad(j) columns)
 //   mode 0 (shrink): Z'[t][c] = s_j sum_k X[t][k] A_cat^T[roff_j + c][k]
-//   mode 1 (dZ)    : dZ[t][c] = s_j sum_k dY[t][k] B_j[c][k]
+//   mode 1 (dZ)    : dZ[t][c] = s_j sum_k dY[t][c_j + k] B_j[c][k] over the
+//                    width of j's projection (first column c_j); K is then
+//                    the row length of dY
 void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nano_count,
                    const uint16_t* P, int64_t K, const uint16_t* acat_t, const void* const* Bptr,
                    const float* scales, uint16_t* out, hipStream_t s);
 
 // Token reductions over the chunks [chunk_begin, chunk_begin + chunk_count)
-// of one padded-rank bucket (r_pad = rp), both in one launch; partial sums in
-// fp32:
-//   dB: partB[cpref][c][n] = sum_t Z'[t][c] dY[t][n]       (n < d_out)
-//   dA: partA[cpref][d][c] = sum_t X[t][d] dZ[t][c]        (d < d_in)
+// of one padded-rank bucket (r_pad = rp) and one projection, both in one
+// launch; partial sums in fp32:
+//   dB: partB[cboff + c*d_out + n] = sum_t Z'[t][c] dY[t][n]   (n < d_out)
+//   dA: partA[cpref][d][c] = sum_t X[t][d] dZ[t][c]            (d < d_in)
+// dY points at the projection's first column, rows ld_dy apart; d_out is the
+// projection's width.
 void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
-                         const uint16_t* dY, const uint16_t* Z, float* partB, int64_t d_out,
-                         const uint16_t* X, const uint16_t* dZ, float* partA, int64_t d_in,
-                         hipStream_t s);
+                         const uint16_t* dY, int64_t ld_dy, const uint16_t* Z, float* partB,
+                         int64_t d_out, const uint16_t* X, const uint16_t* dZ, float* partA,
+                         int64_t d_in, hipStream_t s);
 
 // Fixed-order sum of the chunk partials into the caller's dA_j / dB_j
 // (adapters [a_begin, a_end)); adapters without rows get zeros.

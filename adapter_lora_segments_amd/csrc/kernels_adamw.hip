@@ -42,7 +42,9 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwArgs a) {
   const float lr = ldc(&hp->lr), beta1 = ldc(&hp->beta1), beta2 = ldc(&hp->beta2);
   const float eps = ldc(&hp->eps), wd = ldc(&hp->weight_decay);
 
-  const int64_t numel = (int64_t)ldc(a.t.ranks + i) * (isB ? a.d_out : a.d_in);
+  const int pq = i % a.t.nproj;   // B_i spans its projection's width
+  const int64_t width = (int64_t)ldc(a.t.pcol + pq + 1) - ldc(a.t.pcol + pq);
+  const int64_t numel = (int64_t)ldc(a.t.ranks + i) * (isB ? width : a.d_in);
   const int64_t base = (int64_t)piece * kOptBlockElems + 4 * threadIdx.x;
   float* p = ldc((isB ? a.B : a.A) + i);
   const float* g = ldc((isB ? a.dB : a.dA) + i);

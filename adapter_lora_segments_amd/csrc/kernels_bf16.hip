@@ -104,11 +104,15 @@ __global__ __launch_bounds__(256) void k_prep_b(DevTables t, int32_t n, int64_t 
   const uint16_t* tile = reinterpret_cast<const uint16_t*>(tile4);
   const int64_t n0 = (int64_t)blockIdx.x * 64;
   for (int32_t j = blockIdx.y; j < n; j += gridDim.y) {
+    // pair j's projection owns output columns [c0, c0 + w): other slabs skip it
+    const int pq = j % t.nproj;
+    const int64_t c0 = ldc(t.pcol + pq), w = ldc(t.pcol + pq + 1) - c0;
+    if (n0 < c0 || n0 >= c0 + w) continue;
     const int r = ldc(t.ranks + j), rp = ldc(t.rpad + j), ro = ldc(t.roff + j);
     const uint16_t* Bj = static_cast<const uint16_t*>(ldc(B + j));
     for (int i = threadIdx.x; i < 8 * r; i += 256) {
       const int c = i >> 3, q = i & 7;
-      tile4[i] = *reinterpret_cast<const u32x4*>(Bj + (int64_t)c * d_out + n0 + 8 * q);
+      tile4[i] = *reinterpret_cast<const u32x4*>(Bj + (int64_t)c * w + (n0 - c0) + 8 * q);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < 64 * rp; i += 256) {
@@ -167,12 +171,12 @@ struct SkinnyCfg {
 
 template <int RP, int MODE, bool PERM>
 __device__ __forceinline__ void skinny_body(const DevTables& t, int j, int row0, int nrows,
-                                            const uint16_t* P, int64_t K, const uint16_t* acat_t,
-                                            const void* const* Bptr, float s, uint16_t* out,
-                                            u32x4* ring) {
+                                            const uint16_t* P, int64_t K, int64_t ldp,
+                                            const uint16_t* acat_t, const void* const* Bptr, float s,
+                                            uint16_t* out, u32x4* ring) {
   using C = SkinnyCfg<RP>;
   constexpr int F = RP / 32, NS = C::NS, LPS = C::LPS;
-  const int64_t oj = ldc(t.offsets + j);
+  const int64_t oj = ldc(t.seg0 + j);
   const int64_t zo = ldc(t.zoff + j);
   const int rj = ldc(t.ranks + j);
   const uint16_t* Q = MODE == 0 ? acat_t + (int64_t)ldc(t.roff + j) * K
@@ -201,7 +205,7 @@ __device__ __forceinline__ void skinny_body(const DevTables& t, int j, int row0,
       const int gc = (lane & 15) ^ (row & 15);
       if (row < 32) {
         const int pr = row0 + 32 * rf + min(row, frag_rows - 1);
-        src[q] = P + (int64_t)(PERM ? ldg_i32(t.perm + pr) : pr) * K + 8 * gc;
+        src[q] = P + (int64_t)(PERM ? ldg_i32(t.perm + pr) : pr) * ldp + 8 * gc;
         adv[q] = true;
       } else {
         const int c = row - 32;
@@ -299,11 +303,21 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
   const int nb = nano_begin + blockIdx.x;
   const int j = ldc(t.nano + 3 * nb), row0 = ldc(t.nano + 3 * nb + 1), nrows = ldc(t.nano + 3 * nb + 2);
   const float s = ldc(scales + j);
+  // dZ of pair j reads its projection's columns of dY: K = the projection's
+  // width, rows K0 = the full row length apart
+  int64_t Kj = K;
+  const uint16_t* Pj = P;
+  if (MODE == 1) {
+    const int pq = j % t.nproj;
+    const int64_t c0 = ldc(t.pcol + pq);
+    Kj = ldc(t.pcol + pq + 1) - c0;
+    Pj = P + c0;
+  }
   switch (ldc(t.rpad + j)) {
-    case 32: skinny_body<32, MODE, PERM>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
-    case 64: skinny_body<64, MODE, PERM>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
-    case 128: skinny_body<128, MODE, PERM>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
-    default: skinny_body<256, MODE, PERM>(t, j, row0, nrows, P, K, acat_t, Bptr, s, out, ring); break;
+    case 32: skinny_body<32, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
+    case 64: skinny_body<64, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
+    case 128: skinny_body<128, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
+    default: skinny_body<256, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
   }
 }
 
@@ -339,10 +353,11 @@ void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nan
 struct TokenReduceArgs {
   DevTables t;
   int32_t chunk_begin, n_chunks;
-  const uint16_t* dY;
+  const uint16_t* dY;       // first column of the chunks' projection
+  int64_t ld_dy;            // row stride of dY (all projections' columns)
   const uint16_t* Z;
   float* partB;
-  int64_t d_out;
+  int64_t d_out;            // the projection's width
   const uint16_t* X;
   const uint16_t* dZ;
   float* partA;
@@ -356,12 +371,13 @@ __device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int 
   constexpr int NBLK = 128 + RP;                 // 8x8 blocks per 64-token step
   constexpr int PER = (NBLK + 255) / 256;        // blocks per thread
   const uint16_t* big = MODE == 0 ? a.dY : a.X;
-  const int64_t big_ld = MODE == 0 ? a.d_out : a.d_in;
+  const int64_t big_ld = MODE == 0 ? a.ld_dy : a.d_in;   // row stride
+  const int64_t big_n = MODE == 0 ? a.d_out : a.d_in;    // columns, partial row length
   const uint16_t* rk = MODE == 0 ? a.Z : a.dZ;
   float* part = MODE == 0 ? a.partB : a.partA;
   const int j = ldc(a.t.chunks + 3 * ch), r0 = ldc(a.t.chunks + 3 * ch + 1), nr = ldc(a.t.chunks + 3 * ch + 2);
   const int64_t cp = ldc(a.t.cpref + ch);
-  const uint16_t* rbase = rk + ldc(a.t.zoff + j) + (int64_t)(r0 - ldc(a.t.offsets + j)) * RP;
+  const uint16_t* rbase = rk + ldc(a.t.zoff + j) + (int64_t)(r0 - ldc(a.t.seg0 + j)) * RP;
   const uint16_t* bbase = big + (int64_t)r0 * big_ld;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -383,7 +399,7 @@ __device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int 
         const int bb = isbig ? b : b - 128;
         const int MB = isbig ? 16 : RP / 8;
         const int mb = bb % MB, kb = bb / MB;
-        const int64_t col = isbig ? min((int64_t)(col0 + 8 * mb), big_ld - 8) : 8 * mb;
+        const int64_t col = isbig ? min((int64_t)(col0 + 8 * mb), big_n - 8) : 8 * mb;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int tc = min(t0 + 8 * kb + i, nr - 1);
@@ -406,7 +422,7 @@ __device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int 
         const int bb = isbig ? b : b - 128;
         const int MB = isbig ? 16 : RP / 8;
         const int mb = bb % MB, kb = bb / MB;
-        const bool colok = !isbig || (col0 + 8 * mb < big_ld);
+        const bool colok = !isbig || (col0 + 8 * mb < big_n);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           stage[p][i] = (t0 + 8 * kb + i < nr && colok) ? stage[p][i] : zero4();
@@ -495,14 +511,14 @@ __device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int 
         // lane holds c = 32f + l32, n = col0 + 32w + 8g + 4half + e
         const int c = 32 * f + l32;
         const int n = col0 + 32 * w + 8 * g + 4 * half;
-        if (n < big_ld)
-          *reinterpret_cast<f32x4*>(part + cp * big_ld + (int64_t)c * big_ld + n) = v;
+        if (n < big_n)
+          *reinterpret_cast<f32x4*>(part + ldc(a.t.cboff + ch) + (int64_t)c * big_n + n) = v;
       } else {
         // lane holds d = col0 + 32w + l32, c = 32f + 8g + 4half + e
         const int d = col0 + 32 * w + l32;
         const int c = 32 * f + 8 * g + 4 * half;
-        if (d < big_ld)
-          *reinterpret_cast<f32x4*>(part + cp * big_ld + (int64_t)d * RP + c) = v;
+        if (d < big_n)
+          *reinterpret_cast<f32x4*>(part + cp * big_n + (int64_t)d * RP + c) = v;
       }
     }
   }
@@ -522,11 +538,11 @@ __global__ __launch_bounds__(256) void k_token_reduce(TokenReduceArgs a) {
 }
 
 void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
-                         const uint16_t* dY, const uint16_t* Z, float* partB, int64_t d_out,
-                         const uint16_t* X, const uint16_t* dZ, float* partA, int64_t d_in,
-                         hipStream_t s) {
+                         const uint16_t* dY, int64_t ld_dy, const uint16_t* Z, float* partB,
+                         int64_t d_out, const uint16_t* X, const uint16_t* dZ, float* partA,
+                         int64_t d_in, hipStream_t s) {
   if (chunk_count <= 0) return;
-  TokenReduceArgs a{t, chunk_begin, chunk_count, dY, Z, partB, d_out, X, dZ, partA, d_in};
+  TokenReduceArgs a{t, chunk_begin, chunk_count, dY, ld_dy, Z, partB, d_out, X, dZ, partA, d_in};
   const int nbb_b = (int)((d_out + 127) / 128), nbb_a = (int)((d_in + 127) / 128);
   dim3 grid((unsigned)(chunk_count * (nbb_b + nbb_a))), block(256);
 #define MLORA_TR(R)                                                                 \
@@ -554,7 +570,9 @@ __global__ __launch_bounds__(256) void k_reduce_partials(DevTables t, int32_t a_
   for (int32_t j = a_begin + blockIdx.y; j < a_end; j += gridDim.y) {
     const int r = ldc(t.ranks + j), rp = ldc(t.rpad + j);
     const int first = ldc(t.ch_first + j), cnt = ldc(t.ch_count + j);
-    const int64_t na4 = d_in * (rp / 4), nb4 = (int64_t)r * (d_out / 4);
+    const int pq = j % t.nproj;
+    const int64_t w = ldc(t.pcol + pq + 1) - ldc(t.pcol + pq);   // dB_j is [r][w]
+    const int64_t na4 = d_in * (rp / 4), nb4 = (int64_t)r * (w / 4);
     float* gA = static_cast<float*>(ldc(dA + j));
     float* gB = static_cast<float*>(ldc(dB + j));
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < na4 + nb4;
@@ -572,7 +590,7 @@ __global__ __launch_bounds__(256) void k_reduce_partials(DevTables t, int32_t a_
       } else {
         const int64_t q = 4 * (i - na4);
         for (int k = 0; k < cnt; ++k)
-          sum += *reinterpret_cast<const f32x4*>(partB + (int64_t)ldc(t.cpref + first + k) * d_out + q);
+          sum += *reinterpret_cast<const f32x4*>(partB + ldc(t.cboff + first + k) + q);
         *reinterpret_cast<f32x4*>(gB + q) = sum;
       }
     }
@@ -687,8 +705,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
 
   const int tix = g.tile_begin + tm;
   const int row0 = ldc(g.t.tiles + 2 * tix), mrows = ldc(g.t.tiles + 2 * tix + 1);
-  const int e0 = ldc(g.t.ext_start + tix), e1 = ldc(g.t.ext_start + tix + 1);
   const int n0 = tn * 256;
+  // Extension steps: the forward's column tile lies in one projection and
+  // takes that projection's list; the dX GEMM sums every projection.
+  const int NP = g.t.nproj;
+  int pq = 0;
+  while (FWD && pq + 1 < NP && ldc(g.t.pcol + pq + 1) <= n0) ++pq;
+  const int e0 = ldc(g.t.ext_start + tix * NP + (FWD ? pq : 0));
+  const int e1 = ldc(g.t.ext_start + tix * NP + (FWD ? pq + 1 : NP));
+  const int pc0 = ldc(g.t.pcol + pq), pw = ldc(g.t.pcol + pq + 1) - pc0;  // forward: B_j is [r_j][pw]
   const int nk = g.K / 32;
   const int nsteps = nk + (e1 - e0);
 
@@ -735,7 +760,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
       const int j = ldc(g.t.ext + 4 * e), lo = ldc(g.t.ext + 4 * e + 1), hi = ldc(g.t.ext + 4 * e + 2);
       const int k0 = ldc(g.t.ext + 4 * e + 3);
       const int rp = ldc(g.t.rpad + j);
-      const int64_t oj = ldc(g.t.offsets + j);
+      const int64_t oj = ldc(g.t.seg0 + j);
       const uint16_t* zb = g.ebuf + ldc(g.t.zoff + j);
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
@@ -755,7 +780,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
           const int col = min(n0 + 8 * nc_chunk[i], g.N - 8);
           if (FWD) {
             const int rj = ldc(g.t.ranks + j);
-            src[BPW + i] = k < rj ? static_cast<const uint16_t*>(ldc(g.eb + j)) + (int64_t)k * g.N + col
+            src[BPW + i] = k < rj ? static_cast<const uint16_t*>(ldc(g.eb + j)) + (int64_t)k * pw + (col - pc0)
                                   : g.t.zero;
           } else {
             src[BPW + i] = g.ext_n + (int64_t)(ldc(g.t.roff + j) + k) * g.N + col;

@@ -5,6 +5,8 @@
 // Concurrent LoRA Training for Large Language Models, §2.1 and §9.2); each
 // row finds its adapter by binary search over the segment offsets, and each
 // weight gradient is one thread's sum over its adapter's rows in row order.
+// With several projections sharing the input, pair v = i * nproj + q of
+// adapter i and projection q owns output columns [pcol[q], pcol[q+1]).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -28,11 +30,13 @@ __device__ __forceinline__ int adapter_of(const int64_t* off, int n, int64_t row
 }
 
 // Z'[row][c] = s_j sum_k X[row][k] A_j[k][c]; zero for r_j <= c < r_pad(j).
+// blockIdx.y is the projection.
 __global__ __launch_bounds__(256) void k_f32_shrink(DevTables t, int32_t n, int64_t d_in,
                                                     const float* X, const void* const* A,
                                                     const float* scales, float* Z) {
   const int64_t row = blockIdx.x;
-  const int j = adapter_of(t.offsets, n, row);
+  const int i = adapter_of(t.offsets, n, row);
+  const int j = i * t.nproj + blockIdx.y;
   const int c = threadIdx.x;
   const int r = t.ranks[j], rp = t.rpad[j];
   if (c >= rp) return;
@@ -43,26 +47,29 @@ __global__ __launch_bounds__(256) void k_f32_shrink(DevTables t, int32_t n, int6
     for (int64_t k = 0; k < d_in; ++k) acc = fmaf(x[k], Aj[k * r + c], acc);
     acc *= scales[j];
   }
-  Z[t.zoff[j] + (row - t.offsets[j]) * rp + c] = acc;
+  Z[t.zoff[j] + (row - t.offsets[i]) * rp + c] = acc;
 }
 
-// dZ[row][c] = s_j sum_o dY[row][o] B_j[c][o]
+// dZ[row][c] = s_j sum_o dY[row][c_q + o] B_j[c][o] over projection q's
+// width (blockIdx.y = q; rows of dY are d_out long).
 __global__ __launch_bounds__(256) void k_f32_dz(DevTables t, int32_t n, int64_t d_out,
                                                 const float* dY, const void* const* B,
                                                 const float* scales, float* dZ) {
   const int64_t row = blockIdx.x;
-  const int j = adapter_of(t.offsets, n, row);
+  const int i = adapter_of(t.offsets, n, row);
+  const int q = blockIdx.y, j = i * t.nproj + q;
+  const int64_t c0 = t.pcol[q], w = t.pcol[q + 1] - c0;
   const int c = threadIdx.x;
   const int r = t.ranks[j], rp = t.rpad[j];
   if (c >= rp) return;
   float acc = 0.f;
   if (c < r) {
-    const float* Bj = static_cast<const float*>(B[j]) + (int64_t)c * d_out;
-    const float* g = dY + caller_row(t, row) * d_out;
-    for (int64_t o = 0; o < d_out; ++o) acc = fmaf(g[o], Bj[o], acc);
+    const float* Bj = static_cast<const float*>(B[j]) + (int64_t)c * w;
+    const float* g = dY + caller_row(t, row) * d_out + c0;
+    for (int64_t o = 0; o < w; ++o) acc = fmaf(g[o], Bj[o], acc);
     acc *= scales[j];
   }
-  dZ[t.zoff[j] + (row - t.offsets[j]) * rp + c] = acc;
+  dZ[t.zoff[j] + (row - t.offsets[i]) * rp + c] = acc;
 }
 
 // C = Aop Bop + per-row LoRA term.  64x64 tile, 16x16 threads, 4x4 outputs
@@ -108,42 +115,56 @@ __global__ __launch_bounds__(256) void k_f32_gemm(DevTables t, int32_t n, int64_
     }
     __syncthreads();
   }
+  // Forward: the 64-column tile lies in one projection, whose pair adds its
+  // expand; dX: every projection's pair adds dZ A^T.
+  const int NP = t.nproj;
+  int pq = 0;
+  while (FWD && pq + 1 < NP && t.pcol[pq + 1] <= n0) ++pq;
+  const int64_t pc0 = t.pcol[pq], pw = t.pcol[pq + 1] - pc0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t row = m0 + ty + 16 * i;
     if (row >= T) continue;
-    const int j = adapter_of(t.offsets, n, row);
-    const int r = t.ranks[j], rp = t.rpad[j];
-    const float* e = E + t.zoff[j] + (row - t.offsets[j]) * rp;
-    const float* w = static_cast<const float*>(eb[j]);
+    const int ad = adapter_of(t.offsets, n, row);
+    for (int qq = FWD ? pq : 0; qq < (FWD ? pq + 1 : NP); ++qq) {
+      const int j = ad * NP + qq;
+      const int r = t.ranks[j], rp = t.rpad[j];
+      const float* e = E + t.zoff[j] + (row - t.offsets[ad]) * rp;
+      const float* w = static_cast<const float*>(eb[j]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = n0 + tx + 16 * q;
-      float v = acc[i][q];
-      for (int c = 0; c < r; ++c) {
-        const float ebv = FWD ? w[(int64_t)c * N + col] : w[(int64_t)col * r + c];
-        v = fmaf(e[c], ebv, v);
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + tx + 16 * q;
+        float v = acc[i][q];
+        for (int c = 0; c < r; ++c) {
+          const float ebv = FWD ? w[(int64_t)c * pw + (col - pc0)] : w[(int64_t)col * r + c];
+          v = fmaf(e[c], ebv, v);
+        }
+        acc[i][q] = v;
       }
-      C[caller_row(t, row) * ldc + col] = v;
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) C[caller_row(t, row) * ldc + n0 + tx + 16 * q] = acc[i][q];
   }
 }
 
-// dB_j[c][o] = sum_{rows of j} Z'[t][c] dY[t][o]
+// dB_j[c][o] = sum_{rows of j} Z'[t][c] dY[t][c_q + o] over pairs j (n of
+// them), o below the width of j's projection q; rows of dY are d_out long.
 __global__ __launch_bounds__(256) void k_f32_db(DevTables t, int32_t n, int64_t d_out,
                                                 const float* Z, const float* dY,
                                                 void* const* dB) {
   for (int32_t j = blockIdx.y; j < n; j += gridDim.y) {
     const int r = t.ranks[j], rp = t.rpad[j];
+    const int q = j % t.nproj, ad = j / t.nproj;
+    const int64_t c0 = t.pcol[q], w = t.pcol[q + 1] - c0;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)r * d_out) continue;
-    const int c = (int)(idx / d_out);
-    const int64_t o = idx - (int64_t)c * d_out;
-    const int64_t a = t.offsets[j], b = t.offsets[j + 1];
+    if (idx >= (int64_t)r * w) continue;
+    const int c = (int)(idx / w);
+    const int64_t o = idx - (int64_t)c * w;
+    const int64_t a = t.offsets[ad], b = t.offsets[ad + 1];
     const float* z = Z + t.zoff[j] + c;
     float acc = 0.f;
     for (int64_t row = a; row < b; ++row)
-      acc = fmaf(z[(row - a) * rp], dY[caller_row(t, row) * d_out + o], acc);
+      acc = fmaf(z[(row - a) * rp], dY[caller_row(t, row) * d_out + c0 + o], acc);
     static_cast<float*>(dB[j])[idx] = acc;
   }
 }
@@ -158,7 +179,8 @@ __global__ __launch_bounds__(256) void k_f32_da(DevTables t, int32_t n, int64_t 
     if (idx >= d_in * r) continue;
     const int64_t d = idx / r;
     const int c = (int)(idx - d * r);
-    const int64_t a = t.offsets[j], b = t.offsets[j + 1];
+    const int ad = j / t.nproj;
+    const int64_t a = t.offsets[ad], b = t.offsets[ad + 1];
     const float* g = dZ + t.zoff[j] + c;
     float acc = 0.f;
     for (int64_t row = a; row < b; ++row)
@@ -170,13 +192,15 @@ __global__ __launch_bounds__(256) void k_f32_da(DevTables t, int32_t n, int64_t 
 void launch_f32_shrink(const DevTables& t, int32_t n, int64_t T, int64_t d_in, const float* X,
                        const void* const* A, const float* scales, float* Z, hipStream_t s) {
   if (T <= 0) return;
-  hipLaunchKernelGGL(k_f32_shrink, dim3((unsigned)T), dim3(256), 0, s, t, n, d_in, X, A, scales, Z);
+  hipLaunchKernelGGL(k_f32_shrink, dim3((unsigned)T, (unsigned)t.nproj), dim3(256), 0, s, t, n, d_in, X, A,
+                     scales, Z);
 }
 
 void launch_f32_dz(const DevTables& t, int32_t n, int64_t T, int64_t d_out, const float* dY,
                    const void* const* B, const float* scales, float* dZ, hipStream_t s) {
   if (T <= 0) return;
-  hipLaunchKernelGGL(k_f32_dz, dim3((unsigned)T), dim3(256), 0, s, t, n, d_out, dY, B, scales, dZ);
+  hipLaunchKernelGGL(k_f32_dz, dim3((unsigned)T, (unsigned)t.nproj), dim3(256), 0, s, t, n, d_out, dY, B,
+                     scales, dZ);
 }
 
 void launch_f32_gemm(bool fwd, bool kc, const DevTables& t, int32_t n, int64_t T, const float* A,

@@ -22,22 +22,35 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
-mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ranks, int64_t d_in,
-                        int64_t d_out, int32_t dtype, const mlora_plan_opts* opts, PlanTables& P,
-                        std::string& err) {
-  if (!seg_offsets || !ranks) {
-    err = "seg_offsets and ranks must be non-NULL";
+mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, const int64_t* widths,
+                              const int32_t* ranks, int64_t d_in, int32_t dtype, const mlora_plan_opts* opts,
+                              PlanTables& P_out, std::string& err) {
+  if (!seg_offsets || !ranks || !widths) {
+    err = "seg_offsets, ranks and the projection widths must be non-NULL";
     return MLORA_ERR_INVALID_ARG;
   }
-  if (n < 1 || n > MLORA_MAX_ADAPTERS) {
-    err = "n must be in [1, " + std::to_string(MLORA_MAX_ADAPTERS) + "], got " + std::to_string(n);
+  if (P < 1 || P > MLORA_MAX_PROJECTIONS) {
+    err = "n_proj must be in [1, " + std::to_string(MLORA_MAX_PROJECTIONS) + "], got " + std::to_string(P);
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (n < 1 || (int64_t)n * P > MLORA_MAX_ADAPTERS) {
+    err = "n must be >= 1 and n * n_proj at most " + std::to_string(MLORA_MAX_ADAPTERS) + ", got n = " +
+          std::to_string(n);
     return MLORA_ERR_INVALID_ARG;
   }
   if (dtype != MLORA_FP32 && dtype != MLORA_BF16) {
     err = "unknown dtype " + std::to_string(dtype);
     return MLORA_ERR_INVALID_ARG;
   }
-  if (d_in <= 0 || d_out <= 0) {
+  int64_t d_out = 0;
+  for (int32_t q = 0; q < P; ++q) {
+    if (widths[q] <= 0) {
+      err = "d_in and every output width must be positive";
+      return MLORA_ERR_INVALID_ARG;
+    }
+    d_out += widths[q];
+  }
+  if (d_in <= 0) {
     err = "d_in and d_out must be positive";
     return MLORA_ERR_INVALID_ARG;
   }
@@ -46,6 +59,17 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
           ", " + std::to_string(d_out) + ")";
     return MLORA_ERR_UNSUPPORTED;
   }
+  // Projections split the output columns; a GEMM column tile (256 wide in
+  // bf16, 64 in fp32) must lie inside one projection.
+  const int64_t col_tile = dtype == MLORA_BF16 ? 256 : 64;
+  if (P > 1)
+    for (int32_t q = 0; q < P; ++q)
+      if (widths[q] % col_tile != 0) {
+        err = "with several projections every output width must be a multiple of " +
+              std::to_string(col_tile) + " (width " + std::to_string(q) + " is " +
+              std::to_string(widths[q]) + ")";
+        return MLORA_ERR_UNSUPPORTED;
+      }
   if (seg_offsets[0] != 0) {
     err = "seg_offsets[0] must be 0";
     return MLORA_ERR_INVALID_ARG;
@@ -61,13 +85,16 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
     err = "total rows must be below 2^31 - 1";
     return MLORA_ERR_UNSUPPORTED;
   }
-  for (int32_t i = 0; i < n; ++i) {
-    if (ranks[i] < 1) {
-      err = "rank of adapter " + std::to_string(i) + " must be >= 1";
+  const int32_t nv = n * P;
+  for (int32_t v = 0; v < nv; ++v) {
+    const std::string who = P == 1 ? "adapter " + std::to_string(v)
+                                   : "adapter " + std::to_string(v / P) + ", projection " + std::to_string(v % P);
+    if (ranks[v] < 1) {
+      err = "rank of " + who + " must be >= 1";
       return MLORA_ERR_INVALID_ARG;
     }
-    if (ranks[i] > MLORA_MAX_RANK) {
-      err = "rank of adapter " + std::to_string(i) + " exceeds " + std::to_string(MLORA_MAX_RANK);
+    if (ranks[v] > MLORA_MAX_RANK) {
+      err = "rank of " + who + " exceeds " + std::to_string(MLORA_MAX_RANK);
       return MLORA_ERR_UNSUPPORTED;
     }
   }
@@ -113,25 +140,33 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
 
   PlanTables p;
   p.n = n;
+  p.nproj = P;
   p.T = T;
   p.d_in = d_in;
   p.d_out = d_out;
   p.dtype = dtype;
   p.opts = o;
   p.offsets.assign(seg_offsets, seg_offsets + n + 1);
-  p.ranks.assign(ranks, ranks + n);
+  p.ranks.assign(ranks, ranks + nv);
+  p.pcol.assign(P + 1, 0);
+  for (int32_t q = 0; q < P; ++q) p.pcol[q + 1] = p.pcol[q] + (int32_t)widths[q];
+  auto width_of = [&](int32_t v) { return (int64_t)p.pcol[v % P + 1] - p.pcol[v % P]; };
 
-  // 1-2: padded ranks, Z' offsets, rank offsets
-  p.rpad.resize(n);
-  p.zoff.resize(n);
-  p.roff.resize(n);
+  // 1-2: padded ranks, Z' offsets, rank offsets, first row of each
+  // (adapter, projection) pair v = i*P + p
+  p.rpad.resize(nv);
+  p.zoff.resize(nv);
+  p.roff.resize(nv);
+  p.seg0.resize(nv);
   int64_t z = 0, rr = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    p.rpad[i] = pad_rank(ranks[i]);
-    p.zoff[i] = z;
-    p.roff[i] = (int32_t)rr;
-    z += (seg_offsets[i + 1] - seg_offsets[i]) * p.rpad[i];
-    rr += p.rpad[i];
+  for (int32_t v = 0; v < nv; ++v) {
+    const int32_t i = v / P;
+    p.rpad[v] = pad_rank(ranks[v]);
+    p.zoff[v] = z;
+    p.roff[v] = (int32_t)rr;
+    p.seg0[v] = seg_offsets[i];
+    z += (seg_offsets[i + 1] - seg_offsets[i]) * p.rpad[v];
+    rr += p.rpad[v];
   }
   p.z_elems = z;
   p.rpad_total = rr;
@@ -153,43 +188,52 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
     p.groups[s] = std::max(p.groups[s - 1], a);
   }
 
-  // 4-6: bucket-ordered walk producing nano-batches and reduction chunks
-  p.ch_first.assign(n, 0);
-  p.ch_count.assign(n, 0);
-  int64_t cp = 0;
+  // 4-6: bucket-ordered walk (padded rank descending, then projection, then
+  // adapter) producing nano-batches and reduction chunks
+  p.ch_first.assign(nv, 0);
+  p.ch_count.assign(nv, 0);
+  int64_t cp = 0, cb = 0;
   std::vector<int32_t> order;
   for (int32_t s = 0; s < S; ++s) {
     p.nano_start.push_back((int32_t)p.n_nano());
     p.chunk_start.push_back((int32_t)p.n_chunks());
     order.clear();
-    for (int32_t i = p.groups[s]; i < p.groups[s + 1]; ++i) order.push_back(i);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int32_t a, int32_t b) { return p.rpad[a] > p.rpad[b]; });
-    for (int32_t i : order) {
-      const int64_t lo = seg_offsets[i], hi = seg_offsets[i + 1];
+    for (int32_t v = p.groups[s] * P; v < p.groups[s + 1] * P; ++v) order.push_back(v);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      if (p.rpad[a] != p.rpad[b]) return p.rpad[a] > p.rpad[b];
+      if (a % P != b % P) return a % P < b % P;
+      return a < b;
+    });
+    for (int32_t v : order) {
+      const int64_t lo = seg_offsets[v / P], hi = seg_offsets[v / P + 1];
       for (int64_t r0 = lo; r0 < hi; r0 += o.nano_rows) {
-        p.nano.push_back(i);
+        p.nano.push_back(v);
         p.nano.push_back((int32_t)r0);
         p.nano.push_back((int32_t)std::min<int64_t>(o.nano_rows, hi - r0));
       }
       const int64_t kc = std::min<int64_t>(
-          o.chunk_max, std::max<int64_t>(o.chunk_min, (int64_t)o.chunk_per_rank * p.rpad[i]));
-      p.ch_first[i] = (int32_t)p.n_chunks();
+          o.chunk_max, std::max<int64_t>(o.chunk_min, (int64_t)o.chunk_per_rank * p.rpad[v]));
+      p.ch_first[v] = (int32_t)p.n_chunks();
       for (int64_t r0 = lo; r0 < hi; r0 += kc) {
-        p.chunks.push_back(i);
+        p.chunks.push_back(v);
         p.chunks.push_back((int32_t)r0);
         p.chunks.push_back((int32_t)std::min<int64_t>(kc, hi - r0));
         p.cpref.push_back((int32_t)cp);
-        cp += p.rpad[i];
-        p.ch_count[i] += 1;
+        p.cboff.push_back(cb);
+        cp += p.rpad[v];
+        cb += p.rpad[v] * width_of(v);
+        p.ch_count[v] += 1;
       }
     }
   }
   p.nano_start.push_back((int32_t)p.n_nano());
   p.chunk_start.push_back((int32_t)p.n_chunks());
   p.partial_rows = cp;
+  p.partial_b_elems = cb;
 
-  // 7: GEMM row tiles per group with their extension steps
+  // 7: GEMM row tiles per group; each tile lists its extension steps per
+  // projection (the forward's column tiles take their own projection's list,
+  // the dX GEMM takes all of them)
   const int64_t BM = o.gemm_rows;
   for (int32_t s = 0; s < S; ++s) {
     p.tile_start.push_back((int32_t)p.n_tiles());
@@ -197,17 +241,20 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
     int32_t first = p.groups[s];  // first adapter that can still meet a tile
     for (int64_t t0 = R0; t0 < R1; t0 += BM) {
       const int64_t rows = std::min<int64_t>(BM, R1 - t0);
-      p.ext_start.push_back((int32_t)p.n_ext());
       while (first < p.groups[s + 1] && seg_offsets[first + 1] <= t0) ++first;
-      for (int32_t j = first; j < p.groups[s + 1] && seg_offsets[j] < t0 + rows; ++j) {
-        const int64_t lo = std::max<int64_t>(seg_offsets[j], t0);
-        const int64_t hi = std::min<int64_t>(seg_offsets[j + 1], t0 + rows);
-        if (lo >= hi) continue;
-        for (int32_t k0 = 0; k0 < p.rpad[j]; k0 += kKStep) {
-          p.ext.push_back(j);
-          p.ext.push_back((int32_t)lo);
-          p.ext.push_back((int32_t)hi);
-          p.ext.push_back(k0);
+      for (int32_t q = 0; q < P; ++q) {
+        p.ext_start.push_back((int32_t)p.n_ext());
+        for (int32_t j = first; j < p.groups[s + 1] && seg_offsets[j] < t0 + rows; ++j) {
+          const int64_t lo = std::max<int64_t>(seg_offsets[j], t0);
+          const int64_t hi = std::min<int64_t>(seg_offsets[j + 1], t0 + rows);
+          if (lo >= hi) continue;
+          const int32_t v = j * P + q;
+          for (int32_t k0 = 0; k0 < p.rpad[v]; k0 += kKStep) {
+            p.ext.push_back(v);
+            p.ext.push_back((int32_t)lo);
+            p.ext.push_back((int32_t)hi);
+            p.ext.push_back(k0);
+          }
         }
       }
       p.tiles.push_back((int32_t)t0);
@@ -217,26 +264,32 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
   p.tile_start.push_back((int32_t)p.n_tiles());
   p.ext_start.push_back((int32_t)p.n_ext());
 
-  // 8: optimizer work items, A_i then B_i of every adapter in pieces of
+  // 8: optimizer work items, A_v then B_v of every pair in pieces of
   // kOptBlock elements
   int64_t nob = 0;
-  for (int32_t i = 0; i < n; ++i)
-    nob += (d_in * ranks[i] + kOptBlock - 1) / kOptBlock + (ranks[i] * d_out + kOptBlock - 1) / kOptBlock;
+  for (int32_t v = 0; v < nv; ++v)
+    nob += (d_in * ranks[v] + kOptBlock - 1) / kOptBlock + (ranks[v] * width_of(v) + kOptBlock - 1) / kOptBlock;
   p.oblk_ok = nob <= kMaxOptBlocks;
   if (p.oblk_ok) {
     p.oblk.reserve((size_t)(2 * nob));
-    for (int32_t i = 0; i < n; ++i) {
-      const int64_t numel[2] = {d_in * ranks[i], ranks[i] * d_out};
+    for (int32_t v = 0; v < nv; ++v) {
+      const int64_t numel[2] = {d_in * ranks[v], ranks[v] * width_of(v)};
       for (int w = 0; w < 2; ++w)
         for (int64_t q = 0; q * kOptBlock < numel[w]; ++q) {
-          p.oblk.push_back(2 * i + w);
+          p.oblk.push_back(2 * v + w);
           p.oblk.push_back((int32_t)q);
         }
     }
   }
 
-  P = std::move(p);
+  P_out = std::move(p);
   return MLORA_OK;
+}
+
+mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ranks, int64_t d_in,
+                        int64_t d_out, int32_t dtype, const mlora_plan_opts* opts, PlanTables& P,
+                        std::string& err) {
+  return build_plan_multi(n, seg_offsets, 1, &d_out, ranks, d_in, dtype, opts, P, err);
 }
 
 mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adapter,
@@ -286,14 +339,14 @@ DeviceLayout device_layout(const PlanTables& p) {
     off = align_up(off + std::max<size_t>(bytes, 1), 256);
     return at;
   };
-  const size_t n = (size_t)p.n;
+  const size_t n = (size_t)p.n, nv = (size_t)p.nv();
   L.offsets = take(8 * (n + 1));
-  L.zoff = take(8 * n);
-  L.ranks = take(4 * n);
-  L.rpad = take(4 * n);
-  L.roff = take(4 * n);
-  L.ch_first = take(4 * n);
-  L.ch_count = take(4 * n);
+  L.zoff = take(8 * nv);
+  L.ranks = take(4 * nv);
+  L.rpad = take(4 * nv);
+  L.roff = take(4 * nv);
+  L.ch_first = take(4 * nv);
+  L.ch_count = take(4 * nv);
   L.nano = take(4 * p.nano.size());
   L.chunks = take(4 * p.chunks.size());
   L.cpref = take(4 * p.cpref.size());
@@ -302,6 +355,9 @@ DeviceLayout device_layout(const PlanTables& p) {
   L.ext = take(4 * p.ext.size());
   L.perm = take(4 * p.perm.size());
   L.oblk = take(4 * p.oblk.size());
+  L.seg0 = take(8 * p.seg0.size());
+  L.pcol = take(4 * p.pcol.size());
+  L.cboff = take(8 * p.cboff.size());
   L.zero = take(256);  // a zero page: loads of rows that must read as zero point here
   L.table_bytes = off;
   const size_t esz = p.dtype == MLORA_BF16 ? 2 : 4;
@@ -315,7 +371,7 @@ DeviceLayout device_layout(const PlanTables& p) {
   L.dz = take((size_t)p.z_elems * esz);
   if (p.dtype == MLORA_BF16) {
     L.part_a = take((size_t)p.partial_rows * (size_t)p.d_in * 4);
-    L.part_b = take((size_t)p.partial_rows * (size_t)p.d_out * 4);
+    L.part_b = take((size_t)p.partial_b_elems * 4);
   } else {
     L.part_a = L.part_b = off;
   }
@@ -343,6 +399,9 @@ std::vector<uint8_t> table_blob(const PlanTables& p, const DeviceLayout& L) {
   put(L.ext, p.ext.data(), 4 * p.ext.size());
   put(L.perm, p.perm.data(), 4 * p.perm.size());
   put(L.oblk, p.oblk.data(), 4 * p.oblk.size());
+  put(L.seg0, p.seg0.data(), 8 * p.seg0.size());
+  put(L.pcol, p.pcol.data(), 4 * p.pcol.size());
+  put(L.cboff, p.cboff.data(), 8 * p.cboff.size());
   return b;
 }
 

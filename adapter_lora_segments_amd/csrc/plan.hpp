@@ -26,13 +26,19 @@ struct Opts {
   int32_t w0_layout = MLORA_W0_KN;
 };
 
+// Several projections that share one input (nproj > 1) split the output
+// columns: projection q owns [pcol[q], pcol[q+1]).  Every (adapter i,
+// projection q) pair is planned as its own unit v = i*nproj + q over adapter
+// i's rows; tables indexed "per adapter" below have one entry per pair.  A
+// single projection is nproj = 1 and v = i.
 struct PlanTables {
   int32_t n = 0;
+  int32_t nproj = 1;
   int64_t T = 0, d_in = 0, d_out = 0;
   int32_t dtype = MLORA_BF16;
   Opts opts;
   int32_t n_groups = 0;
-  int64_t z_elems = 0, rpad_total = 0, partial_rows = 0;
+  int64_t z_elems = 0, rpad_total = 0, partial_rows = 0, partial_b_elems = 0;
 
   std::vector<int64_t> offsets, zoff;
   std::vector<int32_t> ranks, rpad, roff, groups;
@@ -41,6 +47,9 @@ struct PlanTables {
   std::vector<int32_t> ch_first, ch_count;
   std::vector<int32_t> tiles, tile_start;          // tiles: [n_tiles][2]
   std::vector<int32_t> ext, ext_start;             // ext: [n_ext][4]
+  std::vector<int32_t> pcol;   // [nproj+1] first output column of each projection
+  std::vector<int64_t> seg0;   // [nv] first row of the pair's adapter
+  std::vector<int64_t> cboff;  // [n_chunks] element offset of the chunk's dB partial
   std::vector<int32_t> perm;  // [T] grouped row -> caller row (plans from ids; empty otherwise)
   std::vector<int32_t> oblk;  // [n_oblk][2] optimizer work items (tensor 2i: A_i, 2i+1: B_i; piece)
   bool oblk_ok = true;        // false: the layer is too large for the optimizer table
@@ -50,12 +59,18 @@ struct PlanTables {
   int64_t n_tiles() const { return (int64_t)tiles.size() / 2; }
   int64_t n_ext() const { return (int64_t)ext.size() / 4; }
   int64_t n_oblk() const { return (int64_t)oblk.size() / 2; }
+  int32_t nv() const { return n * nproj; }
 };
 
 // Validates and fills `out`.  On error returns the status and a message.
 mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ranks, int64_t d_in,
                         int64_t d_out, int32_t dtype, const mlora_plan_opts* opts, PlanTables& out,
                         std::string& err);
+
+// Several projections sharing one input: widths [P], ranks [n][P].
+mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, const int64_t* widths,
+                              const int32_t* ranks, int64_t d_in, int32_t dtype, const mlora_plan_opts* opts,
+                              PlanTables& out, std::string& err);
 
 // The same for rows in the caller's order with per-token adapter ids: a
 // stable counting sort by id gives the segments and the permutation.
@@ -67,7 +82,7 @@ mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adap
 struct DeviceLayout {
   // offsets (bytes) of each table inside the table blob
   size_t offsets, zoff, ranks, rpad, roff, ch_first, ch_count, nano, chunks, cpref, tiles,
-      ext_start, ext, zero, perm, oblk;
+      ext_start, ext, zero, perm, oblk, seg0, pcol, cboff;
   size_t table_bytes;
   // offsets (bytes) of the work buffers inside the workspace
   size_t acat_t, acat, bcat_t, dz, part_a, part_b;

@@ -81,6 +81,7 @@ typedef enum { MLORA_W0_KN = 0, MLORA_W0_NK = 1 } mlora_w0_layout;
 #define MLORA_MAX_RANK 256
 #define MLORA_MAX_ADAPTERS 65536
 #define MLORA_MAX_STREAMS 4
+#define MLORA_MAX_PROJECTIONS 8
 
 /* Plan options.  A zero field takes its default. */
 typedef struct {
@@ -138,6 +139,35 @@ mlora_status mlora_plan_from_ids(int32_t n, int64_t T, const int32_t *token_adap
                                  const int32_t *ranks, int64_t d_in, int64_t d_out, mlora_dtype dtype,
                                  const mlora_plan_opts *opts, mlora_plan_t *out);
 
+/*
+ * mlora_plan_multi -- one packed layer over several projections that share
+ * the same input, e.g. Q, K and V of an attention block or gate and up of an
+ * MLP block (PLoRA §8: an adapter can target each of these matrices; they
+ * all read the block's input).  Projection q has output width widths[q];
+ * the projections are concatenated along the output: q owns columns
+ * [c_q, c_q + widths[q]) of Y, dY and W0 (c_q = sum of earlier widths,
+ * d_out = sum of all widths), so W0 is the concatenated frozen weight
+ * [d_in][d_out] (KN) or [d_out][d_in] (NK).  Adapter i has, for every
+ * projection q, its own rank ranks[i * n_proj + q] in [1, 256], A_iq
+ * [d_in][r_iq], B_iq [r_iq][widths[q]] and scale; forward, backward and
+ * mlora_adamw_step take the per-adapter device arrays (A, B, scales, dA, dB,
+ * and the optimizer's) with n * n_proj entries in that order.  Per pair
+ * (i, q) the layer computes standard LoRA on adapter i's rows and columns of
+ * q; dX sums every projection:
+ *   Y_i[:, cols_q] = X_i W0_q + s_iq X_i A_iq B_iq
+ *   dX_i = sum_q (dY_i[:, cols_q] W0_q^T + s_iq dY_i[:, cols_q] B_iq^T A_iq^T)
+ * The plan is mlora_plan's rule over the pairs v = i * n_proj + q (the
+ * tables indexed per adapter have one entry per pair), with buckets ordered
+ * by padded rank, then projection, then adapter, and each GEMM row tile
+ * listing its extension steps projection by projection (TILE_EXT_START has
+ * n_tiles * n_proj + 1 entries).  1 <= n_proj <= MLORA_MAX_PROJECTIONS; with
+ * n_proj > 1 every width must be a multiple of 256 (bf16) or 64 (fp32), so
+ * no GEMM column tile straddles two projections.  n_proj = 1 is mlora_plan.
+ */
+mlora_status mlora_plan_multi(int32_t n, const int64_t *seg_offsets, int32_t n_proj,
+                              const int64_t *widths, const int32_t *ranks, int64_t d_in,
+                              mlora_dtype dtype, const mlora_plan_opts *opts, mlora_plan_t *out);
+
 void mlora_plan_destroy(mlora_plan_t plan);
 
 typedef struct {
@@ -149,6 +179,7 @@ typedef struct {
   int64_t rpad_total, partial_rows;
   int64_t n_nano, n_chunks, n_tiles, n_ext;
   int64_t n_opt_blocks;      /* optimizer work items (0: layer too large, see mlora_adamw_step) */
+  int64_t n_proj;            /* projections sharing the input (1 unless mlora_plan_multi) */
 } mlora_plan_info;
 
 mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);
@@ -164,7 +195,14 @@ mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);
  *   OFFSETS[n+1], RANKS[n], PERM[T] (plans from ids; empty otherwise),
  *   OPT_BLOCKS[n_opt_blocks][2] (tensor, piece): the work items of
  *   mlora_adamw_step, for every adapter i ascending A_i (tensor 2i) then B_i
- *   (tensor 2i+1), each cut into pieces of 2048 elements. */
+ *   (tensor 2i+1), each cut into pieces of 2048 elements,
+ *   PROJ_COLS[n_proj+1] (first output column of each projection, then
+ *   d_out), SEG_START[n*n_proj] (int64: first row of each pair's adapter),
+ *   CHUNK_BOFF[n_chunks] (int64: element offset of each chunk's dB partial
+ *   sums, rows of the chunk's projection width).
+ * With mlora_plan_multi, "adapter" above means the (adapter, projection)
+ * pair v = i * n_proj + q: RANKS, RPAD, ZOFF, ROFF and the per-adapter chunk
+ * tables have n * n_proj entries; OFFSETS and GROUPS are over adapters. */
 typedef enum {
   MLORA_TAB_RPAD = 0,
   MLORA_TAB_ZOFF,
@@ -185,6 +223,9 @@ typedef enum {
   MLORA_TAB_RANKS,
   MLORA_TAB_PERM,
   MLORA_TAB_OPT_BLOCKS,
+  MLORA_TAB_PROJ_COLS,
+  MLORA_TAB_SEG_START,
+  MLORA_TAB_CHUNK_BOFF,
   MLORA_TAB_COUNT
 } mlora_table;
 

@@ -32,6 +32,16 @@ Rule (all integers; counts and indexes int32, offsets into tensors int64):
     (tensor 2i, d_in r_i elements) then B_i (tensor 2i+1, r_i d_out
     elements), each cut into consecutive pieces of OPT_BLOCK elements (last
     one partial).  Entry (tensor, piece).
+
+Several projections sharing the input (widths d_0 .. d_{P-1}, ranks [n][P]):
+every (adapter i, projection q) pair v = i P + q is planned as a unit over
+adapter i's rows.  Rules 1, 2, 5, 6 and 8 run over pairs (B_v has d_q
+columns); rule 3 stays over adapters; rule 4 orders a group's pairs by
+r_pad descending, then projection, then adapter; rule 7 lists each tile's
+steps projection by projection (tile_ext_start has n_tiles P + 1 entries),
+pairs of one projection by adapter.  A chunk's dB partial sits at element
+offset chunk_boff(c) = sum over earlier chunks of r_pad(v) d_q(v).  P = 1 is
+the single-projection plan (v = i).
 """
 from __future__ import annotations
 
@@ -60,25 +70,35 @@ def _pow2_at_least(r: int) -> int:
     return p
 
 
-def build_plan(offsets, ranks, opts: PlanOpts | None = None) -> dict:
+def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None) -> dict:
+    """The plan tables.  ``widths``: output widths of projections sharing the
+    input (then ``ranks`` is [n][P]); None is one projection (its width only
+    enters chunk_boff, reported as chunk_rpref * d_out by the caller)."""
     opts = opts or PlanOpts()
     o = [int(v) for v in offsets]
-    rk = [int(v) for v in ranks]
-    n = len(rk)
-    assert len(o) == n + 1 and o[0] == 0
+    n = len(o) - 1
+    if widths is None:
+        P, wd = 1, [1]
+        rk = [int(v) for v in ranks]
+    else:
+        P, wd = len(widths), [int(v) for v in widths]
+        rk = [int(ranks[i][q]) for i in range(n) for q in range(P)]
+    nv = n * P
+    assert len(rk) == nv and o[0] == 0
     assert all(o[i] <= o[i + 1] for i in range(n))
     assert all(1 <= r <= 256 for r in rk)
     T = o[n]
     cnt = [o[i + 1] - o[i] for i in range(n)]
     rpad = [max(32, _pow2_at_least(r)) for r in rk]
 
-    zoff, roff = [], []
+    zoff, roff, seg_start = [], [], []
     z = rr = 0
-    for i in range(n):
+    for v in range(nv):
         zoff.append(z)
         roff.append(rr)
-        z += cnt[i] * rpad[i]
-        rr += rpad[i]
+        seg_start.append(o[v // P])
+        z += cnt[v // P] * rpad[v]
+        rr += rpad[v]
 
     S = min(opts.n_streams, n)
     g = [0] * (S + 1)
@@ -93,30 +113,33 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None) -> dict:
         g[s] = max(g[s - 1], a)
 
     def bucket_order(s):
-        idx = list(range(g[s], g[s + 1]))
-        return sorted(idx, key=lambda i: (-rpad[i], i))
+        idx = list(range(g[s] * P, g[s + 1] * P))
+        return sorted(idx, key=lambda v: (-rpad[v], v % P, v // P))
 
     nb, nb_start = [], []
-    ch, ch_start, cpref = [], [], []
-    ch_first = [0] * n
-    ch_count = [0] * n
-    cp = 0
+    ch, ch_start, cpref, cboff = [], [], [], []
+    ch_first = [0] * nv
+    ch_count = [0] * nv
+    cp = cb = 0
     for s in range(S):
         nb_start.append(len(nb))
         ch_start.append(len(ch))
-        for i in bucket_order(s):
-            r0 = o[i]
-            while r0 < o[i + 1]:
-                nb.append((i, r0, min(opts.nano_rows, o[i + 1] - r0)))
+        for v in bucket_order(s):
+            lo, hi = o[v // P], o[v // P + 1]
+            r0 = lo
+            while r0 < hi:
+                nb.append((v, r0, min(opts.nano_rows, hi - r0)))
                 r0 += opts.nano_rows
-            kc = min(opts.chunk_max, max(opts.chunk_min, opts.chunk_per_rank * rpad[i]))
-            ch_first[i] = len(ch)
-            r0 = o[i]
-            while r0 < o[i + 1]:
-                ch.append((i, r0, min(kc, o[i + 1] - r0)))
+            kc = min(opts.chunk_max, max(opts.chunk_min, opts.chunk_per_rank * rpad[v]))
+            ch_first[v] = len(ch)
+            r0 = lo
+            while r0 < hi:
+                ch.append((v, r0, min(kc, hi - r0)))
                 cpref.append(cp)
-                cp += rpad[i]
-                ch_count[i] += 1
+                cboff.append(cb)
+                cp += rpad[v]
+                cb += rpad[v] * wd[v % P]
+                ch_count[v] += 1
                 r0 += kc
     nb_start.append(len(nb))
     ch_start.append(len(ch))
@@ -129,12 +152,14 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None) -> dict:
         t0 = R0
         while t0 < R1:
             rows = min(BM, R1 - t0)
-            ext_start.append(len(ext))
-            for j in range(g[s], g[s + 1]):
-                lo, hi = max(o[j], t0), min(o[j + 1], t0 + rows)
-                if lo < hi:
-                    for k0 in range(0, rpad[j], KSTEP):
-                        ext.append((j, lo, hi, k0))
+            for q in range(P):
+                ext_start.append(len(ext))
+                for j in range(g[s], g[s + 1]):
+                    lo, hi = max(o[j], t0), min(o[j + 1], t0 + rows)
+                    if lo < hi:
+                        v = j * P + q
+                        for k0 in range(0, rpad[v], KSTEP):
+                            ext.append((v, lo, hi, k0))
             tiles.append((t0, rows))
             t0 += BM
     tile_start.append(len(tiles))
@@ -168,6 +193,10 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None) -> dict:
         "tile_start": a32(tile_start),
         "ext": a32(ext, 4),
         "tile_ext_start": a32(ext_start),
+        "seg_start": np.asarray(seg_start, dtype=np.int64),
+        "chunk_boff": np.asarray(cboff, dtype=np.int64),
+        "proj_cols": a32(np.concatenate([[0], np.cumsum(wd)]) if widths is not None else [0]),
+        "partial_b_elems": cb,
     }
 
 
@@ -196,11 +225,17 @@ def build_plan_from_ids(token_adapter, ranks, opts: PlanOpts | None = None) -> d
     return plan
 
 
-def optimizer_blocks(ranks, d_in, d_out) -> np.ndarray:
-    """Rule 8: the (tensor, piece) work items of the per-adapter optimizer step."""
+def optimizer_blocks(ranks, d_in, d_out, widths=None) -> np.ndarray:
+    """Rule 8: the (tensor, piece) work items of the per-adapter optimizer
+    step.  With ``widths``, ranks is [n][P] and pair v = i P + q has B of
+    widths[q] columns."""
+    if widths is None:
+        pairs = [(int(r), int(d_out)) for r in ranks]
+    else:
+        pairs = [(int(ranks[i][q]), int(widths[q])) for i in range(len(ranks)) for q in range(len(widths))]
     out = []
-    for i, r in enumerate(int(v) for v in ranks):
-        for t, numel in ((2 * i, d_in * r), (2 * i + 1, r * d_out)):
+    for i, (r, w) in enumerate(pairs):
+        for t, numel in ((2 * i, d_in * r), (2 * i + 1, r * w)):
             for piece in range(-(-numel // OPT_BLOCK)):
                 out.append((t, piece))
     return np.asarray(out, dtype=np.int32).reshape(-1, 2)

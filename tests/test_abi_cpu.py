@@ -51,6 +51,11 @@ def _mirror_vs_library(off, ranks, d_in, d_out, dtype, opts):
     assert np.array_equal(p.export("offsets"), np.asarray(off, dtype=np.int64))
     ob = optimizer_blocks(ranks, d_in, d_out)
     assert np.array_equal(p.export("opt_blocks"), ob) and p.info["n_opt_blocks"] == ob.shape[0]
+    # one projection: pairs are the adapters, dB partials of d_out columns per rank row
+    assert np.array_equal(p.export("seg_start"), np.asarray(off[:-1], dtype=np.int64))
+    assert np.array_equal(p.export("chunk_boff"), m["chunk_rpref"].astype(np.int64) * d_out)
+    assert np.array_equal(p.export("proj_cols"), np.asarray([0, d_out], dtype=np.int32))
+    assert p.info["n_proj"] == 1
 
 
 @st.composite
@@ -233,3 +238,77 @@ def test_adamw_hparams_layout():
     raw = np.frombuffer(bytes(h), dtype=np.uint8)
     assert np.array_equal(raw[:20].view(np.float32), np.float32([1e-4, 0.9, 0.999, 1e-8, 0.01]))
     assert raw[20:].view(np.int32)[0] == 3
+
+
+TABLES_ALL = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
+              "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count", "tiles", "tile_start", "ext",
+              "tile_ext_start", "seg_start", "chunk_boff", "proj_cols"]
+
+
+@st.composite
+def multi_cases(draw):
+    n = draw(st.integers(1, 12))
+    P = draw(st.integers(1, 4))
+    dtype = draw(st.sampled_from(["bf16", "fp32"]))
+    unit = 256 if dtype == "bf16" else 64
+    widths = [unit * draw(st.integers(1, 6)) for _ in range(P)]
+    toks = draw(st.lists(st.one_of(st.just(0), st.integers(0, 700)), min_size=n, max_size=n))
+    ranks = [draw(st.lists(st.sampled_from([1, 8, 16, 33, 64, 100, 128, 256]), min_size=P, max_size=P))
+             for _ in range(n)]
+    S = draw(st.integers(1, 4))
+    nb = draw(st.sampled_from([32, 64, 256]))
+    off = [0]
+    for t in toks:
+        off.append(off[-1] + t)
+    return off, ranks, widths, dtype, PlanOpts(nano_rows=nb, gemm_rows=256 if dtype == "bf16" else 64,
+                                                n_streams=S)
+
+
+@settings(max_examples=150, deadline=None)
+@given(multi_cases())
+def test_plan_multi_bit_exact_against_mirror(case):
+    """mlora_plan_multi: every table equals the mirror's rule over
+    (adapter, projection) pairs."""
+    off, ranks, widths, dtype, opts = case
+    d_in = 192
+    p = Plan.multi(off, ranks, d_in, widths, dtype, nano_rows=opts.nano_rows, n_streams=opts.n_streams,
+                   gemm_rows=opts.gemm_rows)
+    m = build_plan(off, ranks, opts, widths=widths)
+    for name in TABLES_ALL:
+        got, want = p.export(name), m[name]
+        assert (got.size == 0 and want.size == 0) or (
+            np.array_equal(got, want.reshape(got.shape)) and got.dtype == want.dtype), name
+    assert np.array_equal(p.export("ranks"), np.asarray(ranks, dtype=np.int32).reshape(-1))
+    assert np.array_equal(p.export("offsets"), np.asarray(off, dtype=np.int64))
+    ob = optimizer_blocks(ranks, d_in, None, widths=widths)
+    assert np.array_equal(p.export("opt_blocks"), ob)
+    i = p.info
+    assert i["n_proj"] == len(widths) and i["d_out"] == sum(widths) and i["n"] == len(ranks)
+    assert i["z_elems"] == m["z_elems"] and i["partial_rows"] == m["partial_rows"]
+    assert i["rpad_total"] == m["rpad_total"]
+    if dtype == "bf16":  # the fp32 path keeps no chunk partials
+        assert i["workspace_bytes"] >= i["table_bytes"] + 4 * m["partial_b_elems"]
+
+
+def test_plan_multi_errors():
+    ok = dict(seg_offsets=[0, 5, 9], ranks=[[4, 8], [2, 2]], d_in=128, widths=[256, 512])
+    Plan.multi(**ok)
+    assert _status(lambda: Plan.multi([0, 5, 9], [[4, 8], [2, 2]], 128, [256, 320])) == -2   # width % 256 (bf16)
+    Plan.multi([0, 5, 9], [[4, 8], [2, 2]], 128, [64, 320], "fp32")                        # fp32: % 64
+    assert _status(lambda: Plan.multi([0, 5, 9], [[4, 8], [2, 2]], 128, [64, 96], "fp32")) == -2
+    assert _status(lambda: Plan.multi([0, 5, 9], [[4, 0], [2, 2]], 128, [256, 256])) == -1   # rank 0
+    assert _status(lambda: Plan.multi([0, 5, 9], [[4, 300], [2, 2]], 128, [256, 256])) == -2  # rank > 256
+    assert _status(lambda: Plan.multi([0, 5, 9], [[1] * 9] * 2, 128, [256] * 9)) == -1       # n_proj > 8
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    off = (ctypes.c_int64 * 3)(0, 5, 9)
+    rk = (ctypes.c_int32 * 4)(4, 8, 2, 2)
+    w = (ctypes.c_int64 * 2)(256, 256)
+    assert L.mlora_plan_multi(2, off, 0, w, rk, 128, 1, None, ctypes.byref(h)) == -1          # n_proj 0
+    assert L.mlora_plan_multi(2, off, 2, None, rk, 128, 1, None, ctypes.byref(h)) == -1       # no widths
+    assert L.mlora_plan_multi(40000, off, 2, w, rk, 128, 1, None, ctypes.byref(h)) == -1      # n * n_proj too big
+    assert not h.value
+    p1 = Plan.multi([0, 5, 9], [[4], [8]], 128, [320])                                         # one projection
+    p0 = Plan([0, 5, 9], [4, 8], 128, 320)
+    for name in TABLES_ALL + ["opt_blocks"]:
+        assert np.array_equal(p1.export(name), p0.export(name)), name
