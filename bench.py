@@ -59,22 +59,28 @@ def measured_traffic(workload: str):
     return int(v) if v else None
 
 
-def kernel_rooflines(w, projs, kern, iso, steps):
+def kernel_rooflines(w, units, kern, iso, steps):
     """Achieved rate of every step of the path against its roofline, from the
     per-kernel pass (the weight-gradient kernels from the isolated pass,
     where they do not share the chip with the dX GEMM).  Algorithmic bytes
-    and FLOPs count each operand once (ranks unpadded)."""
+    and FLOPs count each operand once (ranks unpadded); ``units`` lists the
+    projections of each timed layer, and projections in one unit share X,
+    which is then counted once."""
     T = w.T
     snr = sum(n * r for n, r in zip(w.tokens, w.ranks))
     sr = sum(w.ranks)
     work = {"shrink": 0.0, "dz": 0.0, "token_reduce": 0.0, "gemm_fwd": 0.0, "gemm_dx": 0.0}
-    for q in projs:
-        di, do = w.projections[q].d_in, w.projections[q].d_out
-        work["shrink"] += 2.0 * (T * di + di * sr + snr)
-        work["dz"] += 2.0 * (T * do + sr * do + snr)
-        work["token_reduce"] += 2.0 * (T * do + snr) + 4.0 * sr * do + 2.0 * (T * di + snr) + 4.0 * di * sr
-        work["gemm_fwd"] += 2.0 * T * di * do + 2.0 * snr * do
-        work["gemm_dx"] += 2.0 * T * di * do + 2.0 * snr * di
+    for unit in units:
+        di = w.projections[unit[0]].d_in
+        P = len(unit)
+        work["shrink"] += 2.0 * (T * di + P * (di * sr + snr))
+        work["token_reduce"] += 2.0 * T * di + P * (2.0 * snr + 4.0 * di * sr)
+        for q in unit:
+            do = w.projections[q].d_out
+            work["dz"] += 2.0 * (T * do + sr * do + snr)
+            work["token_reduce"] += 2.0 * (T * do + snr) + 4.0 * sr * do
+            work["gemm_fwd"] += 2.0 * T * di * do + 2.0 * snr * do
+            work["gemm_dx"] += 2.0 * T * di * do + 2.0 * snr * di
     out = {}
     for k, src, bound in (("shrink", kern, "hbm"), ("dz", kern, "hbm"), ("token_reduce", iso, "hbm"),
                           ("gemm_fwd", kern, "mfma"), ("gemm_dx", kern, "mfma")):
@@ -147,7 +153,7 @@ def optimizer_step(w, plan, layer, steps, warmup, seed):
     from adapter_lora_segments_amd import AdamW, adamw_hparams
     from workloads import optim
     opt = AdamW(layer)
-    hps = [dict(h, start=0) for h in optim.hyperparameters(w.n, seed)]
+    hps = [dict(h, start=0) for h in optim.hyperparameters(plan.info["n"] * plan.info["n_proj"], seed)]
     hp = adamw_hparams(optim.step_hparams(hps, 0))
     for _ in range(warmup):
         opt.step(hp)
@@ -160,7 +166,7 @@ def optimizer_step(w, plan, layer, steps, warmup, seed):
     tot_ms, n = plan.profile_read()["adamw"]
     plan.profile_enable(False)
     avg = tot_ms / max(n, 1)
-    elems = sum(int(r) * (plan.info["d_in"] + plan.info["d_out"]) for r in plan.ranks)
+    elems = sum(int(r) * (plan.info["d_in"] + int(wd)) for r, wd in zip(plan.ranks, plan.pair_widths))
     gbs = OPT_BYTES_PER_ELEM * elems / (avg * 1e-3) / 1e9
     return {"kernel": "k_adamw (per-adapter AdamW, bf16 copies)", "elements": elems,
             "bytes_per_launch": OPT_BYTES_PER_ELEM * elems, "avg_launch_ms": avg, "launches": n,
@@ -263,6 +269,9 @@ def main():
     ap.add_argument("--no-optimizer", action="store_true",
                     help="skip timing the per-adapter AdamW step (mlora_adamw_step) of the first "
                          "timed projection")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the whole layer with the projections that share an input fused into one "
+                         "packed layer each (q/k/v, gate/up: mlora_plan_multi); implies --all-projections")
     ap.add_argument("--optimizer-only", action="store_true",
                     help="run one forward+backward for real gradients, then time only the "
                          "per-adapter AdamW step of the first projection; one JSON line")
@@ -278,6 +287,7 @@ def main():
     import torch
     from adapter_lora_segments_amd import Plan, PackedLoRALinear, device_check
     from workloads import load_workload
+    from workloads.multi import LAYER_GROUPS, device_multi
     from workloads.tensors import device_tensors
 
     torch.cuda.set_device(0)
@@ -289,10 +299,26 @@ def main():
                           "steps": steps, "data": "synthetic", "results": rows}), flush=True)
         return
     w = load_workload(a.workload, a.seed)
+    if a.fused:
+        a.all_projections, a.no_sequential = True, True
     projs = list(range(len(w.projections))) if a.all_projections else [0]
     SETS = 4
     layers = []
-    for q in projs:
+    groups = LAYER_GROUPS.get(w.name) if a.fused else None
+    if a.fused and not groups:
+        print(f"--fused: {w.name} has no projections that share an input", file=sys.stderr)
+        sys.exit(2)
+    for gname, gp in (groups or []):
+        d = device_multi(w, gp, sets=SETS)
+        plan = Plan.multi(d["offsets"], d["ranks"], d["d_in"], d["widths"], "bf16",
+                          n_streams=a.streams or w.n_streams)
+        flat = lambda nested: [x for row in nested for x in row]
+        layer = PackedLoRALinear(plan, d["W0"], flat(d["A"]), flat(d["B"]), flat(d["scales"]))
+        D = sum(d["widths"])
+        Ys = [torch.empty((w.T, D), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
+        dXs = [torch.empty((w.T, d["d_in"]), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
+        layers.append((plan, layer, d, Ys, dXs))
+    for q in (projs if not groups else []):
         p = w.projections[q]
         d = device_tensors(w, q, sets=SETS)
         if a.shuffled_ids:
@@ -415,6 +441,11 @@ def main():
     p0 = w.projections[0]
     shapes = ", ".join(f"{w.projections[q].name} {w.projections[q].d_in}x{w.projections[q].d_out}"
                        for q in projs)
+    if groups:
+        shapes = "; ".join(f"{g} [" + ", ".join(f"{w.projections[q].name} {w.projections[q].d_in}x"
+                                                f"{w.projections[q].d_out}" for q in gp) + "]"
+                           for g, gp in groups)
+        shapes = "fused groups sharing an input: " + shapes
     out = {
         "metric": "multi-LoRA fwd+bwd tokens/sec per layer",
         "value": tok_s,
@@ -434,23 +465,27 @@ def main():
                    "T": w.T, "d_in": p0.d_in, "d_out": p0.d_out, "adapters": w.n,
                    "projections": [w.projections[q].name for q in projs],
                    "streams": layers[0][0].info["n_groups"],
-                   "rows": "shuffled, per-token adapter ids" if a.shuffled_ids else "adapter segments"},
+                   "rows": "shuffled, per-token adapter ids" if a.shuffled_ids else "adapter segments",
+                   "fused": [g for g, _ in groups] if groups else None},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
     }
     if kern:
         out["kernels_ms_per_step"] = {k: v[0] / a.steps for k, v in kern.items() if v[1]}
-        out["kernel_rooflines"] = kernel_rooflines(w, projs, kern, iso, a.steps)
+        units = [gp for _, gp in groups] if groups else [[q] for q in projs]
+        out["kernel_rooflines"] = kernel_rooflines(w, units, kern, iso, a.steps)
     if prof:
         g_ms, g_n = gemm_rec
         if g_n:
             avg = g_ms / g_n
-            ach = gemm_fwd_flops(w, 0) / (avg * 1e-3) / 1e12
-            out["roofline"] = {"kernel": f"k_gemm<fwd> (base GEMM + fused expand) of {p0.name} "
-                                         f"{p0.d_in}x{p0.d_out}",
+            first = groups[0][1] if groups else [0]
+            ach = sum(gemm_fwd_flops(w, q) for q in first) / (avg * 1e-3) / 1e12
+            kname = "+".join(w.projections[q].name for q in first)
+            out["roofline"] = {"kernel": f"k_gemm<fwd> (base GEMM + fused expand) of {kname} "
+                                         f"{p0.d_in}x{sum(w.projections[q].d_out for q in first)}",
                                "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                               "traffic": measured_traffic(w.name),
+                               "traffic": None if groups else measured_traffic(w.name),
                                "avg_launch_ms": avg}
     if seq_ms is not None:
         out["packed_vs_sequential"] = {
