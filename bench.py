@@ -243,6 +243,47 @@ def packing_sweep(steps, warmup):
     return rows
 
 
+def cost_table(steps, warmup):
+    """Kernel cost table T(r, n, d): one adapter of rank r over n tokens on a
+    d x d layer (bf16, forward + backward), the step time and each kernel
+    kind's share from events on its stream.  The shape of what a planner of
+    packed LoRA jobs consumes (the PLoRA page's cost model, §3.2; its Table 7
+    sizes span d 2048-18944 and ranks 8-128)."""
+    import torch
+    from adapter_lora_segments_amd import Plan, PackedLoRALinear
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rows = []
+    for d in (2048, 4096, 8192):
+        W0 = (torch.randn((d, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        for n in (512, 2048, 8192):
+            X = torch.randn((n, d), generator=g, device="cuda").to(torch.bfloat16)
+            dY = torch.randn((n, d), generator=g, device="cuda").to(torch.bfloat16)
+            Y = torch.empty_like(dY)
+            dX = torch.empty_like(X)
+            for r in (8, 32, 128):
+                A = (torch.randn((d, r), generator=g, device="cuda") * d ** -0.5).to(torch.bfloat16)
+                B = (torch.randn((r, d), generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+                plan = Plan([0, n], [r], d, d, "bf16")
+                layer = PackedLoRALinear(plan, W0, [A], [B], [16.0 / r])
+
+                def one(i):
+                    layer.forward(X, Y)
+                    layer.backward(dY, X, dX)
+                ms = time_steps(one, steps, warmup)
+                plan.profile_enable(True)
+                plan.profile_read()
+                for i in range(steps):
+                    one(i)
+                torch.cuda.synchronize()
+                per = {k: v[0] / steps for k, v in plan.profile_read().items() if v[1]}
+                plan.profile_enable(False)
+                rows.append({"d": d, "tokens": n, "rank": r, "ms_per_step": ms,
+                             "kernels_ms": {k: round(v, 5) for k, v in per.items()}})
+                print(f"# d={d} n={n} r={r}: {ms:.4f} ms", file=sys.stderr, flush=True)
+                del layer, plan, A, B
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,6 +316,9 @@ def main():
     ap.add_argument("--optimizer-only", action="store_true",
                     help="run one forward+backward for real gradients, then time only the "
                          "per-adapter AdamW step of the first projection; one JSON line")
+    ap.add_argument("--cost-table", action="store_true",
+                    help="only measure the kernel cost table T(rank, tokens, hidden) of single-adapter "
+                         "layers and print it as one JSON line")
     ap.add_argument("--packing-sweep", action="store_true",
                     help="only run the packed-against-sequential sweep over Table 7's shapes and "
                          "print its results as one JSON line")
@@ -292,6 +336,13 @@ def main():
 
     torch.cuda.set_device(0)
     device_check()
+    if a.cost_table:
+        steps = min(a.steps, 20)
+        rows = cost_table(steps, min(a.warmup, 5))
+        print(json.dumps({"metric": "single-adapter fwd+bwd time per layer T(rank, tokens, hidden)",
+                          "unit": "ms", "steps": steps, "data": "synthetic", "dtype": "bf16",
+                          "results": rows}), flush=True)
+        return
     if a.packing_sweep:
         steps = min(a.steps, 20)
         rows = packing_sweep(steps, min(a.warmup, 5))
