@@ -16,8 +16,8 @@ W0_LAYOUTS = {"kn": 0, "nk": 1}
 TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
           "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count", "tiles", "tile_start", "ext",
           "tile_ext_start", "offsets", "ranks", "perm", "opt_blocks", "proj_cols", "seg_start",
-          "chunk_boff"]
-TABLE_COLS = {"nb": 3, "chunks": 3, "tiles": 2, "ext": 4, "opt_blocks": 2}
+          "chunk_boff", "ksplit"]
+TABLE_COLS = {"nb": 3, "chunks": 3, "tiles": 2, "ext": 4, "opt_blocks": 2, "ksplit": 2}
 TABLE_I64 = {"zoff", "offsets", "seg_start", "chunk_boff"}
 
 KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep", "adamw"]

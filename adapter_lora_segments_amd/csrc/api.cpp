@@ -373,6 +373,7 @@ mlora_status mlora_plan_export(mlora_plan_t p, int32_t table, void* dst, size_t*
     case MLORA_TAB_PROJ_COLS: v32(P.pcol); break;
     case MLORA_TAB_SEG_START: v64(P.seg0); break;
     case MLORA_TAB_CHUNK_BOFF: v64(P.cboff); break;
+    case MLORA_TAB_KSPLIT: v32(P.ksplit); break;
     default: return fail(MLORA_ERR_INVALID_ARG, "unknown table id " + std::to_string(table));
   }
   if (!dst) {
@@ -473,6 +474,9 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     ga.ext_n = nullptr;
     ga.ext_k = bcat_t;
     ga.rtot = P.rpad_total;
+    ga.ksplit = P.ksplit[2 * g];
+    ga.kper = (int32_t)((P.d_in / 32 + ga.ksplit - 1) / ga.ksplit);
+    ga.part = reinterpret_cast<float*>(wsb + L.kpart) + P.kpart_off[g];
     ga.t = t;
     st = timed(p, MLORA_K_GEMM_FWD, s, [&] { mlora::launch_gemm(true, nk, ga, s); });
     if (st != MLORA_OK) return st;
@@ -598,6 +602,9 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     ga.ext_n = acat_t;
     ga.ext_k = acat;
     ga.rtot = P.rpad_total;
+    ga.ksplit = P.ksplit[2 * g + 1];
+    ga.kper = (int32_t)((P.d_out / 32 + ga.ksplit - 1) / ga.ksplit);
+    ga.part = reinterpret_cast<float*>(wsb + L.kpart) + P.kpart_off[g];
     ga.t = t;
     st = timed(p, MLORA_K_GEMM_DX, s, [&] { mlora::launch_gemm(false, !nk, ga, s); });
     if (st != MLORA_OK) return st;

@@ -95,6 +95,13 @@ struct GemmArgs {
   const uint16_t* ext_n;    // dx, n-contiguous: A_cat^T [rtot][N]
   const uint16_t* ext_k;    // k-contiguous: [N][rtot] (B_cat^T fwd, A_cat dx)
   int64_t rtot;             // sum of padded ranks
+  // Split-K: ksplit > 1 runs ksplit workgroups per output tile, part s
+  // taking main K-steps [s*kper, (s+1)*kper) (the last part also the
+  // extension steps), each writing a 256x256 fp32 partial tile to
+  // part[(s * n_mtiles*n_ntiles + tile)]; a second kernel adds the parts in
+  // order and stores C.
+  int32_t ksplit, kper;
+  float* part;
   DevTables t;
 };
 // main_b_kcontig: Bop element (k, n) at B[n*ldb + k] (else at B[k*ldb + n]).

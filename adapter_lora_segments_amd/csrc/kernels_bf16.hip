@@ -684,7 +684,7 @@ __device__ __forceinline__ u32x4 read_b_tr(const u32x4* tile, int nb, int kb, in
 // refill is a plain K-step of the main operands run a branch-free loop; the
 // few whose refill is a LoRA extension step (or past the end) run a second
 // loop that looks the extension up in the plan's tables.
-template <bool FWD, bool MAIN_B_KC, bool PERM>
+template <bool FWD, bool MAIN_B_KC, bool PERM, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   constexpr int NS = 5;                    // ring stages
   constexpr int FI = 4, FJ = 4;            // 32x32 fragments per wave along M, N
@@ -694,8 +694,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
 
   const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7, q = bid >> 3, per = G >> 3, rem = G & 7;
-  const int L = xcd * per + min(xcd, rem) + q;
+  const int L0 = xcd * per + min(xcd, rem) + q;
   const int nM = g.n_mtiles, nN = g.n_ntiles;
+  const int TT = nM * nN;
+  const int sp = SPLIT ? L0 / TT : 0;        // K part
+  const int L = L0 - sp * TT;                // output tile
   constexpr int GM = 8;
   const int grpm = L / (GM * nN);
   const int fm = grpm * GM;
@@ -712,9 +715,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   int pq = 0;
   while (FWD && pq + 1 < NP && ldc(g.t.pcol + pq + 1) <= n0) ++pq;
   const int e0 = ldc(g.t.ext_start + tix * NP + (FWD ? pq : 0));
-  const int e1 = ldc(g.t.ext_start + tix * NP + (FWD ? pq + 1 : NP));
+  const int e1 = !SPLIT || sp == g.ksplit - 1 ? ldc(g.t.ext_start + tix * NP + (FWD ? pq + 1 : NP)) : e0;
   const int pc0 = ldc(g.t.pcol + pq), pw = ldc(g.t.pcol + pq + 1) - pc0;  // forward: B_j is [r_j][pw]
-  const int nk = g.K / 32;
+  const int kb = SPLIT ? sp * g.kper : 0;         // first main K-step of this part
+  const int nk = SPLIT ? min(g.K / 32 - kb, g.kper) : g.K / 32;
   const int nsteps = nk + (e1 - e0);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -737,11 +741,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int ar = row0 + min(kr_row[i], mrows - 1);  // grouped row; PERM: caller row via the plan
-    aptr[i] = g.A + (int64_t)(PERM ? ldg_i32(g.t.perm + ar) : ar) * g.lda + 8 * kr_chunk[i];
+    aptr[i] = g.A + (int64_t)(PERM ? ldg_i32(g.t.perm + ar) : ar) * g.lda + 8 * kr_chunk[i] + 32 * kb;
     if (MAIN_B_KC)
-      bptr[i] = g.B + (int64_t)min(n0 + kr_row[i], g.N - 1) * g.ldb + 8 * kr_chunk[i];
+      bptr[i] = g.B + (int64_t)min(n0 + kr_row[i], g.N - 1) * g.ldb + 8 * kr_chunk[i] + 32 * kb;
     else
-      bptr[i] = g.B + (int64_t)nc_krow[i] * g.ldb + min(n0 + 8 * nc_chunk[i], g.N - 8);
+      bptr[i] = g.B + (int64_t)(nc_krow[i] + 32 * kb) * g.ldb + min(n0 + 8 * nc_chunk[i], g.N - 8);
   }
 
   // Global sources of this lane's blocks of step `step` (BPW of the A tile,
@@ -889,6 +893,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
 
+  if constexpr (SPLIT) {
+    // fp32 partial tile [256][256] of this K part; rows past the tile are
+    // written too (finite values from clamped rows) and never read
+    float* pt = g.part + (int64_t)(sp * TT + tm * nN + tn) * 65536;
+#pragma unroll
+    for (int fi = 0; fi < FI; ++fi) {
+      const int m = wrow + 32 * fi + l32;
+#pragma unroll
+      for (int fj = 0; fj < FJ; ++fj)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int nn = wcol + 32 * fj + 8 * gg + 4 * half;
+          const f32x4 v = {acc[fi][fj][4 * gg], acc[fi][fj][4 * gg + 1], acc[fi][fj][4 * gg + 2],
+                           acc[fi][fj][4 * gg + 3]};
+          *reinterpret_cast<f32x4*>(pt + m * 256 + nn) = v;
+        }
+    }
+    return;
+  }
+
   // Output tile staged in LDS as bf16 [256][256]: 512-byte rows of 32
   // 16-byte granules, granule c of row m at c ^ (m & 31), so the 32 rows a
   // fragment writes and the 32 granules a row read takes both spread evenly
@@ -925,19 +949,56 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   }
 }
 
+// Sum of the K parts of split-K tiles, in part order, rounded to bf16 and
+// stored at the caller's rows.  One workgroup per 32 rows of a tile, eight
+// columns per thread.
+template <bool PERM>
+__global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
+  const int TT = g.n_mtiles * g.n_ntiles;
+  const int tile = blockIdx.x >> 3, chunk = blockIdx.x & 7;
+  const int tm = tile / g.n_ntiles, tn = tile - tm * g.n_ntiles;
+  const int tix = g.tile_begin + tm;
+  const int row0 = ldc(g.t.tiles + 2 * tix), mrows = ldc(g.t.tiles + 2 * tix + 1);
+  const int c8 = 8 * (threadIdx.x & 31);
+  const int n = tn * 256 + c8;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int m = 32 * chunk + 8 * it + (threadIdx.x >> 5);
+    if (m >= mrows || n >= g.N) continue;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < g.ksplit; ++s) {
+      const float* pt = g.part + (int64_t)(s * TT + tile) * 65536 + m * 256 + c8;
+      lo += *reinterpret_cast<const f32x4*>(pt);
+      hi += *reinterpret_cast<const f32x4*>(pt + 4);
+    }
+    const u32x4 v = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                     pack_bf16x2(hi[2], hi[3])};
+    const int cr = PERM ? ldg_i32(g.t.perm + row0 + m) : row0 + m;
+    *reinterpret_cast<u32x4*>(g.C + (int64_t)cr * g.ldc + n) = v;
+  }
+}
+
 void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s) {
   const int total = g.n_mtiles * g.n_ntiles;
   if (total <= 0) return;
-  dim3 grid((unsigned)total), block(256);
+  dim3 grid((unsigned)(total * g.ksplit)), block(256);
+#define MLORA_GEMM2(F, KC, SP)                                                              \
+  if (g.t.perm) hipLaunchKernelGGL((k_gemm<F, KC, true, SP>), grid, block, 0, s, g);        \
+  else hipLaunchKernelGGL((k_gemm<F, KC, false, SP>), grid, block, 0, s, g);
 #define MLORA_GEMM(F, KC)                                                                  \
-  if (g.t.perm) hipLaunchKernelGGL((k_gemm<F, KC, true>), grid, block, 0, s, g);           \
-  else hipLaunchKernelGGL((k_gemm<F, KC, false>), grid, block, 0, s, g);
+  if (g.ksplit > 1) { MLORA_GEMM2(F, KC, true) } else { MLORA_GEMM2(F, KC, false) }
   if (fwd) {
     if (main_b_kcontig) { MLORA_GEMM(true, true) } else { MLORA_GEMM(true, false) }
   } else {
     if (main_b_kcontig) { MLORA_GEMM(false, true) } else { MLORA_GEMM(false, false) }
   }
 #undef MLORA_GEMM
+#undef MLORA_GEMM2
+  if (g.ksplit > 1) {
+    const dim3 rgrid((unsigned)(total * 8));
+    if (g.t.perm) hipLaunchKernelGGL(k_splitk_reduce<true>, rgrid, block, 0, s, g);
+    else hipLaunchKernelGGL(k_splitk_reduce<false>, rgrid, block, 0, s, g);
+  }
 }
 
 }  // namespace mlora

@@ -22,6 +22,19 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
+// Rule 9: a bf16 GEMM launch of `tiles` 256x256 output tiles and `nk`
+// 32-deep K-steps splits K into S parts when it would fill under half the
+// chip: S x tiles stays within one round of 256 CUs, each part keeps at
+// least 8 K-steps, S <= 16, and the parts are ceil(nk / S) steps each (S
+// recomputed so none is empty).
+int32_t split_k(int64_t tiles, int64_t nk) {
+  if (tiles <= 0 || tiles >= 128 || nk < 16) return 1;
+  int64_t sp = std::min<int64_t>({256 / tiles, nk / 8, 16});
+  if (sp < 2) return 1;
+  const int64_t kper = (nk + sp - 1) / sp;
+  return (int32_t)((nk + kper - 1) / kper);
+}
+
 mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, const int64_t* widths,
                               const int32_t* ranks, int64_t d_in, int32_t dtype, const mlora_plan_opts* opts,
                               PlanTables& P_out, std::string& err) {
@@ -264,6 +277,23 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
   p.tile_start.push_back((int32_t)p.n_tiles());
   p.ext_start.push_back((int32_t)p.n_ext());
 
+  // 9: split-K of each group's forward and dX GEMM (bf16), and each group's
+  // region of fp32 partial tiles (groups run concurrently; a group's two
+  // GEMMs never do)
+  p.ksplit.assign(2 * S, 1);
+  p.kpart_off.assign(S + 1, 0);
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t nm = p.tile_start[s + 1] - p.tile_start[s];
+    const int64_t tf = nm * ((d_out + 255) / 256), td = nm * ((d_in + 255) / 256);
+    if (dtype == MLORA_BF16) {
+      p.ksplit[2 * s] = split_k(tf, d_in / kKStep);
+      p.ksplit[2 * s + 1] = split_k(td, d_out / kKStep);
+    }
+    const int64_t need = std::max(p.ksplit[2 * s] > 1 ? p.ksplit[2 * s] * tf : 0,
+                                  p.ksplit[2 * s + 1] > 1 ? p.ksplit[2 * s + 1] * td : 0);
+    p.kpart_off[s + 1] = p.kpart_off[s] + need * 65536;
+  }
+
   // 8: optimizer work items, A_v then B_v of every pair in pieces of
   // kOptBlock elements
   int64_t nob = 0;
@@ -369,6 +399,7 @@ DeviceLayout device_layout(const PlanTables& p) {
     L.acat_t = L.acat = L.bcat_t = off;
   }
   L.dz = take((size_t)p.z_elems * esz);
+  L.kpart = take((size_t)p.kpart_off.back() * 4);
   if (p.dtype == MLORA_BF16) {
     L.part_a = take((size_t)p.partial_rows * (size_t)p.d_in * 4);
     L.part_b = take((size_t)p.partial_b_elems * 4);

@@ -50,6 +50,8 @@ struct PlanTables {
   std::vector<int32_t> pcol;   // [nproj+1] first output column of each projection
   std::vector<int64_t> seg0;   // [nv] first row of the pair's adapter
   std::vector<int64_t> cboff;  // [n_chunks] element offset of the chunk's dB partial
+  std::vector<int32_t> ksplit;    // [S'][2] K-split of each group's forward and dX GEMM
+  std::vector<int64_t> kpart_off; // [S'+1] each group's fp32 partial tiles (elements)
   std::vector<int32_t> perm;  // [T] grouped row -> caller row (plans from ids; empty otherwise)
   std::vector<int32_t> oblk;  // [n_oblk][2] optimizer work items (tensor 2i: A_i, 2i+1: B_i; piece)
   bool oblk_ok = true;        // false: the layer is too large for the optimizer table
@@ -85,11 +87,14 @@ struct DeviceLayout {
       ext_start, ext, zero, perm, oblk, seg0, pcol, cboff;
   size_t table_bytes;
   // offsets (bytes) of the work buffers inside the workspace
-  size_t acat_t, acat, bcat_t, dz, part_a, part_b;
+  size_t acat_t, acat, bcat_t, dz, kpart, part_a, part_b;
   size_t workspace_bytes;
 };
 
 DeviceLayout device_layout(const PlanTables& p);
+
+// K-split factor of a bf16 GEMM launch (rule 9 of the plan).
+int32_t split_k(int64_t tiles, int64_t nk);
 std::vector<uint8_t> table_blob(const PlanTables& p, const DeviceLayout& L);
 
 }  // namespace mlora

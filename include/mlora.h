@@ -116,6 +116,14 @@ typedef struct mlora_plan_s *mlora_plan_t;
  *     rank-row prefix cpref(c) = sum of r_pad over earlier chunks.
  *  7. GEMM row tiles of BM rows per group; each tile lists extension steps
  *     (adapter j, rows [lo,hi) of j in the tile, k0 = 0,32,..<r_pad(j)).
+ *  8. Optimizer work items (see OPT_BLOCKS below).
+ *  9. bf16 only: a group's GEMM with t = (row tiles) x ceil(N / 256) output
+ *     tiles and nk = K / 32 K-steps (forward: N = d_out, K = d_in; dX:
+ *     N = d_in, K = d_out) splits K into S parts when t < 128 and nk >= 16:
+ *     S = min(floor(256 / t), floor(nk / 8), 16), then with kper =
+ *     ceil(nk / S), S = ceil(nk / kper); S < 2 means no split.  The parts'
+ *     fp32 sums are added in part order, so results stay bitwise
+ *     repeatable.
  * The copies of seg_offsets/ranks are the plan's; the caller's arrays may be
  * freed on return.  On error *out is left untouched.
  */
@@ -199,7 +207,8 @@ mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);
  *   PROJ_COLS[n_proj+1] (first output column of each projection, then
  *   d_out), SEG_START[n*n_proj] (int64: first row of each pair's adapter),
  *   CHUNK_BOFF[n_chunks] (int64: element offset of each chunk's dB partial
- *   sums, rows of the chunk's projection width).
+ *   sums, rows of the chunk's projection width), KSPLIT[S'][2] (K-split of
+ *   each group's forward and dX GEMM, rule 9 of mlora_plan).
  * With mlora_plan_multi, "adapter" above means the (adapter, projection)
  * pair v = i * n_proj + q: RANKS, RPAD, ZOFF, ROFF and the per-adapter chunk
  * tables have n * n_proj entries; OFFSETS and GROUPS are over adapters. */
@@ -226,6 +235,7 @@ typedef enum {
   MLORA_TAB_PROJ_COLS,
   MLORA_TAB_SEG_START,
   MLORA_TAB_CHUNK_BOFF,
+  MLORA_TAB_KSPLIT,
   MLORA_TAB_COUNT
 } mlora_table;
 

@@ -33,6 +33,12 @@ Rule (all integers; counts and indexes int32, offsets into tensors int64):
     elements), each cut into consecutive pieces of OPT_BLOCK elements (last
     one partial).  Entry (tensor, piece).
 
+ 9. Split-K (bf16 only): a group's GEMM with t = (its row tiles) x ceil(N/256)
+    output tiles and nk = K/32 K-steps (forward N = d_out, K = d_in; dX
+    N = d_in, K = d_out) splits K into S parts when t < 128 and nk >= 16:
+    S = min(floor(256/t), floor(nk/8), 16); then kper = ceil(nk/S) and
+    S = ceil(nk/kper); S < 2 means 1.  Entry per group: (S_forward, S_dX).
+
 Several projections sharing the input (widths d_0 .. d_{P-1}, ranks [n][P]):
 every (adapter i, projection q) pair v = i P + q is planned as a unit over
 adapter i's rows.  Rules 1, 2, 5, 6 and 8 run over pairs (B_v has d_q
@@ -70,7 +76,18 @@ def _pow2_at_least(r: int) -> int:
     return p
 
 
-def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None) -> dict:
+def split_k(tiles, nk):
+    """Rule 9 for one GEMM launch."""
+    if tiles <= 0 or tiles >= 128 or nk < 16:
+        return 1
+    sp = min(256 // tiles, nk // 8, 16)
+    if sp < 2:
+        return 1
+    kper = -(-nk // sp)
+    return -(-nk // kper)
+
+
+def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None, dims=None) -> dict:
     """The plan tables.  ``widths``: output widths of projections sharing the
     input (then ``ranks`` is [n][P]); None is one projection (its width only
     enters chunk_boff, reported as chunk_rpref * d_out by the caller)."""
@@ -165,6 +182,17 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None) -> dic
     tile_start.append(len(tiles))
     ext_start.append(len(ext))
 
+    ksplit = []
+    if dims is not None:
+        d_in, d_out, dtype = dims
+        for s in range(S):
+            nm = tile_start[s + 1] - tile_start[s]
+            if dtype == "bf16":
+                ksplit.append((split_k(nm * -(-d_out // 256), d_in // 32),
+                               split_k(nm * -(-d_in // 256), d_out // 32)))
+            else:
+                ksplit.append((1, 1))
+
     def a32(x, cols=None):
         a = np.asarray(x, dtype=np.int32)
         if cols is not None:
@@ -197,6 +225,7 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None) -> dic
         "chunk_boff": np.asarray(cboff, dtype=np.int64),
         "proj_cols": a32(np.concatenate([[0], np.cumsum(wd)]) if widths is not None else [0]),
         "partial_b_elems": cb,
+        "ksplit": a32(ksplit, 2) if dims is not None else None,
     }
 
 

@@ -34,10 +34,10 @@ def _mirror_vs_library(off, ranks, d_in, d_out, dtype, opts):
     p = Plan(off, ranks, d_in, d_out, dtype, nano_rows=opts.nano_rows, gemm_rows=opts.gemm_rows,
              n_streams=opts.n_streams, chunk_min=opts.chunk_min, chunk_max=opts.chunk_max,
              chunk_per_rank=opts.chunk_per_rank)
-    m = build_plan(off, ranks, opts)
+    m = build_plan(off, ranks, opts, dims=(d_in, d_out, dtype))
     for name in ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks",
                  "chunk_start", "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count",
-                 "tiles", "tile_start", "ext", "tile_ext_start"]:
+                 "tiles", "tile_start", "ext", "tile_ext_start", "ksplit"]:
         got = p.export(name)
         want = m[name]
         if want.size == 0:
@@ -273,8 +273,8 @@ def test_plan_multi_bit_exact_against_mirror(case):
     d_in = 192
     p = Plan.multi(off, ranks, d_in, widths, dtype, nano_rows=opts.nano_rows, n_streams=opts.n_streams,
                    gemm_rows=opts.gemm_rows)
-    m = build_plan(off, ranks, opts, widths=widths)
-    for name in TABLES_ALL:
+    m = build_plan(off, ranks, opts, widths=widths, dims=(d_in, sum(widths), dtype))
+    for name in TABLES_ALL + ["ksplit"]:
         got, want = p.export(name), m[name]
         assert (got.size == 0 and want.size == 0) or (
             np.array_equal(got, want.reshape(got.shape)) and got.dtype == want.dtype), name
@@ -312,3 +312,29 @@ def test_plan_multi_errors():
     p0 = Plan([0, 5, 9], [4, 8], 128, 320)
     for name in TABLES_ALL + ["opt_blocks"]:
         assert np.array_equal(p1.export(name), p0.export(name)), name
+
+
+def test_split_k_rule():
+    """Rule 9 read back from the library on hand-worked launches."""
+    from oracle.plan_mirror import split_k
+    # 7680 rows, 4096 x 4096: 30 x 16 = 480 tiles -> no split
+    p = Plan([0, 7680], [16], 4096, 4096)
+    assert p.export("ksplit").tolist() == [[1, 1]]
+    # 512 rows, 2048 x 2048: 2 x 8 = 16 tiles, 64 K-steps: S = min(256 // 16, 64 // 8, 16) = 8
+    p = Plan([0, 512], [16], 2048, 2048)
+    assert p.export("ksplit").tolist() == [[8, 8]]
+    # 300 rows, d_in 512, d_out 8192: forward 2 x 32 = 64 tiles, 16 K-steps -> S = min(4, 2, 16) = 2;
+    # dX 2 x 2 = 4 tiles, 256 K-steps -> S = 16
+    p = Plan([0, 300], [8], 512, 8192)
+    assert p.export("ksplit").tolist() == [[2, 16]]
+    # K below 16 steps never splits; fp32 never splits
+    assert Plan([0, 100], [8], 256, 256).export("ksplit").tolist() == [[1, 1]]
+    assert Plan([0, 512], [16], 2048, 2048, "fp32").export("ksplit").tolist() == [[1, 1]]
+    # 2048 rows, 3584 x 3584: 8 x 14 = 112 tiles -> S = 256 // 112 = 2 (224 workgroups, one round)
+    assert Plan([0, 2048], [64], 3584, 3584).export("ksplit").tolist() == [[2, 2]]
+    # every part non-empty: (S - 1) * ceil(nk / S) < nk over a range of shapes
+    for tiles in range(1, 130):
+        for nk in range(1, 700, 7):
+            S = split_k(tiles, nk)
+            kper = -(-nk // S)
+            assert 1 <= S <= 16 and (S - 1) * kper < nk and (S == 1 or S * tiles <= 256), (tiles, nk, S)
