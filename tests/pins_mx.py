@@ -1,0 +1,92 @@
+"""Checks that pin the MXFP8 decoding oracle (oracle/mx.py) to facts other
+than itself.
+
+- every E4M3 code against torch.float8_e4m3fn (an independent decoder), and
+  hand-worked codes of the format's definition: 1.0, 1.5, 2.0, the largest
+  finite 448, the smallest normal 2^-6, the smallest subnormal 2^-9,
+  negative zero, NaN;
+- E8M0 scale codes: 127 is 1, 0 is 2^-127, 254 is 2^127, 255 is NaN;
+- nearest-even rounding to bf16 on hand-worked bit patterns (ties both ways,
+  a carry into the exponent, NaN kept);
+- dequantization of both layouts: a block's scale covers exactly its 32
+  consecutive inputs of one output column, and the two layouts give the same
+  weight for transposed codes;
+- torch float64 decoding and matmul of a small quantized layer against the
+  oracle's decoded weight fed to the plain layer oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import lora as ol
+
+
+def pin_e4m3_table_vs_torch(om):
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = om.decode_e4m3(codes)
+    both_nan = np.isnan(t) & np.isnan(ours)
+    assert np.array_equal(np.isnan(t), np.isnan(ours)), "NaN codes differ"
+    assert np.array_equal(t[~both_nan], ours[~both_nan]), "E4M3 values differ from torch"
+    assert np.array_equal(np.signbit(t[~both_nan]), np.signbit(ours[~both_nan])), "signed zero differs"
+
+
+def pin_e4m3_hand_codes(om):
+    want = {0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+            0x07: 7 * 2.0 ** -9, 0x00: 0.0, 0xFE: -448.0, 0xB8: -1.0}
+    got = om.decode_e4m3(np.asarray(list(want), dtype=np.uint8))
+    assert np.array_equal(got, np.asarray(list(want.values()))), got
+    assert np.signbit(om.decode_e4m3(np.asarray([0x80], dtype=np.uint8)))[0], "0x80 is negative zero"
+    assert np.all(np.isnan(om.decode_e4m3(np.asarray([0x7F, 0xFF], dtype=np.uint8)))), "S.1111.111 is NaN"
+
+
+def pin_e8m0(om):
+    got = om.decode_e8m0(np.asarray([127, 0, 254, 128, 120], dtype=np.uint8))
+    assert np.array_equal(got, [1.0, 2.0 ** -127, 2.0 ** 127, 2.0, 2.0 ** -7]), got
+    assert np.isnan(om.decode_e8m0(np.asarray([255], dtype=np.uint8)))[0]
+
+
+def pin_round_bf16(om):
+    vals = [1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -7, -2.0, 2 - 2.0 ** -9, 0.0, 448.0 * 2.0 ** -9]
+    want = [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC000, 0x4000, 0x0000, 0x3F60]
+    got = om.round_bf16(np.asarray(vals))
+    assert [int(x) for x in got] == want, [hex(int(x)) for x in got]
+    n = om.round_bf16(np.asarray([np.nan]))[0]
+    assert (int(n) & 0x7F80) == 0x7F80 and (int(n) & 0x7F) != 0, "NaN must stay NaN"
+
+
+def pin_dequant_blocks_and_layouts(om):
+    rng = np.random.default_rng(1)
+    d_in, d_out = 96, 8
+    codes = rng.integers(0, 0x7E, size=(d_in, d_out), dtype=np.uint8)   # KN, finite, non-negative
+    scales = rng.integers(118, 130, size=(d_out, d_in // 32), dtype=np.uint8)
+    w = ol.as_f64(om.dequant_w0(codes, scales, d_in, d_out, "kn"), "bf16")
+    for n in range(d_out):
+        for k in range(d_in):
+            q = om.decode_e4m3(np.asarray([codes[k, n]], dtype=np.uint8))[0]
+            assert w[k, n] == q * 2.0 ** (int(scales[n, k // 32]) - 127), (k, n)
+    w_nk = ol.as_f64(om.dequant_w0(np.ascontiguousarray(codes.T), scales, d_in, d_out, "nk"), "bf16")
+    assert np.array_equal(w, w_nk), "layouts disagree"
+
+
+def pin_layer_vs_torch(om):
+    import torch
+    rng = np.random.default_rng(2)
+    d_in, d_out, T = 64, 16, 5
+    codes = rng.integers(0, 256, size=(d_in, d_out), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                                   # no NaN codes
+    scales = rng.integers(120, 128, size=(d_out, d_in // 32), dtype=np.uint8)
+    X = rng.standard_normal((T, d_in))
+    tq = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
+    ts = torch.from_numpy(2.0 ** (scales.astype(np.float64) - 127)).T.repeat_interleave(32, dim=0)
+    Yt = (torch.from_numpy(X) @ (tq * ts)).numpy()
+    W = om.dequant_w0(codes, scales, d_in, d_out, "kn")
+    A = [np.zeros((d_in, 1))]
+    B = [np.zeros((1, d_out))]
+    Y, _ = ol.forward(X, ol.as_f64(W, "bf16"), A, B, [1.0], [0, T], "fp32")
+    assert np.allclose(Y, Yt, rtol=0, atol=1e-12 * max(1.0, np.abs(Yt).max())), "decoded layer differs from torch"
+
+
+ALL_PINS = [pin_e4m3_table_vs_torch, pin_e4m3_hand_codes, pin_e8m0, pin_round_bf16,
+            pin_dequant_blocks_and_layouts, pin_layer_vs_torch]

@@ -6,12 +6,13 @@ import types
 
 import pytest
 
-from tests import pins, pins_adamw, pins_multi
+from tests import pins, pins_adamw, pins_multi, pins_mx
 
 ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(ORACLE, "lora.py")
 SRC_ADAMW = os.path.join(ORACLE, "adamw.py")
 SRC_MULTI = os.path.join(ORACLE, "multi.py")
+SRC_MX = os.path.join(ORACLE, "mx.py")
 
 MUTATIONS = {
     "drop_scale_fwd": ("Y[r0:r1] = Xc @ W + s * (Zc @ Bi)", "Y[r0:r1] = Xc @ W + (Zc @ Bi)"),
@@ -78,6 +79,22 @@ MULTI_MUTATIONS = {
 }
 
 
+MX_MUTATIONS = {
+    "exponent_bias_6": ("norm = (8 + m) * np.exp2(e - 10.0)", "norm = (8 + m) * np.exp2(e - 9.0)"),
+    "subnormal_scale": ("sub = m * 2.0 ** -9", "sub = m * 2.0 ** -10"),
+    "subnormal_as_normal": ("v = s * np.where(e == 0, sub, norm)", "v = s * norm"),
+    "nan_code_finite": ("return np.where((c & 0x7F) == 0x7F, np.nan, v)", "return v"),
+    "scale_bias_126": ("np.exp2(x - 127.0)", "np.exp2(x - 126.0)"),
+    "scale_nan_ignored": ("return np.where(x == 255, np.nan, np.exp2(x - 127.0))", "return np.exp2(x - 127.0)"),
+    "no_ties_to_even": ("r = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF", "r = ((u + 0x8000) >> 16) & 0xFFFF"),
+    "truncate_not_round": ("r = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF", "r = (u >> 16) & 0xFFFF"),
+    "block_along_output": ("w = q * np.repeat(sc.T, 32, axis=0)",
+                           "w = q * np.repeat(np.repeat(sc.T[:1], d_in, axis=0)[:, :1], d_out, axis=1)"),
+    "nk_not_transposed": ("    if layout != \"kn\":\n        q = q.T", "    if layout != \"kn\":\n        q = q.reshape(d_in, d_out)"),
+    "sign_dropped": ("s = np.where(c >> 7, -1.0, 1.0)", "s = np.where(c >> 7, 1.0, 1.0)"),
+}
+
+
 def _mutant(old, new, src_path=SRC) -> types.ModuleType:
     with open(src_path) as f:
         src = f.read()
@@ -121,6 +138,19 @@ def test_multi_pins_catch_planted_mistake(name):
     mod = _mutant(old, new, SRC_MULTI)
     caught = []
     for pin in pins_multi.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutation {name}"
+
+
+@pytest.mark.parametrize("name", sorted(MX_MUTATIONS))
+def test_mx_pins_catch_planted_mistake(name):
+    old, new = MX_MUTATIONS[name]
+    mod = _mutant(old, new, SRC_MX)
+    caught = []
+    for pin in pins_mx.ALL_PINS:
         try:
             pin(mod)
         except Exception as e:

@@ -29,3 +29,10 @@ def test_adamw_pin(pin):
 def test_multi_pin(pin):
     from oracle import multi
     pin(multi)
+
+
+@pytest.mark.parametrize("pin", __import__("tests.pins_mx", fromlist=["ALL_PINS"]).ALL_PINS,
+                         ids=lambda f: f.__name__)
+def test_mx_pin(pin):
+    from oracle import mx
+    pin(mx)
