@@ -12,6 +12,7 @@ STATUS = {0: "MLORA_OK", -1: "MLORA_ERR_INVALID_ARG", -2: "MLORA_ERR_UNSUPPORTED
           -3: "MLORA_ERR_HIP", -4: "MLORA_ERR_WORKSPACE", -5: "MLORA_ERR_NOMEM"}
 DTYPES = {"fp32": 0, "bf16": 1}
 W0_LAYOUTS = {"kn": 0, "nk": 1}
+W0_FORMATS = {"bf16": 0, "mxfp8": 1}
 
 TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
           "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count", "tiles", "tile_start", "ext",
@@ -20,7 +21,7 @@ TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chun
 TABLE_COLS = {"nb": 3, "chunks": 3, "tiles": 2, "ext": 4, "opt_blocks": 2, "ksplit": 2}
 TABLE_I64 = {"zoff", "offsets", "seg_start", "chunk_boff"}
 
-KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep", "adamw"]
+KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep", "adamw", "dequant"]
 
 # every symbol include/mlora.h declares
 EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_multi", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
@@ -33,7 +34,7 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("nano_rows", ctypes.c_int32), ("gemm_rows", ctypes.c_int32),
                 ("n_streams", ctypes.c_int32), ("chunk_min", ctypes.c_int32),
                 ("chunk_max", ctypes.c_int32), ("chunk_per_rank", ctypes.c_int32),
-                ("w0_layout", ctypes.c_int32)]
+                ("w0_layout", ctypes.c_int32), ("w0_format", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):

@@ -33,10 +33,10 @@ class Plan:
     def __init__(self, seg_offsets, ranks, d_in: int, d_out: int, dtype: str = "bf16",
                  nano_rows: int = 0, n_streams: int = 0, chunk_min: int = 0, chunk_max: int = 0,
                  chunk_per_rank: int = 0, w0_layout: str = "kn", gemm_rows: int = 0, _ids=None,
-                 _widths=None):
+                 _widths=None, w0_format: str = "bf16"):
         rk = np.ascontiguousarray(np.asarray(ranks, dtype=np.int32))
         opts = _lib.PlanOpts(nano_rows, gemm_rows, n_streams, chunk_min, chunk_max, chunk_per_rank,
-                             _lib.W0_LAYOUTS[w0_layout])
+                             _lib.W0_LAYOUTS[w0_layout], _lib.W0_FORMATS[w0_format])
         h = ctypes.c_void_p()
         widths = [int(d_out)] if _widths is None else [int(v) for v in _widths]
         if _widths is not None:
@@ -76,6 +76,7 @@ class Plan:
         self.info = {k: getattr(inf, k) for k, _ in _lib.PlanInfo._fields_}
         self.dtype = dtype
         self.w0_layout = w0_layout
+        self.w0_format = w0_format
         self.offsets = self.export("offsets") if _ids is not None else off
         self.ranks = rk
         self.widths = widths
@@ -204,7 +205,14 @@ def _npairs(plan):
 
 def _w0_shape(plan):
     i = plan.info
+    if plan.w0_format == "mxfp8":  # element codes, then the block scale codes
+        return (i["d_in"] * i["d_out"] + i["d_out"] * (i["d_in"] // 32),)
     return (i["d_in"], i["d_out"]) if plan.w0_layout == "kn" else (i["d_out"], i["d_in"])
+
+
+def _w0_dtype(plan):
+    torch = _torch()
+    return torch.uint8 if plan.w0_format == "mxfp8" else _dt(plan)
 
 
 def mlora_forward(plan: Plan, X, W0, A_ptrs, B_ptrs, scales, Y, Z, ws, stream=None):
@@ -213,7 +221,7 @@ def mlora_forward(plan: Plan, X, W0, A_ptrs, B_ptrs, scales, Y, Z, ws, stream=No
     i = plan.info
     dt = _dt(plan)
     _check_t(X, "X", (i["T"], i["d_in"]), dt)
-    _check_t(W0, "W0", _w0_shape(plan), dt)
+    _check_t(W0, "W0", _w0_shape(plan), _w0_dtype(plan))
     _check_t(Y, "Y", (i["T"], i["d_out"]), dt)
     _check_t(Z, "Z", None, dt, i["z_elems"])
     for nm, t in (("A_ptrs", A_ptrs), ("B_ptrs", B_ptrs)):
@@ -232,7 +240,7 @@ def mlora_backward(plan: Plan, dY, X, W0, A_ptrs, B_ptrs, scales, Z, dX, dA_ptrs
     dt = _dt(plan)
     _check_t(dY, "dY", (i["T"], i["d_out"]), dt)
     _check_t(X, "X", (i["T"], i["d_in"]), dt)
-    _check_t(W0, "W0", _w0_shape(plan), dt)
+    _check_t(W0, "W0", _w0_shape(plan), _w0_dtype(plan))
     _check_t(Z, "Z", None, dt, i["z_elems"])
     if dX is not None:
         _check_t(dX, "dX", (i["T"], i["d_in"]), dt)

@@ -21,7 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmlora.so")
 
-SOURCES = ["plan.cpp", "api.cpp", "kernels_bf16.hip", "kernels_fp32.hip", "kernels_adamw.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "kernels_bf16.hip", "kernels_fp32.hip", "kernels_adamw.hip",
+           "kernels_mx.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

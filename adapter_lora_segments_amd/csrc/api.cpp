@@ -434,6 +434,17 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     });
   }
 
+  // An MXFP8 base is decoded into the workspace first; the GEMMs read that.
+  const uint16_t* W0b = static_cast<const uint16_t*>(W0);
+  if (P.opts.w0_format == MLORA_W0_MXFP8) {
+    const uint8_t* codes = static_cast<const uint8_t*>(W0);
+    uint16_t* w0deq = reinterpret_cast<uint16_t*>(wsb + L.w0deq);
+    st = timed(p, MLORA_K_DEQUANT, cs, [&] {
+      mlora::launch_dequant_mx(nk, codes, codes + P.d_in * P.d_out, P.d_in, P.d_out, w0deq, cs);
+    });
+    if (st != MLORA_OK) return st;
+    W0b = w0deq;
+  }
   // A_cat^T feeds the shrink; with W0 as [d_out][d_in] the expand steps read
   // B in k-contiguous form, B_cat^T.
   uint16_t* acat_t = reinterpret_cast<uint16_t*>(wsb + L.acat_t);
@@ -460,7 +471,7 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     mlora::GemmArgs ga;
     ga.A = (const uint16_t*)X;
     ga.lda = P.d_in;
-    ga.B = (const uint16_t*)W0;
+    ga.B = W0b;
     ga.ldb = nk ? P.d_in : P.d_out;
     ga.C = (uint16_t*)Y;
     ga.ldc = P.d_out;
@@ -544,6 +555,17 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     });
     if (st != MLORA_OK) return st;
   }
+  // dX reads the base weight; an MXFP8 base is decoded into the workspace.
+  const uint16_t* W0b = static_cast<const uint16_t*>(W0);
+  if (dX && P.opts.w0_format == MLORA_W0_MXFP8) {
+    const uint8_t* codes = static_cast<const uint8_t*>(W0);
+    uint16_t* w0deq = reinterpret_cast<uint16_t*>(wsb + L.w0deq);
+    st = timed(p, MLORA_K_DEQUANT, cs, [&] {
+      mlora::launch_dequant_mx(nk, codes, codes + P.d_in * P.d_out, P.d_in, P.d_out, w0deq, cs);
+    });
+    if (st != MLORA_OK) return st;
+    W0b = w0deq;
+  }
   if (dX) {
     st = ensure_wg_streams(p);
     if (st != MLORA_OK) return st;
@@ -588,7 +610,7 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     mlora::GemmArgs ga;
     ga.A = (const uint16_t*)dY;
     ga.lda = P.d_out;
-    ga.B = (const uint16_t*)W0;
+    ga.B = W0b;
     ga.ldb = nk ? P.d_in : P.d_out;
     ga.C = (uint16_t*)dX;
     ga.ldc = P.d_in;

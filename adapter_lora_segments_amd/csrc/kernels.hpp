@@ -107,6 +107,12 @@ struct GemmArgs {
 // main_b_kcontig: Bop element (k, n) at B[n*ldb + k] (else at B[k*ldb + n]).
 void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s);
 
+// MXFP8 base weight -> bf16, same layout: codes [d_in][d_out] (nk: [d_out]
+// [d_in]) E4M3, scales [d_out][d_in / 32] E8M0; out = element x scale,
+// nearest-even bf16.
+void launch_dequant_mx(bool nk, const uint8_t* codes, const uint8_t* scales, int64_t d_in,
+                       int64_t d_out, uint16_t* out, hipStream_t s);
+
 // ---------------- fp32 path (vector ALU) ----------------
 void launch_f32_shrink(const DevTables& t, int32_t n, int64_t T, int64_t d_in, const float* X,
                        const void* const* A, const float* scales, float* Z, hipStream_t s);

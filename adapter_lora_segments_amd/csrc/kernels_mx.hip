@@ -1,0 +1,107 @@
+// Decode of an MXFP8 frozen base weight into bf16 for gfx950.
+//
+// The PLoRA page (PLoRA: Efficient Concurrent LoRA Training for Large
+// Language Models, §5, §11.3) trains adapters over a frozen base that
+// QLoRA-style methods keep in a low precision: the base is only read.  Here
+// it is held in the OCP microscaling format MXFP8 (E4M3 elements, one E8M0
+// power-of-two scale per 32 consecutive inputs of an output column) and
+// decoded per call into the bf16 weight the GEMMs read: element x scale,
+// rounded to nearest even.  Reads 1 + 1/32 bytes and writes 2 bytes per
+// weight: HBM-bound, 16-byte vector loads and stores.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace mlora {
+
+namespace {
+
+// Value of E4M3 code c times 2^sexp in fp32: the element is exact in fp32
+// (at most four significant bits); the scaling rounds to nearest even only
+// below fp32's normal range.  S.1111.111 is NaN, and so is a NaN scale.
+__device__ __forceinline__ float mx_value(uint32_t c, uint32_t x) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e ? ldexpf((float)(8u + m), (int)e - 10) : ldexpf((float)m, -9);
+  v = ldexpf(v, (int)x - 127);
+  v = (c & 0x80u) ? -v : v;
+  return ((c & 0x7Fu) == 0x7Fu || x == 255u) ? __builtin_nanf("") : v;
+}
+
+// 16 codes (one 16-byte vector) -> 16 bf16 (two 16-byte vectors); scale
+// exponent code per element from `xs`.
+template <class XS>
+__device__ __forceinline__ void decode16(const u32x4 cw, XS xs, u32x4& lo, u32x4& hi) {
+  uint32_t out[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 4 * w + 2 * h;
+      const uint32_t c0 = (cw[w] >> (16 * h)) & 0xFFu, c1 = (cw[w] >> (16 * h + 8)) & 0xFFu;
+      out[2 * w + h] = pack_bf16x2(mx_value(c0, xs(i)), mx_value(c1, xs(i + 1)));
+    }
+  }
+  lo = u32x4{out[0], out[1], out[2], out[3]};
+  hi = u32x4{out[4], out[5], out[6], out[7]};
+}
+
+}  // namespace
+
+// W0 as [d_in][d_out]: a workgroup takes one 32-row scale block kb and 512
+// columns; the 512 scale codes of the block go through LDS, then each thread
+// decodes 16 columns of four rows.
+__global__ __launch_bounds__(256) void k_dequant_mx_kn(const uint8_t* codes, const uint8_t* scales,
+                                                       int64_t d_in, int64_t d_out, uint16_t* out) {
+  __shared__ uint8_t sx[512];
+  const int64_t kb = blockIdx.y, n0 = (int64_t)blockIdx.x * 512;
+  const int64_t nkb = d_in / 32;
+  for (int j = threadIdx.x; j < 512; j += 256)
+    sx[j] = n0 + j < d_out ? scales[(n0 + j) * nkb + kb] : (uint8_t)127;
+  __syncthreads();
+  const int c16 = 16 * (threadIdx.x & 31);
+  const int64_t n = n0 + c16;
+  if (n >= d_out) return;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int64_t k = kb * 32 + (threadIdx.x >> 5) + 8 * it;
+    const u32x4 cw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + k * d_out + n));
+    u32x4 lo, hi;
+    decode16(cw, [&](int i) { return (uint32_t)sx[c16 + i]; }, lo, hi);
+    u32x4* dst = reinterpret_cast<u32x4*>(out + k * d_out + n);
+    dst[0] = lo;
+    dst[1] = hi;
+  }
+}
+
+// W0 as [d_out][d_in]: a thread takes one scale block, 32 consecutive codes
+// of a row.
+__global__ __launch_bounds__(256) void k_dequant_mx_nk(const uint8_t* codes, const uint8_t* scales,
+                                                       int64_t d_in, int64_t d_out, uint16_t* out) {
+  const int64_t nkb = d_in / 32;
+  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (item >= d_out * nkb) return;
+  const uint32_t x = scales[item];
+  const int64_t off = item * 32;  // row n = item / nkb, columns 32 (item % nkb) ..
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 cw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + off + 16 * h));
+    u32x4 lo, hi;
+    decode16(cw, [&](int) { return x; }, lo, hi);
+    u32x4* dst = reinterpret_cast<u32x4*>(out + off + 16 * h);
+    dst[0] = lo;
+    dst[1] = hi;
+  }
+}
+
+void launch_dequant_mx(bool nk, const uint8_t* codes, const uint8_t* scales, int64_t d_in,
+                       int64_t d_out, uint16_t* out, hipStream_t s) {
+  if (nk) {
+    const int64_t items = d_out * (d_in / 32);
+    hipLaunchKernelGGL(k_dequant_mx_nk, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, codes,
+                       scales, d_in, d_out, out);
+  } else {
+    hipLaunchKernelGGL(k_dequant_mx_kn, dim3((unsigned)((d_out + 511) / 512), (unsigned)(d_in / 32)),
+                       dim3(256), 0, s, codes, scales, d_in, d_out, out);
+  }
+}
+
+}  // namespace mlora

@@ -120,6 +120,7 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
     if (opts->chunk_max) o.chunk_max = opts->chunk_max;
     if (opts->chunk_per_rank) o.chunk_per_rank = opts->chunk_per_rank;
     o.w0_layout = opts->w0_layout;
+    o.w0_format = opts->w0_format;
   }
   if (o.nano_rows < 16 || o.nano_rows > 256 || o.nano_rows % 16 != 0) {
     err = "nano_rows must be a multiple of 16 in [16, 256]";
@@ -149,6 +150,14 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
   if (o.w0_layout != MLORA_W0_KN && o.w0_layout != MLORA_W0_NK) {
     err = "w0_layout must be MLORA_W0_KN or MLORA_W0_NK";
     return MLORA_ERR_INVALID_ARG;
+  }
+  if (o.w0_format != MLORA_W0_BF16 && o.w0_format != MLORA_W0_MXFP8) {
+    err = "w0_format must be MLORA_W0_BF16 or MLORA_W0_MXFP8";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (o.w0_format == MLORA_W0_MXFP8 && dtype != MLORA_BF16) {
+    err = "an MXFP8 base weight needs a bf16 plan";
+    return MLORA_ERR_UNSUPPORTED;
   }
 
   PlanTables p;
@@ -400,6 +409,7 @@ DeviceLayout device_layout(const PlanTables& p) {
   }
   L.dz = take((size_t)p.z_elems * esz);
   L.kpart = take((size_t)p.kpart_off.back() * 4);
+  L.w0deq = take(p.opts.w0_format == MLORA_W0_MXFP8 ? (size_t)p.d_in * (size_t)p.d_out * 2 : 0);
   if (p.dtype == MLORA_BF16) {
     L.part_a = take((size_t)p.partial_rows * (size_t)p.d_in * 4);
     L.part_b = take((size_t)p.partial_b_elems * 4);

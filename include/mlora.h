@@ -77,6 +77,7 @@ typedef enum {
 
 typedef enum { MLORA_FP32 = 0, MLORA_BF16 = 1 } mlora_dtype;
 typedef enum { MLORA_W0_KN = 0, MLORA_W0_NK = 1 } mlora_w0_layout;
+typedef enum { MLORA_W0_BF16 = 0, MLORA_W0_MXFP8 = 1 } mlora_w0_format;
 
 #define MLORA_MAX_RANK 256
 #define MLORA_MAX_ADAPTERS 65536
@@ -92,6 +93,7 @@ typedef struct {
   int32_t chunk_max;      /*   max(chunk_min, chunk_per_rank * r_pad(i)));                  */
   int32_t chunk_per_rank; /*   defaults 256, 2048, 8                                        */
   int32_t w0_layout;      /* mlora_w0_layout; default MLORA_W0_KN                          */
+  int32_t w0_format;      /* mlora_w0_format; default MLORA_W0_BF16 (MXFP8: bf16 plans only) */
 } mlora_plan_opts;
 
 typedef struct mlora_plan_s *mlora_plan_t;
@@ -252,6 +254,22 @@ mlora_status mlora_plan_export(mlora_plan_t plan, int32_t table, void *dst, size
 mlora_status mlora_plan_upload(mlora_plan_t plan, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * A frozen base in MXFP8 (w0_format = MLORA_W0_MXFP8; the PLoRA page, §5 and
+ * §11.3, trains adapters over bases that QLoRA-style methods keep in a low
+ * precision, since the base is only read).  W0 then points at one buffer:
+ * d_in * d_out E4M3 element codes (OCP FP8: S.EEEE.MMM, bias 7, S.1111.111
+ * NaN, largest 448) laid out as the bf16 W0 of the same w0_layout would be,
+ * followed at byte offset d_in * d_out by d_out * (d_in / 32) E8M0 scale
+ * codes [d_out][d_in / 32] (2^(X - 127), 255 NaN), one per 32 consecutive
+ * inputs of an output column.  The weight the layer multiplies is element x
+ * scale rounded to bf16 (nearest even; exact unless below bf16's normal
+ * range).  forward, and backward when it computes dX, first decode W0 into
+ * the workspace (2 * d_in * d_out bytes, counted in workspace_bytes) with
+ * one HBM-bound kernel (MLORA_K_DEQUANT), then run the bf16 path.  The
+ * resident base takes 1 + 1/32 bytes per weight instead of 2.
+ */
+
+/*
  * mlora_forward -- Y = X W0 + Z' B per adapter, and Z' = s X A saved.
  * X [T][d_in]; W0 per w0_layout; A, B: device arrays of n device pointers;
  * scales: device array of n floats (any value, 0 and negatives allowed).
@@ -338,6 +356,7 @@ typedef enum {
   MLORA_K_GEMM_DX,       /* dX = dY W0^T + dZ A^T (B4)                       */
   MLORA_K_PREP,          /* rank-padded concatenations of A and B            */
   MLORA_K_ADAMW,         /* per-adapter AdamW step (mlora_adamw_step)        */
+  MLORA_K_DEQUANT,       /* decode of an MXFP8 base weight into bf16         */
   MLORA_K_COUNT
 } mlora_kernel_kind;
 

@@ -228,7 +228,7 @@ def test_adamw_rejects_bad_arguments_without_launching():
     assert "fp32" in L.mlora_last_error().decode()
     assert L.mlora_adamw_step(bf.handle, *ok, d, d, d, 16, None) == -4              # workspace small
     assert L.mlora_adamw_step(bf.handle, *ok, None, None, d, 1 << 30, None) == -4   # not uploaded
-    assert _lib.KERNELS[-1] == "adamw" and len(_lib.KERNELS) == 8
+    assert _lib.KERNELS[7] == "adamw" and _lib.KERNELS[8] == "dequant" and len(_lib.KERNELS) == 9
 
 
 def test_adamw_hparams_layout():
@@ -338,3 +338,37 @@ def test_split_k_rule():
             S = split_k(tiles, nk)
             kper = -(-nk // S)
             assert 1 <= S <= 16 and (S - 1) * kper < nk and (S == 1 or S * tiles <= 256), (tiles, nk, S)
+
+
+def test_mxfp8_plan_options():
+    """An MXFP8 base needs a bf16 plan; its decoded weight is counted in the
+    workspace; the binding expects codes then scales in one uint8 buffer."""
+    from adapter_lora_segments_amd.binding import _w0_shape
+    p_bf = Plan([0, 5, 9], [4, 8], 128, 192)
+    p_mx = Plan([0, 5, 9], [4, 8], 128, 192, w0_format="mxfp8")
+    assert p_mx.info["workspace_bytes"] >= p_bf.info["workspace_bytes"] + 2 * 128 * 192 - 256  # an empty region still takes 256
+    assert _w0_shape(p_mx) == (128 * 192 + 192 * 4,)
+    assert _status(lambda: Plan([0, 5, 9], [4, 8], 128, 192, "fp32", w0_format="mxfp8")) == -2
+    for name in ["rpad", "zoff", "nb", "chunks", "tiles", "ext", "ksplit", "opt_blocks"]:
+        assert np.array_equal(p_mx.export(name), p_bf.export(name)), name
+
+
+def test_mx_quantizer_round_trip():
+    """The input quantizer (workloads/mx.py) against the oracle's decoder:
+    every decoded weight is within half an E4M3 step of the float weight, and
+    no block overflows."""
+    from oracle import mx as omx
+    from workloads.mx import quantize_mx
+    rng = np.random.default_rng(0)
+    w = rng.standard_normal((128, 64)) * 0.02
+    w[5, 3] = 0.0
+    for layout in ("kn", "nk"):
+        codes, scales = quantize_mx(w, layout)
+        assert codes.dtype == np.uint8 and scales.shape == (64, 4)
+        dec = omx.decode_e4m3(codes).reshape(codes.shape)
+        if layout == "nk":
+            dec = dec.T
+        sc = omx.decode_e8m0(scales).T.repeat(32, axis=0)
+        assert np.all(np.isfinite(dec)) and np.all(np.abs(dec) <= 448)
+        err = np.abs(dec * sc - w)
+        assert np.all(err <= sc * 2.0 ** -3 * np.maximum(np.abs(dec), 2.0 ** -6) + 1e-300)

@@ -1,0 +1,103 @@
+"""Frozen base in MXFP8 (w0_format = mxfp8) on the GPU.
+
+- The layer with an MXFP8 base is bit-identical, in Y, dX, dA, dB and Z', to
+  the bf16 layer whose W0 is the oracle's decoding of the same codes
+  (oracle/mx.py): the library's decode kernel makes exactly the oracle's
+  weights, and the rest of the path is the bf16 path.  Both W0 layouts; the
+  codes cover the whole E4M3 range, subnormals and negative zero included.
+- Against the layer oracle on the decoded weight, within the bf16 bar.
+- The bench layer (4096x4096, four adapters) at full size, bitwise against
+  the decoded-weight bf16 layer."""
+import numpy as np
+import pytest
+
+from oracle import lora as ol
+from oracle import mx as omx
+from tests.gpu_harness import TOL, custom_workload, say, to_dev, to_host_f64
+from workloads.mx import pack, quantize_mx
+from workloads.tensors import host_tensors
+
+
+def _run(plan, W0dev, h, dt="bf16"):
+    import torch
+    from adapter_lora_segments_amd import PackedLoRALinear
+    layer = PackedLoRALinear(plan, W0dev, [to_dev(a, dt) for a in h["A"]], [to_dev(b, dt) for b in h["B"]],
+                             h["scales"])
+    X, dY = to_dev(h["X"], dt), to_dev(h["dY"], dt)
+    Y = layer.forward(X)
+    dX = layer.backward(dY, X)
+    torch.cuda.synchronize()
+    return {"Y": to_host_f64(Y), "dX": to_host_f64(dX), "dA": [to_host_f64(t) for t in layer.dA],
+            "dB": [to_host_f64(t) for t in layer.dB], "Z": to_host_f64(layer.Z)}
+
+
+def _codes_full_range(rng, d_in, d_out):
+    """Random codes over all finite E4M3 codes, subnormals and -0 included."""
+    c = rng.integers(0, 256, size=(d_in, d_out), dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x80
+    return c
+
+
+CASES = [("kn", 256, 320, [8, 64, 3], [150, 300, 77]), ("nk", 512, 256, [16, 200], [500, 9])]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("layout,d_in,d_out,ranks,tokens", CASES)
+def test_mx_base_bitwise_and_oracle(layout, d_in, d_out, ranks, tokens):
+    import torch
+    from adapter_lora_segments_amd import Plan
+    say(f"case mxfp8 base {layout} {d_in}x{d_out} ranks {ranks} tokens {tokens}")
+    w = custom_workload("mx", "bf16", d_in, d_out, ranks, tokens, seed=4)
+    h = host_tensors(w, 0)
+    rng = np.random.default_rng(5)
+    codes_kn = _codes_full_range(rng, d_in, d_out)
+    scales = rng.integers(112, 124, size=(d_out, d_in // 32), dtype=np.uint8)
+    codes = codes_kn if layout == "kn" else np.ascontiguousarray(codes_kn.T)
+    Wdec = omx.dequant_w0(codes, scales, d_in, d_out, layout)                  # bf16 bits [d_in][d_out]
+    off = h["offsets"]
+    p_mx = Plan(off, h["ranks"], d_in, d_out, "bf16", w0_layout=layout, w0_format="mxfp8")
+    p_bf = Plan(off, h["ranks"], d_in, d_out, "bf16", w0_layout=layout)
+    buf = torch.from_numpy(pack(codes, scales)).cuda()
+    p_mx.profile_enable(["dequant"])
+    p_mx.profile_read()
+    out_mx = _run(p_mx, buf, h)
+    assert p_mx.profile_read()["dequant"][1] == 2, "one decode in forward, one in the backward's dX"
+    p_mx.profile_enable(False)
+    Wb = Wdec if layout == "kn" else np.ascontiguousarray(Wdec.T)
+    out_bf = _run(p_bf, to_dev(Wb, "bf16"), h)
+    for k in ("Y", "dX", "Z"):
+        assert np.array_equal(out_mx[k], out_bf[k]), f"{k} differs from the decoded-weight bf16 layer"
+    for i in range(len(ranks)):
+        assert np.array_equal(out_mx["dA"][i], out_bf["dA"][i]) and np.array_equal(out_mx["dB"][i], out_bf["dB"][i])
+    Yo, _ = ol.forward(h["X"], Wdec, h["A"], h["B"], h["scales"], off, "bf16")
+    dXo, dAo, dBo, _ = ol.backward(h["dY"], h["X"], Wdec, h["A"], h["B"], h["scales"], off, "bf16")
+    errs = {"Y": ol.max_rel_err(out_mx["Y"], Yo), "dX": ol.max_rel_err(out_mx["dX"], dXo)}
+    for i in range(len(ranks)):
+        errs[f"dA{i}"] = ol.max_rel_err(out_mx["dA"][i], dAo[i])
+        errs[f"dB{i}"] = ol.max_rel_err(out_mx["dB"][i], dBo[i])
+    say(f"  bitwise equal to the decoded-weight layer; oracle worst {max(errs.items(), key=lambda kv: kv[1])}")
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
+@pytest.mark.gpu
+def test_mx_base_bench_layer_full_size():
+    import torch
+    from adapter_lora_segments_amd import Plan
+    from workloads import load_workload
+    w = load_workload("llama7b_proj", 0)
+    p = w.projections[0]
+    say(f"case mxfp8 base full size {p.d_in}x{p.d_out}, ranks {w.ranks}, T={w.T}")
+    h = host_tensors(w, 0)
+    wf = ol.as_f64(h["W0"], "bf16")
+    codes, scales = quantize_mx(wf, "kn")
+    Wdec = omx.dequant_w0(codes, scales, p.d_in, p.d_out, "kn")
+    rel = float(np.max(np.abs(ol.as_f64(Wdec, "bf16") - wf)) / np.max(np.abs(wf)))
+    say(f"  quantization changes W0 by at most {rel:.3e} of its largest entry")
+    p_mx = Plan(h["offsets"], h["ranks"], p.d_in, p.d_out, "bf16", w0_format="mxfp8")
+    p_bf = Plan(h["offsets"], h["ranks"], p.d_in, p.d_out, "bf16")
+    out_mx = _run(p_mx, torch.from_numpy(pack(codes, scales)).cuda(), h)
+    out_bf = _run(p_bf, to_dev(Wdec, "bf16"), h)
+    for k in ("Y", "dX"):
+        assert np.array_equal(out_mx[k], out_bf[k]), k
+    for i in range(w.n):
+        assert np.array_equal(out_mx["dA"][i], out_bf["dA"][i]) and np.array_equal(out_mx["dB"][i], out_bf["dB"][i])
