@@ -54,18 +54,26 @@ __global__ __launch_bounds__(256) void k_dequant_mx_kn(const uint8_t* codes, con
   __shared__ uint8_t sx[512];
   const int64_t kb = blockIdx.y, n0 = (int64_t)blockIdx.x * 512;
   const int64_t nkb = d_in / 32;
+  const int c16 = 16 * (threadIdx.x & 31);
+  const int64_t n = n0 + c16;
+  // The four rows' codes are in flight (at a clamped column past d_out)
+  // while the block's scale codes are staged in LDS.
+  const int64_t nc = min(n, d_out - 16);
+  u32x4 cw[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int64_t k = kb * 32 + (threadIdx.x >> 5) + 8 * it;
+    cw[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + k * d_out + nc));
+  }
   for (int j = threadIdx.x; j < 512; j += 256)
     sx[j] = n0 + j < d_out ? scales[(n0 + j) * nkb + kb] : (uint8_t)127;
   __syncthreads();
-  const int c16 = 16 * (threadIdx.x & 31);
-  const int64_t n = n0 + c16;
   if (n >= d_out) return;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int64_t k = kb * 32 + (threadIdx.x >> 5) + 8 * it;
-    const u32x4 cw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + k * d_out + n));
     u32x4 lo, hi;
-    decode16(cw, [&](int i) { return (uint32_t)sx[c16 + i]; }, lo, hi);
+    decode16(cw[it], [&](int i) { return (uint32_t)sx[c16 + i]; }, lo, hi);
     u32x4* dst = reinterpret_cast<u32x4*>(out + k * d_out + n);
     dst[0] = lo;
     dst[1] = hi;

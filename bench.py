@@ -96,6 +96,13 @@ def kernel_rooflines(w, units, kern, iso, steps):
             out[k] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": ach / PEAK_BF16_TFLOPS, "ms_per_step": ms}
     out["gemm_dx"]["note"] = "timed beside the concurrent weight-gradient kernels"
+    if kern.get("dequant", (0.0, 0))[1]:
+        # MXFP8 base: codes (1 B) and scales (1/32 B) read, bf16 (2 B) written per weight, twice a step
+        byt = sum(2 * (1 + 1 / 32 + 2) * w.projections[q[0]].d_in * w.projections[q[0]].d_out for q in units)
+        ms = kern["dequant"][0] / steps
+        ach = byt / (ms * 1e-3) / 1e9
+        out["dequant"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": ach / PEAK_HBM_GBS, "ms_per_step": ms}
     for k in ("reduce", "prep"):
         out[k] = {"bound": "overhead", "ms_per_step": iso[k][0] / steps}
     return out
@@ -313,6 +320,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="time the whole layer with the projections that share an input fused into one "
                          "packed layer each (q/k/v, gate/up: mlora_plan_multi); implies --all-projections")
+    ap.add_argument("--w0-format", default="bf16", choices=["bf16", "mxfp8"],
+                    help="store the frozen base in MXFP8 (E4M3 codes, E8M0 scales per 32 inputs; decoded "
+                         "per call); implies --no-sequential")
     ap.add_argument("--optimizer-only", action="store_true",
                     help="run one forward+backward for real gradients, then time only the "
                          "per-adapter AdamW step of the first projection; one JSON line")
@@ -332,6 +342,7 @@ def main():
     from adapter_lora_segments_amd import Plan, PackedLoRALinear, device_check
     from workloads import load_workload
     from workloads.multi import LAYER_GROUPS, device_multi
+    from workloads.mx import quantize_mx_device
     from workloads.tensors import device_tensors
 
     torch.cuda.set_device(0)
@@ -352,6 +363,12 @@ def main():
     w = load_workload(a.workload, a.seed)
     if a.fused:
         a.all_projections, a.no_sequential = True, True
+    mx = a.w0_format == "mxfp8"
+    if mx:
+        a.no_sequential = True
+        if a.fused or a.shuffled_ids:
+            print("--w0-format mxfp8 runs with segment plans of single projections", file=sys.stderr)
+            sys.exit(2)
     projs = list(range(len(w.projections))) if a.all_projections else [0]
     SETS = 4
     layers = []
@@ -379,8 +396,12 @@ def main():
                                  n_streams=a.streams or w.n_streams)
         else:
             plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16",
-                        n_streams=a.streams or w.n_streams)
-        layer = PackedLoRALinear(plan, d["W0"], d["A"], d["B"], d["scales"])
+                        n_streams=a.streams or w.n_streams, w0_format=a.w0_format)
+        W0 = d["W0"]
+        if mx:
+            W0 = quantize_mx_device(d["W0"], "kn")
+            d["W0_bytes"] = W0.numel()
+        layer = PackedLoRALinear(plan, W0, d["A"], d["B"], d["scales"])
         Ys = [torch.empty((w.T, p.d_out), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
         dXs = [torch.empty((w.T, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
         layers.append((plan, layer, d, Ys, dXs))
@@ -517,7 +538,8 @@ def main():
                    "projections": [w.projections[q].name for q in projs],
                    "streams": layers[0][0].info["n_groups"],
                    "rows": "shuffled, per-token adapter ids" if a.shuffled_ids else "adapter segments",
-                   "fused": [g for g, _ in groups] if groups else None},
+                   "fused": [g for g, _ in groups] if groups else None,
+                   "w0_format": a.w0_format},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
     }
