@@ -389,6 +389,22 @@ __device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int 
   // Threads past the last block (256*PER > NBLK) duplicate block b - NBLK:
   // same loads, same values to the same LDS slots, and no branch around the
   // loads (which would make the compiler drain every load in flight).
+  // PERM: the wide operand's row is the caller's row of grouped row r0 + tc.
+  // Those row indexes are loaded two steps ahead (two register sets, by step
+  // parity), so a step's data loads never wait on its index loads.
+  int ix[PERM ? 2 : 1][PER][8];
+  auto fetch_idx = [&](int step) {
+    if constexpr (PERM) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int b = tid + 256 * p < NBLK ? tid + 256 * p : tid + 256 * p - NBLK;
+        const int kb = b < 128 ? b / 16 : 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          ix[step & 1][p][i] = ldg_i32(a.t.perm + r0 + min(step * 64 + 8 * kb + i, nr - 1)) - r0;
+      }
+    }
+  };
   auto load = [&](int step, u32x4 (&stage)[PER][8]) {
     const int t0 = step * 64;
 #pragma unroll
@@ -403,13 +419,15 @@ __device__ __forceinline__ void token_reduce_body(const TokenReduceArgs& a, int 
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int tc = min(t0 + 8 * kb + i, nr - 1);
-          // PERM: the wide operand's row is the caller's row of grouped row r0 + tc
-          const int64_t br = PERM ? (int64_t)ldg_i32(a.t.perm + r0 + tc) - r0 : tc;
+          const int64_t br = PERM ? (int64_t)ix[step & 1][p][i] : tc;
           stage[p][i] = isbig ? ld16(bbase + br * big_ld + col) : ld16(rbase + (int64_t)tc * RP + col);
         }
       }
     }
+    fetch_idx(step + 2);
   };
+  fetch_idx(0);
+  fetch_idx(1);
   // Rows past the chunk and columns past the operand are zeroed here, when
   // the stage is consumed, not when it is loaded.
   auto store = [&](int buf, int step, u32x4 (&stage)[PER][8]) {
