@@ -30,13 +30,27 @@ from workloads.tensors import f32_to_bf16_bits
 TOLF = TOL["fp32"]
 
 
-def _layer(dt, ranks, d_in, d_out, seed):
+def _layer(dt, ranks, d_in, d_out, seed, widths=None):
+    """With ``widths`` the layer has projections sharing the input: ``ranks``
+    then lists the (adapter, projection) pairs' ranks adapter-major, and pair
+    v's B has widths[v % P] columns."""
     import torch
     from adapter_lora_segments_amd import Plan, PackedLoRALinear, AdamW
     n = len(ranks)
-    off = np.arange(n + 1, dtype=np.int64) * 3   # rows do not enter the optimizer step
-    plan = Plan(off, ranks, d_in, d_out, dt)
-    A32, B32 = optim.masters(ranks, d_in, d_out, seed)
+    if widths is None:
+        off = np.arange(n + 1, dtype=np.int64) * 3   # rows do not enter the optimizer step
+        plan = Plan(off, ranks, d_in, d_out, dt)
+        A32, B32 = optim.masters(ranks, d_in, d_out, seed)
+    else:
+        P = len(widths)
+        off = np.arange(n // P + 1, dtype=np.int64) * 3
+        plan = Plan.multi(off, np.asarray(ranks).reshape(-1, P), d_in, widths, dt)
+        A32, B32 = [], []
+        for v, r in enumerate(ranks):
+            a, b = optim.masters([r], d_in, widths[v % P], seed * 100 + v)
+            A32 += a
+            B32 += b
+    n = len(ranks)
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     A = [torch.from_numpy(a).cuda().to(tdt) for a in A32]
     B = [torch.from_numpy(b).cuda().to(tdt) for b in B32]
@@ -61,9 +75,9 @@ def _err(got, want):
     return num / den
 
 
-def _run(dt, ranks, d_in, d_out, n_steps, seed, sample=None):
+def _run(dt, ranks, d_in, d_out, n_steps, seed, sample=None, widths=None):
     import torch
-    plan, layer, opt, A32, B32 = _layer(dt, ranks, d_in, d_out, seed)
+    plan, layer, opt, A32, B32 = _layer(dt, ranks, d_in, d_out, seed, widths)
     n = len(ranks)
     hps = optim.hyperparameters(n, seed)
     tensors = lambda i: [(opt.A[i], opt.mA[i], opt.vA[i], layer.A[i]),
@@ -95,7 +109,14 @@ def _run(dt, ranks, d_in, d_out, n_steps, seed, sample=None):
     applied = {i: 0 for i in range(n)}
     worst = ("", 0.0)
     for s in range(n_steps):
-        gA, gB = optim.gradients(ranks, d_in, d_out, seed, s)
+        if widths is None:
+            gA, gB = optim.gradients(ranks, d_in, d_out, seed, s)
+        else:
+            gA, gB = [], []
+            for v, r in enumerate(ranks):
+                a, b = optim.gradients([r], d_in, widths[v % len(widths)], seed * 100 + v, s)
+                gA += a
+                gB += b
         for i in range(n):
             layer.dA[i].copy_(torch.from_numpy(gA[i]).cuda())
             layer.dB[i].copy_(torch.from_numpy(gB[i]).cuda())
@@ -170,3 +191,13 @@ def test_adamw_largest_layer_sampled():
     p = w.projections[0]
     say(f"case adamw mlp70b_pair {p.d_in}x{p.d_out}, {w.n} adapters (sampled)")
     _run("bf16", w.ranks, p.d_in, p.d_out, 2, seed=6, sample=512)
+
+
+@pytest.mark.gpu
+def test_adamw_projection_pairs():
+    """A layer with projections sharing the input: every (adapter, projection)
+    pair is its own optimizer unit, and B of a pair has its projection's width."""
+    widths = [512, 256]
+    ranks = [8, 64, 33, 1, 128, 16]          # three adapters x two projections, adapter-major
+    say(f"case adamw projection pairs widths {widths} ranks {ranks}")
+    _run("bf16", ranks, 256, None, 3, seed=8, widths=widths)

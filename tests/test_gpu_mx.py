@@ -101,3 +101,38 @@ def test_mx_base_bench_layer_full_size():
         assert np.array_equal(out_mx[k], out_bf[k]), k
     for i in range(w.n):
         assert np.array_equal(out_mx["dA"][i], out_bf["dA"][i]) and np.array_equal(out_mx["dB"][i], out_bf["dB"][i])
+
+
+@pytest.mark.gpu
+def test_mx_base_with_projections_sharing_the_input():
+    """An MXFP8 base under mlora_plan_multi: the concatenated weight's codes
+    and scales decode per output column across the projections' columns."""
+    import torch
+    from adapter_lora_segments_amd import Plan, PackedLoRALinear
+    from oracle import multi as om
+    from workloads.multi import host_multi
+    widths = [512, 256, 256]
+    ranks = [[8, 8, 8], [64, 16, 100]]
+    say(f"case mxfp8 base with projections {widths}")
+    h = host_multi(9, 512, widths, ranks, [300, 150], "bf16")
+    codes, scales = quantize_mx(ol.as_f64(h["W0"], "bf16"), "nk")
+    Wdec = omx.dequant_w0(codes, scales, 512, sum(widths), "nk")
+    plan = Plan.multi(h["offsets"], ranks, 512, widths, "bf16", w0_layout="nk", w0_format="mxfp8")
+    flat = lambda x: [v for row in x for v in row]
+    layer = PackedLoRALinear(plan, torch.from_numpy(pack(codes, scales)).cuda(),
+                             [to_dev(a, "bf16") for a in flat(h["A"])], [to_dev(b, "bf16") for b in flat(h["B"])],
+                             flat(h["scales"]))
+    X, dY = to_dev(h["X"], "bf16"), to_dev(h["dY"], "bf16")
+    Y = layer.forward(X)
+    dX = layer.backward(dY, X)
+    torch.cuda.synchronize()
+    Yo, _ = om.forward_multi(h["X"], Wdec, h["A"], h["B"], h["scales"], h["offsets"], widths, "bf16")
+    dXo, dAo, dBo, _ = om.backward_multi(h["dY"], h["X"], Wdec, h["A"], h["B"], h["scales"], h["offsets"],
+                                         widths, "bf16")
+    errs = {"Y": ol.max_rel_err(to_host_f64(Y), Yo), "dX": ol.max_rel_err(to_host_f64(dX), dXo)}
+    for i in range(2):
+        for q in range(3):
+            errs[f"dA{i},{q}"] = ol.max_rel_err(to_host_f64(layer.dA[3 * i + q]), dAo[i][q])
+            errs[f"dB{i},{q}"] = ol.max_rel_err(to_host_f64(layer.dB[3 * i + q]), dBo[i][q])
+    say(f"  worst {max(errs.items(), key=lambda kv: kv[1])}")
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
