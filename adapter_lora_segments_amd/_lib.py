@@ -24,7 +24,7 @@ TABLE_I64 = {"zoff", "offsets", "seg_start", "chunk_boff"}
 KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep", "adamw", "dequant"]
 
 # every symbol include/mlora.h declares
-EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_multi", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
+EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_multi", "mlora_plan_multi_from_ids", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
            "mlora_plan_upload", "mlora_forward", "mlora_backward", "mlora_adamw_step", "mlora_profile_enable",
            "mlora_profile_read", "mlora_device_check", "mlora_status_string", "mlora_last_error",
            "mlora_version"]
@@ -86,6 +86,10 @@ def lib() -> ctypes.CDLL:
     L.mlora_plan_multi.argtypes = [i32, ctypes.POINTER(i64), i32, ctypes.POINTER(i64), ctypes.POINTER(i32),
                                    i64, i32, ctypes.POINTER(PlanOpts), ctypes.POINTER(vp)]
     L.mlora_plan_multi.restype = i32
+    L.mlora_plan_multi_from_ids.argtypes = [i32, i64, ctypes.POINTER(i32), i32, ctypes.POINTER(i64),
+                                            ctypes.POINTER(i32), i64, i32, ctypes.POINTER(PlanOpts),
+                                            ctypes.POINTER(vp)]
+    L.mlora_plan_multi_from_ids.restype = i32
     L.mlora_plan_destroy.argtypes = [vp]
     L.mlora_plan_destroy.restype = None
     L.mlora_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]

@@ -45,14 +45,22 @@ class Plan:
                 raise ValueError("ranks must be [n][n_proj] for a multi-projection plan")
             n = int(rk.shape[0])
             rk = np.ascontiguousarray(rk.reshape(-1))
-            off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
-            if off.shape != (n + 1,):
-                raise ValueError("seg_offsets must have n + 1 entries")
             w = np.ascontiguousarray(np.asarray(widths, dtype=np.int64))
-            check(lib().mlora_plan_multi(n, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), P,
-                                         w.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                         rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in),
-                                         _lib.DTYPES[dtype], ctypes.byref(opts), ctypes.byref(h)))
+            if _ids is not None:
+                ids = np.ascontiguousarray(np.asarray(_ids, dtype=np.int32).reshape(-1))
+                check(lib().mlora_plan_multi_from_ids(
+                    n, int(ids.shape[0]), ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), P,
+                    w.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                    rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in), _lib.DTYPES[dtype],
+                    ctypes.byref(opts), ctypes.byref(h)))
+            else:
+                off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
+                if off.shape != (n + 1,):
+                    raise ValueError("seg_offsets must have n + 1 entries")
+                check(lib().mlora_plan_multi(n, off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), P,
+                                             w.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                             rk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), int(d_in),
+                                             _lib.DTYPES[dtype], ctypes.byref(opts), ctypes.byref(h)))
         elif _ids is None:
             n = int(rk.shape[0])
             off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
@@ -77,7 +85,7 @@ class Plan:
         self.dtype = dtype
         self.w0_layout = w0_layout
         self.w0_format = w0_format
-        self.offsets = self.export("offsets") if _ids is not None else off
+        self.offsets = self.export("offsets") if _ids is not None else np.asarray(seg_offsets, dtype=np.int64)
         self.ranks = rk
         self.widths = widths
         self.n_proj = len(widths)
@@ -95,6 +103,12 @@ class Plan:
         """mlora_plan_multi: projections of output widths ``widths`` sharing
         the input; ranks [n][n_proj]."""
         return cls(seg_offsets, ranks, d_in, int(sum(widths)), dtype, _widths=widths, **opts)
+
+    @classmethod
+    def multi_from_ids(cls, token_adapter, ranks, d_in: int, widths, dtype: str = "bf16", **opts):
+        """mlora_plan_multi_from_ids: projections sharing the input, rows in
+        the caller's order with one adapter id per token."""
+        return cls(None, ranks, d_in, int(sum(widths)), dtype, _widths=widths, _ids=token_adapter, **opts)
 
     @property
     def handle(self):

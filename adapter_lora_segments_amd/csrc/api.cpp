@@ -300,6 +300,22 @@ mlora_status mlora_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t n_p
   }
 }
 
+mlora_status mlora_plan_multi_from_ids(int32_t n, int64_t T, const int32_t* token_adapter, int32_t n_proj,
+                                       const int64_t* widths, const int32_t* ranks, int64_t d_in,
+                                       mlora_dtype dtype, const mlora_plan_opts* opts, mlora_plan_t* out) {
+  if (!out) return fail(MLORA_ERR_INVALID_ARG, "out is NULL");
+  try {
+    mlora::PlanTables P;
+    std::string err;
+    mlora_status st = mlora::build_plan_multi_from_ids(n, T, token_adapter, n_proj, widths, ranks, d_in,
+                                                       (int32_t)dtype, opts, P, err);
+    if (st != MLORA_OK) return fail(st, err);
+    return finish_plan(std::move(P), out);
+  } catch (const std::bad_alloc&) {
+    return fail(MLORA_ERR_NOMEM, "host allocation failed while building the plan");
+  }
+}
+
 void mlora_plan_destroy(mlora_plan_t p) {
   if (!p) return;
   // Teardown is best effort: errors here have no caller to report to.

@@ -331,9 +331,10 @@ mlora_status build_plan(int32_t n, const int64_t* seg_offsets, const int32_t* ra
   return build_plan_multi(n, seg_offsets, 1, &d_out, ranks, d_in, dtype, opts, P, err);
 }
 
-mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adapter,
-                                 const int32_t* ranks, int64_t d_in, int64_t d_out, int32_t dtype,
-                                 const mlora_plan_opts* opts, PlanTables& P, std::string& err) {
+mlora_status build_plan_multi_from_ids(int32_t n, int64_t T, const int32_t* token_adapter, int32_t nproj,
+                                       const int64_t* widths, const int32_t* ranks, int64_t d_in,
+                                       int32_t dtype, const mlora_plan_opts* opts, PlanTables& P,
+                                       std::string& err) {
   if (n < 1 || n > MLORA_MAX_ADAPTERS) {
     err = "n must be in [1, " + std::to_string(MLORA_MAX_ADAPTERS) + "], got " + std::to_string(n);
     return MLORA_ERR_INVALID_ARG;
@@ -364,10 +365,16 @@ mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adap
   std::vector<int32_t> perm((size_t)T);
   std::vector<int64_t> next(off.begin(), off.end() - 1);
   for (int64_t t = 0; t < T; ++t) perm[(size_t)next[token_adapter[t]]++] = (int32_t)t;
-  mlora_status st = build_plan(n, off.data(), ranks, d_in, d_out, dtype, opts, P, err);
+  mlora_status st = build_plan_multi(n, off.data(), nproj, widths, ranks, d_in, dtype, opts, P, err);
   if (st != MLORA_OK) return st;
   P.perm = std::move(perm);
   return MLORA_OK;
+}
+
+mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adapter,
+                                 const int32_t* ranks, int64_t d_in, int64_t d_out, int32_t dtype,
+                                 const mlora_plan_opts* opts, PlanTables& P, std::string& err) {
+  return build_plan_multi_from_ids(n, T, token_adapter, 1, &d_out, ranks, d_in, dtype, opts, P, err);
 }
 
 DeviceLayout device_layout(const PlanTables& p) {

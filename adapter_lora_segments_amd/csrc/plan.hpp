@@ -75,6 +75,12 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
                               const int32_t* ranks, int64_t d_in, int32_t dtype, const mlora_plan_opts* opts,
                               PlanTables& out, std::string& err);
 
+// Rows in the caller's order with per-token adapter ids, several projections.
+mlora_status build_plan_multi_from_ids(int32_t n, int64_t T, const int32_t* token_adapter, int32_t nproj,
+                                       const int64_t* widths, const int32_t* ranks, int64_t d_in,
+                                       int32_t dtype, const mlora_plan_opts* opts, PlanTables& out,
+                                       std::string& err);
+
 // The same for rows in the caller's order with per-token adapter ids: a
 // stable counting sort by id gives the segments and the permutation.
 mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adapter,

@@ -178,6 +178,18 @@ mlora_status mlora_plan_multi(int32_t n, const int64_t *seg_offsets, int32_t n_p
                               const int64_t *widths, const int32_t *ranks, int64_t d_in,
                               mlora_dtype dtype, const mlora_plan_opts *opts, mlora_plan_t *out);
 
+/*
+ * mlora_plan_multi_from_ids -- mlora_plan_multi for rows in the caller's
+ * order: token t belongs to adapter token_adapter[t] (as mlora_plan_from_ids;
+ * the stable counting sort gives the segments and MLORA_TAB_PERM), and every
+ * adapter has a rank per projection (ranks[i * n_proj + q]).  Errors as
+ * mlora_plan_multi plus MLORA_ERR_INVALID_ARG for an id out of range.
+ */
+mlora_status mlora_plan_multi_from_ids(int32_t n, int64_t T, const int32_t *token_adapter,
+                                       int32_t n_proj, const int64_t *widths, const int32_t *ranks,
+                                       int64_t d_in, mlora_dtype dtype, const mlora_plan_opts *opts,
+                                       mlora_plan_t *out);
+
 void mlora_plan_destroy(mlora_plan_t plan);
 
 typedef struct {

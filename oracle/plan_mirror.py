@@ -229,7 +229,7 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None, dims=N
     }
 
 
-def build_plan_from_ids(token_adapter, ranks, opts: PlanOpts | None = None) -> dict:
+def build_plan_from_ids(token_adapter, ranks, opts: PlanOpts | None = None, widths=None, dims=None) -> dict:
     """The plan for rows in the caller's order with per-token adapter ids:
     rows grouped by adapter with a stable counting sort (counts, exclusive
     prefix sums, then every row placed at its adapter's next free position,
@@ -248,7 +248,7 @@ def build_plan_from_ids(token_adapter, ranks, opts: PlanOpts | None = None) -> d
     for t, a in enumerate(ids):
         perm[nxt[a]] = t
         nxt[a] += 1
-    plan = build_plan(off, ranks, opts)
+    plan = build_plan(off, ranks, opts, widths=widths, dims=dims)
     plan["perm"] = np.asarray(perm, dtype=np.int32)
     plan["offsets"] = np.asarray(off, dtype=np.int64)
     return plan

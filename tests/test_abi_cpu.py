@@ -372,3 +372,32 @@ def test_mx_quantizer_round_trip():
         assert np.all(np.isfinite(dec)) and np.all(np.abs(dec) <= 448)
         err = np.abs(dec * sc - w)
         assert np.all(err <= sc * 2.0 ** -3 * np.maximum(np.abs(dec), 2.0 ** -6) + 1e-300)
+
+
+@st.composite
+def multi_ids_cases(draw):
+    n = draw(st.integers(1, 10))
+    P = draw(st.integers(1, 3))
+    T = draw(st.integers(0, 1200))
+    ids = draw(st.lists(st.integers(0, n - 1), min_size=T, max_size=T))
+    ranks = [draw(st.lists(st.sampled_from([1, 8, 33, 64, 128, 256]), min_size=P, max_size=P)) for _ in range(n)]
+    widths = [256 * draw(st.integers(1, 4)) for _ in range(P)]
+    S = draw(st.integers(1, 4))
+    return ids, ranks, widths, PlanOpts(nano_rows=32, gemm_rows=256, n_streams=S)
+
+
+@settings(max_examples=100, deadline=None)
+@given(multi_ids_cases())
+def test_plan_multi_from_ids_bit_exact_against_mirror(case):
+    """mlora_plan_multi_from_ids: the permutation and every table equal the
+    mirror's counting sort followed by its multi-projection rule."""
+    from oracle.plan_mirror import build_plan_from_ids
+    ids, ranks, widths, opts = case
+    d_in = 320
+    p = Plan.multi_from_ids(ids, ranks, d_in, widths, "bf16", n_streams=opts.n_streams)
+    m = build_plan_from_ids(ids, ranks, opts, widths=widths, dims=(d_in, sum(widths), "bf16"))
+    assert np.array_equal(p.export("perm"), m["perm"]) and np.array_equal(p.export("offsets"), m["offsets"])
+    for name in TABLES_ALL + ["ksplit"]:
+        got, want = p.export(name), m[name]
+        assert (got.size == 0 and want.size == 0) or np.array_equal(got, want.reshape(got.shape)), name
+    assert _status(lambda: Plan.multi_from_ids([0, 3], [[4, 4], [8, 8]], 128, [256, 256])) == -1  # id 3 >= n

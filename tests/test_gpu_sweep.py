@@ -3,9 +3,9 @@
 Each case draws (from its own seed) a dtype, a W0 layout, a stream count,
 1-8 adapters with ranks 1-256 and token counts 0-700 (empty and ragged
 segments), dimensions that are multiples of 64 (from 64 to 1536, so that
-some GEMM launches split K and some do not), and one of four plan kinds:
+some GEMM launches split K and some do not), and one of five plan kinds:
 segments, per-token ids in a shuffled order, several projections sharing
-the input, or an MXFP8 base.  Every output is compared with the oracle at
+the input (with segments or with shuffled ids), or an MXFP8 base.  Every output is compared with the oracle at
 the dtype's bar: Y, dX, every dA_i and dB_i, and the saved activation Z'
 (padding columns exactly zero)."""
 import numpy as np
@@ -19,13 +19,13 @@ from workloads.multi import host_multi
 from workloads.mx import pack, quantize_mx
 from workloads.tensors import host_tensors
 
-N_CASES = 64
+N_CASES = 80
 
 
 def draw_case(seed):
     g = np.random.default_rng(1000 + seed)
-    kind = ["segments", "ids", "multi", "mxfp8"][seed % 4]
-    dt = "fp32" if (kind in ("segments", "ids", "multi") and g.random() < 0.3) else "bf16"
+    kind = ["segments", "ids", "multi", "mxfp8", "multi_ids"][seed % 5]
+    dt = "fp32" if (kind != "mxfp8" and g.random() < 0.3) else "bf16"
     n = int(g.integers(1, 9))
     ranks = [int(g.choice([1, 4, 8, 16, 31, 33, 64, 100, 128, 200, 256])) for _ in range(n)]
     tokens = [int(g.choice([0, 1, 17, int(g.integers(1, 700))])) for _ in range(n)]
@@ -36,7 +36,7 @@ def draw_case(seed):
     layout = "nk" if g.random() < 0.4 else "kn"
     streams = int(g.integers(1, 5))
     widths = None
-    if kind == "multi":
+    if kind in ("multi", "multi_ids"):
         unit = 256 if dt == "bf16" else 64
         widths = [unit * int(g.integers(1, 4)) for _ in range(int(g.integers(2, 4)))]
     return dict(kind=kind, dt=dt, ranks=ranks, tokens=tokens, d_in=d_in, d_out=d_out, layout=layout,
@@ -69,23 +69,37 @@ def test_sweep(seed):
     dt, layout, kind = c["dt"], c["layout"], c["kind"]
     errs = {}
     zs_check = []
-    if kind == "multi":
+    if kind in ("multi", "multi_ids"):
         widths = c["widths"]
         P = len(widths)
         rk = [[c["ranks"][i]] * P if i % 2 == 0 else [max(1, c["ranks"][i] // (q + 1)) for q in range(P)]
               for i in range(len(c["ranks"]))]
         h = host_multi(seed, c["d_in"], widths, rk, c["tokens"], dt)
-        plan = Plan.multi(h["offsets"], rk, c["d_in"], widths, dt, n_streams=c["streams"], w0_layout=layout)
+        Xh, dYh, order = h["X"], h["dY"], None
+        if kind == "multi_ids":
+            T = Xh.shape[0]
+            order = np.random.default_rng(seed).permutation(T)
+            ids = np.repeat(np.arange(len(rk)), np.diff(h["offsets"]))[order]
+            Xh, dYh = np.ascontiguousarray(Xh[order]), np.ascontiguousarray(dYh[order])
+            plan = Plan.multi_from_ids(ids, rk, c["d_in"], widths, dt, n_streams=c["streams"], w0_layout=layout)
+        else:
+            plan = Plan.multi(h["offsets"], rk, c["d_in"], widths, dt, n_streams=c["streams"], w0_layout=layout)
         W0h = h["W0"] if layout == "kn" else np.ascontiguousarray(h["W0"].T)
         flat = lambda x: [v for row in x for v in row]
         layer = _layer(plan, to_dev(W0h, dt), flat(h["A"]), flat(h["B"]), flat(h["scales"]), dt)
-        X, dY = to_dev(h["X"], dt), to_dev(h["dY"], dt)
+        X, dY = to_dev(Xh, dt), to_dev(dYh, dt)
         Y = layer.forward(X)
         dX = layer.backward(dY, X)
         torch.cuda.synchronize()
-        Yo, Zo = om.forward_multi(h["X"], h["W0"], h["A"], h["B"], h["scales"], h["offsets"], widths, dt)
-        dXo, dAo, dBo, _ = om.backward_multi(h["dY"], h["X"], h["W0"], h["A"], h["B"], h["scales"],
-                                             h["offsets"], widths, dt)
+        # The oracle on the plan's grouped rows (grouped row g is the caller's
+        # row perm[g]); its Y and dX go back to the caller's rows.
+        perm = plan.export("perm") if order is not None else np.arange(Xh.shape[0])
+        Xg, dYg = np.ascontiguousarray(Xh[perm]), np.ascontiguousarray(dYh[perm])
+        Yg, Zo = om.forward_multi(Xg, h["W0"], h["A"], h["B"], h["scales"], h["offsets"], widths, dt)
+        dXg, dAo, dBo, _ = om.backward_multi(dYg, Xg, h["W0"], h["A"], h["B"], h["scales"], h["offsets"],
+                                             widths, dt)
+        Yo, dXo = np.empty_like(Yg), np.empty_like(dXg)
+        Yo[perm], dXo[perm] = Yg, dXg
         errs["Y"], errs["dX"] = ol.max_rel_err(to_host_f64(Y), Yo), ol.max_rel_err(to_host_f64(dX), dXo)
         zs = _z_pairs(plan, layer, h["offsets"], P, len(rk))
         for i in range(len(rk)):
