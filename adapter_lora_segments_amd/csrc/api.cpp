@@ -200,6 +200,21 @@ mlora_status join_groups(mlora_plan_s* p, hipStream_t cs) {
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
+// A graph capture ended in a fault of the runtime when a plan with several
+// stream groups (forks and joins of internal streams, each event recorded in
+// both the forward and the backward) had been captured; such plans are
+// refused on a capturing stream.  One group captures and replays exactly.
+mlora_status check_capture(const mlora_plan_s* p, hipStream_t cs) {
+  if (p->P.n_groups <= 1) return MLORA_OK;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(cs, &cap);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(MLORA_ERR_UNSUPPORTED,
+                "plans with several stream groups are not supported under graph capture; use n_streams = 1");
+  return MLORA_OK;
+}
+
 mlora_status check_ws(const mlora_plan_s* p, void* ws, size_t ws_bytes) {
   if (!ws) return fail(MLORA_ERR_INVALID_ARG, "workspace is NULL");
   if (ws_bytes < p->L.workspace_bytes)
@@ -434,6 +449,8 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
   const auto& P = p->P;
   const auto& L = p->L;
   hipStream_t cs = static_cast<hipStream_t>(stream);
+  st = check_capture(p, cs);
+  if (st != MLORA_OK) return st;
   mlora::DevTables t = dev_tables(p, ws);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   const bool nk = P.opts.w0_layout == MLORA_W0_NK;
@@ -529,6 +546,8 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
   const auto& P = p->P;
   const auto& L = p->L;
   hipStream_t cs = static_cast<hipStream_t>(stream);
+  st = check_capture(p, cs);
+  if (st != MLORA_OK) return st;
   mlora::DevTables t = dev_tables(p, ws);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   const bool nk = P.opts.w0_layout == MLORA_W0_NK;

@@ -51,6 +51,12 @@
  * caller's stream before the call returns, so the caller sees ordinary
  * single-stream ordering.
  *
+ * Graph capture.  forward, backward and mlora_adamw_step enqueue only
+ * kernels and stream-ordering events (no allocation, no memset), so a plan
+ * with one stream group can be captured into a HIP graph and replayed.  A
+ * plan with several stream groups returns MLORA_ERR_UNSUPPORTED on a
+ * capturing stream (ending such a capture faulted in the runtime).
+ *
  * Errors.  Every call validates its arguments on the host before launching
  * anything; on failure it returns a negative status, launches nothing and
  * writes no output.  mlora_last_error() gives a thread-local message.  No call

@@ -1,0 +1,75 @@
+"""Forward and backward captured in a HIP graph (torch.cuda.graph) and replayed.
+
+The library enqueues only kernels and stream-ordering events (no memsets,
+no allocations), so a caller can capture a whole step, internal streams
+included.  Each case runs one eager step first (the plan creates its
+internal streams then), captures forward+backward, and replays the graph
+three times with new inputs copied in eagerly between replays; every replay
+must equal, bit for bit, an eager step on the same inputs.  One case has one
+stream group (its backward still forks the weight-gradient stream and joins
+it inside the graph), one splits K.  Plans with several stream groups are
+refused under capture (see the skipped case)."""
+import numpy as np
+import pytest
+
+from tests.gpu_harness import custom_workload, say, to_dev
+from workloads.tensors import host_tensors
+
+CASES = [
+    ("one stream", 256, 320, [8, 64, 3], [150, 300, 77], 1),
+    pytest.param("three groups", 320, 256, [16, 200, 4, 33], [500, 9, 260, 100], 3,
+                 marks=pytest.mark.skip(reason="ending the capture of a plan with several stream groups "
+                                               "crashed in the runtime (torch.cuda.graph capture_end); the "
+                                               "library now refuses such plans on a capturing stream")),
+    ("split K", 1024, 1024, [16, 64], [200, 160], 1),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,d_in,d_out,ranks,tokens,streams", CASES)
+def test_graph_replay_matches_eager(name, d_in, d_out, ranks, tokens, streams):
+    import torch
+    from adapter_lora_segments_amd import Plan, PackedLoRALinear
+    say(f"case graph {name}: {d_in}x{d_out} ranks {ranks} tokens {tokens} streams {streams}")
+    w = custom_workload(name, "bf16", d_in, d_out, ranks, tokens, seed=13, n_streams=streams)
+    h = host_tensors(w, 0)
+    plan = Plan(h["offsets"], h["ranks"], d_in, d_out, "bf16", n_streams=streams)
+    layer = PackedLoRALinear(plan, to_dev(h["W0"], "bf16"), [to_dev(a, "bf16") for a in h["A"]],
+                             [to_dev(b, "bf16") for b in h["B"]], h["scales"])
+    T = h["X"].shape[0]
+    X = to_dev(h["X"], "bf16")
+    dY = to_dev(h["dY"], "bf16")
+    Y = torch.empty((T, d_out), dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty((T, d_in), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        layer.forward(X, Y)
+        layer.backward(dY, X, dX)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                     # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for rep in range(3):
+        Xn = torch.randn((T, d_in), generator=gen, device="cuda").to(torch.bfloat16)
+        dYn = torch.randn((T, d_out), generator=gen, device="cuda").to(torch.bfloat16)
+        X.copy_(Xn)
+        dY.copy_(dYn)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [Y.clone(), dX.clone()] + [t.clone() for t in layer.dA] + [t.clone() for t in layer.dB]
+        step()                                     # eager on the same inputs
+        torch.cuda.synchronize()
+        want = [Y, dX] + list(layer.dA) + list(layer.dB)
+        for k, (a, b) in enumerate(zip(got, want)):
+            assert torch.equal(a, b), f"replay {rep}: output {k} differs from the eager step"
+    say(f"  3 replays bit-identical to eager steps")
