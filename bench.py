@@ -323,6 +323,8 @@ def main():
     ap.add_argument("--w0-format", default="bf16", choices=["bf16", "mxfp8"],
                     help="store the frozen base in MXFP8 (E4M3 codes, E8M0 scales per 32 inputs; decoded "
                          "per call); implies --no-sequential")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the same steps replayed from a captured HIP graph (one-group plans)")
     ap.add_argument("--optimizer-only", action="store_true",
                     help="run one forward+backward for real gradients, then time only the "
                          "per-adapter AdamW step of the first projection; one JSON line")
@@ -502,6 +504,33 @@ def main():
                                                                 layers[0][4][i % SETS])),
                                min(a.steps, 50), min(a.warmup, 10))
 
+    # The same steps replayed from a HIP graph: one capture of a full
+    # rotation of the input sets, replayed K / SETS times (plans with one
+    # stream group; the library refuses capture of several).
+    graph_ms = None
+    if not a.no_graph and all(pl.info["n_groups"] == 1 for pl, *_ in layers):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(SETS):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(SETS):
+                step(i)
+        reps = max(1, a.steps // SETS)
+        for _ in range(max(1, a.warmup // SETS)):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) / (reps * SETS) * 1e3
+        del graph
+
     opt_out = None
     if prof and not a.no_optimizer:
         opt_out = optimizer_step(w, layers[0][0], layers[0][1], a.steps, a.warmup, a.seed)
@@ -565,6 +594,9 @@ def main():
             "projection": w.projections[projs[0]].name, "packed_ms_per_step": packed_ms,
             "sequential_ms_per_step": seq_ms, "speedup": seq_ms / packed_ms,
             "sequential": f"{len(seq)} one-adapter library calls, each over its own rows"}
+    if graph_ms is not None:
+        out["graph_replay"] = {"ms_per_step": graph_ms, "tokens_per_s": w.T / (graph_ms * 1e-3),
+                               "note": "the same steps replayed from one captured HIP graph"}
     if opt_out is not None:
         out["optimizer"] = opt_out
     if not a.no_cpu_baseline:
