@@ -31,6 +31,12 @@ gradient g and state (m, v) becomes:
 An adapter whose step number is 0 or less is not updated: its parameters and
 state are returned unchanged.  Inputs are upcast to float64 and nothing is
 rounded in between.
+
+Optional per-adapter gradient clipping (max_grad_norm > 0): before the update,
+every gradient of the adapter is multiplied by min(1, max_grad_norm /
+(||g|| + 1e-6)), ||g|| the 2-norm over all of the adapter's trained tensors
+together -- the rule of torch.nn.utils.clip_grad_norm_, applied to each
+adapter (each job) on its own.
 """
 from __future__ import annotations
 
@@ -57,20 +63,32 @@ def adamw_tensor(p, g, m, v, lr, beta1, beta2, eps, weight_decay, step):
     return p, m, v
 
 
+def clip_coef(grads, max_grad_norm):
+    """The factor one adapter's gradients are multiplied by (1 when clipping
+    is off, max_grad_norm <= 0)."""
+    mx = float(max_grad_norm)
+    if mx <= 0.0:
+        return 1.0
+    norm = np.sqrt(sum(float(np.sum(np.asarray(g, dtype=np.float64) ** 2)) for g in grads))
+    return min(1.0, mx / (norm + 1e-6))
+
+
 def adamw_step(params, grads, m, v, hparams):
     """One AdamW step of every adapter.
 
     params, grads, m, v: per adapter, a list of the adapter's trained tensors
     (for the LoRA layer: [A_i, B_i]).  hparams: per adapter, a mapping with
-    lr, beta1, beta2, eps, weight_decay and step.  Returns new lists
+    lr, beta1, beta2, eps, weight_decay, step and optionally max_grad_norm
+    (clipping over the adapter's tensors together).  Returns new lists
     (params, m, v) of float64 arrays, nested as the inputs.
     """
     out_p, out_m, out_v = [], [], []
     for i, h in enumerate(hparams):
         pi, mi, vi = [], [], []
+        c_i = clip_coef(grads[i], h.get("max_grad_norm", 0.0)) if int(h["step"]) > 0 else 1.0
         for p, g, mm, vv in zip(params[i], grads[i], m[i], v[i]):
-            a, b, c = adamw_tensor(p, g, mm, vv, h["lr"], h["beta1"], h["beta2"], h["eps"],
-                                   h["weight_decay"], h["step"])
+            a, b, c = adamw_tensor(p, np.asarray(g, dtype=np.float64) * c_i, mm, vv, h["lr"], h["beta1"],
+                                   h["beta2"], h["eps"], h["weight_decay"], h["step"])
             pi.append(a)
             mi.append(b)
             vi.append(c)

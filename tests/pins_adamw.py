@@ -12,7 +12,10 @@ it) and raises AssertionError when it disagrees with:
   v_t = (1-b2) sum_k b2^(t-k) g_k^2;
 - a zero gradient from zero state: only the decoupled decay acts;
 - betas of zero: the moments are the current g and g^2 and need no correction;
-- step numbers of 0 or less leave everything unchanged.
+- step numbers of 0 or less leave everything unchanged;
+- per-adapter clipping against torch.nn.utils.clip_grad_norm_ followed by
+  torch.optim.AdamW (one adapter clipped, one under its limit, one off), and
+  the closed form of a clipped first step.
 """
 from __future__ import annotations
 
@@ -151,5 +154,47 @@ def pin_elements_match_whole(oa):
         assert np.array_equal(a, b.reshape(-1)[idx]), f"sampled {name} differs from the whole update"
 
 
-ALL_PINS = [pin_torch_adamw, pin_first_step_closed_form, pin_constant_gradient, pin_unrolled_moments,
+def pin_clipping_vs_torch(oa):
+    import torch
+    hps = [dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_grad_norm=0.05),
+           dict(lr=2e-4, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.0, max_grad_norm=1e3),
+           dict(lr=5e-4, beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=0.1, max_grad_norm=0.0)]
+    shapes = [[(8, 4), (4, 16)], [(8, 2), (2, 16)], [(8, 8), (8, 16)]]
+    rng = np.random.default_rng(21)
+    params = [[rng.standard_normal(sh) * 0.05 for sh in s] for s in shapes]
+    m = [[np.zeros(sh) for sh in s] for s in shapes]
+    v = [[np.zeros(sh) for sh in s] for s in shapes]
+    tps = [[torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in pi] for pi in params]
+    opts = [torch.optim.AdamW(tp, lr=h["lr"], betas=(h["beta1"], h["beta2"]), eps=h["eps"],
+                              weight_decay=h["weight_decay"], foreach=False) for tp, h in zip(tps, hps)]
+    for t in range(1, 4):
+        grads = [[rng.standard_normal(sh) * 0.1 for sh in s] for s in shapes]
+        for i, h in enumerate(hps):
+            for tp, g in zip(tps[i], grads[i]):
+                tp.grad = torch.tensor(g, dtype=torch.float64)
+            if h["max_grad_norm"] > 0:
+                torch.nn.utils.clip_grad_norm_(tps[i], h["max_grad_norm"])
+            opts[i].step()
+        params, m, v = oa.adamw_step(params, grads, m, v, [dict(h, step=t) for h in hps])
+        for i in range(3):
+            for k in range(2):
+                _close(params[i][k], tps[i][k].detach().numpy(), 1e-12, f"clipped step {t} adapter {i} tensor {k}")
+
+
+def pin_clipped_first_step_moments(oa):
+    rng = np.random.default_rng(22)
+    g = [rng.standard_normal((6, 3)), rng.standard_normal((3, 5))]
+    norm = np.sqrt(sum(np.sum(x ** 2) for x in g))
+    mx = 0.25 * norm
+    z = [np.zeros_like(x) for x in g]
+    _, m1, v1 = oa.adamw_step([[np.ones_like(x) for x in g]], [g], [z], [z],
+                              [dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1,
+                                    max_grad_norm=mx)])
+    c = mx / (norm + 1e-6)
+    for k in range(2):
+        _close(m1[0][k], 0.1 * c * g[k], 1e-12, "clipped first moment")
+        _close(v1[0][k], 0.001 * (c * g[k]) ** 2, 1e-10, "clipped second moment")
+
+
+ALL_PINS = [pin_clipping_vs_torch, pin_clipped_first_step_moments, pin_torch_adamw, pin_first_step_closed_form, pin_constant_gradient, pin_unrolled_moments,
             pin_zero_grad_pure_decay, pin_zero_betas, pin_skip, pin_elements_match_whole]

@@ -56,6 +56,9 @@ ADAMW_MUTATIONS = {
     "step_zero_updates": ("if t <= 0:", "if t < 0:"),
     "sign_of_step": ("p = p - lr * m_hat", "p = p + lr * m_hat"),
     "wrong_adapter_hparams": ('h["lr"], h["beta1"]', 'hparams[0]["lr"], h["beta1"]'),
+    "clip_norm_not_square_root": ("norm = np.sqrt(sum(", "norm = (sum("),
+    "clip_per_tensor": ("c_i = clip_coef(grads[i], h.get(\"max_grad_norm\", 0.0))", "c_i = clip_coef(grads[i][:1], h.get(\"max_grad_norm\", 0.0))"),
+    "clip_can_amplify": ("return min(1.0, mx / (norm + 1e-6))", "return mx / (norm + 1e-6)"),
 }
 
 
