@@ -17,11 +17,12 @@ W0_FORMATS = {"bf16": 0, "mxfp8": 1}
 TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
           "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count", "tiles", "tile_start", "ext",
           "tile_ext_start", "offsets", "ranks", "perm", "opt_blocks", "proj_cols", "seg_start",
-          "chunk_boff", "ksplit"]
+          "chunk_boff", "ksplit", "opt_first"]
 TABLE_COLS = {"nb": 3, "chunks": 3, "tiles": 2, "ext": 4, "opt_blocks": 2, "ksplit": 2}
 TABLE_I64 = {"zoff", "offsets", "seg_start", "chunk_boff"}
 
-KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep", "adamw", "dequant"]
+KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep", "adamw", "dequant",
+           "grad_norm"]
 
 # every symbol include/mlora.h declares
 EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_multi", "mlora_plan_multi_from_ids", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
@@ -50,7 +51,8 @@ class PlanInfo(ctypes.Structure):
 
 class AdamwHparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
-                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32)]
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32),
+                ("max_grad_norm", ctypes.c_float)]
 
 
 class MloraError(RuntimeError):
@@ -102,7 +104,7 @@ def lib() -> ctypes.CDLL:
     L.mlora_forward.restype = i32
     L.mlora_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.mlora_backward.restype = i32
-    L.mlora_adamw_step.argtypes = [vp] + [vp] * 11 + [vp, sz, vp]
+    L.mlora_adamw_step.argtypes = [vp] + [vp] * 11 + [i32, vp, sz, vp]
     L.mlora_adamw_step.restype = i32
     L.mlora_profile_enable.argtypes = [vp, i32]
     L.mlora_profile_enable.restype = i32

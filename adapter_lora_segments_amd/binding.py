@@ -269,18 +269,18 @@ def mlora_backward(plan: Plan, dY, X, W0, A_ptrs, B_ptrs, scales, Z, dX, dA_ptrs
 
 def adamw_hparams(hparams: Sequence[dict], device="cuda"):
     """Device array of mlora_adamw_hparams from per-adapter mappings with
-    lr, beta1, beta2, eps, weight_decay and step."""
+    lr, beta1, beta2, eps, weight_decay, step and optionally max_grad_norm."""
     torch = _torch()
     arr = (_lib.AdamwHparams * len(hparams))()
     for k, h in enumerate(hparams):
         arr[k] = _lib.AdamwHparams(h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"],
-                                   int(h["step"]))
+                                   int(h["step"]), float(h.get("max_grad_norm", 0.0)))
     raw = np.frombuffer(bytes(arr), dtype=np.uint8).copy()
     return torch.from_numpy(raw).to(device)
 
 
 def mlora_adamw_step(plan: Plan, hparams, A_ptrs, B_ptrs, dA_ptrs, dB_ptrs, mA_ptrs, vA_ptrs,
-                     mB_ptrs, vB_ptrs, A_copy_ptrs, B_copy_ptrs, ws, stream=None):
+                     mB_ptrs, vB_ptrs, A_copy_ptrs, B_copy_ptrs, ws, stream=None, clip_grads=False):
     """One AdamW step of every adapter (fp32 masters and moments through the
     pointer tables; optional bf16 copies)."""
     torch = _torch()
@@ -294,8 +294,8 @@ def mlora_adamw_step(plan: Plan, hparams, A_ptrs, B_ptrs, dA_ptrs, dB_ptrs, mA_p
             _check_t(t, nm, (n,), torch.int64)
     check(lib().mlora_adamw_step(plan.handle, _p(hparams), _p(A_ptrs), _p(B_ptrs), _p(dA_ptrs),
                                  _p(dB_ptrs), _p(mA_ptrs), _p(vA_ptrs), _p(mB_ptrs), _p(vB_ptrs),
-                                 _p(A_copy_ptrs), _p(B_copy_ptrs), _p(ws), ws.numel(),
-                                 _stream(stream)))
+                                 _p(A_copy_ptrs), _p(B_copy_ptrs), 1 if clip_grads else 0, _p(ws),
+                                 ws.numel(), _stream(stream)))
 
 
 def device_check() -> None:
@@ -375,12 +375,14 @@ class AdamW:
         self.mB_ptrs, self.vB_ptrs = tab(self.mB), tab(self.vB)
         self.copies = (layer.A_ptrs, layer.B_ptrs) if bf16 else (None, None)
 
-    def step(self, hparams, stream=None):
+    def step(self, hparams, stream=None, clip_grads=False):
         """hparams: per adapter a mapping (lr, beta1, beta2, eps,
-        weight_decay, step), or a device array from ``adamw_hparams``."""
+        weight_decay, step, optionally max_grad_norm), or a device array
+        from ``adamw_hparams``; clip_grads applies each adapter's
+        max_grad_norm."""
         hp = hparams if hasattr(hparams, "data_ptr") else adamw_hparams(hparams, self.layer.ws.device)
         L = self.layer
         mlora_adamw_step(L.plan, hp, self.A_ptrs, self.B_ptrs, L.dA_ptrs, L.dB_ptrs, self.mA_ptrs,
                          self.vA_ptrs, self.mB_ptrs, self.vB_ptrs, self.copies[0], self.copies[1],
-                         L.ws, stream)
+                         L.ws, stream, clip_grads)
         return hp

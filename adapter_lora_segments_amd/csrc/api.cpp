@@ -91,6 +91,7 @@ mlora::DevTables dev_tables(const mlora_plan_s* p, void* ws) {
   t.zero = reinterpret_cast<const uint16_t*>(b + L.zero);
   t.perm = p->P.perm.empty() ? nullptr : reinterpret_cast<const int32_t*>(b + L.perm);
   t.oblk = reinterpret_cast<const int32_t*>(b + L.oblk);
+  t.oblk_first = reinterpret_cast<const int32_t*>(b + L.oblk_first);
   t.seg0 = reinterpret_cast<const int64_t*>(b + L.seg0);
   t.pcol = reinterpret_cast<const int32_t*>(b + L.pcol);
   t.cboff = reinterpret_cast<const int64_t*>(b + L.cboff);
@@ -405,6 +406,7 @@ mlora_status mlora_plan_export(mlora_plan_t p, int32_t table, void* dst, size_t*
     case MLORA_TAB_SEG_START: v64(P.seg0); break;
     case MLORA_TAB_CHUNK_BOFF: v64(P.cboff); break;
     case MLORA_TAB_KSPLIT: v32(P.ksplit); break;
+    case MLORA_TAB_OPT_FIRST: v32(P.oblk_first); break;
     default: return fail(MLORA_ERR_INVALID_ARG, "unknown table id " + std::to_string(table));
   }
   if (!dst) {
@@ -679,8 +681,8 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
 mlora_status mlora_adamw_step(mlora_plan_t p, const mlora_adamw_hparams* hparams, void* const* A,
                               void* const* B, const void* const* dA, const void* const* dB,
                               void* const* mA, void* const* vA, void* const* mB, void* const* vB,
-                              void* const* A_copy, void* const* B_copy, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              void* const* A_copy, void* const* B_copy, int32_t clip_grads,
+                              void* ws, size_t ws_bytes, void* stream) {
   if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
   for (const void* q : {(const void*)hparams, (const void*)A, (const void*)B, (const void*)dA,
                         (const void*)dB, (const void*)mA, (const void*)vA, (const void*)mB,
@@ -696,6 +698,8 @@ mlora_status mlora_adamw_step(mlora_plan_t p, const mlora_adamw_hparams* hparams
     return fail(MLORA_ERR_INVALID_ARG, "adamw: A_copy and B_copy must be 16-byte aligned");
   if (!p->P.oblk_ok)
     return fail(MLORA_ERR_UNSUPPORTED, "adamw: the layer has more than 2^27 optimizer work items");
+  if (clip_grads != 0 && clip_grads != 1)
+    return fail(MLORA_ERR_INVALID_ARG, "adamw: clip_grads must be 0 or 1");
   mlora_status st = check_ws(p, ws, ws_bytes);
   if (st != MLORA_OK) return st;
   hipStream_t cs = static_cast<hipStream_t>(stream);
@@ -714,6 +718,12 @@ mlora_status mlora_adamw_step(mlora_plan_t p, const mlora_adamw_hparams* hparams
   a.vB = reinterpret_cast<float* const*>(vB);
   a.A_copy = reinterpret_cast<uint16_t* const*>(A_copy);
   a.B_copy = reinterpret_cast<uint16_t* const*>(B_copy);
+  a.gsq = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p->L.gnorm);
+  a.coef = clip_grads ? a.gsq + p->P.n_oblk() : nullptr;
+  if (clip_grads) {
+    st = timed(p, MLORA_K_GRAD_NORM, cs, [&] { mlora::launch_grad_norm(a, p->P.n_oblk(), p->P.nv(), cs); });
+    if (st != MLORA_OK) return st;
+  }
   return timed(p, MLORA_K_ADAMW, cs, [&] { mlora::launch_adamw(a, p->P.n_oblk(), cs); });
 }
 

@@ -27,6 +27,7 @@ struct DevTables {
   const uint16_t* zero;     // 256 zero bytes
   const int32_t* perm;      // [T] grouped row -> caller row, or NULL (rows already grouped)
   const int32_t* oblk;      // [n_oblk][2] optimizer work items (tensor, piece)
+  const int32_t* oblk_first;  // [nv+1] first optimizer work item of each pair
   // Several projections sharing the input: "adapter" j in the tables above
   // is the pair (j / nproj, j % nproj); projection q owns output columns
   // [pcol[q], pcol[q+1]).
@@ -150,7 +151,14 @@ struct AdamwArgs {
   float* const* vB;
   uint16_t* const* A_copy;
   uint16_t* const* B_copy;
+  float* gsq;        // [n_blocks] partial square sums of the gradients (clipping)
+  float* coef;       // [nv] clip factor per pair, or NULL (no clipping)
 };
+// The update; with a.coef set, each pair's gradients are scaled by its clip
+// factor first.
 void launch_adamw(const AdamwArgs& a, int64_t n_blocks, hipStream_t s);
+// Clip factors into a.coef: per work item the gradients' square sum (into
+// a.gsq), then per pair the sum of its items in order (two launches).
+void launch_grad_norm(const AdamwArgs& a, int64_t n_blocks, int32_t nv, hipStream_t s);
 
 }  // namespace mlora

@@ -30,6 +30,67 @@ __device__ __forceinline__ void st_stream(float* q, const f32x4& x) {
 
 }  // namespace
 
+// Square sum of work item blockIdx.x's gradient elements, 0 for an adapter
+// that is not stepped or does not clip.  Fixed order: each thread sums its
+// elements in sequence, then a tree over the workgroup.
+__global__ __launch_bounds__(kThreads) void k_grad_sq(AdamwArgs a) {
+  __shared__ float red[kThreads];
+  const int tsr = ldc(a.t.oblk + 2 * blockIdx.x);
+  const int piece = ldc(a.t.oblk + 2 * blockIdx.x + 1);
+  const int i = tsr >> 1;
+  const bool isB = tsr & 1;
+  const mlora_adamw_hparams* hp = a.hp + i;
+  float acc = 0.f;
+  if (ldc(&hp->step) > 0 && ldc(&hp->max_grad_norm) > 0.f) {
+    const int pq = i % a.t.nproj;
+    const int64_t width = (int64_t)ldc(a.t.pcol + pq + 1) - ldc(a.t.pcol + pq);
+    const int64_t numel = (int64_t)ldc(a.t.ranks + i) * (isB ? width : a.d_in);
+    const int64_t base = (int64_t)piece * kOptBlockElems + 4 * threadIdx.x;
+    const float* g = ldc((isB ? a.dB : a.dA) + i);
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const int64_t e = base + (int64_t)u * 4 * kThreads;
+      if (e < numel) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(g + e);
+        acc = fmaf(x[0], x[0], acc);
+        acc = fmaf(x[1], x[1], acc);
+        acc = fmaf(x[2], x[2], acc);
+        acc = fmaf(x[3], x[3], acc);
+      }
+    }
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.gsq[blockIdx.x] = red[0];
+}
+
+// Clip factor of each pair: the square sums of its work items added in item
+// order (thread-strided, then a tree), min(1, max_grad_norm / (norm + 1e-6)),
+// or 1 without clipping.
+__global__ __launch_bounds__(kThreads) void k_clip_coef(AdamwArgs a, int32_t nv) {
+  __shared__ float red[kThreads];
+  for (int32_t v = blockIdx.x; v < nv; v += gridDim.x) {
+    const int b0 = ldc(a.t.oblk_first + v), b1 = ldc(a.t.oblk_first + v + 1);
+    float acc = 0.f;
+    for (int b = b0 + (int)threadIdx.x; b < b1; b += kThreads) acc += a.gsq[b];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int h = kThreads / 2; h > 0; h >>= 1) {
+      if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+      const float mx = ldc(&a.hp[v].max_grad_norm);
+      a.coef[v] = mx > 0.f ? fminf(1.0f, mx / (sqrtf(red[0]) + 1e-6f)) : 1.0f;
+    }
+    __syncthreads();
+  }
+}
+
 template <bool COPY>
 __global__ __launch_bounds__(kThreads) void k_adamw(AdamwArgs a) {
   const int tsr = ldc(a.t.oblk + 2 * blockIdx.x);
@@ -41,6 +102,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwArgs a) {
   if (step <= 0) return;  // whole workgroup: the adapter is not stepped
   const float lr = ldc(&hp->lr), beta1 = ldc(&hp->beta1), beta2 = ldc(&hp->beta2);
   const float eps = ldc(&hp->eps), wd = ldc(&hp->weight_decay);
+  const float clip = a.coef ? a.coef[i] : 1.0f;   // per-adapter gradient clip factor
 
   const int pq = i % a.t.nproj;   // B_i spans its projection's width
   const int64_t width = (int64_t)ldc(a.t.pcol + pq + 1) - ldc(a.t.pcol + pq);
@@ -79,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwArgs a) {
     f32x4 pn, mn, vn;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float gc = G[u][c];
+      const float gc = G[u][c] * clip;
       const float mc = fmaf(beta1, M[u][c], omb1 * gc);
       const float vc = fmaf(beta2, V[u][c], omb2 * (gc * gc));
       const float den = sqrtf(vc) * inv_sqrt_bc2 + eps;
@@ -96,6 +158,12 @@ __global__ __launch_bounds__(kThreads) void k_adamw(AdamwArgs a) {
                                   reinterpret_cast<u32x2*>(w + e));
     }
   }
+}
+
+void launch_grad_norm(const AdamwArgs& a, int64_t n_blocks, int32_t nv, hipStream_t s) {
+  if (n_blocks > 0) hipLaunchKernelGGL(k_grad_sq, dim3((unsigned)n_blocks), dim3(kThreads), 0, s, a);
+  if (nv > 0)
+    hipLaunchKernelGGL(k_clip_coef, dim3((unsigned)(nv < 65535 ? nv : 65535)), dim3(kThreads), 0, s, a, nv);
 }
 
 void launch_adamw(const AdamwArgs& a, int64_t n_blocks, hipStream_t s) {

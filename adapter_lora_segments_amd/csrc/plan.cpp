@@ -311,7 +311,9 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
   p.oblk_ok = nob <= kMaxOptBlocks;
   if (p.oblk_ok) {
     p.oblk.reserve((size_t)(2 * nob));
+    p.oblk_first.reserve((size_t)nv + 1);
     for (int32_t v = 0; v < nv; ++v) {
+      p.oblk_first.push_back((int32_t)p.n_oblk());
       const int64_t numel[2] = {d_in * ranks[v], ranks[v] * width_of(v)};
       for (int w = 0; w < 2; ++w)
         for (int64_t q = 0; q * kOptBlock < numel[w]; ++q) {
@@ -319,6 +321,7 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
           p.oblk.push_back((int32_t)q);
         }
     }
+    p.oblk_first.push_back((int32_t)p.n_oblk());
   }
 
   P_out = std::move(p);
@@ -401,6 +404,7 @@ DeviceLayout device_layout(const PlanTables& p) {
   L.ext = take(4 * p.ext.size());
   L.perm = take(4 * p.perm.size());
   L.oblk = take(4 * p.oblk.size());
+  L.oblk_first = take(4 * p.oblk_first.size());
   L.seg0 = take(8 * p.seg0.size());
   L.pcol = take(4 * p.pcol.size());
   L.cboff = take(8 * p.cboff.size());
@@ -417,6 +421,9 @@ DeviceLayout device_layout(const PlanTables& p) {
   L.dz = take((size_t)p.z_elems * esz);
   L.kpart = take((size_t)p.kpart_off.back() * 4);
   L.w0deq = take(p.opts.w0_format == MLORA_W0_MXFP8 ? (size_t)p.d_in * (size_t)p.d_out * 2 : 0);
+  // gradient clipping: one partial square sum per optimizer work item, then
+  // one clip factor per pair
+  L.gnorm = take(4 * ((size_t)p.n_oblk() + (size_t)p.nv()));
   if (p.dtype == MLORA_BF16) {
     L.part_a = take((size_t)p.partial_rows * (size_t)p.d_in * 4);
     L.part_b = take((size_t)p.partial_b_elems * 4);
@@ -447,6 +454,7 @@ std::vector<uint8_t> table_blob(const PlanTables& p, const DeviceLayout& L) {
   put(L.ext, p.ext.data(), 4 * p.ext.size());
   put(L.perm, p.perm.data(), 4 * p.perm.size());
   put(L.oblk, p.oblk.data(), 4 * p.oblk.size());
+  put(L.oblk_first, p.oblk_first.data(), 4 * p.oblk_first.size());
   put(L.seg0, p.seg0.data(), 8 * p.seg0.size());
   put(L.pcol, p.pcol.data(), 4 * p.pcol.size());
   put(L.cboff, p.cboff.data(), 8 * p.cboff.size());

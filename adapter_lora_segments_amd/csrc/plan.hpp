@@ -56,6 +56,7 @@ struct PlanTables {
   std::vector<int32_t> perm;  // [T] grouped row -> caller row (plans from ids; empty otherwise)
   std::vector<int32_t> oblk;  // [n_oblk][2] optimizer work items (tensor 2i: A_i, 2i+1: B_i; piece)
   bool oblk_ok = true;        // false: the layer is too large for the optimizer table
+  std::vector<int32_t> oblk_first;  // [nv+1] first optimizer work item of each pair
 
   int64_t n_nano() const { return (int64_t)nano.size() / 3; }
   int64_t n_chunks() const { return (int64_t)chunks.size() / 3; }
@@ -91,10 +92,10 @@ mlora_status build_plan_from_ids(int32_t n, int64_t T, const int32_t* token_adap
 struct DeviceLayout {
   // offsets (bytes) of each table inside the table blob
   size_t offsets, zoff, ranks, rpad, roff, ch_first, ch_count, nano, chunks, cpref, tiles,
-      ext_start, ext, zero, perm, oblk, seg0, pcol, cboff;
+      ext_start, ext, zero, perm, oblk, oblk_first, seg0, pcol, cboff;
   size_t table_bytes;
   // offsets (bytes) of the work buffers inside the workspace
-  size_t acat_t, acat, bcat_t, dz, kpart, w0deq, part_a, part_b;
+  size_t acat_t, acat, bcat_t, dz, kpart, w0deq, gnorm, part_a, part_b;
   size_t workspace_bytes;
 };
 

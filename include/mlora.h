@@ -228,7 +228,8 @@ mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);
  *   d_out), SEG_START[n*n_proj] (int64: first row of each pair's adapter),
  *   CHUNK_BOFF[n_chunks] (int64: element offset of each chunk's dB partial
  *   sums, rows of the chunk's projection width), KSPLIT[S'][2] (K-split of
- *   each group's forward and dX GEMM, rule 9 of mlora_plan).
+ *   each group's forward and dX GEMM, rule 9 of mlora_plan), OPT_FIRST[n+1]
+ *   (first OPT_BLOCKS entry of each adapter).
  * With mlora_plan_multi, "adapter" above means the (adapter, projection)
  * pair v = i * n_proj + q: RANKS, RPAD, ZOFF, ROFF and the per-adapter chunk
  * tables have n * n_proj entries; OFFSETS and GROUPS are over adapters. */
@@ -256,6 +257,7 @@ typedef enum {
   MLORA_TAB_SEG_START,
   MLORA_TAB_CHUNK_BOFF,
   MLORA_TAB_KSPLIT,
+  MLORA_TAB_OPT_FIRST,
   MLORA_TAB_COUNT
 } mlora_table;
 
@@ -326,6 +328,7 @@ mlora_status mlora_backward(mlora_plan_t plan, const void *dY, const void *X, co
 typedef struct {
   float lr, beta1, beta2, eps, weight_decay;
   int32_t step;
+  float max_grad_norm; /* > 0: clip the adapter's gradients to this 2-norm (used when clip_grads = 1) */
 } mlora_adamw_hparams;
 
 /*
@@ -339,6 +342,13 @@ typedef struct {
  *   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2
  *   p <- p - (lr / (1 - b1^step)) m / (sqrt(v / (1 - b2^step)) + eps)
  * in fp32.
+ *
+ * Clipping (clip_grads = 1): an adapter with max_grad_norm > 0 first has all
+ * its gradients multiplied by min(1, max_grad_norm / (||g|| + 1e-6)), ||g||
+ * the 2-norm over its dA and dB together (the rule of PyTorch's
+ * clip_grad_norm_, per adapter: every packed job clips on its own).  The
+ * norms are fp32 sums in a fixed order (bitwise repeatable); two extra
+ * launches.  clip_grads = 0 ignores max_grad_norm.
  *
  * hparams: device array of n mlora_adamw_hparams.  A, B: device arrays of n
  * device pointers to the fp32 master weights ([d_in][r_i] and [r_i][d_out]),
@@ -357,8 +367,8 @@ mlora_status mlora_adamw_step(mlora_plan_t plan, const mlora_adamw_hparams *hpar
                               void *const *A, void *const *B, const void *const *dA,
                               const void *const *dB, void *const *mA, void *const *vA,
                               void *const *mB, void *const *vB, void *const *A_copy,
-                              void *const *B_copy, void *workspace, size_t ws_bytes,
-                              void *stream);
+                              void *const *B_copy, int32_t clip_grads, void *workspace,
+                              size_t ws_bytes, void *stream);
 
 /* Per-kernel timing.  Launches of the selected kinds are bracketed by HIP
  * events on the stream they run on; mlora_profile_read waits for them, adds
@@ -375,6 +385,7 @@ typedef enum {
   MLORA_K_PREP,          /* rank-padded concatenations of A and B            */
   MLORA_K_ADAMW,         /* per-adapter AdamW step (mlora_adamw_step)        */
   MLORA_K_DEQUANT,       /* decode of an MXFP8 base weight into bf16         */
+  MLORA_K_GRAD_NORM,     /* per-adapter gradient norms and clip factors      */
   MLORA_K_COUNT
 } mlora_kernel_kind;
 

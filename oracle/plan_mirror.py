@@ -268,3 +268,12 @@ def optimizer_blocks(ranks, d_in, d_out, widths=None) -> np.ndarray:
             for piece in range(-(-numel // OPT_BLOCK)):
                 out.append((t, piece))
     return np.asarray(out, dtype=np.int32).reshape(-1, 2)
+
+
+def optimizer_first(ranks, d_in, d_out, widths=None) -> np.ndarray:
+    """Rule 8's index of pair v's first work item (nv + 1 entries, the last
+    the item count): the items of a pair are contiguous, A's then B's."""
+    blocks = optimizer_blocks(ranks, d_in, d_out, widths)
+    nv = len(ranks) if widths is None else len(ranks) * len(widths)
+    pair = blocks[:, 0] // 2
+    return np.searchsorted(pair, np.arange(nv + 1), side="left").astype(np.int32)

@@ -13,7 +13,7 @@ from hypothesis import given, settings, strategies as st
 from adapter_lora_segments_amd import _lib
 from adapter_lora_segments_amd.binding import Plan
 from adapter_lora_segments_amd._lib import MloraError
-from oracle.plan_mirror import build_plan, optimizer_blocks, PlanOpts
+from oracle.plan_mirror import build_plan, optimizer_blocks, optimizer_first, PlanOpts
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -51,6 +51,7 @@ def _mirror_vs_library(off, ranks, d_in, d_out, dtype, opts):
     assert np.array_equal(p.export("offsets"), np.asarray(off, dtype=np.int64))
     ob = optimizer_blocks(ranks, d_in, d_out)
     assert np.array_equal(p.export("opt_blocks"), ob) and p.info["n_opt_blocks"] == ob.shape[0]
+    assert np.array_equal(p.export("opt_first"), optimizer_first(ranks, d_in, d_out))
     # one projection: pairs are the adapters, dB partials of d_out columns per rank row
     assert np.array_equal(p.export("seg_start"), np.asarray(off[:-1], dtype=np.int64))
     assert np.array_equal(p.export("chunk_boff"), m["chunk_rpref"].astype(np.int64) * d_out)
@@ -216,28 +217,31 @@ def test_adamw_rejects_bad_arguments_without_launching():
     ok = [d] * 9                      # hparams, A, B, dA, dB, mA, vA, mB, vB
     bf = Plan([0, 5, 9], [4, 8], 128, 64)
     f32 = Plan([0, 5, 9], [4, 8], 128, 64, "fp32")
-    assert L.mlora_adamw_step(None, *ok, None, None, d, 1 << 30, None) == -1
+    assert L.mlora_adamw_step(None, *ok, None, None, 0, d, 1 << 30, None) == -1
     for k in range(9):                # each required array NULL, then misaligned
         args = list(ok)
         args[k] = None
-        assert L.mlora_adamw_step(bf.handle, *args, None, None, d, 1 << 30, None) == -1, k
+        assert L.mlora_adamw_step(bf.handle, *args, None, None, 0, d, 1 << 30, None) == -1, k
         args[k] = vp(4100)
-        assert L.mlora_adamw_step(bf.handle, *args, None, None, d, 1 << 30, None) == -1, k
-    assert L.mlora_adamw_step(bf.handle, *ok, d, None, d, 1 << 30, None) == -1      # one copy only
-    assert L.mlora_adamw_step(f32.handle, *ok, d, d, d, 1 << 30, None) == -1        # fp32 takes none
+        assert L.mlora_adamw_step(bf.handle, *args, None, None, 0, d, 1 << 30, None) == -1, k
+    assert L.mlora_adamw_step(bf.handle, *ok, d, None, 0, d, 1 << 30, None) == -1      # one copy only
+    assert L.mlora_adamw_step(f32.handle, *ok, d, d, 0, d, 1 << 30, None) == -1        # fp32 takes none
     assert "fp32" in L.mlora_last_error().decode()
-    assert L.mlora_adamw_step(bf.handle, *ok, d, d, d, 16, None) == -4              # workspace small
-    assert L.mlora_adamw_step(bf.handle, *ok, None, None, d, 1 << 30, None) == -4   # not uploaded
-    assert _lib.KERNELS[7] == "adamw" and _lib.KERNELS[8] == "dequant" and len(_lib.KERNELS) == 9
+    assert L.mlora_adamw_step(bf.handle, *ok, d, d, 0, d, 16, None) == -4              # workspace small
+    assert L.mlora_adamw_step(bf.handle, *ok, None, None, 0, d, 1 << 30, None) == -4   # not uploaded
+    assert L.mlora_adamw_step(bf.handle, *ok, d, d, 2, d, 1 << 30, None) == -1      # clip_grads not 0/1
+    assert _lib.KERNELS[7:] == ["adamw", "dequant", "grad_norm"] and len(_lib.KERNELS) == 10
 
 
 def test_adamw_hparams_layout():
-    """The ctypes mirror of mlora_adamw_hparams: five floats then the step."""
-    assert ctypes.sizeof(_lib.AdamwHparams) == 24
-    h = _lib.AdamwHparams(1e-4, 0.9, 0.999, 1e-8, 0.01, 3)
+    """The ctypes mirror of mlora_adamw_hparams: five floats, the step, then
+    max_grad_norm."""
+    assert ctypes.sizeof(_lib.AdamwHparams) == 28
+    h = _lib.AdamwHparams(1e-4, 0.9, 0.999, 1e-8, 0.01, 3, 0.5)
     raw = np.frombuffer(bytes(h), dtype=np.uint8)
     assert np.array_equal(raw[:20].view(np.float32), np.float32([1e-4, 0.9, 0.999, 1e-8, 0.01]))
-    assert raw[20:].view(np.int32)[0] == 3
+    assert raw[20:24].view(np.int32)[0] == 3
+    assert raw[24:].view(np.float32)[0] == np.float32(0.5)
 
 
 TABLES_ALL = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
@@ -282,6 +286,7 @@ def test_plan_multi_bit_exact_against_mirror(case):
     assert np.array_equal(p.export("offsets"), np.asarray(off, dtype=np.int64))
     ob = optimizer_blocks(ranks, d_in, None, widths=widths)
     assert np.array_equal(p.export("opt_blocks"), ob)
+    assert np.array_equal(p.export("opt_first"), optimizer_first(ranks, d_in, None, widths=widths))
     i = p.info
     assert i["n_proj"] == len(widths) and i["d_out"] == sum(widths) and i["n"] == len(ranks)
     assert i["z_elems"] == m["z_elems"] and i["partial_rows"] == m["partial_rows"]

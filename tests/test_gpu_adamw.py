@@ -13,7 +13,12 @@ several steps.  Checked per adapter and tensor, at every step:
   of the update);
 - adapters whose step number is <= 0 are untouched, bit for bit;
 - the bf16 copies equal the GPU's own fp32 masters rounded to nearest even,
-  bit for bit (the rounding decision is taken on the same fp32 value).
+  bit for bit (the rounding decision is taken on the same fp32 value);
+- with clipping on, every adapter's gradients are scaled by the oracle's clip
+  factor (oracle.adamw.clip_coef over the adapter's whole A and B gradients
+  in float64) before the update; the limits are set from each adapter's
+  first-step gradient norm so that some adapters are clipped, some stay under
+  their limit and some have clipping off.
 Shapes: a small layer with ranks 1..256 (several pieces per tensor and
 partial last pieces), an fp32 layer, the 4096x4096 layer of four adapters the
 bench times (whole tensors), and the 8192x28672 projection of 32 adapters
@@ -75,7 +80,10 @@ def _err(got, want):
     return num / den
 
 
-def _run(dt, ranks, d_in, d_out, n_steps, seed, sample=None, widths=None):
+CLIP_FACTORS = (0.3, 3.0, 0.0, 0.05)      # limit = factor x first-step norm; 0 turns clipping off
+
+
+def _run(dt, ranks, d_in, d_out, n_steps, seed, sample=None, widths=None, clip=False):
     import torch
     plan, layer, opt, A32, B32 = _layer(dt, ranks, d_in, d_out, seed, widths)
     n = len(ranks)
@@ -121,11 +129,23 @@ def _run(dt, ranks, d_in, d_out, n_steps, seed, sample=None, widths=None):
             layer.dA[i].copy_(torch.from_numpy(gA[i]).cuda())
             layer.dB[i].copy_(torch.from_numpy(gB[i]).cuda())
         hp = optim.step_hparams(hps, s)
-        plan.profile_enable(["adamw"])
+        coef = [1.0] * n
+        if clip:
+            if s == 0:
+                norms = [np.sqrt(np.sum(gA[i].astype(np.float64) ** 2) + np.sum(gB[i].astype(np.float64) ** 2))
+                         for i in range(n)]
+                limits = [float(np.float32(CLIP_FACTORS[i % len(CLIP_FACTORS)] * norms[i])) for i in range(n)]
+            for i in range(n):
+                hp[i]["max_grad_norm"] = limits[i]
+                if hp[i]["step"] >= 1:
+                    coef[i] = oa.clip_coef([gA[i], gB[i]], limits[i])
+        plan.profile_enable(["adamw", "grad_norm"])
         plan.profile_read()
-        opt.step(hp)
+        opt.step(hp, clip_grads=clip)
         torch.cuda.synchronize()
-        assert plan.profile_read()["adamw"][1] == 1, "one optimizer launch per step"
+        prof = plan.profile_read()
+        assert prof["adamw"][1] == 1, "one optimizer launch per step"
+        assert prof["grad_norm"][1] == (1 if clip else 0), "norms are taken only with clipping on"
         plan.profile_enable(False)
         state = {}
         for i in range(n):
@@ -138,7 +158,7 @@ def _run(dt, ranks, d_in, d_out, n_steps, seed, sample=None, widths=None):
                 mg = dev_take(m_d, ik).double().cpu().numpy()
                 vg = dev_take(v_d, ik).double().cpu().numpy()
                 state[ik] = (pg, mg, vg)
-                po[ik], mo[ik], vo[ik] = oa.adamw_tensor(po[ik], take(g, ik), mo[ik], vo[ik], h["lr"],
+                po[ik], mo[ik], vo[ik] = oa.adamw_tensor(po[ik], take(g, ik) * coef[i], mo[ik], vo[ik], h["lr"],
                                                          h["beta1"], h["beta2"], h["eps"],
                                                          h["weight_decay"], h["step"])
                 if h["step"] <= 0:
@@ -162,7 +182,7 @@ def _run(dt, ranks, d_in, d_out, n_steps, seed, sample=None, widths=None):
                     assert np.array_equal(got, want), f"step {s} adapter {i}: bf16 copy is not RNE of the master"
         prev = state
     say(f"  adamw {dt} ranks={list(ranks)[:8]}{'...' if len(ranks) > 8 else ''} {d_in}x{d_out} "
-        f"{n_steps} steps: worst {worst[0]} = {worst[1]:.3e} (tol {TOLF:.0e})")
+        f"{n_steps} steps{' clipped' if clip else ''}: worst {worst[0]} = {worst[1]:.3e} (tol {TOLF:.0e})")
 
 
 @pytest.mark.gpu
@@ -201,3 +221,27 @@ def test_adamw_projection_pairs():
     ranks = [8, 64, 33, 1, 128, 16]          # three adapters x two projections, adapter-major
     say(f"case adamw projection pairs widths {widths} ranks {ranks}")
     _run("bf16", ranks, 256, None, 3, seed=8, widths=widths)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dt,ranks,d_in,d_out,widths", [
+    ("bf16", [4, 16, 33, 64, 256, 8, 1, 100], 256, 320, None),
+    ("fp32", [4, 8, 2, 100], 128, 192, None),
+    ("bf16", [8, 64, 33, 1, 128, 16, 4, 200], 256, None, [512, 256]),
+])
+def test_adamw_clipped_against_oracle(dt, ranks, d_in, d_out, widths):
+    """Per-adapter gradient-norm clipping: clipped, unclipped and off adapters
+    in one call, over steps where some adapters are skipped."""
+    say(f"case adamw clipped {dt} ranks {ranks} {d_in}x{d_out} widths {widths}")
+    _run(dt, ranks, d_in, d_out, 4, seed=9, widths=widths, clip=True)
+
+
+@pytest.mark.gpu
+def test_adamw_clipped_largest_layer_sampled():
+    """Clipping over the 8192x28672 projection: each adapter's norm spans
+    millions of elements (about a thousand work items per B)."""
+    from workloads import load_workload
+    w = load_workload("mlp70b_pair", 0)
+    p = w.projections[0]
+    say(f"case adamw clipped mlp70b_pair {p.d_in}x{p.d_out}, {w.n} adapters (sampled)")
+    _run("bf16", w.ranks, p.d_in, p.d_out, 2, seed=10, sample=512, clip=True)

@@ -173,5 +173,5 @@ def test_profile_mask_selects_kernels():
     plan.profile_enable(False)
     # every kind the forward and backward of a bf16 base launch (the optimizer
     # step is a call of its own; only an MXFP8 base is decoded)
-    assert all(cnt > 0 for k, (ms, cnt) in r.items() if k not in ("adamw", "dequant")), r
-    assert r["adamw"][1] == 0 and r["dequant"][1] == 0, r
+    assert all(cnt > 0 for k, (ms, cnt) in r.items() if k not in ("adamw", "dequant", "grad_norm")), r
+    assert r["adamw"][1] == 0 and r["dequant"][1] == 0 and r["grad_norm"][1] == 0, r
