@@ -638,22 +638,26 @@ void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, 
 // r_j zero).  Output written as bf16, staged through LDS so every store
 // writes whole 512-byte rows.
 // ---------------------------------------------------------------------------
-// LDS tile layouts of one 32-deep K-step (16 KiB each).  LDS has 64 banks
-// of 4 bytes.  Measured on gfx950 (read timings of many layouts): a 16-byte
-// read is served in 16-lane groups that never mix the two half-waves and
-// split each half-wave by the parity of lane-index bits 2 and 4; an 8-byte
-// transposing read in 32-lane groups.  The layouts give every group distinct
-// banks:
-//  k-contiguous: 256 rows x 32 bf16 (four 16-byte chunks, one 64-byte row
-//    each, so a direct copy reads whole rows with four adjacent lanes); chunk
-//    c of row r sits at position c ^ ((r >> 2) & 3).  Within a read group the
-//    rows r and r ^ 16 never meet, so the sixteen rows of a group fill all
-//    sixteen 16-byte positions of a 256-byte bank line;
-//  n-contiguous: 32 k-rows x 256 bf16 (thirty-two chunks); chunk c of k-row
-//    kr sits at c ^ nx(kr), nx the XOR of 4, 8 and 9 over bits 0, 1 and 3 of
-//    kr, so the k-rows and chunks of one transposing read group are distinct.
-__device__ __forceinline__ int kx(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int kpos(int r, int c) { return r * 4 + (c ^ kx(r)); }
+// Base GEMM with the LoRA term as extra K-steps (the expand of the forward,
+// PLoRA §9.2 Case 4's dZ.A^T in the backward).  256x256 tile per workgroup of
+// four waves; 64-deep K-steps copied straight from global memory into an LDS
+// ring; output written as bf16, staged through LDS so every store writes
+// whole 512-byte rows.
+//
+// LDS has 64 banks of 4 bytes.  Measured on gfx950 (read timings of many
+// layouts): a 16-byte read is served in 16-lane groups that never mix the
+// two half-waves and split each half-wave by the parity of lane-index bits 2
+// and 4; an 8-byte transposing read in 32-lane groups.  The layouts of one
+// operand of one step (32 KiB each) give every group distinct banks:
+//  k-contiguous: 256 rows of 128 bytes (eight 16-byte chunks); chunk c of
+//    row r sits at c ^ ((r >> 1) & 7).  In each 16-lane read group the eight
+//    even rows, and the eight odd ones, take eight distinct positions, and
+//    even and odd rows fill the two halves of a 256-byte bank line;
+//  n-contiguous: 64 k-rows of 512 bytes (thirty-two chunks); chunk c of
+//    k-row kr sits at c ^ nx(kr), nx the XOR of 4, 8 and 9 over bits 0, 1
+//    and 3 of kr, so the k-rows and chunks of one transposing read group are
+//    distinct.
+__device__ __forceinline__ int kx8(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int nx(int kr) {
   return ((kr & 1) ? 4 : 0) ^ ((kr & 2) ? 8 : 0) ^ ((kr & 8) ? 9 : 0);
 }
@@ -682,239 +686,49 @@ __device__ __forceinline__ u32x4 read_b_tr(const u32x4* tile, int nb, int kb, in
   return out;
 }
 
-// Four waves, one per SIMD, share one 256x256 output tile, two along M and
-// two along N; each wave owns 128x128 accumulators (256 registers), so every
-// 16-byte fragment read from LDS feeds four MFMAs instead of two or three.
-// Software pipeline at the granularity of a 16-deep slice, fragments double
-// buffered in registers: while the 16 MFMAs of one slice run, the wave reads
-// the next slice's eight fragments into the other register set and issues
-// four of its eight copies of a later step; one memory instruction follows
-// each MFMA, so reads, copies and their address arithmetic hide behind
-// matrix work of the same wave.
-//
-// One barrier per step, between its two slices, after the wave's reads of
-// step k have landed and its copies up to step k+1 have landed: past it
-// every wave's copies of step k+1 are visible and nobody reads slot k % NS
-// any more, so step k+NS refills it: its first four copies during the
-// second slice of step k, the other four during the first slice of step
-// k+1.  Copies past the last step repeat the last step into a slot that is
-// never read again, so every barrier waits for the same vmcnt.  Steps whose
-// refill is a plain K-step of the main operands run a branch-free loop; the
-// few whose refill is a LoRA extension step (or past the end) run a second
-// loop that looks the extension up in the plan's tables.
-template <bool FWD, bool MAIN_B_KC, bool PERM, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
-  constexpr int NS = 5;                    // ring stages
-  constexpr int FI = 4, FJ = 4;            // 32x32 fragments per wave along M, N
-  constexpr int BPW = 4;                   // 1 KiB blocks per operand per wave per stage
-  constexpr int LPS = 2 * BPW;             // direct loads per wave per stage
-  __shared__ u32x4 ring[NS][2][1024];      // [stage][A/B][16 KiB]
-
+// Output tile of workgroup blockIdx.x.  Workgroup b runs on XCD b mod 8;
+// each XCD takes a contiguous run of logical tiles, and logical tiles go
+// down groups of eight row tiles before moving along N, so the tiles an XCD
+// runs together share operand rows in its L2.  With split-K the logical
+// index also names the K part.
+struct TileCoord {
+  int sp, TT, tm, tn;
+};
+template <bool SPLIT>
+__device__ __forceinline__ TileCoord tile_coord(const GemmArgs& g) {
   const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7, q = bid >> 3, per = G >> 3, rem = G & 7;
   const int L0 = xcd * per + min(xcd, rem) + q;
   const int nM = g.n_mtiles, nN = g.n_ntiles;
   const int TT = nM * nN;
-  const int sp = SPLIT ? L0 / TT : 0;        // K part
-  const int L = L0 - sp * TT;                // output tile
+  const int sp = SPLIT ? L0 / TT : 0;
+  const int L = L0 - sp * TT;
   constexpr int GM = 8;
   const int grpm = L / (GM * nN);
   const int fm = grpm * GM;
   const int gm = min(GM, nM - fm);
   const int within = L - grpm * GM * nN;
-  const int tm = fm + within % gm, tn = within / gm;
+  return TileCoord{sp, TT, fm + within % gm, within / gm};
+}
 
-  const int tix = g.tile_begin + tm;
-  const int row0 = ldc(g.t.tiles + 2 * tix), mrows = ldc(g.t.tiles + 2 * tix + 1);
-  const int n0 = tn * 256;
-  // Extension steps: the forward's column tile lies in one projection and
-  // takes that projection's list; the dX GEMM sums every projection.
-  const int NP = g.t.nproj;
-  int pq = 0;
-  while (FWD && pq + 1 < NP && ldc(g.t.pcol + pq + 1) <= n0) ++pq;
-  const int e0 = ldc(g.t.ext_start + tix * NP + (FWD ? pq : 0));
-  const int e1 = !SPLIT || sp == g.ksplit - 1 ? ldc(g.t.ext_start + tix * NP + (FWD ? pq + 1 : NP)) : e0;
-  const int pc0 = ldc(g.t.pcol + pq), pw = ldc(g.t.pcol + pq + 1) - pc0;  // forward: B_j is [r_j][pw]
-  const int kb = SPLIT ? sp * g.kper : 0;         // first main K-step of this part
-  const int nk = SPLIT ? min(g.K / 32 - kb, g.kper) : g.K / 32;
-  const int nsteps = nk + (e1 - e0);
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Epilogue of both GEMM kernels; the ring is free (every wave is past its
+// last read and no copy is in flight).  SPLIT: the fp32 partial tile of K
+// part sp (rows past the tile are written too, finite values from clamped
+// rows, and never read).  Otherwise the tile is staged in LDS as bf16
+// [256][256]: 512-byte rows of 32 16-byte granules, granule c of row m at
+// c ^ (m & 31), so the 32 rows a fragment writes and the 32 granules a row
+// read takes both spread evenly over the banks; each wave then stores 64
+// rows, two 512-byte rows per instruction.  acc[fi][fj][4gg+e] holds
+// C[m = wrow + 32fi + l32][n = wcol + 32fj + 8gg + 4half + e].
+template <bool PERM, bool SPLIT>
+__device__ __forceinline__ void gemm_store(const GemmArgs& g, const f32x16 (&acc)[4][4], char* ct,
+                                           const TileCoord& tc, int row0, int mrows, int n0, int w,
+                                           int lane) {
+  constexpr int FI = 4, FJ = 4;
   const int half = lane >> 5, l32 = lane & 31;
-  const int wm = w >> 1, wn = w & 1;
-  const int wrow = 128 * wm, wcol = 128 * wn;
-
-  int kr_row[BPW], kr_chunk[BPW], nc_krow[BPW], nc_chunk[BPW];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int qb = BPW * w + i;
-    kr_row[i] = 16 * qb + (lane >> 2);
-    kr_chunk[i] = (lane & 3) ^ kx(kr_row[i]);
-    nc_krow[i] = 2 * qb + (lane >> 5);
-    nc_chunk[i] = (lane & 31) ^ nx(nc_krow[i]);
-  }
-  const uint16_t* aptr[BPW];
-  const uint16_t* bptr[BPW];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int ar = row0 + min(kr_row[i], mrows - 1);  // grouped row; PERM: caller row via the plan
-    aptr[i] = g.A + (int64_t)(PERM ? ldg_i32(g.t.perm + ar) : ar) * g.lda + 8 * kr_chunk[i] + 32 * kb;
-    if (MAIN_B_KC)
-      bptr[i] = g.B + (int64_t)min(n0 + kr_row[i], g.N - 1) * g.ldb + 8 * kr_chunk[i] + 32 * kb;
-    else
-      bptr[i] = g.B + (int64_t)(nc_krow[i] + 32 * kb) * g.ldb + min(n0 + 8 * nc_chunk[i], g.N - 8);
-  }
-
-  // Global sources of this lane's blocks of step `step` (BPW of the A tile,
-  // then BPW of the B tile); rows that must read as zero point at the zero
-  // page.
-  auto sources = [&](int step, const uint16_t* (&src)[LPS]) {
-    if (step < nk) {
-      const int k0 = step * 32;
-#pragma unroll
-      for (int i = 0; i < BPW; ++i) src[i] = aptr[i] + k0;
-#pragma unroll
-      for (int i = 0; i < BPW; ++i)
-        src[BPW + i] = MAIN_B_KC ? bptr[i] + k0 : bptr[i] + (int64_t)k0 * g.ldb;
-    } else {
-      const int e = e0 + step - nk;
-      const int j = ldc(g.t.ext + 4 * e), lo = ldc(g.t.ext + 4 * e + 1), hi = ldc(g.t.ext + 4 * e + 2);
-      const int k0 = ldc(g.t.ext + 4 * e + 3);
-      const int rp = ldc(g.t.rpad + j);
-      const int64_t oj = ldc(g.t.seg0 + j);
-      const uint16_t* zb = g.ebuf + ldc(g.t.zoff + j);
-#pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        const int grow = row0 + kr_row[i];
-        src[i] = (grow >= lo && grow < hi) ? zb + (int64_t)(grow - oj) * rp + k0 + 8 * kr_chunk[i]
-                                           : g.t.zero;
-      }
-      if (MAIN_B_KC) {
-        const int64_t ro = ldc(g.t.roff + j);
-#pragma unroll
-        for (int i = 0; i < BPW; ++i)
-          src[BPW + i] = g.ext_k + (int64_t)min(n0 + kr_row[i], g.N - 1) * g.rtot + ro + k0 + 8 * kr_chunk[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-          const int k = k0 + nc_krow[i];
-          const int col = min(n0 + 8 * nc_chunk[i], g.N - 8);
-          if (FWD) {
-            const int rj = ldc(g.t.ranks + j);
-            src[BPW + i] = k < rj ? static_cast<const uint16_t*>(ldc(g.eb + j)) + (int64_t)k * pw + (col - pc0)
-                                  : g.t.zero;
-          } else {
-            src[BPW + i] = g.ext_n + (int64_t)(ldc(g.t.roff + j) + k) * g.N + col;
-          }
-        }
-      }
-    }
-  };
-  // LDS byte address of the ring, computed once; copy i of a stage goes to
-  // block (i / BPW) * 1024 + 64 (BPW w + i % BPW) (in 16-byte units)
-  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(MLORA_LDS void*)&ring[0][0][0]);
-  const uint32_t wave_lds = ring_lds + 16u * 64u * (uint32_t)(BPW * w);
-  auto copy = [&](const uint16_t* src, int slot, int i) {
-    dma16_at(src, wave_lds + 16u * (uint32_t)(slot * 2048 + (i / BPW) * 1024 + 64 * (i % BPW)));
-  };
-  // Source of copy i of main step `step` (step < nk).
-  auto src_main = [&](int step, int i) -> const uint16_t* {
-    const int k0 = step * 32;
-    if (i < BPW) return aptr[i] + k0;
-    return MAIN_B_KC ? bptr[i - BPW] + k0 : bptr[i - BPW] + (int64_t)k0 * g.ldb;
-  };
-
-  f32x16 acc[FI][FJ];
-#pragma unroll
-  for (int a = 0; a < FI; ++a)
-#pragma unroll
-    for (int b = 0; b < FJ; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-
-  // Fragments of one 16-deep slice, two register sets.
-  u32x4 fa[2][FI], fb[2][FJ];
-  // Fragment read r (0..7) of slice ks: A fragments first.
-  auto read_frag = [&](const u32x4* slot, int ks, u32x4 (&ra)[FI], u32x4 (&rb)[FJ], int r) {
-    const u32x4* sa = slot;
-    const u32x4* sb = slot + 1024;
-    if (r < FI) {
-      ra[r] = sa[kpos(wrow + 32 * r + l32, 2 * ks + half)];
-    } else {
-      const int fj = r - FI;
-      if (MAIN_B_KC) rb[fj] = sb[kpos(wcol + 32 * fj + l32, 2 * ks + half)];
-      else rb[fj] = read_b_tr(sb, wcol + 32 * fj, 16 * ks, lane);
-    }
-  };
-  auto mma = [&](const u32x4 (&ra)[FI], const u32x4 (&rb)[FJ], int qq) {
-    const int fi = qq >> 2, fj = qq & 3;
-    acc[fi][fj] = mfma32(rb[fj], ra[fi], acc[fi][fj]);
-  };
-
-  // Step k.  First slice from set 0: the reads of the second slice into set
-  // 1 after its first eight MFMAs, then the last four copies of step
-  // k-1+NS (into slot (k-1) % NS, free since the previous barrier).  Barrier.
-  // Second slice from set 1: the reads of step k+1's first slice into set 0,
-  // then the first four copies of step k+NS into slot k % NS.  MAIN: both
-  // refills are main K-steps, whose sources are the main operands' pointers
-  // plus the step's offset.
-  auto step_block = [&](int k, auto main_tag) {
-    constexpr bool MAIN = decltype(main_tag)::value;
-    const u32x4* cslot = &ring[k % NS][0][0];
-    const int pslot = (k + NS - 1) % NS;
-    const uint16_t* s1[LPS];
-    if (!MAIN) sources(min(k - 1 + NS, nsteps - 1), s1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int qq = 0; qq < 16; ++qq) {
-      mma(fa[0], fb[0], qq);
-      if (qq < 8) read_frag(cslot, 1, fa[1], fb[1], qq);
-      else if (qq < 12) copy(MAIN ? src_main(k - 1 + NS, qq - 4) : s1[qq - 4], pslot, qq - 4);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wait_vm_barrier<(NS - 2) * LPS>();
-    const uint16_t* s2[LPS];
-    if (!MAIN) sources(min(k + NS, nsteps - 1), s2);
-    const int dslot = k % NS;
-    const u32x4* nslot = &ring[(k + 1) % NS][0][0];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int qq = 0; qq < 16; ++qq) {
-      mma(fa[1], fb[1], qq);
-      if (qq < 8) read_frag(nslot, 0, fa[0], fb[0], qq);
-      else if (qq < 12) copy(MAIN ? src_main(k + NS, qq - 8) : s2[qq - 8], dslot, qq - 8);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Prologue: steps 0..NS-2 and the first four copies of step NS-1; step
-  // 0's first slice is read once every wave's copies of it have landed.
-#pragma unroll
-  for (int p = 0; p < NS; ++p) {
-    const uint16_t* src[LPS];
-    sources(min(p, nsteps - 1), src);
-#pragma unroll
-    for (int i = 0; i < (p < NS - 1 ? LPS : LPS / 2); ++i) copy(src[i], p, i);
-  }
-  wait_vm_barrier<(NS - 2) * LPS + LPS / 2>();
-#pragma unroll
-  for (int r = 0; r < FI + FJ; ++r) read_frag(&ring[0][0][0], 0, fa[0], fb[0], r);
-
-  int k = 0;
-  for (; k + NS < nk; ++k) step_block(k, std::true_type());
-  for (; k < nsteps; ++k) step_block(k, std::false_type());
-  // The repeated copies past the last step are still in flight, and every
-  // wave must be done with the ring before it holds the output tile.
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  __syncthreads();
-
+  const int wrow = 128 * (w >> 1), wcol = 128 * (w & 1);
   if constexpr (SPLIT) {
-    // fp32 partial tile [256][256] of this K part; rows past the tile are
-    // written too (finite values from clamped rows) and never read
-    float* pt = g.part + (int64_t)(sp * TT + tm * nN + tn) * 65536;
+    float* pt = g.part + (int64_t)(tc.sp * tc.TT + tc.tm * g.n_ntiles + tc.tn) * 65536;
 #pragma unroll
     for (int fi = 0; fi < FI; ++fi) {
       const int m = wrow + 32 * fi + l32;
@@ -930,13 +744,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     }
     return;
   }
-
-  // Output tile staged in LDS as bf16 [256][256]: 512-byte rows of 32
-  // 16-byte granules, granule c of row m at c ^ (m & 31), so the 32 rows a
-  // fragment writes and the 32 granules a row read takes both spread evenly
-  // over the banks.  acc[fi][fj][4gg+e] holds C[m = wrow + 32fi + l32]
-  // [n = wcol + 32fj + 8gg + 4half + e].
-  char* ct = reinterpret_cast<char*>(&ring[0][0][0]);
 #pragma unroll
   for (int fi = 0; fi < FI; ++fi) {
     const int m = wrow + 32 * fi + l32;
@@ -953,7 +760,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     }
   }
   __syncthreads();
-  // Each wave stores 64 rows, two 512-byte rows per instruction.
   const int gc = lane & 31;
 #pragma unroll 4
   for (int it = 0; it < 32; ++it) {
@@ -965,6 +771,254 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
       *reinterpret_cast<u32x4*>(g.C + (int64_t)cr * g.ldc + n) = v;
     }
   }
+}
+
+// Four waves, one per SIMD, share the tile, two along M and two along N;
+// each wave owns 128x128 accumulators (256 registers), so every 16-byte
+// fragment read from LDS feeds four MFMAs.
+//
+// Steps are 64 deep so that a copy of a k-contiguous operand reads whole
+// 128-byte lines (32-deep steps read half a line per row and cross the L2
+// twice per line).  The 160 KiB ring holds five units of 32 KiB, one operand
+// of one step each: unit u = 2 step + operand, in slot u mod 5.  While step
+// s is read, step s+1 and the A unit of step s+2 are in flight.
+//
+// A step is two 32-deep sub-steps: the main K-steps first, then the tile's
+// LoRA extension steps from the plan's list (adapter, rows, k0): sub-step e
+// loads rows [lo,hi) of E_j (other rows zero) and k-rows [k0, k0+32) of
+// EB_j (rows >= r_j zero).  Chunk c of a k-contiguous row belongs to
+// sub-step 2s + c/4, k-row kr of an n-contiguous unit to sub-step 2s +
+// kr/32; past the last sub-step copies read the zero page.
+//
+// Four 16-deep slices per step with fragments double buffered in
+// registers; one memory instruction follows each MFMA.  Step s:
+//   slices 0-1: read the next slice's fragments; copy unit 2s+4 (A of step
+//     s+2) into the slot freed at the previous step's barrier;
+//   slice 2: read slice 3's fragments; then wait until this wave's copies
+//     of step s+1 have landed (only unit 2s+4's eight may be in flight) and
+//     its reads are done, and meet the other waves: step s+1 is complete in
+//     LDS and nobody reads step s's units any more;
+//   slice 3: read step s+1's first slice; copy unit 2s+5 (B of step s+2)
+//     into the slot of step s's A unit.
+// Copies past the last step repeat the zero page into slots never read
+// again, so every barrier waits for the same count.  Steps whose refills
+// are main K-steps run a branch-free loop; the rest look their sources up
+// in the plan's tables.
+template <bool FWD, bool MAIN_B_KC, bool PERM, bool SPLIT>
+__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
+  constexpr int NU = 5;                    // ring units of 32 KiB
+  constexpr int FI = 4, FJ = 4;            // 32x32 fragments per wave along M, N
+  constexpr int CPW = 8;                   // copies per wave per unit (8 rows x 128 B each)
+  __shared__ u32x4 ring[NU][2048];
+
+  const TileCoord tc = tile_coord<SPLIT>(g);
+  const int sp = tc.sp, tm = tc.tm, tn = tc.tn;
+  const int tix = g.tile_begin + tm;
+  const int row0 = ldc(g.t.tiles + 2 * tix), mrows = ldc(g.t.tiles + 2 * tix + 1);
+  const int n0 = tn * 256;
+  const int NP = g.t.nproj;
+  int pq = 0;
+  while (FWD && pq + 1 < NP && ldc(g.t.pcol + pq + 1) <= n0) ++pq;
+  const int e0 = ldc(g.t.ext_start + tix * NP + (FWD ? pq : 0));
+  const int e1 = !SPLIT || sp == g.ksplit - 1 ? ldc(g.t.ext_start + tix * NP + (FWD ? pq + 1 : NP)) : e0;
+  const int pc0 = ldc(g.t.pcol + pq), pw = ldc(g.t.pcol + pq + 1) - pc0;  // forward: B_j is [r_j][pw]
+  const int kb = SPLIT ? sp * g.kper : 0;         // first main 32-deep sub-step of this part
+  const int nk = SPLIT ? min(g.K / 32 - kb, g.kper) : g.K / 32;
+  const int nsub = nk + (e1 - e0);
+  const int nsteps = (nsub + 1) >> 1;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wrow = 128 * (w >> 1), wcol = 128 * (w & 1);
+
+  // Copy i of a k-contiguous unit: tile row 64w + 8i + lane/8 into LDS
+  // position lane%8, which holds the row's chunk c = (lane%8) ^ kx8(row).
+  // Copy i of an n-contiguous unit: k-row 16w + 2i + lane/32 into LDS
+  // position lane%32, which holds the k-row's chunk (lane%32) ^ nx(k-row).
+  int crow[CPW], cch[CPW], nkr[CPW], nch[CPW];
+  const uint16_t* aptr[CPW];
+  const uint16_t* bptr[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    crow[i] = 64 * w + 8 * i + (lane >> 3);
+    cch[i] = (lane & 7) ^ kx8(crow[i]);
+    nkr[i] = 16 * w + 2 * i + (lane >> 5);
+    nch[i] = (lane & 31) ^ nx(nkr[i]);
+    const int ar = row0 + min(crow[i], mrows - 1);
+    aptr[i] = g.A + (int64_t)(PERM ? ldg_i32(g.t.perm + ar) : ar) * g.lda + 32 * kb + 8 * cch[i];
+    if (MAIN_B_KC)
+      bptr[i] = g.B + (int64_t)min(n0 + crow[i], g.N - 1) * g.ldb + 32 * kb + 8 * cch[i];
+    else
+      bptr[i] = g.B + (int64_t)(32 * kb + nkr[i]) * g.ldb + min(n0 + 8 * nch[i], g.N - 8);
+  }
+
+  // Sources of unit u's copies: main sub-steps at the operand's pointer plus
+  // 64 k per step; extension sub-steps from the plan's list (rows outside the
+  // entry's rows, and B rows past the rank, read as zero); the rest zero.
+  auto unit_sources = [&](int u, const uint16_t* (&src)[CPW]) {
+    const int t = u >> 1, op = u & 1;
+    int kind[2], lo[2], hi[2], k0[2], rp[2], rk[2];
+    int64_t oj[2], ro[2];
+    const uint16_t* zb[2];
+    const uint16_t* ebj[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int sub = 2 * t + h;
+      kind[h] = sub < nk ? 0 : (sub < nsub ? 1 : 2);
+      lo[h] = hi[h] = k0[h] = rp[h] = rk[h] = 0;
+      oj[h] = ro[h] = 0;
+      zb[h] = ebj[h] = g.t.zero;
+      if (kind[h] == 1) {
+        const int e = e0 + sub - nk;
+        const int j = ldc(g.t.ext + 4 * e);
+        if (FWD && !MAIN_B_KC) {
+          rk[h] = ldc(g.t.ranks + j);
+          ebj[h] = static_cast<const uint16_t*>(ldc(g.eb + j));
+        }
+        lo[h] = ldc(g.t.ext + 4 * e + 1);
+        hi[h] = ldc(g.t.ext + 4 * e + 2);
+        k0[h] = ldc(g.t.ext + 4 * e + 3);
+        rp[h] = ldc(g.t.rpad + j);
+        oj[h] = ldc(g.t.seg0 + j);
+        ro[h] = ldc(g.t.roff + j);
+        zb[h] = g.ebuf + ldc(g.t.zoff + j);
+      }
+    }
+    if (op == 1 && !MAIN_B_KC) {
+      // n-contiguous B: k-row nkr of the step is row nkr % 32 of sub-step
+      // 2t + nkr / 32
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int h = nkr[i] >> 5, kr = nkr[i] & 31;
+        const int kd = h ? kind[1] : kind[0];
+        const int col = min(n0 + 8 * nch[i], g.N - 8);
+        const int k = (h ? k0[1] : k0[0]) + kr;
+        const uint16_t* ext;
+        if (FWD) {
+          ext = k < (h ? rk[1] : rk[0]) ? (h ? ebj[1] : ebj[0]) + (int64_t)k * pw + (col - pc0) : g.t.zero;
+        } else {
+          ext = g.ext_n + ((h ? ro[1] : ro[0]) + k) * g.N + col;
+        }
+        src[i] = kd == 0 ? bptr[i] + (int64_t)(64 * t) * g.ldb : (kd == 1 ? ext : g.t.zero);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int h = cch[i] >> 2, kk = 8 * (cch[i] & 3);
+      const int kd = h ? kind[1] : kind[0];
+      const uint16_t* main = (op ? bptr[i] : aptr[i]) + 64 * t;
+      const uint16_t* ext;
+      if (op == 0) {
+        const int grow = row0 + crow[i];
+        const int l = h ? lo[1] : lo[0], hh = h ? hi[1] : hi[0];
+        ext = (grow >= l && grow < hh)
+                  ? (h ? zb[1] : zb[0]) + (int64_t)(grow - (h ? oj[1] : oj[0])) * (h ? rp[1] : rp[0]) +
+                        (h ? k0[1] : k0[0]) + kk
+                  : g.t.zero;
+      } else {
+        ext = g.ext_k + (int64_t)min(n0 + crow[i], g.N - 1) * g.rtot + (h ? ro[1] : ro[0]) +
+              (h ? k0[1] : k0[0]) + kk;
+      }
+      src[i] = kd == 0 ? main : (kd == 1 ? ext : g.t.zero);
+    }
+  };
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(MLORA_LDS void*)&ring[0][0]);
+  auto copy = [&](const uint16_t* src, int u, int i) {
+    dma16_at(src, ring_lds + 16u * (uint32_t)((u % NU) * 2048 + 512 * w + 64 * i));
+  };
+  auto src_main = [&](int u, int i) -> const uint16_t* {
+    if (u & 1) return MAIN_B_KC ? bptr[i] + 64 * (u >> 1) : bptr[i] + (int64_t)(64 * (u >> 1)) * g.ldb;
+    return aptr[i] + 64 * (u >> 1);
+  };
+
+  f32x16 acc[FI][FJ];
+#pragma unroll
+  for (int a = 0; a < FI; ++a)
+#pragma unroll
+    for (int b = 0; b < FJ; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  u32x4 fa[2][FI], fb[2][FJ];
+  // Fragment read r (0..7) of slice ks of step s (A fragments first).
+  auto read_frag = [&](int s, int ks, u32x4 (&ra)[FI], u32x4 (&rb)[FJ], int r) {
+    const int c = 2 * ks + half;
+    if (r < FI) {
+      const int row = wrow + 32 * r + l32;
+      ra[r] = ring[(2 * s) % NU][row * 8 + (c ^ kx8(row))];
+    } else if (MAIN_B_KC) {
+      const int row = wcol + 32 * (r - FI) + l32;
+      rb[r - FI] = ring[(2 * s + 1) % NU][row * 8 + (c ^ kx8(row))];
+    } else {
+      rb[r - FI] = read_b_tr(ring[(2 * s + 1) % NU], wcol + 32 * (r - FI), 16 * ks, lane);
+    }
+  };
+  auto mma = [&](const u32x4 (&ra)[FI], const u32x4 (&rb)[FJ], int qq) {
+    const int fi = qq >> 2, fj = qq & 3;
+    acc[fi][fj] = mfma32(rb[fj], ra[fi], acc[fi][fj]);
+  };
+
+  auto step_block = [&](int s, auto main_tag) {
+    constexpr bool MAIN = decltype(main_tag)::value;   // units 2s+4 and 2s+5 are main K
+    const uint16_t* sa[CPW];
+    if (!MAIN) unit_sources(2 * s + 4, sa);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) {
+      mma(fa[0], fb[0], qq);
+      if (qq < 8) read_frag(s, 1, fa[1], fb[1], qq);
+      else if (qq < 12) copy(MAIN ? src_main(2 * s + 4, qq - 8) : sa[qq - 8], 2 * s + 4, qq - 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) {
+      mma(fa[1], fb[1], qq);
+      if (qq < 8) read_frag(s, 2, fa[0], fb[0], qq);
+      else if (qq < 12) copy(MAIN ? src_main(2 * s + 4, qq - 4) : sa[qq - 4], 2 * s + 4, qq - 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) {
+      mma(fa[0], fb[0], qq);
+      if (qq < 8) read_frag(s, 3, fa[1], fb[1], qq);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wait_vm_barrier<CPW>();
+    const uint16_t* sb[CPW];
+    if (!MAIN) unit_sources(2 * s + 5, sb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) {
+      mma(fa[1], fb[1], qq);
+      if (qq < 8) read_frag(s + 1, 0, fa[0], fb[0], qq);
+      else copy(MAIN ? src_main(2 * s + 5, qq - 8) : sb[qq - 8], 2 * s + 5, qq - 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Prologue: units 0-3 (steps 0 and 1); step 0's first slice is read once
+  // every wave's copies of step 0 have landed.
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint16_t* src[CPW];
+    unit_sources(u, src);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) copy(src[i], u, i);
+  }
+  wait_vm_barrier<2 * CPW>();
+#pragma unroll
+  for (int r = 0; r < FI + FJ; ++r) read_frag(0, 0, fa[0], fb[0], r);
+
+  int s = 0;
+  for (; 2 * s + 6 <= nk; ++s) step_block(s, std::true_type());
+  for (; s < nsteps; ++s) step_block(s, std::false_type());
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+  gemm_store<PERM, SPLIT>(g, acc, reinterpret_cast<char*>(&ring[0][0]), tc, row0, mrows, n0, w, lane);
 }
 
 // Sum of the K parts of split-K tiles, in part order, rounded to bf16 and
