@@ -961,6 +961,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     acc[fi][fj] = mfma32(rb[fj], ra[fi], acc[fi][fj]);
   };
 
+  // Fragment reads of a slice, issued over the MFMA slots of the slice
+  // before.  k-contiguous B: in the order the first MFMAs need them (A0 with
+  // B0..B3 for the first four, then A1, A2, A3), two per slot in the first
+  // four slots, so no MFMA waits for a read issued less than about fifteen
+  // MFMAs earlier.  n-contiguous B (two transposing reads per fragment): one
+  // fragment per slot in the first eight, A fragments first.
+  constexpr int kOrder[FI + FJ] = {0, FI, FI + 1, FI + 2, FI + 3, 1, 2, 3};
+  auto reads_at = [&](int qq, int s, int ks, u32x4 (&ra)[FI], u32x4 (&rb)[FJ]) {
+    if (MAIN_B_KC) {
+      if (qq < 4) {
+        read_frag(s, ks, ra, rb, kOrder[2 * qq]);
+        read_frag(s, ks, ra, rb, kOrder[2 * qq + 1]);
+      }
+    } else if (qq < FI + FJ) {
+      read_frag(s, ks, ra, rb, qq);
+    }
+  };
+  // First MFMA slot of a slice that carries a copy.
+  constexpr int C0 = MAIN_B_KC ? 4 : 8;
   auto step_block = [&](int s, auto main_tag) {
     constexpr bool MAIN = decltype(main_tag)::value;   // units 2s+4 and 2s+5 are main K
     const uint16_t* sa[CPW];
@@ -969,21 +988,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[0], fb[0], qq);
-      if (qq < 8) read_frag(s, 1, fa[1], fb[1], qq);
-      else if (qq < 12) copy(MAIN ? src_main(2 * s + 4, qq - 8) : sa[qq - 8], 2 * s + 4, qq - 8);
+      reads_at(qq, s, 1, fa[1], fb[1]);
+      if (qq >= C0 && qq < C0 + 4) copy(MAIN ? src_main(2 * s + 4, qq - C0) : sa[qq - C0], 2 * s + 4, qq - C0);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[1], fb[1], qq);
-      if (qq < 8) read_frag(s, 2, fa[0], fb[0], qq);
-      else if (qq < 12) copy(MAIN ? src_main(2 * s + 4, qq - 4) : sa[qq - 4], 2 * s + 4, qq - 4);
+      reads_at(qq, s, 2, fa[0], fb[0]);
+      if (qq >= C0 && qq < C0 + 4)
+        copy(MAIN ? src_main(2 * s + 4, qq - C0 + 4) : sa[qq - C0 + 4], 2 * s + 4, qq - C0 + 4);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[0], fb[0], qq);
-      if (qq < 8) read_frag(s, 3, fa[1], fb[1], qq);
+      reads_at(qq, s, 3, fa[1], fb[1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -994,8 +1014,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[1], fb[1], qq);
-      if (qq < 8) read_frag(s + 1, 0, fa[0], fb[0], qq);
-      else copy(MAIN ? src_main(2 * s + 5, qq - 8) : sb[qq - 8], 2 * s + 5, qq - 8);
+      reads_at(qq, s + 1, 0, fa[0], fb[0]);
+      if (qq >= C0 && qq < C0 + 8) copy(MAIN ? src_main(2 * s + 5, qq - C0) : sb[qq - C0], 2 * s + 5, qq - C0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
