@@ -2,6 +2,7 @@
 the plan): the parts' fp32 tiles are added in part order by a second
 kernel.  These cases put every split path on the GPU against the oracle:
 forward and dX splits of different factors, the last part's extension steps,
+parts with an odd number of 32-deep sub-steps,
 rows in the caller's order (ids), several stream groups each with its own
 partial region, several projections sharing the input, and both W0 layouts;
 two runs must be bitwise identical."""
@@ -17,6 +18,11 @@ SEG_CASES = [
     ("tall dX split", 512, 8192, [8, 64], [120, 180], 1, "nk", [[2, 16]]),
     ("three groups", 1024, 1536, [4, 32, 256, 16, 8], [100, 40, 300, 0, 77], 3, "kn", None),
     ("ragged, ranks 1-256", 768, 1024, [1, 33, 256, 100], [17, 250, 33, 64], 1, "nk", None),
+    # 34 sub-steps of 32 split 9+9+9+7: every part has a 64-deep step with one
+    # half past its main K (zero page, or the first extension sub-step in the
+    # last part); N = 1088 leaves a ragged column tile
+    ("odd sub-steps per part", 1088, 1088, [16, 48, 5], [150, 250, 90], 1, "kn", [[4, 4]]),
+    ("odd sub-steps per part, nk", 1088, 1088, [16, 48, 5], [150, 250, 90], 1, "nk", [[4, 4]]),
 ]
 
 
