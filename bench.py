@@ -291,6 +291,63 @@ def cost_table(steps, warmup):
     return rows
 
 
+def vendor_gemm(w, steps, warmup):
+    """The library's base GEMM launches beside torch.matmul (hipBLASLt) on the
+    same base products of the workload's first projection, in both W0
+    layouts: forward X.W0 and dX = dY.W0^T.  Ours: mean event time of one
+    launch of the forward GEMM (base plus fused expand) and of the dX GEMM
+    (base plus dZ.A^T; timed beside the concurrent weight-gradient kernels),
+    each from calls of that direction alone.  TFLOP/s count the base product
+    only, 2 T d_in d_out."""
+    import torch
+    from adapter_lora_segments_amd import Plan, PackedLoRALinear
+    from workloads.tensors import device_tensors
+    p = w.projections[0]
+    d = device_tensors(w, 0, sets=1)
+    X, dY = d["X"][0], d["dY"][0]
+    T = X.shape[0]
+    flops = 2.0 * T * p.d_in * p.d_out
+
+    def ev(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    out = {}
+    Wkn = d["W0"]
+    Wnk = Wkn.t().contiguous()
+    Y = torch.empty((T, p.d_out), dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty((T, p.d_in), dtype=torch.bfloat16, device="cuda")
+    for layout, W0 in (("kn", Wkn), ("nk", Wnk)):
+        plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16", n_streams=1, w0_layout=layout)
+        layer = PackedLoRALinear(plan, W0, d["A"], d["B"], d["scales"])
+        layer.forward(X, Y)
+        layer.backward(dY, X, dX)
+        for kind, fn in (("gemm_fwd", lambda: layer.forward(X, Y)), ("gemm_dx", lambda: layer.backward(dY, X, dX))):
+            plan.profile_enable([kind])
+            plan.profile_read()
+            ev(fn)
+            ms, cnt = plan.profile_read()[kind]
+            plan.profile_enable(False)
+            ms /= max(cnt, 1)
+            out[f"ours {kind} {layout}"] = {"us": ms * 1e3, "tflops": flops / (ms * 1e-3) / 1e12}
+        del layer, plan
+    for name, fn in (("torch fwd kn", lambda: torch.matmul(X, Wkn, out=Y)),
+                     ("torch fwd nk", lambda: torch.matmul(X, Wnk.t(), out=Y)),
+                     ("torch dx kn", lambda: torch.matmul(dY, Wkn.t(), out=dX)),
+                     ("torch dx nk", lambda: torch.matmul(dY, Wnk, out=dX))):
+        ms = ev(fn)
+        out[name] = {"us": ms * 1e3, "tflops": flops / (ms * 1e-3) / 1e12}
+    return {"shape": f"{T}x{p.d_in}x{p.d_out}", "results": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,6 +388,9 @@ def main():
     ap.add_argument("--cost-table", action="store_true",
                     help="only measure the kernel cost table T(rank, tokens, hidden) of single-adapter "
                          "layers and print it as one JSON line")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the base GEMM launches of the workload's first projection in both W0 "
+                         "layouts beside torch.matmul (hipBLASLt) on the same products; one JSON line")
     ap.add_argument("--packing-sweep", action="store_true",
                     help="only run the packed-against-sequential sweep over Table 7's shapes and "
                          "print its results as one JSON line")
@@ -363,6 +423,13 @@ def main():
                           "steps": steps, "data": "synthetic", "results": rows}), flush=True)
         return
     w = load_workload(a.workload, a.seed)
+    if a.vendor_gemm:
+        steps = min(a.steps, 30)
+        r = vendor_gemm(w, steps, min(a.warmup, 5))
+        print(json.dumps({"metric": "base GEMM time per launch, library and torch.matmul", "unit": "us",
+                          "workload": w.name, "steps": steps, "data": "synthetic", "dtype": "bf16", **r}),
+              flush=True)
+        return
     if a.fused:
         a.all_projections, a.no_sequential = True, True
     mx = a.w0_format == "mxfp8"
