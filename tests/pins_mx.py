@@ -13,6 +13,17 @@ than itself.
   weight for transposed codes;
 - torch float64 decoding and matmul of a small quantized layer against the
   oracle's decoded weight fed to the plain layer oracle.
+MXFP4 (torch has no FP4 decoder, so these rest on the format's definition
+worked by hand):
+- all sixteen E2M1 codes: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives
+  (code 8 is negative zero);
+- the nibble order: the even element of a pair in the low four bits;
+- dequantization of both layouts element by element against the hand
+  table times the block's scale, and the two layouts against each other;
+- 1.5 x 2^127 stays exact, 6 x 2^127 becomes bf16 infinity (anything from
+  2^128 up overflows), a scale code of 255 is NaN;
+- a small layer decoded with the hand table in torch float64 against the
+  oracle's weight fed to the plain layer oracle.
 """
 from __future__ import annotations
 
@@ -88,5 +99,75 @@ def pin_layer_vs_torch(om):
     assert np.allclose(Y, Yt, rtol=0, atol=1e-12 * max(1.0, np.abs(Yt).max())), "decoded layer differs from torch"
 
 
+# E2M1 codes 0..15 by hand: S.EE.M, bias 1
+E2M1_HAND = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def _pack4(codes):
+    """[rows][cols] codes 0..15 -> [rows][cols/2] bytes, even element low."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def pin_e2m1_hand_table(om):
+    got = om.decode_e2m1(np.arange(16, dtype=np.uint8))
+    assert np.array_equal(got, np.asarray(E2M1_HAND)), got
+    assert np.array_equal(np.signbit(got), np.arange(16) >= 8), "sign is bit 3"
+
+
+def pin_e2m1_nibble_order(om):
+    # byte 0x21: low nibble 1 (0.5) first, high nibble 2 (1.0) second; 0xF7: 6.0 then -6.0
+    codes = om.unpack_e2m1(np.asarray([[0x21, 0xF7]], dtype=np.uint8), 1, 4)
+    assert np.array_equal(om.decode_e2m1(codes)[0], [0.5, 1.0, 6.0, -6.0]), codes
+    d_in, d_out = 32, 4
+    w = om.dequant_w0(np.full((d_in, d_out // 2), 0x21, np.uint8), np.full((d_out, 1), 127, np.uint8),
+                      d_in, d_out, "kn", fmt="mxfp4")
+    assert np.array_equal(ol.as_f64(w, "bf16")[0], [0.5, 1.0, 0.5, 1.0]), "columns of a KN row pair up"
+
+
+def pin_mxfp4_blocks_and_layouts(om):
+    rng = np.random.default_rng(3)
+    d_in, d_out = 96, 8
+    codes = rng.integers(0, 16, size=(d_in, d_out), dtype=np.uint8)     # [k][n]
+    scales = rng.integers(118, 132, size=(d_out, d_in // 32), dtype=np.uint8)
+    w = ol.as_f64(om.dequant_w0(_pack4(codes), scales, d_in, d_out, "kn", fmt="mxfp4"), "bf16")
+    for n in range(d_out):
+        for k in range(d_in):
+            assert w[k, n] == E2M1_HAND[codes[k, n]] * 2.0 ** (int(scales[n, k // 32]) - 127), (k, n)
+    w_nk = ol.as_f64(om.dequant_w0(_pack4(codes.T), scales, d_in, d_out, "nk", fmt="mxfp4"), "bf16")
+    assert np.array_equal(w, w_nk), "layouts disagree"
+
+
+def pin_mxfp4_overflow_and_nan(om):
+    d_in, d_out = 32, 2
+    codes = np.zeros((d_in, d_out), dtype=np.uint8)
+    codes[0] = [7, 15]                       # 6, -6
+    codes[1] = [3, 1]                        # 1.5, 0.5
+    w = om.dequant_w0(_pack4(codes), np.asarray([[254], [254]], np.uint8), d_in, d_out, "kn", fmt="mxfp4")
+    assert int(w[0, 0]) == 0x7F80 and int(w[0, 1]) == 0xFF80, "6 x 2^127 is beyond bf16: infinity"
+    assert int(w[1, 0]) == 0x7F40 and int(w[1, 1]) == 0x7E80, "1.5 x 2^127 and 0.5 x 2^127 are exact"
+    wn = om.dequant_w0(_pack4(codes), np.asarray([[255], [127]], np.uint8), d_in, d_out, "kn", fmt="mxfp4")
+    f = ol.as_f64(wn, "bf16")
+    assert np.all(np.isnan(f[:, 0])) and not np.any(np.isnan(f[:, 1])), "scale 255 is NaN for its block only"
+
+
+def pin_mxfp4_layer_vs_torch(om):
+    import torch
+    rng = np.random.default_rng(4)
+    d_in, d_out, T = 64, 16, 5
+    codes = rng.integers(0, 16, size=(d_in, d_out), dtype=np.uint8)
+    scales = rng.integers(120, 128, size=(d_out, d_in // 32), dtype=np.uint8)
+    X = rng.standard_normal((T, d_in))
+    table = torch.tensor(E2M1_HAND, dtype=torch.float64)
+    tq = table[torch.from_numpy(codes.astype(np.int64))]
+    ts = torch.from_numpy(2.0 ** (scales.astype(np.float64) - 127)).T.repeat_interleave(32, dim=0)
+    Yt = (torch.from_numpy(X) @ (tq * ts)).numpy()
+    W = om.dequant_w0(_pack4(codes), scales, d_in, d_out, "kn", fmt="mxfp4")
+    Y, _ = ol.forward(X, ol.as_f64(W, "bf16"), [np.zeros((d_in, 1))], [np.zeros((1, d_out))], [1.0], [0, T],
+                      "fp32")
+    assert np.allclose(Y, Yt, rtol=0, atol=1e-12 * max(1.0, np.abs(Yt).max())), "decoded layer differs from torch"
+
+
 ALL_PINS = [pin_e4m3_table_vs_torch, pin_e4m3_hand_codes, pin_e8m0, pin_round_bf16,
-            pin_dequant_blocks_and_layouts, pin_layer_vs_torch]
+            pin_dequant_blocks_and_layouts, pin_layer_vs_torch, pin_e2m1_hand_table, pin_e2m1_nibble_order,
+            pin_mxfp4_blocks_and_layouts, pin_mxfp4_overflow_and_nan, pin_mxfp4_layer_vs_torch]

@@ -95,6 +95,13 @@ MX_MUTATIONS = {
                            "w = q * np.repeat(np.repeat(sc.T[:1], d_in, axis=0)[:, :1], d_out, axis=1)"),
     "nk_not_transposed": ("    if layout != \"kn\":\n        q = q.T", "    if layout != \"kn\":\n        q = q.reshape(d_in, d_out)"),
     "sign_dropped": ("s = np.where(c >> 7, -1.0, 1.0)", "s = np.where(c >> 7, 1.0, 1.0)"),
+    "e2m1_sign_bit_2": ("s = np.where(c >> 3, -1.0, 1.0)", "s = np.where((c >> 2) & 1, -1.0, 1.0)"),
+    "e2m1_bias_2": ("(2 + m) * np.exp2(e - 2.0)", "(2 + m) * np.exp2(e - 3.0)"),
+    "e2m1_subnormal_as_one": ("np.where(e == 0, 0.5 * m,", "np.where(e == 0, 1.0 * m,"),
+    "e2m1_nibbles_swapped": ("    out[:, 0::2] = b & 15\n    out[:, 1::2] = b >> 4",
+                             "    out[:, 0::2] = b >> 4\n    out[:, 1::2] = b & 15"),
+    "e2m1_mantissa_weight": ("(2 + m) * np.exp2", "(2 + 2 * m) * np.exp2"),
+    "mxfp4_decoded_as_fp8": ("    if fmt == \"mxfp4\":", "    if fmt == \"mxfp4-never\":"),
 }
 
 
