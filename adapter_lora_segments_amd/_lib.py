@@ -12,7 +12,7 @@ STATUS = {0: "MLORA_OK", -1: "MLORA_ERR_INVALID_ARG", -2: "MLORA_ERR_UNSUPPORTED
           -3: "MLORA_ERR_HIP", -4: "MLORA_ERR_WORKSPACE", -5: "MLORA_ERR_NOMEM"}
 DTYPES = {"fp32": 0, "bf16": 1}
 W0_LAYOUTS = {"kn": 0, "nk": 1}
-W0_FORMATS = {"bf16": 0, "mxfp8": 1}
+W0_FORMATS = {"bf16": 0, "mxfp8": 1, "mxfp4": 2}
 
 TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
           "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count", "tiles", "tile_start", "ext",

@@ -221,12 +221,14 @@ def _w0_shape(plan):
     i = plan.info
     if plan.w0_format == "mxfp8":  # element codes, then the block scale codes
         return (i["d_in"] * i["d_out"] + i["d_out"] * (i["d_in"] // 32),)
+    if plan.w0_format == "mxfp4":  # element codes two to a byte, then the block scale codes
+        return (i["d_in"] * i["d_out"] // 2 + i["d_out"] * (i["d_in"] // 32),)
     return (i["d_in"], i["d_out"]) if plan.w0_layout == "kn" else (i["d_out"], i["d_in"])
 
 
 def _w0_dtype(plan):
     torch = _torch()
-    return torch.uint8 if plan.w0_format == "mxfp8" else _dt(plan)
+    return torch.uint8 if plan.w0_format in ("mxfp8", "mxfp4") else _dt(plan)
 
 
 def mlora_forward(plan: Plan, X, W0, A_ptrs, B_ptrs, scales, Y, Z, ws, stream=None):

@@ -228,6 +228,20 @@ mlora_status check_ws(const mlora_plan_s* p, void* ws, size_t ws_bytes) {
 
 }  // namespace
 
+// Decode of an MXFP8 or MXFP4 base (codes, then the E8M0 scales) into the
+// workspace's bf16 copy, in the base's layout.
+mlora_status decode_base(mlora_plan_s* p, const void* W0, uint8_t* wsb, bool nk, hipStream_t cs) {
+  const auto& P = p->P;
+  const uint8_t* codes = static_cast<const uint8_t*>(W0);
+  uint16_t* w0deq = reinterpret_cast<uint16_t*>(wsb + p->L.w0deq);
+  const bool fp4 = P.opts.w0_format == MLORA_W0_MXFP4;
+  const int64_t code_bytes = fp4 ? P.d_in * P.d_out / 2 : P.d_in * P.d_out;
+  return timed(p, MLORA_K_DEQUANT, cs, [&] {
+    if (fp4) mlora::launch_dequant_mx4(nk, codes, codes + code_bytes, P.d_in, P.d_out, w0deq, cs);
+    else mlora::launch_dequant_mx(nk, codes, codes + code_bytes, P.d_in, P.d_out, w0deq, cs);
+  });
+}
+
 extern "C" {
 
 const char* mlora_version(void) { return "mlora 0.1 gfx950"; }
@@ -469,16 +483,12 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     });
   }
 
-  // An MXFP8 base is decoded into the workspace first; the GEMMs read that.
+  // A microscaled base is decoded into the workspace first; the GEMMs read that.
   const uint16_t* W0b = static_cast<const uint16_t*>(W0);
-  if (P.opts.w0_format == MLORA_W0_MXFP8) {
-    const uint8_t* codes = static_cast<const uint8_t*>(W0);
-    uint16_t* w0deq = reinterpret_cast<uint16_t*>(wsb + L.w0deq);
-    st = timed(p, MLORA_K_DEQUANT, cs, [&] {
-      mlora::launch_dequant_mx(nk, codes, codes + P.d_in * P.d_out, P.d_in, P.d_out, w0deq, cs);
-    });
+  if (P.opts.w0_format != MLORA_W0_BF16) {
+    st = decode_base(p, W0, wsb, nk, cs);
     if (st != MLORA_OK) return st;
-    W0b = w0deq;
+    W0b = reinterpret_cast<const uint16_t*>(wsb + L.w0deq);
   }
   // A_cat^T feeds the shrink; with W0 as [d_out][d_in] the expand steps read
   // B in k-contiguous form, B_cat^T.
@@ -592,16 +602,12 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     });
     if (st != MLORA_OK) return st;
   }
-  // dX reads the base weight; an MXFP8 base is decoded into the workspace.
+  // dX reads the base weight; a microscaled base is decoded into the workspace.
   const uint16_t* W0b = static_cast<const uint16_t*>(W0);
-  if (dX && P.opts.w0_format == MLORA_W0_MXFP8) {
-    const uint8_t* codes = static_cast<const uint8_t*>(W0);
-    uint16_t* w0deq = reinterpret_cast<uint16_t*>(wsb + L.w0deq);
-    st = timed(p, MLORA_K_DEQUANT, cs, [&] {
-      mlora::launch_dequant_mx(nk, codes, codes + P.d_in * P.d_out, P.d_in, P.d_out, w0deq, cs);
-    });
+  if (dX && P.opts.w0_format != MLORA_W0_BF16) {
+    st = decode_base(p, W0, wsb, nk, cs);
     if (st != MLORA_OK) return st;
-    W0b = w0deq;
+    W0b = reinterpret_cast<const uint16_t*>(wsb + L.w0deq);
   }
   if (dX) {
     st = ensure_wg_streams(p);

@@ -113,6 +113,10 @@ void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s
 // nearest-even bf16.
 void launch_dequant_mx(bool nk, const uint8_t* codes, const uint8_t* scales, int64_t d_in,
                        int64_t d_out, uint16_t* out, hipStream_t s);
+// MXFP4 base weight -> bf16: codes [d_in][d_out / 2] (nk: [d_out][d_in / 2])
+// E2M1, two per byte along the row (even element low), scales as above.
+void launch_dequant_mx4(bool nk, const uint8_t* codes, const uint8_t* scales, int64_t d_in,
+                        int64_t d_out, uint16_t* out, hipStream_t s);
 
 // ---------------- fp32 path (vector ALU) ----------------
 void launch_f32_shrink(const DevTables& t, int32_t n, int64_t T, int64_t d_in, const float* X,

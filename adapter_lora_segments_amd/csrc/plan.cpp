@@ -151,12 +151,12 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
     err = "w0_layout must be MLORA_W0_KN or MLORA_W0_NK";
     return MLORA_ERR_INVALID_ARG;
   }
-  if (o.w0_format != MLORA_W0_BF16 && o.w0_format != MLORA_W0_MXFP8) {
-    err = "w0_format must be MLORA_W0_BF16 or MLORA_W0_MXFP8";
+  if (o.w0_format != MLORA_W0_BF16 && o.w0_format != MLORA_W0_MXFP8 && o.w0_format != MLORA_W0_MXFP4) {
+    err = "w0_format must be MLORA_W0_BF16, MLORA_W0_MXFP8 or MLORA_W0_MXFP4";
     return MLORA_ERR_INVALID_ARG;
   }
-  if (o.w0_format == MLORA_W0_MXFP8 && dtype != MLORA_BF16) {
-    err = "an MXFP8 base weight needs a bf16 plan";
+  if (o.w0_format != MLORA_W0_BF16 && dtype != MLORA_BF16) {
+    err = "a microscaled (MXFP8/MXFP4) base weight needs a bf16 plan";
     return MLORA_ERR_UNSUPPORTED;
   }
 
@@ -420,7 +420,7 @@ DeviceLayout device_layout(const PlanTables& p) {
   }
   L.dz = take((size_t)p.z_elems * esz);
   L.kpart = take((size_t)p.kpart_off.back() * 4);
-  L.w0deq = take(p.opts.w0_format == MLORA_W0_MXFP8 ? (size_t)p.d_in * (size_t)p.d_out * 2 : 0);
+  L.w0deq = take(p.opts.w0_format != MLORA_W0_BF16 ? (size_t)p.d_in * (size_t)p.d_out * 2 : 0);
   // gradient clipping: one partial square sum per optimizer work item, then
   // one clip factor per pair
   L.gnorm = take(4 * ((size_t)p.n_oblk() + (size_t)p.nv()));

@@ -59,7 +59,7 @@ def measured_traffic(workload: str):
     return int(v) if v else None
 
 
-def kernel_rooflines(w, units, kern, iso, steps):
+def kernel_rooflines(w, units, kern, iso, steps, w0_format="bf16"):
     """Achieved rate of every step of the path against its roofline, from the
     per-kernel pass (the weight-gradient kernels from the isolated pass,
     where they do not share the chip with the dX GEMM).  Algorithmic bytes
@@ -97,8 +97,11 @@ def kernel_rooflines(w, units, kern, iso, steps):
                       "frac": ach / PEAK_BF16_TFLOPS, "ms_per_step": ms}
     out["gemm_dx"]["note"] = "timed beside the concurrent weight-gradient kernels"
     if kern.get("dequant", (0.0, 0))[1]:
-        # MXFP8 base: codes (1 B) and scales (1/32 B) read, bf16 (2 B) written per weight, twice a step
-        byt = sum(2 * (1 + 1 / 32 + 2) * w.projections[q[0]].d_in * w.projections[q[0]].d_out for q in units)
+        # microscaled base: codes (1 B for MXFP8, 0.5 B for MXFP4) and scales (1/32 B) read, bf16 (2 B)
+        # written per weight, twice a step
+        code_b = 0.5 if w0_format == "mxfp4" else 1.0
+        byt = sum(2 * (code_b + 1 / 32 + 2) * w.projections[q[0]].d_in * w.projections[q[0]].d_out
+                  for q in units)
         ms = kern["dequant"][0] / steps
         ach = byt / (ms * 1e-3) / 1e9
         out["dequant"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -377,9 +380,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="time the whole layer with the projections that share an input fused into one "
                          "packed layer each (q/k/v, gate/up: mlora_plan_multi); implies --all-projections")
-    ap.add_argument("--w0-format", default="bf16", choices=["bf16", "mxfp8"],
-                    help="store the frozen base in MXFP8 (E4M3 codes, E8M0 scales per 32 inputs; decoded "
-                         "per call); implies --no-sequential")
+    ap.add_argument("--w0-format", default="bf16", choices=["bf16", "mxfp8", "mxfp4"],
+                    help="store the frozen base in MXFP8 (E4M3 codes) or MXFP4 (E2M1 codes, two per byte), "
+                         "with E8M0 scales per 32 inputs, decoded per call; implies --no-sequential")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the same steps replayed from a captured HIP graph (one-group plans)")
     ap.add_argument("--optimizer-only", action="store_true",
@@ -404,7 +407,7 @@ def main():
     from adapter_lora_segments_amd import Plan, PackedLoRALinear, device_check
     from workloads import load_workload
     from workloads.multi import LAYER_GROUPS, device_multi
-    from workloads.mx import quantize_mx_device
+    from workloads.mx import quantize_mx_device, quantize_mx4_device
     from workloads.tensors import device_tensors
 
     torch.cuda.set_device(0)
@@ -432,11 +435,11 @@ def main():
         return
     if a.fused:
         a.all_projections, a.no_sequential = True, True
-    mx = a.w0_format == "mxfp8"
+    mx = a.w0_format in ("mxfp8", "mxfp4")
     if mx:
         a.no_sequential = True
         if a.fused or a.shuffled_ids:
-            print("--w0-format mxfp8 runs with segment plans of single projections", file=sys.stderr)
+            print(f"--w0-format {a.w0_format} runs with segment plans of single projections", file=sys.stderr)
             sys.exit(2)
     projs = list(range(len(w.projections))) if a.all_projections else [0]
     SETS = 4
@@ -468,7 +471,7 @@ def main():
                         n_streams=a.streams or w.n_streams, w0_format=a.w0_format)
         W0 = d["W0"]
         if mx:
-            W0 = quantize_mx_device(d["W0"], "kn")
+            W0 = (quantize_mx4_device if a.w0_format == "mxfp4" else quantize_mx_device)(d["W0"], "kn")
             d["W0_bytes"] = W0.numel()
         layer = PackedLoRALinear(plan, W0, d["A"], d["B"], d["scales"])
         Ys = [torch.empty((w.T, p.d_out), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
@@ -642,7 +645,7 @@ def main():
     if kern:
         out["kernels_ms_per_step"] = {k: v[0] / a.steps for k, v in kern.items() if v[1]}
         units = [gp for _, gp in groups] if groups else [[q] for q in projs]
-        out["kernel_rooflines"] = kernel_rooflines(w, units, kern, iso, a.steps)
+        out["kernel_rooflines"] = kernel_rooflines(w, units, kern, iso, a.steps, a.w0_format)
     if prof:
         g_ms, g_n = gemm_rec
         if g_n:

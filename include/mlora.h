@@ -83,7 +83,7 @@ typedef enum {
 
 typedef enum { MLORA_FP32 = 0, MLORA_BF16 = 1 } mlora_dtype;
 typedef enum { MLORA_W0_KN = 0, MLORA_W0_NK = 1 } mlora_w0_layout;
-typedef enum { MLORA_W0_BF16 = 0, MLORA_W0_MXFP8 = 1 } mlora_w0_format;
+typedef enum { MLORA_W0_BF16 = 0, MLORA_W0_MXFP8 = 1, MLORA_W0_MXFP4 = 2 } mlora_w0_format;
 
 #define MLORA_MAX_RANK 256
 #define MLORA_MAX_ADAPTERS 65536
@@ -99,7 +99,7 @@ typedef struct {
   int32_t chunk_max;      /*   max(chunk_min, chunk_per_rank * r_pad(i)));                  */
   int32_t chunk_per_rank; /*   defaults 256, 2048, 8                                        */
   int32_t w0_layout;      /* mlora_w0_layout; default MLORA_W0_KN                          */
-  int32_t w0_format;      /* mlora_w0_format; default MLORA_W0_BF16 (MXFP8: bf16 plans only) */
+  int32_t w0_format;      /* mlora_w0_format; default MLORA_W0_BF16 (MXFP8, MXFP4: bf16 plans only) */
 } mlora_plan_opts;
 
 typedef struct mlora_plan_s *mlora_plan_t;
@@ -287,6 +287,14 @@ mlora_status mlora_plan_upload(mlora_plan_t plan, void *workspace, size_t ws_byt
  * the workspace (2 * d_in * d_out bytes, counted in workspace_bytes) with
  * one HBM-bound kernel (MLORA_K_DEQUANT), then run the bf16 path.  The
  * resident base takes 1 + 1/32 bytes per weight instead of 2.
+ *
+ * A 4-bit base (QLoRA's setting in §11.3 of the page), taken as MXFP4
+ * (w0_format = MLORA_W0_MXFP4): the same except that the elements are E2M1
+ * codes (OCP FP4: S.EE.M, bias 1, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, no
+ * NaN or infinity), two to a byte along the rows of the layout with the
+ * even element in the low four bits: d_in * d_out / 2 code bytes, the scale
+ * codes following at that byte offset.  Products from 2^128 up decode to
+ * infinity.  The resident base takes 0.5 + 1/32 bytes per weight.
  */
 
 /*
@@ -384,7 +392,7 @@ typedef enum {
   MLORA_K_GEMM_DX,       /* dX = dY W0^T + dZ A^T (B4)                       */
   MLORA_K_PREP,          /* rank-padded concatenations of A and B            */
   MLORA_K_ADAMW,         /* per-adapter AdamW step (mlora_adamw_step)        */
-  MLORA_K_DEQUANT,       /* decode of an MXFP8 base weight into bf16         */
+  MLORA_K_DEQUANT,       /* decode of an MXFP8/MXFP4 base weight into bf16   */
   MLORA_K_GRAD_NORM,     /* per-adapter gradient norms and clip factors      */
   MLORA_K_COUNT
 } mlora_kernel_kind;

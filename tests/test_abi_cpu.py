@@ -358,6 +358,51 @@ def test_mxfp8_plan_options():
         assert np.array_equal(p_mx.export(name), p_bf.export(name)), name
 
 
+def test_mxfp4_plan_options():
+    """An MXFP4 base needs a bf16 plan, counts the same decoded copy in the
+    workspace as MXFP8, and takes half a byte per code then the scales."""
+    from adapter_lora_segments_amd.binding import _w0_shape, _w0_dtype
+    p8 = Plan([0, 5, 9], [4, 8], 128, 192, w0_format="mxfp8")
+    p4 = Plan([0, 5, 9], [4, 8], 128, 192, w0_format="mxfp4", w0_layout="nk")
+    assert p4.info["workspace_bytes"] == p8.info["workspace_bytes"]
+    assert _w0_shape(p4) == (128 * 192 // 2 + 192 * 4,)
+    import torch
+    assert _w0_dtype(p4) == torch.uint8
+    assert _status(lambda: Plan([0, 5, 9], [4, 8], 128, 192, "fp32", w0_format="mxfp4")) == -2
+    o = _lib.PlanOpts()
+    o.w0_format = 3
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    off = (ctypes.c_int64 * 3)(0, 5, 9)
+    rk = (ctypes.c_int32 * 2)(4, 8)
+    assert L.mlora_plan(2, off, rk, 128, 192, 0, ctypes.byref(o), ctypes.byref(h)) == -1
+    assert "MXFP4" in L.mlora_last_error().decode()
+
+
+def test_mx4_quantizer_round_trip():
+    """The MXFP4 input quantizer against the oracle's decoder: every weight
+    decodes to the nearest E2M1 value of its scaled magnitude (ties low), with
+    the weight's sign, and no block overflows."""
+    from oracle import mx as omx
+    from workloads.mx import quantize_mx4, E2M1_MAGNITUDES
+    rng = np.random.default_rng(1)
+    w = rng.standard_normal((128, 64)) * 0.02
+    w[7, 2] = 0.0
+    mags = np.asarray(E2M1_MAGNITUDES)
+    for layout in ("kn", "nk"):
+        codes, scales = quantize_mx4(w, layout)
+        rows, cols = (128, 64) if layout == "kn" else (64, 128)
+        assert codes.shape == (rows, cols // 2) and scales.shape == (64, 4)
+        dec = omx.decode_e2m1(omx.unpack_e2m1(codes, rows, cols))
+        if layout == "nk":
+            dec = dec.T
+        sc = omx.decode_e8m0(scales).T.repeat(32, axis=0)
+        q = w / sc
+        assert np.all(np.abs(q) <= 6.0 + 1e-12)
+        want = mags[np.argmin(np.abs(np.abs(q)[..., None] - mags), axis=-1)] * np.sign(q)
+        assert np.array_equal(dec, want)
+
+
 def test_mx_quantizer_round_trip():
     """The input quantizer (workloads/mx.py) against the oracle's decoder:
     every decoded weight is within half an E4M3 step of the float weight, and

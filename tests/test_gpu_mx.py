@@ -1,4 +1,4 @@
-"""Frozen base in MXFP8 (w0_format = mxfp8) on the GPU.
+"""Frozen base in MXFP8 or MXFP4 (w0_format = mxfp8 / mxfp4) on the GPU.
 
 - The layer with an MXFP8 base is bit-identical, in Y, dX, dA, dB and Z', to
   the bf16 layer whose W0 is the oracle's decoding of the same codes
@@ -7,14 +7,17 @@
   codes cover the whole E4M3 range, subnormals and negative zero included.
 - Against the layer oracle on the decoded weight, within the bf16 bar.
 - The bench layer (4096x4096, four adapters) at full size, bitwise against
-  the decoded-weight bf16 layer."""
+  the decoded-weight bf16 layer.
+- MXFP4 the same way: all sixteen E2M1 codes in both layouts, bitwise
+  against the decoded-weight layer and within the bar of the oracle, and
+  the bench layer at full size."""
 import numpy as np
 import pytest
 
 from oracle import lora as ol
 from oracle import mx as omx
 from tests.gpu_harness import TOL, custom_workload, say, to_dev, to_host_f64
-from workloads.mx import pack, quantize_mx
+from workloads.mx import pack, pack_e2m1, quantize_mx, quantize_mx4
 from workloads.tensors import host_tensors
 
 
@@ -136,3 +139,62 @@ def test_mx_base_with_projections_sharing_the_input():
             errs[f"dB{i},{q}"] = ol.max_rel_err(to_host_f64(layer.dB[3 * i + q]), dBo[i][q])
     say(f"  worst {max(errs.items(), key=lambda kv: kv[1])}")
     assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("layout,d_in,d_out,ranks,tokens", CASES)
+def test_mx4_base_bitwise_and_oracle(layout, d_in, d_out, ranks, tokens):
+    import torch
+    from adapter_lora_segments_amd import Plan
+    say(f"case mxfp4 base {layout} {d_in}x{d_out} ranks {ranks} tokens {tokens}")
+    w = custom_workload("mx4", "bf16", d_in, d_out, ranks, tokens, seed=14)
+    h = host_tensors(w, 0)
+    rng = np.random.default_rng(15)
+    codes_kn = rng.integers(0, 16, size=(d_in, d_out), dtype=np.uint8)       # every E2M1 code, -0 included
+    scales = rng.integers(116, 128, size=(d_out, d_in // 32), dtype=np.uint8)
+    codes = pack_e2m1(codes_kn if layout == "kn" else codes_kn.T)
+    Wdec = omx.dequant_w0(codes, scales, d_in, d_out, layout, fmt="mxfp4")   # bf16 bits [d_in][d_out]
+    off = h["offsets"]
+    p4 = Plan(off, h["ranks"], d_in, d_out, "bf16", w0_layout=layout, w0_format="mxfp4")
+    p_bf = Plan(off, h["ranks"], d_in, d_out, "bf16", w0_layout=layout)
+    p4.profile_enable(["dequant"])
+    p4.profile_read()
+    out4 = _run(p4, torch.from_numpy(pack(codes, scales)).cuda(), h)
+    assert p4.profile_read()["dequant"][1] == 2, "one decode in forward, one in the backward's dX"
+    p4.profile_enable(False)
+    out_bf = _run(p_bf, to_dev(Wdec if layout == "kn" else np.ascontiguousarray(Wdec.T), "bf16"), h)
+    for k in ("Y", "dX", "Z"):
+        assert np.array_equal(out4[k], out_bf[k]), f"{k} differs from the decoded-weight bf16 layer"
+    for i in range(len(ranks)):
+        assert np.array_equal(out4["dA"][i], out_bf["dA"][i]) and np.array_equal(out4["dB"][i], out_bf["dB"][i])
+    Yo, _ = ol.forward(h["X"], Wdec, h["A"], h["B"], h["scales"], off, "bf16")
+    dXo, dAo, dBo, _ = ol.backward(h["dY"], h["X"], Wdec, h["A"], h["B"], h["scales"], off, "bf16")
+    errs = {"Y": ol.max_rel_err(out4["Y"], Yo), "dX": ol.max_rel_err(out4["dX"], dXo)}
+    for i in range(len(ranks)):
+        errs[f"dA{i}"] = ol.max_rel_err(out4["dA"][i], dAo[i])
+        errs[f"dB{i}"] = ol.max_rel_err(out4["dB"][i], dBo[i])
+    say(f"  bitwise equal to the decoded-weight layer; oracle worst {max(errs.items(), key=lambda kv: kv[1])}")
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_mx4_base_bench_layer_full_size(layout):
+    import torch
+    from adapter_lora_segments_amd import Plan
+    from workloads import load_workload
+    w = load_workload("llama7b_proj", 0)
+    p = w.projections[0]
+    say(f"case mxfp4 base full size {layout} {p.d_in}x{p.d_out}, ranks {w.ranks}, T={w.T}")
+    h = host_tensors(w, 0)
+    wf = ol.as_f64(h["W0"], "bf16")
+    codes, scales = quantize_mx4(wf, layout)
+    Wdec = omx.dequant_w0(codes, scales, p.d_in, p.d_out, layout, fmt="mxfp4")
+    p4 = Plan(h["offsets"], h["ranks"], p.d_in, p.d_out, "bf16", w0_layout=layout, w0_format="mxfp4")
+    p_bf = Plan(h["offsets"], h["ranks"], p.d_in, p.d_out, "bf16", w0_layout=layout)
+    out4 = _run(p4, torch.from_numpy(pack(codes, scales)).cuda(), h)
+    out_bf = _run(p_bf, to_dev(Wdec if layout == "kn" else np.ascontiguousarray(Wdec.T), "bf16"), h)
+    for k in ("Y", "dX"):
+        assert np.array_equal(out4[k], out_bf[k]), k
+    for i in range(w.n):
+        assert np.array_equal(out4["dA"][i], out_bf["dA"][i]) and np.array_equal(out4["dB"][i], out_bf["dB"][i])

@@ -5,7 +5,8 @@ Each case draws (from its own seed) a dtype, a W0 layout, a stream count,
 segments), dimensions that are multiples of 64 (from 64 to 1536, so that
 some GEMM launches split K and some do not), and one of five plan kinds:
 segments, per-token ids in a shuffled order, several projections sharing
-the input (with segments or with shuffled ids), or an MXFP8 base.  Every output is compared with the oracle at
+the input (with segments or with shuffled ids), or a microscaled base
+(MXFP8 and MXFP4 in turn).  Every output is compared with the oracle at
 the dtype's bar: Y, dX, every dA_i and dB_i, and the saved activation Z'
 (padding columns exactly zero)."""
 import numpy as np
@@ -16,7 +17,7 @@ from oracle import multi as om
 from oracle import mx as omx
 from tests.gpu_harness import TOL, custom_workload, say, to_dev, to_host_f64
 from workloads.multi import host_multi
-from workloads.mx import pack, quantize_mx
+from workloads.mx import pack, quantize_mx, quantize_mx4
 from workloads.tensors import host_tensors
 
 N_CASES = 80
@@ -39,8 +40,9 @@ def draw_case(seed):
     if kind in ("multi", "multi_ids"):
         unit = 256 if dt == "bf16" else 64
         widths = [unit * int(g.integers(1, 4)) for _ in range(int(g.integers(2, 4)))]
+    fmt = ("mxfp4" if (seed // 5) % 2 else "mxfp8") if kind == "mxfp8" else "bf16"
     return dict(kind=kind, dt=dt, ranks=ranks, tokens=tokens, d_in=d_in, d_out=d_out, layout=layout,
-                streams=streams, widths=widths, seed=seed)
+                streams=streams, widths=widths, seed=seed, fmt=fmt)
 
 
 def _layer(plan, W0dev, A, B, scales, dt):
@@ -123,10 +125,11 @@ def test_sweep(seed):
                                  w0_layout=layout)
         else:
             plan = Plan(off, h["ranks"], c["d_in"], c["d_out"], dt, n_streams=c["streams"], w0_layout=layout,
-                        w0_format="mxfp8" if kind == "mxfp8" else "bf16")
+                        w0_format=c["fmt"])
         if kind == "mxfp8":
-            codes, sc = quantize_mx(ol.as_f64(h["W0"], "bf16"), layout)
-            W0o = omx.dequant_w0(codes, sc, c["d_in"], c["d_out"], layout)
+            quant = quantize_mx4 if c["fmt"] == "mxfp4" else quantize_mx
+            codes, sc = quant(ol.as_f64(h["W0"], "bf16"), layout)
+            W0o = omx.dequant_w0(codes, sc, c["d_in"], c["d_out"], layout, fmt=c["fmt"])
             W0dev = torch.from_numpy(pack(codes, sc)).cuda()
         else:
             W0dev = to_dev(h["W0"] if layout == "kn" else np.ascontiguousarray(h["W0"].T), dt)

@@ -103,3 +103,10 @@ def quantize_mx4_device(w_bf16, layout="kn"):
     import torch
     codes, scales = _quantize_mx4(w_bf16.float(), layout)
     return torch.cat([codes.reshape(-1), scales.reshape(-1)])
+
+
+def pack_e2m1(codes):
+    """[rows][cols] E2M1 codes (0..15) -> [rows][cols / 2] bytes, the even
+    element of each pair in the low four bits."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.ascontiguousarray(c[:, 0::2] | (c[:, 1::2] << 4))
