@@ -6,5 +6,6 @@ Importing the binding does not load the library; the first call does, and
 fails loudly if it has not been built.
 """
 from .binding import (Plan, PackedLoRALinear, AdamW, mlora_plan, mlora_forward,  # noqa: F401
-                      mlora_backward, mlora_adamw_step, adamw_hparams, pointer_table, device_check)
+                      mlora_backward, mlora_adamw_step, adamw_hparams, pointer_table, device_check,
+                      base_both, mlora_base_transpose)
 from ._lib import MloraError, lib  # noqa: F401

@@ -11,7 +11,7 @@ MLORA_OK = 0
 STATUS = {0: "MLORA_OK", -1: "MLORA_ERR_INVALID_ARG", -2: "MLORA_ERR_UNSUPPORTED",
           -3: "MLORA_ERR_HIP", -4: "MLORA_ERR_WORKSPACE", -5: "MLORA_ERR_NOMEM"}
 DTYPES = {"fp32": 0, "bf16": 1}
-W0_LAYOUTS = {"kn": 0, "nk": 1}
+W0_LAYOUTS = {"kn": 0, "nk": 1, "both": 2}
 W0_FORMATS = {"bf16": 0, "mxfp8": 1, "mxfp4": 2}
 
 TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
@@ -28,7 +28,7 @@ KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "pre
 EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_multi", "mlora_plan_multi_from_ids", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
            "mlora_plan_upload", "mlora_forward", "mlora_backward", "mlora_adamw_step", "mlora_profile_enable",
            "mlora_profile_read", "mlora_device_check", "mlora_status_string", "mlora_last_error",
-           "mlora_version"]
+           "mlora_version", "mlora_base_transpose"]
 
 
 class PlanOpts(ctypes.Structure):
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.mlora_plan_multi_from_ids.restype = i32
     L.mlora_plan_destroy.argtypes = [vp]
     L.mlora_plan_destroy.restype = None
+    L.mlora_base_transpose.restype = i32
+    L.mlora_base_transpose.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, i32, vp]
     L.mlora_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     L.mlora_plan_get_info.restype = i32
     L.mlora_plan_export.argtypes = [vp, i32, vp, ctypes.POINTER(sz)]

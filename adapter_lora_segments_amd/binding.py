@@ -223,7 +223,31 @@ def _w0_shape(plan):
         return (i["d_in"] * i["d_out"] + i["d_out"] * (i["d_in"] // 32),)
     if plan.w0_format == "mxfp4":  # element codes two to a byte, then the block scale codes
         return (i["d_in"] * i["d_out"] // 2 + i["d_out"] * (i["d_in"] // 32),)
+    if plan.w0_layout == "both":   # [d_in][d_out], then its transpose
+        return (2 * i["d_in"] * i["d_out"],)
     return (i["d_in"], i["d_out"]) if plan.w0_layout == "kn" else (i["d_out"], i["d_in"])
+
+
+def mlora_base_transpose(W, out, stream=None):
+    """out[c][r] = W[r][c] (bf16 or fp32, dimensions multiples of 64), by the
+    library's transpose kernel."""
+    torch = _torch()
+    rows, cols = W.shape
+    dt = _lib.DTYPES["bf16" if W.dtype == torch.bfloat16 else "fp32"]
+    assert W.is_contiguous() and out.is_contiguous() and out.numel() == W.numel() and out.dtype == W.dtype
+    check(lib().mlora_base_transpose(_p(W), _p(out), rows, cols, dt, _stream(stream)))
+    return out
+
+
+def base_both(W0_kn, stream=None):
+    """The two-layout base buffer (MLORA_W0_BOTH) of a [d_in][d_out] weight:
+    the weight, then its transpose [d_out][d_in] built by the library."""
+    torch = _torch()
+    d_in, d_out = W0_kn.shape
+    buf = torch.empty(2 * d_in * d_out, dtype=W0_kn.dtype, device=W0_kn.device)
+    buf[: d_in * d_out].view(d_in, d_out).copy_(W0_kn)
+    mlora_base_transpose(W0_kn.contiguous(), buf[d_in * d_out:], stream)
+    return buf
 
 
 def _w0_dtype(plan):
@@ -315,6 +339,8 @@ class PackedLoRALinear:
     def __init__(self, plan: Plan, W0, A: Sequence, B: Sequence, scales, device="cuda"):
         torch = _torch()
         self.plan = plan
+        if plan.w0_layout == "both" and W0 is not None and W0.dim() == 2:
+            W0 = base_both(W0)          # given as [d_in][d_out]: add its transpose once
         self.W0 = W0
         self.A = list(A)
         self.B = list(B)

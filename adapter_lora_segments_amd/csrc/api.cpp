@@ -469,7 +469,11 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
   if (st != MLORA_OK) return st;
   mlora::DevTables t = dev_tables(p, ws);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
-  const bool nk = P.opts.w0_layout == MLORA_W0_NK;
+  // The forward reads [d_out][d_in] when it has it: the second half of a
+  // two-layout base.
+  const bool nk = P.opts.w0_layout != MLORA_W0_KN;
+  if (P.opts.w0_layout == MLORA_W0_BOTH)
+    W0 = static_cast<const uint8_t*>(W0) + (size_t)P.d_in * (size_t)P.d_out * (P.dtype == MLORA_FP32 ? 4 : 2);
 
   if (P.dtype == MLORA_FP32) {
     st = timed(p, MLORA_K_SHRINK, cs, [&] {
@@ -495,15 +499,10 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
   uint16_t* acat_t = reinterpret_cast<uint16_t*>(wsb + L.acat_t);
   uint16_t* bcat_t = reinterpret_cast<uint16_t*>(wsb + L.bcat_t);
   st = timed(p, MLORA_K_PREP, cs, [&] {
-    mlora::launch_prep_a(t, P.nv(), P.d_in, P.rpad_total, A, acat_t, nullptr, cs);
+    mlora::launch_prep(t, P.nv(), P.d_in, P.d_out, P.rpad_total, A, acat_t, nullptr, B,
+                       nk ? bcat_t : nullptr, cs);
   });
   if (st != MLORA_OK) return st;
-  if (nk) {
-    st = timed(p, MLORA_K_PREP, cs, [&] {
-      mlora::launch_prep_b(t, P.nv(), P.d_out, P.rpad_total, B, bcat_t, cs);
-    });
-    if (st != MLORA_OK) return st;
-  }
   st = fork_groups(p, cs);
   if (st != MLORA_OK) return st;
   for (int g = 0; g < P.n_groups; ++g) {
@@ -562,6 +561,7 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
   if (st != MLORA_OK) return st;
   mlora::DevTables t = dev_tables(p, ws);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
+  // dX reads [d_in][d_out] when it has it: the first half of a two-layout base.
   const bool nk = P.opts.w0_layout == MLORA_W0_NK;
 
   if (P.dtype == MLORA_FP32) {
@@ -769,6 +769,24 @@ mlora_status mlora_device_check(void) {
   if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(MLORA_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", library is built for gfx950");
+  return MLORA_OK;
+}
+
+mlora_status mlora_base_transpose(const void* in, void* out, int64_t rows, int64_t cols,
+                                  mlora_dtype dtype, void* stream) {
+  if (!in || !out || !aligned16(in) || !aligned16(out))
+    return fail(MLORA_ERR_INVALID_ARG, "base_transpose: in and out must be non-NULL and 16-byte aligned");
+  if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % 64 != 0 || rows > (1 << 20) || cols > (1 << 20))
+    return fail(MLORA_ERR_INVALID_ARG, "base_transpose: rows and cols must be positive multiples of 64");
+  if (dtype != MLORA_BF16 && dtype != MLORA_FP32)
+    return fail(MLORA_ERR_INVALID_ARG, "base_transpose: dtype must be MLORA_BF16 or MLORA_FP32");
+  const size_t bytes = (size_t)rows * (size_t)cols * (dtype == MLORA_FP32 ? 4 : 2);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(out);
+  if (a < b + bytes && b < a + bytes) return fail(MLORA_ERR_INVALID_ARG, "base_transpose: in and out overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  mlora::launch_transpose(in, out, rows, cols, dtype == MLORA_FP32 ? 4 : 2, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "base_transpose launch");
   return MLORA_OK;
 }
 

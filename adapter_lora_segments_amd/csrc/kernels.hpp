@@ -46,6 +46,10 @@ void launch_prep_a(const DevTables& t, int32_t n, int64_t d_in, int64_t rtot, co
                    uint16_t* acat_t, uint16_t* acat, hipStream_t s);
 void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
                    const void* const* B, uint16_t* bcat_t, hipStream_t s);
+// Both in one launch; any output NULL is skipped.
+void launch_prep(const DevTables& t, int32_t n, int64_t d_in, int64_t d_out, int64_t rtot,
+                 const void* const* A, uint16_t* acat_t, uint16_t* acat, const void* const* B,
+                 uint16_t* bcat_t, hipStream_t s);
 
 // Skinny products over nano-batches [nano_begin, nano_begin + nano_count) of
 // any padded ranks: out rows of adapter j (r_pad(j) columns)
@@ -107,6 +111,10 @@ struct GemmArgs {
 };
 // main_b_kcontig: Bop element (k, n) at B[n*ldb + k] (else at B[k*ldb + n]).
 void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s);
+
+// out[c][r] = in[r][c], rows x cols elements of `esz` bytes (2 or 4); rows
+// and cols multiples of 64.
+void launch_transpose(const void* in, void* out, int64_t rows, int64_t cols, int esz, hipStream_t s);
 
 // MXFP8 base weight -> bf16, same layout: codes [d_in][d_out] (nk: [d_out]
 // [d_in]) E4M3, scales [d_out][d_in / 32] E8M0; out = element x scale,

@@ -60,12 +60,11 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // 128-byte rows, so both arrive with 16-byte loads into LDS and leave
 // transposed or padded from there.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_prep_a(DevTables t, int32_t n, int64_t d_in,
-                                                int64_t rtot, const void* const* A,
-                                                uint16_t* acat_t, uint16_t* acat) {
-  __shared__ u32x4 tile4[64 * 256 / 8];          // [64][r] bf16, r <= 256
-  const uint16_t* tile = reinterpret_cast<const uint16_t*>(tile4);
-  const int64_t k0 = (int64_t)blockIdx.x * 64;
+// Slab k0 .. k0+63 of A for every adapter (blockIdx.y strides over them).
+__device__ __forceinline__ void prep_a_slab(u32x4* tile4, int64_t k0, const DevTables& t, int32_t n,
+                                            int64_t d_in, int64_t rtot, const void* const* A,
+                                            uint16_t* acat_t, uint16_t* acat) {
+  const uint16_t* tile = reinterpret_cast<const uint16_t*>(tile4);   // [64][r] bf16, r <= 256
   for (int32_t j = blockIdx.y; j < n; j += gridDim.y) {
     const int r = ldc(t.ranks + j), rp = ldc(t.rpad + j), ro = ldc(t.roff + j);
     const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(ldc(A + j)) + k0 * r);
@@ -97,12 +96,10 @@ __global__ __launch_bounds__(256) void k_prep_a(DevTables t, int32_t n, int64_t 
   }
 }
 
-__global__ __launch_bounds__(256) void k_prep_b(DevTables t, int32_t n, int64_t d_out,
-                                                int64_t rtot, const void* const* B,
-                                                uint16_t* bcat_t) {
-  __shared__ u32x4 tile4[256 * 8];               // [r][64] bf16, r <= 256
-  const uint16_t* tile = reinterpret_cast<const uint16_t*>(tile4);
-  const int64_t n0 = (int64_t)blockIdx.x * 64;
+// Slab n0 .. n0+63 of the output columns of B for every adapter.
+__device__ __forceinline__ void prep_b_slab(u32x4* tile4, int64_t n0, const DevTables& t, int32_t n,
+                                            int64_t rtot, const void* const* B, uint16_t* bcat_t) {
+  const uint16_t* tile = reinterpret_cast<const uint16_t*>(tile4);   // [r][64] bf16, r <= 256
   for (int32_t j = blockIdx.y; j < n; j += gridDim.y) {
     // pair j's projection owns output columns [c0, c0 + w): other slabs skip it
     const int pq = j % t.nproj;
@@ -123,16 +120,36 @@ __global__ __launch_bounds__(256) void k_prep_b(DevTables t, int32_t n, int64_t 
   }
 }
 
+// One launch for whichever concatenations a call needs: blocks x < d_in/64
+// take A slabs, the rest (when bcat_t is set) B slabs.
+__global__ __launch_bounds__(256) void k_prep(DevTables t, int32_t n, int64_t d_in, int64_t d_out,
+                                              int64_t rtot, const void* const* A, uint16_t* acat_t,
+                                              uint16_t* acat, const void* const* B, uint16_t* bcat_t) {
+  __shared__ u32x4 tile4[2048];                  // 32 KiB: [64][r] or [r][64] bf16, r <= 256
+  const int64_t na = (acat_t || acat) ? d_in / 64 : 0;
+  if ((int64_t)blockIdx.x < na)
+    prep_a_slab(tile4, (int64_t)blockIdx.x * 64, t, n, d_in, rtot, A, acat_t, acat);
+  else
+    prep_b_slab(tile4, ((int64_t)blockIdx.x - na) * 64, t, n, rtot, B, bcat_t);
+}
+
+void launch_prep(const DevTables& t, int32_t n, int64_t d_in, int64_t d_out, int64_t rtot,
+                 const void* const* A, uint16_t* acat_t, uint16_t* acat, const void* const* B,
+                 uint16_t* bcat_t, hipStream_t s) {
+  const int64_t na = (acat_t || acat) ? d_in / 64 : 0, nb = bcat_t ? d_out / 64 : 0;
+  if (na + nb == 0) return;
+  dim3 grid((unsigned)(na + nb), (unsigned)(n < 65535 ? n : 65535));
+  hipLaunchKernelGGL(k_prep, grid, dim3(256), 0, s, t, n, d_in, d_out, rtot, A, acat_t, acat, B, bcat_t);
+}
+
 void launch_prep_a(const DevTables& t, int32_t n, int64_t d_in, int64_t rtot, const void* const* A,
                    uint16_t* acat_t, uint16_t* acat, hipStream_t s) {
-  dim3 grid((unsigned)(d_in / 64), (unsigned)(n < 65535 ? n : 65535));
-  hipLaunchKernelGGL(k_prep_a, grid, dim3(256), 0, s, t, n, d_in, rtot, A, acat_t, acat);
+  launch_prep(t, n, d_in, 0, rtot, A, acat_t, acat, nullptr, nullptr, s);
 }
 
 void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
                    const void* const* B, uint16_t* bcat_t, hipStream_t s) {
-  dim3 grid((unsigned)(d_out / 64), (unsigned)(n < 65535 ? n : 65535));
-  hipLaunchKernelGGL(k_prep_b, grid, dim3(256), 0, s, t, n, d_out, rtot, B, bcat_t);
+  launch_prep(t, n, 0, d_out, rtot, nullptr, nullptr, nullptr, B, bcat_t, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -629,14 +646,6 @@ void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, 
                      partA, partB, dA, dB);
 }
 
-// ---------------------------------------------------------------------------
-// Base GEMM with the LoRA term as extra K-steps (the expand of the forward,
-// PLoRA §9.2 Case 4's dZ.A^T in the backward).  256x256 tile per workgroup of
-// four waves, 32-deep K-steps copied straight from global memory into a
-// five-stage LDS ring (160 KiB).  Extension step e of a row tile loads rows
-// [lo,hi) of E_j (other rows zero) and k-rows [k0, k0+32) of EB_j (rows >=
-// r_j zero).  Output written as bf16, staged through LDS so every store
-// writes whole 512-byte rows.
 // ---------------------------------------------------------------------------
 // Base GEMM with the LoRA term as extra K-steps (the expand of the forward,
 // PLoRA §9.2 Case 4's dZ.A^T in the backward).  256x256 tile per workgroup of

@@ -183,6 +183,30 @@ __global__ __launch_bounds__(256) void k_dequant_mx4_nk(const uint8_t* codes, co
   for (int q = 0; q < 4; ++q) dst[q] = v[q];
 }
 
+// Transpose of a base weight (run once: the base is frozen).  A 64x64 tile
+// per workgroup goes through LDS, padded one element per row so the
+// transposed reads spread over the banks; reads and writes are row-major
+// and coalesced.
+template <class T>
+__global__ __launch_bounds__(256) void k_transpose(const T* in, T* out, int64_t rows, int64_t cols) {
+  __shared__ T tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) tile[i][tx] = in[(r0 + i) * cols + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) out[(c0 + i) * rows + r0 + tx] = tile[tx][i];
+}
+
+void launch_transpose(const void* in, void* out, int64_t rows, int64_t cols, int esz, hipStream_t s) {
+  const dim3 grid((unsigned)(cols / 64), (unsigned)(rows / 64));
+  if (esz == 4)
+    hipLaunchKernelGGL(k_transpose<float>, grid, dim3(256), 0, s, static_cast<const float*>(in),
+                       static_cast<float*>(out), rows, cols);
+  else
+    hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(in),
+                       static_cast<uint16_t*>(out), rows, cols);
+}
+
 void launch_dequant_mx4(bool nk, const uint8_t* codes, const uint8_t* scales, int64_t d_in,
                         int64_t d_out, uint16_t* out, hipStream_t s) {
   if (nk) {

@@ -22,11 +22,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
-// Rule 9: a bf16 GEMM launch of `tiles` 256x256 output tiles and `nk`
-// 32-deep K-steps splits K into S parts when it would fill under half the
-// chip: S x tiles stays within one round of 256 CUs, each part keeps at
-// least 8 K-steps, S <= 16, and the parts are ceil(nk / S) steps each (S
-// recomputed so none is empty).
+// Rule 9: a bf16 GEMM launch of `tiles` 256x256 output tiles and `nk` K
+// units of 32 (the GEMM takes them two per step) splits K into S parts when
+// it would fill under half the chip: S x tiles stays within one round of 256
+// CUs, each part keeps at least 8 units, S <= 16, and the parts are
+// ceil(nk / S) units each (S recomputed so none is empty).
 int32_t split_k(int64_t tiles, int64_t nk) {
   if (tiles <= 0 || tiles >= 128 || nk < 16) return 1;
   int64_t sp = std::min<int64_t>({256 / tiles, nk / 8, 16});
@@ -147,13 +147,17 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
     err = "chunk_min/chunk_max/chunk_per_rank out of range";
     return MLORA_ERR_INVALID_ARG;
   }
-  if (o.w0_layout != MLORA_W0_KN && o.w0_layout != MLORA_W0_NK) {
-    err = "w0_layout must be MLORA_W0_KN or MLORA_W0_NK";
+  if (o.w0_layout != MLORA_W0_KN && o.w0_layout != MLORA_W0_NK && o.w0_layout != MLORA_W0_BOTH) {
+    err = "w0_layout must be MLORA_W0_KN, MLORA_W0_NK or MLORA_W0_BOTH";
     return MLORA_ERR_INVALID_ARG;
   }
   if (o.w0_format != MLORA_W0_BF16 && o.w0_format != MLORA_W0_MXFP8 && o.w0_format != MLORA_W0_MXFP4) {
     err = "w0_format must be MLORA_W0_BF16, MLORA_W0_MXFP8 or MLORA_W0_MXFP4";
     return MLORA_ERR_INVALID_ARG;
+  }
+  if (o.w0_format != MLORA_W0_BF16 && o.w0_layout == MLORA_W0_BOTH) {
+    err = "a microscaled base is held in one layout (MLORA_W0_BOTH needs a bf16/fp32 W0)";
+    return MLORA_ERR_UNSUPPORTED;
   }
   if (o.w0_format != MLORA_W0_BF16 && dtype != MLORA_BF16) {
     err = "a microscaled (MXFP8/MXFP4) base weight needs a bf16 plan";

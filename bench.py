@@ -184,7 +184,7 @@ def optimizer_step(w, plan, layer, steps, warmup, seed):
                          "frac": gbs / PEAK_HBM_GBS}}
 
 
-def sequential_layers(w, q, d, sets):
+def sequential_layers(w, q, d, sets, layout="kn", layer_w0=None):
     """The same work as one library call per adapter: a one-adapter plan per
     non-empty segment over its own rows (row slices of the packed tensors)."""
     import torch
@@ -196,8 +196,9 @@ def sequential_layers(w, q, d, sets):
         lo, hi = off[i], off[i + 1]
         if hi == lo:
             continue
-        plan = Plan([0, hi - lo], [int(d["ranks"][i])], p.d_in, p.d_out, "bf16")
-        layer = PackedLoRALinear(plan, d["W0"], [d["A"][i]], [d["B"][i]], [float(d["scales"][i])])
+        plan = Plan([0, hi - lo], [int(d["ranks"][i])], p.d_in, p.d_out, "bf16", w0_layout=layout)
+        W0 = layer_w0 if layer_w0 is not None else d["W0"]
+        layer = PackedLoRALinear(plan, W0, [d["A"][i]], [d["B"][i]], [float(d["scales"][i])])
         Y = [torch.empty((hi - lo, p.d_out), dtype=torch.bfloat16, device="cuda") for _ in range(sets)]
         dX = [torch.empty((hi - lo, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(sets)]
         out.append((lo, hi, plan, layer, Y, dX))
@@ -383,6 +384,9 @@ def main():
     ap.add_argument("--w0-format", default="bf16", choices=["bf16", "mxfp8", "mxfp4"],
                     help="store the frozen base in MXFP8 (E4M3 codes) or MXFP4 (E2M1 codes, two per byte), "
                          "with E8M0 scales per 32 inputs, decoded per call; implies --no-sequential")
+    ap.add_argument("--w0-layout", default="kn", choices=["kn", "nk", "both"],
+                    help="layout of the frozen base: [d_in][d_out], [d_out][d_in], or both (held once in "
+                         "each layout, built before timing; the forward then reads [d_out][d_in])")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the same steps replayed from a captured HIP graph (one-group plans)")
     ap.add_argument("--optimizer-only", action="store_true",
@@ -465,11 +469,12 @@ def main():
             ids = np.repeat(np.arange(w.n), np.diff(np.asarray(d["offsets"])))
             ids = ids[np.random.default_rng(a.seed).permutation(w.T)]
             plan = Plan.from_ids(ids, d["ranks"], p.d_in, p.d_out, "bf16",
-                                 n_streams=a.streams or w.n_streams)
+                                 n_streams=a.streams or w.n_streams, w0_layout=a.w0_layout)
         else:
             plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16",
-                        n_streams=a.streams or w.n_streams, w0_format=a.w0_format)
-        W0 = d["W0"]
+                        n_streams=a.streams or w.n_streams, w0_format=a.w0_format,
+                        w0_layout=a.w0_layout if not mx else "kn")
+        W0 = d["W0"] if a.w0_layout != "nk" or mx else d["W0"].t().contiguous()
         if mx:
             W0 = (quantize_mx4_device if a.w0_format == "mxfp4" else quantize_mx_device)(d["W0"], "kn")
             d["W0_bytes"] = W0.numel()
@@ -561,7 +566,8 @@ def main():
     if not a.no_sequential and not a.shuffled_ids:
         q0 = projs[0]
         d0 = layers[0][2]
-        seq = sequential_layers(w, q0, d0, SETS)
+        # the same base buffer and layout as the packed layer
+        seq = sequential_layers(w, q0, d0, SETS, layers[0][0].w0_layout, layers[0][1].W0)
 
         def seq_step(i):
             k = i % SETS
@@ -638,7 +644,7 @@ def main():
                    "streams": layers[0][0].info["n_groups"],
                    "rows": "shuffled, per-token adapter ids" if a.shuffled_ids else "adapter segments",
                    "fused": [g for g, _ in groups] if groups else None,
-                   "w0_format": a.w0_format},
+                   "w0_format": a.w0_format, "w0_layout": a.w0_layout},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
     }

@@ -29,7 +29,13 @@
  * dY [T][d_out], dX [T][d_in], A_i [d_in][r_i], B_i [r_i][d_out],
  * dA_i [d_in][r_i] fp32, dB_i [r_i][d_out] fp32.  W0 is [d_in][d_out]
  * (MLORA_W0_KN, the math layout) or [d_out][d_in] (MLORA_W0_NK, the layout of
- * an nn.Linear weight).  The saved activation Z' is plan-defined: adapter i
+ * an nn.Linear weight), or both (MLORA_W0_BOTH): one buffer holding
+ * [d_in][d_out] followed by its transpose [d_out][d_in].  The base is
+ * frozen, so a caller with memory to spare keeps both once
+ * (mlora_base_transpose builds the second half).  The forward then reads
+ * [d_out][d_in] and the backward's dX [d_in][d_out]: in both products both
+ * GEMM operands are contiguous along the reduction, the base GEMM's faster
+ * case.  Results are bit-identical to either single layout.  The saved activation Z' is plan-defined: adapter i
  * occupies plan.zoff[i] .. + n_i*r_pad(i) elements as [n_i][r_pad(i)], the
  * padding columns zero.
  *
@@ -82,7 +88,7 @@ typedef enum {
 } mlora_status;
 
 typedef enum { MLORA_FP32 = 0, MLORA_BF16 = 1 } mlora_dtype;
-typedef enum { MLORA_W0_KN = 0, MLORA_W0_NK = 1 } mlora_w0_layout;
+typedef enum { MLORA_W0_KN = 0, MLORA_W0_NK = 1, MLORA_W0_BOTH = 2 } mlora_w0_layout;
 typedef enum { MLORA_W0_BF16 = 0, MLORA_W0_MXFP8 = 1, MLORA_W0_MXFP4 = 2 } mlora_w0_format;
 
 #define MLORA_MAX_RANK 256
@@ -98,7 +104,7 @@ typedef struct {
   int32_t chunk_min;      /* reduction chunk rows, KC_i = min(chunk_max,                    */
   int32_t chunk_max;      /*   max(chunk_min, chunk_per_rank * r_pad(i)));                  */
   int32_t chunk_per_rank; /*   defaults 256, 2048, 8                                        */
-  int32_t w0_layout;      /* mlora_w0_layout; default MLORA_W0_KN                          */
+  int32_t w0_layout;      /* mlora_w0_layout; default MLORA_W0_KN (BOTH: bf16/fp32 W0 only)  */
   int32_t w0_format;      /* mlora_w0_format; default MLORA_W0_BF16 (MXFP8, MXFP4: bf16 plans only) */
 } mlora_plan_opts;
 
@@ -377,6 +383,19 @@ mlora_status mlora_adamw_step(mlora_plan_t plan, const mlora_adamw_hparams *hpar
                               void *const *mB, void *const *vB, void *const *A_copy,
                               void *const *B_copy, int32_t clip_grads, void *workspace,
                               size_t ws_bytes, void *stream);
+
+/*
+ * mlora_base_transpose -- out[c][r] = in[r][c] for a rows x cols matrix of
+ * bf16 (dtype MLORA_BF16) or fp32 (MLORA_FP32) elements, enqueued on
+ * `stream`.  Builds the second half of an MLORA_W0_BOTH base: in = the
+ * [d_in][d_out] half (rows = d_in, cols = d_out), out = in + d_in * d_out
+ * elements.  Device pointers, 16-byte aligned, not overlapping; rows and
+ * cols positive multiples of 64 (the layer's dimensions are).
+ * MLORA_ERR_INVALID_ARG otherwise, with nothing launched.  Not part of any
+ * step: the base is frozen, so it runs once.
+ */
+mlora_status mlora_base_transpose(const void *in, void *out, int64_t rows, int64_t cols,
+                                  mlora_dtype dtype, void *stream);
 
 /* Per-kernel timing.  Launches of the selected kinds are bracketed by HIP
  * events on the stream they run on; mlora_profile_read waits for them, adds

@@ -379,6 +379,31 @@ def test_mxfp4_plan_options():
     assert "MXFP4" in L.mlora_last_error().decode()
 
 
+def test_two_layout_base_options():
+    """MLORA_W0_BOTH: accepted for bf16 and fp32 plans, refused with a
+    microscaled base; the binding expects both layouts in one flat buffer;
+    the transpose entry point checks its arguments before launching."""
+    from adapter_lora_segments_amd.binding import _w0_shape
+    for dt in ("bf16", "fp32"):
+        p2 = Plan([0, 5, 9], [4, 8], 128, 192, dt, w0_layout="both")
+        p1 = Plan([0, 5, 9], [4, 8], 128, 192, dt)
+        assert _w0_shape(p2) == (2 * 128 * 192,)
+        assert p2.info["workspace_bytes"] == p1.info["workspace_bytes"]
+        for name in ["rpad", "zoff", "nb", "chunks", "tiles", "ext", "ksplit"]:
+            assert np.array_equal(p2.export(name), p1.export(name)), name
+    assert _status(lambda: Plan([0, 5, 9], [4, 8], 128, 192, w0_layout="both", w0_format="mxfp4")) == -2
+    L = _lib.lib()
+    vp = ctypes.c_void_p
+    a, b = vp(1 << 20), vp(1 << 24)
+    assert L.mlora_base_transpose(None, b, 64, 64, 0, None) == -1
+    assert L.mlora_base_transpose(a, vp((1 << 24) + 8), 64, 64, 0, None) == -1          # misaligned
+    assert L.mlora_base_transpose(a, b, 64, 96, 0, None) == -1                          # not a multiple of 64
+    assert L.mlora_base_transpose(a, b, 0, 64, 0, None) == -1
+    assert L.mlora_base_transpose(a, b, 64, 64, 7, None) == -1                          # dtype
+    assert L.mlora_base_transpose(a, vp((1 << 20) + 4096), 64, 64, 0, None) == -1       # overlap
+    assert "overlap" in L.mlora_last_error().decode()
+
+
 def test_mx4_quantizer_round_trip():
     """The MXFP4 input quantizer against the oracle's decoder: every weight
     decodes to the nearest E2M1 value of its scaled magnitude (ties low), with
