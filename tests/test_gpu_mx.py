@@ -107,20 +107,23 @@ def test_mx_base_bench_layer_full_size():
 
 
 @pytest.mark.gpu
-def test_mx_base_with_projections_sharing_the_input():
-    """An MXFP8 base under mlora_plan_multi: the concatenated weight's codes
-    and scales decode per output column across the projections' columns."""
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_mx_base_with_projections_sharing_the_input(fmt):
+    """A microscaled base under mlora_plan_multi: the concatenated weight's
+    codes and scales decode per output column across the projections'
+    columns."""
     import torch
     from adapter_lora_segments_amd import Plan, PackedLoRALinear
     from oracle import multi as om
     from workloads.multi import host_multi
     widths = [512, 256, 256]
     ranks = [[8, 8, 8], [64, 16, 100]]
-    say(f"case mxfp8 base with projections {widths}")
+    say(f"case {fmt} base with projections {widths}")
     h = host_multi(9, 512, widths, ranks, [300, 150], "bf16")
-    codes, scales = quantize_mx(ol.as_f64(h["W0"], "bf16"), "nk")
-    Wdec = omx.dequant_w0(codes, scales, 512, sum(widths), "nk")
-    plan = Plan.multi(h["offsets"], ranks, 512, widths, "bf16", w0_layout="nk", w0_format="mxfp8")
+    quant = quantize_mx4 if fmt == "mxfp4" else quantize_mx
+    codes, scales = quant(ol.as_f64(h["W0"], "bf16"), "nk")
+    Wdec = omx.dequant_w0(codes, scales, 512, sum(widths), "nk", fmt=fmt)
+    plan = Plan.multi(h["offsets"], ranks, 512, widths, "bf16", w0_layout="nk", w0_format=fmt)
     flat = lambda x: [v for row in x for v in row]
     layer = PackedLoRALinear(plan, torch.from_numpy(pack(codes, scales)).cuda(),
                              [to_dev(a, "bf16") for a in flat(h["A"])], [to_dev(b, "bf16") for b in flat(h["B"])],
