@@ -154,34 +154,49 @@ def time_steps(step, steps, warmup):
 OPT_BYTES_PER_ELEM = 30    # read p, g, m, v (fp32); write p, m, v (fp32) and the bf16 copy
 
 
-def optimizer_step(w, plan, layer, steps, warmup, seed):
+def optimizer_step(w, plan, layer, steps, warmup, seed, clip=None):
     """The per-adapter AdamW step over the layer's adapters (fp32 masters and
     moments, bf16 copies written back into the layer's A_i, B_i), with every
     adapter stepping: launch time from events on its stream, against the HBM
-    roofline of its algorithmic bytes."""
+    roofline of its algorithmic bytes.  With ``clip``, every adapter clips its
+    gradients to that norm first (two more launches, timed as grad_norm; they
+    read every gradient once more: 4 bytes per element)."""
     import torch
     from adapter_lora_segments_amd import AdamW, adamw_hparams
     from workloads import optim
     opt = AdamW(layer)
     hps = [dict(h, start=0) for h in optim.hyperparameters(plan.info["n"] * plan.info["n_proj"], seed)]
+    if clip is not None:
+        hps = [dict(h, max_grad_norm=float(clip)) for h in hps]
     hp = adamw_hparams(optim.step_hparams(hps, 0))
+    on = clip is not None
     for _ in range(warmup):
-        opt.step(hp)
+        opt.step(hp, clip_grads=on)
     torch.cuda.synchronize()
-    plan.profile_enable(["adamw"])
+    plan.profile_enable(["adamw", "grad_norm"])
     plan.profile_read()
     for _ in range(steps):
-        opt.step(hp)
+        opt.step(hp, clip_grads=on)
     torch.cuda.synchronize()
-    tot_ms, n = plan.profile_read()["adamw"]
+    prof = plan.profile_read()
+    tot_ms, n = prof["adamw"]
+    gn_ms, gn_n = prof["grad_norm"]
     plan.profile_enable(False)
     avg = tot_ms / max(n, 1)
     elems = sum(int(r) * (plan.info["d_in"] + int(wd)) for r, wd in zip(plan.ranks, plan.pair_widths))
     gbs = OPT_BYTES_PER_ELEM * elems / (avg * 1e-3) / 1e9
-    return {"kernel": "k_adamw (per-adapter AdamW, bf16 copies)", "elements": elems,
-            "bytes_per_launch": OPT_BYTES_PER_ELEM * elems, "avg_launch_ms": avg, "launches": n,
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS}}
+    out = {"kernel": "k_adamw (per-adapter AdamW, bf16 copies)", "elements": elems,
+           "bytes_per_launch": OPT_BYTES_PER_ELEM * elems, "avg_launch_ms": avg, "launches": n,
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": gbs / PEAK_HBM_GBS}}
+    if on:
+        gavg = gn_ms / max(gn_n, 1)
+        ggbs = 4 * elems / (gavg * 1e-3) / 1e9
+        out["clip"] = {"max_grad_norm": float(clip), "kernels": "k_grad_sq + k_clip_coef",
+                       "bytes_per_launch": 4 * elems, "avg_launch_ms": gavg, "launches": gn_n,
+                       "roofline": {"bound": "hbm", "achieved": ggbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": ggbs / PEAK_HBM_GBS}}
+    return out
 
 
 def sequential_layers(w, q, d, sets, layout="kn", layer_w0=None):
@@ -389,6 +404,8 @@ def main():
                          "each layout, built before timing; the forward then reads [d_out][d_in])")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the same steps replayed from a captured HIP graph (one-group plans)")
+    ap.add_argument("--clip", type=float, default=None,
+                    help="the optimizer step clips each adapter's gradients to this 2-norm first")
     ap.add_argument("--optimizer-only", action="store_true",
                     help="run one forward+backward for real gradients, then time only the "
                          "per-adapter AdamW step of the first projection; one JSON line")
@@ -513,7 +530,7 @@ def main():
     if a.optimizer_only:
         step(0)
         torch.cuda.synchronize()
-        o = optimizer_step(w, layers[0][0], layers[0][1], a.steps, a.warmup, a.seed)
+        o = optimizer_step(w, layers[0][0], layers[0][1], a.steps, a.warmup, a.seed, a.clip)
         p0 = w.projections[0]
         print(json.dumps({"metric": "per-adapter AdamW step, bytes/s", "value": o["roofline"]["achieved"],
                           "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -609,7 +626,7 @@ def main():
 
     opt_out = None
     if prof and not a.no_optimizer:
-        opt_out = optimizer_step(w, layers[0][0], layers[0][1], a.steps, a.warmup, a.seed)
+        opt_out = optimizer_step(w, layers[0][0], layers[0][1], a.steps, a.warmup, a.seed, a.clip)
 
     ms = el / a.steps * 1e3
     tok_s = w.T * a.steps / el
