@@ -10,7 +10,9 @@
   the decoded-weight bf16 layer.
 - MXFP4 the same way: all sixteen E2M1 codes in both layouts, bitwise
   against the decoded-weight layer and within the bar of the oracle, and
-  the bench layer at full size."""
+  the bench layer at full size.
+- Both formats under projections sharing the input and under a plan from
+  shuffled per-token ids."""
 import numpy as np
 import pytest
 
@@ -201,3 +203,39 @@ def test_mx4_base_bench_layer_full_size(layout):
         assert np.array_equal(out4[k], out_bf[k]), k
     for i in range(w.n):
         assert np.array_equal(out4["dA"][i], out_bf["dA"][i]) and np.array_equal(out4["dB"][i], out_bf["dB"][i])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("fmt,layout", [("mxfp4", "kn"), ("mxfp8", "nk")])
+def test_mx_base_with_shuffled_ids(fmt, layout):
+    """A microscaled base under a plan from per-token adapter ids (rows in the
+    caller's shuffled order): bit-identical to the bf16 layer on the decoded
+    weight, and within the bar of the ids oracle."""
+    import torch
+    from adapter_lora_segments_amd import Plan
+    say(f"case {fmt} base {layout} with shuffled ids")
+    w = custom_workload("mxids", "bf16", 512, 768, [8, 64, 33], [200, 310, 95], seed=31)
+    h = host_tensors(w, 0)
+    T = h["X"].shape[0]
+    order = np.random.default_rng(32).permutation(T)
+    ids = np.repeat(np.arange(3), np.diff(h["offsets"]))[order]
+    hs = dict(h, X=np.ascontiguousarray(h["X"][order]), dY=np.ascontiguousarray(h["dY"][order]))
+    quant = quantize_mx4 if fmt == "mxfp4" else quantize_mx
+    codes, scales = quant(ol.as_f64(h["W0"], "bf16"), layout)
+    Wdec = omx.dequant_w0(codes, scales, 512, 768, layout, fmt=fmt)
+    p_mx = Plan.from_ids(ids, h["ranks"], 512, 768, "bf16", w0_layout=layout, w0_format=fmt)
+    p_bf = Plan.from_ids(ids, h["ranks"], 512, 768, "bf16", w0_layout=layout)
+    out_mx = _run(p_mx, torch.from_numpy(pack(codes, scales)).cuda(), hs)
+    out_bf = _run(p_bf, to_dev(Wdec if layout == "kn" else np.ascontiguousarray(Wdec.T), "bf16"), hs)
+    for k in ("Y", "dX", "Z"):
+        assert np.array_equal(out_mx[k], out_bf[k]), k
+    for i in range(3):
+        assert np.array_equal(out_mx["dA"][i], out_bf["dA"][i]) and np.array_equal(out_mx["dB"][i], out_bf["dB"][i])
+    Yo, _ = ol.forward_ids(hs["X"], Wdec, h["A"], h["B"], h["scales"], ids, "bf16")
+    dXo, dAo, dBo, _ = ol.backward_ids(hs["dY"], hs["X"], Wdec, h["A"], h["B"], h["scales"], ids, "bf16")
+    errs = {"Y": ol.max_rel_err(out_mx["Y"], Yo), "dX": ol.max_rel_err(out_mx["dX"], dXo)}
+    for i in range(3):
+        errs[f"dA{i}"] = ol.max_rel_err(out_mx["dA"][i], dAo[i])
+        errs[f"dB{i}"] = ol.max_rel_err(out_mx["dB"][i], dBo[i])
+    say(f"  worst {max(errs.items(), key=lambda kv: kv[1])}")
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
