@@ -340,6 +340,9 @@ class PackedLoRALinear:
         torch = _torch()
         self.plan = plan
         if plan.w0_layout == "both" and W0 is not None and W0.dim() == 2:
+            want = (plan.info["d_in"], plan.info["d_out"])
+            if tuple(W0.shape) != want:
+                raise ValueError(f"a two-layout base is given as [d_in][d_out] = {want}, got {tuple(W0.shape)}")
             W0 = base_both(W0)          # given as [d_in][d_out]: add its transpose once
         self.W0 = W0
         self.A = list(A)

@@ -402,6 +402,12 @@ def test_two_layout_base_options():
     assert L.mlora_base_transpose(a, b, 64, 64, 7, None) == -1                          # dtype
     assert L.mlora_base_transpose(a, vp((1 << 20) + 4096), 64, 64, 0, None) == -1       # overlap
     assert "overlap" in L.mlora_last_error().decode()
+    import torch
+    from adapter_lora_segments_amd import PackedLoRALinear
+    p2 = Plan([0, 5, 9], [4, 8], 128, 192, w0_layout="both")
+    with pytest.raises(ValueError, match="d_in"):
+        PackedLoRALinear(p2, torch.zeros((192, 128), dtype=torch.bfloat16), [None, None], [None, None], [1.0, 1.0],
+                         device="cpu")
 
 
 def test_mx4_quantizer_round_trip():
