@@ -21,7 +21,7 @@ from workloads.multi import host_multi
 from workloads.mx import pack, quantize_mx, quantize_mx4
 from workloads.tensors import host_tensors
 
-N_CASES = 80
+N_CASES = 240
 
 
 def draw_case(seed):
