@@ -8,7 +8,9 @@ three times with new inputs copied in eagerly between replays; every replay
 must equal, bit for bit, an eager step on the same inputs.  One case has one
 stream group (its backward still forks the weight-gradient stream and joins
 it inside the graph), one splits K.  Plans with several stream groups are
-refused under capture (see the skipped case)."""
+refused under capture (see the skipped case).  The per-adapter AdamW step,
+with and without gradient clipping, is captured the same way and each
+replay from a restored state equals the eager step."""
 import numpy as np
 import pytest
 
@@ -73,3 +75,59 @@ def test_graph_replay_matches_eager(name, d_in, d_out, ranks, tokens, streams):
         for k, (a, b) in enumerate(zip(got, want)):
             assert torch.equal(a, b), f"replay {rep}: output {k} differs from the eager step"
     say(f"  3 replays bit-identical to eager steps")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("clip", [False, True])
+def test_adamw_step_graph_replay_matches_eager(clip):
+    """The per-adapter AdamW step (with and without gradient clipping)
+    captured once and replayed from a restored state: every replay equals
+    the eager step from the same state, bit for bit (masters, moments and
+    the bf16 copies)."""
+    import torch
+    from adapter_lora_segments_amd import Plan, PackedLoRALinear, AdamW, adamw_hparams
+    from workloads import optim
+    say(f"case graph adamw clip={clip}")
+    ranks, d_in, d_out = [8, 64, 33, 1], 256, 320
+    plan = Plan(np.arange(5, dtype=np.int64) * 3, ranks, d_in, d_out, "bf16")
+    A32, B32 = optim.masters(ranks, d_in, d_out, 41)
+    A = [torch.from_numpy(a).cuda().to(torch.bfloat16) for a in A32]
+    B = [torch.from_numpy(b).cuda().to(torch.bfloat16) for b in B32]
+    layer = PackedLoRALinear(plan, None, A, B, [1.0] * len(ranks))
+    opt = AdamW(layer)
+    for dst, src in zip(opt.A + opt.B, A32 + B32):
+        dst.copy_(torch.from_numpy(src).cuda())
+    gA, gB = optim.gradients(ranks, d_in, d_out, 41, 0)
+    for i in range(len(ranks)):
+        layer.dA[i].copy_(torch.from_numpy(gA[i]).cuda())
+        layer.dB[i].copy_(torch.from_numpy(gB[i]).cuda())
+    hps = [dict(h, start=0, max_grad_norm=0.05 if i % 2 == 0 else 0.0)
+           for i, h in enumerate(optim.hyperparameters(len(ranks), 41))]
+    hp = adamw_hparams(optim.step_hparams(hps, 0))
+    state = opt.A + opt.B + opt.mA + opt.vA + opt.mB + opt.vB + list(layer.A) + list(layer.B)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        opt.step(hp, clip_grads=clip)                 # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    s0 = [t.clone() for t in state]                   # the state the graph starts from
+    opt.step(hp, clip_grads=clip)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in state]
+    for t, v in zip(state, s0):
+        t.copy_(v)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        opt.step(hp, clip_grads=clip)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t, v in zip(state, s0):
+            t.copy_(v)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(state, want)):
+            assert torch.equal(a, b), f"replay {rep}: state tensor {k} differs from the eager step"
+    say("  3 replays bit-identical to the eager step")
