@@ -328,6 +328,38 @@ def device_check() -> None:
     check(lib().mlora_device_check())
 
 
+def _check_adapters(plan: Plan, A: Sequence, B: Sequence, scales) -> None:
+    """The library reads A_i and B_i through raw device pointers with the
+    plan's ranks and widths, so every tensor is checked here first: A_i is
+    [d_in][r_i] and B_i is [r_i][w_i] (w_i its projection's width) in the
+    plan's dtype, dense, on a GPU, 16-byte aligned."""
+    n = _npairs(plan)
+    if len(A) != n or len(B) != n:
+        raise ValueError(f"expected {n} adapter tensors for A and for B, got {len(A)} and {len(B)}")
+    if np.asarray(scales).size != n:
+        raise ValueError(f"expected {n} scales, got {np.asarray(scales).size}")
+    dt = _dt(plan)
+    d_in = plan.info["d_in"]
+    items = []
+    for v in range(n):
+        r, w = int(plan.ranks[v]), int(plan.pair_widths[v])
+        items += [(f"A[{v}]", A[v], (d_in, r)), (f"B[{v}]", B[v], (r, w))]
+    for name, t, shape in items:        # what the plan fixes, on every tensor first
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        if t.dtype != dt:
+            raise ValueError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t, _ in items:            # then where the memory is
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.data_ptr() % 16 != 0:
+            raise ValueError(f"{name} must be 16-byte aligned")
+
+
 class PackedLoRALinear:
     """One packed layer with its adapters, buffers and pointer tables.
 
@@ -339,6 +371,7 @@ class PackedLoRALinear:
     def __init__(self, plan: Plan, W0, A: Sequence, B: Sequence, scales, device="cuda"):
         torch = _torch()
         self.plan = plan
+        _check_adapters(plan, A, B, scales)
         if plan.w0_layout == "both" and W0 is not None and W0.dim() == 2:
             want = (plan.info["d_in"], plan.info["d_out"])
             if tuple(W0.shape) != want:
@@ -353,7 +386,6 @@ class PackedLoRALinear:
                    for r in plan.ranks]
         self.dB = [torch.empty((int(r), int(w)), dtype=torch.float32, device=device)
                    for r, w in zip(plan.ranks, plan.pair_widths)]
-        assert len(self.A) == n and len(self.B) == n
         self.A_ptrs = pointer_table(self.A, device)
         self.B_ptrs = pointer_table(self.B, device)
         self.dA_ptrs = pointer_table(self.dA, device)

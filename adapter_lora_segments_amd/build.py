@@ -40,6 +40,10 @@ def _compile(src: str) -> str:
     out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+    # An inline-asm statement that clobbers a register the compiler reserves
+    # (M0, EXEC, VCC) is undefined behaviour: refuse the build.
+    if "Reserved registers on the clobber list" in out:
+        raise RuntimeError(f"{src}: inline assembly clobbers a reserved register:\n{out}")
     if out.strip():
         print(out, file=sys.stderr)
     return obj

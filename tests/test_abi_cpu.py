@@ -482,3 +482,33 @@ def test_plan_multi_from_ids_bit_exact_against_mirror(case):
         got, want = p.export(name), m[name]
         assert (got.size == 0 and want.size == 0) or np.array_equal(got, want.reshape(got.shape)), name
     assert _status(lambda: Plan.multi_from_ids([0, 3], [[4, 4], [8, 8]], 128, [256, 256])) == -1  # id 3 >= n
+
+
+def test_packed_layer_checks_adapter_tensors_before_any_device_call():
+    """PackedLoRALinear refuses adapter tensors the kernels would misread
+    through their raw pointers (wrong shape, dtype, layout or device),
+    before it allocates anything on a device."""
+    import torch
+    from adapter_lora_segments_amd.binding import PackedLoRALinear
+    ranks, d_in, d_out = [8, 33], 128, 192
+    plan = Plan([0, 5, 9], ranks, d_in, d_out, "bf16")
+    good_A = [torch.zeros((d_in, r), dtype=torch.bfloat16) for r in ranks]
+    good_B = [torch.zeros((r, d_out), dtype=torch.bfloat16) for r in ranks]
+
+    def refuse(A, B, scales=(1.0, 1.0), match=""):
+        with pytest.raises(ValueError, match=match):
+            PackedLoRALinear(plan, None, A, B, list(scales))
+
+    refuse(good_A, good_B, match="device tensor")                    # host tensors
+    refuse([good_A[0], torch.zeros((d_in, 32), dtype=torch.bfloat16)], good_B, match=r"A\[1\].*shape")
+    refuse(good_A, [good_B[0], torch.zeros((33, d_out - 64), dtype=torch.bfloat16)], match=r"B\[1\].*shape")
+    refuse([good_A[0], good_A[1].float()], good_B, match=r"A\[1\].*bfloat16")
+    refuse(good_A, [good_B[0], torch.zeros((d_out, 33), dtype=torch.bfloat16).t()], match="contiguous")
+    refuse(good_A[:1], good_B, match="adapter tensors")
+    refuse(good_A, good_B, scales=(1.0,), match="scales")
+    # a multi-projection plan: B of pair (i, q) is [r][width of q]
+    mp = Plan.multi([0, 4, 9], [[8, 16], [4, 32]], d_in, [256, 512], "bf16")
+    A = [torch.zeros((d_in, r), dtype=torch.bfloat16) for r in (8, 16, 4, 32)]
+    B = [torch.zeros((r, w), dtype=torch.bfloat16) for r, w in ((8, 256), (16, 512), (4, 256), (32, 256))]
+    with pytest.raises(ValueError, match=r"B\[3\].*shape"):
+        PackedLoRALinear(mp, None, A, B, [1.0] * 4)
