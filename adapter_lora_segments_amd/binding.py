@@ -371,11 +371,13 @@ class PackedLoRALinear:
     def __init__(self, plan: Plan, W0, A: Sequence, B: Sequence, scales, device="cuda"):
         torch = _torch()
         self.plan = plan
-        _check_adapters(plan, A, B, scales)
-        if plan.w0_layout == "both" and W0 is not None and W0.dim() == 2:
+        both_2d = plan.w0_layout == "both" and W0 is not None and W0.dim() == 2
+        if both_2d:
             want = (plan.info["d_in"], plan.info["d_out"])
             if tuple(W0.shape) != want:
                 raise ValueError(f"a two-layout base is given as [d_in][d_out] = {want}, got {tuple(W0.shape)}")
+        _check_adapters(plan, A, B, scales)
+        if both_2d:
             W0 = base_both(W0)          # given as [d_in][d_out]: add its transpose once
         self.W0 = W0
         self.A = list(A)

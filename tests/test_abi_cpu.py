@@ -512,3 +512,49 @@ def test_packed_layer_checks_adapter_tensors_before_any_device_call():
     B = [torch.zeros((r, w), dtype=torch.bfloat16) for r, w in ((8, 256), (16, 512), (4, 256), (32, 256))]
     with pytest.raises(ValueError, match=r"B\[3\].*shape"):
         PackedLoRALinear(mp, None, A, B, [1.0] * 4)
+
+
+def _lib_tables_match(p, expect, skip=()):
+    """Library export of every table named in a hand-worked golden."""
+    info_keys = {"T", "n_groups", "z_elems", "rpad_total", "partial_rows"}
+    for k, v in expect.items():
+        if k in skip:
+            continue
+        if k in info_keys:
+            assert p.info[k] == v, (k, p.info[k], v)
+            continue
+        got = p.export(k)
+        want = np.asarray(v).reshape(got.shape) if got.size else np.asarray(v)
+        assert np.array_equal(got, want), (k, got, v)
+
+
+def test_library_plans_match_hand_worked_goldens():
+    """The C++ plan builder against the plans worked by hand (the same
+    goldens that pin the Python mirror): one projection, two projections
+    sharing the input, and rows as per-token ids."""
+    import json
+    gdir = os.path.join(ROOT, "tests", "golden")
+    g = json.load(open(os.path.join(gdir, "plan_hand.json")))
+    o = g["opts"]
+    p = Plan(g["offsets"], g["ranks"], 256, 256, "fp32", nano_rows=o["nano_rows"], gemm_rows=o["gemm_rows"],
+             n_streams=o["n_streams"], chunk_min=o["chunk_min"], chunk_max=o["chunk_max"],
+             chunk_per_rank=o["chunk_per_rank"])
+    _lib_tables_match(p, g["expect"])
+
+    g = json.load(open(os.path.join(gdir, "plan_multi_hand.json")))
+    o = g["opts"]
+    p = Plan.multi(g["offsets"], g["ranks"], g["d_in"], g["widths"], g["dtype"], nano_rows=o["nano_rows"],
+                   gemm_rows=o["gemm_rows"], n_streams=o["n_streams"], chunk_min=o["chunk_min"],
+                   chunk_max=o["chunk_max"], chunk_per_rank=o["chunk_per_rank"])
+    # partial_b_elems is the mirror's running total, not a library table
+    _lib_tables_match(p, g["expect"], skip=("partial_b_elems",))
+
+    g = json.load(open(os.path.join(gdir, "plan_ids_hand.json")))
+    o = g["opts"]
+    p = Plan.from_ids(g["ids"], g["ranks"], g["d_in"], g["d_out"], g["dtype"], nano_rows=o["nano_rows"],
+                      gemm_rows=o["gemm_rows"], n_streams=o["n_streams"], chunk_min=o["chunk_min"],
+                      chunk_max=o["chunk_max"], chunk_per_rank=o["chunk_per_rank"])
+    _lib_tables_match(p, g["expect"])
+    # rule 9 rebalanced by hand: 10 forward tiles over 130 K-steps -> 15 parts,
+    # 17 dX tiles over 80 K-steps -> 10 parts
+    assert Plan([0, 256], [8], 4160, 2560).export("ksplit").tolist() == [[15, 10]]

@@ -2,17 +2,19 @@
 that the pin suite notices every one of them."""
 import importlib.util
 import os
+import sys
 import types
 
 import pytest
 
-from tests import pins, pins_adamw, pins_multi, pins_mx
+from tests import pins, pins_adamw, pins_multi, pins_mx, pins_plan
 
 ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(ORACLE, "lora.py")
 SRC_ADAMW = os.path.join(ORACLE, "adamw.py")
 SRC_MULTI = os.path.join(ORACLE, "multi.py")
 SRC_MX = os.path.join(ORACLE, "mx.py")
+SRC_PLAN = os.path.join(ORACLE, "plan_mirror.py")
 
 MUTATIONS = {
     "drop_scale_fwd": ("Y[r0:r1] = Xc @ W + s * (Zc @ Bi)", "Y[r0:r1] = Xc @ W + (Zc @ Bi)"),
@@ -105,6 +107,33 @@ MX_MUTATIONS = {
 }
 
 
+PLAN_MUTATIONS = {
+    "rpad_min_16": ("rpad = [max(32, _pow2_at_least(r)) for r in rk]", "rpad = [max(16, _pow2_at_least(r)) for r in rk]"),
+    "zoff_without_rows": ("z += cnt[v // P] * rpad[v]", "z += rpad[v]"),
+    "roff_unpadded": ("rr += rpad[v]", "rr += rk[v]"),
+    "seg_start_by_projection": ("seg_start.append(o[v // P])", "seg_start.append(o[v % P])"),
+    "group_floor": ("target = -(-(s * T) // S)  # ceil", "target = (s * T) // S"),
+    "group_not_monotone": ("g[s] = max(g[s - 1], a)", "g[s] = a if a < n else g[s - 1]"),
+    "bucket_ascending": ("key=lambda v: (-rpad[v], v % P, v // P)", "key=lambda v: (rpad[v], v % P, v // P)"),
+    "bucket_adapter_before_projection": ("key=lambda v: (-rpad[v], v % P, v // P)",
+                                         "key=lambda v: (-rpad[v], v // P, v % P)"),
+    "nano_tail_dropped": ("nb.append((v, r0, min(opts.nano_rows, hi - r0)))", "nb.append((v, r0, opts.nano_rows)) if r0 + opts.nano_rows <= hi else None"),
+    "chunk_by_rank_not_rpad": ("opts.chunk_per_rank * rpad[v])", "opts.chunk_per_rank * rk[v])"),
+    "chunk_max_ignored": ("kc = min(opts.chunk_max, max(", "kc = (max("),
+    "cpref_after": ("cpref.append(cp)\n                cboff.append(cb)\n                cp += rpad[v]",
+                    "cp += rpad[v]\n                cpref.append(cp)\n                cboff.append(cb)"),
+    "cboff_without_width": ("cb += rpad[v] * wd[v % P]", "cb += rpad[v] * wd[0]"),
+    "ext_wrong_projection": ("v = j * P + q", "v = j * P"),
+    "ext_k_step_64": ("for k0 in range(0, rpad[v], KSTEP):", "for k0 in range(0, rpad[v], 2 * KSTEP):"),
+    "tiles_across_groups": ("R0, R1 = o[g[s]], o[g[s + 1]]", "R0, R1 = o[g[s]], o[g[s + 1]] + (BM if s + 1 < S else 0)"),
+    "split_k_no_rebalance": ("    return -(-nk // kper)", "    return sp"),
+    "split_k_limit_64": ("if tiles <= 0 or tiles >= 128 or nk < 16:", "if tiles <= 0 or tiles >= 64 or nk < 16:"),
+    "ids_reverse_within_adapter": ("    for t, a in enumerate(ids):\n        perm[nxt[a]] = t",
+                                   "    for t, a in reversed(list(enumerate(ids))):\n        perm[nxt[a]] = t"),
+    "ids_prefix_off_by_one": ("        off[a + 1] += 1", "        off[min(a + 2, n)] += 1"),
+}
+
+
 def _mutant(old, new, src_path=SRC) -> types.ModuleType:
     with open(src_path) as f:
         src = f.read()
@@ -112,7 +141,12 @@ def _mutant(old, new, src_path=SRC) -> types.ModuleType:
     src = src.replace(old, new, 1)
     mod = types.ModuleType("oracle.oracle_mutant")
     mod.__package__ = "oracle"
-    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    # dataclasses look their module up in sys.modules while the class body runs
+    sys.modules[mod.__name__] = mod
+    try:
+        exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    finally:
+        del sys.modules[mod.__name__]
     return mod
 
 
@@ -161,6 +195,19 @@ def test_mx_pins_catch_planted_mistake(name):
     mod = _mutant(old, new, SRC_MX)
     caught = []
     for pin in pins_mx.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutation {name}"
+
+
+@pytest.mark.parametrize("name", sorted(PLAN_MUTATIONS))
+def test_plan_pins_catch_planted_mistake(name):
+    old, new = PLAN_MUTATIONS[name]
+    mod = _mutant(old, new, SRC_PLAN)
+    caught = []
+    for pin in pins_plan.ALL_PINS:
         try:
             pin(mod)
         except Exception as e:

@@ -1,81 +1,19 @@
-"""The plan mirror against a hand-worked plan and against invariants any
-correct plan must satisfy (every row covered once, chunks partition each
-adapter, extension steps cover exactly the adapters meeting each tile)."""
-import json
-import os
-
-import numpy as np
+"""The plan mirror against plans worked by hand (one projection, two
+projections sharing the input, rows as per-token ids), split-K factors
+worked by hand, and invariants any correct plan must satisfy (every row
+covered once per projection, chunks partition each pair, extension steps
+cover exactly the pairs meeting each tile), seeded and under hypothesis."""
+import pytest
 from hypothesis import given, settings, strategies as st
 
+from oracle import plan_mirror
 from oracle.plan_mirror import build_plan, PlanOpts
-
-GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-
-
-def test_hand_worked_plan():
-    with open(os.path.join(GOLDEN, "plan_hand.json")) as f:
-        g = json.load(f)
-    p = build_plan(g["offsets"], g["ranks"], PlanOpts(**g["opts"]))
-    for k, v in g["expect"].items():
-        got = p[k]
-        if isinstance(got, np.ndarray):
-            assert np.array_equal(got, np.asarray(v, dtype=got.dtype).reshape(got.shape)), (k, got, v)
-        else:
-            assert got == v, (k, got, v)
+from tests import pins_plan
 
 
-def check_invariants(offsets, ranks, opts, p):
-    o = [int(x) for x in offsets]
-    n = len(ranks)
-    T = o[-1]
-    rpad = p["rpad"]
-    for i, r in enumerate(ranks):
-        assert rpad[i] >= max(32, r) and (rpad[i] & (rpad[i] - 1)) == 0 and rpad[i] < 2 * max(32, r)
-    g = p["group_first_adapter"]
-    assert g[0] == 0 and g[-1] == n and all(g[k] <= g[k + 1] for k in range(len(g) - 1))
-    # nano-batches: each row of each adapter exactly once, pieces <= NB, within a group
-    cover = np.zeros(T, dtype=np.int64)
-    for (a, r0, m) in p["nb"]:
-        assert 1 <= m <= opts.nano_rows and o[a] <= r0 and r0 + m <= o[a + 1]
-        cover[r0:r0 + m] += 1
-    assert np.all(cover == 1)
-    for s in range(p["n_groups"]):
-        for (a, _, _) in p["nb"][p["nb_start"][s]:p["nb_start"][s + 1]]:
-            assert g[s] <= a < g[s + 1]
-    # chunks partition each adapter, in row order, consecutive per adapter
-    for i in range(n):
-        f, c = p["adapter_chunk_first"][i], p["adapter_chunk_count"][i]
-        rows = [(r0, m) for (a, r0, m) in p["chunks"][f:f + c]]
-        assert all(a == i for (a, _, _) in p["chunks"][f:f + c])
-        pos = o[i]
-        for r0, m in rows:
-            assert r0 == pos and m >= 1
-            pos += m
-        assert pos == o[i + 1]
-    cp = 0
-    for k, (a, _, _) in enumerate(p["chunks"]):
-        assert p["chunk_rpref"][k] == cp
-        cp += rpad[a]
-    assert cp == p["partial_rows"]
-    # tiles cover [0, T) once; extension entries = adapters meeting the tile
-    cover = np.zeros(T, dtype=np.int64)
-    for t, (r0, m) in enumerate(p["tiles"]):
-        assert 1 <= m <= opts.gemm_rows
-        cover[r0:r0 + m] += 1
-        want = []
-        for j in range(n):
-            lo, hi = max(o[j], r0), min(o[j + 1], r0 + m)
-            if lo < hi:
-                want += [(j, lo, hi, k0) for k0 in range(0, int(rpad[j]), 32)]
-        got = [tuple(e) for e in p["ext"][p["tile_ext_start"][t]:p["tile_ext_start"][t + 1]]]
-        assert got == want
-    assert np.all(cover == 1)
-    # offsets
-    z = 0
-    for i in range(n):
-        assert p["zoff"][i] == z
-        z += (o[i + 1] - o[i]) * rpad[i]
-    assert z == p["z_elems"]
+@pytest.mark.parametrize("pin", pins_plan.ALL_PINS, ids=lambda f: f.__name__)
+def test_plan_pin(pin):
+    pin(plan_mirror)
 
 
 @st.composite
@@ -97,4 +35,30 @@ def plan_inputs(draw):
 def test_plan_invariants(args):
     off, ranks, opts = args
     p = build_plan(off, ranks, opts)
-    check_invariants(off, ranks, opts, p)
+    pins_plan.check_invariants(plan_mirror, off, ranks, opts, p)
+
+
+@st.composite
+def multi_inputs(draw):
+    n = draw(st.integers(1, 12))
+    P = draw(st.integers(1, 4))
+    toks = draw(st.lists(st.integers(0, 500), min_size=n, max_size=n))
+    ranks = [draw(st.lists(st.integers(1, 256), min_size=P, max_size=P)) for _ in range(n)]
+    widths = draw(st.lists(st.sampled_from([256, 512, 768]), min_size=P, max_size=P))
+    nb = draw(st.sampled_from([16, 32, 64]))
+    S = draw(st.integers(1, 5))
+    cmin = draw(st.sampled_from([16, 64, 256]))
+    cmax = cmin * draw(st.sampled_from([1, 4]))
+    off = [0]
+    for t in toks:
+        off.append(off[-1] + t)
+    return off, ranks, widths, PlanOpts(nano_rows=nb, gemm_rows=256, n_streams=S, chunk_min=cmin,
+                                         chunk_max=cmax, chunk_per_rank=draw(st.sampled_from([1, 8])))
+
+
+@settings(max_examples=150, deadline=None)
+@given(multi_inputs())
+def test_plan_invariants_several_projections(args):
+    off, ranks, widths, opts = args
+    p = build_plan(off, ranks, opts, widths=widths)
+    pins_plan.check_invariants(plan_mirror, off, ranks, opts, p, widths=widths)
