@@ -46,7 +46,8 @@ class PlanInfo(ctypes.Structure):
                 ("rpad_total", ctypes.c_int64), ("partial_rows", ctypes.c_int64),
                 ("n_nano", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
                 ("n_tiles", ctypes.c_int64), ("n_ext", ctypes.c_int64),
-                ("n_opt_blocks", ctypes.c_int64), ("n_proj", ctypes.c_int64)]
+                ("n_opt_blocks", ctypes.c_int64), ("n_proj", ctypes.c_int64),
+                ("dz_offset", ctypes.c_int64)]
 
 
 class AdamwHparams(ctypes.Structure):

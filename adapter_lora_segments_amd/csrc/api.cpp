@@ -385,6 +385,7 @@ mlora_status mlora_plan_get_info(mlora_plan_t p, mlora_plan_info* info) {
   i.n_ext = P.n_ext();
   i.n_opt_blocks = P.n_oblk();
   i.n_proj = P.nproj;
+  i.dz_offset = (int64_t)p->L.dz;
   *info = i;
   return MLORA_OK;
 }

@@ -61,6 +61,12 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
       err = "d_in and every output width must be positive";
       return MLORA_ERR_INVALID_ARG;
     }
+    // bounded before the sum, so no width can overflow it
+    if (widths[q] > (1 << 20)) {
+      err = "every output width must be at most 2^20 (width " + std::to_string(q) + " is " +
+            std::to_string(widths[q]) + ")";
+      return MLORA_ERR_UNSUPPORTED;
+    }
     d_out += widths[q];
   }
   if (d_in <= 0) {

@@ -214,6 +214,9 @@ typedef struct {
   int64_t n_nano, n_chunks, n_tiles, n_ext;
   int64_t n_opt_blocks;      /* optimizer work items (0: layer too large, see mlora_adamw_step) */
   int64_t n_proj;            /* projections sharing the input (1 unless mlora_plan_multi) */
+  int64_t dz_offset;         /* byte offset in the workspace of dZ = s dY B^T (PLoRA §9.2,
+                                Case 2) as the last backward left it: z_elems elements in
+                                the layout of Z' (plan dtype), padding columns zero */
 } mlora_plan_info;
 
 mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);

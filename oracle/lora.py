@@ -181,36 +181,6 @@ def sampled_rows(rows, X, W0, A, B, scales, offsets, dY=None, dtype="fp32", with
     return Y, dX
 
 
-def projected_grads(X, dY, A, B, scales, offsets, U, V, dtype="fp32", chunk=CHUNK):
-    """dA_i u_i and dB_i v_i for given vectors u_i (length r_i) and v_i
-    (length d_out), float64, without forming dA_i or dB_i.
-
-    From the definitions above, dA_i = s_i X_i^T dY_i B_i^T and
-    dB_i = s_i A_i^T X_i^T dY_i, so
-        dA_i u = s_i X_i^T (dY_i (B_i^T u)),   dB_i v = s_i A_i^T (X_i^T (dY_i v)),
-    each a chain of matrix-vector products over the adapter's rows.  A
-    random u, v turns a full-size gradient check into these products
-    (Freivalds' check).  Streams over row chunks."""
-    out_a, out_b = [], []
-    for i, (lo, hi) in enumerate(_segments(offsets)):
-        Ai = as_f64(A[i], dtype)
-        Bi = as_f64(B[i], dtype)
-        s = float(scales[i])
-        bu = Bi.T @ np.asarray(U[i], dtype=np.float64)          # d_out
-        v = np.asarray(V[i], dtype=np.float64)                  # d_out
-        ga = np.zeros(Ai.shape[0])                              # X_i^T (dY_i B_i^T u)
-        gb = np.zeros(Ai.shape[0])                              # X_i^T (dY_i v)
-        for r0 in range(lo, hi, chunk):
-            r1 = min(hi, r0 + chunk)
-            Xc = as_f64(X[r0:r1], dtype)
-            Gc = as_f64(dY[r0:r1], dtype)
-            ga += Xc.T @ (Gc @ bu)
-            gb += Xc.T @ (Gc @ v)
-        out_a.append(s * ga)
-        out_b.append(s * (Ai.T @ gb))
-    return out_a, out_b
-
-
 def max_rel_err(got, ref) -> float:
     """Normwise-max relative error max|g - o| / max|o|.  With max|o| = 0 the
     result is 0 if g is all zero and +inf otherwise."""

@@ -147,34 +147,3 @@ def sampled_rows_multi(rows, X, W0, A, B, scales, offsets, widths, dY=None, dtyp
             if g is not None:
                 dX[ks] += g[:, c0:c1] @ W[:, c0:c1].T + (s * (g[:, c0:c1] @ Bip.T)) @ Aip.T
     return Y, dX, Zs
-
-
-def projected_grads_multi(X, dY, A, B, scales, offsets, widths, U, V, dtype="fp32", chunk=CHUNK):
-    """dA_ip u_ip and dB_ip v_ip for vectors u_ip (length r_ip) and v_ip
-    (length d_p), without forming the gradients:
-        dA_ip u = s_ip X_i^T (dY_i[:, cols_p] (B_ip^T u)),
-        dB_ip v = s_ip A_ip^T (X_i^T (dY_i[:, cols_p] v)).
-    Returns nested lists [adapter][projection]."""
-    cols = columns(widths)
-    P = len(widths)
-    out_a, out_b = [], []
-    for i, (lo, hi) in enumerate(_segments(offsets)):
-        ra, rb = [], []
-        bus = [as_f64(B[i][p], dtype).T @ np.asarray(U[i][p], dtype=np.float64) for p in range(P)]
-        ga = [np.zeros(np.asarray(A[i][p]).shape[0]) for p in range(P)]
-        gb = [np.zeros(np.asarray(A[i][p]).shape[0]) for p in range(P)]
-        for r0 in range(lo, hi, chunk):
-            r1 = min(hi, r0 + chunk)
-            Xc = as_f64(X[r0:r1], dtype)
-            Gc = as_f64(dY[r0:r1], dtype)
-            for p in range(P):
-                Gp = Gc[:, cols[p]:cols[p + 1]]
-                ga[p] += Xc.T @ (Gp @ bus[p])
-                gb[p] += Xc.T @ (Gp @ np.asarray(V[i][p], dtype=np.float64))
-        for p in range(P):
-            s = float(scales[i][p])
-            ra.append(s * ga[p])
-            rb.append(s * (as_f64(A[i][p], dtype).T @ gb[p]))
-        out_a.append(ra)
-        out_b.append(rb)
-    return out_a, out_b

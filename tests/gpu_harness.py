@@ -61,6 +61,7 @@ def run_gpu(w: Workload, proj=0, w0_layout="kn", n_streams=None, nano_rows=0, h=
     dX = layer.backward(dY, X, want_dx=want_dx)
     torch.cuda.synchronize()
     out = {
+        "dZ": workspace_dz(plan, layer),
         "Y": to_host_f64(Y),
         "dX": to_host_f64(dX) if want_dx else None,
         "dA": [to_host_f64(t) for t in layer.dA],
@@ -71,6 +72,17 @@ def run_gpu(w: Workload, proj=0, w0_layout="kn", n_streams=None, nano_rows=0, h=
         "dev": dict(X=X, dY=dY, Y=Y, dX=dX),
     }
     return h, out
+
+
+def workspace_dz(plan, layer):
+    """dZ = s dY B^T as the last backward left it in the workspace (layout of
+    Z'), float64 on the host."""
+    import torch
+    i = plan.info
+    esz = 2 if plan.dtype == "bf16" else 4
+    raw = layer.ws[i["dz_offset"]:i["dz_offset"] + i["z_elems"] * esz]
+    t = raw.view(torch.bfloat16 if esz == 2 else torch.float32)
+    return to_host_f64(t)
 
 
 def compare(w: Workload, h, out, tol=None, what=""):
@@ -95,6 +107,10 @@ def compare(w: Workload, h, out, tol=None, what=""):
         zi = out["Z"][zoff[i]:zoff[i] + n_i * rpad[i]].reshape(n_i, rpad[i])
         errs[f"Z{i}"] = ol.max_rel_err(zi[:, :r], float(h["scales"][i]) * Zs[i])
         assert np.all(zi[:, r:] == 0.0), f"{what}: padded Z columns of adapter {i} not zero"
+        # the backward's intermediate dZ_i = s_i dY_i B_i^T (PLoRA §9.2, Case 2)
+        dzi = out["dZ"][zoff[i]:zoff[i] + n_i * rpad[i]].reshape(n_i, rpad[i])
+        errs[f"dZ{i}"] = ol.max_rel_err(dzi[:, :r], dZ[i])
+        assert np.all(dzi[:, r:] == 0.0), f"{what}: padded dZ columns of adapter {i} not zero"
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
     worst = max(errs.items(), key=lambda kv: kv[1])
     say(f"  {what}: worst {worst[0]} = {worst[1]:.3e} (tol {tol:.0e})")

@@ -325,21 +325,6 @@ def pin_sampled_z_rows(ol):
         _close(zr[k], float(c["s"][i]) * Zs[i][t - c["off"][i]], 1e-13, "sampled Z")
 
 
-def pin_projected_grads(ol):
-    # Freivalds' check: the projected gradients equal the full gradients
-    # times the same random vectors, including an empty adapter and a chunk
-    # smaller than an adapter (so the row streaming is exercised)
-    c = rand_case(11, 12, 10, [3, 5, 2, 4], [6, 0, 9, 3])
-    _, dA, dB, _ = _bwd(ol, c)
-    rng = np.random.default_rng(5)
-    U = [rng.standard_normal(a.shape[1]) for a in c["A"]]
-    V = [rng.standard_normal(c["W0"].shape[1]) for _ in c["A"]]
-    pa, pb = ol.projected_grads(c["X"], c["dY"], c["A"], c["B"], c["s"], c["off"], U, V, chunk=4)
-    for i in range(len(c["A"])):
-        _close(pa[i], dA[i] @ U[i], 1e-12, "projected dA")
-        _close(pb[i], dB[i] @ V[i], 1e-12, "projected dB")
-
-
 def pin_bf16_decode(ol):
     # bf16 bit patterns: 0x3F80 = 1.0, 0xC000 = -2.0, 0x3E80 = 0.25, 0x0000 = 0.
     bits = np.asarray([[0x3F80, 0xC000], [0x3E80, 0x0000]], dtype=np.uint16)
@@ -410,4 +395,4 @@ def pin_ids_sorted_is_segments(ol):
 ALL_PINS = [pin_ids_golden_order, pin_ids_brute_force, pin_ids_sorted_is_segments, pin_hand_example, pin_b_zero, pin_fused_equals_sequential, pin_finite_differences,
             pin_merged_weight, pin_brute_force, pin_rank_padding, pin_permutation,
             pin_scale_linearity, pin_torch_autograd, pin_sampled_rows, pin_sampled_z_rows,
-            pin_projected_grads, pin_bf16_decode]
+            pin_bf16_decode]

@@ -12,7 +12,7 @@ it disagrees with:
   Y_i = X_i W0 + (X_i [A_i1 .. A_iP]) blockdiag(s_i1 B_i1, .., s_iP B_iP),
   differentiated through L = sum(dY * Y);
 - pure-Python loops on tiny shapes;
-- the sampled-row and projected-gradient forms against the whole results.
+- the sampled-row form against the whole results.
 """
 from __future__ import annotations
 
@@ -158,7 +158,7 @@ def pin_multi_brute_force(om):
                     assert abs(gb - dB[i][p][q][o - cols[p]]) < 1e-12, ("dB", i, p, q, o)
 
 
-def pin_multi_sampled_and_projected(om):
+def pin_multi_sampled(om):
     widths = [4, 8]
     ranks = [[2, 1], [3, 5], [1, 2]]
     c = _case(5, 12, widths, ranks, [6, 0, 9])
@@ -173,15 +173,7 @@ def pin_multi_sampled_and_projected(om):
         i = own[k]
         for p in range(2):
             _close(Zs[k][p], c["s"][i][p] * Z[i][p][t - c["off"][i]], 1e-12, f"sampled Z row {t}")
-    rng = np.random.default_rng(9)
-    U = [[rng.standard_normal(ranks[i][p]) for p in range(2)] for i in range(3)]
-    V = [[rng.standard_normal(widths[p]) for p in range(2)] for i in range(3)]
-    ga, gb = om.projected_grads_multi(c["X"], c["dY"], c["A"], c["B"], c["s"], c["off"], widths, U, V, chunk=4)
-    for i in range(3):
-        for p in range(2):
-            _close(ga[i][p], dA[i][p] @ U[i][p], 1e-12, f"dA u {i},{p}")
-            _close(gb[i][p], dB[i][p] @ V[i][p], 1e-12, f"dB v {i},{p}")
 
 
 ALL_PINS = [pin_multi_one_projection, pin_multi_equals_per_projection_layers, pin_multi_torch_block_diagonal,
-            pin_multi_brute_force, pin_multi_sampled_and_projected]
+            pin_multi_brute_force, pin_multi_sampled]

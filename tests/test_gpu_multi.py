@@ -9,14 +9,16 @@
   visit the same extension steps, nano-batches and chunks in the same
   order); dX, a sum over projections, agrees within the bar.
 - Full size, in the bench's launch configuration: the q/k/v and gate/up
-  groups of the Llama-3-8B-shaped layer (16 adapters, 34816 rows), on
-  sampled rows and through random projections of every dA and dB."""
+  groups of the Llama-3-8B-shaped layer (16 adapters, 34816 rows): every
+  pair's dA, dB and dZ element by element, and Y, dX and Z' on each
+  adapter's first and last row plus 32 seeded rows inside it."""
 import numpy as np
 import pytest
 
 from oracle import lora as ol
 from oracle import multi as om
-from tests.gpu_harness import TOL, say, to_dev, to_host_f64
+from tests.gpu_harness import TOL, say, to_dev, to_host_f64, workspace_dz
+from tests.test_gpu_fullsize import stratified_rows
 from workloads.multi import host_multi
 
 CASES = [
@@ -147,18 +149,19 @@ def test_multi_full_size_llama3(group):
     Ah = [[_bits(a) for a in row] for row in d["A"]]
     Bh = [[_bits(b) for b in row] for row in d["B"]]
     rng = np.random.default_rng(23)
-    rows = []
-    for i in range(w.n):
-        if off[i + 1] > off[i]:
-            rows += [int(off[i]), int(off[i + 1]) - 1, int(rng.integers(off[i], off[i + 1]))]
-    rows = np.unique(np.asarray(rows, dtype=np.int64))
+    rows = stratified_rows(off, rng)
     rt = torch.from_numpy(rows).cuda()
+    gY = Y.index_select(0, rt).float().cpu().numpy()
+    gdX = dX.index_select(0, rt).float().cpu().numpy()
+    Zd = layer.Z.float().cpu().numpy()
+    dZd = workspace_dz(plan, layer)
+    gA = [t.double().cpu().numpy() for t in layer.dA]
+    gB = [t.double().cpu().numpy() for t in layer.dB]
+    say(f"  GPU done; oracle on {len(rows)} rows and the full weight gradients")
     Ys, dXs, Zs = om.sampled_rows_multi(rows, Xh, W0h, Ah, Bh, d["scales"], off, widths, dY=dYh, dtype="bf16")
-    errs = {"Y": ol.max_rel_err(Y.index_select(0, rt).float().cpu().numpy(), Ys),
-            "dX": ol.max_rel_err(dX.index_select(0, rt).float().cpu().numpy(), dXs)}
+    errs = {"Y": ol.max_rel_err(gY, Ys), "dX": ol.max_rel_err(gdX, dXs)}
     P = len(widths)
     zoff, rpad = plan.export("zoff"), plan.export("rpad")
-    Zd = layer.Z.float().cpu().numpy()
     own = np.searchsorted(off, rows, side="right") - 1
     gz, wz = [], []
     for k, (t, i) in enumerate(zip(rows, own)):
@@ -167,15 +170,17 @@ def test_multi_full_size_llama3(group):
             gz.append(Zd[zoff[v] + (t - off[i]) * rpad[v]:][:d["ranks"][i][q]])
             wz.append(Zs[k][q])
     errs["Z"] = ol.max_rel_err(np.concatenate(gz), np.concatenate(wz))
-    U = [[rng.standard_normal(d["ranks"][i][q]) for q in range(P)] for i in range(w.n)]
-    V = [[rng.standard_normal(widths[q]) for q in range(P)] for i in range(w.n)]
-    pa, pb = om.projected_grads_multi(Xh, dYh, Ah, Bh, d["scales"], off, widths, U, V, dtype="bf16", chunk=1024)
+    _, dA, dB, dZ = om.backward_multi(dYh, Xh, W0h, Ah, Bh, d["scales"], off, widths, "bf16", want_dx=False)
     for i in range(w.n):
+        n_i = int(off[i + 1] - off[i])
         for q in range(P):
-            v = i * P + q
-            errs[f"dA{i},{q}.u"] = ol.max_rel_err(layer.dA[v].double().cpu().numpy() @ U[i][q], pa[i][q])
-            errs[f"dB{i},{q}.v"] = ol.max_rel_err(layer.dB[v].double().cpu().numpy() @ V[i][q], pb[i][q])
+            v, r = i * P + q, int(d["ranks"][i][q])
+            errs[f"dA{i},{q}"] = ol.max_rel_err(gA[v], dA[i][q])
+            errs[f"dB{i},{q}"] = ol.max_rel_err(gB[v], dB[i][q])
+            dzv = dZd[zoff[v]:zoff[v] + n_i * rpad[v]].reshape(n_i, rpad[v])
+            errs[f"dZ{i},{q}"] = ol.max_rel_err(dzv[:, :r], dZ[i][q])
+            assert np.all(dzv[:, r:] == 0.0), f"padded dZ columns of pair {v} not zero"
     worst = max(errs.items(), key=lambda kv: kv[1])
-    say(f"  {group}: {len(rows)} sampled rows, worst {worst[0]} = {worst[1]:.3e}")
+    say(f"  {group}: {len(rows)} rows, every dA/dB/dZ element, worst {worst[0]} = {worst[1]:.3e}")
     bad = {k: e for k, e in errs.items() if not e <= TOL["bf16"]}
     assert not bad, bad

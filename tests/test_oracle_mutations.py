@@ -33,10 +33,6 @@ MUTATIONS = {
                         "        s = float(scales[i])\n        Zi"),
     "wrong_scale_index": ("s = float(scales[i])\n        Zi", "s = float(scales[0])\n        Zi"),
     "bf16_decode_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
-    "proj_da_drop_scale": ("out_a.append(s * ga)", "out_a.append(ga)"),
-    "proj_db_wrong_vector": ("gb += Xc.T @ (Gc @ v)", "gb += Xc.T @ (Gc @ bu)"),
-    "proj_chunk_tail_lost": ("            r1 = min(hi, r0 + chunk)\n            Xc = as_f64(X[r0:r1], dtype)\n            Gc",
-                             "            r1 = min(hi - 1, r0 + chunk)\n            Xc = as_f64(X[r0:r1], dtype)\n            Gc"),
     "sampled_z_no_scale": ("zi = s * (x @ Ai)", "zi = (x @ Ai)"),
     "ids_unstable_sort": ('perm = np.argsort(ids, kind="stable")', 'perm = np.argsort(-ids, kind="stable")[::-1]'),
     "ids_offsets_shift": ("offsets[1:] = np.cumsum(np.bincount(ids, minlength=n))",
@@ -79,8 +75,6 @@ MULTI_MUTATIONS = {
     "db_drop_scale": ("gB += s * (Zc.T @ Gp)", "gB += (Zc.T @ Gp)"),
     "columns_off_by_one": ("        c.append(c[-1] + int(d))", "        c.append(c[-1] + int(d) - (1 if len(c) == 2 else 0))"),
     "sampled_dx_overwrites": ("dX[ks] += g[:, c0:c1] @ W[:, c0:c1].T", "dX[ks] = g[:, c0:c1] @ W[:, c0:c1].T"),
-    "projected_db_wrong_accumulator": ("rb.append(s * (as_f64(A[i][p], dtype).T @ gb[p]))",
-                                       "rb.append(s * (as_f64(A[i][p], dtype).T @ ga[p]))"),
 }
 
 
