@@ -20,9 +20,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmlora.so")
+PROBES_LIB = os.path.join(PKG, "libmlora_probes.so")
 
 SOURCES = ["plan.cpp", "api.cpp", "kernels_bf16.hip", "kernels_fp32.hip", "kernels_adamw.hip",
            "kernels_mx.hip"]
+# measured-ceiling probes (include/mlora_probes.h), a library of their own
+PROBE_SOURCES = ["probes.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -54,16 +57,17 @@ def build(jobs: int = 4, verbose: bool = True) -> str:
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + objs + \
-        ["-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    shutil.move(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    for lib, parts in ((LIB, objs[:len(SOURCES)]), (PROBES_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + parts + \
+            ["-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+        shutil.move(tmp, lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 

@@ -38,11 +38,14 @@ def gemm_fwd_flops(w, proj):
     return 2 * w.T * p.d_in * p.d_out + sum(2 * n * r * p.d_out for n, r in zip(w.tokens, w.ranks))
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, layout: str = "kn"):
     """HBM bytes per forward-GEMM launch from the committed counter summary
-    (profiles/hbm_bytes_<workload>.txt), or None when that file is missing or
-    was taken from a different version of the kernel source."""
+    (profiles/hbm_bytes_<workload>.txt), or None when that file is missing,
+    covers another W0 layout, or was taken from a different version of the
+    kernel source."""
     import hashlib
+    if layout != "kn":
+        return None
     path = os.path.join(ROOT, "profiles", f"hbm_bytes_{workload}.txt")
     src = os.path.join(ROOT, "adapter_lora_segments_amd", "csrc", "kernels_bf16.hip")
     if not os.path.exists(path):
@@ -111,31 +114,117 @@ def kernel_rooflines(w, units, kern, iso, steps, w0_format="bf16"):
     return out
 
 
-def cpu_baseline(w, projs, flop_budget=2.0e12):
-    """The oracle (numpy float64) on the host over a bounded sample of the
-    workload: the first M tokens of every timed projection, M chosen so the
-    sample is about ``flop_budget`` floating-point operations (10-30 s on a
-    host), or the whole workload when it is smaller."""
+def _oracle_step_seconds(w, projs):
+    """One oracle forward+backward over every listed projection of ``w``
+    (host tensors drawn first, not timed)."""
     from oracle import lora as ol
     from workloads.tensors import host_tensors
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:
-        threads = os.cpu_count()
-    per_token = sum(4.0 * w.projections[q].d_in * w.projections[q].d_out for q in projs)
-    M = int(min(w.T, max(256, flop_budget // per_token)))
     dt = 0.0
     for q in projs:
-        h = host_tensors(w, q, rows=M)
+        h = host_tensors(w, q)
         t0 = time.perf_counter()
         ol.forward(h["X"], h["W0"], h["A"], h["B"], h["scales"], h["offsets"], w.dtype)
         ol.backward(h["dY"], h["X"], h["W0"], h["A"], h["B"], h["scales"], h["offsets"], w.dtype)
         dt += time.perf_counter() - t0
-    what = "the whole workload" if M == w.T else f"the first {M} of {w.T} tokens"
-    return {"value": M / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one forward+backward of {what} over {len(projs)} projection(s) "
-                      f"in float64 numpy, {dt:.2f} s"}
+    return dt
+
+
+def cpu_baseline(w, projs, flop_budget=2.0e12):
+    """The oracle (numpy float64) on the host over a bounded sample of the
+    workload: the same layer shapes, adapters and ranks with every adapter's
+    token count scaled down in proportion (at least one token each), chosen
+    so the sample is about ``flop_budget`` floating-point operations (10-30 s
+    on a host); the whole workload when it is smaller.  Beside it, the oracle
+    on one thread on the two smallest workloads (the fp32 256x256 layer
+    whole, and the 4096x4096 layer on 1024 sampled tokens)."""
+    from workloads import load_workload
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threadpool_limits = None
+        threads = os.cpu_count()
+    per_token = sum(4.0 * w.projections[q].d_in * w.projections[q].d_out for q in projs)
+    M = int(min(w.T, max(256, flop_budget // per_token)))
+    sample = w.scaled_down(M)
+    dt = _oracle_step_seconds(sample, projs)
+    what = "the whole workload" if sample.T == w.T else \
+        f"{sample.T} of {w.T} tokens (every adapter's tokens scaled by {M}/{w.T}, at least one each)"
+    out = {"value": sample.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"one forward+backward of {what} over {len(projs)} projection(s) "
+                     f"in float64 numpy, {dt:.2f} s"}
+    if threadpool_limits is not None:
+        one = {}
+        with threadpool_limits(limits=1):
+            for name, rows in (("tiny_fp32", None), ("llama7b_proj", 1024)):
+                wl = load_workload(name, 0)
+                if rows:
+                    wl = wl.scaled_down(rows)
+                t = _oracle_step_seconds(wl, [0])
+                one[name] = {"value": wl.T / t, "unit": "tokens/s", "tokens": wl.T, "seconds": t}
+        out["one_thread"] = one
+    return out
+
+
+def ceilings(random_only=False):
+    """Measured ceilings of this GPU (libmlora_probes.so): the pure-MFMA loop
+    in the base GEMM's instruction pattern with random and with zero bf16
+    operands (TFLOP/s), and streaming copy and read bandwidth (GB/s), each the
+    best of several timed launches on torch's current stream."""
+    import ctypes
+    import torch
+    from adapter_lora_segments_amd import _lib
+    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libmlora_probes.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with `python -m adapter_lora_segments_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.mlora_probe_mfma.argtypes = [i64, i64, vp, vp, vp]
+    L.mlora_probe_copy.argtypes = [vp, vp, i64, vp]
+    L.mlora_probe_read.argtypes = [vp, i64, vp, vp]
+    for f in (L.mlora_probe_mfma, L.mlora_probe_copy, L.mlora_probe_read):
+        f.restype = ctypes.c_int
+    stream = vp(torch.cuda.current_stream().cuda_stream)
+
+    def best(launch, reps=6):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = launch()
+            b.record()
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: hipError {rc}")
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return min(ts[1:])                       # the first launch warms up
+
+    out = {}
+    n_wg, iters = 1024, 8192
+    flops = n_wg * 4 * iters * 16 * 32768
+    res = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(3)
+    ops = {"random": torch.randn(4096, generator=g, device="cuda").to(torch.bfloat16),
+           "zeros": torch.zeros(4096, dtype=torch.bfloat16, device="cuda")}
+    for name, op in ops.items():
+        if random_only and name != "random":
+            continue
+        ms = best(lambda: L.mlora_probe_mfma(n_wg, iters, vp(op.data_ptr()), vp(res.data_ptr()), stream))
+        out[f"mfma_bf16_{name}_operands"] = {"achieved": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                                            "ms": ms}
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = best(lambda: L.mlora_probe_copy(vp(src.data_ptr()), vp(dst.data_ptr()), nbytes, stream))
+    out["hbm_copy"] = {"achieved": 2 * nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms": ms,
+                       "bytes_per_launch": 2 * nbytes}
+    red = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    ms = best(lambda: L.mlora_probe_read(vp(src.data_ptr()), nbytes, vp(red.data_ptr()), stream))
+    out["hbm_read"] = {"achieved": (nbytes + red.numel() * 4) / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms": ms,
+                       "bytes_per_launch": nbytes + red.numel() * 4}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_steps(step, steps, warmup):
@@ -372,12 +461,20 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="llama7b_proj")
+    ap.add_argument("--workload", default="mlp70b_pair")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--streams", type=int, default=0)
     ap.add_argument("--all-projections", action="store_true",
-                    help="time every projection of the workload in each step (tokens/s per layer "
-                         "= T / the summed forward+backward time); default: the first projection")
+                    help="time every projection of the workload in each step (the default)")
+    ap.add_argument("--first-projection", action="store_true",
+                    help="time only the workload's first projection (tokens/s per layer is otherwise "
+                         "T / the summed forward+backward time of every projection)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure this GPU's MFMA and HBM ceilings (libmlora_probes.so); one JSON line")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip measuring the MFMA and HBM ceilings beside the roofline")
+    ap.add_argument("--no-one-group", action="store_true",
+                    help="with several stream groups, skip timing the same layers planned as one group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one elementwise copy kernel (torch.neg on float32) reading and "
@@ -440,6 +537,10 @@ def main():
                           "unit": "ms", "steps": steps, "data": "synthetic", "dtype": "bf16",
                           "results": rows}), flush=True)
         return
+    if a.ceilings:
+        print(json.dumps({"metric": "measured ceilings of this GPU", "data": "synthetic",
+                          "ceilings": ceilings()}), flush=True)
+        return
     if a.packing_sweep:
         steps = min(a.steps, 20)
         rows = packing_sweep(steps, min(a.warmup, 5))
@@ -462,47 +563,61 @@ def main():
         if a.fused or a.shuffled_ids:
             print(f"--w0-format {a.w0_format} runs with segment plans of single projections", file=sys.stderr)
             sys.exit(2)
-    projs = list(range(len(w.projections))) if a.all_projections else [0]
+    projs = [0] if a.first_projection else list(range(len(w.projections)))
     SETS = 4
     layers = []
     groups = LAYER_GROUPS.get(w.name) if a.fused else None
     if a.fused and not groups:
         print(f"--fused: {w.name} has no projections that share an input", file=sys.stderr)
         sys.exit(2)
+    # device inputs (drawn once) and output buffers, shared by every plan built over them
+    datas = []
     for gname, gp in (groups or []):
         d = device_multi(w, gp, sets=SETS)
-        plan = Plan.multi(d["offsets"], d["ranks"], d["d_in"], d["widths"], "bf16",
-                          n_streams=a.streams or w.n_streams)
-        flat = lambda nested: [x for row in nested for x in row]
-        layer = PackedLoRALinear(plan, d["W0"], flat(d["A"]), flat(d["B"]), flat(d["scales"]))
         D = sum(d["widths"])
-        Ys = [torch.empty((w.T, D), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
-        dXs = [torch.empty((w.T, d["d_in"]), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
-        layers.append((plan, layer, d, Ys, dXs))
+        datas.append(("multi", d, [torch.empty((w.T, D), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)],
+                      [torch.empty((w.T, d["d_in"]), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]))
     for q in (projs if not groups else []):
         p = w.projections[q]
         d = device_tensors(w, q, sets=SETS)
-        if a.shuffled_ids:
-            ids = np.repeat(np.arange(w.n), np.diff(np.asarray(d["offsets"])))
-            ids = ids[np.random.default_rng(a.seed).permutation(w.T)]
-            plan = Plan.from_ids(ids, d["ranks"], p.d_in, p.d_out, "bf16",
-                                 n_streams=a.streams or w.n_streams, w0_layout=a.w0_layout)
-        else:
-            plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16",
-                        n_streams=a.streams or w.n_streams, w0_format=a.w0_format,
-                        w0_layout=a.w0_layout if not mx else "kn")
-        W0 = d["W0"] if a.w0_layout != "nk" or mx else d["W0"].t().contiguous()
         if mx:
-            W0 = (quantize_mx4_device if a.w0_format == "mxfp4" else quantize_mx_device)(d["W0"], "kn")
-            d["W0_bytes"] = W0.numel()
-        layer = PackedLoRALinear(plan, W0, d["A"], d["B"], d["scales"])
-        Ys = [torch.empty((w.T, p.d_out), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
-        dXs = [torch.empty((w.T, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]
-        layers.append((plan, layer, d, Ys, dXs))
+            d["W0_codes"] = (quantize_mx4_device if a.w0_format == "mxfp4" else quantize_mx_device)(d["W0"], "kn")
+            d["W0_bytes"] = d["W0_codes"].numel()
+        datas.append(("single", d, [torch.empty((w.T, p.d_out), dtype=torch.bfloat16, device="cuda")
+                                    for _ in range(SETS)],
+                      [torch.empty((w.T, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]))
 
-    def step(i):
+    def make_layers(n_streams):
+        out = []
+        for kind, d, Ys, dXs in datas:
+            if kind == "multi":
+                plan = Plan.multi(d["offsets"], d["ranks"], d["d_in"], d["widths"], "bf16", n_streams=n_streams)
+                flat = lambda nested: [x for row in nested for x in row]
+                layer = PackedLoRALinear(plan, d["W0"], flat(d["A"]), flat(d["B"]), flat(d["scales"]))
+            else:
+                if a.shuffled_ids:
+                    ids = np.repeat(np.arange(w.n), np.diff(np.asarray(d["offsets"])))
+                    ids = ids[np.random.default_rng(a.seed).permutation(w.T)]
+                    plan = Plan.from_ids(ids, d["ranks"], d["d_in"], d["d_out"], "bf16", n_streams=n_streams,
+                                         w0_layout=a.w0_layout)
+                else:
+                    plan = Plan(d["offsets"], d["ranks"], d["d_in"], d["d_out"], "bf16", n_streams=n_streams,
+                                w0_format=a.w0_format, w0_layout=a.w0_layout if not mx else "kn")
+                if mx:
+                    W0 = d["W0_codes"]
+                elif a.w0_layout == "nk":
+                    W0 = d.setdefault("W0_nk", d["W0"].t().contiguous())
+                else:
+                    W0 = d["W0"]
+                layer = PackedLoRALinear(plan, W0, d["A"], d["B"], d["scales"])
+            out.append((plan, layer, d, Ys, dXs))
+        return out
+
+    layers = make_layers(a.streams or w.n_streams)
+
+    def step(i, lays=None):
         k = i % SETS
-        for plan, layer, d, Ys, dXs in layers:
+        for plan, layer, d, Ys, dXs in (lays if lays is not None else layers):
             layer.forward(d["X"][k], Ys[k])
             layer.backward(d["dY"][k], d["X"][k], dXs[k])
 
@@ -578,6 +693,31 @@ def main():
         torch.cuda.synchronize()
         iso = {k: (v[0] / nb * a.steps, v[1]) for k, v in collect().items()}
         profile(False)
+
+    # The same layers planned as one stream group, timed the same way; with
+    # several groups the forward-GEMM launches of different groups overlap on
+    # their streams, so the roofline's per-launch time is taken here, where
+    # each launch has the chip to itself.
+    one_group = None
+    if not a.no_one_group and any(pl.info["n_groups"] > 1 for pl, *_ in layers):
+        ones = make_layers(1)
+        for i in range(a.warmup):
+            step(i, ones)
+        for j, (plan, *_) in enumerate(ones):
+            plan.profile_enable(["gemm_fwd"] if prof and j == 0 else False)
+            plan.profile_read()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(a.steps):
+            step(i, ones)
+        torch.cuda.synchronize()
+        el1 = time.perf_counter() - t0
+        if prof:
+            gemm_rec = ones[0][0].profile_read()["gemm_fwd"]
+            ones[0][0].profile_enable(False)
+        one_group = {"ms_per_step": el1 / a.steps * 1e3, "tokens_per_s": w.T * a.steps / el1,
+                     "note": "the same layers, inputs and steps planned as one stream group"}
+        del ones
 
     seq_ms = None
     if not a.no_sequential and not a.shuffled_ids:
@@ -655,7 +795,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": (f"{w.name}: {p0.d_in}x{p0.d_out} bf16, " if len(projs) == 1 else
                                 f"{w.name}: projections {shapes}, bf16, ") +
-                               f"{w.n} adapters, ranks {sorted(set(w.ranks))}, {w.T} tokens (seed {w.seed})",
+                               f"{w.n} adapters, ranks {sorted(set(w.ranks))}, {w.T} tokens (seed {w.seed}), "
+                               f"{layers[0][0].info['n_groups']} stream group(s)" +
+                               (f"; one_group: the same planned as one stream group" if one_group else ""),
                    "T": w.T, "d_in": p0.d_in, "d_out": p0.d_out, "adapters": w.n,
                    "projections": [w.projections[q].name for q in projs],
                    "streams": layers[0][0].info["n_groups"],
@@ -669,19 +811,32 @@ def main():
         out["kernels_ms_per_step"] = {k: v[0] / a.steps for k, v in kern.items() if v[1]}
         units = [gp for _, gp in groups] if groups else [[q] for q in projs]
         out["kernel_rooflines"] = kernel_rooflines(w, units, kern, iso, a.steps, a.w0_format)
+    if one_group is not None:
+        out["one_group"] = one_group
+    ceil = None if a.no_ceilings else ceilings()
+    if ceil is not None:
+        out["ceilings"] = ceil
     if prof:
         g_ms, g_n = gemm_rec
         if g_n:
             avg = g_ms / g_n
+            per_step = g_n / a.steps      # launches of the first layer's forward GEMM per step
             first = groups[0][1] if groups else [0]
-            ach = sum(gemm_fwd_flops(w, q) for q in first) / (avg * 1e-3) / 1e12
+            ach = sum(gemm_fwd_flops(w, q) for q in first) / per_step / (avg * 1e-3) / 1e12
             kname = "+".join(w.projections[q].name for q in first)
             out["roofline"] = {"kernel": f"k_gemm<fwd> (base GEMM + fused expand) of {kname} "
                                          f"{p0.d_in}x{sum(w.projections[q].d_out for q in first)}",
                                "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                               "traffic": None if groups else measured_traffic(w.name),
-                               "avg_launch_ms": avg}
+                               "traffic": None if groups else measured_traffic(w.name, a.w0_layout),
+                               "avg_launch_ms": avg,
+                               "timed_in": "one-group pass" if one_group is not None else "the timed steps"}
+            if per_step > 1:
+                out["roofline"]["note"] = "several group launches per step that overlap on their streams"
+            if ceil is not None:
+                mp = ceil["mfma_bf16_random_operands"]["achieved"]
+                out["roofline"]["measured_peak"] = mp
+                out["roofline"]["frac_measured"] = ach / mp
     if seq_ms is not None:
         out["packed_vs_sequential"] = {
             "projection": w.projections[projs[0]].name, "packed_ms_per_step": packed_ms,

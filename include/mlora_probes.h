@@ -1,0 +1,45 @@
+/*
+ * mlora_probes.h -- measured ceilings of the MI355X this library runs on, for
+ * reporting achieved rates against the machine as it behaves, beside the
+ * published peaks.  Not part of the layer: libmlora_probes.so, separate
+ * from libmlora.so.  Every call enqueues one kernel on `stream` (a
+ * hipStream_t as void*, NULL = null stream) and returns the hipError_t of
+ * the launch as an int (0 = success); a malformed call returns
+ * hipErrorInvalidValue (1) and launches nothing.
+ */
+#ifndef MLORA_PROBES_H
+#define MLORA_PROBES_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Pure-MFMA loop: n_wg workgroups of four waves, one per SIMD; each wave
+ * keeps sixteen 32x32 fp32 accumulators and issues `iters` rounds of
+ * sixteen independent v_mfma_f32_32x32x16_bf16 (the base GEMM's
+ * instruction and operand pattern, without memory traffic).  Work =
+ * n_wg * 4 * iters * 16 * 32768 flops.  operands: device, at least 8192
+ * bytes of bf16 values (random ones draw the power a real GEMM draws; zeros
+ * let the clock run higher); out: device, n_wg * 256 floats (a sum of the
+ * accumulators, so the loop is not removed).  n_wg in [1, 2^20], iters in
+ * [1, 2^24].
+ */
+int mlora_probe_mfma(int64_t n_wg, int64_t iters, const void *operands, float *out, void *stream);
+
+/* Streaming copy dst[i] = src[i] of `bytes` bytes (a multiple of 16, both
+ * 16-byte aligned, not overlapping) with 16-byte loads and stores: HBM
+ * traffic = 2 * bytes. */
+int mlora_probe_copy(const void *src, void *dst, int64_t bytes, void *stream);
+
+/* Streaming read of `bytes` bytes (a multiple of 16, 16-byte aligned) with
+ * 16-byte loads; each of the 2048 * 256 threads writes one float of its sum
+ * to out (device, 524288 floats): HBM traffic = bytes + 2 MiB. */
+int mlora_probe_read(const void *src, int64_t bytes, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLORA_PROBES_H */
