@@ -7,5 +7,5 @@ fails loudly if it has not been built.
 """
 from .binding import (Plan, PackedLoRALinear, AdamW, mlora_plan, mlora_forward,  # noqa: F401
                       mlora_backward, mlora_adamw_step, adamw_hparams, pointer_table, device_check,
-                      base_both, mlora_base_transpose)
+                      base_both, mlora_base_transpose, mlora_forward_noalloc)
 from ._lib import MloraError, lib  # noqa: F401

@@ -28,7 +28,7 @@ KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "pre
 EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_multi", "mlora_plan_multi_from_ids", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
            "mlora_plan_upload", "mlora_forward", "mlora_backward", "mlora_adamw_step", "mlora_profile_enable",
            "mlora_profile_read", "mlora_device_check", "mlora_status_string", "mlora_last_error",
-           "mlora_version", "mlora_base_transpose"]
+           "mlora_version", "mlora_base_transpose", "mlora_forward_noalloc"]
 
 
 class PlanOpts(ctypes.Structure):
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.mlora_plan_upload.restype = i32
     L.mlora_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.mlora_forward.restype = i32
+    L.mlora_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.mlora_forward_noalloc.restype = i32
     L.mlora_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.mlora_backward.restype = i32
     L.mlora_adamw_step.argtypes = [vp] + [vp] * 11 + [i32, vp, sz, vp]

@@ -272,6 +272,25 @@ def mlora_forward(plan: Plan, X, W0, A_ptrs, B_ptrs, scales, Y, Z, ws, stream=No
     return Y, Z
 
 
+def mlora_forward_noalloc(plan: Plan, X, W0, A_ptrs, B_ptrs, scales, Y, Z, stream=None):
+    """mlora_forward with the library's static scratch instead of a
+    workspace: nothing is allocated (layers whose buffers exceed the scratch
+    are refused)."""
+    torch = _torch()
+    i = plan.info
+    dt = _dt(plan)
+    _check_t(X, "X", (i["T"], i["d_in"]), dt)
+    _check_t(W0, "W0", _w0_shape(plan), _w0_dtype(plan))
+    _check_t(Y, "Y", (i["T"], i["d_out"]), dt)
+    _check_t(Z, "Z", None, dt, i["z_elems"])
+    for nm, t in (("A_ptrs", A_ptrs), ("B_ptrs", B_ptrs)):
+        _check_t(t, nm, (_npairs(plan),), torch.int64)
+    _check_t(scales, "scales", (_npairs(plan),), torch.float32)
+    check(lib().mlora_forward_noalloc(plan.handle, _p(X), _p(W0), _p(A_ptrs), _p(B_ptrs), _p(scales),
+                                      _p(Y), _p(Z), _stream(stream)))
+    return Y, Z
+
+
 def mlora_backward(plan: Plan, dY, X, W0, A_ptrs, B_ptrs, scales, Z, dX, dA_ptrs, dB_ptrs, ws,
                    stream=None):
     """dX (optional) and fp32 dA_i, dB_i through the pointer tables."""

@@ -230,10 +230,9 @@ mlora_status check_ws(const mlora_plan_s* p, void* ws, size_t ws_bytes) {
 
 // Decode of an MXFP8 or MXFP4 base (codes, then the E8M0 scales) into the
 // workspace's bf16 copy, in the base's layout.
-mlora_status decode_base(mlora_plan_s* p, const void* W0, uint8_t* wsb, bool nk, hipStream_t cs) {
+mlora_status decode_base(mlora_plan_s* p, const void* W0, uint16_t* w0deq, bool nk, hipStream_t cs) {
   const auto& P = p->P;
   const uint8_t* codes = static_cast<const uint8_t*>(W0);
-  uint16_t* w0deq = reinterpret_cast<uint16_t*>(wsb + p->L.w0deq);
   const bool fp4 = P.opts.w0_format == MLORA_W0_MXFP4;
   const int64_t code_bytes = fp4 ? P.d_in * P.d_out / 2 : P.d_in * P.d_out;
   return timed(p, MLORA_K_DEQUANT, cs, [&] {
@@ -451,25 +450,46 @@ mlora_status mlora_plan_upload(mlora_plan_t p, void* ws, size_t ws_bytes, void* 
   return MLORA_OK;
 }
 
-mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const void* const* A,
-                           const void* const* B, const float* scales, void* Y, void* Z, void* ws,
-                           size_t ws_bytes, void* stream) {
-  if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
+}  // extern "C"
+
+namespace {
+
+// Device buffers of one forward call: the uploaded plan tables (the
+// DevTables offsets are relative to their base), the rank-padded
+// concatenations the kernels read, the split-K partial tiles and, for a
+// microscaled base, its bf16 decoding.
+struct FwdBufs {
+  uint8_t* tables;
+  uint16_t* acat_t;
+  uint16_t* bcat_t;
+  float* kpart;
+  uint16_t* w0deq;
+};
+
+bool forward_args_ok(const mlora_plan_s* p, const void* X, const void* W0, const void* const* A,
+                     const void* const* B, const float* scales, const void* Y, const void* Z,
+                     mlora_status* st) {
   // With no rows at all, the row-indexed buffers may be NULL.
   const bool rows = p->P.T > 0;
-  if ((rows && (!X || !Y || !Z)) || !W0 || !A || !B || !scales)
-    return fail(MLORA_ERR_INVALID_ARG, "forward: X, W0, A, B, scales, Y and Z must be non-NULL");
-  for (const void* q : {X, W0, (const void*)A, (const void*)B, (const void*)scales, (const void*)Y, (const void*)Z})
-    if (!aligned16(q)) return fail(MLORA_ERR_INVALID_ARG, "forward: device pointers must be 16-byte aligned");
-  mlora_status st = check_ws(p, ws, ws_bytes);
-  if (st != MLORA_OK) return st;
+  if ((rows && (!X || !Y || !Z)) || !W0 || !A || !B || !scales) {
+    *st = fail(MLORA_ERR_INVALID_ARG, "forward: X, W0, A, B, scales, Y and Z must be non-NULL");
+    return false;
+  }
+  for (const void* q : {X, W0, (const void*)A, (const void*)B, (const void*)scales, Y, Z})
+    if (!aligned16(q)) {
+      *st = fail(MLORA_ERR_INVALID_ARG, "forward: device pointers must be 16-byte aligned");
+      return false;
+    }
+  return true;
+}
+
+mlora_status forward_impl(mlora_plan_s* p, const void* X, const void* W0, const void* const* A,
+                          const void* const* B, const float* scales, void* Y, void* Z, const FwdBufs& fb,
+                          hipStream_t cs) {
   const auto& P = p->P;
-  const auto& L = p->L;
-  hipStream_t cs = static_cast<hipStream_t>(stream);
-  st = check_capture(p, cs);
+  mlora_status st = check_capture(p, cs);
   if (st != MLORA_OK) return st;
-  mlora::DevTables t = dev_tables(p, ws);
-  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  mlora::DevTables t = dev_tables(p, fb.tables);
   // The forward reads [d_out][d_in] when it has it: the second half of a
   // two-layout base.
   const bool nk = P.opts.w0_layout != MLORA_W0_KN;
@@ -488,20 +508,18 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     });
   }
 
-  // A microscaled base is decoded into the workspace first; the GEMMs read that.
+  // A microscaled base is decoded first; the GEMMs read that.
   const uint16_t* W0b = static_cast<const uint16_t*>(W0);
   if (P.opts.w0_format != MLORA_W0_BF16) {
-    st = decode_base(p, W0, wsb, nk, cs);
+    st = decode_base(p, W0, fb.w0deq, nk, cs);
     if (st != MLORA_OK) return st;
-    W0b = reinterpret_cast<const uint16_t*>(wsb + L.w0deq);
+    W0b = fb.w0deq;
   }
   // A_cat^T feeds the shrink; with W0 as [d_out][d_in] the expand steps read
   // B in k-contiguous form, B_cat^T.
-  uint16_t* acat_t = reinterpret_cast<uint16_t*>(wsb + L.acat_t);
-  uint16_t* bcat_t = reinterpret_cast<uint16_t*>(wsb + L.bcat_t);
   st = timed(p, MLORA_K_PREP, cs, [&] {
-    mlora::launch_prep(t, P.nv(), P.d_in, P.d_out, P.rpad_total, A, acat_t, nullptr, B,
-                       nk ? bcat_t : nullptr, cs);
+    mlora::launch_prep(t, P.nv(), P.d_in, P.d_out, P.rpad_total, A, fb.acat_t, nullptr, B,
+                       nk ? fb.bcat_t : nullptr, cs);
   });
   if (st != MLORA_OK) return st;
   st = fork_groups(p, cs);
@@ -510,7 +528,7 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     hipStream_t s = P.n_groups > 1 ? p->streams[g] : cs;
     st = timed(p, MLORA_K_SHRINK, s, [&] {
       mlora::launch_skinny(0, t, P.nano_start[g], P.nano_start[g + 1] - P.nano_start[g],
-                           (const uint16_t*)X, P.d_in, acat_t, nullptr, scales, (uint16_t*)Z, s);
+                           (const uint16_t*)X, P.d_in, fb.acat_t, nullptr, scales, (uint16_t*)Z, s);
     });
     if (st != MLORA_OK) return st;
     mlora::GemmArgs ga;
@@ -528,16 +546,94 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
     ga.ebuf = (const uint16_t*)Z;
     ga.eb = B;
     ga.ext_n = nullptr;
-    ga.ext_k = bcat_t;
+    ga.ext_k = fb.bcat_t;
     ga.rtot = P.rpad_total;
     ga.ksplit = P.ksplit[2 * g];
     ga.kper = (int32_t)((P.d_in / 32 + ga.ksplit - 1) / ga.ksplit);
-    ga.part = reinterpret_cast<float*>(wsb + L.kpart) + P.kpart_off[g];
+    ga.part = fb.kpart + P.kpart_off[g];
     ga.t = t;
     st = timed(p, MLORA_K_GEMM_FWD, s, [&] { mlora::launch_gemm(true, nk, ga, s); });
     if (st != MLORA_OK) return st;
   }
   return join_groups(p, cs);
+}
+
+mlora_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = mlora::noalloc_scratch(out, &dev);
+  if (e == hipErrorInvalidDevice && dev >= 0)
+    return fail(MLORA_ERR_UNSUPPORTED, "device " + std::to_string(dev) + " is beyond the static scratch table");
+  if (e != hipSuccess) return hip_fail(e, "static scratch address (hipGetDevice / hipGetSymbolAddress)");
+  return MLORA_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// The forward's buffers packed after the tables: A_cat^T, B_cat^T (a
+// [d_out][d_in] base only), split-K partial tiles, the decoded base (a
+// microscaled base only).  Sizes as in the workspace layout.
+size_t noalloc_layout(const mlora_plan_s* p, size_t off[4]) {
+  const auto& P = p->P;
+  size_t at = p->L.table_bytes;
+  const bool bf16 = P.dtype == MLORA_BF16;
+  const bool nk = P.opts.w0_layout != MLORA_W0_KN;
+  const size_t sz[4] = {bf16 ? (size_t)P.rpad_total * (size_t)P.d_in * 2 : 0,
+                        bf16 && nk ? (size_t)P.rpad_total * (size_t)P.d_out * 2 : 0,
+                        bf16 ? (size_t)P.kpart_off.back() * 4 : 0,
+                        bf16 && P.opts.w0_format != MLORA_W0_BF16 ? (size_t)P.d_in * (size_t)P.d_out * 2 : 0};
+  for (int k = 0; k < 4; ++k) {
+    off[k] = at;
+    at += align256(sz[k]);
+  }
+  return at;
+}
+
+}  // namespace
+
+extern "C" {
+
+mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const void* const* A,
+                           const void* const* B, const float* scales, void* Y, void* Z, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
+  mlora_status st;
+  if (!forward_args_ok(p, X, W0, A, B, scales, Y, Z, &st)) return st;
+  st = check_ws(p, ws, ws_bytes);
+  if (st != MLORA_OK) return st;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const auto& L = p->L;
+  const FwdBufs fb{wsb, reinterpret_cast<uint16_t*>(wsb + L.acat_t), reinterpret_cast<uint16_t*>(wsb + L.bcat_t),
+                   reinterpret_cast<float*>(wsb + L.kpart), reinterpret_cast<uint16_t*>(wsb + L.w0deq)};
+  return forward_impl(p, X, W0, A, B, scales, Y, Z, fb, static_cast<hipStream_t>(stream));
+}
+
+mlora_status mlora_forward_noalloc(mlora_plan_t p, const void* X, const void* W0, const void* const* A,
+                                   const void* const* B, const float* scales, void* Y, void* Z,
+                                   void* stream) {
+  if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
+  mlora_status st;
+  if (!forward_args_ok(p, X, W0, A, B, scales, Y, Z, &st)) return st;
+  size_t off[4];
+  const size_t need = noalloc_layout(p, off);
+  if (need > mlora::kNoallocScratchBytes)
+    return fail(MLORA_ERR_UNSUPPORTED, "forward_noalloc: the layer needs " + std::to_string(need) +
+                                           " bytes of scratch; the static scratch holds " +
+                                           std::to_string(mlora::kNoallocScratchBytes) + " (use mlora_forward)");
+  hipStream_t cs = static_cast<hipStream_t>(stream);
+  st = check_capture(p, cs);
+  if (st != MLORA_OK) return st;
+  void* sp = nullptr;
+  st = scratch_for_current_device(&sp);
+  if (st != MLORA_OK) return st;
+  uint8_t* b = static_cast<uint8_t*>(sp);
+  // The scratch keeps whatever the last call on this device left: the plan
+  // tables (the zero page among them) go in first, and every other byte the
+  // kernels read is written earlier in this call.
+  hipError_t e = hipMemcpyAsync(b, p->blob.data(), p->blob.size(), hipMemcpyHostToDevice, cs);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan tables into the static scratch)");
+  const FwdBufs fb{b, reinterpret_cast<uint16_t*>(b + off[0]), reinterpret_cast<uint16_t*>(b + off[1]),
+                   reinterpret_cast<float*>(b + off[2]), reinterpret_cast<uint16_t*>(b + off[3])};
+  return forward_impl(p, X, W0, A, B, scales, Y, Z, fb, cs);
 }
 
 mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const void* W0,
@@ -606,7 +702,7 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
   // dX reads the base weight; a microscaled base is decoded into the workspace.
   const uint16_t* W0b = static_cast<const uint16_t*>(W0);
   if (dX && P.opts.w0_format != MLORA_W0_BF16) {
-    st = decode_base(p, W0, wsb, nk, cs);
+    st = decode_base(p, W0, reinterpret_cast<uint16_t*>(wsb + L.w0deq), nk, cs);
     if (st != MLORA_OK) return st;
     W0b = reinterpret_cast<const uint16_t*>(wsb + L.w0deq);
   }

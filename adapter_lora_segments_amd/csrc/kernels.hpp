@@ -168,6 +168,15 @@ struct AdamwArgs {
 };
 // The update; with a.coef set, each pair's gradients are scaled by its clip
 // factor first.
+// ---------------- static scratch of the allocation-free forward ----------------
+// A file-scope device array (scratch.hip) of this many bytes per GPU, held
+// until the process ends.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+// Device address of the current device's copy (looked up with
+// hipGetSymbolAddress once per device, then cached); *dev receives the
+// device index.  hipErrorInvalidDevice for an index beyond the cache.
+hipError_t noalloc_scratch(void** out, int* dev);
+
 void launch_adamw(const AdamwArgs& a, int64_t n_blocks, hipStream_t s);
 // Clip factors into a.coef: per work item the gradients' square sum (into
 // a.gsq), then per pair the sum of its items in order (two launches).

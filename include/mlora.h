@@ -320,6 +320,28 @@ mlora_status mlora_forward(mlora_plan_t plan, const void *X, const void *W0, con
                            void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * mlora_forward_noalloc -- mlora_forward without a workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The same kernels in the
+ * same order, so Y and Z are bit-identical to mlora_forward's.  The work
+ * buffers (the plan tables, the rank-padded concatenations of A_i and B_i,
+ * split-K partial tiles, a microscaled base's bf16 decoding) live in a
+ * static device array of 64 MiB per GPU, held until the process ends; no
+ * call allocates or frees anything.  Every call copies the plan tables in
+ * first (an asynchronous host-to-device copy on `stream`), and writes every
+ * other scratch byte it reads earlier in the same call, so nothing carries
+ * over from the previous call.  All calls on one GPU share that array:
+ * calls that overlap on one GPU (several streams, several threads) race and
+ * must be ordered by the caller.  A layer whose buffers exceed the scratch
+ * returns MLORA_ERR_UNSUPPORTED with nothing launched (mlora_forward has no
+ * such limit).  Arguments and errors otherwise as mlora_forward; no
+ * mlora_plan_upload is needed.
+ */
+mlora_status mlora_forward_noalloc(mlora_plan_t plan, const void *X, const void *W0, const void *const *A,
+                                   const void *const *B, const float *scales, void *Y, void *Z,
+                                   void *stream);
+
+/*
  * mlora_backward -- dX (optional, NULL skips it), dA_i, dB_i (fp32).
  * Inputs as in forward plus dY [T][d_out] and the Z' saved by forward.
  * dA, dB: device arrays of n device pointers to fp32 buffers.  Case 2 (dZ)

@@ -57,6 +57,11 @@ void launch_f32_da(const DevTables&, int32_t, int64_t, const float*, const float
                    hipStream_t) { reached("f32_da"); }
 void launch_adamw(const AdamwArgs&, int64_t, hipStream_t) { reached("adamw"); }
 void launch_grad_norm(const AdamwArgs&, int64_t, int32_t, hipStream_t) { reached("grad_norm"); }
+// the static scratch lives in device code, which this build does not have
+hipError_t noalloc_scratch(void**, int* dev) {
+  *dev = -1;
+  return hipErrorNoDevice;
+}
 }  // namespace mlora
 
 namespace {
@@ -137,6 +142,10 @@ void exercise(mlora_plan_t p) {
   expect_error(mlora_forward(p, fake, fake, pp, pp, sc, fake, fake, nullptr, ws, nullptr), "forward, NULL ws");
   expect_error(mlora_forward(p, fake, fake, pp, pp, sc, fake, fake, fake, ws ? ws - 1 : 0, nullptr),
                "forward, small ws");
+  expect_error(mlora_forward_noalloc(p, fake, nullptr, pp, pp, sc, fake, fake, nullptr), "noalloc, NULL W0");
+  expect_error(mlora_forward_noalloc(p, odd, fake, pp, pp, sc, fake, fake, nullptr), "noalloc, misaligned");
+  // well-formed arguments: refused for size, or at the scratch lookup (no device in this build)
+  expect_error(mlora_forward_noalloc(p, fake, fake, pp, pp, sc, fake, fake, nullptr), "noalloc, no device");
   expect_error(mlora_backward(p, fake, fake, fake, pp, pp, sc, fake, fake, wp, wp, fake, ws, nullptr),
                "backward, not uploaded");
   expect_error(mlora_backward(p, fake, fake, fake, pp, pp, sc, fake, odd, wp, wp, fake, ws, nullptr),
