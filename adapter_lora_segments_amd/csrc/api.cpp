@@ -37,15 +37,15 @@ struct mlora_plan_s {
   std::vector<std::vector<Range>> chunk_b;  // per group: one chunk range per padded rank
   std::vector<int32_t> group_max_rank;
   int32_t max_rank = 1;
-  // internal streams (n_groups > 1) and fork/join events
-  std::vector<hipStream_t> streams;
-  std::vector<hipEvent_t> join_ev;
-  hipEvent_t fork_ev = nullptr;
-  // per group: the stream of the weight-gradient branch of the backward
-  // (token reductions and partial sums, concurrent with the dX GEMM), and the
-  // events that fork it after dZ and join it back
-  std::vector<hipStream_t> wg_streams;
-  std::vector<hipEvent_t> dz_ev, wg_ev;
+  // The side stream: with one stream group, the backward's weight-gradient
+  // branch (beside the dX GEMM); with several, every group's HBM-bound LoRA
+  // work (shrink; dZ and the weight gradients), one group ahead of the base
+  // GEMMs on the caller's stream.  Created on first use.  Events: fork_ev
+  // (caller -> side), group_ev[g] (side -> caller: group g's shrink or dZ is
+  // done), done_ev (side -> caller: the weight gradients are done).
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, done_ev = nullptr;
+  std::vector<hipEvent_t> group_ev;
   // profiling
   uint32_t prof = 0;  // bit k: bracket launches of kernel kind k
   struct Rec {
@@ -138,73 +138,55 @@ mlora_status timed(mlora_plan_s* p, int kind, hipStream_t s, F&& launch) {
 // kernel's completion makes its results visible to the device).
 constexpr unsigned kOrderEvent = hipEventDisableTiming | hipEventDisableSystemFence;
 
-mlora_status ensure_streams(mlora_plan_s* p) {
-  const int S = p->P.n_groups;
-  if (S <= 1 || (int)p->streams.size() == S) return MLORA_OK;
-  for (int g = (int)p->streams.size(); g < S; ++g) {
-    hipStream_t s;
-    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
-    p->streams.push_back(s);
-    hipEvent_t ev;
-    e = hipEventCreateWithFlags(&ev, kOrderEvent);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-    p->join_ev.push_back(ev);
-  }
-  if (!p->fork_ev) {
-    hipError_t e = hipEventCreateWithFlags(&p->fork_ev, kOrderEvent);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-  }
-  return MLORA_OK;
-}
-
-mlora_status ensure_wg_streams(mlora_plan_s* p) {
-  const int S = p->P.n_groups;
-  for (int g = (int)p->wg_streams.size(); g < S; ++g) {
-    hipStream_t s;
-    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
-    p->wg_streams.push_back(s);
-    for (auto* v : {&p->dz_ev, &p->wg_ev}) {
-      hipEvent_t ev;
-      e = hipEventCreateWithFlags(&ev, kOrderEvent);
-      if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-      v->push_back(ev);
+mlora_status ensure_side(mlora_plan_s* p) {
+  if (!p->side) {
+    hipError_t e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      p->side = nullptr;
+      return hip_fail(e, "hipStreamCreateWithFlags");
     }
   }
+  for (hipEvent_t* ev : {&p->fork_ev, &p->done_ev})
+    if (!*ev) {
+      hipError_t e = hipEventCreateWithFlags(ev, kOrderEvent);
+      if (e != hipSuccess) {
+        *ev = nullptr;
+        return hip_fail(e, "hipEventCreateWithFlags");
+      }
+    }
+  while ((int)p->group_ev.size() < p->P.n_groups) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreateWithFlags(&ev, kOrderEvent);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    p->group_ev.push_back(ev);
+  }
   return MLORA_OK;
 }
 
-mlora_status fork_groups(mlora_plan_s* p, hipStream_t cs) {
-  if (p->P.n_groups <= 1) return MLORA_OK;
-  mlora_status st = ensure_streams(p);
+// The side stream starts after everything enqueued on the caller's stream so far.
+mlora_status fork_side(mlora_plan_s* p, hipStream_t cs) {
+  mlora_status st = ensure_side(p);
   if (st != MLORA_OK) return st;
   hipError_t e = hipEventRecord(p->fork_ev, cs);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  for (hipStream_t s : p->streams) {
-    e = hipStreamWaitEvent(s, p->fork_ev, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-  }
-  return MLORA_OK;
+  if (e == hipSuccess) e = hipStreamWaitEvent(p->side, p->fork_ev, 0);
+  return e == hipSuccess ? MLORA_OK : hip_fail(e, "fork of the side stream");
 }
 
-mlora_status join_groups(mlora_plan_s* p, hipStream_t cs) {
-  if (p->P.n_groups <= 1) return MLORA_OK;
-  for (size_t g = 0; g < p->streams.size(); ++g) {
-    hipError_t e = hipEventRecord(p->join_ev[g], p->streams[g]);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    e = hipStreamWaitEvent(cs, p->join_ev[g], 0);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-  }
-  return MLORA_OK;
+// The caller's stream waits for what the side stream has done so far; ev is
+// recorded on the side stream.
+mlora_status wait_side(mlora_plan_s* p, hipEvent_t ev, hipStream_t cs) {
+  hipError_t e = hipEventRecord(ev, p->side);
+  if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev, 0);
+  return e == hipSuccess ? MLORA_OK : hip_fail(e, "join of the side stream");
 }
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-// A graph capture ended in a fault of the runtime when a plan with several
-// stream groups (forks and joins of internal streams, each event recorded in
-// both the forward and the backward) had been captured; such plans are
-// refused on a capturing stream.  One group captures and replays exactly.
+// A graph capture of a plan with several stream groups once ended in a fault
+// of the runtime, under an earlier arrangement of the internal streams (one
+// stream per group, forked twice per step, each forking a weight-gradient
+// stream of its own).  Its cause was not shown, so such plans stay refused
+// on a capturing stream; one group captures and replays exactly.
 mlora_status check_capture(const mlora_plan_s* p, hipStream_t cs) {
   if (p->P.n_groups <= 1) return MLORA_OK;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -348,12 +330,10 @@ mlora_status mlora_plan_multi_from_ids(int32_t n, int64_t T, const int32_t* toke
 void mlora_plan_destroy(mlora_plan_t p) {
   if (!p) return;
   // Teardown is best effort: errors here have no caller to report to.
-  for (hipStream_t s : p->streams) (void)hipStreamDestroy(s);
-  for (hipEvent_t e : p->join_ev) (void)hipEventDestroy(e);
-  if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
-  for (hipStream_t s : p->wg_streams) (void)hipStreamDestroy(s);
-  for (hipEvent_t e : p->dz_ev) (void)hipEventDestroy(e);
-  for (hipEvent_t e : p->wg_ev) (void)hipEventDestroy(e);
+  if (p->side) (void)hipStreamDestroy(p->side);
+  for (hipEvent_t e : {p->fork_ev, p->done_ev})
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->group_ev) (void)hipEventDestroy(e);
   for (auto& r : p->recs) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
@@ -522,15 +502,33 @@ mlora_status forward_impl(mlora_plan_s* p, const void* X, const void* W0, const 
                        nk ? fb.bcat_t : nullptr, cs);
   });
   if (st != MLORA_OK) return st;
-  st = fork_groups(p, cs);
-  if (st != MLORA_OK) return st;
+  // Several groups: the shrinks run on the side stream, group by group, and
+  // each group's base GEMM on the caller's stream waits only for its own
+  // group's shrink, so the shrink of group g+1 overlaps the GEMM of group g
+  // while the GEMMs themselves run one at a time.  One group: all in order
+  // on the caller's stream.
+  const bool pipe = P.n_groups > 1;
+  if (pipe) {
+    st = fork_side(p, cs);
+    if (st != MLORA_OK) return st;
+  }
+  hipStream_t ss = pipe ? p->side : cs;
   for (int g = 0; g < P.n_groups; ++g) {
-    hipStream_t s = P.n_groups > 1 ? p->streams[g] : cs;
-    st = timed(p, MLORA_K_SHRINK, s, [&] {
+    st = timed(p, MLORA_K_SHRINK, ss, [&] {
       mlora::launch_skinny(0, t, P.nano_start[g], P.nano_start[g + 1] - P.nano_start[g],
-                           (const uint16_t*)X, P.d_in, fb.acat_t, nullptr, scales, (uint16_t*)Z, s);
+                           (const uint16_t*)X, P.d_in, fb.acat_t, nullptr, scales, (uint16_t*)Z, ss);
     });
     if (st != MLORA_OK) return st;
+    if (pipe) {
+      hipError_t e = hipEventRecord(p->group_ev[g], ss);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+  }
+  for (int g = 0; g < P.n_groups; ++g) {
+    if (pipe) {
+      hipError_t e = hipStreamWaitEvent(cs, p->group_ev[g], 0);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    }
     mlora::GemmArgs ga;
     ga.A = (const uint16_t*)X;
     ga.lda = P.d_in;
@@ -552,10 +550,11 @@ mlora_status forward_impl(mlora_plan_s* p, const void* X, const void* W0, const 
     ga.kper = (int32_t)((P.d_in / 32 + ga.ksplit - 1) / ga.ksplit);
     ga.part = fb.kpart + P.kpart_off[g];
     ga.t = t;
-    st = timed(p, MLORA_K_GEMM_FWD, s, [&] { mlora::launch_gemm(true, nk, ga, s); });
+    st = timed(p, MLORA_K_GEMM_FWD, cs, [&] { mlora::launch_gemm(true, nk, ga, cs); });
     if (st != MLORA_OK) return st;
   }
-  return join_groups(p, cs);
+  // the last GEMM waited for the side stream's last event: it is joined
+  return MLORA_OK;
 }
 
 mlora_status scratch_for_current_device(void** out) {
@@ -706,47 +705,29 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     if (st != MLORA_OK) return st;
     W0b = reinterpret_cast<const uint16_t*>(wsb + L.w0deq);
   }
-  if (dX) {
-    st = ensure_wg_streams(p);
-    if (st != MLORA_OK) return st;
-  }
-  st = fork_groups(p, cs);
-  if (st != MLORA_OK) return st;
-  for (int g = 0; g < P.n_groups; ++g) {
-    hipStream_t s = P.n_groups > 1 ? p->streams[g] : cs;
-    st = timed(p, MLORA_K_DZ, s, [&] {
+  auto dz = [&](int g, hipStream_t s) -> mlora_status {
+    return timed(p, MLORA_K_DZ, s, [&] {
       mlora::launch_skinny(1, t, P.nano_start[g], P.nano_start[g + 1] - P.nano_start[g],
                            (const uint16_t*)dY, P.d_out, nullptr, B, scales, dZ, s);
     });
-    if (st != MLORA_OK) return st;
-    // Weight gradients: token reductions, then the fixed-order partial sums.
-    auto weight_grads = [&](hipStream_t sw) -> mlora_status {
-      for (const Range& r : p->chunk_b[g]) {
-        mlora_status s2 = timed(p, MLORA_K_TOKEN_REDUCE, sw, [&] {
-          const int64_t c0 = P.pcol[r.proj], w = P.pcol[r.proj + 1] - c0;
-          mlora::launch_token_reduce(r.rp, t, r.begin, r.count, (const uint16_t*)dY + c0, P.d_out,
-                                     (const uint16_t*)Z, partB, w, (const uint16_t*)X, dZ, partA,
-                                     P.d_in, sw);
-        });
-        if (s2 != MLORA_OK) return s2;
-      }
-      return timed(p, MLORA_K_REDUCE, sw, [&] {
-        mlora::launch_reduce_partials(t, P.groups[g] * P.nproj, P.groups[g + 1] * P.nproj, P.d_in,
-                                      P.d_out, partA, partB, dA, dB, p->group_max_rank[g], sw);
+  };
+  // Weight gradients of group g: token reductions, then the fixed-order
+  // partial sums.
+  auto weight_grads = [&](int g, hipStream_t sw) -> mlora_status {
+    for (const Range& r : p->chunk_b[g]) {
+      mlora_status s2 = timed(p, MLORA_K_TOKEN_REDUCE, sw, [&] {
+        const int64_t c0 = P.pcol[r.proj], w = P.pcol[r.proj + 1] - c0;
+        mlora::launch_token_reduce(r.rp, t, r.begin, r.count, (const uint16_t*)dY + c0, P.d_out,
+                                   (const uint16_t*)Z, partB, w, (const uint16_t*)X, dZ, partA, P.d_in, sw);
       });
-    };
-    if (!dX) {
-      st = weight_grads(s);
-      if (st != MLORA_OK) return st;
-      continue;
+      if (s2 != MLORA_OK) return s2;
     }
-    // With dX requested, the weight gradients need dZ but not dX: they run on
-    // a second stream, enqueued after the dX GEMM so the GEMM's tiles take
-    // the chip first and the reductions fill the CUs its last round of tiles
-    // leaves idle.
-    hipStream_t sw = p->wg_streams[g];
-    hipError_t e = hipEventRecord(p->dz_ev[g], s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return timed(p, MLORA_K_REDUCE, sw, [&] {
+      mlora::launch_reduce_partials(t, P.groups[g] * P.nproj, P.groups[g + 1] * P.nproj, P.d_in, P.d_out,
+                                    partA, partB, dA, dB, p->group_max_rank[g], sw);
+    });
+  };
+  auto dx_gemm = [&](int g) -> mlora_status {
     mlora::GemmArgs ga;
     ga.A = (const uint16_t*)dY;
     ga.lda = P.d_out;
@@ -768,17 +749,45 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     ga.kper = (int32_t)((P.d_out / 32 + ga.ksplit - 1) / ga.ksplit);
     ga.part = reinterpret_cast<float*>(wsb + L.kpart) + P.kpart_off[g];
     ga.t = t;
-    st = timed(p, MLORA_K_GEMM_DX, s, [&] { mlora::launch_gemm(false, !nk, ga, s); });
-    if (st != MLORA_OK) return st;
-    e = hipStreamWaitEvent(sw, p->dz_ev[g], 0);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-    st = weight_grads(sw);
-    if (st != MLORA_OK) return st;
-    e = hipEventRecord(p->wg_ev[g], sw);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s, p->wg_ev[g], 0);
-    if (e != hipSuccess) return hip_fail(e, "join of the weight-gradient stream");
+    return timed(p, MLORA_K_GEMM_DX, cs, [&] { mlora::launch_gemm(false, !nk, ga, cs); });
+  };
+
+  if (!dX) {
+    for (int g = 0; g < P.n_groups; ++g) {
+      if ((st = dz(g, cs)) != MLORA_OK || (st = weight_grads(g, cs)) != MLORA_OK) return st;
+    }
+    return MLORA_OK;
   }
-  return join_groups(p, cs);
+  if (P.n_groups == 1) {
+    // The weight gradients need dZ but not dX: they run on the side stream,
+    // enqueued after the dX GEMM so the GEMM's tiles take the chip first and
+    // the reductions fill the CUs its last round of tiles leaves idle.
+    if ((st = dz(0, cs)) != MLORA_OK || (st = fork_side(p, cs)) != MLORA_OK || (st = dx_gemm(0)) != MLORA_OK ||
+        (st = weight_grads(0, p->side)) != MLORA_OK)
+      return st;
+    return wait_side(p, p->done_ev, cs);
+  }
+  // Several groups: every group's dZ, then every group's weight gradients,
+  // on the side stream; the dX GEMM of group g, on the caller's stream,
+  // waits only for group g's dZ, so the GEMMs run one at a time while the
+  // side stream's HBM-bound work runs beside them.
+  if ((st = fork_side(p, cs)) != MLORA_OK) return st;
+  for (int g = 0; g < P.n_groups; ++g) {
+    if ((st = dz(g, p->side)) != MLORA_OK) return st;
+    hipError_t e = hipEventRecord(p->group_ev[g], p->side);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  for (int g = 0; g < P.n_groups; ++g)
+    if ((st = weight_grads(g, p->side)) != MLORA_OK) return st;
+  hipError_t e = hipEventRecord(p->done_ev, p->side);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  for (int g = 0; g < P.n_groups; ++g) {
+    e = hipStreamWaitEvent(cs, p->group_ev[g], 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    if ((st = dx_gemm(g)) != MLORA_OK) return st;
+  }
+  e = hipStreamWaitEvent(cs, p->done_ev, 0);
+  return e == hipSuccess ? MLORA_OK : hip_fail(e, "join of the side stream");
 }
 
 mlora_status mlora_adamw_step(mlora_plan_t p, const mlora_adamw_hparams* hparams, void* const* A,

@@ -621,14 +621,14 @@ def main():
             layer.forward(d["X"][k], Ys[k])
             layer.backward(d["dY"][k], d["X"][k], dXs[k])
 
-    def profile(kinds):
-        for plan, *_ in layers:
+    def profile(kinds, lays):
+        for plan, *_ in lays:
             plan.profile_enable(kinds)
             plan.profile_read()  # clear
 
-    def collect():
+    def collect(lays):
         tot = {}
-        for plan, *_ in layers:
+        for plan, *_ in lays:
             for k, (ms, n) in plan.profile_read().items():
                 m0, n0 = tot.get(k, (0.0, 0))
                 tot[k] = (m0 + ms, n0 + n)
@@ -671,34 +671,12 @@ def main():
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     gemm_rec = layers[0][0].profile_read()["gemm_fwd"] if prof else (0.0, 0)
-    # Per-kernel breakdown from a separate pass with every launch bracketed
-    # (the events themselves lengthen that pass's steps; kernels that run
-    # concurrently on two streams include each other's time).
-    kern = {}
-    if prof:
-        nb = max(3, min(a.steps, 10))
-        profile(True)
-        for i in range(nb):
-            step(i)
-        torch.cuda.synchronize()
-        kern = {k: (v[0] / nb * a.steps, v[1]) for k, v in collect().items()}
-        # Isolated pass: a backward without dX runs the weight-gradient
-        # kernels on the group's own stream, alone, for clean times.
-        profile(True)
-        for i in range(nb):
-            k = i % SETS
-            for plan, layer, d, Ys, dXs in layers:
-                layer.forward(d["X"][k], Ys[k])
-                layer.backward(d["dY"][k], d["X"][k], want_dx=False)
-        torch.cuda.synchronize()
-        iso = {k: (v[0] / nb * a.steps, v[1]) for k, v in collect().items()}
-        profile(False)
-
     # The same layers planned as one stream group, timed the same way; with
     # several groups the forward-GEMM launches of different groups overlap on
     # their streams, so the roofline's per-launch time is taken here, where
     # each launch has the chip to itself.
     one_group = None
+    ones = None
     if not a.no_one_group and any(pl.info["n_groups"] > 1 for pl, *_ in layers):
         ones = make_layers(1)
         for i in range(a.warmup):
@@ -717,8 +695,34 @@ def main():
             ones[0][0].profile_enable(False)
         one_group = {"ms_per_step": el1 / a.steps * 1e3, "tokens_per_s": w.T * a.steps / el1,
                      "note": "the same layers, inputs and steps planned as one stream group"}
-        del ones
 
+    # Per-kernel breakdown from a separate pass with every launch bracketed
+    # (the events themselves lengthen that pass's steps; kernels that run
+    # concurrently on two streams include each other's time), over the
+    # one-group layers when the timed layers have several groups (whose
+    # side-stream kernels overlap the GEMMs by design).
+    kern = {}
+    klayers = ones if ones is not None else layers
+    if prof:
+        nb = max(3, min(a.steps, 10))
+        profile(True, klayers)
+        for i in range(nb):
+            step(i, klayers)
+        torch.cuda.synchronize()
+        kern = {k: (v[0] / nb * a.steps, v[1]) for k, v in collect(klayers).items()}
+        # Isolated pass: a backward without dX runs the weight-gradient
+        # kernels on the group's own stream, alone, for clean times.
+        profile(True, klayers)
+        for i in range(nb):
+            k = i % SETS
+            for plan, layer, d, Ys, dXs in klayers:
+                layer.forward(d["X"][k], Ys[k])
+                layer.backward(d["dY"][k], d["X"][k], want_dx=False)
+        torch.cuda.synchronize()
+        iso = {k: (v[0] / nb * a.steps, v[1]) for k, v in collect(klayers).items()}
+        profile(False, klayers)
+
+    del ones, klayers
     seq_ms = None
     if not a.no_sequential and not a.shuffled_ids:
         q0 = projs[0]

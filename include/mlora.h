@@ -49,13 +49,16 @@
  * and events.
  *
  * Streams.  Work is enqueued on the caller's stream (a hipStream_t passed as
- * void*, NULL = the null stream) and the calls return without waiting.  With
- * n_streams > 1 the plan forks its adapter groups onto internal streams with
- * events; a backward that computes dX also runs each group's weight
- * gradients (dA, dB) on an internal stream of their own, concurrently with
- * that group's dX GEMM.  Every internal stream is joined back onto the
- * caller's stream before the call returns, so the caller sees ordinary
- * single-stream ordering.
+ * void*, NULL = the null stream) and the calls return without waiting.  The
+ * plan's internal side stream, forked from the caller's stream and joined
+ * back to it with events before a call returns (so the caller sees ordinary
+ * single-stream ordering), runs the HBM-bound LoRA work beside the base
+ * GEMMs: with one stream group, the backward's weight gradients (dA, dB)
+ * beside the dX GEMM; with n_streams > 1 adapter groups, every group's
+ * shrink, dZ and weight gradients, group by group, while each group's base
+ * GEMM runs on the caller's stream once its own group's shrink or dZ is
+ * done.  The GEMMs of different groups never run at the same time, so each
+ * has the chip and its caches to itself.
  *
  * Graph capture.  forward, backward and mlora_adamw_step enqueue only
  * kernels and stream-ordering events (no allocation, no memset), so a plan
