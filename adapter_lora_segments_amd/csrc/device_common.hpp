@@ -74,4 +74,43 @@ __device__ __forceinline__ T ldc(const T* p) {
   return *(const __attribute__((address_space(4))) T*)p;
 }
 
+#define MLORA_LDS __attribute__((address_space(3)))
+
+// 16 bytes per lane from global memory straight into LDS: the wave's 64 lanes
+// fill the 1 KiB block at LDS byte address `lds` (wave-uniform) in lane order
+// (lane i at byte 16 i), with global_load_lds_dwordx4, whose LDS base is M0.
+// Inline assembly, not the compiler builtin: with the builtin the compiler
+// waits for every copy in flight (vmcnt(0)) before each transposing LDS read
+// (ds_read_b64_tr_b16), which would serialize the copy pipeline; the kernels'
+// own vmcnt waits and barriers order the ring.  M0 is saved to a scratch
+// SGPR and restored inside the statement, so the compiler's use of M0 is
+// untouched (M0 is read when the load issues).  The "memory" clobber keeps
+// LDS reads from being cached or moved across the copy.
+__device__ __forceinline__ void dma16_at(const uint16_t* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(src)
+      : "memory");
+}
+
+// The same copy into the 1 KiB block at `blk`.
+__device__ __forceinline__ void dma16(const uint16_t* src, u32x4* blk) {
+  dma16_at(src, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLORA_LDS void*)blk));
+}
+
+// Wait until at most N direct-to-LDS loads of this wave are in flight, then
+// meet the other waves.  A bare s_barrier (no fence): the loads still in
+// flight target other ring stages and must not be drained here.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N <= 63, "vmcnt takes 0..63");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
 }  // namespace mlora

@@ -47,7 +47,7 @@ def measured_traffic(workload: str, layout: str = "kn"):
     if layout != "kn":
         return None
     path = os.path.join(ROOT, "profiles", f"hbm_bytes_{workload}.txt")
-    src = os.path.join(ROOT, "adapter_lora_segments_amd", "csrc", "kernels_bf16.hip")
+    src = os.path.join(ROOT, "adapter_lora_segments_amd", "csrc", "kernels_gemm.hip")
     if not os.path.exists(path):
         return None
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -56,7 +56,7 @@ def measured_traffic(workload: str, layout: str = "kn"):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernels_bf16_sha256_16") != sha:
+    if vals.get("kernels_gemm_sha256_16") != sha:
         return None
     v = vals.get("traffic_bytes k_gemm_fwd")
     return int(v) if v else None
@@ -456,6 +456,65 @@ def vendor_gemm(w, steps, warmup):
     return {"shape": f"{T}x{p.d_in}x{p.d_out}", "results": out}
 
 
+def _short_kernel_name(name):
+    """A kernel's name without its argument list and return type; torch's
+    elementwise kernels keep the functor that tells them apart."""
+    n = name[5:] if name.startswith("void ") else name
+    if "at::native" in n:
+        for key in ("neg_kernel", "MulFunctor", "FillFunctor", "copy_kernel", "normal_kernel", "bfloat16_copy"):
+            if key in n:
+                return n.split("<")[0] + "<" + key + ">"
+    depth, out = 0, []
+    for ch in n:                    # cut at the first '(' outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            break
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def summarize_rocprof(root):
+    """Per-(kernel, grid size) summary of the rocprofv3 CSV files under
+    ``root``: dispatch count and average duration from kernel traces, and the
+    average value of each counter from counter collections (FETCH_SIZE and
+    WRITE_SIZE in KiB per dispatch)."""
+    import csv
+    import glob
+    trace, ctr = {}, {}
+    for path in sorted(glob.glob(os.path.join(root, "**", "*.csv"), recursive=True)):
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                name = row.get("Kernel_Name")
+                if not name:
+                    continue
+                grid = row.get("Grid_Size") or row.get("Grid_Size_X") or "?"
+                key = (_short_kernel_name(name), grid)
+                if path.endswith("kernel_trace.csv"):
+                    t = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                    n, tot = trace.get(key, (0, 0.0))
+                    trace[key] = (n + 1, tot + t)
+                elif path.endswith("counter_collection.csv"):
+                    c = row["Counter_Name"]
+                    n, tot = ctr.setdefault(key, {}).get(c, (0, 0.0))
+                    ctr[key][c] = (n + 1, tot + float(row["Counter_Value"]))
+    lines = []
+    if trace:
+        lines.append(f"{'grid':>10s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s}  kernel")
+        for (k, g), (n, tot) in sorted(trace.items(), key=lambda kv: -kv[1][1]):
+            lines.append(f"{g:>10s} {n:6d} {tot / n:10.1f} {tot / 1e3:10.2f}  {k}")
+    if ctr:
+        names = sorted({c for v in ctr.values() for c in v})
+        lines.append(f"{'grid':>10s} {'calls':>6s} " + " ".join(f"{c + '/disp':>18s}" for c in names) + "  kernel")
+        for (k, g), v in sorted(ctr.items()):
+            n = max(v[c][0] for c in v)
+            lines.append(f"{g:>10s} {n:6d} " +
+                         " ".join(f"{v[c][1] / v[c][0]:18.1f}" if c in v else f"{'-':>18s}" for c in names) + f"  {k}")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -469,6 +528,8 @@ def main():
     ap.add_argument("--first-projection", action="store_true",
                     help="time only the workload's first projection (tokens/s per layer is otherwise "
                          "T / the summed forward+backward time of every projection)")
+    ap.add_argument("--summarize-rocprof", default=None, metavar="DIR",
+                    help="only print a per-kernel summary of the rocprofv3 CSV output under DIR (no GPU)")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure this GPU's MFMA and HBM ceilings (libmlora_probes.so); one JSON line")
     ap.add_argument("--no-ceilings", action="store_true",
@@ -516,6 +577,9 @@ def main():
                     help="only run the packed-against-sequential sweep over Table 7's shapes and "
                          "print its results as one JSON line")
     a = ap.parse_args()
+    if a.summarize_rocprof:
+        print(summarize_rocprof(a.summarize_rocprof))
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: the packed layer is measured on one device's "
               f"share (--gpus {a.gpus} requested)", file=sys.stderr)
