@@ -122,161 +122,186 @@ void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
 }
 
 // ---------------------------------------------------------------------------
-// Skinny products over one nano-batch (<= nano_rows rows of one adapter):
+// Skinny products over one nano-batch (rows of one adapter):
 //   out[row][c] = s_j * sum_k P[row][k] * Q_j[c][k],  c < RP = r_pad(j)
 // MODE 0: shrink (P = X, Q = rows of A_cat^T, all RP rows present);
 // MODE 1: dZ (P = dY, Q = B_j, rows >= r_j read as zeros).
 //
-// One workgroup of four waves per nano-batch, 32 rows at a time.  Both
-// operands are k-contiguous rows; a wave-wide load in MFMA fragment order
-// would give every lane a different row (64 separate cache accesses per
-// instruction), so each K-stage of 128 is copied straight into LDS instead,
-// 256 contiguous bytes per row (16 lanes per row), and the fragments are read
-// from LDS.  Stage layout: the 32 P rows then the RP Q rows, 16 chunks of 16
-// bytes per row, chunk c of row r at position c ^ (r & 15), so the 16 rows
-// one fragment read touches per 256-byte phase hit distinct banks.  A ring of
-// NS stages keeps NS-1 stages of copies in flight; each wave takes two of the
-// eight 16-deep k-steps of every stage, and the four partial accumulators are
-// summed through LDS in wave order.  One launch covers every padded-rank
-// bucket of a stream group: each workgroup switches on its adapter's r_pad.
+// One workgroup of four waves per nano-batch, in blocks of up to 128 rows.
+// A block of R row fragments of 32 rows (R = 1, 2 or 4 by the block's
+// rows) gives fragment f to waves f, f + R, ..; those 4/R waves split the
+// 16-deep k-steps of every stage between them and their partial sums are
+// added through LDS in wave order at the end.  Both operands are
+// k-contiguous rows; each 64-deep stage of the block's 32 R P-rows and the RP
+// Q-rows is copied straight into LDS, 128 contiguous bytes per row, chunk c of
+// row r at c ^ ((r >> 1) & 7) (the base GEMM's conflict-free layout), and
+// fragments are read from there.  The Q rows of a stage are read from L2 once
+// per block and shared by all its row fragments, so larger blocks put more of
+// the ring's bytes into the streamed operand P.  A ring of NS stages keeps
+// NS - 1 stages of copies in flight.  One launch covers every padded-rank
+// bucket of a stream group: each workgroup switches on its adapter's r_pad
+// and its block's row count.
 // ---------------------------------------------------------------------------
-constexpr int kSkinnyKB = 128;                  // K per stage
-constexpr int kSkinnyNC = kSkinnyKB / 8;        // 16-byte chunks per row per stage
-constexpr int kSkinnyLdsEntries = 9216;         // 144 KiB of u32x4
+constexpr int kSkinnyRows = 1280;               // 128-byte LDS rows: 160 KiB
 
-template <int RP>
+template <int RP, int R>
 struct SkinnyCfg {
-  static constexpr int ROWS = 32 + RP;                       // rows per stage
-  static constexpr int STAGE = ROWS * kSkinnyNC;             // u32x4 per stage
-  static constexpr int NS = RP == 32 ? 9 : (RP == 64 ? 6 : (RP == 128 ? 3 : 2));
-  static constexpr int LPS = ROWS / 16;                      // copies per wave per stage
-  static_assert(NS * STAGE <= kSkinnyLdsEntries, "ring exceeds LDS");
-  static_assert(4 * 16 * 64 / 4 <= NS * STAGE, "reduction area exceeds ring");
+  static constexpr int ROWS = 32 * R + RP;                  // LDS rows per stage
+  static constexpr int NS0 = kSkinnyRows / ROWS;
+  static constexpr int NS = NS0 > 16 ? 16 : NS0;            // ring stages
+  static constexpr int LPS = ROWS / 32;                     // copies per wave per stage
+  static_assert(NS >= 3, "ring too short");
   static_assert((NS - 2) * LPS <= 63, "vmcnt takes 0..63");
+  static_assert(4 * 16 * 64 * 4 <= NS * ROWS * 128, "reduction area exceeds ring");
 };
 
-template <int RP, int MODE, bool PERM>
-__device__ __forceinline__ void skinny_body(const DevTables& t, int j, int row0, int nrows,
-                                            const uint16_t* P, int64_t K, int64_t ldp,
-                                            const uint16_t* acat_t, const void* const* Bptr, float s,
-                                            uint16_t* out, u32x4* ring) {
-  using C = SkinnyCfg<RP>;
-  constexpr int F = RP / 32, NS = C::NS, LPS = C::LPS;
+__device__ __forceinline__ int skx(int r) { return (r >> 1) & 7; }
+
+template <int RP, int R, int MODE, bool PERM>
+__device__ __forceinline__ void skinny_block(const DevTables& t, int j, int row0, int nrows,
+                                             const uint16_t* P, int64_t K, int64_t ldp,
+                                             const uint16_t* acat_t, const void* const* Bptr, float s,
+                                             uint16_t* out, u32x4* ring) {
+  using C = SkinnyCfg<RP, R>;
+  constexpr int F = RP / 32, NS = C::NS, LPS = C::LPS, SK = 4 / R;
   const int64_t oj = ldc(t.seg0 + j);
   const int64_t zo = ldc(t.zoff + j);
   const int rj = ldc(t.ranks + j);
   const uint16_t* Q = MODE == 0 ? acat_t + (int64_t)ldc(t.roff + j) * K
                                 : static_cast<const uint16_t*>(ldc(Bptr + j));
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: the copies' LDS base
   const int half = lane >> 5, l32 = lane & 31;
-  const int nks = (int)(K >> 4);                    // 16-deep k-steps
-  const int nst = (int)((K + kSkinnyKB - 1) / kSkinnyKB);
-  float* red = reinterpret_cast<float*>(ring);
+  const int rf = w % R, kg = w / R;          // this wave's row fragment and k-step group
+  const int nst = (int)(K >> 6);             // 64-deep stages (K is a multiple of 64)
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLORA_LDS void*)ring);
 
-  for (int rf = 0; rf * 32 < nrows; ++rf) {
-    // vmcnt also counts the previous fragment's output stores: drain them so
-    // the ring waits below count copies only
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const int frag_rows = min(32, nrows - 32 * rf);
-    // Copy q of this wave fills stage entries [64 m, 64 m + 64), m = w + 4 q:
-    // lane i -> row 4 m + i / 16, position i % 16, global chunk
-    // (i % 16) ^ (row & 15).  Rows past the operand read zeros (no advance).
-    const uint16_t* src[LPS];
-    bool adv[LPS];
+  // Copy q of this wave fills stage rows 8 m .. 8 m + 7, m = w + 4 q: lane i
+  // -> row 8 m + i / 8 at position i % 8, holding the row's chunk
+  // (i % 8) ^ skx(row).  P rows past the block read its last row (never
+  // stored); Q rows past the rank read the zero page (no advance).
+  const uint16_t* src[LPS];
+  bool adv[LPS];
 #pragma unroll
-    for (int q = 0; q < LPS; ++q) {
-      const int m = w + 4 * q;
-      const int row = 4 * m + (lane >> 4);
-      const int gc = (lane & 15) ^ (row & 15);
-      if (row < 32) {
-        const int pr = row0 + 32 * rf + min(row, frag_rows - 1);
-        src[q] = P + (int64_t)(PERM ? ldg_i32(t.perm + pr) : pr) * ldp + 8 * gc;
-        adv[q] = true;
-      } else {
-        const int c = row - 32;
-        adv[q] = MODE == 0 || c < rj;
-        src[q] = adv[q] ? Q + (int64_t)c * K + 8 * gc : t.zero + 8 * (lane & 15);
+  for (int q = 0; q < LPS; ++q) {
+    const int row = 8 * (w + 4 * q) + (lane >> 3);
+    const int ch = (lane & 7) ^ skx(row);
+    if (row < 32 * R) {
+      const int pr = row0 + min(row, nrows - 1);
+      src[q] = P + (int64_t)(PERM ? ldg_i32(t.perm + pr) : pr) * ldp + 8 * ch;
+      adv[q] = true;
+    } else {
+      const int c = row - 32 * R;
+      adv[q] = MODE == 0 || c < rj;
+      src[q] = adv[q] ? Q + (int64_t)c * K + 8 * ch : t.zero + 8 * (lane & 7);
+    }
+  }
+  // Stages past the end repeat the last one into slots never read, so every
+  // wave issues the same number of copies per stage.
+  auto issue = [&](int stage) {
+    const int sc = min(stage, nst - 1);
+    const uint32_t slot = ring_lds + 16u * (uint32_t)((stage % NS) * C::ROWS * 8);
+#pragma unroll
+    for (int q = 0; q < LPS; ++q)
+      dma16_at(adv[q] ? src[q] + 64 * (int64_t)sc : src[q], slot + 1024u * (uint32_t)(w + 4 * q));
+  };
+
+  f32x16 acc[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[f][e] = 0.f;
+
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) issue(i);
+  for (int st = 0; st < nst; ++st) {
+    wait_vm_barrier<(NS - 2) * LPS>();
+    issue(st + NS - 1);
+    const u32x4* slot = ring + (st % NS) * C::ROWS * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4 / SK; ++kk) {
+      const int ks = kg + SK * kk;           // 16-deep k-step of the stage
+      const int c = 2 * ks + half;
+      const int prow = 32 * rf + l32;
+      const u32x4 pa = slot[prow * 8 + (c ^ skx(prow))];
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int qrow = 32 * R + 32 * f + l32;
+        const u32x4 qa = slot[qrow * 8 + (c ^ skx(qrow))];
+        acc[f] = mfma32(qa, pa, acc[f]);
       }
     }
-    // Stages past the end repeat the last one (the ring slot is never read),
-    // so every wave issues the same number of copies per step.  A partial
-    // last stage reads its upper chunks from a clamped column, never used.
-    auto issue = [&](int stage) {
-      const int sc = min(stage, nst - 1);
-      u32x4* slot = ring + (stage % NS) * C::STAGE;
-#pragma unroll
-      for (int q = 0; q < LPS; ++q) {
-        const int m = w + 4 * q;
-        int64_t ko = (int64_t)sc * kSkinnyKB;
-        const uint16_t* p = src[q];
-        if (adv[q]) {
-          // clamp so a 64-wide tail stage never reads past column K
-          const int gc = (lane & 15) ^ ((4 * m + (lane >> 4)) & 15);
-          ko = min(ko, K - 8 - 8 * (int64_t)gc);
-          p += ko;
-        }
-        dma16(p, slot + 64 * m);
-      }
-    };
+  }
+  // drain the trailing copies before the ring is reused for the reduction
+  wait_vm_barrier<0>();
 
-    f32x16 acc[F];
+  // acc[f][4g+e] = D[c = 32f + 8g + 4 half + e][row = 32 rf + l32]
+  if constexpr (R == 4) {
 #pragma unroll
-    for (int f = 0; f < F; ++f)
+    for (int f = 0; f < F; ++f) {
+      const int row = 32 * rf + l32;
+      if (row < nrows) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[f][e] = 0.f;
-
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i) issue(i);
-    for (int st = 0; st < nst; ++st) {
-      wait_vm_barrier<(NS - 2) * LPS>();
-      issue(st + NS - 1);
-      const u32x4* slot = ring + (st % NS) * C::STAGE;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ks = 2 * w + kk;
-        if (st * (kSkinnyKB / 16) + ks < nks) {
-          const int c = 2 * ks + half;
-          const int pos = c ^ (l32 & 15);
-          const u32x4 pa = slot[l32 * kSkinnyNC + pos];
-#pragma unroll
-          for (int f = 0; f < F; ++f) {
-            const u32x4 qa = slot[(32 + 32 * f + l32) * kSkinnyNC + pos];
-            acc[f] = mfma32(qa, pa, acc[f]);
-          }
+        for (int g = 0; g < 4; ++g) {
+          const int c = 32 * f + 8 * g + 4 * half;
+          u32x2 pk;
+          pk[0] = pack_bf16x2(s * acc[f][4 * g + 0], s * acc[f][4 * g + 1]);
+          pk[1] = pack_bf16x2(s * acc[f][4 * g + 2], s * acc[f][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(out + zo + (int64_t)(row0 + row - oj) * RP + c) = pk;
         }
       }
     }
-    // drain the trailing copies before the ring is reused for the reduction
-    wait_vm_barrier<0>();
-
-    // acc[f][4g+e] = D[c = 32f + 8g + 4*half + e][row = l32]; thread (l, g)
-    // sums elements 4g..4g+3 of lane l over the four waves.
+  } else {
+    // The 4/R waves of each fragment are added in wave order: thread tid
+    // takes fragment fr = tid / (256 / R), lane l of it, and the R groups
+    // g = gq R .. gq R + R - 1 of four elements each.
+    float* red = reinterpret_cast<float*>(ring);
+    const int fr = tid / (256 / R), l = tid & 63, gq = (tid % (256 / R)) >> 6;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) red[(w * 16 + e) * 64 + lane] = acc[f][e];
       __syncthreads();
-      {
-        const int l = tid & 63, g = tid >> 6;
+      const int row = 32 * fr + (l & 31);
+#pragma unroll
+      for (int gg = 0; gg < R; ++gg) {
+        const int g = gq * R + gg;
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = 4 * g + i;
-          v[i] = red[(0 * 16 + e) * 64 + l] + red[(1 * 16 + e) * 64 + l] +
-                 red[(2 * 16 + e) * 64 + l] + red[(3 * 16 + e) * 64 + l];
+          float sum = 0.f;
+#pragma unroll
+          for (int k2 = 0; k2 < SK; ++k2) sum += red[((fr + R * k2) * 16 + 4 * g + i) * 64 + l];
+          v[i] = sum;
         }
-        const int row = l & 31;
-        if (row < frag_rows) {
+        if (row < nrows) {
           const int c = 32 * f + 8 * g + 4 * (l >> 5);
           u32x2 pk;
           pk[0] = pack_bf16x2(s * v[0], s * v[1]);
           pk[1] = pack_bf16x2(s * v[2], s * v[3]);
-          *reinterpret_cast<u32x2*>(out + zo + (int64_t)(row0 + 32 * rf + row - oj) * RP + c) = pk;
+          *reinterpret_cast<u32x2*>(out + zo + (int64_t)(row0 + row - oj) * RP + c) = pk;
         }
       }
       __syncthreads();
     }
+  }
+}
+
+template <int RP, int MODE, bool PERM>
+__device__ __forceinline__ void skinny_item(const DevTables& t, int j, int row0, int nrows, const uint16_t* P,
+                                            int64_t K, int64_t ldp, const uint16_t* acat_t,
+                                            const void* const* Bptr, float s, uint16_t* out, u32x4* ring) {
+  // blocks of up to 128 rows; each block's copies are drained before the next
+  for (int b0 = 0; b0 < nrows; b0 += 128) {
+    const int nb = min(128, nrows - b0);
+    if (nb <= 32)
+      skinny_block<RP, 1, MODE, PERM>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, s, out, ring);
+    else if (nb <= 64)
+      skinny_block<RP, 2, MODE, PERM>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, s, out, ring);
+    else
+      skinny_block<RP, 4, MODE, PERM>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, s, out, ring);
+    __syncthreads();
   }
 }
 
@@ -285,7 +310,7 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
                                                 int64_t K, const uint16_t* acat_t,
                                                 const void* const* Bptr, const float* scales,
                                                 uint16_t* out) {
-  __shared__ u32x4 ring[kSkinnyLdsEntries];
+  __shared__ u32x4 ring[kSkinnyRows * 8];
   const int nb = nano_begin + blockIdx.x;
   const int j = ldc(t.nano + 3 * nb), row0 = ldc(t.nano + 3 * nb + 1), nrows = ldc(t.nano + 3 * nb + 2);
   const float s = ldc(scales + j);
@@ -300,10 +325,10 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
     Pj = P + c0;
   }
   switch (ldc(t.rpad + j)) {
-    case 32: skinny_body<32, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
-    case 64: skinny_body<64, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
-    case 128: skinny_body<128, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
-    default: skinny_body<256, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
+    case 32: skinny_item<32, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
+    case 64: skinny_item<64, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
+    case 128: skinny_item<128, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
+    default: skinny_item<256, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
   }
 }
 

@@ -27,6 +27,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // it would fill under half the chip: S x tiles stays within one round of 256
 // CUs, each part keeps at least 8 units, S <= 16, and the parts are
 // ceil(nk / S) units each (S recomputed so none is empty).
+int32_t auto_nano_rows(int64_t T, int32_t nproj) {
+  const int64_t rows = T * nproj;
+  return rows >= 65536 ? 128 : (rows >= 32768 ? 64 : 32);
+}
+
 int32_t split_k(int64_t tiles, int64_t nk) {
   if (tiles <= 0 || tiles >= 128 || nk < 16) return 1;
   int64_t sp = std::min<int64_t>({256 / tiles, nk / 8, 16});
@@ -128,7 +133,7 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
     o.w0_layout = opts->w0_layout;
     o.w0_format = opts->w0_format;
   }
-  if (o.nano_rows < 16 || o.nano_rows > 256 || o.nano_rows % 16 != 0) {
+  if (o.nano_rows != 0 && (o.nano_rows < 16 || o.nano_rows > 256 || o.nano_rows % 16 != 0)) {
     err = "nano_rows must be a multiple of 16 in [16, 256]";
     return MLORA_ERR_INVALID_ARG;
   }
@@ -144,6 +149,8 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
     err = "bf16 plans need nano_rows to be a multiple of 32";
     return MLORA_ERR_UNSUPPORTED;
   }
+  if (o.nano_rows == 0) o.nano_rows = auto_nano_rows(T, P);
+
   if (o.n_streams < 1 || o.n_streams > MLORA_MAX_STREAMS) {
     err = "n_streams must be in [1, " + std::to_string(MLORA_MAX_STREAMS) + "]";
     return MLORA_ERR_INVALID_ARG;

@@ -17,7 +17,7 @@ constexpr int kOptBlock = 2048;  // elements per work item of the optimizer step
 constexpr int64_t kMaxOptBlocks = int64_t(1) << 27;  // larger layers get no optimizer table
 
 struct Opts {
-  int32_t nano_rows = 32;
+  int32_t nano_rows = 0;   // 0: chosen from the rows a launch covers (auto_nano_rows)
   int32_t gemm_rows = 256;
   int32_t n_streams = 1;
   int32_t chunk_min = 256;
@@ -100,6 +100,10 @@ struct DeviceLayout {
 };
 
 DeviceLayout device_layout(const PlanTables& p);
+
+// Default rows per nano-batch (rule 5 of the plan): 128 when T * n_proj >=
+// 65536, 64 when >= 32768, else 32.
+int32_t auto_nano_rows(int64_t T, int32_t nproj);
 
 // K-split factor of a bf16 GEMM launch (rule 9 of the plan).
 int32_t split_k(int64_t tiles, int64_t nk);

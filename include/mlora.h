@@ -101,7 +101,8 @@ typedef enum { MLORA_W0_BF16 = 0, MLORA_W0_MXFP8 = 1, MLORA_W0_MXFP4 = 2 } mlora
 
 /* Plan options.  A zero field takes its default. */
 typedef struct {
-  int32_t nano_rows;      /* NB, rows per nano-batch (16..256, multiple of 16); default 32 */
+  int32_t nano_rows;      /* NB, rows per nano-batch (16..256, multiple of 16; bf16: of 32);
+                             default: 128 when T * n_proj >= 65536, 64 when >= 32768, else 32 */
   int32_t gemm_rows;      /* BM, rows per GEMM tile; default 256 (bf16 requires 256)        */
   int32_t n_streams;      /* adapter groups on separate streams, 1..4; default 1            */
   int32_t chunk_min;      /* reduction chunk rows, KC_i = min(chunk_max,                    */
@@ -128,7 +129,10 @@ typedef struct mlora_plan_s *mlora_plan_t;
  *     g_S' = n, g_s = max(g_{s-1}, first a with o_a >= ceil(s T / S')).
  *  4. Inside a group adapters are visited by r_pad descending, index
  *     ascending.
- *  5. Nano-batches: each adapter's rows cut into pieces of NB rows.
+ *  5. Nano-batches: each adapter's rows cut into pieces of NB rows (NB from
+ *     the options, else 128, 64 or 32 as T * n_proj reaches 65536, 32768
+ *     or neither: larger pieces share the rank operand over more rows while
+ *     a small layer keeps enough pieces to fill the chip).
  *  6. Reduction chunks: pieces of KC_i rows; chunk c's partial sums sit at
  *     rank-row prefix cpref(c) = sum of r_pad over earlier chunks.
  *  7. GEMM row tiles of BM rows per group; each tile lists extension steps

@@ -18,7 +18,9 @@ Rule (all integers; counts and indexes int32, offsets into tensors int64):
     ascending ("bucket order").
  5. Nano-batches: in bucket order, each adapter's rows cut into consecutive
     pieces of NB rows (last one partial; none when n_i = 0).  Entry
-    (adapter, first row, rows).
+    (adapter, first row, rows).  NB given as 0 (the default) is chosen from
+    the rows the nano-batches cover, T P (P projections): 128 when
+    T P >= 65536, 64 when T P >= 32768, else 32.
  6. Reduction chunks: the same walk with KC_i = min(chunk_max, max(chunk_min,
     chunk_per_rank * r_pad(i))) rows per piece.  Entry (adapter, first row,
     rows); cpref(c) = sum of r_pad over earlier chunks.  Each adapter's chunks
@@ -61,7 +63,7 @@ OPT_BLOCK = 2048
 
 @dataclass
 class PlanOpts:
-    nano_rows: int = 32
+    nano_rows: int = 0
     gemm_rows: int = 256
     n_streams: int = 1
     chunk_min: int = 256
@@ -133,6 +135,9 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None, dims=N
         idx = list(range(g[s] * P, g[s + 1] * P))
         return sorted(idx, key=lambda v: (-rpad[v], v % P, v // P))
 
+    NB = opts.nano_rows
+    if NB == 0:
+        NB = 128 if T * P >= 65536 else (64 if T * P >= 32768 else 32)
     nb, nb_start = [], []
     ch, ch_start, cpref, cboff = [], [], [], []
     ch_first = [0] * nv
@@ -145,8 +150,8 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None, dims=N
             lo, hi = o[v // P], o[v // P + 1]
             r0 = lo
             while r0 < hi:
-                nb.append((v, r0, min(opts.nano_rows, hi - r0)))
-                r0 += opts.nano_rows
+                nb.append((v, r0, min(NB, hi - r0)))
+                r0 += NB
             kc = min(opts.chunk_max, max(opts.chunk_min, opts.chunk_per_rank * rpad[v]))
             ch_first[v] = len(ch)
             r0 = lo
@@ -225,6 +230,7 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None, dims=N
         "chunk_boff": np.asarray(cboff, dtype=np.int64),
         "proj_cols": a32(np.concatenate([[0], np.cumsum(wd)]) if widths is not None else [0]),
         "partial_b_elems": cb,
+        "nano_rows": NB,
         "ksplit": a32(ksplit, 2) if dims is not None else None,
     }
 

@@ -54,16 +54,18 @@ def check_invariants(m, offsets, ranks, opts, p, widths=None):
     # order, in pieces of exactly NB rows but the last
     cover = np.zeros((P, T), dtype=np.int64)
     per_pair = {}
+    NB = opts.nano_rows or p["nano_rows"]
+    assert p["nano_rows"] == NB
     for (v, r0, mm) in p["nb"]:
         i = v // P
-        assert 1 <= mm <= opts.nano_rows and o[i] <= r0 and r0 + mm <= o[i + 1]
+        assert 1 <= mm <= NB and o[i] <= r0 and r0 + mm <= o[i + 1]
         cover[v % P, r0:r0 + mm] += 1
         per_pair.setdefault(int(v), []).append((int(r0), int(mm)))
     assert np.all(cover == 1)
     for v, pieces in per_pair.items():
         pos = o[v // P]
         for k, (r0, mm) in enumerate(pieces):
-            assert r0 == pos and (mm == opts.nano_rows or k == len(pieces) - 1)
+            assert r0 == pos and (mm == NB or k == len(pieces) - 1)
             pos += mm
     for s in range(S):
         seen = [int(v) for (v, _, _) in p["nb"][p["nb_start"][s]:p["nb_start"][s + 1]]]
@@ -165,6 +167,24 @@ def pin_ids_definition(m):
             assert np.all(ids[rows] == i) and np.all(np.diff(rows) > 0)
 
 
+def pin_default_nano_rows_by_hand(m):
+    """Rule 5's default nano-batch size, at the thresholds, worked by hand."""
+    for T, want in ((65536, 128), (65535, 64), (32768, 64), (32767, 32), (7680, 32), (0, 32)):
+        p = m.build_plan([0, T // 2, T], [8, 16], m.PlanOpts())
+        assert p["nano_rows"] == want, (T, p["nano_rows"], want)
+    # three projections over 22000 rows cover 66000 rows of pairs: 128; two over 16384 rows: 64 (32768)
+    p = m.build_plan([0, 11000, 22000], [[8, 8, 8], [16, 16, 16]], m.PlanOpts(), widths=[256, 256, 256])
+    assert p["nano_rows"] == 128
+    p = m.build_plan([0, 8192, 16384], [[8, 8], [16, 16]], m.PlanOpts(), widths=[256, 256])
+    assert p["nano_rows"] == 64
+    # the 70B MLP pair's 65536 rows: 128-row pieces, the last of each adapter partial
+    p = m.build_plan([0, 300, 65536], [64, 128], m.PlanOpts())
+    assert [tuple(x) for x in p["nb"][:3]] == [(1, 300, 128), (1, 428, 128), (1, 556, 128)]
+    assert tuple(p["nb"][-1]) == (0, 256, 44)
+    # an explicit size overrides the default
+    assert m.build_plan([0, 300, 65536], [64, 128], m.PlanOpts(nano_rows=32))["nano_rows"] == 32
+
+
 def pin_split_k_by_hand(m):
     """Rule 9 on launches worked by hand."""
     # 16 tiles, 64 K-steps: min(16, 8, 16) = 8, kper 8 -> 8
@@ -190,7 +210,7 @@ def pin_invariants_random(m):
         P = int(rng.integers(1, 5)) if case % 2 else 1
         toks = rng.integers(0, 600, size=n) * (rng.random(n) > 0.15)
         off = np.concatenate([[0], np.cumsum(toks)]).tolist()
-        opts = m.PlanOpts(nano_rows=int(rng.choice([16, 32, 64])), gemm_rows=int(rng.choice([128, 256])),
+        opts = m.PlanOpts(nano_rows=int(rng.choice([0, 16, 32, 64])), gemm_rows=int(rng.choice([128, 256])),
                           n_streams=int(rng.integers(1, 6)), chunk_min=int(rng.choice([16, 64, 256])),
                           chunk_max=0, chunk_per_rank=int(rng.choice([1, 8])))
         opts.chunk_max = opts.chunk_min * int(rng.choice([1, 4, 8]))
@@ -206,4 +226,4 @@ def pin_invariants_random(m):
 
 
 ALL_PINS = [pin_hand_single, pin_hand_multi, pin_hand_ids, pin_ids_definition, pin_split_k_by_hand,
-            pin_invariants_random]
+            pin_default_nano_rows_by_hand, pin_invariants_random]

@@ -88,11 +88,12 @@ def test_bf16_scales_zero_and_negative():
     assert np.all(out["dB"][0] == 0.0) and np.all(out["dA"][0] == 0.0)
 
 
-@pytest.mark.parametrize("nano_rows", [64, 96])
+@pytest.mark.parametrize("nano_rows", [32, 64, 96, 160, 256])
 def test_bf16_long_nano_batches(nano_rows):
-    # nano-batches of several 32-row fragments, the last one partial; K with a
-    # 64-wide tail stage in both skinny products
-    w = custom_workload("bf16_nano", "bf16", 320, 192, [8, 128, 256, 32], [150, 70, 97, 33], seed=13)
+    # nano-batches of one, two and four 32-row fragments, the last one
+    # partial, and (160, 256) of several 128-row blocks; K = 320 and 192, five
+    # and three 64-deep stages in the two skinny products
+    w = custom_workload("bf16_nano", "bf16", 320, 192, [8, 128, 256, 32], [150, 70, 297, 33], seed=13)
     say(f"case bf16 nano_rows {nano_rows}")
     h, out = run_gpu(w, nano_rows=nano_rows)
     compare(w, h, out, what=f"bf16_nano{nano_rows}")

@@ -111,7 +111,7 @@ PLAN_MUTATIONS = {
     "bucket_ascending": ("key=lambda v: (-rpad[v], v % P, v // P)", "key=lambda v: (rpad[v], v % P, v // P)"),
     "bucket_adapter_before_projection": ("key=lambda v: (-rpad[v], v % P, v // P)",
                                          "key=lambda v: (-rpad[v], v // P, v % P)"),
-    "nano_tail_dropped": ("nb.append((v, r0, min(opts.nano_rows, hi - r0)))", "nb.append((v, r0, opts.nano_rows)) if r0 + opts.nano_rows <= hi else None"),
+    "nano_tail_dropped": ("nb.append((v, r0, min(NB, hi - r0)))", "nb.append((v, r0, NB)) if r0 + NB <= hi else None"),
     "chunk_by_rank_not_rpad": ("opts.chunk_per_rank * rpad[v])", "opts.chunk_per_rank * rk[v])"),
     "chunk_max_ignored": ("kc = min(opts.chunk_max, max(", "kc = (max("),
     "cpref_after": ("cpref.append(cp)\n                cboff.append(cb)\n                cp += rpad[v]",
@@ -120,6 +120,8 @@ PLAN_MUTATIONS = {
     "ext_wrong_projection": ("v = j * P + q", "v = j * P"),
     "ext_k_step_64": ("for k0 in range(0, rpad[v], KSTEP):", "for k0 in range(0, rpad[v], 2 * KSTEP):"),
     "tiles_across_groups": ("R0, R1 = o[g[s]], o[g[s + 1]]", "R0, R1 = o[g[s]], o[g[s + 1]] + (BM if s + 1 < S else 0)"),
+    "default_nano_rows_threshold": ("NB = 128 if T * P >= 65536 else", "NB = 128 if T * P > 65536 else"),
+    "default_nano_rows_ignores_projections": ("(64 if T * P >= 32768 else 32)", "(64 if T >= 32768 else 32)"),
     "split_k_no_rebalance": ("    return -(-nk // kper)", "    return sp"),
     "split_k_limit_64": ("if tiles <= 0 or tiles >= 128 or nk < 16:", "if tiles <= 0 or tiles >= 64 or nk < 16:"),
     "ids_reverse_within_adapter": ("    for t, a in enumerate(ids):\n        perm[nxt[a]] = t",
