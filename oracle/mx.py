@@ -37,6 +37,21 @@ cores take; QLoRA's own NF4 code book belongs to one library):
   except above its range (2^128 and more, e.g. 2 x 2^127, become infinity)
   and deep in its subnormal range.
 
+Activations for the base product on the scaled matrix cores.  With an MXFP8
+base, the product X W0 can run on gfx950's MXFP8 x MXFP8 matrix
+instructions; X is then quantized to MXFP8 as well, by the OCP
+microscaling conversion, per row in blocks of 32 consecutive inputs (along
+d_in, the reduction axis, as the base's blocks):
+- the block's shared exponent is floor(log2(max |x|)) - 8 (8 being the
+  largest exponent of an E4M3 element), clamped to [-127, 127]; a block of
+  zeros takes -127; the E8M0 scale code is that exponent + 127;
+- each element x / 2^exponent is rounded to the nearest E4M3 value, ties to
+  even, and values from 448 up (the largest finite E4M3) saturate to 448.
+The layer then computes Y = Q(X) W0 + s_i (X A_i) B_i: only the frozen
+base's product uses the quantized activations; the adapters' shrink, the
+saved Z' and the whole backward use X itself (the backward's dX through the
+base is dY W0^T, the straight-through reading of the quantizer).
+
 W0 codes are laid out like a bf16 W0 of the same layout (KN: [d_in][d_out],
 NK: [d_out][d_in]), MXFP4 codes two to a byte along the row; scales are
 [d_out][d_in / 32] in both layouts.
@@ -114,3 +129,66 @@ def dequant_w0(codes, scales, d_in, d_out, layout="kn", fmt="mxfp8"):
     sc = decode_e8m0(scales).reshape(d_out, d_in // 32)       # [n][k block]
     w = q * np.repeat(sc.T, 32, axis=0)                       # [d_in][d_out]
     return round_bf16(w)
+
+
+def encode_e4m3(v) -> np.ndarray:
+    """E4M3 codes (uint8) of float64 values, nearest with ties to even, from
+    448 up saturating to 448 (finite inputs)."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.signbit(v).astype(np.int64) << 7
+    a = np.abs(v)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6                                  # subnormal range: steps of 2^-9
+    code = np.where(sub, np.rint(a * 2.0 ** 9).astype(np.int64), code)   # 8 -> 0x08, the smallest normal
+    _, ex = np.frexp(np.where(sub, 1.0, a))               # a = m 2^ex, m in [0.5, 1): floor(log2 a) = ex - 1
+    e = ex - 1
+    n = np.rint(np.where(sub, 8.0, a) * np.exp2(3.0 - e)).astype(np.int64)   # 8 .. 16: 1.mmm in eighths
+    e = np.where(n == 16, e + 1, e)
+    n = np.where(n == 16, 8, n)
+    norm = ((e + 7) << 3) | (n - 8)
+    code = np.where(sub, code, norm)
+    code = np.where(a >= 448.0, 0x7E, code)
+    return (sign | code).astype(np.uint8)
+
+
+def quantize_act_mxfp8(X):
+    """MXFP8 form of bf16 activations X ([T][K] uint16 bit patterns, K a
+    multiple of 32): E4M3 element codes [T][K] and E8M0 scale codes
+    [T][K / 32], by the conversion stated in this module's header."""
+    from oracle.lora import as_f64
+    x = as_f64(X, "bf16")
+    T, K = x.shape
+    blk = x.reshape(T, K // 32, 32)
+    amax = np.max(np.abs(blk), axis=2)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    shared = np.where(amax > 0, np.clip(ex - 1 - 8, -127, 127), -127)
+    v = blk / np.exp2(shared.astype(np.float64))[:, :, None]
+    codes = encode_e4m3(v).reshape(T, K)
+    return codes, (shared + 127).astype(np.uint8)
+
+
+def dequant_act(codes, scales) -> np.ndarray:
+    """float64 values of MXFP8 activations: element times its block's scale."""
+    q = decode_e4m3(codes)
+    T, K = q.shape
+    return (q.reshape(T, K // 32, 32) * decode_e8m0(scales)[:, :, None]).reshape(T, K)
+
+
+def forward_act_mx(X, W0, A, B, scales, offsets):
+    """Y = Q(X) W0 + s_i (X_i A_i) B_i, float64, and the saved Z_i = X_i A_i:
+    the base product over the MXFP8 form of the activations, the adapters
+    over X itself.  X, W0 (the base as the layer multiplies it, e.g.
+    dequant_w0's result), A_i, B_i are bf16 bit patterns."""
+    from oracle.lora import as_f64
+    Xq = dequant_act(*quantize_act_mxfp8(X))
+    W = as_f64(W0, "bf16")
+    o = [int(v) for v in offsets]
+    Y = np.zeros((o[-1], W.shape[1]))
+    Z = []
+    for i in range(len(o) - 1):
+        lo, hi = o[i], o[i + 1]
+        Xi = as_f64(np.asarray(X)[lo:hi], "bf16")
+        Zi = Xi @ as_f64(A[i], "bf16")
+        Y[lo:hi] = Xq[lo:hi] @ W + float(scales[i]) * (Zi @ as_f64(B[i], "bf16"))
+        Z.append(Zi)
+    return Y, Z

@@ -24,6 +24,17 @@ worked by hand):
   2^128 up overflows), a scale code of 255 is NaN;
 - a small layer decoded with the hand table in torch float64 against the
   oracle's weight fed to the plain layer oracle.
+Activations quantized to MXFP8 for the base product (the OCP conversion):
+- blocks worked by hand: shared exponents from a block's largest magnitude
+  (1.0 -> 2^-8; 2^100 -> 2^92; a bf16 subnormal clamped at 2^-127; zeros),
+  element codes of exact values, both tie directions, a subnormal element,
+  saturation at 448;
+- element rounding against torch.float8_e4m3fn's conversion (nearest, ties
+  to even) on scaled values below 448, and against the format's half-step
+  error bound;
+- the layer: activations already on the MXFP8 grid give exactly the plain
+  oracle's Y; the adapters' term is computed on X itself (the layer minus
+  its B = 0 form equals the plain oracle's LoRA term).
 """
 from __future__ import annotations
 
@@ -168,6 +179,92 @@ def pin_mxfp4_layer_vs_torch(om):
     assert np.allclose(Y, Yt, rtol=0, atol=1e-12 * max(1.0, np.abs(Yt).max())), "decoded layer differs from torch"
 
 
+def _bits(vals):
+    from workloads.tensors import f32_to_bf16_bits
+    return f32_to_bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+def pin_act_quant_hand_blocks(om):
+    # row 0: largest magnitude 1.0 -> shared exponent 0 - 8, scale code 119; elements x 2^8
+    #   1.0 -> 256 = 1.000 x 2^8 -> 0x78; 0.30078125 -> 77 = 1.203 x 2^6 -> 9.625 eighths -> 10 -> 0x6A;
+    #   -0.5 -> -128 -> 0xF0; 2^-16 -> 2^-8, subnormal 2 x 2^-9 -> 0x02; ties: 68 = 8.5 eighths x 2^3
+    #   -> 8 -> 0x68, 76 = 9.5 eighths -> 10 -> 0x6A
+    # row 1: 1.9921875 -> 510 and 1.75 -> 448 saturate to 0x7E; 1.5 -> 384 = 12 eighths x 2^5 -> 0x7C
+    # row 2: zeros -> scale code 0, codes 0
+    # row 3: largest 2^100 -> exponent 92, scale code 219; 2^100 -> 2^8 -> 0x78; 2^97 -> 2^5 -> 0x60
+    # row 4: largest 2^-130 (a bf16 subnormal) -> 2^-138 clamped to 2^-127, code 0; 2^-130 -> 2^-3 -> 0x20
+    x = np.zeros((5, 32), dtype=np.float32)
+    x[0, :6] = [1.0, 0.30078125, -0.5, 2.0 ** -16, 0.265625, 0.296875]
+    x[1, :3] = [1.9921875, 1.75, 1.5]
+    x[3, :2] = [2.0 ** 100, 2.0 ** 97]
+    x[4, 0] = 2.0 ** -130
+    codes, sc = om.quantize_act_mxfp8(_bits(x))
+    assert sc.shape == (5, 1) and sc[:, 0].tolist() == [119, 119, 0, 219, 0], sc[:, 0]
+    assert codes[0, :7].tolist() == [0x78, 0x6A, 0xF0, 0x02, 0x68, 0x6A, 0x00], [hex(c) for c in codes[0, :7]]
+    assert codes[1, :4].tolist() == [0x7E, 0x7E, 0x7C, 0x00]
+    assert not codes[2].any()
+    assert codes[3, :2].tolist() == [0x78, 0x60] and codes[4, 0] == 0x20
+    # blocks are 32 inputs along the row: a second block gets its own scale
+    y = np.zeros((1, 64), dtype=np.float32)
+    y[0, 0], y[0, 32] = 1.0, 4.0
+    codes, sc = om.quantize_act_mxfp8(_bits(y))
+    assert sc[0].tolist() == [119, 121] and codes[0, 0] == 0x78 and codes[0, 32] == 0x78
+
+
+def pin_act_quant_vs_torch_rounding(om):
+    import torch
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((64, 256)) * np.exp2(rng.integers(-20, 20, size=(64, 1)))).astype(np.float32)
+    X = _bits(x)
+    codes, sc = om.quantize_act_mxfp8(X)
+    from oracle.lora import as_f64
+    v = as_f64(X, "bf16").reshape(64, 8, 32) / om.decode_e8m0(sc)[:, :, None]
+    v = v.reshape(64, 256)
+    ok = np.abs(v) < 448
+    t = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(t[ok], codes[ok]), "element rounding differs from torch's E4M3 conversion"
+    assert np.all(codes[~ok] & 0x7F == 0x7E)
+    q = om.decode_e4m3(codes)
+    normal = np.abs(v) >= 2.0 ** -6
+    assert np.all(np.abs(q - v)[normal & ok] <= np.abs(v)[normal & ok] * 2.0 ** -4)
+    assert np.all(np.abs(q - v)[~normal] <= 2.0 ** -10)
+    # every block's largest magnitude lands in [256, 512) before saturation
+    amax = np.abs(v).reshape(64, 8, 32).max(axis=2)
+    assert np.all((amax >= 256) & (amax < 512))
+
+
+def pin_forward_act_mx(om):
+    from oracle import lora as ol
+    rng = np.random.default_rng(8)
+    d_in, d_out, ranks, toks = 64, 96, [3, 5], [7, 6]
+    off = np.concatenate([[0], np.cumsum(toks)])
+    T = int(off[-1])
+    W0 = _bits(rng.standard_normal((d_in, d_out)) * 0.1)
+    A = [_bits(rng.standard_normal((d_in, r)) * 0.2) for r in ranks]
+    B = [_bits(rng.standard_normal((r, d_out)) * 0.2) for r in ranks]
+    sc = np.asarray([0.5, -2.0], dtype=np.float32)
+    # activations already on the MXFP8 grid (+-1, +-2, 0.5, 0 with every block's largest 2):
+    # the quantizer is exact and the layer is the plain one
+    grid = rng.choice([0.0, 1.0, -1.0, 2.0, -2.0, 0.5], size=(T, d_in))
+    grid[:, ::32] = 2.0
+    Xg = _bits(grid)
+    Y, Z = om.forward_act_mx(Xg, W0, A, B, sc, off)
+    Yp, Zp = ol.forward(Xg, W0, A, B, sc, off, "bf16")
+    assert np.array_equal(Y, Yp), "activations on the MXFP8 grid must give the plain layer"
+    # the adapters' term uses X itself: Y minus its B = 0 form is the plain oracle's LoRA term
+    X = _bits(rng.standard_normal((T, d_in)))
+    Y1, _ = om.forward_act_mx(X, W0, A, B, sc, off)
+    Y0, _ = om.forward_act_mx(X, W0, A, [np.zeros_like(b) for b in B], sc, off)
+    L1, _ = ol.forward(X, np.zeros_like(W0), A, B, sc, off, "bf16")
+    assert np.allclose(Y1 - Y0, L1, rtol=1e-12, atol=1e-12)
+    # and the base term uses the quantized X: it differs from X W0 by the quantization only
+    Yb, _ = om.forward_act_mx(X, W0, A, [np.zeros_like(b) for b in B], sc, off)
+    Xq = om.dequant_act(*om.quantize_act_mxfp8(X))
+    assert np.allclose(Yb, Xq @ ol.as_f64(W0, "bf16"), rtol=1e-12, atol=1e-12)
+    assert not np.allclose(Yb, ol.as_f64(X, "bf16") @ ol.as_f64(W0, "bf16"), rtol=1e-6)
+
+
 ALL_PINS = [pin_e4m3_table_vs_torch, pin_e4m3_hand_codes, pin_e8m0, pin_round_bf16,
             pin_dequant_blocks_and_layouts, pin_layer_vs_torch, pin_e2m1_hand_table, pin_e2m1_nibble_order,
-            pin_mxfp4_blocks_and_layouts, pin_mxfp4_overflow_and_nan, pin_mxfp4_layer_vs_torch]
+            pin_mxfp4_blocks_and_layouts, pin_mxfp4_overflow_and_nan, pin_mxfp4_layer_vs_torch,
+            pin_act_quant_hand_blocks, pin_act_quant_vs_torch_rounding, pin_forward_act_mx]

@@ -79,6 +79,15 @@ MULTI_MUTATIONS = {
 
 
 MX_MUTATIONS = {
+    "act_emax_7": ("np.clip(ex - 1 - 8, -127, 127)", "np.clip(ex - 1 - 7, -127, 127)"),
+    "act_exponent_rounded_up": ("np.clip(ex - 1 - 8, -127, 127)", "np.clip(ex - 8, -127, 127)"),
+    "act_no_clamp": ("np.clip(ex - 1 - 8, -127, 127)", "(ex - 1 - 8)"),
+    "act_no_saturation": ("code = np.where(a >= 448.0, 0x7E, code)", "code = code"),
+    "act_truncating": ("n = np.rint(np.where(sub, 8.0, a) * np.exp2(3.0 - e))", "n = np.floor(np.where(sub, 8.0, a) * np.exp2(3.0 - e))"),
+    "act_subnormal_step": ("np.rint(a * 2.0 ** 9)", "np.rint(a * 2.0 ** 8)"),
+    "act_block_along_rows": ("blk = x.reshape(T, K // 32, 32)", "blk = x.T.reshape(K, T // 32, 32).transpose(1, 0, 2).reshape(T, K // 32, 32) if T % 32 == 0 else x.reshape(T, K // 32, 32) * 1.01"),
+    "act_lora_on_quantized": ("Zi = Xi @ as_f64(A[i], \"bf16\")", "Zi = Xq[lo:hi] @ as_f64(A[i], \"bf16\")"),
+    "act_base_unquantized": ("Y[lo:hi] = Xq[lo:hi] @ W +", "Y[lo:hi] = Xi @ W +"),
     "exponent_bias_6": ("norm = (8 + m) * np.exp2(e - 10.0)", "norm = (8 + m) * np.exp2(e - 9.0)"),
     "subnormal_scale": ("sub = m * 2.0 ** -9", "sub = m * 2.0 ** -10"),
     "subnormal_as_normal": ("v = s * np.where(e == 0, sub, norm)", "v = s * norm"),
