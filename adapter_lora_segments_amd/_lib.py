@@ -13,6 +13,7 @@ STATUS = {0: "MLORA_OK", -1: "MLORA_ERR_INVALID_ARG", -2: "MLORA_ERR_UNSUPPORTED
 DTYPES = {"fp32": 0, "bf16": 1}
 W0_LAYOUTS = {"kn": 0, "nk": 1, "both": 2}
 W0_FORMATS = {"bf16": 0, "mxfp8": 1, "mxfp4": 2}
+ACT_FORMATS = {"bf16": 0, "mxfp8": 1}
 
 TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
           "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count", "tiles", "tile_start", "ext",
@@ -22,7 +23,7 @@ TABLE_COLS = {"nb": 3, "chunks": 3, "tiles": 2, "ext": 4, "opt_blocks": 2, "kspl
 TABLE_I64 = {"zoff", "offsets", "seg_start", "chunk_boff"}
 
 KERNELS = ["shrink", "gemm_fwd", "dz", "token_reduce", "reduce", "gemm_dx", "prep", "adamw", "dequant",
-           "grad_norm"]
+           "grad_norm", "quant_act"]
 
 # every symbol include/mlora.h declares
 EXPORTS = ["mlora_plan", "mlora_plan_from_ids", "mlora_plan_multi", "mlora_plan_multi_from_ids", "mlora_plan_destroy", "mlora_plan_get_info", "mlora_plan_export",
@@ -35,7 +36,8 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("nano_rows", ctypes.c_int32), ("gemm_rows", ctypes.c_int32),
                 ("n_streams", ctypes.c_int32), ("chunk_min", ctypes.c_int32),
                 ("chunk_max", ctypes.c_int32), ("chunk_per_rank", ctypes.c_int32),
-                ("w0_layout", ctypes.c_int32), ("w0_format", ctypes.c_int32)]
+                ("w0_layout", ctypes.c_int32), ("w0_format", ctypes.c_int32),
+                ("act_format", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -47,7 +49,7 @@ class PlanInfo(ctypes.Structure):
                 ("n_nano", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
                 ("n_tiles", ctypes.c_int64), ("n_ext", ctypes.c_int64),
                 ("n_opt_blocks", ctypes.c_int64), ("n_proj", ctypes.c_int64),
-                ("dz_offset", ctypes.c_int64)]
+                ("act_offset", ctypes.c_int64), ("dz_offset", ctypes.c_int64)]
 
 
 class AdamwHparams(ctypes.Structure):

@@ -33,10 +33,11 @@ class Plan:
     def __init__(self, seg_offsets, ranks, d_in: int, d_out: int, dtype: str = "bf16",
                  nano_rows: int = 0, n_streams: int = 0, chunk_min: int = 0, chunk_max: int = 0,
                  chunk_per_rank: int = 0, w0_layout: str = "kn", gemm_rows: int = 0, _ids=None,
-                 _widths=None, w0_format: str = "bf16"):
+                 _widths=None, w0_format: str = "bf16", act_format: str = "bf16"):
         rk = np.ascontiguousarray(np.asarray(ranks, dtype=np.int32))
         opts = _lib.PlanOpts(nano_rows, gemm_rows, n_streams, chunk_min, chunk_max, chunk_per_rank,
-                             _lib.W0_LAYOUTS[w0_layout], _lib.W0_FORMATS[w0_format])
+                             _lib.W0_LAYOUTS[w0_layout], _lib.W0_FORMATS[w0_format],
+                             _lib.ACT_FORMATS[act_format])
         h = ctypes.c_void_p()
         widths = [int(d_out)] if _widths is None else [int(v) for v in _widths]
         if _widths is not None:
@@ -85,6 +86,7 @@ class Plan:
         self.dtype = dtype
         self.w0_layout = w0_layout
         self.w0_format = w0_format
+        self.act_format = act_format
         self.offsets = self.export("offsets") if _ids is not None else np.asarray(seg_offsets, dtype=np.int64)
         self.ranks = rk
         self.widths = widths

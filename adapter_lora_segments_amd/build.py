@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmlora.so")
 PROBES_LIB = os.path.join(PKG, "libmlora_probes.so")
 
-SOURCES = ["plan.cpp", "api.cpp", "kernels_bf16.hip", "kernels_gemm.hip", "kernels_fp32.hip", "kernels_adamw.hip",
+SOURCES = ["plan.cpp", "api.cpp", "kernels_bf16.hip", "kernels_gemm.hip", "kernels_gemm_mx.hip", "kernels_fp32.hip", "kernels_adamw.hip",
            "kernels_mx.hip", "scratch.hip"]
 # measured-ceiling probes (include/mlora_probes.h), a library of their own
 PROBE_SOURCES = ["probes.hip"]

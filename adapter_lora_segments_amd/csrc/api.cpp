@@ -365,6 +365,7 @@ mlora_status mlora_plan_get_info(mlora_plan_t p, mlora_plan_info* info) {
   i.n_opt_blocks = P.n_oblk();
   i.n_proj = P.nproj;
   i.dz_offset = (int64_t)p->L.dz;
+  i.act_offset = P.opts.act_format == MLORA_ACT_MXFP8 ? (int64_t)p->L.xq : -1;
   *info = i;
   return MLORA_OK;
 }
@@ -444,6 +445,7 @@ struct FwdBufs {
   uint16_t* bcat_t;
   float* kpart;
   uint16_t* w0deq;
+  uint8_t* xq;  // MXFP8 activations: codes [T][d_in], then scales [T][d_in / 32]
 };
 
 bool forward_args_ok(const mlora_plan_s* p, const void* X, const void* W0, const void* const* A,
@@ -488,9 +490,20 @@ mlora_status forward_impl(mlora_plan_s* p, const void* X, const void* W0, const 
     });
   }
 
-  // A microscaled base is decoded first; the GEMMs read that.
+  // MXFP8 activations: X quantized first; the base GEMM reads its codes and
+  // the base's own codes, with no decoded copy of W0.
+  const bool mxact = P.opts.act_format == MLORA_ACT_MXFP8;
+  uint8_t* xq_codes = fb.xq;
+  uint8_t* xq_scales = fb.xq + (size_t)P.T * (size_t)P.d_in;
+  if (mxact) {
+    st = timed(p, MLORA_K_QUANT_ACT, cs, [&] {
+      mlora::launch_quant_act_mx8((const uint16_t*)X, P.T, P.d_in, xq_codes, xq_scales, cs);
+    });
+    if (st != MLORA_OK) return st;
+  }
+  // A microscaled base is otherwise decoded first; the GEMMs read that.
   const uint16_t* W0b = static_cast<const uint16_t*>(W0);
-  if (P.opts.w0_format != MLORA_W0_BF16) {
+  if (P.opts.w0_format != MLORA_W0_BF16 && !mxact) {
     st = decode_base(p, W0, fb.w0deq, nk, cs);
     if (st != MLORA_OK) return st;
     W0b = fb.w0deq;
@@ -550,7 +563,18 @@ mlora_status forward_impl(mlora_plan_s* p, const void* X, const void* W0, const 
     ga.kper = (int32_t)((P.d_in / 32 + ga.ksplit - 1) / ga.ksplit);
     ga.part = fb.kpart + P.kpart_off[g];
     ga.t = t;
-    st = timed(p, MLORA_K_GEMM_FWD, cs, [&] { mlora::launch_gemm(true, nk, ga, cs); });
+    if (mxact) {
+      mlora::GemmMxArgs gm;
+      gm.g = ga;
+      gm.g.ksplit = 1;
+      gm.Aq = xq_codes;
+      gm.Asc = xq_scales;
+      gm.Bq = static_cast<const uint8_t*>(W0);
+      gm.Bsc = static_cast<const uint8_t*>(W0) + (size_t)P.d_in * (size_t)P.d_out;
+      st = timed(p, MLORA_K_GEMM_FWD, cs, [&] { mlora::launch_gemm_mx8(gm, cs); });
+    } else {
+      st = timed(p, MLORA_K_GEMM_FWD, cs, [&] { mlora::launch_gemm(true, nk, ga, cs); });
+    }
     if (st != MLORA_OK) return st;
   }
   // the last GEMM waited for the side stream's last event: it is joined
@@ -571,16 +595,18 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // The forward's buffers packed after the tables: A_cat^T, B_cat^T (a
 // [d_out][d_in] base only), split-K partial tiles, the decoded base (a
 // microscaled base only).  Sizes as in the workspace layout.
-size_t noalloc_layout(const mlora_plan_s* p, size_t off[4]) {
+size_t noalloc_layout(const mlora_plan_s* p, size_t off[5]) {
   const auto& P = p->P;
   size_t at = p->L.table_bytes;
   const bool bf16 = P.dtype == MLORA_BF16;
   const bool nk = P.opts.w0_layout != MLORA_W0_KN;
-  const size_t sz[4] = {bf16 ? (size_t)P.rpad_total * (size_t)P.d_in * 2 : 0,
+  const bool mxact = P.opts.act_format == MLORA_ACT_MXFP8;
+  const size_t sz[5] = {bf16 ? (size_t)P.rpad_total * (size_t)P.d_in * 2 : 0,
                         bf16 && nk ? (size_t)P.rpad_total * (size_t)P.d_out * 2 : 0,
                         bf16 ? (size_t)P.kpart_off.back() * 4 : 0,
-                        bf16 && P.opts.w0_format != MLORA_W0_BF16 ? (size_t)P.d_in * (size_t)P.d_out * 2 : 0};
-  for (int k = 0; k < 4; ++k) {
+                        bf16 && P.opts.w0_format != MLORA_W0_BF16 && !mxact ? (size_t)P.d_in * (size_t)P.d_out * 2 : 0,
+                        mxact ? (size_t)P.T * (size_t)P.d_in * 33 / 32 : 0};
+  for (int k = 0; k < 5; ++k) {
     off[k] = at;
     at += align256(sz[k]);
   }
@@ -602,7 +628,7 @@ mlora_status mlora_forward(mlora_plan_t p, const void* X, const void* W0, const 
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   const auto& L = p->L;
   const FwdBufs fb{wsb, reinterpret_cast<uint16_t*>(wsb + L.acat_t), reinterpret_cast<uint16_t*>(wsb + L.bcat_t),
-                   reinterpret_cast<float*>(wsb + L.kpart), reinterpret_cast<uint16_t*>(wsb + L.w0deq)};
+                   reinterpret_cast<float*>(wsb + L.kpart), reinterpret_cast<uint16_t*>(wsb + L.w0deq), wsb + L.xq};
   return forward_impl(p, X, W0, A, B, scales, Y, Z, fb, static_cast<hipStream_t>(stream));
 }
 
@@ -612,7 +638,7 @@ mlora_status mlora_forward_noalloc(mlora_plan_t p, const void* X, const void* W0
   if (!p) return fail(MLORA_ERR_INVALID_ARG, "plan is NULL");
   mlora_status st;
   if (!forward_args_ok(p, X, W0, A, B, scales, Y, Z, &st)) return st;
-  size_t off[4];
+  size_t off[5];
   const size_t need = noalloc_layout(p, off);
   if (need > mlora::kNoallocScratchBytes)
     return fail(MLORA_ERR_UNSUPPORTED, "forward_noalloc: the layer needs " + std::to_string(need) +
@@ -631,7 +657,7 @@ mlora_status mlora_forward_noalloc(mlora_plan_t p, const void* X, const void* W0
   hipError_t e = hipMemcpyAsync(b, p->blob.data(), p->blob.size(), hipMemcpyHostToDevice, cs);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan tables into the static scratch)");
   const FwdBufs fb{b, reinterpret_cast<uint16_t*>(b + off[0]), reinterpret_cast<uint16_t*>(b + off[1]),
-                   reinterpret_cast<float*>(b + off[2]), reinterpret_cast<uint16_t*>(b + off[3])};
+                   reinterpret_cast<float*>(b + off[2]), reinterpret_cast<uint16_t*>(b + off[3]), b + off[4]};
   return forward_impl(p, X, W0, A, B, scales, Y, Z, fb, cs);
 }
 

@@ -86,7 +86,7 @@ __device__ __forceinline__ T ldc(const T* p) {
 // SGPR and restored inside the statement, so the compiler's use of M0 is
 // untouched (M0 is read when the load issues).  The "memory" clobber keeps
 // LDS reads from being cached or moved across the copy.
-__device__ __forceinline__ void dma16_at(const uint16_t* src, uint32_t lds) {
+__device__ __forceinline__ void dma16_at(const void* src, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -99,8 +99,24 @@ __device__ __forceinline__ void dma16_at(const uint16_t* src, uint32_t lds) {
       : "memory");
 }
 
+// 4 bytes per lane straight into LDS (global_load_lds_dword): the wave's 64
+// lanes fill the 256-byte block at LDS byte address `lds` (wave-uniform) in
+// lane order.  Same M0 handling as dma16_at.
+__device__ __forceinline__ void dma4_at(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(src)
+      : "memory");
+}
+
 // The same copy into the 1 KiB block at `blk`.
-__device__ __forceinline__ void dma16(const uint16_t* src, u32x4* blk) {
+__device__ __forceinline__ void dma16(const void* src, u32x4* blk) {
   dma16_at(src, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLORA_LDS void*)blk));
 }
 

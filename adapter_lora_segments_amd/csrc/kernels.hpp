@@ -109,6 +109,22 @@ struct GemmArgs {
   float* part;
   DevTables t;
 };
+// Forward GEMM over MXFP8 operands (kernels_gemm_mx.hip): g as for
+// launch_gemm(true, true, ...) without split-K; the main operands are X's
+// E4M3 codes [rows][K] with scales [rows][K / 32] (rows in the caller's
+// order) and W0's codes [N][K] with scales [N][K / 32]; K a multiple of 128.
+struct GemmMxArgs {
+  GemmArgs g;
+  const uint8_t* Aq;
+  const uint8_t* Asc;
+  const uint8_t* Bq;
+  const uint8_t* Bsc;
+};
+void launch_gemm_mx8(const GemmMxArgs& m, hipStream_t s);
+// Activations [T][K] (bf16, rows dense) to MXFP8 codes [T][K] and scales [T][K / 32].
+void launch_quant_act_mx8(const uint16_t* X, int64_t T, int64_t K, uint8_t* codes, uint8_t* scales,
+                          hipStream_t s);
+
 // main_b_kcontig: Bop element (k, n) at B[n*ldb + k] (else at B[k*ldb + n]).
 void launch_gemm(bool fwd, bool main_b_kcontig, const GemmArgs& g, hipStream_t s);
 

@@ -132,6 +132,7 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
     if (opts->chunk_per_rank) o.chunk_per_rank = opts->chunk_per_rank;
     o.w0_layout = opts->w0_layout;
     o.w0_format = opts->w0_format;
+    o.act_format = opts->act_format;
   }
   if (o.nano_rows != 0 && (o.nano_rows < 16 || o.nano_rows > 256 || o.nano_rows % 16 != 0)) {
     err = "nano_rows must be a multiple of 16 in [16, 256]";
@@ -174,6 +175,15 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
   }
   if (o.w0_format != MLORA_W0_BF16 && dtype != MLORA_BF16) {
     err = "a microscaled (MXFP8/MXFP4) base weight needs a bf16 plan";
+    return MLORA_ERR_UNSUPPORTED;
+  }
+  if (o.act_format != MLORA_ACT_BF16 && o.act_format != MLORA_ACT_MXFP8) {
+    err = "act_format must be MLORA_ACT_BF16 or MLORA_ACT_MXFP8";
+    return MLORA_ERR_INVALID_ARG;
+  }
+  if (o.act_format == MLORA_ACT_MXFP8 &&
+      (o.w0_format != MLORA_W0_MXFP8 || o.w0_layout != MLORA_W0_NK || d_in % 128 != 0)) {
+    err = "MXFP8 activations need an MXFP8 base held as [d_out][d_in] (w0_layout NK) and d_in a multiple of 128";
     return MLORA_ERR_UNSUPPORTED;
   }
 
@@ -438,6 +448,8 @@ DeviceLayout device_layout(const PlanTables& p) {
   L.dz = take((size_t)p.z_elems * esz);
   L.kpart = take((size_t)p.kpart_off.back() * 4);
   L.w0deq = take(p.opts.w0_format != MLORA_W0_BF16 ? (size_t)p.d_in * (size_t)p.d_out * 2 : 0);
+  // MXFP8 activations: E4M3 codes [T][d_in], then E8M0 scales [T][d_in / 32]
+  L.xq = take(p.opts.act_format == MLORA_ACT_MXFP8 ? (size_t)p.T * (size_t)p.d_in * 33 / 32 : 0);
   // gradient clipping: one partial square sum per optimizer work item, then
   // one clip factor per pair
   L.gnorm = take(4 * ((size_t)p.n_oblk() + (size_t)p.nv()));

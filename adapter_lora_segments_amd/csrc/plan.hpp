@@ -25,6 +25,7 @@ struct Opts {
   int32_t chunk_per_rank = 8;
   int32_t w0_layout = MLORA_W0_KN;
   int32_t w0_format = MLORA_W0_BF16;
+  int32_t act_format = MLORA_ACT_BF16;
 };
 
 // Several projections that share one input (nproj > 1) split the output
@@ -95,7 +96,7 @@ struct DeviceLayout {
       ext_start, ext, zero, perm, oblk, oblk_first, seg0, pcol, cboff;
   size_t table_bytes;
   // offsets (bytes) of the work buffers inside the workspace
-  size_t acat_t, acat, bcat_t, dz, kpart, w0deq, gnorm, part_a, part_b;
+  size_t acat_t, acat, bcat_t, dz, kpart, w0deq, xq, gnorm, part_a, part_b;
   size_t workspace_bytes;
 };
 

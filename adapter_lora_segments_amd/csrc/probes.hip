@@ -65,6 +65,37 @@ __global__ __launch_bounds__(256) void k_read(const u32x4* src, int64_t n16, flo
   out[(int64_t)blockIdx.x * 256 + threadIdx.x] = (float)acc;
 }
 
+// The same loop on the MXFP8 instruction of the quantized base's forward
+// (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3, unit scales): 131072
+// flops per instruction.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(256, 1) void k_mfma8_loop(const u32x4* ops, int64_t iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  i32x8 a[4], b[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const u32x4 p0 = ops[f * 64 + lane], p1 = ops[(4 + f) * 64 + lane];
+    a[f] = __builtin_bit_cast(i32x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
+    b[f] = __builtin_bit_cast(i32x8, __builtin_shufflevector(p1, p0, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  f32x16 acc[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[q][e] = 0.f;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[q & 3], a[q >> 2], acc[q], 0, 0, 0, 127, 0, 127);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[q][e];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 constexpr int kStreamBlocks = 2048;
 
 }  // namespace
@@ -76,6 +107,15 @@ int mlora_probe_mfma(int64_t n_wg, int64_t iters, const void* operands, float* o
       (reinterpret_cast<uintptr_t>(operands) & 15u))
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(k_mfma_loop, dim3((unsigned)n_wg), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(operands), iters, out);
+  return (int)hipGetLastError();
+}
+
+int mlora_probe_mfma8(int64_t n_wg, int64_t iters, const void* operands, float* out, void* stream) {
+  if (n_wg < 1 || n_wg > (1 << 20) || iters < 1 || iters > (1 << 24) || !operands || !out ||
+      (reinterpret_cast<uintptr_t>(operands) & 15u))
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mfma8_loop, dim3((unsigned)n_wg), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(operands), iters, out);
   return (int)hipGetLastError();
 }

@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -62,7 +63,7 @@ def measured_traffic(workload: str, layout: str = "kn"):
     return int(v) if v else None
 
 
-def kernel_rooflines(w, units, kern, iso, steps, w0_format="bf16"):
+def kernel_rooflines(w, units, kern, iso, steps, w0_format="bf16", act_format="bf16"):
     """Achieved rate of every step of the path against its roofline, from the
     per-kernel pass (the weight-gradient kernels from the isolated pass,
     where they do not share the chip with the dX GEMM).  Algorithmic bytes
@@ -96,19 +97,29 @@ def kernel_rooflines(w, units, kern, iso, steps, w0_format="bf16"):
                       "frac": ach / PEAK_HBM_GBS, "ms_per_step": ms}
         else:
             ach = work[k] / (ms * 1e-3) / 1e12
-            out[k] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                      "frac": ach / PEAK_BF16_TFLOPS, "ms_per_step": ms}
+            # the forward's base product on MXFP8 operands takes the fp8 peak
+            peak = PEAK_FP8_TFLOPS if (k == "gemm_fwd" and act_format == "mxfp8") else PEAK_BF16_TFLOPS
+            out[k] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                      "frac": ach / peak, "ms_per_step": ms}
     out["gemm_dx"]["note"] = "timed beside the concurrent weight-gradient kernels"
     if kern.get("dequant", (0.0, 0))[1]:
         # microscaled base: codes (1 B for MXFP8, 0.5 B for MXFP4) and scales (1/32 B) read, bf16 (2 B)
-        # written per weight, twice a step
+        # written per weight, once per decode (two a step, one with MXFP8 activations)
         code_b = 0.5 if w0_format == "mxfp4" else 1.0
-        byt = sum(2 * (code_b + 1 / 32 + 2) * w.projections[q[0]].d_in * w.projections[q[0]].d_out
+        per_step = 1 if act_format == "mxfp8" else 2
+        byt = sum(per_step * (code_b + 1 / 32 + 2) * w.projections[q[0]].d_in * w.projections[q[0]].d_out
                   for q in units)
         ms = kern["dequant"][0] / steps
         ach = byt / (ms * 1e-3) / 1e9
         out["dequant"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": ach / PEAK_HBM_GBS, "ms_per_step": ms}
+    if kern.get("quant_act", (0.0, 0))[1]:
+        # activations to MXFP8: 2 B read, 1 + 1/32 B written per input
+        byt = sum((2 + 1 + 1 / 32) * w.T * w.projections[q[0]].d_in for q in units)
+        ms = kern["quant_act"][0] / steps
+        ach = byt / (ms * 1e-3) / 1e9
+        out["quant_act"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": ach / PEAK_HBM_GBS, "ms_per_step": ms}
     for k in ("reduce", "prep"):
         out[k] = {"bound": "overhead", "ms_per_step": iso[k][0] / steps}
     return out
@@ -180,9 +191,10 @@ def ceilings(random_only=False):
     L = ctypes.CDLL(path)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     L.mlora_probe_mfma.argtypes = [i64, i64, vp, vp, vp]
+    L.mlora_probe_mfma8.argtypes = [i64, i64, vp, vp, vp]
     L.mlora_probe_copy.argtypes = [vp, vp, i64, vp]
     L.mlora_probe_read.argtypes = [vp, i64, vp, vp]
-    for f in (L.mlora_probe_mfma, L.mlora_probe_copy, L.mlora_probe_read):
+    for f in (L.mlora_probe_mfma, L.mlora_probe_mfma8, L.mlora_probe_copy, L.mlora_probe_read):
         f.restype = ctypes.c_int
     stream = vp(torch.cuda.current_stream().cuda_stream)
 
@@ -212,6 +224,11 @@ def ceilings(random_only=False):
         ms = best(lambda: L.mlora_probe_mfma(n_wg, iters, vp(op.data_ptr()), vp(res.data_ptr()), stream))
         out[f"mfma_bf16_{name}_operands"] = {"achieved": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
                                             "ms": ms}
+    # MXFP8 instruction: E4M3 codes of random normal values (no NaN codes)
+    op8 = torch.randn(8192, generator=g, device="cuda").to(torch.float8_e4m3fn).view(torch.uint8)
+    ms = best(lambda: L.mlora_probe_mfma8(n_wg, iters // 2, vp(op8.data_ptr()), vp(res.data_ptr()), stream))
+    out["mfma_mxfp8_random_operands"] = {"achieved": n_wg * 4 * (iters // 2) * 16 * 131072 / (ms * 1e-3) / 1e12,
+                                         "unit": "TFLOP/s", "ms": ms}
     nbytes = 2 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -557,6 +574,9 @@ def main():
     ap.add_argument("--w0-format", default="bf16", choices=["bf16", "mxfp8", "mxfp4"],
                     help="store the frozen base in MXFP8 (E4M3 codes) or MXFP4 (E2M1 codes, two per byte), "
                          "with E8M0 scales per 32 inputs, decoded per call; implies --no-sequential")
+    ap.add_argument("--act-format", default="bf16", choices=["bf16", "mxfp8"],
+                    help="mxfp8: quantize the activations of the forward's base product to MXFP8 and run it "
+                         "on the MXFP8 matrix cores (needs --w0-format mxfp8; the base is held as [d_out][d_in])")
     ap.add_argument("--w0-layout", default="kn", choices=["kn", "nk", "both"],
                     help="layout of the frozen base: [d_in][d_out], [d_out][d_in], or both (held once in "
                          "each layout, built before timing; the forward then reads [d_out][d_in])")
@@ -622,6 +642,10 @@ def main():
     if a.fused:
         a.all_projections, a.no_sequential = True, True
     mx = a.w0_format in ("mxfp8", "mxfp4")
+    if a.act_format == "mxfp8" and a.w0_format != "mxfp8":
+        print("--act-format mxfp8 needs --w0-format mxfp8", file=sys.stderr)
+        sys.exit(2)
+    mx_layout = "nk" if a.act_format == "mxfp8" else "kn"
     if mx:
         a.no_sequential = True
         if a.fused or a.shuffled_ids:
@@ -645,7 +669,7 @@ def main():
         p = w.projections[q]
         d = device_tensors(w, q, sets=SETS)
         if mx:
-            d["W0_codes"] = (quantize_mx4_device if a.w0_format == "mxfp4" else quantize_mx_device)(d["W0"], "kn")
+            d["W0_codes"] = (quantize_mx4_device if a.w0_format == "mxfp4" else quantize_mx_device)(d["W0"], mx_layout)
             d["W0_bytes"] = d["W0_codes"].numel()
         datas.append(("single", d, [torch.empty((w.T, p.d_out), dtype=torch.bfloat16, device="cuda")
                                     for _ in range(SETS)],
@@ -666,7 +690,8 @@ def main():
                                          w0_layout=a.w0_layout)
                 else:
                     plan = Plan(d["offsets"], d["ranks"], d["d_in"], d["d_out"], "bf16", n_streams=n_streams,
-                                w0_format=a.w0_format, w0_layout=a.w0_layout if not mx else "kn")
+                                w0_format=a.w0_format, w0_layout=a.w0_layout if not mx else mx_layout,
+                                act_format=a.act_format)
                 if mx:
                     W0 = d["W0_codes"]
                 elif a.w0_layout == "nk":
@@ -871,14 +896,15 @@ def main():
                    "streams": layers[0][0].info["n_groups"],
                    "rows": "shuffled, per-token adapter ids" if a.shuffled_ids else "adapter segments",
                    "fused": [g for g, _ in groups] if groups else None,
-                   "w0_format": a.w0_format, "w0_layout": a.w0_layout},
+                   "w0_format": a.w0_format, "w0_layout": a.w0_layout if not mx else mx_layout,
+                   "act_format": a.act_format},
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
     }
     if kern:
         out["kernels_ms_per_step"] = {k: v[0] / a.steps for k, v in kern.items() if v[1]}
         units = [gp for _, gp in groups] if groups else [[q] for q in projs]
-        out["kernel_rooflines"] = kernel_rooflines(w, units, kern, iso, a.steps, a.w0_format)
+        out["kernel_rooflines"] = kernel_rooflines(w, units, kern, iso, a.steps, a.w0_format, a.act_format)
     if one_group is not None:
         out["one_group"] = one_group
     ceil = None if a.no_ceilings else ceilings()
@@ -892,17 +918,20 @@ def main():
             first = groups[0][1] if groups else [0]
             ach = sum(gemm_fwd_flops(w, q) for q in first) / per_step / (avg * 1e-3) / 1e12
             kname = "+".join(w.projections[q].name for q in first)
-            out["roofline"] = {"kernel": f"k_gemm<fwd> (base GEMM + fused expand) of {kname} "
+            mxk = a.act_format == "mxfp8"
+            peak = PEAK_FP8_TFLOPS if mxk else PEAK_BF16_TFLOPS
+            out["roofline"] = {"kernel": (f"k_gemm_mx8 (MXFP8 base GEMM + fused bf16 expand) of {kname} " if mxk else
+                                          f"k_gemm<fwd> (base GEMM + fused expand) of {kname} ") +
                                          f"{p0.d_in}x{sum(w.projections[q].d_out for q in first)}",
-                               "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                               "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                               "traffic": None if groups else measured_traffic(w.name, a.w0_layout),
+                               "bound": "mfma", "achieved": ach, "peak": peak,
+                               "unit": "TFLOP/s", "frac": ach / peak,
+                               "traffic": None if (groups or mx) else measured_traffic(w.name, a.w0_layout),
                                "avg_launch_ms": avg,
                                "timed_in": "one-group pass" if one_group is not None else "the timed steps"}
             if per_step > 1:
                 out["roofline"]["note"] = "several group launches per step that overlap on their streams"
             if ceil is not None:
-                mp = ceil["mfma_bf16_random_operands"]["achieved"]
+                mp = ceil["mfma_mxfp8_random_operands" if mxk else "mfma_bf16_random_operands"]["achieved"]
                 out["roofline"]["measured_peak"] = mp
                 out["roofline"]["frac_measured"] = ach / mp
     if seq_ms is not None:

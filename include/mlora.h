@@ -93,6 +93,7 @@ typedef enum {
 typedef enum { MLORA_FP32 = 0, MLORA_BF16 = 1 } mlora_dtype;
 typedef enum { MLORA_W0_KN = 0, MLORA_W0_NK = 1, MLORA_W0_BOTH = 2 } mlora_w0_layout;
 typedef enum { MLORA_W0_BF16 = 0, MLORA_W0_MXFP8 = 1, MLORA_W0_MXFP4 = 2 } mlora_w0_format;
+typedef enum { MLORA_ACT_BF16 = 0, MLORA_ACT_MXFP8 = 1 } mlora_act_format;
 
 #define MLORA_MAX_RANK 256
 #define MLORA_MAX_ADAPTERS 65536
@@ -110,6 +111,9 @@ typedef struct {
   int32_t chunk_per_rank; /*   defaults 256, 2048, 8                                        */
   int32_t w0_layout;      /* mlora_w0_layout; default MLORA_W0_KN (BOTH: bf16/fp32 W0 only)  */
   int32_t w0_format;      /* mlora_w0_format; default MLORA_W0_BF16 (MXFP8, MXFP4: bf16 plans only) */
+  int32_t act_format;     /* mlora_act_format of the activations in the forward's base product;
+                             MLORA_ACT_MXFP8 needs w0_format MXFP8, w0_layout NK and d_in a
+                             multiple of 128 (see "Activations on the MXFP8 matrix cores") */
 } mlora_plan_opts;
 
 typedef struct mlora_plan_s *mlora_plan_t;
@@ -221,6 +225,10 @@ typedef struct {
   int64_t n_nano, n_chunks, n_tiles, n_ext;
   int64_t n_opt_blocks;      /* optimizer work items (0: layer too large, see mlora_adamw_step) */
   int64_t n_proj;            /* projections sharing the input (1 unless mlora_plan_multi) */
+  int64_t act_offset;        /* act_format MLORA_ACT_MXFP8: byte offset in the workspace of the
+                                last forward's MXFP8 activations, T * d_in E4M3 codes [T][d_in]
+                                (rows in the caller's order), then T * d_in / 32 E8M0 scale
+                                codes [T][d_in / 32]; -1 otherwise */
   int64_t dz_offset;         /* byte offset in the workspace of dZ = s dY B^T (PLoRA §9.2,
                                 Case 2) as the last backward left it: z_elems elements in
                                 the layout of Z' (plan dtype), padding columns zero */
@@ -311,6 +319,23 @@ mlora_status mlora_plan_upload(mlora_plan_t plan, void *workspace, size_t ws_byt
  * even element in the low four bits: d_in * d_out / 2 code bytes, the scale
  * codes following at that byte offset.  Products from 2^128 up decode to
  * infinity.  The resident base takes 0.5 + 1/32 bytes per weight.
+ *
+ * Activations on the MXFP8 matrix cores (act_format = MLORA_ACT_MXFP8, with
+ * an MXFP8 base held as [d_out][d_in]): the forward's base product runs on
+ * gfx950's MXFP8 x MXFP8 instruction (v_mfma_scale_f32_32x32x64_f8f6f4)
+ * with no bf16 copy of W0.  X is first quantized to MXFP8 by the OCP
+ * microscaling conversion, per row in blocks of 32 inputs along d_in: the
+ * block's shared exponent is floor(log2 max|x|) - 8, clamped to [-127, 127]
+ * (-127 for a block of zeros); elements x 2^-exponent are rounded to the
+ * nearest E4M3 value, ties to even, saturating at 448 (one HBM-bound
+ * kernel, MLORA_K_QUANT_ACT; the result stays in the workspace,
+ * mlora_plan_info.act_offset).  The forward then computes
+ *   Y = Q(X) W0 + Z' B,  Z' = s X A
+ * with the LoRA terms on X itself, as bf16 extension steps of the same
+ * GEMM.  The backward is unchanged (dX = dY W0^T + dZ A^T over the decoded
+ * base: the straight-through reading of the activation quantizer).  The
+ * forward over a large K split into parts (rule 9) is not split on this
+ * path.
  */
 
 /*
@@ -445,6 +470,7 @@ typedef enum {
   MLORA_K_ADAMW,         /* per-adapter AdamW step (mlora_adamw_step)        */
   MLORA_K_DEQUANT,       /* decode of an MXFP8/MXFP4 base weight into bf16   */
   MLORA_K_GRAD_NORM,     /* per-adapter gradient norms and clip factors      */
+  MLORA_K_QUANT_ACT,     /* activations to MXFP8 (act_format MLORA_ACT_MXFP8) */
   MLORA_K_COUNT
 } mlora_kernel_kind;
 

@@ -29,6 +29,12 @@ extern "C" {
  */
 int mlora_probe_mfma(int64_t n_wg, int64_t iters, const void *operands, float *out, void *stream);
 
+/* The same loop on the MXFP8 instruction (v_mfma_scale_f32_32x32x64_f8f6f4,
+ * E4M3 x E4M3, unit scales): work = n_wg * 4 * iters * 16 * 131072 flops;
+ * operands: at least 8192 bytes (E4M3 codes: random bytes draw realistic
+ * power, though some codes are NaN). */
+int mlora_probe_mfma8(int64_t n_wg, int64_t iters, const void *operands, float *out, void *stream);
+
 /* Streaming copy dst[i] = src[i] of `bytes` bytes (a multiple of 16, both
  * 16-byte aligned, not overlapping) with 16-byte loads and stores: HBM
  * traffic = 2 * bytes. */

@@ -56,6 +56,10 @@ void launch_f32_db(const DevTables&, int32_t, int64_t, const float*, const float
 void launch_f32_da(const DevTables&, int32_t, int64_t, const float*, const float*, void* const*, int32_t,
                    hipStream_t) { reached("f32_da"); }
 void launch_adamw(const AdamwArgs&, int64_t, hipStream_t) { reached("adamw"); }
+void launch_gemm_mx8(const GemmMxArgs&, hipStream_t) { reached("gemm_mx8"); }
+void launch_quant_act_mx8(const uint16_t*, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t) {
+  reached("quant_act_mx8");
+}
 void launch_grad_norm(const AdamwArgs&, int64_t, int32_t, hipStream_t) { reached("grad_norm"); }
 // the static scratch lives in device code, which this build does not have
 hipError_t noalloc_scratch(void**, int* dev) {
@@ -105,6 +109,7 @@ mlora_plan_opts opts() {
   o.chunk_per_rank = (int32_t)uni(chance(5) ? -2 : 0, 16);
   o.w0_layout = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 5 : 2);
   o.w0_format = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 5 : 2);
+  o.act_format = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 3 : 1);
   return o;
 }
 

@@ -230,7 +230,7 @@ def test_adamw_rejects_bad_arguments_without_launching():
     assert L.mlora_adamw_step(bf.handle, *ok, d, d, 0, d, 16, None) == -4              # workspace small
     assert L.mlora_adamw_step(bf.handle, *ok, None, None, 0, d, 1 << 30, None) == -4   # not uploaded
     assert L.mlora_adamw_step(bf.handle, *ok, d, d, 2, d, 1 << 30, None) == -1      # clip_grads not 0/1
-    assert _lib.KERNELS[7:] == ["adamw", "dequant", "grad_norm"] and len(_lib.KERNELS) == 10
+    assert _lib.KERNELS[7:] == ["adamw", "dequant", "grad_norm", "quant_act"] and len(_lib.KERNELS) == 11
 
 
 def test_adamw_hparams_layout():
