@@ -39,25 +39,37 @@ def gemm_fwd_flops(w, proj):
     return 2 * w.T * p.d_in * p.d_out + sum(2 * n * r * p.d_out for n, r in zip(w.tokens, w.ranks))
 
 
+GEMM_SOURCES = ("kernels_gemm.hip", "gemm_common.hpp", "device_common.hpp")
+
+
+def gemm_source_hash() -> str:
+    """First 16 hex digits of the sha256 of the bf16 GEMM's source files
+    (the kernel file and the headers it includes, in that order), the key
+    under which measured counters are stored."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, "adapter_lora_segments_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload: str, layout: str = "kn"):
     """HBM bytes per forward-GEMM launch from the committed counter summary
     (profiles/hbm_bytes_<workload>.txt), or None when that file is missing,
     covers another W0 layout, or was taken from a different version of the
     kernel source."""
-    import hashlib
     if layout != "kn":
         return None
     path = os.path.join(ROOT, "profiles", f"hbm_bytes_{workload}.txt")
-    src = os.path.join(ROOT, "adapter_lora_segments_amd", "csrc", "kernels_gemm.hip")
     if not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = gemm_source_hash()
     vals = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernels_gemm_sha256_16") != sha:
+    if vals.get("gemm_sources_sha256_16") != sha:
         return None
     v = vals.get("traffic_bytes k_gemm_fwd")
     return int(v) if v else None
@@ -632,6 +644,10 @@ def main():
                           "steps": steps, "data": "synthetic", "results": rows}), flush=True)
         return
     w = load_workload(a.workload, a.seed)
+    if w.dtype != "bf16":
+        print(f"{w.name} is a {w.dtype} workload: the oracle-sized case of the parity tests; the bench "
+              "times the bf16 workloads", file=sys.stderr)
+        sys.exit(2)
     if a.vendor_gemm:
         steps = min(a.steps, 30)
         r = vendor_gemm(w, steps, min(a.warmup, 5))
