@@ -353,7 +353,10 @@ void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nan
 //   dB item: part[c][n] = sum_t R[t][c] Wd[t][n]  (R = Z', Wd = dY)
 //   dA item: part[d][c] = sum_t Wd[t][d] R[t][c]  (R = dZ, Wd = X)
 // One launch per padded-rank bucket holds the dB items of the bucket's chunks
-// followed by their dA items.  Both operands are token-major, so each 8x8
+// followed by their dA items.  This register-staged form serves plans whose
+// rows come in the caller's order: each thread gathers its rows through the
+// permutation table (k_token_reduce_dma below serves grouped rows).  Both
+// operands are token-major, so each 8x8
 // block is transposed in registers on its way into k-contiguous, swizzled LDS
 // tiles (double buffered, one barrier per 64-token step).  The global loads
 // run two steps ahead in two register stages up to r_pad 64 (one above, to
@@ -566,24 +569,258 @@ __global__ __launch_bounds__(256) void k_token_reduce(TokenReduceArgs a) {
     token_reduce_body<RP, 1, PERM>(a, a.chunk_begin + (b - nb_b) / nbb_a, ((b - nb_b) % nbb_a) * 128, sbig, srk);
 }
 
+// ---------------------------------------------------------------------------
+// The same token reductions with both operands copied straight into LDS
+// (plans whose rows are already grouped by adapter).  One (chunk, WN-column
+// block) per workgroup.  Each KS-token stage holds the wide operand's
+// KS x WN block and the rank operand's KS x r_pad block, both with the
+// token axis along LDS rows as they lie in memory; the MFMA fragments, which take eight consecutive tokens per lane,
+// are read with the transposing ds_read_b64_tr_b16, so no register staging
+// and no transposes.  NS stages form a ring: while one is reduced, the next
+// NS - 1 are in flight.  Copies of rows past the chunk (and of columns past
+// the operand) read the zero page, so every stage issues the same number of
+// copies and one vmcnt bound fits every wait.
+//
+// LDS rows: a k-row (token) of CH 16-byte chunks; chunk c of k-row kr sits
+// at c ^ trsw<CH>(kr).  A transposing read group (32 lanes) covers four
+// consecutive k-rows (a multiple of 4 first) and four consecutive chunks (a
+// multiple of 4 first), i.e. 16 chunks that must fall in distinct 16-byte
+// bank groups (chunk index mod 16 of the tile): 16 or more chunks per row:
+// XOR bits 2-3 with the k-row's low bits; 8 per row (two rows per bank
+// line): XOR bit 2 with bit 1 of the k-row; 4 per row: already distinct.
+// ---------------------------------------------------------------------------
+template <int CH>
+__device__ __forceinline__ int trsw(int kr) {
+  return CH >= 16 ? ((kr & 3) << 2) : (CH == 8 ? (((kr >> 1) & 1) << 2) : 0);
+}
+
+// Operand fragment of a 32x32x16 MFMA from a token-major tile: lane l gets
+// tokens kb + 8 (l/32) + 0..7 of column cb + l%32.  ds_read_b64_tr_b16 hands
+// lane i of a 16-lane group element (i % 4) of the 8 bytes addressed by group
+// lane 4e + i/4, so group lane s addresses k-row kb' + s/4, columns
+// cb' + 4 (s%4); two reads cover the eight tokens.
+template <int CH>
+__device__ __forceinline__ u32x4 read_tok(const MLORA_LDS char* tile, int cb, int kb, int lane) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int g = lane >> 4, s = lane & 15;
+  const int n = cb + 16 * (g & 1) + 4 * (s & 3);
+  const int k = kb + 8 * (g >> 1) + (s >> 2);
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kr = k + 4 * h;
+    const int byte = (kr * CH + ((n >> 3) ^ trsw<CH>(kr))) * 16 + 2 * (n & 7);
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLORA_LDS s16x4*)(tile + byte));
+    const u32x2 u = __builtin_bit_cast(u32x2, v);
+    out[2 * h] = u[0];
+    out[2 * h + 1] = u[1];
+  }
+  return out;
+}
+
+// Shape per padded rank: WN wide columns per workgroup, KS tokens per
+// stage, WA x WB waves along the wide block and the rank, NS ring stages,
+// WGS workgroups per CU (160 KiB of LDS).  Measured on the 70B-shaped MLP
+// pair (isolated launches, one projection): 256-wide blocks in 32-token
+// stages took the r_pad 256 bucket from 693 to 500-530 us and r_pad 64/128
+// down 5%; at r_pad 32 they gain 2.5% there but lose 15% on a 4096x4096
+// layer, whose few chunks then fill fewer CUs.
+template <int RP>
+struct TrShape;
+template <> struct TrShape<32> { static constexpr int WN = 128, KS = 64, WA = 4, NS = 4, WGS = 2; };
+template <> struct TrShape<64> { static constexpr int WN = 256, KS = 32, WA = 2, NS = 4, WGS = 1; };
+template <> struct TrShape<128> { static constexpr int WN = 256, KS = 32, WA = 2, NS = 6, WGS = 1; };
+template <> struct TrShape<256> { static constexpr int WN = 256, KS = 32, WA = 2, NS = 4, WGS = 1; };
+
+template <int RP>
+struct TrCfg : TrShape<RP> {
+  using S = TrShape<RP>;
+  static constexpr int CHW = S::WN / 8;           // 16-byte chunks per wide k-row
+  static constexpr int CHR = RP / 8;              //   and per rank k-row
+  static constexpr int WB = 4 / S::WA;
+  static constexpr int FW = S::WN / S::WA / 32;   // wide fragments per wave
+  static constexpr int FR = RP / WB / 32;         // rank fragments per wave
+  static constexpr int WIDE = S::KS * S::WN * 2;  // bytes of a stage's wide block
+  static constexpr int RANK = S::KS * RP * 2;     //   and rank block
+  static constexpr int STAGE = WIDE + RANK;
+  static constexpr int CWW = WIDE / 4096;         // 1 KiB copies per wave per stage: wide
+  static constexpr int CWR = RANK / 4096;         //   and rank
+  static constexpr int CW = CWW + CWR;
+  static_assert(WIDE % 4096 == 0 && RANK % 4096 == 0 && FW >= 1 && FR >= 1, "shape");
+  static_assert(S::NS * STAGE * S::WGS <= 160 * 1024, "LDS");
+  static_assert((S::NS - 2) * CW <= 63, "vmcnt");
+};
+
+template <int RP, int MODE>
+__device__ __forceinline__ void token_reduce_dma_body(const TokenReduceArgs& a, int ch, int col0,
+                                                      const MLORA_LDS char* lds, uint32_t ring_lds) {
+  using C = TrCfg<RP>;
+  constexpr int KS = C::KS, NS = C::NS;
+  const uint16_t* big = MODE == 0 ? a.dY : a.X;
+  const int64_t big_ld = MODE == 0 ? a.ld_dy : a.d_in;   // row stride
+  const int64_t big_n = MODE == 0 ? a.d_out : a.d_in;    // columns, partial row length
+  const uint16_t* rk = MODE == 0 ? a.Z : a.dZ;
+  float* part = MODE == 0 ? a.partB : a.partA;
+  const int j = ldc(a.t.chunks + 3 * ch), r0 = ldc(a.t.chunks + 3 * ch + 1), nr = ldc(a.t.chunks + 3 * ch + 2);
+  const int64_t cp = ldc(a.t.cpref + ch);
+  const uint16_t* rbase = rk + ldc(a.t.zoff + j) + (int64_t)(r0 - ldc(a.t.seg0 + j)) * RP;
+  const uint16_t* wbase = big + (int64_t)r0 * big_ld;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+
+  // Copy i of wave w fills LDS chunks 64 (CW* w + i) + lane of its block:
+  // chunk q is k-row q / CH at position q % CH, which holds the row's chunk
+  // (q % CH) ^ trsw<CH>(k-row).
+  int wkr[C::CWW], wcol[C::CWW], rkr[C::CWR], roff[C::CWR];
+#pragma unroll
+  for (int i = 0; i < C::CWW; ++i) {
+    const int q = 64 * (C::CWW * w + i) + lane;
+    wkr[i] = q / C::CHW;
+    wcol[i] = col0 + 8 * ((q % C::CHW) ^ trsw<C::CHW>(wkr[i]));
+  }
+#pragma unroll
+  for (int i = 0; i < C::CWR; ++i) {
+    const int q = 64 * (C::CWR * w + i) + lane;
+    rkr[i] = q / C::CHR;
+    roff[i] = rkr[i] * RP + 8 * ((q % C::CHR) ^ trsw<C::CHR>(rkr[i]));
+  }
+  auto issue = [&](int st, int slot) {
+    const int t0 = KS * st;
+    const uint32_t base = ring_lds + (uint32_t)(slot * C::STAGE);
+#pragma unroll
+    for (int i = 0; i < C::CWW; ++i) {
+      const int t = t0 + wkr[i];
+      const void* src = (wcol[i] < big_n && t < nr) ? (const void*)(wbase + (int64_t)t * big_ld + wcol[i])
+                                                    : (const void*)a.t.zero;
+      dma16_at(src, base + 1024u * (uint32_t)(C::CWW * w + i));
+    }
+#pragma unroll
+    for (int i = 0; i < C::CWR; ++i) {
+      const void* src = t0 + rkr[i] < nr ? (const void*)(rbase + (int64_t)t0 * RP + roff[i]) : (const void*)a.t.zero;
+      dma16_at(src, base + (uint32_t)C::WIDE + 1024u * (uint32_t)(C::CWR * w + i));
+    }
+  };
+
+  const int wa = w % C::WA, wb = w / C::WA;
+  f32x16 acc[C::FW][C::FR];
+#pragma unroll
+  for (int x = 0; x < C::FW; ++x)
+#pragma unroll
+    for (int y = 0; y < C::FR; ++y)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
+  auto compute = [&](int slot) {
+    const MLORA_LDS char* wt = lds + slot * C::STAGE;
+    const MLORA_LDS char* rt = wt + C::WIDE;
+#pragma unroll
+    for (int ks = 0; ks < KS / 16; ++ks) {
+      u32x4 fw[C::FW], fr[C::FR];
+#pragma unroll
+      for (int x = 0; x < C::FW; ++x) fw[x] = read_tok<C::CHW>(wt, 32 * (C::FW * wa + x), 16 * ks, lane);
+#pragma unroll
+      for (int y = 0; y < C::FR; ++y) fr[y] = read_tok<C::CHR>(rt, 32 * (C::FR * wb + y), 16 * ks, lane);
+#pragma unroll
+      for (int x = 0; x < C::FW; ++x)
+#pragma unroll
+        for (int y = 0; y < C::FR; ++y)
+          acc[x][y] = MODE == 0 ? mfma32(fw[x], fr[y], acc[x][y])    // D[n][c]
+                                : mfma32(fr[y], fw[x], acc[x][y]);   // D[c][d]
+    }
+  };
+
+  const int steps = (nr + KS - 1) / KS;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) issue(st, st);
+  for (int st = 0; st < steps; ++st) {
+    // This wave's reads of the slot refilled below (step st-1's) are done;
+    // once its copies of stage st have landed, meet the other waves.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wait_vm_barrier<(NS - 2) * C::CW>();
+    issue(st + NS - 1, (st + NS - 1) % NS);
+    compute(st % NS);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // zero-page copies past the last stage
+
+#pragma unroll
+  for (int x = 0; x < C::FW; ++x) {
+#pragma unroll
+    for (int y = 0; y < C::FR; ++y) {
+      const int nb = col0 + 32 * (C::FW * wa + x), cb = 32 * (C::FR * wb + y);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v;
+        v[0] = acc[x][y][4 * g + 0];
+        v[1] = acc[x][y][4 * g + 1];
+        v[2] = acc[x][y][4 * g + 2];
+        v[3] = acc[x][y][4 * g + 3];
+        if (MODE == 0) {
+          // D[n][c]: lane holds c = cb + l32, n = nb + 8g + 4half + e
+          const int c = cb + l32;
+          const int n = nb + 8 * g + 4 * half;
+          if (n < big_n)
+            *reinterpret_cast<f32x4*>(part + ldc(a.t.cboff + ch) + (int64_t)c * big_n + n) = v;
+        } else {
+          // D[c][d]: lane holds d = nb + l32, c = cb + 8g + 4half + e
+          const int d = nb + l32;
+          const int c = cb + 8 * g + 4 * half;
+          if (d < big_n)
+            *reinterpret_cast<f32x4*>(part + cp * big_n + (int64_t)d * RP + c) = v;
+        }
+      }
+    }
+  }
+}
+
+// Workgroup b runs on XCD b % 8; item b' gives XCD x the contiguous items
+// [x q + min(x, r), ...) of total = 8 q + r, so the column blocks of one
+// chunk, which share its rank operand, meet in one XCD's L2.
+__device__ __forceinline__ int xcd_item(int b, int total) {
+  const int x = b & 7, q = total >> 3, r = total & 7;
+  return x * q + min(x, r) + (b >> 3);
+}
+
+template <int RP>
+__global__ __launch_bounds__(256, TrCfg<RP>::WGS) void k_token_reduce_dma(TokenReduceArgs a) {
+  __shared__ u32x4 ring[TrCfg<RP>::NS * TrCfg<RP>::STAGE / 16];
+  const MLORA_LDS char* lds = (const MLORA_LDS char*)(MLORA_LDS void*)&ring[0];
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLORA_LDS void*)&ring[0]);
+  constexpr int WN = TrCfg<RP>::WN;
+  const int nbb_b = (int)((a.d_out + WN - 1) / WN);
+  const int nbb_a = (int)((a.d_in + WN - 1) / WN);
+  const int nb_b = a.n_chunks * nbb_b;
+  const int b = xcd_item(blockIdx.x, a.n_chunks * (nbb_b + nbb_a));
+  if (b < nb_b)
+    token_reduce_dma_body<RP, 0>(a, a.chunk_begin + b / nbb_b, (b % nbb_b) * WN, lds, ring_lds);
+  else
+    token_reduce_dma_body<RP, 1>(a, a.chunk_begin + (b - nb_b) / nbb_a, ((b - nb_b) % nbb_a) * WN, lds,
+                                 ring_lds);
+}
+
+// Rows in the caller's order (a permutation table) go through the register
+// path, which gathers them; grouped rows through the direct-to-LDS path.
+template <int RP>
+static void launch_token_reduce_rp(const TokenReduceArgs& a, hipStream_t s) {
+  const int wn = a.t.perm ? 128 : TrCfg<RP>::WN;
+  const int nbb = (int)((a.d_out + wn - 1) / wn + (a.d_in + wn - 1) / wn);
+  const dim3 grid((unsigned)(a.n_chunks * nbb)), block(256);
+  if (a.t.perm) hipLaunchKernelGGL((k_token_reduce<RP, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_token_reduce_dma<RP>), grid, block, 0, s, a);
+}
+
 void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
                          const uint16_t* dY, int64_t ld_dy, const uint16_t* Z, float* partB,
                          int64_t d_out, const uint16_t* X, const uint16_t* dZ, float* partA,
                          int64_t d_in, hipStream_t s) {
   if (chunk_count <= 0) return;
-  TokenReduceArgs a{t, chunk_begin, chunk_count, dY, ld_dy, Z, partB, d_out, X, dZ, partA, d_in};
-  const int nbb_b = (int)((d_out + 127) / 128), nbb_a = (int)((d_in + 127) / 128);
-  dim3 grid((unsigned)(chunk_count * (nbb_b + nbb_a))), block(256);
-#define MLORA_TR(R)                                                                 \
-  if (t.perm) hipLaunchKernelGGL((k_token_reduce<R, true>), grid, block, 0, s, a);  \
-  else hipLaunchKernelGGL((k_token_reduce<R, false>), grid, block, 0, s, a);
+  const TokenReduceArgs a{t, chunk_begin, chunk_count, dY, ld_dy, Z, partB, d_out, X, dZ, partA, d_in};
   switch (rp) {
-    case 32: MLORA_TR(32) break;
-    case 64: MLORA_TR(64) break;
-    case 128: MLORA_TR(128) break;
-    default: MLORA_TR(256) break;
+    case 32: launch_token_reduce_rp<32>(a, s); break;
+    case 64: launch_token_reduce_rp<64>(a, s); break;
+    case 128: launch_token_reduce_rp<128>(a, s); break;
+    default: launch_token_reduce_rp<256>(a, s); break;
   }
-#undef MLORA_TR
 }
 
 // ---------------------------------------------------------------------------
