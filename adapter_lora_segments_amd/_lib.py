@@ -14,6 +14,7 @@ DTYPES = {"fp32": 0, "bf16": 1}
 W0_LAYOUTS = {"kn": 0, "nk": 1, "both": 2}
 W0_FORMATS = {"bf16": 0, "mxfp8": 1, "mxfp4": 2}
 ACT_FORMATS = {"bf16": 0, "mxfp8": 1}
+WG_OVERLAP = {"auto": 0, "side": 1, "after": 2}
 
 TABLES = ["rpad", "zoff", "roff", "group_first_adapter", "nb", "nb_start", "chunks", "chunk_start",
           "chunk_rpref", "adapter_chunk_first", "adapter_chunk_count", "tiles", "tile_start", "ext",
@@ -37,7 +38,7 @@ class PlanOpts(ctypes.Structure):
                 ("n_streams", ctypes.c_int32), ("chunk_min", ctypes.c_int32),
                 ("chunk_max", ctypes.c_int32), ("chunk_per_rank", ctypes.c_int32),
                 ("w0_layout", ctypes.c_int32), ("w0_format", ctypes.c_int32),
-                ("act_format", ctypes.c_int32)]
+                ("act_format", ctypes.c_int32), ("wg_overlap", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -49,7 +50,8 @@ class PlanInfo(ctypes.Structure):
                 ("n_nano", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
                 ("n_tiles", ctypes.c_int64), ("n_ext", ctypes.c_int64),
                 ("n_opt_blocks", ctypes.c_int64), ("n_proj", ctypes.c_int64),
-                ("act_offset", ctypes.c_int64), ("dz_offset", ctypes.c_int64)]
+                ("act_offset", ctypes.c_int64), ("dz_offset", ctypes.c_int64),
+                ("wg_side", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class AdamwHparams(ctypes.Structure):

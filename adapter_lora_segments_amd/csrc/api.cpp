@@ -37,6 +37,9 @@ struct mlora_plan_s {
   std::vector<std::vector<Range>> chunk_b;  // per group: one chunk range per padded rank
   std::vector<int32_t> group_max_rank;
   int32_t max_rank = 1;
+  // One stream group: the backward's weight gradients run beside the dX GEMM
+  // on the side stream (wg_overlap resolved), else after it.
+  bool wg_side = true;
   // The side stream: with one stream group, the backward's weight-gradient
   // branch (beside the dX GEMM); with several, every group's HBM-bound LoRA
   // work (shrink; dZ and the weight gradients), one group ahead of the base
@@ -258,6 +261,16 @@ mlora_status finish_plan(mlora::PlanTables&& P, mlora_plan_t* out) {
       p->group_max_rank[g] = std::max(p->group_max_rank[g], p->P.ranks[v]);
     p->max_rank = std::max(p->max_rank, p->group_max_rank[g]);
   }
+  // Where the weight gradients run (the fp32 path runs everything on the
+  // caller's stream): by wg_overlap, AUTO choosing the side stream while the
+  // dX GEMMs of all groups together have at most 16 rounds of 256 output
+  // tiles.
+  const auto& Q = p->P;
+  const int64_t dx_tiles = (int64_t)(Q.tile_start[S] - Q.tile_start[0]) * ((Q.d_in + 255) / 256);
+  if (Q.dtype != MLORA_BF16) p->wg_side = false;
+  else if (Q.opts.wg_overlap == MLORA_WG_SIDE) p->wg_side = true;
+  else if (Q.opts.wg_overlap == MLORA_WG_AFTER) p->wg_side = false;
+  else p->wg_side = dx_tiles <= 16 * 256;
   *out = p;
   return MLORA_OK;
 }
@@ -366,6 +379,7 @@ mlora_status mlora_plan_get_info(mlora_plan_t p, mlora_plan_info* info) {
   i.n_proj = P.nproj;
   i.dz_offset = (int64_t)p->L.dz;
   i.act_offset = P.opts.act_format == MLORA_ACT_MXFP8 ? (int64_t)p->L.xq : -1;
+  i.wg_side = p->wg_side ? 1 : 0;
   *info = i;
   return MLORA_OK;
 }
@@ -785,26 +799,33 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     return MLORA_OK;
   }
   if (P.n_groups == 1) {
-    // The weight gradients need dZ but not dX: they run on the side stream,
-    // enqueued after the dX GEMM so the GEMM's tiles take the chip first and
-    // the reductions fill the CUs its last round of tiles leaves idle.
+    // The weight gradients need dZ but not dX.  Side: they run on the side
+    // stream, enqueued after the dX GEMM so the GEMM's tiles take the chip
+    // first and the reductions fill the CUs its last round of tiles leaves
+    // idle.  After: on the caller's stream once the GEMM is done.
+    if (!p->wg_side) {
+      if ((st = dz(0, cs)) != MLORA_OK || (st = dx_gemm(0)) != MLORA_OK) return st;
+      return weight_grads(0, cs);
+    }
     if ((st = dz(0, cs)) != MLORA_OK || (st = fork_side(p, cs)) != MLORA_OK || (st = dx_gemm(0)) != MLORA_OK ||
         (st = weight_grads(0, p->side)) != MLORA_OK)
       return st;
     return wait_side(p, p->done_ev, cs);
   }
-  // Several groups: every group's dZ, then every group's weight gradients,
-  // on the side stream; the dX GEMM of group g, on the caller's stream,
-  // waits only for group g's dZ, so the GEMMs run one at a time while the
-  // side stream's HBM-bound work runs beside them.
+  // Several groups: every group's dZ on the side stream, then (side) every
+  // group's weight gradients there too; the dX GEMM of group g, on the
+  // caller's stream, waits only for group g's dZ, so the GEMMs run one at a
+  // time while the side stream's HBM-bound work runs beside them.  After:
+  // the weight gradients follow the last GEMM on the caller's stream.
   if ((st = fork_side(p, cs)) != MLORA_OK) return st;
   for (int g = 0; g < P.n_groups; ++g) {
     if ((st = dz(g, p->side)) != MLORA_OK) return st;
     hipError_t e = hipEventRecord(p->group_ev[g], p->side);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
-  for (int g = 0; g < P.n_groups; ++g)
-    if ((st = weight_grads(g, p->side)) != MLORA_OK) return st;
+  if (p->wg_side)
+    for (int g = 0; g < P.n_groups; ++g)
+      if ((st = weight_grads(g, p->side)) != MLORA_OK) return st;
   hipError_t e = hipEventRecord(p->done_ev, p->side);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   for (int g = 0; g < P.n_groups; ++g) {
@@ -813,7 +834,11 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
     if ((st = dx_gemm(g)) != MLORA_OK) return st;
   }
   e = hipStreamWaitEvent(cs, p->done_ev, 0);
-  return e == hipSuccess ? MLORA_OK : hip_fail(e, "join of the side stream");
+  if (e != hipSuccess) return hip_fail(e, "join of the side stream");
+  if (!p->wg_side)
+    for (int g = 0; g < P.n_groups; ++g)
+      if ((st = weight_grads(g, cs)) != MLORA_OK) return st;
+  return MLORA_OK;
 }
 
 mlora_status mlora_adamw_step(mlora_plan_t p, const mlora_adamw_hparams* hparams, void* const* A,

@@ -53,12 +53,13 @@
  * plan's internal side stream, forked from the caller's stream and joined
  * back to it with events before a call returns (so the caller sees ordinary
  * single-stream ordering), runs the HBM-bound LoRA work beside the base
- * GEMMs: with one stream group, the backward's weight gradients (dA, dB)
- * beside the dX GEMM; with n_streams > 1 adapter groups, every group's
- * shrink, dZ and weight gradients, group by group, while each group's base
- * GEMM runs on the caller's stream once its own group's shrink or dZ is
- * done.  The GEMMs of different groups never run at the same time, so each
- * has the chip and its caches to itself.
+ * GEMMs: with n_streams > 1 adapter groups, every group's shrink and dZ,
+ * group by group, while each group's base GEMM runs on the caller's stream
+ * once its own group's shrink or dZ is done; and the backward's weight
+ * gradients (dA, dB) beside the dX GEMMs when wg_overlap resolves to
+ * MLORA_WG_SIDE (otherwise they follow the last dX GEMM on the caller's
+ * stream).  The GEMMs of different groups never run at the same time, so
+ * each has the chip and its caches to itself.
  *
  * Graph capture.  forward, backward and mlora_adamw_step enqueue only
  * kernels and stream-ordering events (no allocation, no memset), so a plan
@@ -95,6 +96,17 @@ typedef enum { MLORA_W0_KN = 0, MLORA_W0_NK = 1, MLORA_W0_BOTH = 2 } mlora_w0_la
 typedef enum { MLORA_W0_BF16 = 0, MLORA_W0_MXFP8 = 1, MLORA_W0_MXFP4 = 2 } mlora_w0_format;
 typedef enum { MLORA_ACT_BF16 = 0, MLORA_ACT_MXFP8 = 1 } mlora_act_format;
 
+/* The backward's weight gradients (dA, dB) run on the side stream beside the
+ * dX GEMM(s) (SIDE), or after them on the caller's stream (AFTER).  AUTO:
+ * SIDE when the dX GEMMs of all stream groups together have at most 16
+ * rounds of 256 output tiles (their last round leaves CUs idle that the
+ * reductions fill), AFTER when they have more (the HBM-bound reductions then
+ * mostly compete with the GEMM for CUs and memory bandwidth: on the
+ * 70B-shaped MLP pair beside costs the dX GEMMs 7.6 ms a step, after costs
+ * 3.7 ms).  bf16 plans; the fp32 path runs everything on the caller's
+ * stream.  Results are bitwise identical either way. */
+typedef enum { MLORA_WG_AUTO = 0, MLORA_WG_SIDE = 1, MLORA_WG_AFTER = 2 } mlora_wg_overlap;
+
 #define MLORA_MAX_RANK 256
 #define MLORA_MAX_ADAPTERS 65536
 #define MLORA_MAX_STREAMS 4
@@ -114,6 +126,8 @@ typedef struct {
   int32_t act_format;     /* mlora_act_format of the activations in the forward's base product;
                              MLORA_ACT_MXFP8 needs w0_format MXFP8, w0_layout NK and d_in a
                              multiple of 128 (see "Activations on the MXFP8 matrix cores") */
+  int32_t wg_overlap;     /* mlora_wg_overlap: where the backward's weight gradients run
+                             (see "Streams"); default MLORA_WG_AUTO */
 } mlora_plan_opts;
 
 typedef struct mlora_plan_s *mlora_plan_t;
@@ -232,6 +246,9 @@ typedef struct {
   int64_t dz_offset;         /* byte offset in the workspace of dZ = s dY B^T (PLoRA §9.2,
                                 Case 2) as the last backward left it: z_elems elements in
                                 the layout of Z' (plan dtype), padding columns zero */
+  int32_t wg_side;           /* 1: the backward's weight gradients run beside the dX GEMM
+                                on the side stream (wg_overlap resolved); 0: after it */
+  int32_t reserved;
 } mlora_plan_info;
 
 mlora_status mlora_plan_get_info(mlora_plan_t plan, mlora_plan_info *info);

@@ -39,7 +39,7 @@ def custom_workload(name, dtype, d_in, d_out, ranks, tokens, scales=None, seed=0
 
 
 def run_gpu(w: Workload, proj=0, w0_layout="kn", n_streams=None, nano_rows=0, h=None,
-            want_dx=True, chunk_min=0, chunk_max=0, chunk_per_rank=0):
+            want_dx=True, chunk_min=0, chunk_max=0, chunk_per_rank=0, wg_overlap="auto"):
     """Run forward+backward on the GPU.  Returns (host inputs, outputs dict)."""
     import torch
     from adapter_lora_segments_amd import Plan, PackedLoRALinear
@@ -49,7 +49,7 @@ def run_gpu(w: Workload, proj=0, w0_layout="kn", n_streams=None, nano_rows=0, h=
     plan = Plan(h["offsets"], h["ranks"], h["d_in"], h["d_out"], dt,
                 n_streams=n_streams if n_streams is not None else w.n_streams,
                 nano_rows=nano_rows, w0_layout=w0_layout, chunk_min=chunk_min,
-                chunk_max=chunk_max, chunk_per_rank=chunk_per_rank)
+                chunk_max=chunk_max, chunk_per_rank=chunk_per_rank, wg_overlap=wg_overlap)
     W0h = h["W0"] if w0_layout == "kn" else np.ascontiguousarray(h["W0"].T)
     W0 = to_dev(W0h, dt)
     A = [to_dev(a, dt) for a in h["A"]]

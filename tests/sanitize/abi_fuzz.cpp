@@ -110,12 +110,14 @@ mlora_plan_opts opts() {
   o.w0_layout = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 5 : 2);
   o.w0_format = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 5 : 2);
   o.act_format = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 3 : 1);
+  o.wg_overlap = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 4 : 2);
   return o;
 }
 
 void exercise(mlora_plan_t p) {
   mlora_plan_info info{};
   if (mlora_plan_get_info(p, &info) != MLORA_OK) std::abort();
+  if (info.wg_side != 0 && info.wg_side != 1) std::abort();
   for (int32_t t = -1; t <= MLORA_TAB_COUNT; ++t) {
     size_t bytes = 0;
     mlora_status s = mlora_plan_export(p, t, nullptr, &bytes);

@@ -558,3 +558,30 @@ def test_library_plans_match_hand_worked_goldens():
     # rule 9 rebalanced by hand: 10 forward tiles over 130 K-steps -> 15 parts,
     # 17 dX tiles over 80 K-steps -> 10 parts
     assert Plan([0, 256], [8], 4160, 2560).export("ksplit").tolist() == [[15, 10]]
+
+
+def test_weight_gradient_placement_rule():
+    """wg_overlap: AUTO puts a bf16 plan's weight gradients beside the dX
+    GEMMs while those (all stream groups together) have at most 16 rounds of
+    256 output tiles (4096 tiles), after them otherwise; SIDE and AFTER force
+    the choice; fp32 plans run them on the caller's stream; other values are
+    refused."""
+    # 4096 tiles exactly: 256 row tiles x 16 column tiles (T = 65536, d_in = 4096)
+    assert Plan([0, 65536], [8], 4096, 256).info["wg_side"] == 1
+    # one more column tile: 256 x 17
+    assert Plan([0, 65536], [8], 4352, 256).info["wg_side"] == 0
+    assert Plan([0, 65536], [8], 4352, 256, wg_overlap="side").info["wg_side"] == 1
+    assert Plan([0, 100], [8], 256, 256, wg_overlap="after").info["wg_side"] == 0
+    assert Plan([0, 100], [8], 256, 256).info["wg_side"] == 1
+    assert Plan([0, 65536, 70000], [8, 16], 4352, 256, n_streams=2).info["wg_side"] == 0
+    assert Plan([0, 30000, 65536], [8, 16], 4096, 256, n_streams=2).info["wg_side"] == 1
+    assert Plan([0, 30000, 65536], [8, 16], 4096, 256, n_streams=2, wg_overlap="after").info["wg_side"] == 0
+    assert Plan([0, 100], [8], 256, 256, "fp32", wg_overlap="side").info["wg_side"] == 0
+    o = _lib.PlanOpts()
+    o.wg_overlap = 3
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    off = (ctypes.c_int64 * 2)(0, 100)
+    rk = (ctypes.c_int32 * 1)(8)
+    assert L.mlora_plan(1, off, rk, 256, 256, 0, ctypes.byref(o), ctypes.byref(h)) == -1
+    assert "wg_overlap" in L.mlora_last_error().decode()

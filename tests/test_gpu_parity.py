@@ -143,6 +143,26 @@ def test_bitwise_repeatable():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("streams", [1, 3])
+def test_weight_gradients_beside_or_after_dx(streams):
+    """The backward's weight gradients on the side stream beside the dX GEMM
+    and on the caller's stream after it: the same kernels on the same data,
+    so every output is bitwise identical, and within the bar of the oracle."""
+    w = custom_workload("placement", "bf16", 512, 768, [64, 16, 256, 8], [600, 257, 300, 33], seed=8)
+    say(f"case weight gradients beside or after the dX GEMM, {streams} stream group(s)")
+    res = {}
+    for mode in ("side", "after"):
+        h, out = run_gpu(w, wg_overlap=mode, n_streams=streams)
+        assert out["plan"].info["wg_side"] == (1 if mode == "side" else 0)
+        compare(w, h, out, what=f"bf16_wg_{mode}")
+        res[mode] = out
+    for k in ("Y", "dX", "Z", "dZ"):
+        assert np.array_equal(res["side"][k], res["after"][k]), k
+    for k in ("dA", "dB"):
+        for a, b in zip(res["side"][k], res["after"][k]):
+            assert np.array_equal(a, b), k
+
+
 def test_llama7b_proj_full_size():
     """The 4096x4096 workload at full size, every output element checked."""
     w = load_workload("llama7b_proj", 0)
