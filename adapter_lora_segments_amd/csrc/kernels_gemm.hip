@@ -60,6 +60,28 @@ __device__ __forceinline__ u32x4 read_b_tr(const u32x4* tile, int nb, int kb, in
   return out;
 }
 
+// 16 bytes per lane into LDS from a wave-uniform base plus a 32-bit lane
+// offset (global_load_lds_dwordx4 with a scalar base): the base lives in
+// SGPRs, so advancing it costs scalar adds only.  M0 as in dma16_at.
+__device__ __forceinline__ uint64_t uniform64(const void* p) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  // readfirstlane returns int: widen through uint32_t, never sign-extend
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
+}
+__device__ __forceinline__ void dma16_sv(uint64_t sbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
 // Four waves, one per SIMD, share the tile, two along M and two along N;
 // each wave owns 128x128 accumulators (256 registers), so every 16-byte
 // fragment read from LDS feeds four MFMAs.
@@ -123,22 +145,37 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   // position lane%8, which holds the row's chunk c = (lane%8) ^ kx8(row).
   // Copy i of an n-contiguous unit: k-row 16w + 2i + lane/32 into LDS
   // position lane%32, which holds the k-row's chunk (lane%32) ^ nx(k-row).
+  // Main K-steps read a wave-uniform base (the tile's first row or column at
+  // the step's k) plus a fixed 32-bit lane offset (bytes), so a step only
+  // advances scalar bases; with rows through the permutation table the A
+  // copies keep one full pointer each.
   int crow[CPW], cch[CPW], nkr[CPW], nch[CPW];
+  uint32_t aoff[CPW], boff[CPW];
   const uint16_t* aptr[CPW];
-  const uint16_t* bptr[CPW];
+  const char* const baseA = reinterpret_cast<const char*>(g.A + (int64_t)row0 * g.lda + 32 * kb);
+  const char* const baseB = reinterpret_cast<const char*>(
+      MAIN_B_KC ? g.B + (int64_t)n0 * g.ldb + 32 * kb : g.B + (int64_t)(32 * kb) * g.ldb + n0);
+  const int64_t strideB = MAIN_B_KC ? 128 : (int64_t)128 * g.ldb;   // bytes per 64-deep step
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     crow[i] = 64 * w + 8 * i + (lane >> 3);
     cch[i] = (lane & 7) ^ kx8(crow[i]);
     nkr[i] = 16 * w + 2 * i + (lane >> 5);
     nch[i] = (lane & 31) ^ nx(nkr[i]);
-    const int ar = row0 + min(crow[i], mrows - 1);
-    aptr[i] = g.A + (int64_t)(PERM ? ldg_i32(g.t.perm + ar) : ar) * g.lda + 32 * kb + 8 * cch[i];
-    if (MAIN_B_KC)
-      bptr[i] = g.B + (int64_t)min(n0 + crow[i], g.N - 1) * g.ldb + 32 * kb + 8 * cch[i];
+    const int ar = min(crow[i], mrows - 1);
+    if constexpr (PERM)
+      aptr[i] = g.A + (int64_t)ldg_i32(g.t.perm + row0 + ar) * g.lda + 32 * kb + 8 * cch[i];
     else
-      bptr[i] = g.B + (int64_t)(32 * kb + nkr[i]) * g.ldb + min(n0 + 8 * nch[i], g.N - 8);
+      aoff[i] = (uint32_t)(((int64_t)ar * g.lda + 8 * cch[i]) * 2);
+    boff[i] = MAIN_B_KC ? (uint32_t)(((int64_t)(min(n0 + crow[i], g.N - 1) - n0) * g.ldb + 8 * cch[i]) * 2)
+                        : (uint32_t)(((int64_t)nkr[i] * g.ldb + (min(n0 + 8 * nch[i], g.N - 8) - n0)) * 2);
   }
+  // Copy i of main K-step t, operand op: its source as a pointer.
+  auto main_src = [&](int t, int op, int i) -> const uint16_t* {
+    if (op) return reinterpret_cast<const uint16_t*>(baseB + t * strideB + boff[i]);
+    if constexpr (PERM) return aptr[i] + 64 * t;
+    return reinterpret_cast<const uint16_t*>(baseA + (int64_t)t * 128 + aoff[i]);
+  };
 
   // Sources of unit u's copies: main sub-steps at the operand's pointer plus
   // 64 k per step; extension sub-steps from the plan's list (rows outside the
@@ -187,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
         } else {
           ext = g.ext_n + ((h ? ro[1] : ro[0]) + k) * g.N + col;
         }
-        src[i] = kd == 0 ? bptr[i] + (int64_t)(64 * t) * g.ldb : (kd == 1 ? ext : g.t.zero);
+        src[i] = kd == 0 ? main_src(t, 1, i) : (kd == 1 ? ext : g.t.zero);
       }
       return;
     }
@@ -195,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     for (int i = 0; i < CPW; ++i) {
       const int h = cch[i] >> 2, kk = 8 * (cch[i] & 3);
       const int kd = h ? kind[1] : kind[0];
-      const uint16_t* main = (op ? bptr[i] : aptr[i]) + 64 * t;
+      const uint16_t* main = main_src(t, op, i);
       const uint16_t* ext;
       if (op == 0) {
         const int grow = row0 + crow[i];
@@ -216,9 +253,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   auto copy = [&](const uint16_t* src, int u, int i) {
     dma16_at(src, ring_lds + 16u * (uint32_t)((u % NU) * 2048 + 512 * w + 64 * i));
   };
-  auto src_main = [&](int u, int i) -> const uint16_t* {
-    if (u & 1) return MAIN_B_KC ? bptr[i] + 64 * (u >> 1) : bptr[i] + (int64_t)(64 * (u >> 1)) * g.ldb;
-    return aptr[i] + 64 * (u >> 1);
+  // Copy i of unit u, a main K-step.
+  // Copy i of unit u, a main K-step; sbase: the operand's uniform base at
+  // the unit's step (made once per unit).
+  auto copy_main = [&](int u, int i, uint64_t sbase) {
+    const uint32_t lds = ring_lds + 16u * (uint32_t)((u % NU) * 2048 + 512 * w + 64 * i);
+    if (u & 1) dma16_sv(sbase, boff[i], lds);
+    else if constexpr (PERM) dma16_at(aptr[i] + 64 * (u >> 1), lds);
+    else dma16_sv(sbase, aoff[i], lds);
   };
 
   f32x16 acc[FI][FJ];
@@ -230,17 +272,70 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
   u32x4 fa[2][FI], fb[2][FJ];
-  // Fragment read r (0..7) of slice ks of step s (A fragments first).
-  auto read_frag = [&](int s, int ks, u32x4 (&ra)[FI], u32x4 (&rb)[FJ], int r) {
-    const int c = 2 * ks + half;
+  // LDS byte offsets of this lane's fragment reads, split into a lane part
+  // and immediates.  k-contiguous: row wrow + 32 r + l32 (r: +4096 bytes),
+  // chunk (2 ks + half) ^ kx8(l32), one lane part per ks.  n-contiguous
+  // (transposing reads): one lane part per fragment fj, with ks (+8192) and
+  // the second half of the k-rows (+2048) as immediates (nx depends only on
+  // k-row bits 0, 1 and 3, which the lane fixes).
+  const MLORA_LDS char* const lds0 = (const MLORA_LDS char*)(MLORA_LDS void*)&ring[0][0];
+  uint32_t alane[4], blane[4];
+  {
+    const int kxl = kx8(l32);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      alane[ks] = (uint32_t)(((wrow + l32) * 8 + ((2 * ks + half) ^ kxl)) * 16);
+      if (MAIN_B_KC) blane[ks] = (uint32_t)(((wcol + l32) * 8 + ((2 * ks + half) ^ kxl)) * 16);
+    }
+    if (!MAIN_B_KC) {
+      const int gq = lane >> 4, sq = lane & 15;
+      const int kq = 8 * (gq >> 1) + (sq >> 2);
+#pragma unroll
+      for (int fj = 0; fj < FJ; ++fj) {
+        const int n = wcol + 32 * fj + 16 * (gq & 1) + 4 * (sq & 3);
+        blane[fj] = (uint32_t)(npos(kq, n >> 3) * 16 + 2 * (n & 7));
+      }
+    }
+  }
+  // Per-step read bases: a lane part plus the step's ring slot, made once
+  // per step (the empty asm keeps the compiler from folding the slot into
+  // every read's address), so each read is a base plus an immediate.
+  struct Bases {
+    uint32_t a[4], b[4];   // A per ks; B per ks (k-contiguous) or per fragment (n-contiguous)
+  };
+  auto step_bases = [&](int s, Bases& bs, int ks0, int ks1) {
+    const uint32_t sa = (uint32_t)((2 * s) % NU) * 32768u, sb = (uint32_t)((2 * s + 1) % NU) * 32768u;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < ks0 || ks > ks1) continue;
+      bs.a[ks] = alane[ks] + sa;
+      asm volatile("" : "+v"(bs.a[ks]));
+      if (MAIN_B_KC) {
+        bs.b[ks] = blane[ks] + sb;
+        asm volatile("" : "+v"(bs.b[ks]));
+      }
+    }
+    if (!MAIN_B_KC) {
+#pragma unroll
+      for (int fj = 0; fj < FJ; ++fj) {
+        bs.b[fj] = blane[fj] + sb;
+        asm volatile("" : "+v"(bs.b[fj]));
+      }
+    }
+  };
+  // Fragment read r (0..7) of slice ks (A fragments first) from bases bs.
+  auto read_frag = [&](const Bases& bs, int ks, u32x4 (&ra)[FI], u32x4 (&rb)[FJ], int r) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
     if (r < FI) {
-      const int row = wrow + 32 * r + l32;
-      ra[r] = ring[(2 * s) % NU][row * 8 + (c ^ kx8(row))];
+      ra[r] = *(const MLORA_LDS u32x4*)(lds0 + bs.a[ks] + 4096 * r);
     } else if (MAIN_B_KC) {
-      const int row = wcol + 32 * (r - FI) + l32;
-      rb[r - FI] = ring[(2 * s + 1) % NU][row * 8 + (c ^ kx8(row))];
+      rb[r - FI] = *(const MLORA_LDS u32x4*)(lds0 + bs.b[ks] + 4096 * (r - FI));
     } else {
-      rb[r - FI] = read_b_tr(ring[(2 * s + 1) % NU], wcol + 32 * (r - FI), 16 * ks, lane);
+      const MLORA_LDS char* p = lds0 + bs.b[r - FI] + 8192 * ks;
+      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLORA_LDS s16x4*)p);
+      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLORA_LDS s16x4*)(p + 2048));
+      const u32x2 u0 = __builtin_bit_cast(u32x2, v0), u1 = __builtin_bit_cast(u32x2, v1);
+      rb[r - FI] = u32x4{u0[0], u0[1], u1[0], u1[1]};
     }
   };
   auto mma = [&](const u32x4 (&ra)[FI], const u32x4 (&rb)[FJ], int qq) {
@@ -255,14 +350,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   // MFMAs earlier.  n-contiguous B (two transposing reads per fragment): one
   // fragment per slot in the first eight, A fragments first.
   constexpr int kOrder[FI + FJ] = {0, FI, FI + 1, FI + 2, FI + 3, 1, 2, 3};
-  auto reads_at = [&](int qq, int s, int ks, u32x4 (&ra)[FI], u32x4 (&rb)[FJ]) {
+  auto reads_at = [&](int qq, const Bases& bs, int ks, u32x4 (&ra)[FI], u32x4 (&rb)[FJ]) {
     if (MAIN_B_KC) {
       if (qq < 4) {
-        read_frag(s, ks, ra, rb, kOrder[2 * qq]);
-        read_frag(s, ks, ra, rb, kOrder[2 * qq + 1]);
+        read_frag(bs, ks, ra, rb, kOrder[2 * qq]);
+        read_frag(bs, ks, ra, rb, kOrder[2 * qq + 1]);
       }
     } else if (qq < FI + FJ) {
-      read_frag(s, ks, ra, rb, qq);
+      read_frag(bs, ks, ra, rb, qq);
     }
   };
   // First MFMA slot of a slice that carries a copy.
@@ -271,38 +366,52 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     constexpr bool MAIN = decltype(main_tag)::value;   // units 2s+4 and 2s+5 are main K
     const uint16_t* sa[CPW];
     if (!MAIN) unit_sources(2 * s + 4, sa);
+    Bases cur;
+    step_bases(s, cur, 1, 3);
+    const uint64_t cbA = MAIN && !PERM ? uniform64(baseA + (int64_t)(s + 2) * 128) : 0;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[0], fb[0], qq);
-      reads_at(qq, s, 1, fa[1], fb[1]);
-      if (qq >= C0 && qq < C0 + 4) copy(MAIN ? src_main(2 * s + 4, qq - C0) : sa[qq - C0], 2 * s + 4, qq - C0);
+      reads_at(qq, cur, 1, fa[1], fb[1]);
+      if (qq >= C0 && qq < C0 + 4) {
+        if (MAIN) copy_main(2 * s + 4, qq - C0, cbA);
+        else copy(sa[qq - C0], 2 * s + 4, qq - C0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[1], fb[1], qq);
-      reads_at(qq, s, 2, fa[0], fb[0]);
-      if (qq >= C0 && qq < C0 + 4)
-        copy(MAIN ? src_main(2 * s + 4, qq - C0 + 4) : sa[qq - C0 + 4], 2 * s + 4, qq - C0 + 4);
+      reads_at(qq, cur, 2, fa[0], fb[0]);
+      if (qq >= C0 && qq < C0 + 4) {
+        if (MAIN) copy_main(2 * s + 4, qq - C0 + 4, cbA);
+        else copy(sa[qq - C0 + 4], 2 * s + 4, qq - C0 + 4);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[0], fb[0], qq);
-      reads_at(qq, s, 3, fa[1], fb[1]);
+      reads_at(qq, cur, 3, fa[1], fb[1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     wait_vm_barrier<CPW>();
     const uint16_t* sb[CPW];
     if (!MAIN) unit_sources(2 * s + 5, sb);
+    Bases nxt;
+    step_bases(s + 1, nxt, 0, 0);
+    const uint64_t cbB = MAIN ? uniform64(baseB + (int64_t)(s + 2) * strideB) : 0;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[1], fb[1], qq);
-      reads_at(qq, s + 1, 0, fa[0], fb[0]);
-      if (qq >= C0 && qq < C0 + 8) copy(MAIN ? src_main(2 * s + 5, qq - C0) : sb[qq - C0], 2 * s + 5, qq - C0);
+      reads_at(qq, nxt, 0, fa[0], fb[0]);
+      if (qq >= C0 && qq < C0 + 8) {
+        if (MAIN) copy_main(2 * s + 5, qq - C0, cbB);
+        else copy(sb[qq - C0], 2 * s + 5, qq - C0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -317,8 +426,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     for (int i = 0; i < CPW; ++i) copy(src[i], u, i);
   }
   wait_vm_barrier<2 * CPW>();
+  {
+    Bases b0;
+    step_bases(0, b0, 0, 0);
 #pragma unroll
-  for (int r = 0; r < FI + FJ; ++r) read_frag(0, 0, fa[0], fb[0], r);
+    for (int r = 0; r < FI + FJ; ++r) read_frag(b0, 0, fa[0], fb[0], r);
+  }
 
   int s = 0;
   for (; 2 * s + 6 <= nk; ++s) step_block(s, std::true_type());
