@@ -758,7 +758,8 @@ mlora_status mlora_backward(mlora_plan_t p, const void* dY, const void* X, const
       mlora_status s2 = timed(p, MLORA_K_TOKEN_REDUCE, sw, [&] {
         const int64_t c0 = P.pcol[r.proj], w = P.pcol[r.proj + 1] - c0;
         mlora::launch_token_reduce(r.rp, t, r.begin, r.count, (const uint16_t*)dY + c0, P.d_out,
-                                   (const uint16_t*)Z, partB, w, (const uint16_t*)X, dZ, partA, P.d_in, sw);
+                                   (const uint16_t*)Z, partB, w, (const uint16_t*)X, dZ, partA, P.d_in, dA, dB,
+                                   sw);
       });
       if (s2 != MLORA_OK) return s2;
     }

@@ -67,14 +67,18 @@ void launch_skinny(int mode, const DevTables& t, int32_t nano_begin, int32_t nan
 //   dB: partB[cboff + c*d_out + n] = sum_t Z'[t][c] dY[t][n]   (n < d_out)
 //   dA: partA[cpref][d][c] = sum_t X[t][d] dZ[t][c]            (d < d_in)
 // dY points at the projection's first column, rows ld_dy apart; d_out is the
-// projection's width.
+// projection's width.  With rows grouped by adapter (no permutation table),
+// an adapter with a single chunk writes its fp32 dA_j [d_in][r_j] and dB_j
+// [r_j][d_out] (pointer arrays dA, dB) directly instead of a partial.
 void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
                          const uint16_t* dY, int64_t ld_dy, const uint16_t* Z, float* partB,
                          int64_t d_out, const uint16_t* X, const uint16_t* dZ, float* partA,
-                         int64_t d_in, hipStream_t s);
+                         int64_t d_in, void* const* dA, void* const* dB, hipStream_t s);
 
 // Fixed-order sum of the chunk partials into the caller's dA_j / dB_j
-// (adapters [a_begin, a_end)); adapters without rows get zeros.
+// (adapters [a_begin, a_end)); adapters without rows get zeros; with rows
+// grouped by adapter, single-chunk adapters are skipped (the token
+// reductions wrote them).
 void launch_reduce_partials(const DevTables& t, int32_t a_begin, int32_t a_end, int64_t d_in,
                             int64_t d_out, const float* partA, const float* partB,
                             void* const* dA, void* const* dB, int32_t max_rank, hipStream_t s);

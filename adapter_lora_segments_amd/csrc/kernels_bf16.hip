@@ -376,6 +376,11 @@ struct TokenReduceArgs {
   const uint16_t* dZ;
   float* partA;
   int64_t d_in;
+  // Grouped rows: an adapter with a single chunk writes its dA_j / dB_j
+  // (fp32, rank r_j unpadded) directly, and the partial sums skip it.
+  void* const* dA;
+  void* const* dB;
+  int32_t direct;
 };
 
 template <int RP, int MODE, bool PERM>
@@ -743,6 +748,11 @@ __device__ __forceinline__ void token_reduce_dma_body(const TokenReduceArgs& a, 
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // zero-page copies past the last stage
 
+  // A single-chunk adapter's sum is its gradient: written straight to dB_j
+  // [r_j][big_n] or dA_j [d_in][r_j] (columns c < r_j), not to the partials.
+  const bool direct = a.direct && ldc(a.t.ch_count + j) == 1;
+  const int rj = ldc(a.t.ranks + j);
+  float* const grad = direct ? static_cast<float*>(ldc((MODE == 0 ? a.dB : a.dA) + j)) : nullptr;
 #pragma unroll
   for (int x = 0; x < C::FW; ++x) {
 #pragma unroll
@@ -759,14 +769,25 @@ __device__ __forceinline__ void token_reduce_dma_body(const TokenReduceArgs& a, 
           // D[n][c]: lane holds c = cb + l32, n = nb + 8g + 4half + e
           const int c = cb + l32;
           const int n = nb + 8 * g + 4 * half;
-          if (n < big_n)
-            *reinterpret_cast<f32x4*>(part + ldc(a.t.cboff + ch) + (int64_t)c * big_n + n) = v;
+          if (n < big_n) {
+            if (!direct)
+              *reinterpret_cast<f32x4*>(part + ldc(a.t.cboff + ch) + (int64_t)c * big_n + n) = v;
+            else if (c < rj)
+              *reinterpret_cast<f32x4*>(grad + (int64_t)c * big_n + n) = v;
+          }
         } else {
           // D[c][d]: lane holds d = nb + l32, c = cb + 8g + 4half + e
           const int d = nb + l32;
           const int c = cb + 8 * g + 4 * half;
-          if (d < big_n)
-            *reinterpret_cast<f32x4*>(part + cp * big_n + (int64_t)d * RP + c) = v;
+          if (d < big_n) {
+            if (!direct) {
+              *reinterpret_cast<f32x4*>(part + cp * big_n + (int64_t)d * RP + c) = v;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (c + e < rj) grad[(int64_t)d * rj + c + e] = v[e];
+            }
+          }
         }
       }
     }
@@ -812,9 +833,10 @@ static void launch_token_reduce_rp(const TokenReduceArgs& a, hipStream_t s) {
 void launch_token_reduce(int rp, const DevTables& t, int32_t chunk_begin, int32_t chunk_count,
                          const uint16_t* dY, int64_t ld_dy, const uint16_t* Z, float* partB,
                          int64_t d_out, const uint16_t* X, const uint16_t* dZ, float* partA,
-                         int64_t d_in, hipStream_t s) {
+                         int64_t d_in, void* const* dA, void* const* dB, hipStream_t s) {
   if (chunk_count <= 0) return;
-  const TokenReduceArgs a{t, chunk_begin, chunk_count, dY, ld_dy, Z, partB, d_out, X, dZ, partA, d_in};
+  const TokenReduceArgs a{t, chunk_begin, chunk_count, dY, ld_dy, Z, partB, d_out, X, dZ, partA, d_in,
+                          dA, dB, t.perm ? 0 : 1};
   switch (rp) {
     case 32: launch_token_reduce_rp<32>(a, s); break;
     case 64: launch_token_reduce_rp<64>(a, s); break;
@@ -836,6 +858,7 @@ __global__ __launch_bounds__(256) void k_reduce_partials(DevTables t, int32_t a_
   for (int32_t j = a_begin + blockIdx.y; j < a_end; j += gridDim.y) {
     const int r = ldc(t.ranks + j), rp = ldc(t.rpad + j);
     const int first = ldc(t.ch_first + j), cnt = ldc(t.ch_count + j);
+    if (cnt == 1 && !t.perm) continue;   // written by the token reduction itself
     const int pq = j % t.nproj;
     const int64_t w = ldc(t.pcol + pq + 1) - ldc(t.pcol + pq);   // dB_j is [r][w]
     const int64_t na4 = d_in * (rp / 4), nb4 = (int64_t)r * (w / 4);
