@@ -583,8 +583,9 @@ mlora_status forward_impl(mlora_plan_s* p, const void* X, const void* W0, const 
       gm.g.ksplit = 1;
       gm.Aq = xq_codes;
       gm.Asc = xq_scales;
+      gm.b4 = P.opts.w0_format == MLORA_W0_MXFP4 ? 1 : 0;
       gm.Bq = static_cast<const uint8_t*>(W0);
-      gm.Bsc = static_cast<const uint8_t*>(W0) + (size_t)P.d_in * (size_t)P.d_out;
+      gm.Bsc = static_cast<const uint8_t*>(W0) + (size_t)P.d_in * (size_t)P.d_out / (gm.b4 ? 2 : 1);
       st = timed(p, MLORA_K_GEMM_FWD, cs, [&] { mlora::launch_gemm_mx8(gm, cs); });
     } else {
       st = timed(p, MLORA_K_GEMM_FWD, cs, [&] { mlora::launch_gemm(true, nk, ga, cs); });

@@ -113,16 +113,18 @@ struct GemmArgs {
   float* part;
   DevTables t;
 };
-// Forward GEMM over MXFP8 operands (kernels_gemm_mx.hip): g as for
+// Forward GEMM over microscaled operands (kernels_gemm_mx.hip): g as for
 // launch_gemm(true, true, ...) without split-K; the main operands are X's
 // E4M3 codes [rows][K] with scales [rows][K / 32] (rows in the caller's
-// order) and W0's codes [N][K] with scales [N][K / 32]; K a multiple of 128.
+// order) and W0's codes [N][K] (b4: E2M1, [N][K / 2], two a byte, the even
+// element low) with scales [N][K / 32]; K a multiple of 128.
 struct GemmMxArgs {
   GemmArgs g;
   const uint8_t* Aq;
   const uint8_t* Asc;
   const uint8_t* Bq;
   const uint8_t* Bsc;
+  int32_t b4;
 };
 void launch_gemm_mx8(const GemmMxArgs& m, hipStream_t s);
 // Activations [T][K] (bf16, rows dense) to MXFP8 codes [T][K] and scales [T][K / 32].

@@ -107,8 +107,15 @@ void launch_quant_act_mx8(const uint16_t* X, int64_t T, int64_t K, uint8_t* code
 // bf16 kernel.  The scale MFMA takes 64 of K: lane l = r + 32 h holds row r's
 // 16-value pieces h of both 32-blocks of the slice (chunk 4 sl + h, then
 // 4 sl + 2 + h) and supplies the scale of block h.
+// B4: W0 as MXFP4 (E2M1 codes, two a byte along K, [N][K / 2]) on the same
+// instruction with an FP4 first operand.  A main step's W0 unit is then 256
+// rows of 64 bytes (chunk c of row r at c ^ ((r >> 2) & 3), which spreads a
+// read group's rows over the banks), copied four per wave; measured with a
+// structured probe, an FP4 operand's lane r + 32 h holds row r's whole
+// 32-block h of the 64-K slice (16 bytes, the low nibble first), one 16-byte
+// read, and supplies block h's scale as in the FP8 case.
 // ---------------------------------------------------------------------------
-template <bool PERM>
+template <bool PERM, bool B4>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx8(GemmMxArgs m) {
   const GemmArgs& g = m.g;
   constexpr int FI = 4, FJ = 4, CPW = 8;
@@ -136,16 +143,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx8(GemmMxArgs m) {
 
   // Copy i of a unit: tile row 64 w + 8 i + lane / 8 into LDS position
   // lane % 8, which holds the row's chunk (lane % 8) ^ kx8(row).
+  // B4: copy i (< 4) of a W0 unit: rows 64 w + 16 i + lane / 4, LDS position
+  // lane % 4 holding chunk (lane % 4) ^ ((row >> 2) & 3).
   int crow[CPW], cch[CPW];
   const uint8_t* aq[CPW];
   const uint8_t* bq[CPW];
+  const int64_t kbq = B4 ? g.K / 2 : g.K;        // W0 code bytes per row
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     crow[i] = 64 * w + 8 * i + (lane >> 3);
     cch[i] = (lane & 7) ^ kx8(crow[i]);
     const int ar = row0 + min(crow[i], mrows - 1);
     aq[i] = m.Aq + (int64_t)(PERM ? ldg_i32(g.t.perm + ar) : ar) * g.K + 16 * cch[i];
-    bq[i] = m.Bq + (int64_t)min(n0 + crow[i], g.N - 1) * g.K + 16 * cch[i];
+    if (B4) {
+      const int br = 64 * w + 16 * (i & 3) + (lane >> 2);
+      bq[i] = m.Bq + (int64_t)min(n0 + br, g.N - 1) * kbq + 16 * ((lane & 3) ^ ((br >> 2) & 3));
+    } else {
+      bq[i] = m.Bq + (int64_t)min(n0 + crow[i], g.N - 1) * kbq + 16 * cch[i];
+    }
   }
   // scale words: lane -> row 64 w + lane of the tile
   const int sr = row0 + min(64 * w + lane, mrows - 1);
@@ -162,8 +177,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx8(GemmMxArgs m) {
     if (st < nk) {
 #pragma unroll
       for (int i = 0; i < CPW; ++i) dma16_at(aq[i] + 128 * (int64_t)st, ua + 1024u * i);
+      if (B4) {
+        const uint32_t ub4 = ring_lds + 16u * (uint32_t)((2 * b + 1) * 2048 + 256 * w);
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) dma16_at(bq[i] + 128 * (int64_t)st, ub + 1024u * i);
+        for (int i = 0; i < 4; ++i) dma16_at(bq[i] + 64 * (int64_t)st, ub4 + 1024u * i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) dma16_at(bq[i] + 128 * (int64_t)st, ub + 1024u * i);
+      }
       dma4_at(asc + 4 * st, scl_lds + 4u * (uint32_t)((b * 2 + 0) * 256 + 64 * w));
       dma4_at(bsc + 4 * st, scl_lds + 4u * (uint32_t)((b * 2 + 1) * 256 + 64 * w));
       return;
@@ -226,6 +247,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx8(GemmMxArgs m) {
     const u32x4 p1 = unit[r * 8 + ((4 * sl + 2 + half) ^ kx8(r))];
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
+  // W0 fragment of slice sl: FP8 as above; FP4 (B4) 16 bytes of row r, chunk
+  // 2 sl + half, in the first four dwords.
+  auto fragb = [&](const u32x4* unit, int r, int sl) -> i32x8 {
+    if constexpr (B4) {
+      const u32x4 p = unit[r * 4 + ((2 * sl + half) ^ ((r >> 2) & 3))];
+      return __builtin_bit_cast(i32x8, __builtin_shufflevector(p, zero4(), 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return frag8(unit, r, sl);
+    }
+  };
+  constexpr int FMT_B = B4 ? 4 : 0;              // first operand: E2M1 (4) or E4M3 (0)
 
   issue(0, 0);
   int st = 0;
@@ -247,18 +279,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx8(GemmMxArgs m) {
       i32x8 fa[FI];
 #pragma unroll
       for (int f = 0; f < FI; ++f) fa[f] = frag8(ua, wrow + 32 * f + l32, sl);
-      i32x8 fbc = frag8(ub, wcol + l32, sl);
+      i32x8 fbc = fragb(ub, wcol + l32, sl);
 #pragma unroll
       for (int fj = 0; fj < FJ; ++fj) {
-        const i32x8 fbn = fj + 1 < FJ ? frag8(ub, wcol + 32 * (fj + 1) + l32, sl) : fbc;
+        const i32x8 fbn = fj + 1 < FJ ? fragb(ub, wcol + 32 * (fj + 1) + l32, sl) : fbc;
 #pragma unroll
         for (int fi = 0; fi < FI; ++fi) {
           if (sl == 0)
-            acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbc, fa[fi], acc[fi][fj], 0, 0, 0, sb[fj],
-                                                                          0, sa[fi]);
+            acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbc, fa[fi], acc[fi][fj], FMT_B, 0, 0,
+                                                                          sb[fj], 0, sa[fi]);
           else
-            acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbc, fa[fi], acc[fi][fj], 0, 0, 2, sb[fj],
-                                                                          2, sa[fi]);
+            acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbc, fa[fi], acc[fi][fj], FMT_B, 0, 2,
+                                                                          sb[fj], 2, sa[fi]);
         }
         fbc = fbn;
       }
@@ -300,8 +332,13 @@ void launch_gemm_mx8(const GemmMxArgs& m, hipStream_t s) {
   const int total = m.g.n_mtiles * m.g.n_ntiles;
   if (total <= 0) return;
   dim3 grid((unsigned)total), block(256);
-  if (m.g.t.perm) hipLaunchKernelGGL(k_gemm_mx8<true>, grid, block, 0, s, m);
-  else hipLaunchKernelGGL(k_gemm_mx8<false>, grid, block, 0, s, m);
+  if (m.b4) {
+    if (m.g.t.perm) hipLaunchKernelGGL((k_gemm_mx8<true, true>), grid, block, 0, s, m);
+    else hipLaunchKernelGGL((k_gemm_mx8<false, true>), grid, block, 0, s, m);
+  } else {
+    if (m.g.t.perm) hipLaunchKernelGGL((k_gemm_mx8<true, false>), grid, block, 0, s, m);
+    else hipLaunchKernelGGL((k_gemm_mx8<false, false>), grid, block, 0, s, m);
+  }
 }
 
 }  // namespace mlora

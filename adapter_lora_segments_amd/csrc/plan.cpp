@@ -187,8 +187,8 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
     return MLORA_ERR_INVALID_ARG;
   }
   if (o.act_format == MLORA_ACT_MXFP8 &&
-      (o.w0_format != MLORA_W0_MXFP8 || o.w0_layout != MLORA_W0_NK || d_in % 128 != 0)) {
-    err = "MXFP8 activations need an MXFP8 base held as [d_out][d_in] (w0_layout NK) and d_in a multiple of 128";
+      (o.w0_format == MLORA_W0_BF16 || o.w0_layout != MLORA_W0_NK || d_in % 128 != 0)) {
+    err = "MXFP8 activations need an MXFP8 or MXFP4 base held as [d_out][d_in] (w0_layout NK) and d_in a multiple of 128";
     return MLORA_ERR_UNSUPPORTED;
   }
 

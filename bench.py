@@ -588,7 +588,7 @@ def main():
                          "with E8M0 scales per 32 inputs, decoded per call; implies --no-sequential")
     ap.add_argument("--act-format", default="bf16", choices=["bf16", "mxfp8"],
                     help="mxfp8: quantize the activations of the forward's base product to MXFP8 and run it "
-                         "on the MXFP8 matrix cores (needs --w0-format mxfp8; the base is held as [d_out][d_in])")
+                         "on the scaled matrix cores (needs --w0-format mxfp8 or mxfp4; the base is held as [d_out][d_in])")
     ap.add_argument("--w0-layout", default="kn", choices=["kn", "nk", "both"],
                     help="layout of the frozen base: [d_in][d_out], [d_out][d_in], or both (held once in "
                          "each layout, built before timing; the forward then reads [d_out][d_in])")
@@ -658,8 +658,8 @@ def main():
     if a.fused:
         a.all_projections, a.no_sequential = True, True
     mx = a.w0_format in ("mxfp8", "mxfp4")
-    if a.act_format == "mxfp8" and a.w0_format != "mxfp8":
-        print("--act-format mxfp8 needs --w0-format mxfp8", file=sys.stderr)
+    if a.act_format == "mxfp8" and a.w0_format == "bf16":
+        print("--act-format mxfp8 needs --w0-format mxfp8 or mxfp4", file=sys.stderr)
         sys.exit(2)
     mx_layout = "nk" if a.act_format == "mxfp8" else "kn"
     if mx:

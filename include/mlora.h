@@ -124,8 +124,8 @@ typedef struct {
   int32_t w0_layout;      /* mlora_w0_layout; default MLORA_W0_KN (BOTH: bf16/fp32 W0 only)  */
   int32_t w0_format;      /* mlora_w0_format; default MLORA_W0_BF16 (MXFP8, MXFP4: bf16 plans only) */
   int32_t act_format;     /* mlora_act_format of the activations in the forward's base product;
-                             MLORA_ACT_MXFP8 needs w0_format MXFP8, w0_layout NK and d_in a
-                             multiple of 128 (see "Activations on the MXFP8 matrix cores") */
+                             MLORA_ACT_MXFP8 needs w0_format MXFP8 or MXFP4, w0_layout NK and
+                             d_in a multiple of 128 (see "Activations on the MXFP8 matrix cores") */
   int32_t wg_overlap;     /* mlora_wg_overlap: where the backward's weight gradients run
                              (see "Streams"); default MLORA_WG_AUTO */
 } mlora_plan_opts;
@@ -338,9 +338,10 @@ mlora_status mlora_plan_upload(mlora_plan_t plan, void *workspace, size_t ws_byt
  * infinity.  The resident base takes 0.5 + 1/32 bytes per weight.
  *
  * Activations on the MXFP8 matrix cores (act_format = MLORA_ACT_MXFP8, with
- * an MXFP8 base held as [d_out][d_in]): the forward's base product runs on
- * gfx950's MXFP8 x MXFP8 instruction (v_mfma_scale_f32_32x32x64_f8f6f4)
- * with no bf16 copy of W0.  X is first quantized to MXFP8 by the OCP
+ * an MXFP8 or MXFP4 base held as [d_out][d_in]): the forward's base product
+ * runs on gfx950's scaled matrix instruction (v_mfma_scale_f32_32x32x64_
+ * f8f6f4: E4M3 x E4M3, or an E2M1 base against E4M3 activations) with no
+ * bf16 copy of W0.  X is first quantized to MXFP8 by the OCP
  * microscaling conversion, per row in blocks of 32 inputs along d_in: the
  * block's shared exponent is floor(log2 max|x|) - 8, clamped to [-127, 127]
  * (-127 for a block of zeros); elements x 2^-exponent are rounded to the

@@ -585,3 +585,19 @@ def test_weight_gradient_placement_rule():
     rk = (ctypes.c_int32 * 1)(8)
     assert L.mlora_plan(1, off, rk, 256, 256, 0, ctypes.byref(o), ctypes.byref(h)) == -1
     assert "wg_overlap" in L.mlora_last_error().decode()
+
+
+def test_mxfp8_activation_plan_options():
+    """MXFP8 activations: accepted with an MXFP8 or MXFP4 base held as
+    [d_out][d_in] and d_in a multiple of 128; refused otherwise, with a
+    message; the workspace then holds the activations' codes and scales."""
+    for fmt in ("mxfp8", "mxfp4"):
+        p = Plan([0, 5, 9], [4, 8], 256, 192, w0_format=fmt, w0_layout="nk", act_format="mxfp8")
+        q = Plan([0, 5, 9], [4, 8], 256, 192, w0_format=fmt, w0_layout="nk")
+        assert p.info["act_offset"] >= 0 and q.info["act_offset"] == -1
+        assert p.info["workspace_bytes"] >= q.info["workspace_bytes"] - 2 * 256 * 192 + 9 * 256 * 33 // 32
+        assert _status(lambda: Plan([0, 5, 9], [4, 8], 256, 192, w0_format=fmt, act_format="mxfp8")) == -2
+        assert _status(lambda: Plan([0, 5, 9], [4, 8], 192, 192, w0_format=fmt, w0_layout="nk",
+                                    act_format="mxfp8")) == -2
+    assert _status(lambda: Plan([0, 5, 9], [4, 8], 256, 192, w0_layout="nk", act_format="mxfp8")) == -2
+    assert "MXFP4" in _lib.lib().mlora_last_error().decode()

@@ -1,5 +1,5 @@
-"""MXFP8 activations on the MXFP8 matrix cores (act_format = mxfp8, with an
-MXFP8 base held as [d_out][d_in]) on the GPU.
+"""MXFP8 activations on the scaled matrix cores (act_format = mxfp8, with an
+MXFP8 or MXFP4 base held as [d_out][d_in]) on the GPU.
 
 - The quantized activations the forward leaves in the workspace are
   bit-identical to the oracle's OCP conversion (oracle/mx.py,
@@ -11,15 +11,17 @@ MXFP8 base held as [d_out][d_in]) on the GPU.
   backward is the straight-through one), within the bf16 bar; over
   segments, two stream groups and rows as shuffled per-token ids.
 - Full size in the bench's configuration (the 4096x4096 layer, the
-  8192x28672 projection of the 70B pair): Y on each adapter's first and
-  last row plus 32 seeded rows."""
+  8192x28672 projection of the 70B pair; with an MXFP4 base the 4096x4096
+  layer and the 28672x8192 projection): Y on each adapter's first and last
+  row plus 32 seeded rows.
+Both bases are checked over segments, two stream groups and shuffled ids."""
 import numpy as np
 import pytest
 
 from oracle import lora as ol
 from oracle import mx as omx
 from tests.gpu_harness import TOL, compare, custom_workload, say, to_dev, to_host_f64, workspace_dz
-from workloads.mx import pack, quantize_mx
+from workloads.mx import pack, quantize_mx, quantize_mx4
 from workloads.tensors import f32_to_bf16_bits, host_tensors
 
 
@@ -31,9 +33,10 @@ def _act_region(plan, layer):
     return raw[:T * K].reshape(T, K), raw[T * K:].reshape(T, K // 32)
 
 
-def _mx_base(h, d_in, d_out):
-    codes, sc = quantize_mx(ol.as_f64(h["W0"], "bf16"), "nk")
-    return codes, sc, omx.dequant_w0(codes, sc, d_in, d_out, "nk")
+def _mx_base(h, d_in, d_out, fmt="mxfp8"):
+    q = quantize_mx4 if fmt == "mxfp4" else quantize_mx
+    codes, sc = q(ol.as_f64(h["W0"], "bf16"), "nk")
+    return codes, sc, omx.dequant_w0(codes, sc, d_in, d_out, "nk", fmt=fmt)
 
 
 @pytest.mark.gpu
@@ -82,18 +85,22 @@ CASES = [
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("name,d_in,d_out,ranks,tokens,streams,ids", CASES)
-def test_mxfp8_activation_layer_vs_oracle(name, d_in, d_out, ranks, tokens, streams, ids):
+def test_mxfp8_activation_layer_vs_oracle(name, d_in, d_out, ranks, tokens, streams, ids, fmt):
+    """MXFP8 activations against an MXFP8 base (E4M3 x E4M3) or an MXFP4
+    base (E2M1 first operand) on the scaled matrix instruction."""
     import torch
     from types import SimpleNamespace
     from adapter_lora_segments_amd import Plan, PackedLoRALinear
-    say(f"case mxfp8 activations {name}: {d_in}x{d_out} ranks {ranks} tokens {tokens} streams {streams}")
+    say(f"case mxfp8 activations, {fmt} base, {name}: {d_in}x{d_out} ranks {ranks} tokens {tokens} "
+        f"streams {streams}")
     w = custom_workload("mxact", "bf16", d_in, d_out, ranks, tokens, seed=9)
     h = host_tensors(w, 0)
-    codes, sc, Wdec = _mx_base(h, d_in, d_out)
+    codes, sc, Wdec = _mx_base(h, d_in, d_out, fmt)
     off = h["offsets"]
     T = int(off[-1])
-    opts = dict(n_streams=streams, w0_layout="nk", w0_format="mxfp8", act_format="mxfp8")
+    opts = dict(n_streams=streams, w0_layout="nk", w0_format=fmt, act_format="mxfp8")
     if ids:
         tok = np.repeat(np.arange(len(ranks)), tokens)
         perm = np.random.default_rng(2).permutation(T)
@@ -121,7 +128,7 @@ def test_mxfp8_activation_layer_vs_oracle(name, d_in, d_out, ranks, tokens, stre
     # the backward, Z' and dZ against the plain oracle over the decoded base; Y is checked below
     errs = compare(SimpleNamespace(dtype="bf16"), hh, dict(out, Y=ol.forward(X, Wdec, h["A"], h["B"], h["scales"],
                                                                                   off, "bf16")[0]),
-                   what=f"mxfp8 activations {name} (backward)")
+                   what=f"mxfp8 activations, {fmt} base, {name} (backward)")
     Yo, _ = omx.forward_act_mx(X, Wdec, h["A"], h["B"], h["scales"], off)
     e = ol.max_rel_err(Yh, Yo)
     # and the quantization is visible: Y differs from the bf16-activation layer's
@@ -131,21 +138,23 @@ def test_mxfp8_activation_layer_vs_oracle(name, d_in, d_out, ranks, tokens, stre
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("workload,proj", [("llama7b_proj", 0), ("mlp70b_pair", 0)])
-def test_mxfp8_activations_full_size(workload, proj):
+@pytest.mark.parametrize("workload,proj,fmt", [("llama7b_proj", 0, "mxfp8"), ("mlp70b_pair", 0, "mxfp8"),
+                                               ("llama7b_proj", 0, "mxfp4"), ("mlp70b_pair", 1, "mxfp4")])
+def test_mxfp8_activations_full_size(workload, proj, fmt):
     import torch
     from adapter_lora_segments_amd import Plan, PackedLoRALinear
     from tests.test_gpu_fullsize import stratified_rows
     from workloads import load_workload
-    from workloads.mx import quantize_mx_device
+    from workloads.mx import quantize_mx_device, quantize_mx4_device
     from workloads.tensors import device_tensors
     w = load_workload(workload, 0)
     p = w.projections[proj]
-    say(f"case mxfp8 activations full size {workload}/{p.name} ({p.d_in}x{p.d_out}, T={w.T})")
+    say(f"case mxfp8 activations, {fmt} base, full size {workload}/{p.name} ({p.d_in}x{p.d_out}, T={w.T})")
     d = device_tensors(w, proj)
-    Wmx = quantize_mx_device(d["W0"], "nk")                          # [d_out][d_in] codes, then scales
+    q = quantize_mx4_device if fmt == "mxfp4" else quantize_mx_device
+    Wmx = q(d["W0"], "nk")                                           # [d_out][d_in] codes, then scales
     plan = Plan(d["offsets"], d["ranks"], p.d_in, p.d_out, "bf16", n_streams=w.n_streams, w0_layout="nk",
-                w0_format="mxfp8", act_format="mxfp8")
+                w0_format=fmt, act_format="mxfp8")
     layer = PackedLoRALinear(plan, Wmx, d["A"], d["B"], d["scales"])
     X = d["X"][0]
     Y = layer.forward(X)
@@ -156,9 +165,10 @@ def test_mxfp8_activations_full_size(workload, proj):
     bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     Xr = bits(X.index_select(0, rt))
     raw = Wmx.cpu().numpy()
-    codes = raw[:p.d_in * p.d_out].reshape(p.d_out, p.d_in)
-    sc = raw[p.d_in * p.d_out:].reshape(p.d_out, p.d_in // 32)
-    Wdec = omx.dequant_w0(codes, sc, p.d_in, p.d_out, "nk")
+    ncb = p.d_in * p.d_out // (2 if fmt == "mxfp4" else 1)          # code bytes
+    codes = raw[:ncb].reshape(p.d_out, -1)
+    sc = raw[ncb:].reshape(p.d_out, p.d_in // 32)
+    Wdec = omx.dequant_w0(codes, sc, p.d_in, p.d_out, "nk", fmt=fmt)
     own = ol.adapter_of_rows(d["offsets"], rows)
     sub_off = np.concatenate([[0], np.cumsum(np.bincount(own, minlength=w.n))])
     Yo, _ = omx.forward_act_mx(Xr, Wdec, [bits(a) for a in d["A"]], [bits(b) for b in d["B"]], d["scales"], sub_off)
