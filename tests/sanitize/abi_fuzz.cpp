@@ -30,7 +30,8 @@ void launch_prep(const DevTables&, int32_t, int64_t, int64_t, int64_t, const voi
 void launch_skinny(int, const DevTables&, int32_t, int32_t, const uint16_t*, int64_t, const uint16_t*,
                    const void* const*, const float*, uint16_t*, hipStream_t) { reached("skinny"); }
 void launch_token_reduce(int, const DevTables&, int32_t, int32_t, const uint16_t*, int64_t, const uint16_t*,
-                         float*, int64_t, const uint16_t*, const uint16_t*, float*, int64_t, hipStream_t) {
+                         float*, int64_t, const uint16_t*, const uint16_t*, float*, int64_t, void* const*,
+                         void* const*, hipStream_t) {
   reached("token_reduce");
 }
 void launch_reduce_partials(const DevTables&, int32_t, int32_t, int64_t, int64_t, const float*, const float*,
