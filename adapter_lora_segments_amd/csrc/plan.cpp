@@ -285,20 +285,31 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
   p.partial_rows = cp;
   p.partial_b_elems = cb;
 
-  // 7: GEMM row tiles per group; each tile lists its extension steps per
-  // projection (the forward's column tiles take their own projection's list,
-  // the dX GEMM takes all of them)
+  // 7: GEMM row tiles of BM rows from row 0; group s's GEMMs take tiles
+  // [a_s, a_s+1), each boundary the largest multiple of G tiles that still
+  // ends at or before the group's first row (so a group's GEMM holds rows of
+  // its own and earlier groups only, whose shrink or dZ has run).  G = 16
+  // when every group can average two such units: a launch then covers whole
+  // rounds of 256 output tiles for any output width that is a multiple of
+  // 4096, with no partial row tile at a group boundary.  Each tile lists its
+  // extension steps per projection (the forward's column tiles take their
+  // own projection's list, the dX GEMM takes all of them).
   const int64_t BM = o.gemm_rows;
+  const int64_t ntile = (T + BM - 1) / BM;
+  const int64_t G = ntile >= 32 * (int64_t)S ? 16 : 1;
+  std::vector<int64_t> bound(S + 1, 0);
+  bound[S] = ntile;
+  for (int32_t s = 1; s < S; ++s)
+    bound[s] = std::max(bound[s - 1], seg_offsets[p.groups[s]] / BM / G * G);
+  int32_t first = 0;  // first adapter that can still meet a tile
   for (int32_t s = 0; s < S; ++s) {
     p.tile_start.push_back((int32_t)p.n_tiles());
-    const int64_t R0 = seg_offsets[p.groups[s]], R1 = seg_offsets[p.groups[s + 1]];
-    int32_t first = p.groups[s];  // first adapter that can still meet a tile
-    for (int64_t t0 = R0; t0 < R1; t0 += BM) {
-      const int64_t rows = std::min<int64_t>(BM, R1 - t0);
-      while (first < p.groups[s + 1] && seg_offsets[first + 1] <= t0) ++first;
+    for (int64_t tt = bound[s]; tt < bound[s + 1]; ++tt) {
+      const int64_t t0 = tt * BM, rows = std::min<int64_t>(BM, T - t0);
+      while (first < n && seg_offsets[first + 1] <= t0) ++first;
       for (int32_t q = 0; q < P; ++q) {
         p.ext_start.push_back((int32_t)p.n_ext());
-        for (int32_t j = first; j < p.groups[s + 1] && seg_offsets[j] < t0 + rows; ++j) {
+        for (int32_t j = first; j < n && seg_offsets[j] < t0 + rows; ++j) {
           const int64_t lo = std::max<int64_t>(seg_offsets[j], t0);
           const int64_t hi = std::min<int64_t>(seg_offsets[j + 1], t0 + rows);
           if (lo >= hi) continue;

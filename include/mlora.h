@@ -54,8 +54,9 @@
  * back to it with events before a call returns (so the caller sees ordinary
  * single-stream ordering), runs the HBM-bound LoRA work beside the base
  * GEMMs: with n_streams > 1 adapter groups, every group's shrink and dZ,
- * group by group, while each group's base GEMM runs on the caller's stream
- * once its own group's shrink or dZ is done; and the backward's weight
+ * group by group, while each group's base GEMM (its row tiles, rule 7 of
+ * mlora_plan) runs on the caller's stream once its own group's shrink or dZ
+ * is done; and the backward's weight
  * gradients (dA, dB) beside the dX GEMMs when wg_overlap resolves to
  * MLORA_WG_SIDE (otherwise they follow the last dX GEMM on the caller's
  * stream).  The GEMMs of different groups never run at the same time, so
@@ -153,8 +154,15 @@ typedef struct mlora_plan_s *mlora_plan_t;
  *     a small layer keeps enough pieces to fill the chip).
  *  6. Reduction chunks: pieces of KC_i rows; chunk c's partial sums sit at
  *     rank-row prefix cpref(c) = sum of r_pad over earlier chunks.
- *  7. GEMM row tiles of BM rows per group; each tile lists extension steps
- *     (adapter j, rows [lo,hi) of j in the tile, k0 = 0,32,..<r_pad(j)).
+ *  7. GEMM row tiles of BM rows from row 0, M = ceil(T / BM) of them (the
+ *     last one partial).  Group s's GEMMs take tiles [a_s, a_{s+1}): a_0 = 0,
+ *     a_S' = M, a_s = max(a_{s-1}, G floor(floor(o_{g_s} / BM) / G)), G = 16
+ *     when M >= 32 S' and 1 otherwise.  A group's GEMM thus holds rows of
+ *     its own and earlier groups only (whose shrink and dZ have run), and
+ *     with G = 16 it covers whole rounds of 256 output tiles for any output
+ *     width that is a multiple of 4096.  Each tile lists extension steps
+ *     (adapter j of any group, rows [lo,hi) of j in the tile,
+ *     k0 = 0,32,..<r_pad(j)).
  *  8. Optimizer work items (see OPT_BLOCKS below).
  *  9. bf16 only: a group's GEMM with t = (row tiles) x ceil(N / 256) output
  *     tiles and nk = K / 32 K-steps (forward: N = d_out, K = d_in; dX:

@@ -26,10 +26,14 @@ Rule (all integers; counts and indexes int32, offsets into tensors int64):
     rows); cpref(c) = sum of r_pad over earlier chunks.  Each adapter's chunks
     are consecutive: first(i), count(i) (first = total chunks before it in the
     walk order when count is 0 is still defined as the walk position).
- 7. GEMM row tiles: per group, rows [o_{g_s}, o_{g_{s+1}}) cut into tiles of
-    BM rows.  For each tile, its extension steps: for every adapter j
-    (ascending) whose rows meet the tile, for k0 = 0, 32, ... < r_pad(j): entry
-    (j, lo, hi, k0) with [lo, hi) the rows of j inside the tile.
+ 7. GEMM row tiles: rows [0, T) cut into tiles of BM rows from row 0 (the
+    last one partial), M = ceil(T / BM) of them.  Group s takes tiles
+    [a_s, a_{s+1}): a_0 = 0, a_S' = M, and for 1 <= s < S'
+    a_s = max(a_{s-1}, G floor(floor(o_{g_s} / BM) / G)) with G = 16 when
+    M >= 32 S', else 1.  For each tile, its extension steps: for every
+    adapter j (ascending, whatever its group) whose rows meet the tile, for
+    k0 = 0, 32, ... < r_pad(j): entry (j, lo, hi, k0) with [lo, hi) the rows
+    of j inside the tile.
  8. Optimizer blocks: for every adapter i ascending, its trained tensors A_i
     (tensor 2i, d_in r_i elements) then B_i (tensor 2i+1, r_i d_out
     elements), each cut into consecutive pieces of OPT_BLOCK elements (last
@@ -168,22 +172,26 @@ def build_plan(offsets, ranks, opts: PlanOpts | None = None, widths=None, dims=N
 
     tiles, tile_start, ext, ext_start = [], [], [], []
     BM = opts.gemm_rows
+    ntile = -(-T // BM)
+    G = 16 if ntile >= 32 * S else 1
+    a = [0] * (S + 1)
+    a[S] = ntile
+    for s in range(1, S):
+        a[s] = max(a[s - 1], G * ((o[g[s]] // BM) // G))
     for s in range(S):
         tile_start.append(len(tiles))
-        R0, R1 = o[g[s]], o[g[s + 1]]
-        t0 = R0
-        while t0 < R1:
-            rows = min(BM, R1 - t0)
+        for t in range(a[s], a[s + 1]):
+            t0 = t * BM
+            rows = min(BM, T - t0)
             for q in range(P):
                 ext_start.append(len(ext))
-                for j in range(g[s], g[s + 1]):
+                for j in range(n):
                     lo, hi = max(o[j], t0), min(o[j + 1], t0 + rows)
                     if lo < hi:
                         v = j * P + q
                         for k0 in range(0, rpad[v], KSTEP):
                             ext.append((v, lo, hi, k0))
             tiles.append((t0, rows))
-            t0 += BM
     tile_start.append(len(tiles))
     ext_start.append(len(ext))
 

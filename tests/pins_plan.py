@@ -98,16 +98,23 @@ def check_invariants(m, offsets, ranks, opts, p, widths=None):
         cp += int(rpad[v])
         cb += int(rpad[v]) * wd[v % P]
     assert cp == p["partial_rows"] and cb == p["partial_b_elems"]
-    # tiles: each group's rows cut into BM-row tiles; extension entries per
-    # (tile, projection) are exactly the pairs of that projection meeting the
-    # tile, adapters ascending, k0 = 0, 32, .. < r_pad
-    for s in range(S):
-        pos = o[g[s]]
-        for t in range(p["tile_start"][s], p["tile_start"][s + 1]):
-            r0, mm = (int(x) for x in p["tiles"][t])
-            assert r0 == pos and (mm == opts.gemm_rows or t == p["tile_start"][s + 1] - 1)
-            pos += mm
-        assert pos == o[g[s + 1]]
+    # tiles: BM-row tiles from row 0 over every row, in order; group s takes
+    # a contiguous run whose rows all belong to groups <= s, each boundary the
+    # largest multiple of G tiles (16 with at least 32 tiles per group, else
+    # 1) ending at or before the next group's first row, never below the
+    # previous boundary
+    BM = opts.gemm_rows
+    M = -(-T // BM)
+    assert [tuple(int(x) for x in t) for t in p["tiles"]] == [(k * BM, min(BM, T - k * BM)) for k in range(M)]
+    ts = [int(x) for x in p["tile_start"]]
+    assert len(ts) == S + 1 and ts[0] == 0 and ts[S] == M
+    G = 16 if M >= 32 * S else 1
+    for s in range(1, S):
+        fits = [k for k in range(0, M + 1, G) if k * BM <= o[g[s]]]
+        assert ts[s] == max(ts[s - 1], max(fits))
+        assert ts[s] * BM <= o[g[s]]
+    # extension entries per (tile, projection) are exactly the pairs of that
+    # projection meeting the tile, adapters ascending, k0 = 0, 32, .. < r_pad
     es = p["tile_ext_start"]
     assert len(es) == len(p["tiles"]) * P + 1
     for t, (r0, mm) in enumerate(p["tiles"]):
@@ -149,6 +156,31 @@ def pin_hand_ids(m):
     p = m.build_plan_from_ids(g["ids"], g["ranks"], m.PlanOpts(**g["opts"]),
                               dims=(g["d_in"], g["d_out"], g["dtype"]))
     _expect(p, g)
+
+
+def pin_group_tiles_by_hand(m):
+    """Rule 7's group boundaries on layers worked by hand."""
+    # 65536 rows, four groups: 256 tiles >= 32 x 4, so boundaries are multiples
+    # of 16 tiles.  Groups start at adapters 1, 2, 3 (rows 20000, 40000,
+    # 50000 >= 16384, 32768, 49152); floor(row / 256) = 78, 156, 195, rounded
+    # down to 64, 144, 192.
+    p = m.build_plan([0, 20000, 40000, 50000, 65536], [8, 16, 32, 64], m.PlanOpts(n_streams=4))
+    assert p["tile_start"].tolist() == [0, 64, 144, 192, 256]
+    assert p["tiles"][78].tolist() == [19968, 256] and p["tiles"][255].tolist() == [65280, 256]
+    # tile 78 (group 1's run) holds adapter 0's last 32 rows and adapter 1's first 224
+    e0, e1 = p["tile_ext_start"][78], p["tile_ext_start"][79]
+    assert p["ext"][e0:e1].tolist() == [[0, 19968, 20000, 0], [1, 20000, 20224, 0]]
+    # 1000 rows, two groups: 4 tiles < 64, boundaries not rounded; group 1 starts
+    # at row 600, floor(600 / 256) = 2, so tile 2 (rows 512..767, both adapters) is group 1's
+    p = m.build_plan([0, 600, 1000], [8, 8], m.PlanOpts(n_streams=2))
+    assert p["tile_start"].tolist() == [0, 2, 4]
+    assert p["tiles"].tolist() == [[0, 256], [256, 256], [512, 256], [768, 232]]
+    e0, e1 = p["tile_ext_start"][2], p["tile_ext_start"][3]
+    assert p["ext"][e0:e1].tolist() == [[0, 512, 600, 0], [1, 600, 768, 0]]
+    # the threshold: 16384 rows make 64 tiles = 32 x 2 (rounded: floor(9000 / 256) = 35 -> 32);
+    # 16128 rows make 63 (not rounded: 35)
+    assert m.build_plan([0, 9000, 16384], [8, 8], m.PlanOpts(n_streams=2))["tile_start"].tolist() == [0, 32, 64]
+    assert m.build_plan([0, 9000, 16128], [8, 8], m.PlanOpts(n_streams=2))["tile_start"].tolist() == [0, 35, 63]
 
 
 def pin_ids_definition(m):
@@ -223,7 +255,15 @@ def pin_invariants_random(m):
             widths = rng.choice([256, 512, 768], size=P).tolist()
             p = m.build_plan(off, ranks, opts, widths=widths)
             check_invariants(m, off, ranks, opts, p, widths=widths)
+    # layers large enough that the group boundaries round to 16 tiles
+    for case in range(12):
+        n = int(rng.integers(2, 20))
+        toks = rng.integers(0, 12000, size=n)
+        off = np.concatenate([[0], np.cumsum(toks)]).tolist()
+        opts = m.PlanOpts(n_streams=int(rng.integers(2, 5)))
+        ranks = rng.integers(1, 257, size=n).tolist()
+        check_invariants(m, off, ranks, opts, m.build_plan(off, ranks, opts))
 
 
-ALL_PINS = [pin_hand_single, pin_hand_multi, pin_hand_ids, pin_ids_definition, pin_split_k_by_hand,
-            pin_default_nano_rows_by_hand, pin_invariants_random]
+ALL_PINS = [pin_hand_single, pin_hand_multi, pin_hand_ids, pin_group_tiles_by_hand, pin_ids_definition,
+            pin_split_k_by_hand, pin_default_nano_rows_by_hand, pin_invariants_random]

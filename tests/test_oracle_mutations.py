@@ -128,7 +128,12 @@ PLAN_MUTATIONS = {
     "cboff_without_width": ("cb += rpad[v] * wd[v % P]", "cb += rpad[v] * wd[0]"),
     "ext_wrong_projection": ("v = j * P + q", "v = j * P"),
     "ext_k_step_64": ("for k0 in range(0, rpad[v], KSTEP):", "for k0 in range(0, rpad[v], 2 * KSTEP):"),
-    "tiles_across_groups": ("R0, R1 = o[g[s]], o[g[s + 1]]", "R0, R1 = o[g[s]], o[g[s + 1]] + (BM if s + 1 < S else 0)"),
+    "tile_boundary_rounded_up": ("a[s] = max(a[s - 1], G * ((o[g[s]] // BM) // G))",
+                                 "a[s] = max(a[s - 1], G * -(-(o[g[s]] // BM) // G))"),
+    "tile_boundary_not_aligned": ("G = 16 if ntile >= 32 * S else 1", "G = 1"),
+    "tile_alignment_threshold_per_plan": ("G = 16 if ntile >= 32 * S else 1", "G = 16 if ntile >= 32 else 1"),
+    "tile_ext_own_group_only": ("                for j in range(n):\n                    lo, hi = max(o[j], t0)",
+                                "                for j in range(g[s], g[s + 1]):\n                    lo, hi = max(o[j], t0)"),
     "default_nano_rows_threshold": ("NB = 128 if T * P >= 65536 else", "NB = 128 if T * P > 65536 else"),
     "default_nano_rows_ignores_projections": ("(64 if T * P >= 32768 else 32)", "(64 if T >= 32768 else 32)"),
     "split_k_no_rebalance": ("    return -(-nk // kper)", "    return sp"),
