@@ -552,6 +552,10 @@ def main():
     ap.add_argument("--workload", default="mlp70b_pair")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--streams", type=int, default=0)
+    ap.add_argument("--chunk-per-rank", type=int, default=0,
+                    help="plan option: reduction chunk rows per padded rank (0: the plan's default)")
+    ap.add_argument("--chunk-max", type=int, default=0,
+                    help="plan option: most rows in a reduction chunk (0: the plan's default)")
     ap.add_argument("--all-projections", action="store_true",
                     help="time every projection of the workload in each step (the default)")
     ap.add_argument("--first-projection", action="store_true",
@@ -691,11 +695,14 @@ def main():
                                     for _ in range(SETS)],
                       [torch.empty((w.T, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]))
 
+    chunk_opts = dict(chunk_per_rank=a.chunk_per_rank, chunk_max=a.chunk_max)
+
     def make_layers(n_streams):
         out = []
         for kind, d, Ys, dXs in datas:
             if kind == "multi":
-                plan = Plan.multi(d["offsets"], d["ranks"], d["d_in"], d["widths"], "bf16", n_streams=n_streams)
+                plan = Plan.multi(d["offsets"], d["ranks"], d["d_in"], d["widths"], "bf16", n_streams=n_streams,
+                                  **chunk_opts)
                 flat = lambda nested: [x for row in nested for x in row]
                 layer = PackedLoRALinear(plan, d["W0"], flat(d["A"]), flat(d["B"]), flat(d["scales"]))
             else:
@@ -703,11 +710,11 @@ def main():
                     ids = np.repeat(np.arange(w.n), np.diff(np.asarray(d["offsets"])))
                     ids = ids[np.random.default_rng(a.seed).permutation(w.T)]
                     plan = Plan.from_ids(ids, d["ranks"], d["d_in"], d["d_out"], "bf16", n_streams=n_streams,
-                                         w0_layout=a.w0_layout)
+                                         w0_layout=a.w0_layout, **chunk_opts)
                 else:
                     plan = Plan(d["offsets"], d["ranks"], d["d_in"], d["d_out"], "bf16", n_streams=n_streams,
                                 w0_format=a.w0_format, w0_layout=a.w0_layout if not mx else mx_layout,
-                                act_format=a.act_format)
+                                act_format=a.act_format, **chunk_opts)
                 if mx:
                     W0 = d["W0_codes"]
                 elif a.w0_layout == "nk":
