@@ -1,5 +1,6 @@
 // Ceiling probes (include/mlora_probes.h): a pure-MFMA loop in the base
-// GEMM's instruction pattern, and streaming copy / read kernels.
+// GEMM's instruction pattern, streaming copy / read kernels, and the paths
+// from L2 into LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -98,6 +99,62 @@ __global__ __launch_bounds__(256, 1) void k_mfma8_loop(const u32x4* ops, int64_t
 
 constexpr int kStreamBlocks = 2048;
 
+// Three ways to move L2-resident operand blocks into LDS, the base GEMM's
+// copy path and its alternatives.  Every workgroup (160 KiB of LDS, so one
+// per CU) streams its own 64 KiB slab `iters` times, each wave sixteen
+// 1 KiB pieces per pass:
+//   L2L_DIRECT: global_load_lds_dwordx4 (the GEMM's copies), sixteen of the
+//     wave's loads in flight;
+//   L2L_STAGED: global_load_dwordx4 into registers one pass ahead, then
+//     ds_write_b128;
+//   L2L_VGPR: the same loads into registers only.
+// The slab of workgroup b is src[b * 4096 .. b * 4096 + 4096] (16-byte
+// vectors; the staged and register paths read one vector past it on odd
+// passes, so src holds n_wg + 1 slabs).
+constexpr int kL2lVec = 4096;                  // 16-byte vectors per slab
+
+__device__ __forceinline__ uint32_t l2l_slot(int64_t it, int w, int i) {
+  return (uint32_t)((((int)(it & 1)) * 64 + w * 16 + i) % 160);
+}
+
+__global__ __launch_bounds__(256, 1) void k_l2l_direct(const u32x4* src, int64_t iters, uint32_t* out) {
+  __shared__ u32x4 lds[10240];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const u32x4* slab = src + (int64_t)blockIdx.x * kL2lVec;
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MLORA_LDS void*)lds);
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mlora::dma16_at(slab + (w * 16 + i) * 64 + lane, base + 1024u * l2l_slot(it, w, i));
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = lds[threadIdx.x][0];
+}
+
+template <bool STORE>
+__global__ __launch_bounds__(256, 1) void k_l2l_vgpr(const u32x4* src, int64_t iters, uint32_t* out) {
+  __shared__ u32x4 lds[10240];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const u32x4* slab = src + (int64_t)blockIdx.x * kL2lVec;
+  u32x4 v[16], sink = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __builtin_nontemporal_load(slab + (w * 16 + i) * 64 + lane);
+  for (int64_t it = 1; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (STORE) lds[l2l_slot(it, w, i) * 64 + lane] = v[i];
+      else sink ^= v[i];
+      v[i] = __builtin_nontemporal_load(slab + (w * 16 + i) * 64 + lane + (it & 1));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sink ^= v[i];
+  lds[4096 + threadIdx.x] = sink;
+  __syncthreads();
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = lds[threadIdx.x][0] ^ lds[4096 + threadIdx.x][1];
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,6 +192,19 @@ int mlora_probe_read(const void* src, int64_t bytes, float* out, void* stream) {
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(k_read, dim3(kStreamBlocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), bytes / 16, out);
+  return (int)hipGetLastError();
+}
+
+int mlora_probe_l2_to_lds(int path, int64_t n_wg, int64_t iters, const void* src, uint32_t* out,
+                          void* stream) {
+  if (path < 0 || path > 2 || n_wg < 1 || n_wg > 4096 || iters < 2 || iters > (1 << 20) || !src || !out ||
+      (reinterpret_cast<uintptr_t>(src) & 15u))
+    return (int)hipErrorInvalidValue;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const u32x4* v = static_cast<const u32x4*>(src);
+  if (path == MLORA_L2L_DIRECT) hipLaunchKernelGGL(k_l2l_direct, dim3((unsigned)n_wg), dim3(256), 0, s, v, iters, out);
+  else if (path == MLORA_L2L_STAGED) hipLaunchKernelGGL(k_l2l_vgpr<true>, dim3((unsigned)n_wg), dim3(256), 0, s, v, iters, out);
+  else hipLaunchKernelGGL(k_l2l_vgpr<false>, dim3((unsigned)n_wg), dim3(256), 0, s, v, iters, out);
   return (int)hipGetLastError();
 }
 

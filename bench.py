@@ -192,8 +192,11 @@ def cpu_baseline(w, projs, flop_budget=2.0e12):
 def ceilings(random_only=False):
     """Measured ceilings of this GPU (libmlora_probes.so): the pure-MFMA loop
     in the base GEMM's instruction pattern with random and with zero bf16
-    operands (TFLOP/s), and streaming copy and read bandwidth (GB/s), each the
-    best of several timed launches on torch's current stream."""
+    operands (TFLOP/s), streaming copy and read bandwidth (GB/s), and the
+    rate at which L2-resident operand blocks reach LDS by the base GEMM's
+    direct-to-LDS copies, by register-staged copies, and into registers only
+    (GB/s, and per CU), each the best of several timed launches on torch's
+    current stream."""
     import ctypes
     import torch
     from adapter_lora_segments_amd import _lib
@@ -206,7 +209,9 @@ def ceilings(random_only=False):
     L.mlora_probe_mfma8.argtypes = [i64, i64, vp, vp, vp]
     L.mlora_probe_copy.argtypes = [vp, vp, i64, vp]
     L.mlora_probe_read.argtypes = [vp, i64, vp, vp]
-    for f in (L.mlora_probe_mfma, L.mlora_probe_mfma8, L.mlora_probe_copy, L.mlora_probe_read):
+    L.mlora_probe_l2_to_lds.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
+    for f in (L.mlora_probe_mfma, L.mlora_probe_mfma8, L.mlora_probe_copy, L.mlora_probe_read,
+              L.mlora_probe_l2_to_lds):
         f.restype = ctypes.c_int
     stream = vp(torch.cuda.current_stream().cuda_stream)
 
@@ -251,6 +256,16 @@ def ceilings(random_only=False):
     ms = best(lambda: L.mlora_probe_read(vp(src.data_ptr()), nbytes, vp(red.data_ptr()), stream))
     out["hbm_read"] = {"achieved": (nbytes + red.numel() * 4) / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms": ms,
                        "bytes_per_launch": nbytes + red.numel() * 4}
+    # operand blocks from L2 into LDS, one workgroup per CU, each on its own 64 KiB slab
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    l2l_iters = 2000
+    l2l_out = torch.empty(ncu * 256, dtype=torch.int32, device="cuda")
+    for path, name in ((0, "l2_to_lds_direct"), (1, "l2_to_lds_staged"), (2, "l2_to_registers")):
+        ms = best(lambda: L.mlora_probe_l2_to_lds(path, ncu, l2l_iters, vp(src.data_ptr()),
+                                                   vp(l2l_out.data_ptr()), stream))
+        moved = ncu * l2l_iters * 65536
+        out[name] = {"achieved": moved / (ms * 1e-3) / 1e9, "unit": "GB/s", "ms": ms,
+                     "per_cu": moved / ncu / (ms * 1e-3) / 1e9}
     del src, dst
     torch.cuda.empty_cache()
     return out

@@ -45,6 +45,24 @@ int mlora_probe_copy(const void *src, void *dst, int64_t bytes, void *stream);
  * to out (device, 524288 floats): HBM traffic = bytes + 2 MiB. */
 int mlora_probe_read(const void *src, int64_t bytes, float *out, void *stream);
 
+/* Operand blocks from L2 into LDS: n_wg workgroups (one per CU: each holds
+ * 160 KiB of LDS) each stream their own 64 KiB slab `iters` times, 16 KiB
+ * per wave per pass, by one of three paths:
+ *   MLORA_L2L_DIRECT  global_load_lds_dwordx4 (the base GEMM's copies);
+ *   MLORA_L2L_STAGED  global_load_dwordx4 into registers one pass ahead,
+ *                     then ds_write_b128;
+ *   MLORA_L2L_VGPR    the same loads into registers only.
+ * Bytes moved = n_wg * iters * 65536.  src: device, 16-byte aligned, at
+ * least (n_wg + 1) * 65536 bytes (slab b at byte 65536 b; the staged and
+ * register paths read 16 bytes past their slab on odd passes); with n_wg
+ * up to 32 per XCD the slabs stay in L2.  out: device, n_wg * 256 uint32 (a
+ * digest of LDS, so no load is removed).  path in [0, 2], n_wg in
+ * [1, 4096], iters in [2, 2^20]. */
+#define MLORA_L2L_DIRECT 0
+#define MLORA_L2L_STAGED 1
+#define MLORA_L2L_VGPR 2
+int mlora_probe_l2_to_lds(int path, int64_t n_wg, int64_t iters, const void *src, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

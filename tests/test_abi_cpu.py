@@ -30,6 +30,36 @@ def test_library_exports_every_declared_symbol():
     assert L.mlora_status_string(-4).decode() == "MLORA_ERR_WORKSPACE"
 
 
+def test_probe_library_exports_every_declared_symbol():
+    """libmlora_probes.so (the measured ceilings) exports what
+    include/mlora_probes.h declares, and refuses malformed calls before any
+    HIP call (hipErrorInvalidValue = 1)."""
+    with open(os.path.join(ROOT, "include", "mlora_probes.h")) as f:
+        hdr = f.read()
+    declared = set(re.findall(r"\b(mlora_probe_[a-z0-9_]+)\s*\(", hdr))
+    assert declared == {"mlora_probe_mfma", "mlora_probe_mfma8", "mlora_probe_copy", "mlora_probe_read",
+                        "mlora_probe_l2_to_lds"}, declared
+    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "libmlora_probes.so")
+    L = ctypes.CDLL(path)
+    for name in declared:
+        assert hasattr(L, name), name
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    f = L.mlora_probe_l2_to_lds
+    f.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
+    f.restype = ctypes.c_int
+    buf = ctypes.create_string_buffer(64)
+    ok = ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16
+    assert f(3, 1, 2, vp(ok), vp(ok), None) == 1            # no such path
+    assert f(0, 0, 2, vp(ok), vp(ok), None) == 1            # no workgroup
+    assert f(0, 1, 1, vp(ok), vp(ok), None) == 1            # fewer than two passes
+    assert f(0, 1, 2, vp(ok + 4), vp(ok), None) == 1        # misaligned source
+    assert f(0, 1, 2, None, vp(ok), None) == 1
+    g = L.mlora_probe_copy
+    g.argtypes = [vp, vp, i64, vp]
+    g.restype = ctypes.c_int
+    assert g(vp(ok), vp(ok), 16, None) == 1                  # overlapping
+
+
 def _mirror_vs_library(off, ranks, d_in, d_out, dtype, opts):
     p = Plan(off, ranks, d_in, d_out, dtype, nano_rows=opts.nano_rows, gemm_rows=opts.gemm_rows,
              n_streams=opts.n_streams, chunk_min=opts.chunk_min, chunk_max=opts.chunk_max,
