@@ -567,6 +567,8 @@ def main():
     ap.add_argument("--workload", default="mlp70b_pair")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--streams", type=int, default=0)
+    ap.add_argument("--nano-rows", type=int, default=0,
+                    help="plan option: rows per nano-batch of the skinny products (0: the plan's default)")
     ap.add_argument("--chunk-per-rank", type=int, default=0,
                     help="plan option: reduction chunk rows per padded rank (0: the plan's default)")
     ap.add_argument("--chunk-max", type=int, default=0,
@@ -710,7 +712,7 @@ def main():
                                     for _ in range(SETS)],
                       [torch.empty((w.T, p.d_in), dtype=torch.bfloat16, device="cuda") for _ in range(SETS)]))
 
-    chunk_opts = dict(chunk_per_rank=a.chunk_per_rank, chunk_max=a.chunk_max)
+    chunk_opts = dict(chunk_per_rank=a.chunk_per_rank, chunk_max=a.chunk_max, nano_rows=a.nano_rows)
 
     def make_layers(n_streams):
         out = []
