@@ -38,7 +38,8 @@ class PlanOpts(ctypes.Structure):
                 ("n_streams", ctypes.c_int32), ("chunk_min", ctypes.c_int32),
                 ("chunk_max", ctypes.c_int32), ("chunk_per_rank", ctypes.c_int32),
                 ("w0_layout", ctypes.c_int32), ("w0_format", ctypes.c_int32),
-                ("act_format", ctypes.c_int32), ("wg_overlap", ctypes.c_int32)]
+                ("act_format", ctypes.c_int32), ("wg_overlap", ctypes.c_int32),
+                ("grad_accumulate", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):

@@ -33,11 +33,13 @@ class Plan:
     def __init__(self, seg_offsets, ranks, d_in: int, d_out: int, dtype: str = "bf16",
                  nano_rows: int = 0, n_streams: int = 0, chunk_min: int = 0, chunk_max: int = 0,
                  chunk_per_rank: int = 0, w0_layout: str = "kn", gemm_rows: int = 0, _ids=None,
-                 _widths=None, w0_format: str = "bf16", act_format: str = "bf16", wg_overlap: str = "auto"):
+                 _widths=None, w0_format: str = "bf16", act_format: str = "bf16", wg_overlap: str = "auto",
+                 grad_accumulate: bool = False):
         rk = np.ascontiguousarray(np.asarray(ranks, dtype=np.int32))
         opts = _lib.PlanOpts(nano_rows, gemm_rows, n_streams, chunk_min, chunk_max, chunk_per_rank,
                              _lib.W0_LAYOUTS[w0_layout], _lib.W0_FORMATS[w0_format],
-                             _lib.ACT_FORMATS[act_format], _lib.WG_OVERLAP[wg_overlap])
+                             _lib.ACT_FORMATS[act_format], _lib.WG_OVERLAP[wg_overlap],
+                             1 if grad_accumulate else 0)
         h = ctypes.c_void_p()
         widths = [int(d_out)] if _widths is None else [int(v) for v in _widths]
         if _widths is not None:

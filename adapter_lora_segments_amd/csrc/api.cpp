@@ -99,6 +99,7 @@ mlora::DevTables dev_tables(const mlora_plan_s* p, void* ws) {
   t.pcol = reinterpret_cast<const int32_t*>(b + L.pcol);
   t.cboff = reinterpret_cast<const int64_t*>(b + L.cboff);
   t.nproj = p->P.nproj;
+  t.accumulate = p->P.opts.grad_accumulate;
   return t;
 }
 

@@ -35,6 +35,7 @@ struct DevTables {
   const int32_t* pcol;      // [nproj+1]
   const int64_t* cboff;     // [n_chunks] element offset of a chunk's dB partial
   int32_t nproj;
+  int32_t accumulate;       // 1: the backward adds to dA_i, dB_i; 0: it overwrites them
 };
 
 // ---------------- bf16 path (MFMA) ----------------

@@ -772,8 +772,10 @@ __device__ __forceinline__ void token_reduce_dma_body(const TokenReduceArgs& a, 
           if (n < big_n) {
             if (!direct)
               *reinterpret_cast<f32x4*>(part + ldc(a.t.cboff + ch) + (int64_t)c * big_n + n) = v;
-            else if (c < rj)
-              *reinterpret_cast<f32x4*>(grad + (int64_t)c * big_n + n) = v;
+            else if (c < rj) {
+              f32x4* gp = reinterpret_cast<f32x4*>(grad + (int64_t)c * big_n + n);
+              *gp = a.t.accumulate ? *gp + v : v;
+            }
           }
         } else {
           // D[c][d]: lane holds d = nb + l32, c = cb + 8g + 4half + e
@@ -785,7 +787,10 @@ __device__ __forceinline__ void token_reduce_dma_body(const TokenReduceArgs& a, 
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (c + e < rj) grad[(int64_t)d * rj + c + e] = v[e];
+                if (c + e < rj) {
+                  float* gp = grad + (int64_t)d * rj + c + e;
+                  *gp = a.t.accumulate ? *gp + v[e] : v[e];
+                }
             }
           }
         }
@@ -875,11 +880,12 @@ __global__ __launch_bounds__(256) void k_reduce_partials(DevTables t, int32_t a_
           sum += *reinterpret_cast<const f32x4*>(partA + (int64_t)ldc(t.cpref + first + k) * d_in + d * rp + c0);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (c0 + e < r) gA[d * r + c0 + e] = sum[e];
+          if (c0 + e < r) gA[d * r + c0 + e] = t.accumulate ? gA[d * r + c0 + e] + sum[e] : sum[e];
       } else {
         const int64_t q = 4 * (i - na4);
         for (int k = 0; k < cnt; ++k)
           sum += *reinterpret_cast<const f32x4*>(partB + ldc(t.cboff + first + k) + q);
+        if (t.accumulate) sum += *reinterpret_cast<const f32x4*>(gB + q);
         *reinterpret_cast<f32x4*>(gB + q) = sum;
       }
     }

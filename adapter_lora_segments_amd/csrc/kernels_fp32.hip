@@ -165,7 +165,8 @@ __global__ __launch_bounds__(256) void k_f32_db(DevTables t, int32_t n, int64_t 
     float acc = 0.f;
     for (int64_t row = a; row < b; ++row)
       acc = fmaf(z[(row - a) * rp], dY[caller_row(t, row) * d_out + c0 + o], acc);
-    static_cast<float*>(dB[j])[idx] = acc;
+    float* gp = static_cast<float*>(dB[j]) + idx;
+    *gp = t.accumulate ? *gp + acc : acc;
   }
 }
 
@@ -185,7 +186,8 @@ __global__ __launch_bounds__(256) void k_f32_da(DevTables t, int32_t n, int64_t 
     float acc = 0.f;
     for (int64_t row = a; row < b; ++row)
       acc = fmaf(X[caller_row(t, row) * d_in + d], g[(row - a) * rp], acc);
-    static_cast<float*>(dA[j])[idx] = acc;
+    float* gp = static_cast<float*>(dA[j]) + idx;
+    *gp = t.accumulate ? *gp + acc : acc;
   }
 }
 

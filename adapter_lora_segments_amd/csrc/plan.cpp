@@ -134,6 +134,7 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
     o.w0_format = opts->w0_format;
     o.act_format = opts->act_format;
     o.wg_overlap = opts->wg_overlap;
+    o.grad_accumulate = opts->grad_accumulate;
   }
   if (o.nano_rows != 0 && (o.nano_rows < 16 || o.nano_rows > 256 || o.nano_rows % 16 != 0)) {
     err = "nano_rows must be a multiple of 16 in [16, 256]";
@@ -177,6 +178,10 @@ mlora_status build_plan_multi(int32_t n, const int64_t* seg_offsets, int32_t P, 
   if (o.w0_format != MLORA_W0_BF16 && dtype != MLORA_BF16) {
     err = "a microscaled (MXFP8/MXFP4) base weight needs a bf16 plan";
     return MLORA_ERR_UNSUPPORTED;
+  }
+  if (o.grad_accumulate != 0 && o.grad_accumulate != 1) {
+    err = "grad_accumulate must be 0 or 1";
+    return MLORA_ERR_INVALID_ARG;
   }
   if (o.wg_overlap != MLORA_WG_AUTO && o.wg_overlap != MLORA_WG_SIDE && o.wg_overlap != MLORA_WG_AFTER) {
     err = "wg_overlap must be MLORA_WG_AUTO, MLORA_WG_SIDE or MLORA_WG_AFTER";

@@ -27,6 +27,7 @@ struct Opts {
   int32_t w0_format = MLORA_W0_BF16;
   int32_t act_format = MLORA_ACT_BF16;
   int32_t wg_overlap = MLORA_WG_AUTO;
+  int32_t grad_accumulate = 0;
 };
 
 // Several projections that share one input (nproj > 1) split the output

@@ -129,6 +129,10 @@ typedef struct {
                              d_in a multiple of 128 (see "Activations on the MXFP8 matrix cores") */
   int32_t wg_overlap;     /* mlora_wg_overlap: where the backward's weight gradients run
                              (see "Streams"); default MLORA_WG_AUTO */
+  int32_t grad_accumulate;/* 0 (default): mlora_backward overwrites dA_i and dB_i (an adapter
+                             with no rows gets zeros); 1: it adds this call's gradients to
+                             what dA_i and dB_i hold (accumulation over micro-batches; an
+                             adapter with no rows keeps its values) */
 } mlora_plan_opts;
 
 typedef struct mlora_plan_s *mlora_plan_t;
@@ -406,7 +410,9 @@ mlora_status mlora_forward_noalloc(mlora_plan_t plan, const void *X, const void 
  * reduces over d_out inside one workgroup; Cases 1 and 3 reduce over tokens in
  * fixed-size chunks whose partial sums are added in a fixed order (no float
  * atomics: results are bitwise repeatable for a given plan); Case 4 runs as
- * extra K-steps of the dX GEMM.
+ * extra K-steps of the dX GEMM.  dA_i and dB_i are overwritten, or, with the
+ * plan option grad_accumulate, this call's gradients are added to them (one
+ * fp32 rounding per element; dX is overwritten either way).
  */
 mlora_status mlora_backward(mlora_plan_t plan, const void *dY, const void *X, const void *W0,
                             const void *const *A, const void *const *B, const float *scales,

@@ -112,6 +112,7 @@ mlora_plan_opts opts() {
   o.w0_format = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 5 : 2);
   o.act_format = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 3 : 1);
   o.wg_overlap = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 4 : 2);
+  o.grad_accumulate = (int32_t)uni(chance(5) ? -1 : 0, chance(5) ? 3 : 1);
   return o;
 }
 

@@ -617,6 +617,25 @@ def test_weight_gradient_placement_rule():
     assert "wg_overlap" in L.mlora_last_error().decode()
 
 
+def test_grad_accumulate_option():
+    """grad_accumulate: 0 and 1 are accepted (the plan's tables do not depend
+    on it); any other value is refused with a message."""
+    a = Plan([0, 100, 300], [8, 16], 256, 256)
+    b = Plan([0, 100, 300], [8, 16], 256, 256, grad_accumulate=True)
+    for name in ("nb", "chunks", "tiles", "ext"):
+        assert np.array_equal(a.export(name), b.export(name)), name
+    assert a.info["workspace_bytes"] == b.info["workspace_bytes"]
+    L = _lib.lib()
+    off = (ctypes.c_int64 * 2)(0, 100)
+    rk = (ctypes.c_int32 * 1)(8)
+    for bad in (-1, 2):
+        o = _lib.PlanOpts()
+        o.grad_accumulate = bad
+        h = ctypes.c_void_p()
+        assert L.mlora_plan(1, off, rk, 256, 256, 0, ctypes.byref(o), ctypes.byref(h)) == -1
+        assert "grad_accumulate" in L.mlora_last_error().decode()
+
+
 def test_mxfp8_activation_plan_options():
     """MXFP8 activations: accepted with an MXFP8 or MXFP4 base held as
     [d_out][d_in] and d_in a multiple of 128; refused otherwise, with a
