@@ -109,10 +109,11 @@ __device__ __forceinline__ void dma16_sv(uint64_t sbase, uint32_t voff, uint32_t
 //     LDS and nobody reads step s's units any more;
 //   slice 3: read step s+1's first slice; copy unit 2s+5 (B of step s+2)
 //     into the slot of step s's A unit.
-// Copies past the last step repeat the zero page into slots never read
-// again, so every barrier waits for the same count.  Steps whose refills
-// are main K-steps run a branch-free loop; the rest look their sources up
-// in the plan's tables.
+// Steps whose refills are main K-steps run a branch-free loop; the ones
+// that refill LoRA steps look their sources up in the plan's tables; the
+// last two, whose refills would lie past the last sub-step, copy nothing
+// and wait for every copy in flight at their barrier (else every barrier
+// waits for the same count: only the eight copies of unit 2s+4 in flight).
 template <bool FWD, bool MAIN_B_KC, bool PERM, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   constexpr int NU = 5;                    // ring units of 32 KiB
@@ -362,10 +363,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   };
   // First MFMA slot of a slice that carries a copy.
   constexpr int C0 = MAIN_B_KC ? 4 : 8;
-  auto step_block = [&](int s, auto main_tag) {
-    constexpr bool MAIN = decltype(main_tag)::value;   // units 2s+4 and 2s+5 are main K
+  // Step kinds (the units a step refills are 2s+4 and 2s+5, those of step
+  // s+2): 0, both are main K-steps (scalar bases, no lookups); 1, they look
+  // their sources up (LoRA steps, or a mix); 2, step s+2 does not exist:
+  // no copies, and the barrier waits for every copy in flight.
+  auto step_block = [&](int s, auto kind_tag) {
+    constexpr int KIND = decltype(kind_tag)::value;
+    constexpr bool MAIN = KIND == 0, LOOKUP = KIND == 1, COPY = KIND != 2;
     const uint16_t* sa[CPW];
-    if (!MAIN) unit_sources(2 * s + 4, sa);
+    if (LOOKUP) unit_sources(2 * s + 4, sa);
     Bases cur;
     step_bases(s, cur, 1, 3);
     const uint64_t cbA = MAIN && !PERM ? uniform64(baseA + (int64_t)(s + 2) * 128) : 0;
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[0], fb[0], qq);
       reads_at(qq, cur, 1, fa[1], fb[1]);
-      if (qq >= C0 && qq < C0 + 4) {
+      if (COPY && qq >= C0 && qq < C0 + 4) {
         if (MAIN) copy_main(2 * s + 4, qq - C0, cbA);
         else copy(sa[qq - C0], 2 * s + 4, qq - C0);
       }
@@ -384,7 +390,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[1], fb[1], qq);
       reads_at(qq, cur, 2, fa[0], fb[0]);
-      if (qq >= C0 && qq < C0 + 4) {
+      if (COPY && qq >= C0 && qq < C0 + 4) {
         if (MAIN) copy_main(2 * s + 4, qq - C0 + 4, cbA);
         else copy(sa[qq - C0 + 4], 2 * s + 4, qq - C0 + 4);
       }
@@ -397,9 +403,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wait_vm_barrier<CPW>();
+    wait_vm_barrier<COPY ? CPW : 0>();
     const uint16_t* sb[CPW];
-    if (!MAIN) unit_sources(2 * s + 5, sb);
+    if (LOOKUP) unit_sources(2 * s + 5, sb);
     Bases nxt;
     step_bases(s + 1, nxt, 0, 0);
     const uint64_t cbB = MAIN ? uniform64(baseB + (int64_t)(s + 2) * strideB) : 0;
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
     for (int qq = 0; qq < 16; ++qq) {
       mma(fa[1], fb[1], qq);
       reads_at(qq, nxt, 0, fa[0], fb[0]);
-      if (qq >= C0 && qq < C0 + 8) {
+      if (COPY && qq >= C0 && qq < C0 + 8) {
         if (MAIN) copy_main(2 * s + 5, qq - C0, cbB);
         else copy(sb[qq - C0], 2 * s + 5, qq - C0);
       }
@@ -434,8 +440,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   }
 
   int s = 0;
-  for (; 2 * s + 6 <= nk; ++s) step_block(s, std::true_type());
-  for (; s < nsteps; ++s) step_block(s, std::false_type());
+  for (; 2 * s + 6 <= nk; ++s) step_block(s, std::integral_constant<int, 0>());
+  for (; s < nsteps - 2; ++s) step_block(s, std::integral_constant<int, 1>());
+  for (; s < nsteps; ++s) step_block(s, std::integral_constant<int, 2>());
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
   gemm_store<PERM, SPLIT>(g, acc, reinterpret_cast<char*>(&ring[0][0]), tc, row0, mrows, n0, w, lane);
