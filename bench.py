@@ -152,13 +152,12 @@ def _oracle_step_seconds(w, projs):
     return dt
 
 
-def cpu_baseline(w, projs, flop_budget=5.0e12):
+def cpu_baseline(w, projs, flop_budget=1.0e13):
     """The oracle (numpy float64) on the host over a bounded sample of the
     workload: the same layer shapes, adapters and ranks with every adapter's
     token count scaled down in proportion (at least one token each), chosen
-    so the sample is about ``flop_budget`` floating-point operations (about
-    11 s on 16 host threads, where 2e12 took 4.5 s); the whole workload when
-    it is smaller.  Beside it, the oracle
+    so the sample is about ``flop_budget`` floating-point operations (5e12
+    took 6.8 s on 16 host threads); the whole workload when it is smaller.  Beside it, the oracle
     on one thread on the two smallest workloads (the fp32 256x256 layer
     whole, and the 4096x4096 layer on 1024 sampled tokens)."""
     from workloads import load_workload
