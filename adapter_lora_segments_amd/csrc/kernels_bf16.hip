@@ -141,6 +141,14 @@ void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
 // NS - 1 stages of copies in flight.  One launch covers every padded-rank
 // bucket of a stream group: each workgroup switches on its adapter's r_pad
 // and its block's row count.
+//
+// Projections sharing the input (plans over (adapter, projection) pairs):
+// when the padded ranks of an adapter's projections sum to at most 256, the
+// shrink of its first pair computes every projection's Z' at once (FUSED),
+// so X is read once for all of them: A_cat^T holds the pairs of an adapter
+// in consecutive rows, the rows past their sum read as zero, and column c
+// goes to the pair whose rows it falls in, scaled by that pair's s.  The
+// nano-batches of the adapter's other pairs then have nothing to do.
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyRows = 1280;               // 128-byte LDS rows: 160 KiB
 
@@ -157,15 +165,29 @@ struct SkinnyCfg {
 
 __device__ __forceinline__ int skx(int r) { return (r >> 1) & 7; }
 
-template <int RP, int R, int MODE, bool PERM>
+// The pair that column block c0 (a multiple of 32) of a fused shrink belongs
+// to, among pairs j0 .. j0 + np - 1, and c0's column within that pair.
+struct FusedCol {
+  int j, c;
+};
+__device__ __forceinline__ FusedCol fused_col(const DevTables& t, int j0, int np, int c0) {
+  int off = 0;
+  for (int q = 0; q < np - 1; ++q) {
+    const int rp = ldc(t.rpad + j0 + q);
+    if (c0 < off + rp) return FusedCol{j0 + q, c0 - off};
+    off += rp;
+  }
+  return FusedCol{j0 + np - 1, c0 - off};
+}
+
+template <int RP, int R, int MODE, bool PERM, bool FUSED>
 __device__ __forceinline__ void skinny_block(const DevTables& t, int j, int row0, int nrows,
                                              const uint16_t* P, int64_t K, int64_t ldp,
-                                             const uint16_t* acat_t, const void* const* Bptr, float s,
-                                             uint16_t* out, u32x4* ring) {
+                                             const uint16_t* acat_t, const void* const* Bptr,
+                                             const float* scales, uint16_t* out, u32x4* ring, int rlim) {
   using C = SkinnyCfg<RP, R>;
   constexpr int F = RP / 32, NS = C::NS, LPS = C::LPS, SK = 4 / R;
   const int64_t oj = ldc(t.seg0 + j);
-  const int64_t zo = ldc(t.zoff + j);
   const int rj = ldc(t.ranks + j);
   const uint16_t* Q = MODE == 0 ? acat_t + (int64_t)ldc(t.roff + j) * K
                                 : static_cast<const uint16_t*>(ldc(Bptr + j));
@@ -193,7 +215,7 @@ __device__ __forceinline__ void skinny_block(const DevTables& t, int j, int row0
       adv[q] = true;
     } else {
       const int c = row - 32 * R;
-      adv[q] = MODE == 0 || c < rj;
+      adv[q] = MODE == 0 ? (!FUSED || c < rlim) : c < rj;
       src[q] = adv[q] ? Q + (int64_t)c * K + 8 * ch : t.zero + 8 * (lane & 7);
     }
   }
@@ -237,18 +259,34 @@ __device__ __forceinline__ void skinny_block(const DevTables& t, int j, int row0
   wait_vm_barrier<0>();
 
   // acc[f][4g+e] = D[c = 32f + 8g + 4 half + e][row = 32 rf + l32]
+  // Where column block f (32 columns) of the result goes: pair, its Z'
+  // slab, row stride (the pair's r_pad), first column and scale.
+  struct Dst {
+    uint16_t* base;
+    int ld, c;
+    float s;
+  };
+  auto dst = [&](int f) -> Dst {
+    if constexpr (FUSED) {
+      const FusedCol fc = fused_col(t, j, t.nproj, 32 * f);
+      return Dst{out + ldc(t.zoff + fc.j), ldc(t.rpad + fc.j), fc.c, ldc(scales + fc.j)};
+    }
+    return Dst{out + ldc(t.zoff + j), RP, 32 * f, ldc(scales + j)};
+  };
   if constexpr (R == 4) {
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const int row = 32 * rf + l32;
+      if (FUSED && 32 * f >= rlim) continue;
+      const Dst d = dst(f);
       if (row < nrows) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int c = 32 * f + 8 * g + 4 * half;
+          const int c = d.c + 8 * g + 4 * half;
           u32x2 pk;
-          pk[0] = pack_bf16x2(s * acc[f][4 * g + 0], s * acc[f][4 * g + 1]);
-          pk[1] = pack_bf16x2(s * acc[f][4 * g + 2], s * acc[f][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(out + zo + (int64_t)(row0 + row - oj) * RP + c) = pk;
+          pk[0] = pack_bf16x2(d.s * acc[f][4 * g + 0], d.s * acc[f][4 * g + 1]);
+          pk[1] = pack_bf16x2(d.s * acc[f][4 * g + 2], d.s * acc[f][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(d.base + (int64_t)(row0 + row - oj) * d.ld + c) = pk;
         }
       }
     }
@@ -260,6 +298,8 @@ __device__ __forceinline__ void skinny_block(const DevTables& t, int j, int row0
     const int fr = tid / (256 / R), l = tid & 63, gq = (tid % (256 / R)) >> 6;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
+      if (FUSED && 32 * f >= rlim) continue;
+      const Dst d = dst(f);
 #pragma unroll
       for (int e = 0; e < 16; ++e) red[(w * 16 + e) * 64 + lane] = acc[f][e];
       __syncthreads();
@@ -276,11 +316,11 @@ __device__ __forceinline__ void skinny_block(const DevTables& t, int j, int row0
           v[i] = sum;
         }
         if (row < nrows) {
-          const int c = 32 * f + 8 * g + 4 * (l >> 5);
+          const int c = d.c + 8 * g + 4 * (l >> 5);
           u32x2 pk;
-          pk[0] = pack_bf16x2(s * v[0], s * v[1]);
-          pk[1] = pack_bf16x2(s * v[2], s * v[3]);
-          *reinterpret_cast<u32x2*>(out + zo + (int64_t)(row0 + row - oj) * RP + c) = pk;
+          pk[0] = pack_bf16x2(d.s * v[0], d.s * v[1]);
+          pk[1] = pack_bf16x2(d.s * v[2], d.s * v[3]);
+          *reinterpret_cast<u32x2*>(d.base + (int64_t)(row0 + row - oj) * d.ld + c) = pk;
         }
       }
       __syncthreads();
@@ -288,19 +328,20 @@ __device__ __forceinline__ void skinny_block(const DevTables& t, int j, int row0
   }
 }
 
-template <int RP, int MODE, bool PERM>
+template <int RP, int MODE, bool PERM, bool FUSED>
 __device__ __forceinline__ void skinny_item(const DevTables& t, int j, int row0, int nrows, const uint16_t* P,
                                             int64_t K, int64_t ldp, const uint16_t* acat_t,
-                                            const void* const* Bptr, float s, uint16_t* out, u32x4* ring) {
+                                            const void* const* Bptr, const float* scales, uint16_t* out,
+                                            u32x4* ring, int rlim) {
   // blocks of up to 128 rows; each block's copies are drained before the next
   for (int b0 = 0; b0 < nrows; b0 += 128) {
     const int nb = min(128, nrows - b0);
     if (nb <= 32)
-      skinny_block<RP, 1, MODE, PERM>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, s, out, ring);
+      skinny_block<RP, 1, MODE, PERM, FUSED>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, scales, out, ring, rlim);
     else if (nb <= 64)
-      skinny_block<RP, 2, MODE, PERM>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, s, out, ring);
+      skinny_block<RP, 2, MODE, PERM, FUSED>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, scales, out, ring, rlim);
     else
-      skinny_block<RP, 4, MODE, PERM>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, s, out, ring);
+      skinny_block<RP, 4, MODE, PERM, FUSED>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, scales, out, ring, rlim);
     __syncthreads();
   }
 }
@@ -313,7 +354,20 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
   __shared__ u32x4 ring[kSkinnyRows * 8];
   const int nb = nano_begin + blockIdx.x;
   const int j = ldc(t.nano + 3 * nb), row0 = ldc(t.nano + 3 * nb + 1), nrows = ldc(t.nano + 3 * nb + 2);
-  const float s = ldc(scales + j);
+  if (MODE == 0 && t.nproj > 1) {
+    // Shrink of an adapter whose projections' padded ranks sum to at most
+    // 256: its first pair computes all of them (X read once).
+    const int np = t.nproj, j0 = j - j % np;
+    int rs = 0;
+    for (int q = 0; q < np; ++q) rs += ldc(t.rpad + j0 + q);
+    if (rs <= 256) {
+      if (j != j0) return;
+      if (rs <= 64) skinny_item<64, 0, PERM, true>(t, j0, row0, nrows, P, K, K, acat_t, Bptr, scales, out, ring, rs);
+      else if (rs <= 128) skinny_item<128, 0, PERM, true>(t, j0, row0, nrows, P, K, K, acat_t, Bptr, scales, out, ring, rs);
+      else skinny_item<256, 0, PERM, true>(t, j0, row0, nrows, P, K, K, acat_t, Bptr, scales, out, ring, rs);
+      return;
+    }
+  }
   // dZ of pair j reads its projection's columns of dY: K = the projection's
   // width, rows K0 = the full row length apart
   int64_t Kj = K;
@@ -325,10 +379,10 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
     Pj = P + c0;
   }
   switch (ldc(t.rpad + j)) {
-    case 32: skinny_item<32, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
-    case 64: skinny_item<64, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
-    case 128: skinny_item<128, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
-    default: skinny_item<256, MODE, PERM>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, s, out, ring); break;
+    case 32: skinny_item<32, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 32); break;
+    case 64: skinny_item<64, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 64); break;
+    case 128: skinny_item<128, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 128); break;
+    default: skinny_item<256, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 256); break;
   }
 }
 
