@@ -3,7 +3,9 @@
 - Against the oracle (oracle/multi.py) on small layers: Y, dX, every pair's
   saved activation Z' (padding columns exactly zero), dA and dB; bf16 with
   both W0 layouts and one to three stream groups, fp32 with both layouts;
-  ranks 1..256, an adapter with no rows, projections of different widths.
+  ranks 1..256, an adapter with no rows, projections of different widths;
+  adapters whose padded ranks over the projections sum to at most 256
+  (their shrink runs once for all projections), exactly 256, and above.
 - The fused layer against one single-projection layer per projection over
   the same adapters: Y, Z', dA and dB are bit-identical (the same kernels
   visit the same extension steps, nano-batches and chunks in the same
@@ -25,6 +27,9 @@ CASES = [
     ("bf16", 256, [512, 256, 256], [[8, 8, 8], [64, 16, 33], [128, 1, 4], [256, 64, 32]], [150, 300, 0, 77], 1, "kn"),
     ("bf16", 320, [256, 512], [[16, 200], [3, 64], [256, 256]], [500, 9, 260], 3, "nk"),
     ("bf16", 256, [768, 768], [[256, 256], [32, 32]], [600, 333], 2, "kn"),
+    # shrink over an adapter's projections at once: one adapter over the limit, one exactly at 256, and the
+    # last one (padded ranks 3 x 32) in a 128-wide rank tile whose rows past the sum lie past A_cat^T
+    ("bf16", 256, [256, 256, 512], [[256, 8, 8], [128, 64, 64], [1, 1, 1]], [200, 90, 131], 1, "nk"),
     ("fp32", 128, [128, 64, 64], [[4, 8, 2], [16, 1, 3]], [40, 57], 1, "kn"),
     ("fp32", 128, [64, 192], [[5, 7], [2, 2], [1, 33]], [13, 0, 29], 2, "nk"),
 ]
