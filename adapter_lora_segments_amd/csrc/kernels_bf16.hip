@@ -143,12 +143,13 @@ void launch_prep_b(const DevTables& t, int32_t n, int64_t d_out, int64_t rtot,
 // and its block's row count.
 //
 // Projections sharing the input (plans over (adapter, projection) pairs):
-// when the padded ranks of an adapter's projections sum to at most 256, the
-// shrink of its first pair computes every projection's Z' at once (FUSED),
-// so X is read once for all of them: A_cat^T holds the pairs of an adapter
-// in consecutive rows, the rows past their sum read as zero, and column c
-// goes to the pair whose rows it falls in, scaled by that pair's s.  The
-// nano-batches of the adapter's other pairs then have nothing to do.
+// an adapter's projections are cut, in order, into groups whose padded
+// ranks sum to at most 256, and the shrink of a group's first pair computes
+// every pair of the group at once (FUSED), so X is read once per group:
+// A_cat^T holds the pairs of an adapter in consecutive rows, the rows past
+// the group's sum read as zero, and column c goes to the pair whose rows it
+// falls in, scaled by that pair's s.  The nano-batches of the group's other
+// pairs then have nothing to do.
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyRows = 1280;               // 128-byte LDS rows: 160 KiB
 
@@ -184,7 +185,8 @@ template <int RP, int R, int MODE, bool PERM, bool FUSED>
 __device__ __forceinline__ void skinny_block(const DevTables& t, int j, int row0, int nrows,
                                              const uint16_t* P, int64_t K, int64_t ldp,
                                              const uint16_t* acat_t, const void* const* Bptr,
-                                             const float* scales, uint16_t* out, u32x4* ring, int rlim) {
+                                             const float* scales, uint16_t* out, u32x4* ring, int rlim,
+                                             int fnp) {
   using C = SkinnyCfg<RP, R>;
   constexpr int F = RP / 32, NS = C::NS, LPS = C::LPS, SK = 4 / R;
   const int64_t oj = ldc(t.seg0 + j);
@@ -268,7 +270,7 @@ __device__ __forceinline__ void skinny_block(const DevTables& t, int j, int row0
   };
   auto dst = [&](int f) -> Dst {
     if constexpr (FUSED) {
-      const FusedCol fc = fused_col(t, j, t.nproj, 32 * f);
+      const FusedCol fc = fused_col(t, j, fnp, 32 * f);
       return Dst{out + ldc(t.zoff + fc.j), ldc(t.rpad + fc.j), fc.c, ldc(scales + fc.j)};
     }
     return Dst{out + ldc(t.zoff + j), RP, 32 * f, ldc(scales + j)};
@@ -332,16 +334,16 @@ template <int RP, int MODE, bool PERM, bool FUSED>
 __device__ __forceinline__ void skinny_item(const DevTables& t, int j, int row0, int nrows, const uint16_t* P,
                                             int64_t K, int64_t ldp, const uint16_t* acat_t,
                                             const void* const* Bptr, const float* scales, uint16_t* out,
-                                            u32x4* ring, int rlim) {
+                                            u32x4* ring, int rlim, int fnp) {
   // blocks of up to 128 rows; each block's copies are drained before the next
   for (int b0 = 0; b0 < nrows; b0 += 128) {
     const int nb = min(128, nrows - b0);
     if (nb <= 32)
-      skinny_block<RP, 1, MODE, PERM, FUSED>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, scales, out, ring, rlim);
+      skinny_block<RP, 1, MODE, PERM, FUSED>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, scales, out, ring, rlim, fnp);
     else if (nb <= 64)
-      skinny_block<RP, 2, MODE, PERM, FUSED>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, scales, out, ring, rlim);
+      skinny_block<RP, 2, MODE, PERM, FUSED>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, scales, out, ring, rlim, fnp);
     else
-      skinny_block<RP, 4, MODE, PERM, FUSED>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, scales, out, ring, rlim);
+      skinny_block<RP, 4, MODE, PERM, FUSED>(t, j, row0 + b0, nb, P, K, ldp, acat_t, Bptr, scales, out, ring, rlim, fnp);
     __syncthreads();
   }
 }
@@ -355,16 +357,27 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
   const int nb = nano_begin + blockIdx.x;
   const int j = ldc(t.nano + 3 * nb), row0 = ldc(t.nano + 3 * nb + 1), nrows = ldc(t.nano + 3 * nb + 2);
   if (MODE == 0 && t.nproj > 1) {
-    // Shrink of an adapter whose projections' padded ranks sum to at most
-    // 256: its first pair computes all of them (X read once).
-    const int np = t.nproj, j0 = j - j % np;
-    int rs = 0;
-    for (int q = 0; q < np; ++q) rs += ldc(t.rpad + j0 + q);
-    if (rs <= 256) {
-      if (j != j0) return;
-      if (rs <= 64) skinny_item<64, 0, PERM, true>(t, j0, row0, nrows, P, K, K, acat_t, Bptr, scales, out, ring, rs);
-      else if (rs <= 128) skinny_item<128, 0, PERM, true>(t, j0, row0, nrows, P, K, K, acat_t, Bptr, scales, out, ring, rs);
-      else skinny_item<256, 0, PERM, true>(t, j0, row0, nrows, P, K, K, acat_t, Bptr, scales, out, ring, rs);
+    // Shrink over a group of an adapter's projections (consecutive, padded
+    // ranks summing to at most 256, cut greedily from the first): the
+    // group's first pair computes all of them (X read once per group).
+    const int np = t.nproj, j0 = j - j % np, qj = j % np;
+    int gs = 0, rs = 0;
+    for (int q = 0; q <= qj; ++q) {
+      const int rp = ldc(t.rpad + j0 + q);
+      if (rs + rp > 256) {
+        gs = q;
+        rs = 0;
+      }
+      rs += rp;
+    }
+    int ge = qj + 1;
+    while (ge < np && rs + ldc(t.rpad + j0 + ge) <= 256) rs += ldc(t.rpad + j0 + ge++);
+    if (ge - gs > 1) {
+      if (qj != gs) return;
+      const int jg = j0 + gs, gn = ge - gs;
+      if (rs <= 64) skinny_item<64, 0, PERM, true>(t, jg, row0, nrows, P, K, K, acat_t, Bptr, scales, out, ring, rs, gn);
+      else if (rs <= 128) skinny_item<128, 0, PERM, true>(t, jg, row0, nrows, P, K, K, acat_t, Bptr, scales, out, ring, rs, gn);
+      else skinny_item<256, 0, PERM, true>(t, jg, row0, nrows, P, K, K, acat_t, Bptr, scales, out, ring, rs, gn);
       return;
     }
   }
@@ -379,10 +392,10 @@ __global__ __launch_bounds__(256) void k_skinny(DevTables t, int32_t nano_begin,
     Pj = P + c0;
   }
   switch (ldc(t.rpad + j)) {
-    case 32: skinny_item<32, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 32); break;
-    case 64: skinny_item<64, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 64); break;
-    case 128: skinny_item<128, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 128); break;
-    default: skinny_item<256, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 256); break;
+    case 32: skinny_item<32, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 32, 1); break;
+    case 64: skinny_item<64, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 64, 1); break;
+    case 128: skinny_item<128, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 128, 1); break;
+    default: skinny_item<256, MODE, PERM, false>(t, j, row0, nrows, Pj, Kj, K, acat_t, Bptr, scales, out, ring, 256, 1); break;
   }
 }
 
